@@ -1,0 +1,219 @@
+"""Python binding of libgdr, the MI355X gated delta-rule forward pass.
+
+Argument marshalling only: this module checks tensor devices, dtypes, shapes
+and contiguity, allocates outputs and workspace with torch (device memory is
+the only thing torch is used for, with the current stream), and calls the
+C ABI declared in ``include/gdr.h``.  Every step of the computation runs in
+the HIP kernels of ``libgdr.so``; there is no fallback.  If the library is not
+built, importing works but every call raises ``GdrNotBuilt``.
+
+Entry points (same names as the C ABI):
+  chunk_fwd(q, k, v, g, beta, ...)        -> (o, s_final)   chunked prefill
+  recurrent_step(q, k, v, g, beta, state) -> o              one decode step (state in place)
+  chunk_fwd_workspace_size(...)           -> bytes
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_workspace_size", "GdrError", "GdrNotBuilt",
+           "library_path", "abi_version", "load_library", "Desc"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libgdr.so")
+
+F32, BF16 = 0, 1
+DECAY_SCALAR, DECAY_PER_CHANNEL = 0, 1
+BETA_GIVEN, BETA_KACZMARZ = 0, 1
+ALGOS = {"auto": 0, "vector": 1, "matrix": 2}
+STATUS = {0: "GDR_OK", -1: "GDR_E_NULL", -2: "GDR_E_SHAPE", -3: "GDR_E_UNSUPPORTED", -4: "GDR_E_ALIGN",
+          -5: "GDR_E_WORKSPACE", -6: "GDR_E_HIP", -7: "GDR_E_ALIAS", -8: "GDR_E_MODE"}
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status})")
+
+
+class GdrNotBuilt(RuntimeError):
+    pass
+
+
+class Desc(ctypes.Structure):
+    """Mirror of ``gdr_desc`` in include/gdr.h."""
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("qkv_dtype", ctypes.c_int32), ("o_dtype", ctypes.c_int32),
+                ("decay_mode", ctypes.c_int32), ("beta_mode", ctypes.c_int32),
+                ("algo", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def load_library(path: str | None = None):
+    """Load libgdr.so (once) and declare its ABI."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or library_path
+    if not os.path.exists(p):
+        raise GdrNotBuilt(f"{p} is missing: build it with __graft_entry__.build() "
+                          f"(or python gated_delta_rule_26_amd/build.py)")
+    lib = ctypes.CDLL(p)
+    V = ctypes.c_void_p
+    D = ctypes.POINTER(Desc)
+    lib.gdr_abi_version.restype = ctypes.c_int
+    lib.gdr_status_string.restype = ctypes.c_char_p
+    lib.gdr_status_string.argtypes = [ctypes.c_int]
+    lib.gdr_chunk_fwd_workspace_size.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_chunk_fwd.restype = ctypes.c_int
+    lib.gdr_chunk_fwd.argtypes = [D, V, V, V, V, V, V, V, V, V, ctypes.c_size_t, V]
+    lib.gdr_chunk_fwd_stage.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_stage.argtypes = [ctypes.c_int, D, V, V, V, V, V, V, V, V, V, ctypes.c_size_t, V]
+    lib.gdr_recurrent_step.restype = ctypes.c_int
+    lib.gdr_recurrent_step.argtypes = [D, V, V, V, V, V, V, V, V]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return int(load_library().gdr_abi_version())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return F32
+    if t == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t}; use float32 or bfloat16")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(name, t, device, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def make_desc(B, T, H, Dk, Dv, *, qkv_dtype, o_dtype, per_channel=False, kaczmarz=False, eps=0.0,
+              scale=1.0, algo="auto", chunk=64) -> Desc:
+    return Desc(B=B, T=T, H=H, Dk=Dk, Dv=Dv, chunk=chunk, qkv_dtype=_dtype_code(qkv_dtype),
+                o_dtype=_dtype_code(o_dtype), decay_mode=DECAY_PER_CHANNEL if per_channel else DECAY_SCALAR,
+                beta_mode=BETA_KACZMARZ if kaczmarz else BETA_GIVEN, algo=ALGOS[algo], reserved=0,
+                eps=float(eps), scale=float(scale))
+
+
+def chunk_fwd_workspace_size(desc: Desc) -> int:
+    out = ctypes.c_size_t(0)
+    rc = load_library().gdr_chunk_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(out))
+    if rc != 0:
+        raise GdrError(rc, "gdr_chunk_fwd_workspace_size")
+    return int(out.value)
+
+
+def chunk_fwd(q, k, v, g, beta, *, per_channel: bool = False, kaczmarz: bool = False, eps: float = 0.0,
+              scale: float = 1.0, s0=None, output_final_state: bool = True, s_final=None, o=None,
+              o_dtype=None, algo: str = "auto", workspace=None, stream=None, stage=None):
+    """Chunked forward pass (prefill) through ``gdr_chunk_fwd``.
+
+    q, k [B,T,H,Dk] and v [B,T,H,Dv] in float32 or bfloat16; g float32
+    [B,T,H] (scalar decay) or [B,T,H,Dk] (``per_channel``); beta float32
+    [B,T,H] (eta when ``kaczmarz``); s0 float32 [B,H,Dk,Dv] or None.
+    ``s_final`` may be ``s0`` itself for an in-place state update.
+    Returns (o [B,T,H,Dv], s_final [B,H,Dk,Dv] or None).  The work is enqueued
+    on ``stream`` (default: torch's current stream of q's device).  ``stage``
+    (0 = intra kernel, 1 = state kernel) runs one kernel of the pipeline
+    through ``gdr_chunk_fwd_stage``; both stages must then share ``workspace``.
+    """
+    lib = load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _check_dev("q", q, dev)
+    _check_dev("k", k, dev, q.dtype, (B, T, H, Dk))
+    _check_dev("v", v, dev, q.dtype, (B, T, H, Dv))
+    _check_dev("g", g, dev, torch.float32, (B, T, H, Dk) if per_channel else (B, T, H))
+    _check_dev("beta", beta, dev, torch.float32, (B, T, H))
+    if s0 is not None:
+        _check_dev("s0", s0, dev, torch.float32, (B, H, Dk, Dv))
+    o_dtype = o_dtype or q.dtype
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=o_dtype, device=dev)
+    else:
+        _check_dev("o", o, dev, o_dtype, (B, T, H, Dv))
+    if s_final is None and output_final_state:
+        s_final = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    elif s_final is not None:
+        _check_dev("s_final", s_final, dev, torch.float32, (B, H, Dk, Dv))
+    desc = make_desc(B, T, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=o_dtype, per_channel=per_channel,
+                     kaczmarz=kaczmarz, eps=eps, scale=scale, algo=algo)
+    need = chunk_fwd_workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _check_dev("workspace", workspace, dev, torch.uint8)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(o),
+            _ptr(s_final), _ptr(workspace), workspace.numel(), ctypes.c_void_p(st.cuda_stream))
+    if stage is None:
+        rc = lib.gdr_chunk_fwd(*args)
+    else:
+        rc = lib.gdr_chunk_fwd_stage(int(stage), *args)
+    if rc != 0:
+        raise GdrError(rc, "gdr_chunk_fwd" if stage is None else "gdr_chunk_fwd_stage")
+    return o, s_final
+
+
+def recurrent_step(q, k, v, g, beta, state, *, per_channel: bool = False, kaczmarz: bool = False,
+                   eps: float = 0.0, scale: float = 1.0, o=None, o_dtype=None, stream=None):
+    """One fused decode step through ``gdr_recurrent_step``.
+
+    q, k [N,H,Dk], v [N,H,Dv] (float32 or bfloat16); g float32 [N,H] or
+    [N,H,Dk]; beta float32 [N,H]; state float32 [N,H,Dk,Dv], updated in
+    place.  Returns o [N,H,Dv].
+    """
+    lib = load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _check_dev("q", q, dev)
+    _check_dev("k", k, dev, q.dtype, (N, H, Dk))
+    _check_dev("v", v, dev, q.dtype, (N, H, Dv))
+    _check_dev("g", g, dev, torch.float32, (N, H, Dk) if per_channel else (N, H))
+    _check_dev("beta", beta, dev, torch.float32, (N, H))
+    _check_dev("state", state, dev, torch.float32, (N, H, Dk, Dv))
+    o_dtype = o_dtype or q.dtype
+    if o is None:
+        o = torch.empty((N, H, Dv), dtype=o_dtype, device=dev)
+    else:
+        _check_dev("o", o, dev, o_dtype, (N, H, Dv))
+    desc = make_desc(N, 1, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=o_dtype, per_channel=per_channel,
+                     kaczmarz=kaczmarz, eps=eps, scale=scale)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    rc = lib.gdr_recurrent_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                _ptr(state), _ptr(o), ctypes.c_void_p(st.cuda_stream))
+    if rc != 0:
+        raise GdrError(rc, "gdr_recurrent_step")
+    return o

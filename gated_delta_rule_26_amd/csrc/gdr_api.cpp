@@ -1,0 +1,255 @@
+// libgdr C ABI: argument validation (pure host code, before any HIP call)
+// and dispatch to the kernels.  See include/gdr.h for the contract.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "gdr_internal.h"
+
+namespace {
+
+using gdr::ChunkArgs;
+using gdr::StepArgs;
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+Range range_of(const void *p, size_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + bytes};
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// a*b*... with overflow detection (all factors >= 0)
+bool mul_ok(size_t &acc, size_t f) {
+    if (f != 0 && acc > SIZE_MAX / f) return false;
+    acc *= f;
+    return true;
+}
+
+struct Sizes {
+    size_t qk, v, g, beta, state, o;  // element counts
+};
+
+// Shared descriptor validation.  `step` selects the recurrent-step reading
+// (T = 1, no chunk constraint).
+int check_desc(const gdr_desc *d, bool step, Sizes *sz) {
+    if (!d) return GDR_E_NULL;
+    if (d->reserved != 0) return GDR_E_MODE;
+    if (d->qkv_dtype != GDR_F32 && d->qkv_dtype != GDR_BF16) return GDR_E_MODE;
+    if (d->o_dtype != GDR_F32 && d->o_dtype != GDR_BF16) return GDR_E_MODE;
+    if (d->decay_mode != GDR_DECAY_SCALAR && d->decay_mode != GDR_DECAY_PER_CHANNEL) return GDR_E_MODE;
+    if (d->beta_mode != GDR_BETA_GIVEN && d->beta_mode != GDR_BETA_KACZMARZ) return GDR_E_MODE;
+    if (d->algo != GDR_ALGO_AUTO && d->algo != GDR_ALGO_VECTOR && d->algo != GDR_ALGO_MATRIX) return GDR_E_MODE;
+    if (!std::isfinite(d->scale)) return GDR_E_MODE;
+    if (d->beta_mode == GDR_BETA_KACZMARZ && !(std::isfinite(d->eps) && d->eps >= 0.f)) return GDR_E_MODE;
+    const int T = step ? 1 : d->T;
+    if (d->B < 0 || d->H < 0 || T < 0 || d->Dk < 0 || d->Dv < 0) return GDR_E_SHAPE;
+    if (!(d->Dk == 64 || d->Dk == 128) || !(d->Dv == 64 || d->Dv == 128)) return GDR_E_UNSUPPORTED;
+    if (!step && d->chunk != gdr::kChunk) return GDR_E_UNSUPPORTED;
+    size_t tok = 1;  // B*T*H
+    if (!mul_ok(tok, (size_t)d->B) || !mul_ok(tok, (size_t)T) || !mul_ok(tok, (size_t)d->H)) return GDR_E_SHAPE;
+    size_t qk = tok, vv = tok, st = (size_t)d->B;
+    if (!mul_ok(qk, (size_t)d->Dk) || !mul_ok(vv, (size_t)d->Dv)) return GDR_E_SHAPE;
+    if (!mul_ok(st, (size_t)d->H) || !mul_ok(st, (size_t)d->Dk) || !mul_ok(st, (size_t)d->Dv)) return GDR_E_SHAPE;
+    // byte counts and 64-bit kernel offsets must fit comfortably
+    const size_t lim = (size_t)1 << 60;
+    if (qk > lim || vv > lim || st > lim) return GDR_E_SHAPE;
+    // grid-size limits of the launches (blocks per dimension < 2^31)
+    if ((size_t)d->B * d->H * 2 >= ((size_t)1 << 31)) return GDR_E_SHAPE;
+    if (sz) {
+        sz->qk = qk;
+        sz->v = vv;
+        sz->g = d->decay_mode == GDR_DECAY_PER_CHANNEL ? qk : tok;
+        sz->beta = tok;
+        sz->state = st;
+        sz->o = vv;
+    }
+    return GDR_OK;
+}
+
+int resolve_algo(const gdr_desc *d) {
+    if (d->algo == GDR_ALGO_AUTO) return d->qkv_dtype == GDR_BF16 ? GDR_ALGO_MATRIX : GDR_ALGO_VECTOR;
+    return d->algo;
+}
+
+// The matrix-core path is not built yet: every call goes to the vector path.
+bool matrix_path_available(const gdr_desc *d) {
+    (void)d;
+    return false;
+}
+
+int chunk_workspace(const gdr_desc *d, size_t *bytes) {
+    const int NC = (d->T + gdr::kChunk - 1) / gdr::kChunk;
+    // one workgroup per (sequence, head, chunk): the grid must stay below 2^31
+    if ((size_t)d->B * d->H * (size_t)NC >= ((size_t)1 << 31)) return GDR_E_SHAPE;
+    const bool pc = d->decay_mode == GDR_DECAY_PER_CHANNEL;
+    int algo = resolve_algo(d);
+    if (algo == GDR_ALGO_MATRIX && !matrix_path_available(d)) {
+        if (d->algo == GDR_ALGO_MATRIX) return GDR_E_UNSUPPORTED;
+        algo = GDR_ALGO_VECTOR;
+    }
+    *bytes = algo == GDR_ALGO_MATRIX ? gdr::chunk_matrix_workspace_bytes(d->B, d->H, NC, d->Dk, d->Dv, pc)
+                                     : gdr::chunk_vector_workspace_bytes(d->B, d->H, NC, d->Dk, d->Dv, pc);
+    return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr_abi_version(void) { return GDR_ABI_VERSION; }
+
+const char *gdr_status_string(int status) {
+    switch (status) {
+        case GDR_OK: return "GDR_OK: success (work enqueued)";
+        case GDR_E_NULL: return "GDR_E_NULL: a required pointer is NULL";
+        case GDR_E_SHAPE: return "GDR_E_SHAPE: negative size or element count overflow";
+        case GDR_E_UNSUPPORTED: return "GDR_E_UNSUPPORTED: unsupported Dk/Dv/chunk or algorithm";
+        case GDR_E_ALIGN: return "GDR_E_ALIGN: misaligned pointer";
+        case GDR_E_WORKSPACE: return "GDR_E_WORKSPACE: workspace missing or too small";
+        case GDR_E_HIP: return "GDR_E_HIP: a HIP launch failed";
+        case GDR_E_ALIAS: return "GDR_E_ALIAS: an output overlaps an input";
+        case GDR_E_MODE: return "GDR_E_MODE: bad mode, dtype, eps or scale";
+        default: return "unknown gdr status";
+    }
+}
+
+int gdr_chunk_fwd_workspace_size(const gdr_desc *desc, size_t *bytes) {
+    if (!bytes) return GDR_E_NULL;
+    Sizes sz;
+    const int rc = check_desc(desc, false, &sz);
+    if (rc != GDR_OK) return rc;
+    return chunk_workspace(desc, bytes);
+}
+
+}  // extern "C"
+
+namespace {
+
+// stage: -1 = the whole chunked pass, 0 = intra kernel, 1 = state kernel
+int chunk_fwd_impl(int stage, const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
+                   const float *beta_or_eta, const float *s0, void *o, float *s_final, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    Sizes sz;
+    int rc = check_desc(d, false, &sz);
+    if (rc != GDR_OK) return rc;
+    size_t need = 0;
+    rc = chunk_workspace(d, &need);
+    if (rc != GDR_OK) return rc;
+    if (d->B == 0 || d->H == 0) return GDR_OK;
+    const bool pc = d->decay_mode == GDR_DECAY_PER_CHANNEL;
+    const size_t in_es = d->qkv_dtype == GDR_BF16 ? 2 : 4;
+    const size_t out_es = d->o_dtype == GDR_BF16 ? 2 : 4;
+    const bool have_tokens = d->T > 0;
+
+    if (have_tokens) {
+        if (!q || !k || !v || !g || !beta_or_eta || !o) return GDR_E_NULL;
+        if (need > 0 && !workspace) return GDR_E_WORKSPACE;
+        if (workspace_bytes < need) return GDR_E_WORKSPACE;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return GDR_E_ALIGN;
+        if (!aligned(g, pc ? 16 : 4) || !aligned(beta_or_eta, 4)) return GDR_E_ALIGN;
+        if (workspace && !aligned(workspace, 16)) return GDR_E_ALIGN;
+    }
+    if (s0 && !aligned(s0, 16)) return GDR_E_ALIGN;
+    if (s_final && !aligned(s_final, 16)) return GDR_E_ALIGN;
+
+    const Range rq = range_of(q, sz.qk * in_es), rk = range_of(k, sz.qk * in_es), rv = range_of(v, sz.v * in_es);
+    const Range rg = range_of(g, sz.g * 4), rb = range_of(beta_or_eta, sz.beta * 4);
+    const Range ro = range_of(o, have_tokens ? sz.o * out_es : 0);
+    const Range rs0 = range_of(s0, s0 ? sz.state * 4 : 0);
+    const Range rsf = range_of(s_final, s_final ? sz.state * 4 : 0);
+    const Range rws = range_of(workspace, have_tokens ? need : 0);
+    const Range ins[] = {rq, rk, rv, rg, rb};
+    for (const Range &r : ins) {
+        if (have_tokens && (overlap(r, ro) || overlap(r, rws))) return GDR_E_ALIAS;
+        if (overlap(r, rsf)) return GDR_E_ALIAS;
+    }
+    if (overlap(ro, rsf) || overlap(ro, rws) || overlap(rsf, rws) || overlap(rs0, ro) || overlap(rs0, rws))
+        return GDR_E_ALIAS;
+    if (s0 && s_final && s0 != s_final && overlap(rs0, rsf)) return GDR_E_ALIAS;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!have_tokens) {
+        if (stage == 0 || !s_final || s_final == s0) return GDR_OK;
+        return gdr::launch_state_init(s_final, s0, sz.state, st) == hipSuccess ? GDR_OK : GDR_E_HIP;
+    }
+
+    ChunkArgs a;
+    a.B = d->B; a.T = d->T; a.H = d->H; a.Dk = d->Dk; a.Dv = d->Dv;
+    a.NC = (d->T + gdr::kChunk - 1) / gdr::kChunk;
+    a.qkv_bf16 = d->qkv_dtype == GDR_BF16;
+    a.o_bf16 = d->o_dtype == GDR_BF16;
+    a.per_channel = pc;
+    a.kaczmarz = d->beta_mode == GDR_BETA_KACZMARZ;
+    a.eps = a.kaczmarz ? d->eps : 0.f;
+    a.scale = d->scale;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta_or_eta;
+    a.s0 = s0; a.o = o; a.s_final = s_final;
+    a.ws = workspace;
+    a.stream = st;
+    int algo = resolve_algo(d);
+    if (algo == GDR_ALGO_MATRIX && !matrix_path_available(d)) algo = GDR_ALGO_VECTOR;
+    const hipError_t e =
+        algo == GDR_ALGO_MATRIX ? gdr::launch_chunk_matrix(a, stage) : gdr::launch_chunk_vector(a, stage);
+    return e == hipSuccess ? GDR_OK : GDR_E_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
+                  const float *beta_or_eta, const float *s0, void *o, float *s_final, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    return chunk_fwd_impl(-1, d, q, k, v, g, beta_or_eta, s0, o, s_final, workspace, workspace_bytes, stream);
+}
+
+int gdr_chunk_fwd_stage(int stage, const gdr_desc *d, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta_or_eta, const float *s0, void *o, float *s_final,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    if (stage != GDR_STAGE_INTRA && stage != GDR_STAGE_STATE) return GDR_E_MODE;
+    return chunk_fwd_impl(stage, d, q, k, v, g, beta_or_eta, s0, o, s_final, workspace, workspace_bytes,
+                          stream);
+}
+
+int gdr_recurrent_step(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
+                       const float *beta_or_eta, float *state, void *o, void *stream) {
+    Sizes sz;
+    const int rc = check_desc(d, true, &sz);
+    if (rc != GDR_OK) return rc;
+    if (d->B == 0 || d->H == 0) return GDR_OK;
+    if (!q || !k || !v || !g || !beta_or_eta || !state || !o) return GDR_E_NULL;
+    const bool pc = d->decay_mode == GDR_DECAY_PER_CHANNEL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(state, 16))
+        return GDR_E_ALIGN;
+    if (!aligned(g, pc ? 16 : 4) || !aligned(beta_or_eta, 4)) return GDR_E_ALIGN;
+    const size_t in_es = d->qkv_dtype == GDR_BF16 ? 2 : 4;
+    const size_t out_es = d->o_dtype == GDR_BF16 ? 2 : 4;
+    const Range rq = range_of(q, sz.qk * in_es), rk = range_of(k, sz.qk * in_es), rv = range_of(v, sz.v * in_es);
+    const Range rg = range_of(g, sz.g * 4), rb = range_of(beta_or_eta, sz.beta * 4);
+    const Range rs = range_of(state, sz.state * 4), ro = range_of(o, sz.o * out_es);
+    const Range ins[] = {rq, rk, rv, rg, rb};
+    for (const Range &r : ins)
+        if (overlap(r, rs) || overlap(r, ro)) return GDR_E_ALIAS;
+    if (overlap(rs, ro)) return GDR_E_ALIAS;
+
+    StepArgs a;
+    a.N = d->B; a.H = d->H; a.Dk = d->Dk; a.Dv = d->Dv;
+    a.qkv_bf16 = d->qkv_dtype == GDR_BF16;
+    a.o_bf16 = d->o_dtype == GDR_BF16;
+    a.per_channel = pc;
+    a.kaczmarz = d->beta_mode == GDR_BETA_KACZMARZ;
+    a.eps = a.kaczmarz ? d->eps : 0.f;
+    a.scale = d->scale;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta_or_eta;
+    a.state = state; a.o = o;
+    a.stream = static_cast<hipStream_t>(stream);
+    return gdr::launch_recurrent_step(a) == hipSuccess ? GDR_OK : GDR_E_HIP;
+}
+
+}  // extern "C"

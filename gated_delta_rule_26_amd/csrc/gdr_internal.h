@@ -1,0 +1,93 @@
+// Internal declarations shared by the libgdr sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gdr.h"
+
+namespace gdr {
+
+// Validated arguments of gdr_chunk_fwd, as the launchers see them.
+struct ChunkArgs {
+    int B, T, H, Dk, Dv;
+    int NC;                  // chunks per sequence, ceil(T / 64)
+    bool qkv_bf16, o_bf16, per_channel, kaczmarz;
+    float eps, scale;
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const float *s0;         // may be NULL (zero start)
+    void *o;
+    float *s_final;          // may be NULL
+    void *ws;
+    hipStream_t stream;
+};
+
+// Validated arguments of gdr_recurrent_step.
+struct StepArgs {
+    int N, H, Dk, Dv;
+    bool qkv_bf16, o_bf16, per_channel, kaczmarz;
+    float eps, scale;
+    const void *q, *k, *v;
+    const float *g, *beta;
+    float *state;
+    void *o;
+    hipStream_t stream;
+};
+
+constexpr int kChunk = 64;
+
+// Vector-ALU chunked path (fp32 arithmetic, any input dtype).
+size_t chunk_vector_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel);
+// stage: -1 = both kernels, 0 = intra kernel only, 1 = state kernel only
+hipError_t launch_chunk_vector(const ChunkArgs &a, int stage);
+
+// Matrix-core chunked path (bf16 MFMA with fp32 accumulation, bf16 inputs).
+size_t chunk_matrix_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel);
+hipError_t launch_chunk_matrix(const ChunkArgs &a, int stage);
+
+// T == 0: s_final = s0 (or zero).
+hipError_t launch_state_init(float *dst, const float *src, size_t n, hipStream_t stream);
+
+// Fused single-token recurrent step.
+hipError_t launch_recurrent_step(const StepArgs &a);
+
+}  // namespace gdr
+
+// ---------------------------------------------------------------- device helpers
+#if defined(__HIPCC__)
+namespace gdr {
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (quiet NaN kept).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_in(const void *p, size_t i) {
+    if constexpr (BF16) return bf16_bits_to_f32(static_cast<const uint16_t *>(p)[i]);
+    else return static_cast<const float *>(p)[i];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_out(void *p, size_t i, float x) {
+    if constexpr (BF16) static_cast<uint16_t *>(p)[i] = f32_to_bf16_bits(x);
+    else static_cast<float *>(p)[i] = x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+}  // namespace gdr
+#endif

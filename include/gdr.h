@@ -1,0 +1,188 @@
+/*
+ * gdr.h -- C ABI of libgdr, the MI355X (gfx950) gated delta-rule forward pass.
+ *
+ * The operation (one independent recurrence per sequence and head), with the
+ * state S a d_k x d_v fp32 matrix (row i = key channel i, d_v contiguous, the
+ * orientation of the Kaczmarz page, gist.science "Kaczmarz Linear Attention",
+ * section "Derivazione Teorica"):
+ *
+ *   S~  = D_t S_{t-1}         D_t = exp(g_t) I (Gated DeltaNet) or
+ *                             Diag(exp(g_t)) over key channels (KDA);
+ *                             blog summary on the DeltaNet family, sections
+ *                             "Gated DeltaNet" and "Kimi Delta Attention"; g is
+ *                             the stored log-decay, DPLR subsection
+ *   e_t = v_t - S~^T k_t      predict after the forget step (same sections)
+ *   S_t = S~ + beta_t k_t e_t^T
+ *   o_t = scale * S_t^T q_t   read after the write (the token sees its own
+ *                             write: blog summary, KDA step 5 and the chunked
+ *                             output subsection)
+ *
+ * with beta_t given, or the Kaczmarz step beta_t = eta_t / (||k_t||^2 + eps)
+ * (Kaczmarz page, "La Regola di Aggiornamento KLA").
+ *
+ * Two schedules of the same recurrence (blog summary, "Kernel Triton
+ * recurrente fusionado" and "Pipeline Triton por chunks"): a chunked prefill
+ * (gdr_chunk_fwd) and a fused single-token decode step (gdr_recurrent_step).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent) and
+ *    are owned by the caller.  The library allocates nothing, frees nothing,
+ *    never synchronises, and keeps no global state: it is reentrant.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  A
+ *    GDR_OK return means the work is ENQUEUED on that stream, not finished.
+ *  - Every argument is validated on the host before any HIP call.  A bad
+ *    argument returns a negative gdr_status synchronously and nothing is
+ *    enqueued.  A failed kernel launch returns GDR_E_HIP.  Nothing is printed.
+ *  - Values are not checked: g should be finite and <= 0, beta / eta finite and
+ *    >= 0 (beta is never clamped; the Kaczmarz beta exceeds 1 for short keys),
+ *    and keys are used as given (the caller normalises them if it wants to).
+ *  - Alignment: q, k, v, o, s0, s_final, state and workspace must be 16-byte
+ *    aligned; g and beta_or_eta 4-byte aligned (16-byte for per-channel g).
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDR_ABI_VERSION 1
+
+/* decay_mode */
+#define GDR_DECAY_SCALAR 0       /* g is [.., H]: one log-decay per token and head */
+#define GDR_DECAY_PER_CHANNEL 1  /* g is [.., H, Dk]: one log-decay per key channel */
+/* beta_mode */
+#define GDR_BETA_GIVEN 0         /* beta_or_eta holds beta_t */
+#define GDR_BETA_KACZMARZ 1      /* beta_or_eta holds eta_t; beta_t = eta_t / (||k_t||^2 + eps) */
+/* dtypes of q, k, v (qkv_dtype) and of o (o_dtype) */
+#define GDR_F32 0
+#define GDR_BF16 1
+/* algo: which kernels run the chunked path */
+#define GDR_ALGO_AUTO 0          /* bf16 q/k/v -> matrix-core kernels; fp32 -> vector kernels */
+#define GDR_ALGO_VECTOR 1        /* fp32 vector-ALU kernels (any dtype) */
+#define GDR_ALGO_MATRIX 2        /* bf16 MFMA kernels (bf16 q/k/v only) */
+
+typedef enum gdr_status {
+    GDR_OK = 0,
+    GDR_E_NULL = -1,         /* a required pointer is NULL */
+    GDR_E_SHAPE = -2,        /* a size is negative or the element count overflows */
+    GDR_E_UNSUPPORTED = -3,  /* Dk/Dv not in {64,128}, chunk != 64, algo not available */
+    GDR_E_ALIGN = -4,        /* a pointer is misaligned */
+    GDR_E_WORKSPACE = -5,    /* workspace missing or smaller than the queried size */
+    GDR_E_HIP = -6,          /* a HIP launch failed */
+    GDR_E_ALIAS = -7,        /* outputs overlap inputs (s_final == s0 exactly is allowed) */
+    GDR_E_MODE = -8          /* bad enum value, negative/non-finite eps, non-finite scale */
+} gdr_status;
+
+/* Problem descriptor.  All fields are plain integers / floats. */
+typedef struct gdr_desc {
+    int32_t B;           /* sequences (batch); for gdr_recurrent_step: N sequences */
+    int32_t T;           /* tokens per sequence; ignored by gdr_recurrent_step (= 1) */
+    int32_t H;           /* heads (q, k and v share H) */
+    int32_t Dk;          /* key width, 64 or 128 */
+    int32_t Dv;          /* value width, 64 or 128 */
+    int32_t chunk;       /* chunk length C of the chunked path, must be 64 */
+    int32_t qkv_dtype;   /* GDR_F32 or GDR_BF16 */
+    int32_t o_dtype;     /* GDR_F32 or GDR_BF16 */
+    int32_t decay_mode;  /* GDR_DECAY_* */
+    int32_t beta_mode;   /* GDR_BETA_* */
+    int32_t algo;        /* GDR_ALGO_*; gdr_recurrent_step ignores it */
+    int32_t reserved;    /* must be 0 */
+    float eps;           /* Kaczmarz stabiliser (>= 0); ignored for GDR_BETA_GIVEN */
+    float scale;         /* output scale; 1 = the plain read, 1/sqrt(Dk) = KDA's read */
+} gdr_desc;
+
+/* Version of this ABI (GDR_ABI_VERSION). */
+int gdr_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *gdr_status_string(int status);
+
+/*
+ * Bytes of device workspace gdr_chunk_fwd needs for `desc`, written to *bytes.
+ * Host-only; returns a gdr_status (the same validation of desc as
+ * gdr_chunk_fwd, pointers aside).
+ */
+int gdr_chunk_fwd_workspace_size(const gdr_desc *desc, size_t *bytes);
+
+/*
+ * Chunked forward pass over whole sequences (prefill).
+ *
+ * The chunked algebra is the blog summary's section "KDA por chunks": within
+ * a chunk of C tokens the corrected writes solve a unit lower-triangular
+ * system (I + R) E = Ebar, one per value channel; the chunk-end state is
+ * S_{c+1} = D_{0:C-1} S_c + (K^end)^T E; the in-chunk outputs add a causal
+ * read matrix (diagonal included) to the read of the entering state.  The
+ * Kaczmarz page states that only the diagonal beta matrix changes for KLA.
+ *
+ *   q, k        [B, T, H, Dk]  qkv_dtype, contiguous
+ *   v           [B, T, H, Dv]  qkv_dtype, contiguous
+ *   g           [B, T, H] (scalar decay) or [B, T, H, Dk] (per channel), fp32
+ *   beta_or_eta [B, T, H] fp32
+ *   s0          [B, H, Dk, Dv] fp32 initial state, or NULL for zero
+ *   o           [B, T, H, Dv]  o_dtype (written)
+ *   s_final     [B, H, Dk, Dv] fp32 final state (written), or NULL; may be
+ *               the same pointer as s0 (in-place state update)
+ *   workspace   device scratch of at least gdr_chunk_fwd_workspace_size bytes;
+ *               its contents on entry do not matter and are clobbered
+ * T may be any value >= 0 (the last chunk may be partial); with T == 0 only
+ * s_final is written (s0, or zero).  B == 0 or H == 0 is a no-op.
+ * q, k, v, g and beta_or_eta must not overlap o, s_final or workspace.
+ */
+int gdr_chunk_fwd(const gdr_desc *desc,
+                  const void *q, const void *k, const void *v,
+                  const float *g, const float *beta_or_eta,
+                  const float *s0, void *o, float *s_final,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One stage of gdr_chunk_fwd, with the same arguments.  The chunked path is a
+ * pipeline of two kernels (blog summary, "Pipeline Triton por chunks": an
+ * intra-chunk kernel builds the in-chunk interaction matrices and the WY-like
+ * form of the corrected writes; the state kernel is the only walk across
+ * chunks and produces the outputs):
+ *   stage 0 (GDR_STAGE_INTRA): every chunk in parallel; reads q, k, v, g,
+ *            beta_or_eta and writes the workspace only.
+ *   stage 1 (GDR_STAGE_STATE): walks the chunks of each sequence in order;
+ *            reads q, k, v, g, beta_or_eta, s0 and the workspace written by
+ *            stage 0 with the same arguments, and writes o and s_final.
+ * Stage 0 followed by stage 1 on one stream is exactly gdr_chunk_fwd.  The
+ * split exists so that callers (profilers, benchmarks) can time each kernel;
+ * validation is identical to gdr_chunk_fwd.
+ */
+#define GDR_STAGE_INTRA 0
+#define GDR_STAGE_STATE 1
+int gdr_chunk_fwd_stage(int stage, const gdr_desc *desc,
+                        const void *q, const void *k, const void *v,
+                        const float *g, const float *beta_or_eta,
+                        const float *s0, void *o, float *s_final,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One fused recurrent step for B = N independent sequences (decode): the
+ * seven steps above for a single token, with the state read once and written
+ * once (blog summary, "Kernel Triton recurrente fusionado": decay, predict,
+ * residual, rank-1 write and read fused in one pass).
+ *
+ *   q, k        [N, H, Dk]  qkv_dtype
+ *   v           [N, H, Dv]  qkv_dtype
+ *   g           [N, H] or [N, H, Dk] fp32
+ *   beta_or_eta [N, H] fp32
+ *   state       [N, H, Dk, Dv] fp32, read and updated in place
+ *   o           [N, H, Dv] o_dtype (written)
+ * desc->T and desc->chunk are ignored.  q, k, v, g, beta_or_eta must not
+ * overlap state or o.
+ */
+int gdr_recurrent_step(const gdr_desc *desc,
+                       const void *q, const void *k, const void *v,
+                       const float *g, const float *beta_or_eta,
+                       float *state, void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

@@ -1,0 +1,144 @@
+"""libgdr on a host without a GPU: the library loads, exports every function
+include/gdr.h declares, and its host-side validation rejects bad arguments
+with the documented status codes before any HIP call.  No call here passes
+validation, so nothing is ever launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_26_amd as gdr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(gdr.library_path), reason="libgdr.so not built")
+
+E = {name: code for code, name in gdr.STATUS.items()}
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = gdr.load_library()
+    names = declared_functions()
+    assert names == sorted(["gdr_abi_version", "gdr_status_string", "gdr_chunk_fwd_workspace_size",
+                            "gdr_chunk_fwd", "gdr_chunk_fwd_stage", "gdr_recurrent_step"])
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_desc_layout_matches_header():
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct gdr_desc"):text.index("} gdr_desc;")]
+    fields = re.findall(r"(int32_t|float)\s+(\w+);", body)
+    assert [f for _, f in fields] == [f for f, _ in gdr.Desc._fields_]
+    assert ctypes.sizeof(gdr.Desc) == 4 * len(fields)
+
+
+def test_version_and_strings():
+    lib = gdr.load_library()
+    assert lib.gdr_abi_version() == 1
+    for code in gdr.STATUS:
+        assert lib.gdr_status_string(code).decode().startswith(gdr.STATUS[code])
+
+
+def _desc(**kw):
+    base = dict(B=2, T=100, H=3, Dk=128, Dv=128, qkv_dtype=__import__("torch").bfloat16,
+                o_dtype=__import__("torch").float32)
+    base.update(kw)
+    return gdr.make_desc(**base)
+
+
+def _ws(desc):
+    n = ctypes.c_size_t(0)
+    rc = gdr.load_library().gdr_chunk_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_size_query():
+    rc, n = _ws(_desc())
+    assert rc == 0 and n > 0
+    rc2, n2 = _ws(_desc(T=200))
+    assert rc2 == 0 and n2 > n
+    assert _ws(_desc(Dk=96))[0] == E["GDR_E_UNSUPPORTED"]
+    assert _ws(_desc(chunk=32))[0] == E["GDR_E_UNSUPPORTED"]
+    assert _ws(_desc(B=-1))[0] == E["GDR_E_SHAPE"]
+    d = _desc()
+    d.reserved = 1
+    assert _ws(d)[0] == E["GDR_E_MODE"]
+    d = _desc()
+    d.decay_mode = 7
+    assert _ws(d)[0] == E["GDR_E_MODE"]
+    d = _desc(kaczmarz=True, eps=-1.0)
+    assert _ws(d)[0] == E["GDR_E_MODE"]
+    d = _desc(scale=float("inf"))
+    assert _ws(d)[0] == E["GDR_E_MODE"]
+    # huge problems are rejected, not overflowed
+    assert _ws(_desc(B=2 ** 30, T=2 ** 30, H=2 ** 10))[0] == E["GDR_E_SHAPE"]
+    lib = gdr.load_library()
+    assert lib.gdr_chunk_fwd_workspace_size(None, ctypes.byref(ctypes.c_size_t())) == E["GDR_E_NULL"]
+
+
+# Fake, well-separated "device" addresses: these calls never reach a launch.
+BASE = 1 << 40
+def P(i, off=0):
+    return ctypes.c_void_p(BASE + i * (1 << 32) + off)
+
+
+def _call_chunk(desc, q=P(1), k=P(2), v=P(3), g=P(4), b=P(5), s0=None, o=P(6), sf=P(7), ws=P(8), wsb=None):
+    if wsb is None:
+        wsb = _ws(desc)[1]
+    return gdr.load_library().gdr_chunk_fwd(ctypes.byref(desc), q, k, v, g, b, s0, o, sf, ws, wsb, None)
+
+
+def test_chunk_validation_errors():
+    d = _desc()
+    assert _call_chunk(d, q=None) == E["GDR_E_NULL"]
+    assert _call_chunk(d, o=None) == E["GDR_E_NULL"]
+    assert _call_chunk(d, ws=None) == E["GDR_E_WORKSPACE"]
+    assert _call_chunk(d, wsb=_ws(d)[1] - 1) == E["GDR_E_WORKSPACE"]
+    assert _call_chunk(d, q=P(1, 8)) == E["GDR_E_ALIGN"]
+    assert _call_chunk(d, g=P(4, 2)) == E["GDR_E_ALIGN"]
+    assert _call_chunk(_desc(per_channel=True), g=P(4, 4)) == E["GDR_E_ALIGN"]
+    assert _call_chunk(d, o=P(1)) == E["GDR_E_ALIAS"]            # o on top of q
+    assert _call_chunk(d, sf=P(6, 1024)) == E["GDR_E_ALIAS"]    # s_final inside o
+    assert _call_chunk(d, ws=P(2, 4096)) == E["GDR_E_ALIAS"]    # workspace inside k
+    assert _call_chunk(d, s0=P(9), sf=P(9, 16)) == E["GDR_E_ALIAS"]  # partial s0/s_final overlap
+    assert _call_chunk(_desc(Dv=80)) == E["GDR_E_UNSUPPORTED"]
+    assert gdr.load_library().gdr_chunk_fwd(None, P(1), P(2), P(3), P(4), P(5), None, P(6), P(7), P(8), 0,
+                                            None) == E["GDR_E_NULL"]
+    lib = gdr.load_library()
+    wsb = _ws(d)[1]
+    assert lib.gdr_chunk_fwd_stage(2, ctypes.byref(d), P(1), P(2), P(3), P(4), P(5), None, P(6), P(7), P(8),
+                                   wsb, None) == E["GDR_E_MODE"]
+    assert lib.gdr_chunk_fwd_stage(0, ctypes.byref(d), None, P(2), P(3), P(4), P(5), None, P(6), P(7), P(8),
+                                   wsb, None) == E["GDR_E_NULL"]
+
+
+def test_matrix_algo_rejects_fp32_inputs():
+    d = _desc(qkv_dtype=__import__("torch").float32, algo="matrix")
+    assert _ws(d)[0] == E["GDR_E_UNSUPPORTED"]
+
+
+def test_step_validation_errors():
+    lib = gdr.load_library()
+    d = _desc(T=1)
+
+    def call(q=P(1), k=P(2), v=P(3), g=P(4), b=P(5), s=P(6), o=P(7), desc=d):
+        return lib.gdr_recurrent_step(ctypes.byref(desc), q, k, v, g, b, s, o, None)
+
+    assert call(q=None) == E["GDR_E_NULL"]
+    assert call(s=None) == E["GDR_E_NULL"]
+    assert call(s=P(6, 4)) == E["GDR_E_ALIGN"]
+    assert call(o=P(6, 64)) == E["GDR_E_ALIAS"]
+    assert call(s=P(2)) == E["GDR_E_ALIAS"]
+    assert call(desc=_desc(Dk=32)) == E["GDR_E_UNSUPPORTED"]
+    bad = _desc()
+    bad.o_dtype = 5
+    assert call(desc=bad) == E["GDR_E_MODE"]

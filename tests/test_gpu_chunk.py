@@ -1,0 +1,204 @@
+"""Chunked prefill on the GPU against the fp64 oracle: modes, dtypes, widths,
+ragged tails, edge cases, and the full benchmark workloads (sampled heads)."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_26_amd as gdr
+import oracle
+from gdr_inputs import WORKLOADS, prefill_inputs, random_inputs
+from tests.gpu_util import DEV, TOL, host, rel, to_dev
+
+pytestmark = pytest.mark.gpu
+
+MODES = {"gdn": dict(per_channel=False, kaczmarz=False),
+         "kda": dict(per_channel=True, kaczmarz=False),
+         "kla": dict(per_channel=False, kaczmarz=True)}
+ALGOS = ["vector"]
+
+
+def _inputs(seed, B, T, H, Dk, Dv, mode, dtype, with_s0=True, **kw):
+    m = MODES[mode]
+    return random_inputs(seed, B, T, H, Dk, Dv, dtype=dtype, per_channel=m["per_channel"],
+                         kaczmarz=m["kaczmarz"], key_norm="lognormal_norm" if m["kaczmarz"] else "unit",
+                         with_s0=with_s0, **kw)
+
+
+def _gpu(x, mode, dtype, *, algo="vector", o_dtype=torch.float32, scale=1.0, eps=1e-6, s_final=None):
+    m = MODES[mode]
+    d = to_dev(x, dtype)
+    o, s = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], s0=d["s0"], o_dtype=o_dtype,
+                         scale=scale, eps=eps if m["kaczmarz"] else 0.0, algo=algo, s_final=s_final, **m)
+    torch.cuda.synchronize()
+    return o, s
+
+
+def _ref(x, mode, scale=1.0, eps=1e-6, heads=None):
+    m = MODES[mode]
+    return oracle.oracle_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], s0=x["s0"], scale=scale,
+                             eps=eps if m["kaczmarz"] else 0.0, heads=heads, **m)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("T", [1, 63, 64, 200])
+@pytest.mark.parametrize("mode", ["gdn", "kda", "kla"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [(128, 128), (64, 64)])
+def test_chunk_parity(algo, T, mode, dtype, D):
+    x = _inputs(1000 + T, 2, T, 3, D[0], D[1], mode, dtype, with_s0=(T % 2 == 0))
+    o, s = _gpu(x, mode, dtype, algo=algo)
+    o_ref, s_ref = _ref(x, mode)
+    eo, es = rel(host(o), o_ref), rel(host(s), s_ref)
+    print(f"chunk {algo} {mode} {dtype} T={T} D={D}: rel o {eo:.2e} S {es:.2e}")
+    assert eo < TOL[dtype] and es < TOL[dtype]
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("D", [(128, 64), (64, 128)])
+def test_chunk_mixed_widths(algo, D):
+    x = _inputs(7, 1, 150, 2, D[0], D[1], "kda", "bf16")
+    o, s = _gpu(x, "kda", "bf16", algo=algo)
+    o_ref, s_ref = _ref(x, "kda")
+    assert rel(host(o), o_ref) < TOL["bf16"] and rel(host(s), s_ref) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_bf16_output_and_scale(algo):
+    x = _inputs(8, 2, 130, 2, 128, 128, "gdn", "bf16")
+    sc = 128 ** -0.5
+    o, s = _gpu(x, "gdn", "bf16", algo=algo, o_dtype=torch.bfloat16, scale=sc)
+    o_ref, s_ref = _ref(x, "gdn", scale=sc)
+    eo = rel(host(o), o_ref)
+    print(f"bf16 output: rel o {eo:.2e}")
+    assert eo < TOL["bf16"] and rel(host(s), s_ref) < TOL["bf16"]
+
+
+def test_empty_and_zero_length():
+    x = _inputs(9, 2, 0, 2, 64, 64, "gdn", "bf16")
+    o, s = _gpu(x, "gdn", "bf16")
+    assert o.shape == (2, 0, 2, 64)
+    np.testing.assert_array_equal(host(s), x["s0"])
+    x["s0"] = None
+    o, s = _gpu(x, "gdn", "bf16")
+    assert not host(s).any()
+    # B = 0 is a no-op
+    x = _inputs(9, 1, 10, 1, 64, 64, "gdn", "bf16")
+    d = to_dev(x, "bf16")
+    o, s = gdr.chunk_fwd(d["q"][:0], d["k"][:0], d["v"][:0], d["g"][:0], d["beta"][:0])
+    assert o.shape[0] == 0 and s.shape[0] == 0
+
+
+def test_in_place_state_and_resume():
+    x = _inputs(10, 2, 200, 2, 128, 128, "kla", "bf16")
+    o_full, s_full = _gpu(x, "kla", "bf16")
+    d = to_dev(x, "bf16")
+    state = d["s0"].clone()
+    outs = []
+    for t0, t1 in [(0, 130), (130, 131), (131, 200)]:   # split mid-chunk, and a single token
+        sl = {key: (d[key][:, t0:t1].contiguous() if key != "s0" else None) for key in d}
+        o, _ = gdr.chunk_fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], s0=state, s_final=state,
+                             o_dtype=torch.float32, kaczmarz=True, eps=1e-6)
+        outs.append(o)
+    torch.cuda.synchronize()
+    o_split = torch.cat(outs, dim=1)
+    assert rel(host(o_split), host(o_full)) < 1e-5
+    assert rel(host(state), host(s_full)) < 1e-5
+
+
+def test_prefill_then_decode_step():
+    x = _inputs(11, 2, 129, 3, 128, 128, "gdn", "bf16")
+    d = to_dev(x, "bf16")
+    T = 129
+    cut = {key: (d[key][:, :T - 1].contiguous() if key != "s0" else d[key]) for key in d}
+    _, s = gdr.chunk_fwd(cut["q"], cut["k"], cut["v"], cut["g"], cut["beta"], s0=cut["s0"],
+                         o_dtype=torch.float32)
+    last = {key: d[key][:, T - 1].contiguous() for key in ("q", "k", "v", "g", "beta")}
+    o_last = gdr.recurrent_step(last["q"], last["k"], last["v"], last["g"], last["beta"], s,
+                                o_dtype=torch.float32)
+    o_full, s_full = _gpu(x, "gdn", "bf16")
+    assert rel(host(o_last), host(o_full[:, T - 1])) < 1e-5
+    assert rel(host(s), host(s_full)) < 1e-5
+
+
+@pytest.mark.parametrize("mode", ["gdn", "kda"])
+def test_beta_zero_and_one(mode):
+    x = _inputs(12, 1, 100, 2, 64, 64, mode, "bf16")
+    x["beta"] = np.zeros_like(x["beta"])
+    o, s = _gpu(x, mode, "bf16")
+    o_ref, s_ref = _ref(x, mode)
+    assert rel(host(s), s_ref) < 1e-5 and rel(host(o), o_ref) < 1e-5
+    x["beta"] = np.ones_like(x["beta"])
+    o, s = _gpu(x, mode, "bf16")
+    o_ref, s_ref = _ref(x, mode)
+    assert rel(host(s), s_ref) < TOL["bf16"] and rel(host(o), o_ref) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("mode", ["gdn", "kda"])
+def test_strong_decay(mode):
+    x = _inputs(13, 1, 150, 2, 128, 128, mode, "bf16")
+    x["g"] = np.full_like(x["g"], -5.0)
+    o, s = _gpu(x, mode, "bf16")
+    o_ref, s_ref = _ref(x, mode)
+    assert np.isfinite(host(o)).all()
+    assert rel(host(o), o_ref) < TOL["bf16"] and rel(host(s), s_ref) < TOL["bf16"]
+
+
+def test_per_channel_with_uniform_gate_equals_scalar():
+    x = _inputs(14, 1, 150, 2, 128, 128, "gdn", "bf16")
+    o1, s1 = _gpu(x, "gdn", "bf16")
+    xp = dict(x)
+    xp["g"] = np.repeat(x["g"][..., None], 128, axis=-1)
+    o2, s2 = _gpu(xp, "kda", "bf16")
+    assert rel(host(o2), host(o1)) < 1e-5 and rel(host(s2), host(s1)) < 1e-5
+
+
+def test_deterministic_and_workspace_poison_does_not_leak():
+    x = _inputs(15, 2, 190, 2, 128, 128, "kda", "bf16")
+    d = to_dev(x, "bf16")
+    desc = gdr.make_desc(2, 190, 2, 128, 128, qkv_dtype=torch.bfloat16, o_dtype=torch.float32,
+                         per_channel=True)
+    ws = torch.empty(gdr.chunk_fwd_workspace_size(desc), dtype=torch.uint8, device=DEV)
+    runs = []
+    for fill in (0.0, float("nan")):
+        ws.view(torch.float32)[: ws.numel() // 4].fill_(fill) if ws.numel() >= 4 else None
+        o, s = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], s0=d["s0"], per_channel=True,
+                             o_dtype=torch.float32, workspace=ws, algo="vector")
+        torch.cuda.synchronize()
+        runs.append((o.clone(), s.clone()))
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
+
+
+# ------------------------------------------------------------ full workloads
+FULL = {
+    "gdn_tiny": dict(mode="gdn", heads=None),
+    "gdn_prefill": dict(mode="gdn", heads=8),
+    "kda_prefill": dict(mode="kda", heads=8),
+    "kla_prefill": dict(mode="kla", heads=2),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_workload_sampled(name):
+    """Each prefill benchmark workload at full size, in the launch
+    configuration the benchmark times (auto algorithm, fp32 output), checked
+    on sampled (batch, head) pairs against the oracle."""
+    w = WORKLOADS[name]
+    spec = FULL[name]
+    print(f"full workload {name}: generating inputs", flush=True)
+    x = prefill_inputs(w)
+    d = to_dev(x, w.dtype)
+    m = MODES[spec["mode"]]
+    o, s = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], o_dtype=torch.float32,
+                         eps=w.eps, **m)
+    torch.cuda.synchronize()
+    nbh = w.B * w.H
+    heads = np.arange(nbh) if spec["heads"] is None else \
+        np.sort(np.random.default_rng(1).choice(nbh, spec["heads"], replace=False))
+    print(f"full workload {name}: oracle on {len(heads)} heads", flush=True)
+    o_ref, s_ref = oracle.oracle_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], eps=w.eps, heads=heads, **m)
+    hb, hh = heads // w.H, heads % w.H
+    o_g = o[torch.from_numpy(hb).to(DEV), :, torch.from_numpy(hh).to(DEV)].cpu().numpy()
+    s_g = s[torch.from_numpy(hb).to(DEV), torch.from_numpy(hh).to(DEV)].cpu().numpy()
+    eo, es = rel(o_g, o_ref[hb, :, hh]), rel(s_g, s_ref[hb, hh])
+    print(f"full workload {name}: rel o {eo:.2e} S {es:.2e}")
+    assert eo < TOL[w.dtype] and es < TOL[w.dtype]

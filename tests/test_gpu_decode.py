@@ -1,0 +1,86 @@
+"""Fused recurrent decode step on the GPU against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_26_amd as gdr
+import oracle
+from gdr_inputs import WORKLOADS, decode_state0, decode_step_inputs
+from tests.gpu_util import DEV, TOL, host, rel, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, steps, *, o_dtype=torch.float32, scale=1.0, kaczmarz=False):
+    s0 = decode_state0(w)
+    state = torch.from_numpy(s0).to(DEV)
+    inputs, outs = [], []
+    for t in range(steps):
+        x = decode_step_inputs(w, t)
+        if kaczmarz:
+            x["beta"] = (x["beta"] * 1.5).astype(np.float32)   # eta
+        inputs.append(x)
+        d = to_dev(x, w.dtype)
+        o = gdr.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, per_channel=w.per_channel,
+                               kaczmarz=kaczmarz, eps=1e-6 if kaczmarz else 0.0, scale=scale, o_dtype=o_dtype)
+        outs.append(host(o))
+    torch.cuda.synchronize()
+    st = {key: np.stack([x[key] for x in inputs]) for key in inputs[0]}
+    o_ref, s_ref = oracle.oracle_decode(st["q"], st["k"], st["v"], st["g"], st["beta"], s0,
+                                        per_channel=w.per_channel, kaczmarz=kaczmarz,
+                                        eps=1e-6 if kaczmarz else 0.0, scale=scale)
+    return np.stack(outs), host(state), o_ref, s_ref
+
+
+@pytest.mark.parametrize("D", [(128, 128), (64, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("mode", ["gdn", "kda", "kla"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_parity(D, mode, dtype):
+    w = WORKLOADS["decode"].scaled(B=5, H=3, Dk=D[0], Dv=D[1], dtype=dtype,
+                                   decay="per_channel" if mode == "kda" else "scalar")
+    o, s, o_ref, s_ref = _run(w, 12, kaczmarz=mode == "kla")
+    eo, es = rel(o, o_ref), rel(s, s_ref)
+    print(f"decode {mode} {dtype} D={D}: rel o {eo:.2e} S {es:.2e}")
+    assert eo < TOL[dtype] and es < TOL[dtype]
+    assert eo < 1e-5 and es < 1e-5          # fp32 arithmetic on exact inputs
+
+
+def test_decode_bf16_output_and_scale():
+    w = WORKLOADS["decode"].scaled(B=4, H=2)
+    o, s, o_ref, s_ref = _run(w, 6, o_dtype=torch.bfloat16, scale=128 ** -0.5)
+    assert rel(o, o_ref) < TOL["bf16"] and rel(s, s_ref) < 1e-5
+
+
+def test_decode_full_workload_sampled():
+    """256 sequences x 16 heads, d128, 1000 steps (the decode benchmark
+    workload), checked on 48 sampled (sequence, head) states."""
+    w = WORKLOADS["decode"]
+    steps = w.steps
+    rng = np.random.default_rng(0)
+    heads = np.sort(rng.choice(w.B * w.H, 48, replace=False))
+    hb, hh = heads // w.H, heads % w.H
+    s0 = decode_state0(w)
+    state = torch.from_numpy(s0).to(DEV)
+    o_dev = torch.empty((w.B, w.H, w.Dv), dtype=torch.float32, device=DEV)
+    keep = {key: [] for key in ("q", "k", "v", "g", "beta")}
+    outs = []
+    idx_b = torch.from_numpy(hb).to(DEV)
+    idx_h = torch.from_numpy(hh).to(DEV)
+    for t in range(steps):
+        x = decode_step_inputs(w, t)
+        for key in keep:
+            keep[key].append(x[key][hb, hh])
+        d = to_dev(x, w.dtype)
+        gdr.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, o=o_dev, o_dtype=torch.float32)
+        outs.append(o_dev[idx_b, idx_h].clone())
+        if t % 250 == 0:
+            print(f"decode full workload: step {t}", flush=True)
+    torch.cuda.synchronize()
+    o = torch.stack(outs).cpu().numpy()                      # [steps, n, Dv]
+    s = state[idx_b, idx_h].cpu().numpy()
+    st = {key: np.stack(val)[:, :, None] for key, val in keep.items()}   # [steps, n, 1, ...]
+    o_ref, s_ref = oracle.oracle_decode(st["q"], st["k"], st["v"], st["g"], st["beta"],
+                                        s0[hb, hh][:, None])
+    eo, es = rel(o, o_ref[:, :, 0]), rel(s, s_ref[:, 0])
+    print(f"decode full workload (48 sampled states): rel o {eo:.2e} S {es:.2e}")
+    assert eo < TOL["bf16"] and es < TOL["bf16"]
