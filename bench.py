@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated delta-rule forward pass on one MI355X.
+
+A step is one chunked prefill over the Gated DeltaNet workload (B4 H16 T4096,
+d_k = d_v = 128, bf16 q/k/v, fp32 state, chunk 64): the intra-chunk kernel
+then the state/output kernel, with inputs resident in HBM.  The fused decode
+step is timed beside it on the decode workload (256 sequences x 16 heads,
+d128, fp32 state updated in place).  Kernel times come from HIP events
+recorded on the stream the kernels are launched on (torch's current stream).
+
+Prints ONE JSON line.  ``--gpus`` above 1 is refused: this build runs on one
+GPU (the path shards over (sequence, head) pairs with no communication).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+C = 64
+PEAK_BF16_MFMA = 2500.0      # TFLOP/s, MI355X dense bf16
+PEAK_FP32_VALU = 157.3       # TFLOP/s, MI355X fp32 vector
+PEAK_HBM = 8000.0            # GB/s, MI355X HBM3E
+
+
+def alg_flops_per_token_head(dk: int, dv: int) -> dict:
+    """Algorithmic (triangle-aware) flops per token and head, by kernel.
+
+    intra: R = beta.decay-weighted K K^T strictly below the diagonal
+    ((C-1) dk), the causal read matrix A (diagonal kept, (C+1) dk), the
+    triangular inverse (C^2/3) and W, U ((C+1)(dk + dv)).
+    state: E = U - W S, the read (decayed Q) S and the update K^T E
+    (2 dk dv each) plus the in-chunk read A E ((C+1) dv).
+    """
+    intra = (C - 1) * dk + (C + 1) * dk + C * C / 3.0 + (C + 1) * dk + (C + 1) * dv
+    state = 6.0 * dk * dv + (C + 1) * dv
+    return {"intra": intra, "state": state, "total": intra + state}
+
+
+def alg_bytes_prefill(B, T, H, dk, dv, in_bytes=2, out_bytes=4, per_channel=False) -> float:
+    """Minimal HBM bytes of one chunked pass: read q, k, v, g, beta once,
+    write o and the final state once."""
+    tok = B * T * H
+    g_bytes = 4 * (dk if per_channel else 1)
+    return tok * ((2 * dk + dv) * in_bytes + g_bytes + 4 + dv * out_bytes) + B * H * dk * dv * 4
+
+
+def decode_bytes_per_step(N, H, dk, dv, in_bytes=2, out_bytes=4) -> float:
+    """Minimal HBM bytes of one decode step: the state in and out, plus the
+    token's q, k, v, g, beta and the output."""
+    return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * in_bytes + 8 + dv * out_bytes)
+
+
+def cpu_baseline(w, x, heads=None):
+    """The fp64 oracle, as it stands, on the same prefill inputs."""
+    import oracle
+    threads = oracle.max_threads()
+    nbh = w.B * w.H
+    heads = list(range(nbh)) if heads is None else heads
+    t0 = time.perf_counter()
+    oracle.oracle_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], per_channel=w.per_channel,
+                      kaczmarz=w.kaczmarz, eps=w.eps, heads=heads, threads=threads)
+    dt = time.perf_counter() - t0
+    tok_heads = len(heads) * w.T
+    return {"value": tok_heads / w.H / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{w.name}: {len(heads)} of {nbh} (batch, head) pairs, all {w.T} tokens each, fp64 "
+                      f"token recurrence; {dt:.2f} s wall; tokens/s counts all {w.H} heads of a token",
+            "seconds": dt, "cpu": platform.processor() or platform.machine()}
+
+
+def bench_prefill(w, steps, warmup, algo, o_dtype):
+    import torch
+    import gated_delta_rule_26_amd as gdr
+    from gdr_inputs import prefill_inputs
+
+    dev = torch.device("cuda:0")
+    x = prefill_inputs(w)
+    d = {}
+    for key, val in x.items():
+        if val is None:
+            continue
+        t = torch.from_numpy(val).to(dev)
+        d[key] = t.to(torch.bfloat16) if key in ("q", "k", "v") and w.dtype == "bf16" else t
+    B, T, H, Dk, Dv = w.B, w.T, w.H, w.Dk, w.Dv
+    odt = torch.float32 if o_dtype == "f32" else torch.bfloat16
+    qdt = d["q"].dtype
+    o = torch.empty((B, T, H, Dv), dtype=odt, device=dev)
+    s = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    desc = gdr.make_desc(B, T, H, Dk, Dv, qkv_dtype=qdt, o_dtype=odt, per_channel=w.per_channel,
+                         kaczmarz=w.kaczmarz, eps=w.eps, algo=algo)
+    ws = torch.empty(max(1, gdr.chunk_fwd_workspace_size(desc)), dtype=torch.uint8, device=dev)
+    kw = dict(per_channel=w.per_channel, kaczmarz=w.kaczmarz, eps=w.eps, o=o, s_final=s, o_dtype=odt,
+              algo=algo, workspace=ws)
+
+    def step(events=None):
+        if events is not None:
+            events[0].record()
+        gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], stage=0, **kw)
+        if events is not None:
+            events[1].record()
+        gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], stage=1, **kw)
+        if events is not None:
+            events[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    intra_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    state_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    return {"wall_s": wall, "intra_ms": intra_ms, "state_ms": state_ms, "step_ms": step_ms, "inputs": x,
+            "o_bytes": 4 if odt == torch.float32 else 2, "in_bytes": 2 if qdt == torch.bfloat16 else 4}
+
+
+def bench_decode(w, steps, distinct):
+    import torch
+    import gated_delta_rule_26_amd as gdr
+    from gdr_inputs import decode_state0, decode_step_inputs
+
+    dev = torch.device("cuda:0")
+    state = torch.from_numpy(decode_state0(w)).to(dev)
+    inputs = []
+    for i in range(distinct):
+        x = decode_step_inputs(w, i)
+        dd = {key: torch.from_numpy(val).to(dev) for key, val in x.items()}
+        for key in ("q", "k", "v"):
+            dd[key] = dd[key].to(torch.bfloat16)
+        inputs.append(dd)
+    o = torch.empty((w.B, w.H, w.Dv), dtype=torch.float32, device=dev)
+    kw = dict(per_channel=w.per_channel, kaczmarz=w.kaczmarz, eps=w.eps, o=o, o_dtype=torch.float32)
+    for i in range(10):
+        dd = inputs[i % distinct]
+        gdr.recurrent_step(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], state, **kw)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(steps):
+        dd = inputs[i % distinct]
+        gdr.recurrent_step(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], state, **kw)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return {"wall_s": wall, "step_ms": per}
+
+
+def calibrate_copy(nbytes=1 << 30, reps=3):
+    """A plain device copy of known size, so that rocprofv3 byte counters of
+    the same command can be scaled (FETCH_SIZE / WRITE_SIZE per dispatch)."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return nbytes
+
+
+def median(xs):
+    ys = sorted(xs)
+    return ys[len(ys) // 2] if ys else float("nan")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gdn_prefill",
+                    choices=["gdn_prefill", "kda_prefill", "kla_prefill", "gdn_tiny"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "vector", "matrix"])
+    ap.add_argument("--o-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--decode-distinct", type=int, default=16,
+                    help="distinct decode-step inputs kept resident and cycled through")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (for rocprofv3 counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one MI355X; the path "
+              f"shards over independent (sequence, head) pairs, so N GPUs run N independent shares.",
+              file=sys.stderr)
+        sys.exit(2)
+    rank = int(os.environ.get("RANK", "0"))
+
+    import torch
+    import gated_delta_rule_26_amd as gdr
+    from gdr_inputs import WORKLOADS
+
+    gdr.load_library()  # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(3)
+
+    w = WORKLOADS[args.workload]
+    pre = bench_prefill(w, args.steps, args.warmup, args.algo, args.o_dtype)
+    tok_heads = w.B * w.T * w.H
+    ms_step = pre["wall_s"] / args.steps * 1e3
+    value = w.B * w.T / (ms_step / 1e3)
+    fl = alg_flops_per_token_head(w.Dk, w.Dv)
+    intra_ms = sum(pre["intra_ms"]) / len(pre["intra_ms"])
+    state_ms = sum(pre["state_ms"]) / len(pre["state_ms"])
+    event_step_ms = sum(pre["step_ms"]) / len(pre["step_ms"])
+    algo = args.algo
+    if algo == "auto":
+        algo = "matrix" if (w.dtype == "bf16" and w.Dk == 128 and w.Dv == 128 and gdr_matrix_ready()) else "vector"
+    dom = "state" if state_ms >= intra_ms else "intra"
+    dom_ms = state_ms if dom == "state" else intra_ms
+    dom_flops = fl[dom] * tok_heads
+    if algo == "matrix":
+        bound, peak, unit = "mfma", PEAK_BF16_MFMA, "TFLOP/s"
+    else:
+        bound, peak, unit = "alu", PEAK_FP32_VALU, "TFLOP/s"
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    total_tflops = fl["total"] * tok_heads / (event_step_ms * 1e-3) / 1e12
+    abytes = alg_bytes_prefill(w.B, w.T, w.H, w.Dk, w.Dv, pre["in_bytes"], pre["o_bytes"], w.per_channel)
+
+    out = {
+        "metric": "prefill tokens/s (chunkwise GDN, H16 d128, % MFMA peak) + decode HBM GB/s",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if algo == "matrix" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: chunked prefill B{w.B} H{w.H} T{w.T} d_k={w.Dk} d_v={w.Dv}, "
+                               f"{w.dtype} q/k/v, fp32 state, {args.o_dtype} output, chunk {C}, "
+                               f"{w.decay} decay, {w.beta_mode} beta",
+                   "B": w.B, "T": w.T, "H": w.H, "Dk": w.Dk, "Dv": w.Dv, "chunk": C,
+                   "algo": algo, "o_dtype": args.o_dtype},
+        "roofline": {"bound": bound, "kernel": f"{dom} ({algo} path)", "achieved": achieved, "peak": peak,
+                     "unit": unit, "frac": achieved / peak, "traffic": None,
+                     "alg_flops_per_launch": dom_flops, "avg_launch_ms": dom_ms},
+        "prefill": {"intra_ms": intra_ms, "state_ms": state_ms, "event_step_ms": event_step_ms,
+                    "intra_ms_median": median(pre["intra_ms"]), "state_ms_median": median(pre["state_ms"]),
+                    "alg_tflops": total_tflops, "frac_bf16_mfma_peak": total_tflops / PEAK_BF16_MFMA,
+                    "alg_bytes": abytes, "alg_gbps": abytes / (event_step_ms * 1e-3) / 1e9,
+                    "frac_hbm_peak": abytes / (event_step_ms * 1e-3) / 1e9 / PEAK_HBM,
+                    "alg_flops_per_token_head": fl},
+    }
+
+    if not args.no_decode:
+        wd = WORKLOADS["decode"]
+        dec = bench_decode(wd, args.decode_steps, args.decode_distinct)
+        dms = sum(dec["step_ms"]) / len(dec["step_ms"])
+        dbytes = decode_bytes_per_step(wd.B, wd.H, wd.Dk, wd.Dv)
+        gbps = dbytes / (dms * 1e-3) / 1e9
+        out["decode"] = {
+            "workload": f"decode: {wd.B} sequences x H{wd.H}, d_k=d_v={wd.Dk}, bf16 q/k/v, fp32 state in place, "
+                        f"scalar decay, given beta; {args.decode_steps} steps cycling {args.decode_distinct} "
+                        f"resident inputs",
+            "ms_per_step": dms, "ms_per_step_median": median(dec["step_ms"]),
+            "tokens_per_s": wd.B / (dms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM, "unit": "GB/s",
+                         "frac": gbps / PEAK_HBM, "traffic": None, "alg_bytes_per_launch": dbytes,
+                         "avg_launch_ms": dms},
+        }
+
+    if args.calibrate_copy:
+        out["calibration_copy_bytes"] = calibrate_copy()
+
+    if not args.no_cpu_baseline and rank == 0:
+        out["cpu_baseline"] = cpu_baseline(w, pre["inputs"])
+
+    print(json.dumps(out), flush=True)
+
+
+def gdr_matrix_ready() -> bool:
+    """Whether the library routes bf16 d128 inputs to the matrix-core path
+    (the workspace size differs between the two paths)."""
+    import torch
+    import gated_delta_rule_26_amd as gdr
+    try:
+        gdr.chunk_fwd_workspace_size(gdr.make_desc(1, 64, 1, 128, 128, qkv_dtype=torch.bfloat16,
+                                                   o_dtype=torch.float32, algo="matrix"))
+        return True
+    except gdr.GdrError:
+        return False
+
+
+if __name__ == "__main__":
+    main()
