@@ -224,6 +224,8 @@ def main():
     dom = "state" if state_ms >= intra_ms else "intra"
     dom_ms = state_ms if dom == "state" else intra_ms
     dom_flops = fl[dom] * tok_heads
+    if algo == "matrix":  # one fused kernel does the whole pass
+        dom, dom_flops = "fused chunk kernel", fl["total"] * tok_heads
     if algo == "matrix":
         bound, peak, unit = "mfma", PEAK_BF16_MFMA, "TFLOP/s"
     else:

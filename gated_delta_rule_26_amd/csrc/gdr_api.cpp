@@ -77,10 +77,9 @@ int resolve_algo(const gdr_desc *d) {
     return d->algo;
 }
 
-// The matrix-core path is not built yet: every call goes to the vector path.
 bool matrix_path_available(const gdr_desc *d) {
-    (void)d;
-    return false;
+    return gdr::chunk_matrix_supported(d->Dk, d->Dv, d->qkv_dtype == GDR_BF16,
+                                       d->decay_mode == GDR_DECAY_PER_CHANNEL);
 }
 
 int chunk_workspace(const gdr_desc *d, size_t *bytes) {

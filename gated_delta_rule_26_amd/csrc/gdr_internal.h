@@ -45,6 +45,7 @@ hipError_t launch_chunk_vector(const ChunkArgs &a, int stage);
 
 // Matrix-core chunked path (bf16 MFMA with fp32 accumulation, bf16 inputs).
 size_t chunk_matrix_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel);
+bool chunk_matrix_supported(int Dk, int Dv, bool qkv_bf16, bool per_channel);
 hipError_t launch_chunk_matrix(const ChunkArgs &a, int stage);
 
 // T == 0: s_final = s0 (or zero).

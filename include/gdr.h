@@ -61,9 +61,9 @@ extern "C" {
 #define GDR_F32 0
 #define GDR_BF16 1
 /* algo: which kernels run the chunked path */
-#define GDR_ALGO_AUTO 0          /* bf16 q/k/v -> matrix-core kernels; fp32 -> vector kernels */
-#define GDR_ALGO_VECTOR 1        /* fp32 vector-ALU kernels (any dtype) */
-#define GDR_ALGO_MATRIX 2        /* bf16 MFMA kernels (bf16 q/k/v only) */
+#define GDR_ALGO_AUTO 0          /* matrix-core kernel where supported, else vector kernels */
+#define GDR_ALGO_VECTOR 1        /* fp32 vector-ALU kernels (any dtype, any mode) */
+#define GDR_ALGO_MATRIX 2        /* bf16 MFMA kernel: bf16 q/k/v, Dk = Dv = 128, scalar decay */
 
 typedef enum gdr_status {
     GDR_OK = 0,
@@ -151,7 +151,9 @@ int gdr_chunk_fwd(const gdr_desc *desc,
  *            stage 0 with the same arguments, and writes o and s_final.
  * Stage 0 followed by stage 1 on one stream is exactly gdr_chunk_fwd.  The
  * split exists so that callers (profilers, benchmarks) can time each kernel;
- * validation is identical to gdr_chunk_fwd.
+ * validation is identical to gdr_chunk_fwd.  The matrix-core path is a single
+ * fused kernel that needs no workspace: its stage 0 enqueues nothing and its
+ * stage 1 does the whole pass.
  */
 #define GDR_STAGE_INTRA 0
 #define GDR_STAGE_STATE 1

@@ -49,8 +49,10 @@ def test_version_and_strings():
 
 
 def _desc(**kw):
+    # The vector path needs a workspace, so a missing workspace fails validation;
+    # no call in this file may pass validation (it would launch a kernel).
     base = dict(B=2, T=100, H=3, Dk=128, Dv=128, qkv_dtype=__import__("torch").bfloat16,
-                o_dtype=__import__("torch").float32)
+                o_dtype=__import__("torch").float32, algo="vector")
     base.update(kw)
     return gdr.make_desc(**base)
 
@@ -121,9 +123,15 @@ def test_chunk_validation_errors():
                                    wsb, None) == E["GDR_E_NULL"]
 
 
-def test_matrix_algo_rejects_fp32_inputs():
-    d = _desc(qkv_dtype=__import__("torch").float32, algo="matrix")
-    assert _ws(d)[0] == E["GDR_E_UNSUPPORTED"]
+def test_matrix_algo_support_and_workspace():
+    torch = __import__("torch")
+    assert _ws(_desc(qkv_dtype=torch.float32, algo="matrix"))[0] == E["GDR_E_UNSUPPORTED"]
+    assert _ws(_desc(Dk=64, Dv=64, algo="matrix"))[0] == E["GDR_E_UNSUPPORTED"]
+    assert _ws(_desc(per_channel=True, algo="matrix"))[0] == E["GDR_E_UNSUPPORTED"]
+    assert _ws(_desc(algo="matrix")) == (0, 0)      # the fused kernel needs no workspace
+    assert _ws(_desc(algo="auto")) == (0, 0)
+    rc, n = _ws(_desc(per_channel=True, algo="auto"))   # auto falls back to the vector path
+    assert rc == 0 and n > 0
 
 
 def test_step_validation_errors():

@@ -14,7 +14,13 @@ pytestmark = pytest.mark.gpu
 MODES = {"gdn": dict(per_channel=False, kaczmarz=False),
          "kda": dict(per_channel=True, kaczmarz=False),
          "kla": dict(per_channel=False, kaczmarz=True)}
-ALGOS = ["vector"]
+ALGOS = ["vector", "matrix"]
+
+
+def _skip_unsupported(algo, mode, dtype, D):
+    """The matrix-core kernel covers bf16 inputs, d_k = d_v = 128, scalar decay."""
+    if algo == "matrix" and (dtype != "bf16" or tuple(D) != (128, 128) or mode == "kda"):
+        pytest.skip("matrix path: bf16, d128, scalar decay only")
 
 
 def _inputs(seed, B, T, H, Dk, Dv, mode, dtype, with_s0=True, **kw):
@@ -45,6 +51,7 @@ def _ref(x, mode, scale=1.0, eps=1e-6, heads=None):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("D", [(128, 128), (64, 64)])
 def test_chunk_parity(algo, T, mode, dtype, D):
+    _skip_unsupported(algo, mode, dtype, D)
     x = _inputs(1000 + T, 2, T, 3, D[0], D[1], mode, dtype, with_s0=(T % 2 == 0))
     o, s = _gpu(x, mode, dtype, algo=algo)
     o_ref, s_ref = _ref(x, mode)
@@ -56,6 +63,7 @@ def test_chunk_parity(algo, T, mode, dtype, D):
 @pytest.mark.parametrize("algo", ALGOS)
 @pytest.mark.parametrize("D", [(128, 64), (64, 128)])
 def test_chunk_mixed_widths(algo, D):
+    _skip_unsupported(algo, "kda", "bf16", D)
     x = _inputs(7, 1, 150, 2, D[0], D[1], "kda", "bf16")
     o, s = _gpu(x, "kda", "bf16", algo=algo)
     o_ref, s_ref = _ref(x, "kda")
@@ -88,56 +96,70 @@ def test_empty_and_zero_length():
     assert o.shape[0] == 0 and s.shape[0] == 0
 
 
-def test_in_place_state_and_resume():
+@pytest.mark.parametrize("algo", ALGOS)
+def test_in_place_state_and_resume(algo):
     x = _inputs(10, 2, 200, 2, 128, 128, "kla", "bf16")
-    o_full, s_full = _gpu(x, "kla", "bf16")
+    o_full, s_full = _gpu(x, "kla", "bf16", algo=algo)
     d = to_dev(x, "bf16")
     state = d["s0"].clone()
     outs = []
     for t0, t1 in [(0, 130), (130, 131), (131, 200)]:   # split mid-chunk, and a single token
         sl = {key: (d[key][:, t0:t1].contiguous() if key != "s0" else None) for key in d}
         o, _ = gdr.chunk_fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], s0=state, s_final=state,
-                             o_dtype=torch.float32, kaczmarz=True, eps=1e-6)
+                             o_dtype=torch.float32, kaczmarz=True, eps=1e-6, algo=algo)
         outs.append(o)
     torch.cuda.synchronize()
     o_split = torch.cat(outs, dim=1)
-    assert rel(host(o_split), host(o_full)) < 1e-5
-    assert rel(host(state), host(s_full)) < 1e-5
+    o_ref, s_ref = _ref(x, "kla")
+    # both schedules meet the bar against the oracle; the vector path (fp32
+    # throughout) also agrees with itself across chunk boundaries to 1e-5
+    assert rel(host(o_split), o_ref) < TOL["bf16"] and rel(host(state), s_ref) < TOL["bf16"]
+    assert rel(host(o_full), o_ref) < TOL["bf16"] and rel(host(s_full), s_ref) < TOL["bf16"]
+    if algo == "vector":
+        assert rel(host(o_split), host(o_full)) < 1e-5
+        assert rel(host(state), host(s_full)) < 1e-5
 
 
-def test_prefill_then_decode_step():
+@pytest.mark.parametrize("algo", ALGOS)
+def test_prefill_then_decode_step(algo):
     x = _inputs(11, 2, 129, 3, 128, 128, "gdn", "bf16")
     d = to_dev(x, "bf16")
     T = 129
     cut = {key: (d[key][:, :T - 1].contiguous() if key != "s0" else d[key]) for key in d}
     _, s = gdr.chunk_fwd(cut["q"], cut["k"], cut["v"], cut["g"], cut["beta"], s0=cut["s0"],
-                         o_dtype=torch.float32)
+                         o_dtype=torch.float32, algo=algo)
     last = {key: d[key][:, T - 1].contiguous() for key in ("q", "k", "v", "g", "beta")}
     o_last = gdr.recurrent_step(last["q"], last["k"], last["v"], last["g"], last["beta"], s,
                                 o_dtype=torch.float32)
-    o_full, s_full = _gpu(x, "gdn", "bf16")
-    assert rel(host(o_last), host(o_full[:, T - 1])) < 1e-5
-    assert rel(host(s), host(s_full)) < 1e-5
+    o_full, s_full = _gpu(x, "gdn", "bf16", algo=algo)
+    tol = 1e-5 if algo == "vector" else 2e-4
+    assert rel(host(o_last), host(o_full[:, T - 1])) < tol
+    assert rel(host(s), host(s_full)) < tol
 
 
+@pytest.mark.parametrize("algo", ALGOS)
 @pytest.mark.parametrize("mode", ["gdn", "kda"])
-def test_beta_zero_and_one(mode):
-    x = _inputs(12, 1, 100, 2, 64, 64, mode, "bf16")
+def test_beta_zero_and_one(mode, algo):
+    D = 128 if algo == "matrix" else 64
+    _skip_unsupported(algo, mode, "bf16", (D, D))
+    x = _inputs(12, 1, 100, 2, D, D, mode, "bf16")
     x["beta"] = np.zeros_like(x["beta"])
-    o, s = _gpu(x, mode, "bf16")
+    o, s = _gpu(x, mode, "bf16", algo=algo)
     o_ref, s_ref = _ref(x, mode)
     assert rel(host(s), s_ref) < 1e-5 and rel(host(o), o_ref) < 1e-5
     x["beta"] = np.ones_like(x["beta"])
-    o, s = _gpu(x, mode, "bf16")
+    o, s = _gpu(x, mode, "bf16", algo=algo)
     o_ref, s_ref = _ref(x, mode)
     assert rel(host(s), s_ref) < TOL["bf16"] and rel(host(o), o_ref) < TOL["bf16"]
 
 
+@pytest.mark.parametrize("algo", ALGOS)
 @pytest.mark.parametrize("mode", ["gdn", "kda"])
-def test_strong_decay(mode):
+def test_strong_decay(mode, algo):
+    _skip_unsupported(algo, mode, "bf16", (128, 128))
     x = _inputs(13, 1, 150, 2, 128, 128, mode, "bf16")
     x["g"] = np.full_like(x["g"], -5.0)
-    o, s = _gpu(x, mode, "bf16")
+    o, s = _gpu(x, mode, "bf16", algo=algo)
     o_ref, s_ref = _ref(x, mode)
     assert np.isfinite(host(o)).all()
     assert rel(host(o), o_ref) < TOL["bf16"] and rel(host(s), s_ref) < TOL["bf16"]
@@ -145,10 +167,10 @@ def test_strong_decay(mode):
 
 def test_per_channel_with_uniform_gate_equals_scalar():
     x = _inputs(14, 1, 150, 2, 128, 128, "gdn", "bf16")
-    o1, s1 = _gpu(x, "gdn", "bf16")
+    o1, s1 = _gpu(x, "gdn", "bf16", algo="vector")
     xp = dict(x)
     xp["g"] = np.repeat(x["g"][..., None], 128, axis=-1)
-    o2, s2 = _gpu(xp, "kda", "bf16")
+    o2, s2 = _gpu(xp, "kda", "bf16", algo="vector")
     assert rel(host(o2), host(o1)) < 1e-5 and rel(host(s2), host(s1)) < 1e-5
 
 
@@ -166,6 +188,18 @@ def test_deterministic_and_workspace_poison_does_not_leak():
         torch.cuda.synchronize()
         runs.append((o.clone(), s.clone()))
     assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
+
+
+@pytest.mark.parametrize("mode", ["gdn", "kla"])
+def test_matrix_path_deterministic_and_close_to_vector_path(mode):
+    x = _inputs(16, 2, 333, 3, 128, 128, mode, "bf16")
+    o1, s1 = _gpu(x, mode, "bf16", algo="matrix")
+    o2, s2 = _gpu(x, mode, "bf16", algo="matrix")
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    ov, sv = _gpu(x, mode, "bf16", algo="vector")
+    eo, es = rel(host(o1), host(ov)), rel(host(s1), host(sv))
+    print(f"matrix vs vector {mode}: rel o {eo:.2e} S {es:.2e}")
+    assert eo < TOL["bf16"] and es < TOL["bf16"]
 
 
 # ------------------------------------------------------------ full workloads
