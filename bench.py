@@ -29,6 +29,38 @@ PEAK_FP32_VALU = 157.3       # TFLOP/s, MI355X fp32 vector
 PEAK_HBM = 8000.0            # GB/s, MI355X HBM3E
 
 
+# HBM bytes per launch from rocprofv3 FETCH_SIZE (x2.0) + WRITE_SIZE (x1.0), scaled by a 1 GiB device
+# copy read in the same runs.  Each figure holds only for the kernel source it was measured on: when the
+# file's sha256 differs, the figure is reported as null.
+MEASURED_TRAFFIC = {
+    ("matrix", "state"): ("gated_delta_rule_26_amd/csrc/chunk_matrix.hip",
+                          "2ea52c7fd3934cc999a41f63550b8f3333ddd126249cbc008a276178a5eafeea",
+                          (160320.5 * 2.0 + 135168.0) * 1024),
+    ("matrix", "intra"): ("gated_delta_rule_26_amd/csrc/chunk_matrix.hip",
+                          "2ea52c7fd3934cc999a41f63550b8f3333ddd126249cbc008a276178a5eafeea",
+                          (67136.6 * 2.0 + 123906.3) * 1024),
+    ("decode", "step"): ("gated_delta_rule_26_amd/csrc/recurrent_step.hip",
+                         "e7e419c4fce8d18e58aad36eae998f3c36e35efc9c754b1783925800a8b15b99",
+                         (133011.2 * 2.0 + 264192.0) * 1024),
+}
+
+
+def measured_traffic(path_kind: str, kernel: str):
+    """Counter-measured HBM bytes per launch, or None if not measured on the current source."""
+    import hashlib
+    entry = MEASURED_TRAFFIC.get((path_kind, kernel))
+    if entry is None:
+        return None
+    src, sha, nbytes = entry
+    try:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != sha:
+                return None
+    except OSError:
+        return None
+    return nbytes
+
+
 def alg_flops_per_token_head(dk: int, dv: int) -> dict:
     """Algorithmic (triangle-aware) flops per token and head, by kernel.
 
@@ -224,8 +256,6 @@ def main():
     dom = "state" if state_ms >= intra_ms else "intra"
     dom_ms = state_ms if dom == "state" else intra_ms
     dom_flops = fl[dom] * tok_heads
-    if algo == "matrix":  # one fused kernel does the whole pass
-        dom, dom_flops = "fused chunk kernel", fl["total"] * tok_heads
     if algo == "matrix":
         bound, peak, unit = "mfma", PEAK_BF16_MFMA, "TFLOP/s"
     else:
@@ -253,7 +283,7 @@ def main():
                    "B": w.B, "T": w.T, "H": w.H, "Dk": w.Dk, "Dv": w.Dv, "chunk": C,
                    "algo": algo, "o_dtype": args.o_dtype},
         "roofline": {"bound": bound, "kernel": f"{dom} ({algo} path)", "achieved": achieved, "peak": peak,
-                     "unit": unit, "frac": achieved / peak, "traffic": None,
+                     "unit": unit, "frac": achieved / peak, "traffic": measured_traffic(algo, dom),
                      "alg_flops_per_launch": dom_flops, "avg_launch_ms": dom_ms},
         "prefill": {"intra_ms": intra_ms, "state_ms": state_ms, "event_step_ms": event_step_ms,
                     "intra_ms_median": median(pre["intra_ms"]), "state_ms_median": median(pre["state_ms"]),
@@ -276,7 +306,8 @@ def main():
             "ms_per_step": dms, "ms_per_step_median": median(dec["step_ms"]),
             "tokens_per_s": wd.B / (dms * 1e-3),
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM, "unit": "GB/s",
-                         "frac": gbps / PEAK_HBM, "traffic": None, "alg_bytes_per_launch": dbytes,
+                         "frac": gbps / PEAK_HBM, "traffic": measured_traffic("decode", "step"),
+                         "alg_bytes_per_launch": dbytes,
                          "avg_launch_ms": dms},
         }
 

@@ -151,9 +151,7 @@ int gdr_chunk_fwd(const gdr_desc *desc,
  *            stage 0 with the same arguments, and writes o and s_final.
  * Stage 0 followed by stage 1 on one stream is exactly gdr_chunk_fwd.  The
  * split exists so that callers (profilers, benchmarks) can time each kernel;
- * validation is identical to gdr_chunk_fwd.  The matrix-core path is a single
- * fused kernel that needs no workspace: its stage 0 enqueues nothing and its
- * stage 1 does the whole pass.
+ * validation is identical to gdr_chunk_fwd.
  */
 #define GDR_STAGE_INTRA 0
 #define GDR_STAGE_STATE 1
