@@ -13,36 +13,43 @@
 //   S   <- gend S + K^T Diag(Gend) E                  chunk-end state
 // Padded rows of a partial last chunk are zero (k = q = v = g = beta = 0).
 //
+// W is never formed: E = U - W S = T'' (V - Diag(Gam) K S) with
+// T'' = T Diag(beta), so the walk multiplies K by the state (the same work as
+// W S) and applies the 64 x 64 triangle T'' to the 64 x 16 result.
+//
 // Two kernels, as in the blog summary's "Pipeline Triton por chunks" (an
 // intra-chunk kernel, then the state walk that also produces the outputs):
 //  * intra: one workgroup per chunk, all chunks in parallel: gates, K K^T and
-//    Q K^T on the lower 16x16 tiles, R, A and T = (I + R)^{-1}.  Writes to the
-//    workspace, as bf16 hi + lo pairs of their lower 16x16 tiles, the three
-//    operands the state walk needs -- T' = T Diag(beta Gam), T'' = T Diag(beta)
-//    and A -- plus G (30 KiB per chunk).  Small LDS, so several workgroups
-//    share a compute unit and hide each other's latencies.
-//  * state: one 8-wavefront workgroup per (sequence, head, BV-column value
-//    slice), chunks in order, the fp32 state slice in registers:
-//    W^T = K^T T'^T, U = T'' V, E = U - W S, O and the state update.  Two
-//    wavefronts per SIMD: one wavefront per SIMD reaches only about half of
-//    the LDS read bandwidth (measured 134 vs 256 B/clk per CU).  Everything a
-//    chunk needs from HBM is loaded into registers during the previous chunk.
+//    Q K^T on the lower 16x16 tiles, R, A and T = (I + R)^{-1}.  Writes T'' and
+//    A, each split into bf16 hi + lo and laid out as the exact MFMA operand
+//    fragments the walk loads (one 16-byte load per lane per fragment), and G.
+//  * state: one workgroup per (sequence, head, 32 value columns), chunks in
+//    order.  Two "chain" wavefronts each own the fp32 state of 16 value
+//    columns in registers and do the dependent work of a chunk:
+//    P = K S, X = V - Gam P, E = T'' X, S <- gend S + K^T (Gend E).  Their
+//    operands stay in registers from one product to the next (see Layout),
+//    so a chunk needs no exchange between chain wavefronts.  Two "helper"
+//    wavefronts stage the next chunk's q, k, v and decays in LDS and, one
+//    chunk behind, compute the outputs O = scale Gam (Q S) + A E from the
+//    chain's S (bf16 hi, lo) and E, passed through LDS.  One barrier per
+//    chunk; every LDS buffer that crosses it is doubled, and q and exp(G) are
+//    tripled: while the chain works on chunk c, the helpers read chunk c-1's
+//    and write chunk c+1's.
 //
 // Layout.  v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8(l/16)+e],
-// B[8(l/16)+e][l%16] (e = 0..7) and D[4(l/16)+r][l%16] (r = 0..3).  A sum
-// over tokens may take its 32 terms in any order shared by both operands;
-// here the 8 terms of lane group p = l/16 within a 32-token block are tokens
-// {4p..4p+3} and {16+4p..16+4p+3}, which is exactly what two stacked D tiles
-// hold.  So a D tile is directly a token-reduction operand, and K^T, V^T are
-// produced in registers by one MFMA against a 0/1 selector instead of
-// transposed LDS writes.  W^T's D layout lets W be stored token-major with
-// 8-byte writes.  The off-diagonal 16x16 blocks of T use
-// v_mfma_f32_16x16x4f32 (fp32 operands, same D layout).
+// B[8(l/16)+e][l%16] (e = 0..7) and D[4(l/16)+r][l%16] (r = 0..3).  A
+// reduction may take its 32 terms (per 32-block) in any order shared by
+// both operands; here the 8 terms of lane group p = l/16 are indices
+// {4p..4p+3} and {16+4p..16+4p+3} of the block, which is exactly what two
+// stacked D tiles hold.  So a D tile (the state, X, E) is directly the B
+// operand of the next product, and the other operand (k, k^T, T'', A, q) is
+// stored or loaded in that permuted order.  The off-diagonal 16x16 blocks of
+// T use v_mfma_f32_16x16x4f32 (fp32 operands, same D layout).
 //
 // Precision.  Products of two exact bf16 inputs accumulate in fp32.  Every
-// fp32-derived operand (T', T'', S, E, A) is split into bf16 hi + lo and
+// fp32-derived operand (T'', A, S, X, E) is split into bf16 hi + lo and
 // multiplied as hi*x + lo*x (hi*hi + hi*lo + lo*hi when both sides are
-// split), which carries ~16 significant bits; W is stored as plain bf16.
+// split), which carries ~16 significant bits.
 #include "gdr_internal.h"
 
 namespace gdr {
@@ -50,17 +57,14 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int C = kChunk;      // 64 tokens per chunk
 constexpr int DK = 128;
 constexpr int DV = 128;
-constexpr int kThreads = 256;
-constexpr int LDQ = DK + 8;    // bf16 row stride of Q, K, W (token-major)
-constexpr int LDV = 32 + 8;    // bf16 row stride of the value slice (token-major, 32 columns)
-constexpr int LDE = C + 8;     // bf16 row stride of E^T (token index contiguous)
+constexpr int LDQ = DK + 8;    // bf16 row stride of q, k in the intra kernel (token-major)
 constexpr int LDF = C + 4;     // fp32 row stride of R, T, A
-constexpr int LDS_ = DK + 8;   // bf16 row stride of S^T (d_k contiguous)
 
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -75,32 +79,19 @@ __device__ __forceinline__ bf16x8 frag(const __bf16 *base, int ld, int r0, int k
     return *reinterpret_cast<const bf16x8 *>(base + (r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
 }
 
-// Token-reduction fragment (tokens 32kb .. 32kb+31 in the lane-group order
-// above) of a bf16 matrix with the token index contiguous.
-__device__ __forceinline__ bf16x8 frag_tok(const __bf16 *base, int ld, int r0, int kb, int lane) {
-    const __bf16 *p = base + (r0 + (lane & 15)) * ld + 32 * kb + 4 * (lane >> 4);
-    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(p);
-    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(p + 16);
-    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
+// Index, inside a 32-block, of term e (0..7) of lane group p (0..3).
+__host__ __device__ constexpr int kperm(int p, int e) { return e < 4 ? 4 * p + e : 12 + 4 * p + e; }
 
-// Two stacked D tiles (tokens 32kb .. +15 and 32kb+16 .. +31) as one
-// token-reduction operand in bf16.
-__device__ __forceinline__ bf16x8 pack_tok(f32x4 t0, f32x4 t1) {
-    return bf16x8{static_cast<__bf16>(t0[0]), static_cast<__bf16>(t0[1]), static_cast<__bf16>(t0[2]),
-                  static_cast<__bf16>(t0[3]), static_cast<__bf16>(t1[0]), static_cast<__bf16>(t1[1]),
-                  static_cast<__bf16>(t1[2]), static_cast<__bf16>(t1[3])};
-}
-
-// 0/1 selector: MFMA(X rows, selector(u)) = columns 16u .. 16u+15 of a
-// 32-wide block of X, as a D tile (one column per lane, four consecutive
-// rows).  Exact: bf16 values times 1 summed with zeros in fp32.
-__device__ __forceinline__ bf16x8 selector(int u, int lane) {
-    bf16x8 s;
+// Two stacked D tiles (block rows 0..15 and 16..31) as one permuted operand,
+// split into bf16 hi and lo.
+__device__ __forceinline__ void pair_split(f32x4 t0, f32x4 t1, bf16x8 &hi, bf16x8 &lo) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-        s[e] = static_cast<__bf16>((8 * (lane >> 4) + e) == ((lane & 15) + 16 * u) ? 1.0f : 0.0f);
-    return s;
+    for (int r = 0; r < 4; ++r) {
+        hi[r] = static_cast<__bf16>(t0[r]);
+        lo[r] = static_cast<__bf16>(t0[r] - static_cast<float>(hi[r]));
+        hi[4 + r] = static_cast<__bf16>(t1[r]);
+        lo[4 + r] = static_cast<__bf16>(t1[r] - static_cast<float>(hi[4 + r]));
+    }
 }
 
 // Off-diagonal 16x16 block of the unit lower-triangular inverse, by one
@@ -122,30 +113,23 @@ __device__ __forceinline__ void inverse_block(float *sT, const float *sR, int I,
     for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * lg + r) * LDF + 16 * J + lr] = -out[r];
 }
 
-
-
-// Lower 16x16 tile t (0..9) of a 64x64 matrix: (0,0) (1,0) (1,1) (2,0) ...
-__host__ __device__ constexpr int lower_I(int t) { return t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3; }
-__host__ __device__ constexpr int lower_J(int t) { return t - lower_I(t) * (lower_I(t) + 1) / 2; }
-
-// Per-chunk workspace record.  Six packed bf16 matrices (T' hi, T' lo,
-// T'' hi, T'' lo, A hi, A lo), each as its ten lower 16x16 tiles, a tile
-// row-major (512 B per tile, 5120 B per matrix), then G of the 64 tokens.
-constexpr int kPackBytes = 10 * 256 * 2;
-constexpr int kRecGOffsetFloats = 6 * kPackBytes / 4;
-constexpr int kRecFloats = kRecGOffsetFloats + C;
-
-// 16-byte piece p (0..319) of a packed matrix: tile t, row rr, half hf.
-__device__ __forceinline__ void packed_piece(int p, int &row, int &col, int &byte_off) {
-    const int t = p >> 5, rr = (p >> 1) & 15, hf = p & 1;
-    row = 16 * lower_I(t) + rr;
-    col = 16 * lower_J(t) + 8 * hf;
-    byte_off = t * 512 + rr * 32 + hf * 16;
-}
-
-__device__ __forceinline__ uint4 ld16(const void *p, bool ok) {
-    return ok ? *reinterpret_cast<const uint4 *>(p) : make_uint4(0, 0, 0, 0);
-}
+// ---- per-chunk workspace record
+// T'' hi, T'' lo, A hi, A lo: each the six 16x32 operand fragments (M, kb) of
+// its lower triangle -- (0,0) (1,0) (2,0) (2,1) (3,0) (3,1), rows 16M ..
+// 16M+15, tokens 32kb .. 32kb+31 in the permuted order -- as 64 lanes x
+// 16 bytes; then, for the 64 tokens, Gam = exp(G) and Gend = exp(G_63 - G)
+// (fp32), so the walk needs no exponentials.
+constexpr int kFragBytes = 64 * 16;
+constexpr int kRecTH = 0;
+constexpr int kRecTL = 6 * kFragBytes;
+constexpr int kRecAH = 12 * kFragBytes;
+constexpr int kRecAL = 18 * kFragBytes;
+constexpr int kRecGam = 24 * kFragBytes;
+constexpr int kRecGend = kRecGam + C * 4;
+constexpr int kRecBytes = kRecGend + C * 4;  // 25088, a multiple of 256
+__host__ __device__ constexpr int lower_frag(int M, int kb) { return M < 2 ? M : 2 * M - 2 + kb; }
+__host__ __device__ constexpr int frag_M(int f) { return f < 2 ? f : 2 + ((f - 2) >> 1); }
+__host__ __device__ constexpr int frag_kb(int f) { return f < 2 ? 0 : (f - 2) & 1; }
 
 __device__ __forceinline__ float sumsq8(uint4 x) {
     const __bf16 *e = reinterpret_cast<const __bf16 *>(&x);
@@ -153,19 +137,6 @@ __device__ __forceinline__ float sumsq8(uint4 x) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) s += static_cast<float>(e[i]) * static_cast<float>(e[i]);
     return s;
-}
-
-// 8 fp32 values times 8 scales, split into bf16 hi and lo (16 bytes each).
-__device__ __forceinline__ void split8(const float *x, const float *sc, uint4 &hi, uint4 &lo) {
-    __bf16 h[8], l[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float y = sc ? x[e] * sc[e] : x[e];
-        h[e] = static_cast<__bf16>(y);
-        l[e] = static_cast<__bf16>(y - static_cast<float>(h[e]));
-    }
-    hi = *reinterpret_cast<const uint4 *>(h);
-    lo = *reinterpret_cast<const uint4 *>(l);
 }
 
 // ============================================================ intra kernel
@@ -182,14 +153,13 @@ struct alignas(16) IntraSmem {
     } ka;
     float R[C * LDF];
     float kk[C];
-    float cw[C];                  // beta_j exp(G_j)
     float cb[C];                  // beta_j
 };
 
 template <bool KZ>
 __global__ __launch_bounds__(kIntraThreads) void intra_matrix_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const float *__restrict__ g,
-    const float *__restrict__ beta, int T, int H, int NC, float eps, float scale, float *__restrict__ ws) {
+    const float *__restrict__ beta, int T, int H, int NC, float eps, float scale, char *__restrict__ ws) {
     __shared__ IntraSmem sm;
     const int ci = blockIdx.x;  // (b*H + h)*NC + c
     const int c = ci % NC;
@@ -201,8 +171,7 @@ __global__ __launch_bounds__(kIntraThreads) void intra_matrix_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
-    float *rec = ws + (size_t)ci * kRecFloats;
-    char *recb = reinterpret_cast<char *>(rec);
+    char *recb = ws + (size_t)ci * kRecBytes;
 
     // ---- stage q, k token-major; gates of token `lane` in every wavefront
     {
@@ -210,9 +179,11 @@ __global__ __launch_bounds__(kIntraThreads) void intra_matrix_kernel(
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int i = i0 + 16 * it;
-            const size_t off = (row0 + (size_t)i * H) * DK + 8 * seg;
-            const uint4 qv = ld16(q + off, i < n);
-            const uint4 kv = ld16(k + off, i < n);
+            // rows past a partial last chunk repeat its last row: finite, and
+            // their beta (hence R's rows, T''s columns) is zero
+            const size_t off = (row0 + (size_t)min(i, n - 1) * H) * DK + 8 * seg;
+            const uint4 qv = *reinterpret_cast<const uint4 *>(q + off);
+            const uint4 kv = *reinterpret_cast<const uint4 *>(k + off);
             *reinterpret_cast<uint4 *>(&sm.qt.Q[i * LDQ + 8 * seg]) = qv;
             *reinterpret_cast<uint4 *>(&sm.ka.K[i * LDQ + 8 * seg]) = kv;
             if constexpr (KZ) {
@@ -225,19 +196,21 @@ __global__ __launch_bounds__(kIntraThreads) void intra_matrix_kernel(
             }
         }
     }
-    float Gl = lane < n ? g[row0 + (size_t)lane * H] : 0.f;
+    float Gl = g[row0 + (size_t)min(lane, n - 1) * H];
+    if (lane >= n) Gl = 0.f;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const float up = __shfl_up(Gl, off, 64);
         if (lane >= off) Gl += up;
     }
-    const float given = lane < n ? beta[row0 + (size_t)lane * H] : 0.f;
+    float given = beta[row0 + (size_t)min(lane, n - 1) * H];
+    if (lane >= n) given = 0.f;
     __syncthreads();
     float Bl = given;
     if constexpr (KZ) Bl = lane < n ? given / (sm.kk[lane] + eps) : 0.f;
     if (w == 0) {
-        rec[kRecGOffsetFloats + lane] = Gl;
-        sm.cw[lane] = Bl * __expf(Gl);
+        reinterpret_cast<float *>(recb + kRecGam)[lane] = __expf(Gl);
+        reinterpret_cast<float *>(recb + kRecGend)[lane] = __expf(__shfl(Gl, C - 1, 64) - Gl);
         sm.cb[lane] = Bl;
     }
 
@@ -327,105 +300,88 @@ __global__ __launch_bounds__(kIntraThreads) void intra_matrix_kernel(
     if (w == 0) inverse_block(sm.qt.T, sm.R, 3, 0, lane);
     __syncthreads();
 
-    // ---- packed bf16 hi/lo operands: T' = T Diag(cw), T'' = T Diag(cb), A
-    for (int u = tid; u < 640; u += kIntraThreads) {
-        const int p = u < 320 ? u : u - 320;
-        int row, col, boff;
-        packed_piece(p, row, col, boff);
-        uint4 hi, lo;
-        if (u < 320) {
-            const float *x = &sm.qt.T[row * LDF + col];
-            split8(x, &sm.cw[col], hi, lo);
-            *reinterpret_cast<uint4 *>(recb + 0 * kPackBytes + boff) = hi;
-            *reinterpret_cast<uint4 *>(recb + 1 * kPackBytes + boff) = lo;
-            split8(x, &sm.cb[col], hi, lo);
-            *reinterpret_cast<uint4 *>(recb + 2 * kPackBytes + boff) = hi;
-            *reinterpret_cast<uint4 *>(recb + 3 * kPackBytes + boff) = lo;
-        } else {
-            split8(&sm.ka.A[row * LDF + col], nullptr, hi, lo);
-            *reinterpret_cast<uint4 *>(recb + 4 * kPackBytes + boff) = hi;
-            *reinterpret_cast<uint4 *>(recb + 5 * kPackBytes + boff) = lo;
+    // ---- operand fragments: T'' = T Diag(beta) and A, lower triangle only
+    // (entries above the diagonal are written as zero), bf16 hi + lo
+    for (int u = tid; u < 2 * 6 * 64; u += kIntraThreads) {
+        const int mat = u / 384, f = (u >> 6) % 6, l = u & 63;
+        const int row = 16 * frag_M(f) + (l & 15), p = l >> 4, c0 = 32 * frag_kb(f);
+        bf16x8 hv, lv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int col = c0 + kperm(p, e);
+            float x = 0.f;
+            if (col <= row) x = mat == 0 ? sm.qt.T[row * LDF + col] * sm.cb[col] : sm.ka.A[row * LDF + col];
+            hv[e] = static_cast<__bf16>(x);
+            lv[e] = static_cast<__bf16>(x - static_cast<float>(hv[e]));
         }
+        char *dst = recb + (mat == 0 ? kRecTH : kRecAH) + f * kFragBytes + l * 16;
+        *reinterpret_cast<bf16x8 *>(dst) = hv;
+        *reinterpret_cast<bf16x8 *>(dst + 6 * kFragBytes) = lv;
     }
 }
 
 // ============================================================ state kernel
-constexpr int kStateThreads = 512;  // 8 wavefronts
+constexpr int kStateThreads = 256;  // chain wavefronts 0, 1; helper wavefronts 2, 3
+constexpr int BV = 32;              // value columns per workgroup
+constexpr int NS = DV / BV;         // workgroups per (sequence, head)
+constexpr int LDK = DK + 8;         // bf16 row stride of the token-major q, k
+constexpr int LDV = BV + 8;         // bf16 row stride of the token-major v slice
+constexpr int kXFrags = 12;         // chain -> helper: S hi (4), S lo (4), E (4 fp32 tiles)
 
-template <int BV>
 struct alignas(16) StateSmem {
-    __bf16 Q[C * LDQ];            // q, token-major
-    __bf16 K[C * LDQ];            // k, token-major
-    __bf16 W[C * LDQ];            // W (bf16), token-major
-    __bf16 V[C * LDV];            // v slice token-major (columns BV..31 stay zero)
-    __bf16 P6[6][C * LDE];        // T' hi, lo; T'' hi, lo; A hi, lo (upper tiles stay zero)
-    __bf16 E[4][BV * LDE];        // E^T hi, lo and (Gend E)^T hi, lo
-    __bf16 ST[2][BV * LDS_];      // S^T hi, lo of the slice
+    __bf16 K[2][C * LDK];          // k, token-major, key channels permuted within 32-blocks
+    __bf16 Q[3][C * LDK];          // q, the same layout (three buffers, see below)
+    __bf16 V[2][C * LDV];          // v slice, token-major
+    float Gam[3][C];               // exp(G_i)
+    float Gend[2][C];              // exp(G_63 - G_i)
+    uint4 X[2][2][kXFrags][64];    // per chain wavefront and chunk parity
 };
 
-// This thread's share of a chunk's state-kernel inputs, loaded ahead of use.
-struct StatePref {
-    uint4 q0, q1, k0, k1, v, p0, p1, p2, p3;
-    float g;
-};
+// Workgroup barrier for data exchanged through LDS only: waits for this
+// wavefront's LDS operations, not for its global loads, so loads issued for a
+// later chunk stay in flight across it (a full __syncthreads also waits for
+// every outstanding global load).  The memory clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int BV>
-__device__ __forceinline__ StatePref load_state_chunk(const __bf16 *q, const __bf16 *k, const __bf16 *v,
-                                                      const float *ws, int c, int T, int H, int NC, int b,
-                                                      int h, int bh, int j0, int tid) {
-    constexpr int VSEG = BV / 8;
-    const int t0 = c * C;
-    const int n = min(C, T - t0);
-    const size_t row0 = ((size_t)b * T + t0) * H + h;
-    const int seg = tid & 15, i0 = tid >> 4;  // i0 < 32
-    const float *rec = ws + ((size_t)bh * NC + c) * kRecFloats;
-    const char *recb = reinterpret_cast<const char *>(rec);
-    StatePref p;
-    const size_t o0 = (row0 + (size_t)i0 * H) * DK + 8 * seg;
-    const size_t o1 = (row0 + (size_t)(i0 + 32) * H) * DK + 8 * seg;
-    p.q0 = ld16(q + o0, i0 < n);
-    p.q1 = ld16(q + o1, i0 + 32 < n);
-    p.k0 = ld16(k + o0, i0 < n);
-    p.k1 = ld16(k + o1, i0 + 32 < n);
-    const int vi = tid / VSEG, vs = tid % VSEG;
-    p.v = ld16(v + (row0 + (size_t)vi * H) * DV + j0 + 8 * vs, tid < C * VSEG && vi < n);
-    // packed pieces tid + 512 m of the six matrices (1920 pieces)
-    {
-        int row, col, boff;
-        const int m0 = tid, m1 = tid + 512, m2 = tid + 1024, m3 = tid + 1536;
-        packed_piece(m0 % 320, row, col, boff);
-        p.p0 = *reinterpret_cast<const uint4 *>(recb + (m0 / 320) * kPackBytes + boff);
-        packed_piece(m1 % 320, row, col, boff);
-        p.p1 = *reinterpret_cast<const uint4 *>(recb + (m1 / 320) * kPackBytes + boff);
-        packed_piece(m2 % 320, row, col, boff);
-        p.p2 = *reinterpret_cast<const uint4 *>(recb + (m2 / 320) * kPackBytes + boff);
-        if (m3 < 1920) {
-            packed_piece(m3 % 320, row, col, boff);
-            p.p3 = *reinterpret_cast<const uint4 *>(recb + (m3 / 320) * kPackBytes + boff);
-        } else {
-            p.p3 = make_uint4(0, 0, 0, 0);
-        }
-    }
-    p.g = rec[kRecGOffsetFloats + (tid & 63)];
-    return p;
+// Raw buffer resource over `rows` rows of `row_bytes` bytes spaced `stride`
+// bytes apart, starting at `base`: loads past the last row return zero and
+// stores past it are dropped, with no branch in the instruction stream
+// (0x00020000 is the gfx9-family descriptor word for untyped 32-bit data).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void *base, int rows, int stride, int row_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (rows - 1) * stride + row_bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-template <int BV>
-__device__ __forceinline__ void stage_packed(StateSmem<BV> &sm, int m, uint4 val) {
-    int row, col, boff;
-    packed_piece(m % 320, row, col, boff);
-    *reinterpret_cast<uint4 *>(&sm.P6[m / 320][row * LDE + col]) = val;
+// ds_read_b64_tr_b16 (gfx950): every lane names 8 bytes (four bf16) of LDS;
+// within each group of 16 lanes, element e of lane i of the result is element
+// i % 4 of the 8 bytes named by lane 4e + i / 4 of the group.  So if lane j of
+// group p names elements c0 + 4 (j % 4) .. +3 of row r0 + 4p + j / 4 of a
+// row-major matrix, lane (i, p) receives rows r0 + 4p + e, e = 0..3, of column
+// c0 + i: a transposed 4x16 block, as MFMA fragments and D tiles hold it.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p) {
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(p));
+    return __builtin_bit_cast(bf16x4, r);
 }
 
-template <int BV, bool OUT_BF16>
+// Column, in the permuted token-major layout, of the 8-byte half hh (0, 1)
+// of key-channel segment seg (8 channels, 0..15).
+__device__ __forceinline__ int kperm_col(int seg, int hh) {
+    const int s = seg & 3;
+    return 32 * (seg >> 2) + 8 * ((2 * s + hh) & 3) + 4 * (s >> 1);
+}
+
+template <bool OUT_BF16>
 __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
-    const float *__restrict__ ws, const float *__restrict__ s0, void *__restrict__ o,
+    const char *__restrict__ ws, const float *__restrict__ s0, void *__restrict__ o,
     float *__restrict__ s_final, int T, int H, int NC, int BH, float scale) {
-    constexpr int NS = DV / BV;   // slices per (sequence, head)
-    constexpr int NT = BV / 16;   // 16-column tiles per slice
-    constexpr int VSEG = BV / 8;  // 16-byte segments per token row of the slice
-    __shared__ StateSmem<BV> sm;
+    __shared__ StateSmem sm;
 
     // XCD-aware placement: consecutive workgroup ids go to different XCDs, so
     // the slices of one (sequence, head) get ids that are equal modulo 8 and
@@ -443,194 +399,332 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
     const int b = bh / H, h = bh % H;
     const int j0 = slice * BV;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;  // w = 0..7
+    const int lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
-    const int M = w >> 1, mt = w & 1;        // (token tile, value tile) of this wavefront
-    const bool has_mt = mt < NT;
-
-    // Never written inside the chunk loop, so they stay zero: the upper tiles
-    // of the packed operands and the value columns BV .. 31.
-    for (int idx = tid; idx < 6 * C * LDE; idx += kStateThreads) (&sm.P6[0][0])[idx] = static_cast<__bf16>(0.f);
-    for (int idx = tid; idx < C * LDV; idx += kStateThreads) sm.V[idx] = static_cast<__bf16>(0.f);
-
-    // State slice in registers: wavefront w owns rows 16w + 4lg + r (d_k
-    // tile w), columns j0 + 16nt + lr.
-    f32x4 S[NT];
+    const char *recs = ws + (size_t)bh * NC * kRecBytes;
     const size_t sbase = (size_t)bh * DK * DV;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * w + 4 * lg + r;
-            S[nt][r] = s0 ? s0[sbase + (size_t)row * DV + j0 + 16 * nt + lr] : 0.f;
-        }
-    auto publish_state = [&]() {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            bf16x4 hv, lv;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                hv[r] = static_cast<__bf16>(S[nt][r]);
-                lv[r] = static_cast<__bf16>(S[nt][r] - static_cast<float>(hv[r]));
-            }
-            const int off = (16 * nt + lr) * LDS_ + 16 * w + 4 * lg;
-            *reinterpret_cast<bf16x4 *>(&sm.ST[0][off]) = hv;
-            *reinterpret_cast<bf16x4 *>(&sm.ST[1][off]) = lv;
-        }
-    };
-
-    const bf16x8 sel0 = selector(0, lane), sel1 = selector(1, lane);
-    const bf16x8 selw = (w & 1) ? sel1 : sel0;   // K^T: d_k columns 16w .. 16w+15
-    const bf16x8 selv = mt ? sel1 : sel0;        // V^T: value columns 16mt .. 16mt+15
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    StatePref pf = load_state_chunk<BV>(q, k, v, ws, 0, T, H, NC, b, h, bh, j0, tid);
-    __syncthreads();  // zero fills done before the first staging writes
-    publish_state();
-
-    for (int c = 0; c < NC; ++c) {
-        const int t0 = c * C;
-        const int n = min(C, T - t0);
-        const size_t row0 = ((size_t)b * T + t0) * H + h;
-
-        // ---- stage this chunk from the prefetch registers
-        {
-            const int seg = tid & 15, i0 = tid >> 4;
-            *reinterpret_cast<uint4 *>(&sm.Q[i0 * LDQ + 8 * seg]) = pf.q0;
-            *reinterpret_cast<uint4 *>(&sm.Q[(i0 + 32) * LDQ + 8 * seg]) = pf.q1;
-            *reinterpret_cast<uint4 *>(&sm.K[i0 * LDQ + 8 * seg]) = pf.k0;
-            *reinterpret_cast<uint4 *>(&sm.K[(i0 + 32) * LDQ + 8 * seg]) = pf.k1;
-            if (tid < C * VSEG) *reinterpret_cast<uint4 *>(&sm.V[(tid / VSEG) * LDV + 8 * (tid % VSEG)]) = pf.v;
-            stage_packed(sm, tid, pf.p0);
-            stage_packed(sm, tid + 512, pf.p1);
-            stage_packed(sm, tid + 1024, pf.p2);
-            if (tid + 1536 < 1920) stage_packed(sm, tid + 1536, pf.p3);
+    if (NC == 0) {  // empty sequence: the final state is the initial one
+        if (s_final && w < 2) {
+            const int jt = j0 + 16 * w;
+            for (int i = 0; i < 8; ++i)
+                for (int r = 0; r < 4; ++r) {
+                    const size_t idx = sbase + (size_t)(16 * i + 4 * lg + r) * DV + jt + lr;
+                    s_final[idx] = s0 ? s0[idx] : 0.f;
+                }
         }
-        const float Gl = pf.g;  // G of token `lane`
-        __syncthreads();
-
-        // ---- next chunk's inputs: loads in flight until the next staging
-        if (c + 1 < NC) pf = load_state_chunk<BV>(q, k, v, ws, c + 1, T, H, NC, b, h, bh, j0, tid);
-
-        // ---- K^T of d_k tile w (both token blocks) and V^T of value tile mt
-        bf16x8 KTf[2];
-        {
-            f32x4 tr[4];
-#pragma unroll
-            for (int tau = 0; tau < 4; ++tau) tr[tau] = mma(frag(sm.K, LDQ, 16 * tau, 32 * (w >> 1), lane), selw, zero4);
-            KTf[0] = pack_tok(tr[0], tr[1]);
-            KTf[1] = pack_tok(tr[2], tr[3]);
-        }
-        // ---- W^T = K^T T'^T for d_k tile w (all token tiles), stored token-major
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            f32x4 aw = zero4;
-#pragma unroll
-            for (int kb = 0; kb <= (I >> 1); ++kb) {
-                aw = mma(KTf[kb], frag_tok(sm.P6[0], LDE, 16 * I, kb, lane), aw);
-                aw = mma(KTf[kb], frag_tok(sm.P6[1], LDE, 16 * I, kb, lane), aw);
-            }
-            const bf16x4 wv = {static_cast<__bf16>(aw[0]), static_cast<__bf16>(aw[1]),
-                               static_cast<__bf16>(aw[2]), static_cast<__bf16>(aw[3])};
-            *reinterpret_cast<bf16x4 *>(&sm.W[(16 * I + lr) * LDQ + 16 * w + 4 * lg]) = wv;
-        }
-        // ---- U = T'' V for (token tile M, value tile mt)
-        f32x4 U = zero4;
-        if (has_mt) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if (kb > (M >> 1)) break;
-                const f32x4 t0v = mma(frag(sm.V, LDV, 32 * kb, 0, lane), selv, zero4);
-                const f32x4 t1v = mma(frag(sm.V, LDV, 32 * kb + 16, 0, lane), selv, zero4);
-                const bf16x8 vt = pack_tok(t0v, t1v);
-                U = mma(frag_tok(sm.P6[2], LDE, 16 * M, kb, lane), vt, U);
-                U = mma(frag_tok(sm.P6[3], LDE, 16 * M, kb, lane), vt, U);
-            }
-        }
-        __syncthreads();
-
-        // ---- E = U - W S and the read of the entering state, (M, mt)
-        f32x4 Oa = zero4;
-        const float Gend = __shfl(Gl, C - 1, 64);
-        if (has_mt) {
-            f32x4 P = zero4;
-#pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb) {
-                const bf16x8 aw = frag(sm.W, LDQ, 16 * M, 32 * kb, lane);
-                const bf16x8 aq = frag(sm.Q, LDQ, 16 * M, 32 * kb, lane);
-                const bf16x8 shi = frag(sm.ST[0], LDS_, 16 * mt, 32 * kb, lane);
-                const bf16x8 slo = frag(sm.ST[1], LDS_, 16 * mt, 32 * kb, lane);
-                P = mma(aw, shi, P);
-                P = mma(aw, slo, P);
-                Oa = mma(aq, shi, Oa);
-                Oa = mma(aq, slo, Oa);
-            }
-            bf16x4 eh, el, ph, pl;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float gi = __shfl(Gl, 16 * M + 4 * lg + r, 64);
-                const float e = U[r] - P[r];
-                const float ep = e * __expf(Gend - gi);
-                Oa[r] *= scale * __expf(gi);
-                eh[r] = static_cast<__bf16>(e);
-                el[r] = static_cast<__bf16>(e - static_cast<float>(eh[r]));
-                ph[r] = static_cast<__bf16>(ep);
-                pl[r] = static_cast<__bf16>(ep - static_cast<float>(ph[r]));
-            }
-            const int off = (16 * mt + lr) * LDE + 16 * M + 4 * lg;
-            *reinterpret_cast<bf16x4 *>(&sm.E[0][off]) = eh;
-            *reinterpret_cast<bf16x4 *>(&sm.E[1][off]) = el;
-            *reinterpret_cast<bf16x4 *>(&sm.E[2][off]) = ph;
-            *reinterpret_cast<bf16x4 *>(&sm.E[3][off]) = pl;
-        }
-        __syncthreads();
-
-        // ---- S <- gend S + K^T (Gend E), d_k tile w
-        const float gscale = __expf(Gend);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            f32x4 acc = S[nt] * gscale;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                acc = mma(KTf[kb], frag_tok(sm.E[2], LDE, 16 * nt, kb, lane), acc);
-                acc = mma(KTf[kb], frag_tok(sm.E[3], LDE, 16 * nt, kb, lane), acc);
-            }
-            S[nt] = acc;
-        }
-
-        // ---- O += A E (causal in-chunk reads), (M, mt)
-        if (has_mt) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if (kb > (M >> 1)) break;
-                const bf16x8 ahi = frag_tok(sm.P6[4], LDE, 16 * M, kb, lane);
-                const bf16x8 alo = frag_tok(sm.P6[5], LDE, 16 * M, kb, lane);
-                const bf16x8 ehi = frag_tok(sm.E[0], LDE, 16 * mt, kb, lane);
-                const bf16x8 elo = frag_tok(sm.E[1], LDE, 16 * mt, kb, lane);
-                Oa = mma(ahi, ehi, Oa);
-                Oa = mma(ahi, elo, Oa);
-                Oa = mma(alo, ehi, Oa);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * M + 4 * lg + r;
-                if (i < n) store_out<OUT_BF16>(o, (row0 + (size_t)i * H) * DV + j0 + 16 * mt + lr, Oa[r]);
-            }
-        }
-
-        // every wavefront has read S^T (before the E barrier): publish the new state
-        publish_state();
-        __syncthreads();
+        return;
     }
 
-    if (s_final) {
+    // The two roles run separate loops with the same number of barriers (one
+    // before the first chunk, then one after each of the steps c = 0 .. NC),
+    // so neither role's registers are live in the other's code.  Inside the
+    // loops every global load and store is issued unconditionally (chunk
+    // indices are clamped instead): the compiler's wait counts are exact only
+    // when the number of memory operations between a load and its use does
+    // not depend on a branch; otherwise it waits for all of them.
+    if (w < 2) {
+        // ================= chain wavefront: value columns jt .. jt+15
+        const int jt = j0 + 16 * w;
+        f32x4 S[8];  // S[i][r] = S[16i + 4lg + r][jt + lr]
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * w + 4 * lg + r;
-                s_final[sbase + (size_t)row * DV + j0 + 16 * nt + lr] = S[nt][r];
+            for (int r = 0; r < 4; ++r)
+                S[i][r] = s0 ? s0[sbase + (size_t)(16 * i + 4 * lg + r) * DV + jt + lr] : 0.f;
+        // T'' fragments of even chunks in tA, of odd chunks in tB: each chunk
+        // loads the next one's into the other set (no register copies).
+        bf16x8 tAh[6], tAl[6], tBh[6], tBl[6];
+#pragma unroll
+        for (int f = 0; f < 6; ++f) {
+            tAh[f] = *reinterpret_cast<const bf16x8 *>(recs + kRecTH + f * kFragBytes + lane * 16);
+            tAl[f] = *reinterpret_cast<const bf16x8 *>(recs + kRecTL + f * kFragBytes + lane * 16);
+        }
+        auto step = [&](int c, const bf16x8 *th, const bf16x8 *tl, bf16x8 *thn, bf16x8 *tln)
+                        __attribute__((always_inline)) {
+            const int buf = c & 1;
+            // next chunk's T'' fragments, in flight during this chunk
+            {
+                const char *rn = recs + (size_t)min(c + 1, NC - 1) * kRecBytes;
+#pragma unroll
+                for (int f = 0; f < 6; ++f) {
+                    thn[f] = *reinterpret_cast<const bf16x8 *>(rn + kRecTH + f * kFragBytes + lane * 16);
+                    tln[f] = *reinterpret_cast<const bf16x8 *>(rn + kRecTL + f * kFragBytes + lane * 16);
+                }
             }
+            uint4 *xo = &sm.X[buf][w][0][0];
+            // decays and this wavefront's v columns, read now for the X step
+            f32x4 gam[4], gnd[4];
+            bf16x4 vv[4];
+            const int buf3 = c % 3;
+            const float gs = sm.Gam[buf3][C - 1];  // exp(G_63), the chunk's state decay
+#pragma unroll
+            for (int M = 0; M < 4; ++M) {
+                gam[M] = *reinterpret_cast<const f32x4 *>(&sm.Gam[buf3][16 * M + 4 * lg]);
+                gnd[M] = *reinterpret_cast<const f32x4 *>(&sm.Gend[buf][16 * M + 4 * lg]);
+                // V[16M + 4lg + r][16w + lr], r = 0..3
+                vv[M] = lds_read_tr(&sm.V[buf][(16 * M + 4 * lg + (lr >> 2)) * LDV + 16 * w + 4 * (lr & 3)]);
+            }
+            // S as the B operand over key channels (hi, lo)
+            bf16x8 SH[4], SL[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                pair_split(S[2 * kb], S[2 * kb + 1], SH[kb], SL[kb]);
+                xo[kb * 64 + lane] = *reinterpret_cast<const uint4 *>(&SH[kb]);
+                xo[(4 + kb) * 64 + lane] = *reinterpret_cast<const uint4 *>(&SL[kb]);
+            }
+            // P = K S (token tile M, this wavefront's 16 value columns); the
+            // fragments of the next 32 key channels are read during the
+            // products of the current ones
+            f32x4 P[4] = {zero4, zero4, zero4, zero4};
+            const __bf16 *sK = sm.K[buf];
+            bf16x8 ka[2][4];
+#pragma unroll
+            for (int M = 0; M < 4; ++M) ka[0][M] = *reinterpret_cast<const bf16x8 *>(&sK[(16 * M + lr) * LDK + 8 * lg]);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int cur = kb & 1;
+                if (kb + 1 < 4) {
+#pragma unroll
+                    for (int M = 0; M < 4; ++M)
+                        ka[cur ^ 1][M] = *reinterpret_cast<const bf16x8 *>(&sK[(16 * M + lr) * LDK + 32 * (kb + 1) + 8 * lg]);
+                }
+#pragma unroll
+                for (int M = 0; M < 4; ++M) P[M] = mma(ka[cur][M], SH[kb], P[M]);
+#pragma unroll
+                for (int M = 0; M < 4; ++M) P[M] = mma(ka[cur][M], SL[kb], P[M]);
+            }
+            // X = V - Gam P, rows 16M + 4lg + r
+            f32x4 Xv[4];
+#pragma unroll
+            for (int M = 0; M < 4; ++M)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Xv[M][r] = static_cast<float>(vv[M][r]) - gam[M][r] * P[M][r];
+            bf16x8 XH[2], XL[2];
+            pair_split(Xv[0], Xv[1], XH[0], XL[0]);
+            pair_split(Xv[2], Xv[3], XH[1], XL[1]);
+            // k^T fragments (key-channel tile i, token block kb) for the update,
+            // read transposed from the token-major k: term e of lane group lg is
+            // token 32kb + kperm(lg, e), key channel 16i + lr.  Tile 0 now.
+            auto kt_frag = [&](int i, int kb) {
+                const int col = 32 * (i >> 1) + 8 * (lr & 3) + 4 * (i & 1);  // 16i + 4(lr%4), permuted
+                const int row = 32 * kb + 4 * lg + (lr >> 2);
+                const bf16x4 a = lds_read_tr(&sK[row * LDK + col]);
+                const bf16x4 c = lds_read_tr(&sK[(row + 16) * LDK + col]);
+                return bf16x8{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+            };
+            bf16x8 kt[2][2];
+            kt[0][0] = kt_frag(0, 0);
+            kt[0][1] = kt_frag(0, 1);
+            // E = T'' X
+            f32x4 E[4];
+#pragma unroll
+            for (int M = 0; M < 4; ++M) {
+                E[M] = zero4;
+#pragma unroll
+                for (int kb = 0; kb <= (M >> 1); ++kb) {
+                    const int f = lower_frag(M, kb);
+                    E[M] = mma(th[f], XH[kb], E[M]);
+                    E[M] = mma(th[f], XL[kb], E[M]);
+                    E[M] = mma(tl[f], XH[kb], E[M]);
+                }
+            }
+            // E to the helper; Gend E as the update's B operand
+            f32x4 Ep[4];
+#pragma unroll
+            for (int M = 0; M < 4; ++M) {
+                xo[(8 + M) * 64 + lane] = *reinterpret_cast<const uint4 *>(&E[M]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Ep[M][r] = E[M][r] * gnd[M][r];
+            }
+            bf16x8 PH[2], PL[2];
+            pair_split(Ep[0], Ep[1], PH[0], PL[0]);
+            pair_split(Ep[2], Ep[3], PH[1], PL[1]);
+            // S <- gend S + K^T (Gend E), key-channel tile i (tile i+1's
+            // fragments are read during tile i's products)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int cur = i & 1;
+                if (i + 1 < 8) {
+                    kt[cur ^ 1][0] = kt_frag(i + 1, 0);
+                    kt[cur ^ 1][1] = kt_frag(i + 1, 1);
+                }
+                f32x4 acc = S[i] * gs;
+                acc = mma(kt[cur][0], PH[0], acc);
+                acc = mma(kt[cur][0], PL[0], acc);
+                acc = mma(kt[cur][1], PH[1], acc);
+                acc = mma(kt[cur][1], PL[1], acc);
+                S[i] = acc;
+            }
+        };
+        barrier_lds();
+        int c = 0;
+        for (; c + 1 < NC; c += 2) {
+            step(c, tAh, tAl, tBh, tBl);
+            barrier_lds();
+            step(c + 1, tBh, tBl, tAh, tAl);
+            barrier_lds();
+        }
+        if (c < NC) {
+            step(c, tAh, tAl, tBh, tBl);
+            barrier_lds();
+        }
+        barrier_lds();  // step NC: the helpers finish the last chunk's outputs
+        if (s_final) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    s_final[sbase + (size_t)(16 * i + 4 * lg + r) * DV + jt + lr] = S[i][r];
+        }
+    } else {
+        // ================= helper wavefront: stages chunk c+1, outputs of chunk c-1
+        const int vt = w - 2;
+        const int jt = j0 + 16 * vt;
+        const int ht = tid - 128;  // 0..127
+        // Rows past the end of a partial last chunk read as zero (buffer
+        // bounds); T'' and A are zero in those rows and columns anyway.
+        uint4 kreg[8], qreg[8], vreg[2];
+        float gam_reg, gnd_reg;
+        const size_t head0 = (size_t)b * T * H + h;  // row of token 0 of this head
+        const int qk_stride = H * DK * 2, v_stride = H * DV * 2;
+        // byte offsets, inside a chunk, of this thread's q/k and v pieces
+        int qk_off[8], v_off[2];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) qk_off[u] = (8 * (ht >> 4) + u) * qk_stride + 16 * (ht & 15);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) v_off[u] = (2 * (ht >> 2) + u) * v_stride + 2 * (j0 + 8 * (ht & 3));
+        auto load_stage = [&](int cc) {  // chunk cc's q, k, v slice and G into registers
+            const int t0 = cc * C;
+            const int n = min(C, T - t0);
+            const size_t row0 = head0 + (size_t)t0 * H;
+            const auto rk = rows_rsrc(k + row0 * DK, n, qk_stride, DK * 2);
+            const auto rq = rows_rsrc(q + row0 * DK, n, qk_stride, DK * 2);
+            const auto rv = rows_rsrc(v + row0 * DV, n, v_stride, DV * 2);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                kreg[u] = buf_ld16(rk, qk_off[u]);
+                qreg[u] = buf_ld16(rq, qk_off[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) vreg[u] = buf_ld16(rv, v_off[u]);
+            const char *rec = recs + (size_t)cc * kRecBytes;
+            gam_reg = reinterpret_cast<const float *>(rec + kRecGam)[ht & 63];
+            gnd_reg = reinterpret_cast<const float *>(rec + kRecGend)[ht & 63];
+        };
+        auto store_stage = [&](int cc) {  // registers -> LDS buffers of chunk cc
+            const int buf = cc & 1, buf3 = cc % 3;
+            const int seg = ht & 15, tg = ht >> 4;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = 8 * tg + u;
+                const uint2 *kh = reinterpret_cast<const uint2 *>(&kreg[u]);
+                const uint2 *qh = reinterpret_cast<const uint2 *>(&qreg[u]);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int col = kperm_col(seg, hh);
+                    *reinterpret_cast<uint2 *>(&sm.K[buf][i * LDK + col]) = kh[hh];
+                    *reinterpret_cast<uint2 *>(&sm.Q[buf3][i * LDK + col]) = qh[hh];
+                }
+            }
+            {
+                const int sv = ht & 3, tq = ht >> 2;
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    *reinterpret_cast<uint4 *>(&sm.V[buf][(2 * tq + u) * LDV + 8 * sv]) = vreg[u];
+            }
+            if (ht < C) {
+                sm.Gam[buf3][ht] = gam_reg;
+                sm.Gend[buf][ht] = gnd_reg;
+            }
+        };
+        bf16x8 ah[6], al[6];
+        auto load_out_ops = [&](int cc) {  // chunk cc's A fragments
+            const char *rec = recs + (size_t)cc * kRecBytes;
+#pragma unroll
+            for (int f = 0; f < 6; ++f) {
+                ah[f] = *reinterpret_cast<const bf16x8 *>(rec + kRecAH + f * kFragBytes + lane * 16);
+                al[f] = *reinterpret_cast<const bf16x8 *>(rec + kRecAL + f * kFragBytes + lane * 16);
+            }
+        };
+        // outputs of chunk cp: O = scale Gam (Q S) + A E, with S (hi, lo) and E
+        // from the chain; rows past the end of the sequence are dropped by the
+        // buffer bounds
+        auto outputs = [&](int cp) __attribute__((always_inline)) {
+            const int buf3 = cp % 3;
+            const uint4 *xi = &sm.X[cp & 1][vt][0][0];
+            const __bf16 *sQ = sm.Q[buf3];
+            f32x4 O[4] = {zero4, zero4, zero4, zero4};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                bf16x8 sh, sl, qa[4];
+                *reinterpret_cast<uint4 *>(&sh) = xi[kb * 64 + lane];
+                *reinterpret_cast<uint4 *>(&sl) = xi[(4 + kb) * 64 + lane];
+#pragma unroll
+                for (int M = 0; M < 4; ++M) qa[M] = *reinterpret_cast<const bf16x8 *>(&sQ[(16 * M + lr) * LDK + 32 * kb + 8 * lg]);
+#pragma unroll
+                for (int M = 0; M < 4; ++M) O[M] = mma(qa[M], sh, O[M]);
+#pragma unroll
+                for (int M = 0; M < 4; ++M) O[M] = mma(qa[M], sl, O[M]);
+            }
+            f32x4 E[4];
+            bf16x8 eh[2], el[2];
+#pragma unroll
+            for (int M = 0; M < 4; ++M) {
+                *reinterpret_cast<uint4 *>(&E[M]) = xi[(8 + M) * 64 + lane];
+                const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&sm.Gam[buf3][16 * M + 4 * lg]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) O[M][r] *= scale * g4[r];
+            }
+            pair_split(E[0], E[1], eh[0], el[0]);
+            pair_split(E[2], E[3], eh[1], el[1]);
+#pragma unroll
+            for (int M = 0; M < 4; ++M)
+#pragma unroll
+                for (int kb = 0; kb <= (M >> 1); ++kb) {
+                    const int f = lower_frag(M, kb);
+                    O[M] = mma(ah[f], eh[kb], O[M]);
+                    O[M] = mma(ah[f], el[kb], O[M]);
+                    O[M] = mma(al[f], eh[kb], O[M]);
+                }
+            const int t0 = cp * C;
+            const int n = min(C, T - t0);
+            const size_t row0 = head0 + (size_t)t0 * H;
+            constexpr int es = OUT_BF16 ? 2 : 4;
+            const auto ro = rows_rsrc(static_cast<char *>(o) + row0 * DV * es, n, H * DV * es, DV * es);
+#pragma unroll
+            for (int M = 0; M < 4; ++M)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int off = ((16 * M + 4 * lg + r) * H * DV + jt + lr) * es;
+                    if constexpr (OUT_BF16) {
+                        const __bf16 hv = static_cast<__bf16>(O[M][r]);
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hv), ro, off, 0, 0);
+                    } else {
+                        const float val = O[M][r];
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, off, 0, 0);
+                    }
+                }
+        };
+        // step 0: stage chunk 0 (and 1); step c >= 1: outputs of chunk c-1
+        load_stage(0);
+        store_stage(0);
+        load_stage(min(1, NC - 1));
+        barrier_lds();
+        if (NC > 1) store_stage(1);
+        load_stage(min(2, NC - 1));
+        load_out_ops(0);
+        barrier_lds();
+        for (int c = 1; c < NC; ++c) {
+            if (c + 1 < NC) store_stage(c + 1);
+            load_stage(min(c + 2, NC - 1));
+            outputs(c - 1);
+            load_out_ops(c);
+            barrier_lds();
+        }
+        outputs(NC - 1);
+        barrier_lds();
     }
 }
 
@@ -638,19 +732,20 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
 template <bool KZ>
 hipError_t launch_intra(const ChunkArgs &a) {
     const unsigned grid = (unsigned)((size_t)a.B * a.H * a.NC);
+    if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((intra_matrix_kernel<KZ>), dim3(grid), dim3(kIntraThreads), 0, a.stream,
                        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), a.g, a.beta, a.T, a.H,
-                       a.NC, a.eps, a.scale, static_cast<float *>(a.ws));
+                       a.NC, a.eps, a.scale, static_cast<char *>(a.ws));
     return hipGetLastError();
 }
 
-template <int BV, bool OB>
+template <bool OB>
 hipError_t launch_state(const ChunkArgs &a) {
     const int BH = a.B * a.H;
-    const unsigned grid = (unsigned)(BH * (DV / BV));
-    hipLaunchKernelGGL((state_matrix_kernel<BV, OB>), dim3(grid), dim3(kStateThreads), 0, a.stream,
+    const unsigned grid = (unsigned)(BH * NS);
+    hipLaunchKernelGGL((state_matrix_kernel<OB>), dim3(grid), dim3(kStateThreads), 0, a.stream,
                        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k),
-                       static_cast<const __bf16 *>(a.v), static_cast<const float *>(a.ws), a.s0, a.o, a.s_final,
+                       static_cast<const __bf16 *>(a.v), static_cast<const char *>(a.ws), a.s0, a.o, a.s_final,
                        a.T, a.H, a.NC, BH, a.scale);
     return hipGetLastError();
 }
@@ -658,23 +753,19 @@ hipError_t launch_state(const ChunkArgs &a) {
 }  // namespace
 
 size_t chunk_matrix_workspace_bytes(int B, int H, int NC, int, int, bool) {
-    return (size_t)B * H * NC * kRecFloats * sizeof(float);
+    return (size_t)B * H * NC * kRecBytes;
 }
 
 bool chunk_matrix_supported(int Dk, int Dv, bool qkv_bf16, bool per_channel) {
     return qkv_bf16 && Dk == DK && Dv == DV && !per_channel;
 }
 
-// Slice width of the state kernel: 32 value columns when that already gives
-// one workgroup per compute unit, else 16 (twice the workgroups).
 hipError_t launch_chunk_matrix(const ChunkArgs &a, int stage) {
     if (stage != 1) {
         const hipError_t e = a.kaczmarz ? launch_intra<true>(a) : launch_intra<false>(a);
         if (e != hipSuccess || stage == 0) return e;
     }
-    const bool wide = (long)a.B * a.H * (DV / 32) >= 256;
-    if (wide) return a.o_bf16 ? launch_state<32, true>(a) : launch_state<32, false>(a);
-    return a.o_bf16 ? launch_state<16, true>(a) : launch_state<16, false>(a);
+    return a.o_bf16 ? launch_state<true>(a) : launch_state<false>(a);
 }
 
 }  // namespace gdr

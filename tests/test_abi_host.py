@@ -128,9 +128,10 @@ def test_matrix_algo_support_and_workspace():
     assert _ws(_desc(qkv_dtype=torch.float32, algo="matrix"))[0] == E["GDR_E_UNSUPPORTED"]
     assert _ws(_desc(Dk=64, Dv=64, algo="matrix"))[0] == E["GDR_E_UNSUPPORTED"]
     assert _ws(_desc(per_channel=True, algo="matrix"))[0] == E["GDR_E_UNSUPPORTED"]
-    # matrix path, per chunk: six packed bf16 matrices of ten 16x16 tiles, 64 fp32 G
+    # matrix path, per chunk: T'' and A, each hi and lo, as six 1 KiB MFMA operand
+    # fragments, then two fp32 decay factors per token
     nc = (100 + 63) // 64
-    assert _ws(_desc(algo="matrix")) == (0, 2 * 3 * nc * (6 * 10 * 256 * 2 + 64 * 4))
+    assert _ws(_desc(algo="matrix")) == (0, 2 * 3 * nc * (4 * 6 * 1024 + 2 * 64 * 4))
     assert _ws(_desc(algo="auto")) == _ws(_desc(algo="matrix"))
     rc, n = _ws(_desc(per_channel=True, algo="auto"))   # auto falls back to the vector path
     assert rc == 0 and n > 0
