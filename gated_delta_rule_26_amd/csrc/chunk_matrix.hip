@@ -63,20 +63,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int C = kChunk;      // 64 tokens per chunk
 constexpr int DK = 128;
 constexpr int DV = 128;
-constexpr int LDQ = DK + 8;    // bf16 row stride of q, k in the intra kernel (token-major)
-constexpr int LDF = C + 4;     // fp32 row stride of R, T, A
 
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mma32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// 16x32 fragment of a bf16 matrix stored with the reduction index contiguous
-// (rows r0 .. r0+15, reduction k0 .. k0+31, natural order).
-__device__ __forceinline__ bf16x8 frag(const __bf16 *base, int ld, int r0, int k0, int lane) {
-    return *reinterpret_cast<const bf16x8 *>(base + (r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
 }
 
 // Index, inside a 32-block, of term e (0..7) of lane group p (0..3).
@@ -92,25 +84,6 @@ __device__ __forceinline__ void pair_split(f32x4 t0, f32x4 t1, bf16x8 &hi, bf16x
         hi[4 + r] = static_cast<__bf16>(t1[r]);
         lo[4 + r] = static_cast<__bf16>(t1[r] - static_cast<float>(hi[4 + r]));
     }
-}
-
-// Off-diagonal 16x16 block of the unit lower-triangular inverse, by one
-// wavefront on fp32 MFMA:  T_IJ = -T_II * sum_{M=J}^{I-1} R_IM T_MJ.
-// Reduction index k = 4 (lane/16) + s at step s, so the partial product P
-// (a D tile) is the B operand of the second product without any exchange.
-__device__ __forceinline__ void inverse_block(float *sT, const float *sR, int I, int J, int lane) {
-    const int lr = lane & 15, lg = lane >> 4;
-    f32x4 P = {0.f, 0.f, 0.f, 0.f};
-    for (int M = J; M < I; ++M) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            P = mma32(sR[(16 * I + lr) * LDF + 16 * M + 4 * lg + s], sT[(16 * M + 4 * lg + s) * LDF + 16 * J + lr], P);
-    }
-    f32x4 out = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) out = mma32(sT[(16 * I + lr) * LDF + 16 * I + 4 * lg + s], P[s], out);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * lg + r) * LDF + 16 * J + lr] = -out[r];
 }
 
 // ---- per-chunk workspace record
@@ -131,104 +104,141 @@ __host__ __device__ constexpr int lower_frag(int M, int kb) { return M < 2 ? M :
 __host__ __device__ constexpr int frag_M(int f) { return f < 2 ? f : 2 + ((f - 2) >> 1); }
 __host__ __device__ constexpr int frag_kb(int f) { return f < 2 ? 0 : (f - 2) & 1; }
 
-__device__ __forceinline__ float sumsq8(uint4 x) {
-    const __bf16 *e = reinterpret_cast<const __bf16 *>(&x);
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s += static_cast<float>(e[i]) * static_cast<float>(e[i]);
-    return s;
+// Raw buffer resource over `rows` rows of `row_bytes` bytes spaced `stride`
+// bytes apart, starting at `base`: loads past the last row return zero and
+// stores past it are dropped, with no branch in the instruction stream
+// (0x00020000 is the gfx9-family descriptor word for untyped 32-bit data).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void *base, int rows, int stride, int row_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (rows - 1) * stride + row_bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
 // ============================================================ intra kernel
 constexpr int kIntraThreads = 256;
+constexpr int LT = 20;                  // fp32 row stride of a 16x16 tile in LDS (16-byte aligned rows)
+constexpr int LQK = DK + 8;             // bf16 row stride of the staged q, k (token-major)
+constexpr int kTile = 16 * LT;          // floats per tile
+__host__ __device__ constexpr int tile_id(int I, int J) { return I * (I + 1) / 2 + J; }  // lower tiles 0..9
+__host__ __device__ constexpr int offdiag_id(int I, int J) { return I * (I - 1) / 2 + J; }  // J < I: 0..5
 
+// q and k are staged token-major for the K K^T and Q K^T products; the same
+// space then holds the lower 16x16 tiles of R, T and A.  T's diagonal blocks
+// overwrite R's (R_II is not needed once T_II is known; R_IJ with J < I is).
 struct alignas(16) IntraSmem {
     union {
-        __bf16 Q[C * LDQ];        // q token-major ...
-        float T[C * LDF];         // ... then (I + R)^{-1}
-    } qt;
-    union {
-        __bf16 K[C * LDQ];        // k token-major ...
-        float A[C * LDF];         // ... then the causal read matrix
-    } ka;
-    float R[C * LDF];
-    float kk[C];
-    float cb[C];                  // beta_j
+        struct {
+            __bf16 Q[C * LQK];
+            __bf16 K[C * LQK];
+        } qk;
+        struct {
+            float R[10 * kTile];
+            float Toff[6 * kTile];
+            float A[10 * kTile];
+        } t;
+    } u;
+    float G[C];                 // in-chunk cumulative log-decay
+    float eta[C];               // beta, or eta for the Kaczmarz step size (0 past the end)
+    float kk[C];                // |k_i|^2 (Kaczmarz only)
 };
 
 template <bool KZ>
-__global__ __launch_bounds__(kIntraThreads) void intra_matrix_kernel(
+__global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const float *__restrict__ g,
-    const float *__restrict__ beta, int T, int H, int NC, float eps, float scale, char *__restrict__ ws) {
+    const float *__restrict__ beta, int T, int H, int NC, int total, float eps, float scale,
+    char *__restrict__ ws) {
     __shared__ IntraSmem sm;
-    const int ci = blockIdx.x;  // (b*H + h)*NC + c
+    const int qk_stride = H * DK * 2;
+    auto Tb = [&](int I, int J) -> float * {  // block (I, J) of T, J <= I
+        return I == J ? &sm.u.t.R[tile_id(I, I) * kTile] : &sm.u.t.Toff[offdiag_id(I, J) * kTile];
+    };
+    const int seg = threadIdx.x & 15, i0 = threadIdx.x >> 4;
+    const int lane0 = threadIdx.x & 63;
+
+    // Persistent: the workgroup takes chunks ci = blockIdx.x + k gridDim.x
+    // ((b*H + h)*NC + c) and loads the next one's q, k and gates into
+    // registers while it computes the current one.
+    uint4 qv[4], kv[4];
+    float gv, ev;
+    auto prefetch = [&](int cj) {
+        const int cc = cj % NC, bhj = cj / NC;
+        const int tt = cc * C, nn = min(C, T - tt);
+        const size_t r0 = ((size_t)(bhj / H) * T + tt) * H + bhj % H;
+        const auto rk = rows_rsrc(k + r0 * DK, nn, qk_stride, DK * 2);
+        const auto rq = rows_rsrc(q + r0 * DK, nn, qk_stride, DK * 2);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int off = (i0 + 16 * it) * qk_stride + 16 * seg;
+            qv[it] = buf_ld16(rq, off);
+            kv[it] = buf_ld16(rk, off);
+        }
+        gv = g[r0 + (size_t)min(lane0, nn - 1) * H];
+        ev = beta[r0 + (size_t)min(lane0, nn - 1) * H];
+    };
+    prefetch(min((int)blockIdx.x, total - 1));
+    for (int ci = blockIdx.x; ci < total; ci += gridDim.x) {
+    // The thread index passes through an empty asm each chunk, so the many
+    // per-lane LDS addresses below are recomputed per chunk instead of being
+    // hoisted out of the loop and kept live (which would spill).
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
     const int c = ci % NC;
     const int bh = ci / NC;
     const int b = bh / H, h = bh % H;
     const int t0 = c * C;
     const int n = min(C, T - t0);
     const size_t row0 = ((size_t)b * T + t0) * H + h;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
     char *recb = ws + (size_t)ci * kRecBytes;
+    __syncthreads();  // the previous chunk's tiles are no longer read
 
-    // ---- stage q, k token-major; gates of token `lane` in every wavefront
-    {
-        const int seg = tid & 15, i0 = tid >> 4;
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int i = i0 + 16 * it;
-            // rows past a partial last chunk repeat its last row: finite, and
-            // their beta (hence R's rows, T''s columns) is zero
-            const size_t off = (row0 + (size_t)min(i, n - 1) * H) * DK + 8 * seg;
-            const uint4 qv = *reinterpret_cast<const uint4 *>(q + off);
-            const uint4 kv = *reinterpret_cast<const uint4 *>(k + off);
-            *reinterpret_cast<uint4 *>(&sm.qt.Q[i * LDQ + 8 * seg]) = qv;
-            *reinterpret_cast<uint4 *>(&sm.ka.K[i * LDQ + 8 * seg]) = kv;
-            if constexpr (KZ) {
-                float s2 = sumsq8(kv);
-                s2 += __shfl_xor(s2, 1, 64);
-                s2 += __shfl_xor(s2, 2, 64);
-                s2 += __shfl_xor(s2, 4, 64);
-                s2 += __shfl_xor(s2, 8, 64);
-                if (seg == 0) sm.kk[i] = s2;
-            }
-        }
-    }
-    float Gl = g[row0 + (size_t)min(lane, n - 1) * H];
-    if (lane >= n) Gl = 0.f;
+    // ---- gates of token `lane`: cumulative log-decay and beta (eta)
+    float Gl = lane < n ? gv : 0.f;
+    const float El = lane < n ? ev : 0.f;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const float up = __shfl_up(Gl, off, 64);
         if (lane >= off) Gl += up;
     }
-    float given = beta[row0 + (size_t)min(lane, n - 1) * H];
-    if (lane >= n) given = 0.f;
-    __syncthreads();
-    float Bl = given;
-    if constexpr (KZ) Bl = lane < n ? given / (sm.kk[lane] + eps) : 0.f;
     if (w == 0) {
+        sm.G[lane] = Gl;
+        sm.eta[lane] = El;
         reinterpret_cast<float *>(recb + kRecGam)[lane] = __expf(Gl);
         reinterpret_cast<float *>(recb + kRecGend)[lane] = __expf(__shfl(Gl, C - 1, 64) - Gl);
-        sm.cb[lane] = Bl;
     }
 
-    // ---- K K^T -> R (wavefronts 0, 1) and Q K^T (2, 3) on the lower tiles:
-    // even wavefronts take row blocks {0, 3}, odd ones {1, 2}
+    // ---- stage q, k token-major (rows past the chunk read as zero), then
+    // start loading the next chunk
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        *reinterpret_cast<uint4 *>(&sm.u.qk.Q[(i0 + 16 * it) * LQK + 8 * seg]) = qv[it];
+        *reinterpret_cast<uint4 *>(&sm.u.qk.K[(i0 + 16 * it) * LQK + 8 * seg]) = kv[it];
+    }
+    prefetch(min(ci + (int)gridDim.x, total - 1));
+    __syncthreads();
+
+    // ---- K K^T (wavefronts 0, 1) and Q K^T (2, 3) on the lower tiles: even
+    // wavefronts take row blocks {0, 3}, odd ones {1, 2}
+    const int Ia = (w & 1) ? 1 : 0, Ib = (w & 1) ? 2 : 3;
     f32x4 acc[5];
 #pragma unroll
     for (int t = 0; t < 5; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-        const __bf16 *X = w >= 2 ? sm.qt.Q : sm.ka.K;
-        const int Ia = (w & 1) ? 1 : 0, Ib = (w & 1) ? 2 : 3;
+        const __bf16 *X = w >= 2 ? sm.u.qk.Q : sm.u.qk.K;
+        const __bf16 *Kt = sm.u.qk.K;
+        auto fr = [&](const __bf16 *base, int row, int kb) {
+            return *reinterpret_cast<const bf16x8 *>(base + row * LQK + 32 * kb + 8 * lg);
+        };
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
-            const bf16x8 xa = frag(X, LDQ, 16 * Ia, 32 * kb, lane);
-            const bf16x8 xb = frag(X, LDQ, 16 * Ib, 32 * kb, lane);
-            const bf16x8 k0 = frag(sm.ka.K, LDQ, 0, 32 * kb, lane);
-            const bf16x8 k1 = frag(sm.ka.K, LDQ, 16, 32 * kb, lane);
-            const bf16x8 k2 = frag(sm.ka.K, LDQ, 32, 32 * kb, lane);
+            const bf16x8 xa = fr(X, 16 * Ia + lr, kb);
+            const bf16x8 xb = fr(X, 16 * Ib + lr, kb);
+            const bf16x8 k0 = fr(Kt, lr, kb);
+            const bf16x8 k1 = fr(Kt, 16 + lr, kb);
+            const bf16x8 k2 = fr(Kt, 32 + lr, kb);
             if (w & 1) {  // tiles (1,0) (1,1) (2,0) (2,1) (2,2)
                 acc[0] = mma(xa, k0, acc[0]);
                 acc[1] = mma(xa, k1, acc[1]);
@@ -236,7 +246,7 @@ __global__ __launch_bounds__(kIntraThreads) void intra_matrix_kernel(
                 acc[3] = mma(xb, k1, acc[3]);
                 acc[4] = mma(xb, k2, acc[4]);
             } else {      // tiles (0,0) (3,0) (3,1) (3,2) (3,3)
-                const bf16x8 k3 = frag(sm.ka.K, LDQ, 48, 32 * kb, lane);
+                const bf16x8 k3 = fr(Kt, 48 + lr, kb);
                 acc[0] = mma(xa, k0, acc[0]);
                 acc[1] = mma(xb, k0, acc[1]);
                 acc[2] = mma(xb, k1, acc[2]);
@@ -245,79 +255,133 @@ __global__ __launch_bounds__(kIntraThreads) void intra_matrix_kernel(
             }
         }
     }
-    // decay (and beta for R) applied in fp32; R to LDS now, A after the barrier
+    auto tileI = [&](int t) { return (w & 1) ? (t < 2 ? 1 : 2) : (t < 1 ? 0 : 3); };
+    auto tileJ = [&](int t) { return (w & 1) ? (t < 2 ? t : t - 2) : (t < 1 ? 0 : t - 1); };
+    if constexpr (KZ) {  // |k_i|^2 is the diagonal of K K^T
+        if (w < 2) {
 #pragma unroll
-    for (int t = 0; t < 5; ++t) {
-        const int I = (w & 1) ? (t < 2 ? 1 : 2) : (t < 1 ? 0 : 3);
-        const int J = (w & 1) ? (t < 2 ? t : t - 2) : (t < 1 ? 0 : t - 1);
-        const int j = 16 * J + lr;
-        const float gj = __shfl(Gl, j, 64);
+            for (int t = 0; t < 5; ++t) {
+                if (tileI(t) != tileJ(t)) continue;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * I + 4 * lg + r;
-            const float gi = __shfl(Gl, i, 64);
-            const float dec = j <= i ? __expf(gi - gj) : 0.f;
-            if (w >= 2) {
-                acc[t][r] = scale * dec * acc[t][r];
-            } else {
-                const float bi = __shfl(Bl, i, 64);
-                sm.R[i * LDF + j] = j < i ? bi * dec * acc[t][r] : 0.f;
+                for (int r = 0; r < 4; ++r)
+                    if (lr == 4 * lg + r) sm.kk[16 * tileI(t) + lr] = acc[t][r];
             }
         }
     }
-    __syncthreads();  // R complete; q and k no longer read: their space now holds T and A
+    __syncthreads();  // G, eta (and |k|^2) in LDS; q and k no longer read
 
-    if (w >= 2) {
+    // ---- decay (and beta for R) applied in fp32; R and A tiles to LDS
 #pragma unroll
-        for (int t = 0; t < 5; ++t) {
-            const int I = (w & 1) ? (t < 2 ? 1 : 2) : (t < 1 ? 0 : 3);
-            const int J = (w & 1) ? (t < 2 ? t : t - 2) : (t < 1 ? 0 : t - 1);
+    for (int t = 0; t < 5; ++t) {
+        const int I = tileI(t), J = tileJ(t);
+        const int j = 16 * J + lr;
+        const float gj = sm.G[j];
+        const f32x4 gi4 = *reinterpret_cast<const f32x4 *>(&sm.G[16 * I + 4 * lg]);
+        float *dst = (w >= 2 ? sm.u.t.A : sm.u.t.R) + tile_id(I, J) * kTile;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm.ka.A[(16 * I + 4 * lg + r) * LDF + 16 * J + lr] = acc[t][r];
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * I + 4 * lg + r;
+            const float dec = j <= i ? __expf(gi4[r] - gj) : 0.f;
+            float val;
+            if (w >= 2) {
+                val = scale * dec * acc[t][r];
+            } else {
+                float bi = sm.eta[i];
+                if constexpr (KZ) bi = i < n ? bi / (sm.kk[i] + eps) : 0.f;
+                val = j < i ? bi * dec * acc[t][r] : 0.f;
+            }
+            dst[(4 * lg + r) * LT + lr] = val;
         }
     }
+    __syncthreads();
 
-    // ---- T = (I + R)^{-1}: diagonal 16x16 blocks by forward substitution,
-    // then three levels of off-diagonal blocks on fp32 MFMA
+    // ---- T = (I + R)^{-1}: diagonal 16x16 blocks by forward substitution
+    // (one column per lane), then three levels of off-diagonal blocks on
+    // fp32 MFMA:  T_IJ = -T_II sum_{M=J}^{I-1} R_IM T_MJ
     if (lane < 16) {
-        const int cc = lane, base = 16 * w;
+        const int cc = lane;
+        float *blk = &sm.u.t.R[tile_id(w, w) * kTile];
         float xcol[16];
+        f32x4 row[2][4];  // R row i (broadcast to every lane), the next row read ahead
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) row[0][q4] = *reinterpret_cast<const f32x4 *>(&blk[4 * q4]);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            float accv = i == cc ? 1.f : 0.f;
+            const int cur = i & 1;
+            if (i + 1 < 16) {
 #pragma unroll
-            for (int m = 0; m < i; ++m) accv -= sm.R[(base + i) * LDF + base + m] * xcol[m];
-            xcol[i] = i < cc ? 0.f : accv;
+                for (int q4 = 0; q4 < 4; ++q4)
+                    if (4 * q4 < i + 1) row[cur ^ 1][q4] = *reinterpret_cast<const f32x4 *>(&blk[(i + 1) * LT + 4 * q4]);
+            }
+            float a0 = i == cc ? 1.f : 0.f, a1 = 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) {
+                if (m & 1) a1 -= row[cur][m >> 2][m & 3] * xcol[m];
+                else a0 -= row[cur][m >> 2][m & 3] * xcol[m];
+            }
+            xcol[i] = i < cc ? 0.f : a0 + a1;
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sm.qt.T[(base + i) * LDF + base + cc] = xcol[i];
+        for (int i = 0; i < 16; ++i) blk[i * LT + cc] = xcol[i];
     }
     __syncthreads();
-    if (w < 3) inverse_block(sm.qt.T, sm.R, w + 1, w, lane);
+    auto inverse_tile = [&](int I, int J) {
+        f32x4 P = {0.f, 0.f, 0.f, 0.f};
+        for (int M = J; M < I; ++M) {
+            const float *Rt = &sm.u.t.R[tile_id(I, M) * kTile];
+            const float *Tt = Tb(M, J);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) P = mma32(Rt[lr * LT + 4 * lg + s], Tt[(4 * lg + s) * LT + lr], P);
+        }
+        const float *Tii = Tb(I, I);
+        f32x4 out = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) out = mma32(Tii[lr * LT + 4 * lg + s], P[s], out);
+        float *dst = Tb(I, J);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(4 * lg + r) * LT + lr] = -out[r];
+    };
+    if (w < 3) inverse_tile(w + 1, w);
     __syncthreads();
-    if (w < 2) inverse_block(sm.qt.T, sm.R, w + 2, w, lane);
+    if (w < 2) inverse_tile(w + 2, w);
     __syncthreads();
-    if (w == 0) inverse_block(sm.qt.T, sm.R, 3, 0, lane);
+    if (w == 0) inverse_tile(3, 0);
     __syncthreads();
 
-    // ---- operand fragments: T'' = T Diag(beta) and A, lower triangle only
-    // (entries above the diagonal are written as zero), bf16 hi + lo
+    // ---- operand fragments: T'' = T Diag(beta) and A, lower triangle only,
+    // bf16 hi + lo.  Terms 0..3 of lane group p are tile columns 4p .. 4p+3
+    // of tile (M, 2kb), terms 4..7 the same columns of tile (M, 2kb + 1).
     for (int u = tid; u < 2 * 6 * 64; u += kIntraThreads) {
         const int mat = u / 384, f = (u >> 6) % 6, l = u & 63;
-        const int row = 16 * frag_M(f) + (l & 15), p = l >> 4, c0 = 32 * frag_kb(f);
+        const int M = frag_M(f), kb = frag_kb(f), rr = l & 15, p = l >> 4;
         bf16x8 hv, lv;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int col = c0 + kperm(p, e);
-            float x = 0.f;
-            if (col <= row) x = mat == 0 ? sm.qt.T[row * LDF + col] * sm.cb[col] : sm.ka.A[row * LDF + col];
-            hv[e] = static_cast<__bf16>(x);
-            lv[e] = static_cast<__bf16>(x - static_cast<float>(hv[e]));
+        for (int half = 0; half < 2; ++half) {
+            const int J = 2 * kb + half;
+            f32x4 x4 = {0.f, 0.f, 0.f, 0.f};
+            if (J <= M) {
+                const float *tile = mat == 0 ? Tb(M, J) : &sm.u.t.A[tile_id(M, J) * kTile];
+                x4 = *reinterpret_cast<const f32x4 *>(&tile[rr * LT + 4 * p]);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int col = 4 * p + e;
+                float x = (J < M || (J == M && col <= rr)) ? x4[e] : 0.f;
+                if (mat == 0) {
+                    const int jt = 16 * J + col;
+                    float bj = sm.eta[jt];
+                    if constexpr (KZ) bj = jt < n ? bj / (sm.kk[jt] + eps) : 0.f;
+                    x *= bj;
+                }
+                hv[4 * half + e] = static_cast<__bf16>(x);
+                lv[4 * half + e] = static_cast<__bf16>(x - static_cast<float>(hv[4 * half + e]));
+            }
         }
         char *dst = recb + (mat == 0 ? kRecTH : kRecAH) + f * kFragBytes + l * 16;
         *reinterpret_cast<bf16x8 *>(dst) = hv;
         *reinterpret_cast<bf16x8 *>(dst + 6 * kFragBytes) = lv;
     }
+    }  // chunk loop
 }
 
 // ============================================================ state kernel
@@ -343,18 +407,6 @@ struct alignas(16) StateSmem {
 // every outstanding global load).  The memory clobber keeps the compiler from
 // moving LDS accesses across it.
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Raw buffer resource over `rows` rows of `row_bytes` bytes spaced `stride`
-// bytes apart, starting at `base`: loads past the last row return zero and
-// stores past it are dropped, with no branch in the instruction stream
-// (0x00020000 is the gfx9-family descriptor word for untyped 32-bit data).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void *base, int rows, int stride, int row_bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (rows - 1) * stride + row_bytes,
-                                             0x00020000);
-}
-__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
 
 // ds_read_b64_tr_b16 (gfx950): every lane names 8 bytes (four bf16) of LDS;
 // within each group of 16 lanes, element e of lane i of the result is element
@@ -729,13 +781,23 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
 }
 
 // ============================================================ launchers
+// Workgroups of the persistent intra kernel: four per compute unit (its LDS
+// allows four), or one per chunk when there are fewer chunks.
+int intra_grid(long total) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    return (int)std::min<long>(total, 4L * cus);
+}
+
 template <bool KZ>
 hipError_t launch_intra(const ChunkArgs &a) {
-    const unsigned grid = (unsigned)((size_t)a.B * a.H * a.NC);
-    if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((intra_matrix_kernel<KZ>), dim3(grid), dim3(kIntraThreads), 0, a.stream,
+    const long total = (long)a.B * a.H * a.NC;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL((intra_matrix_kernel<KZ>), dim3(intra_grid(total)), dim3(kIntraThreads), 0, a.stream,
                        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), a.g, a.beta, a.T, a.H,
-                       a.NC, a.eps, a.scale, static_cast<char *>(a.ws));
+                       a.NC, (int)total, a.eps, a.scale, static_cast<char *>(a.ws));
     return hipGetLastError();
 }
 
