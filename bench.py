@@ -34,11 +34,11 @@ PEAK_HBM = 8000.0            # GB/s, MI355X HBM3E
 # file's sha256 differs, the figure is reported as null.
 MEASURED_TRAFFIC = {
     ("matrix", "state"): ("gated_delta_rule_26_amd/csrc/chunk_matrix.hip",
-                          "2ea52c7fd3934cc999a41f63550b8f3333ddd126249cbc008a276178a5eafeea",
-                          (160320.5 * 2.0 + 135168.0) * 1024),
+                          "0ac215d329af0975541a7f07d6804b6edf633c6b28e0f4db9413bcd5d277cc6a",
+                          (148676.5 * 2.0 + 135267.9) * 1024),
     ("matrix", "intra"): ("gated_delta_rule_26_amd/csrc/chunk_matrix.hip",
-                          "2ea52c7fd3934cc999a41f63550b8f3333ddd126249cbc008a276178a5eafeea",
-                          (67136.6 * 2.0 + 123906.3) * 1024),
+                          "0ac215d329af0975541a7f07d6804b6edf633c6b28e0f4db9413bcd5d277cc6a",
+                          (66888.5 * 2.0 + 100352.0) * 1024),
     ("decode", "step"): ("gated_delta_rule_26_amd/csrc/recurrent_step.hip",
                          "e7e419c4fce8d18e58aad36eae998f3c36e35efc9c754b1783925800a8b15b99",
                          (133011.2 * 2.0 + 264192.0) * 1024),
