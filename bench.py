@@ -252,7 +252,8 @@ def main():
     event_step_ms = sum(pre["step_ms"]) / len(pre["step_ms"])
     algo = args.algo
     if algo == "auto":
-        algo = "matrix" if (w.dtype == "bf16" and w.Dk == 128 and w.Dv == 128 and gdr_matrix_ready()) else "vector"
+        algo = "matrix" if (w.dtype == "bf16" and w.Dk == 128 and w.Dv == 128 and
+                            gdr_matrix_ready(w.per_channel)) else "vector"
     dom = "state" if state_ms >= intra_ms else "intra"
     dom_ms = state_ms if dom == "state" else intra_ms
     dom_flops = fl[dom] * tok_heads
@@ -320,14 +321,15 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def gdr_matrix_ready() -> bool:
-    """Whether the library routes bf16 d128 inputs to the matrix-core path
-    (the workspace size differs between the two paths)."""
+def gdr_matrix_ready(per_channel: bool = False) -> bool:
+    """Whether the library has a matrix-core path for bf16 d128 inputs with
+    this decay mode (``algo=auto`` takes it when it exists)."""
     import torch
     import gated_delta_rule_26_amd as gdr
     try:
         gdr.chunk_fwd_workspace_size(gdr.make_desc(1, 64, 1, 128, 128, qkv_dtype=torch.bfloat16,
-                                                   o_dtype=torch.float32, algo="matrix"))
+                                                   o_dtype=torch.float32, algo="matrix",
+                                                   per_channel=per_channel))
         return True
     except gdr.GdrError:
         return False

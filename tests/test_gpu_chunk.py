@@ -236,3 +236,29 @@ def test_full_workload_sampled(name):
     eo, es = rel(o_g, o_ref[hb, :, hh]), rel(s_g, s_ref[hb, hh])
     print(f"full workload {name}: rel o {eo:.2e} S {es:.2e}")
     assert eo < TOL[w.dtype] and es < TOL[w.dtype]
+
+
+@pytest.mark.parametrize("B,H,T", [(1, 8, 130), (3, 8, 70), (1, 2, 65), (2, 1, 129), (1, 2, 64 * 40 + 5)])
+def test_matrix_chunk_counts_and_workgroup_mapping(B, H, T):
+    """Matrix path: chunk counts that exercise the doubled and tripled LDS
+    buffers (2, 3 and 41 chunks), and (sequence, head) counts that do and do
+    not divide by 8 (the XCD-aware workgroup mapping and its fallback)."""
+    x = _inputs(2000 + T + 7 * H + B, B, T, H, 128, 128, "gdn", "bf16", with_s0=True)
+    o, s = _gpu(x, "gdn", "bf16", algo="matrix")
+    o_ref, s_ref = _ref(x, "gdn")
+    eo, es = rel(host(o), o_ref), rel(host(s), s_ref)
+    print(f"matrix B{B} H{H} T{T}: rel o {eo:.2e} S {es:.2e}")
+    assert eo < TOL["bf16"] and es < TOL["bf16"]
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_kaczmarz_eps_zero_with_partial_chunk(algo):
+    """KLA with eps = 0 and a partial last chunk: the padded rows (zero keys)
+    must not turn 0 / |0|^2 into NaN; valid rows match the oracle."""
+    x = _inputs(2100, 2, 100, 2, 128, 128, "kla", "bf16", with_s0=False)
+    o, s = _gpu(x, "kla", "bf16", algo=algo, eps=0.0)
+    o_ref, s_ref = _ref(x, "kla", eps=0.0)
+    assert torch.isfinite(o).all() and torch.isfinite(s).all()
+    eo, es = rel(host(o), o_ref), rel(host(s), s_ref)
+    print(f"kla eps=0 {algo}: rel o {eo:.2e} S {es:.2e}")
+    assert eo < TOL["bf16"] and es < TOL["bf16"]
