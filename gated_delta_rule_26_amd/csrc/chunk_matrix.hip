@@ -28,13 +28,12 @@
 //    columns in registers and do the dependent work of a chunk:
 //    P = K S, X = V - Gam P, E = T'' X, S <- gend S + K^T (Gend E).  Their
 //    operands stay in registers from one product to the next (see Layout),
-//    so a chunk needs no exchange between chain wavefronts.  Two "helper"
+//    so a chunk needs no exchange between chain wavefronts.  They also form
+//    the read Q S, which shares the state operand with K S.  Two "helper"
 //    wavefronts stage the next chunk's q, k, v and decays in LDS and, one
-//    chunk behind, compute the outputs O = scale Gam (Q S) + A E from the
-//    chain's S (bf16 hi, lo) and E, passed through LDS.  One barrier per
-//    chunk; every LDS buffer that crosses it is doubled, and q and exp(G) are
-//    tripled: while the chain works on chunk c, the helpers read chunk c-1's
-//    and write chunk c+1's.
+//    chunk behind, finish the outputs O = scale Gam (Q S) + A E from the
+//    chain's Q S and E, passed through LDS.  One barrier per chunk; every LDS
+//    buffer that crosses it is doubled.
 //
 // Layout.  v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8(l/16)+e],
 // B[8(l/16)+e][l%16] (e = 0..7) and D[4(l/16)+r][l%16] (r = 0..3).  A
@@ -390,13 +389,13 @@ constexpr int BV = 32;              // value columns per workgroup
 constexpr int NS = DV / BV;         // workgroups per (sequence, head)
 constexpr int LDK = DK + 8;         // bf16 row stride of the token-major q, k
 constexpr int LDV = BV + 8;         // bf16 row stride of the token-major v slice
-constexpr int kXFrags = 12;         // chain -> helper: S hi (4), S lo (4), E (4 fp32 tiles)
+constexpr int kXFrags = 8;          // chain -> helper: scale Gam Q S and E (4 fp32 tiles each)
 
 struct alignas(16) StateSmem {
     __bf16 K[2][C * LDK];          // k, token-major, key channels permuted within 32-blocks
-    __bf16 Q[3][C * LDK];          // q, the same layout (three buffers, see below)
+    __bf16 Q[2][C * LDK];          // q, the same layout
     __bf16 V[2][C * LDV];          // v slice, token-major
-    float Gam[3][C];               // exp(G_i)
+    float Gam[2][C];               // exp(G_i)
     float Gend[2][C];              // exp(G_63 - G_i)
     uint4 X[2][2][kXFrags][64];    // per chain wavefront and chunk parity
 };
@@ -509,11 +508,10 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
             // decays and this wavefront's v columns, read now for the X step
             f32x4 gam[4], gnd[4];
             bf16x4 vv[4];
-            const int buf3 = c % 3;
-            const float gs = sm.Gam[buf3][C - 1];  // exp(G_63), the chunk's state decay
+            const float gs = sm.Gam[buf][C - 1];  // exp(G_63), the chunk's state decay
 #pragma unroll
             for (int M = 0; M < 4; ++M) {
-                gam[M] = *reinterpret_cast<const f32x4 *>(&sm.Gam[buf3][16 * M + 4 * lg]);
+                gam[M] = *reinterpret_cast<const f32x4 *>(&sm.Gam[buf][16 * M + 4 * lg]);
                 gnd[M] = *reinterpret_cast<const f32x4 *>(&sm.Gend[buf][16 * M + 4 * lg]);
                 // V[16M + 4lg + r][16w + lr], r = 0..3
                 vv[M] = lds_read_tr(&sm.V[buf][(16 * M + 4 * lg + (lr >> 2)) * LDV + 16 * w + 4 * (lr & 3)]);
@@ -521,38 +519,50 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
             // S as the B operand over key channels (hi, lo)
             bf16x8 SH[4], SL[4];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                pair_split(S[2 * kb], S[2 * kb + 1], SH[kb], SL[kb]);
-                xo[kb * 64 + lane] = *reinterpret_cast<const uint4 *>(&SH[kb]);
-                xo[(4 + kb) * 64 + lane] = *reinterpret_cast<const uint4 *>(&SL[kb]);
-            }
-            // P = K S (token tile M, this wavefront's 16 value columns); the
-            // fragments of the next 32 key channels are read during the
-            // products of the current ones
+            for (int kb = 0; kb < 4; ++kb) pair_split(S[2 * kb], S[2 * kb + 1], SH[kb], SL[kb]);
+            // P = K S and Q S (token tile M, this wavefront's 16 value columns,
+            // sharing the state operand); the fragments of the next 32 key
+            // channels are read during the products of the current ones
             f32x4 P[4] = {zero4, zero4, zero4, zero4};
+            f32x4 QS[4] = {zero4, zero4, zero4, zero4};
             const __bf16 *sK = sm.K[buf];
-            bf16x8 ka[2][4];
+            const __bf16 *sQ = sm.Q[buf];
+            bf16x8 ka[2][4], qa[2][4];
 #pragma unroll
-            for (int M = 0; M < 4; ++M) ka[0][M] = *reinterpret_cast<const bf16x8 *>(&sK[(16 * M + lr) * LDK + 8 * lg]);
+            for (int M = 0; M < 4; ++M) {
+                ka[0][M] = *reinterpret_cast<const bf16x8 *>(&sK[(16 * M + lr) * LDK + 8 * lg]);
+                qa[0][M] = *reinterpret_cast<const bf16x8 *>(&sQ[(16 * M + lr) * LDK + 8 * lg]);
+            }
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const int cur = kb & 1;
                 if (kb + 1 < 4) {
 #pragma unroll
-                    for (int M = 0; M < 4; ++M)
+                    for (int M = 0; M < 4; ++M) {
                         ka[cur ^ 1][M] = *reinterpret_cast<const bf16x8 *>(&sK[(16 * M + lr) * LDK + 32 * (kb + 1) + 8 * lg]);
+                        qa[cur ^ 1][M] = *reinterpret_cast<const bf16x8 *>(&sQ[(16 * M + lr) * LDK + 32 * (kb + 1) + 8 * lg]);
+                    }
                 }
 #pragma unroll
                 for (int M = 0; M < 4; ++M) P[M] = mma(ka[cur][M], SH[kb], P[M]);
 #pragma unroll
                 for (int M = 0; M < 4; ++M) P[M] = mma(ka[cur][M], SL[kb], P[M]);
+#pragma unroll
+                for (int M = 0; M < 4; ++M) QS[M] = mma(qa[cur][M], SH[kb], QS[M]);
+#pragma unroll
+                for (int M = 0; M < 4; ++M) QS[M] = mma(qa[cur][M], SL[kb], QS[M]);
             }
-            // X = V - Gam P, rows 16M + 4lg + r
+            // X = V - Gam P, rows 16M + 4lg + r; the read scale Gam Q S to the helper
             f32x4 Xv[4];
 #pragma unroll
-            for (int M = 0; M < 4; ++M)
+            for (int M = 0; M < 4; ++M) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Xv[M][r] = static_cast<float>(vv[M][r]) - gam[M][r] * P[M][r];
+                for (int r = 0; r < 4; ++r) {
+                    Xv[M][r] = static_cast<float>(vv[M][r]) - gam[M][r] * P[M][r];
+                    QS[M][r] *= scale * gam[M][r];
+                }
+                xo[M * 64 + lane] = *reinterpret_cast<const uint4 *>(&QS[M]);
+            }
             bf16x8 XH[2], XL[2];
             pair_split(Xv[0], Xv[1], XH[0], XL[0]);
             pair_split(Xv[2], Xv[3], XH[1], XL[1]);
@@ -586,7 +596,7 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
             f32x4 Ep[4];
 #pragma unroll
             for (int M = 0; M < 4; ++M) {
-                xo[(8 + M) * 64 + lane] = *reinterpret_cast<const uint4 *>(&E[M]);
+                xo[(4 + M) * 64 + lane] = *reinterpret_cast<const uint4 *>(&E[M]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) Ep[M][r] = E[M][r] * gnd[M][r];
             }
@@ -666,7 +676,7 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
             gnd_reg = reinterpret_cast<const float *>(rec + kRecGend)[ht & 63];
         };
         auto store_stage = [&](int cc) {  // registers -> LDS buffers of chunk cc
-            const int buf = cc & 1, buf3 = cc % 3;
+            const int buf = cc & 1;
             const int seg = ht & 15, tg = ht >> 4;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -677,7 +687,7 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
                 for (int hh = 0; hh < 2; ++hh) {
                     const int col = kperm_col(seg, hh);
                     *reinterpret_cast<uint2 *>(&sm.K[buf][i * LDK + col]) = kh[hh];
-                    *reinterpret_cast<uint2 *>(&sm.Q[buf3][i * LDK + col]) = qh[hh];
+                    *reinterpret_cast<uint2 *>(&sm.Q[buf][i * LDK + col]) = qh[hh];
                 }
             }
             {
@@ -687,7 +697,7 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
                     *reinterpret_cast<uint4 *>(&sm.V[buf][(2 * tq + u) * LDV + 8 * sv]) = vreg[u];
             }
             if (ht < C) {
-                sm.Gam[buf3][ht] = gam_reg;
+                sm.Gam[buf][ht] = gam_reg;
                 sm.Gend[buf][ht] = gnd_reg;
             }
         };
@@ -700,34 +710,16 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
                 al[f] = *reinterpret_cast<const bf16x8 *>(rec + kRecAL + f * kFragBytes + lane * 16);
             }
         };
-        // outputs of chunk cp: O = scale Gam (Q S) + A E, with S (hi, lo) and E
-        // from the chain; rows past the end of the sequence are dropped by the
-        // buffer bounds
+        // outputs of chunk cp: O = (scale Gam Q S, from the chain) + A E; rows
+        // past the end of the sequence are dropped by the buffer bounds
         auto outputs = [&](int cp) __attribute__((always_inline)) {
-            const int buf3 = cp % 3;
             const uint4 *xi = &sm.X[cp & 1][vt][0][0];
-            const __bf16 *sQ = sm.Q[buf3];
-            f32x4 O[4] = {zero4, zero4, zero4, zero4};
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                bf16x8 sh, sl, qa[4];
-                *reinterpret_cast<uint4 *>(&sh) = xi[kb * 64 + lane];
-                *reinterpret_cast<uint4 *>(&sl) = xi[(4 + kb) * 64 + lane];
-#pragma unroll
-                for (int M = 0; M < 4; ++M) qa[M] = *reinterpret_cast<const bf16x8 *>(&sQ[(16 * M + lr) * LDK + 32 * kb + 8 * lg]);
-#pragma unroll
-                for (int M = 0; M < 4; ++M) O[M] = mma(qa[M], sh, O[M]);
-#pragma unroll
-                for (int M = 0; M < 4; ++M) O[M] = mma(qa[M], sl, O[M]);
-            }
-            f32x4 E[4];
+            f32x4 O[4], E[4];
             bf16x8 eh[2], el[2];
 #pragma unroll
             for (int M = 0; M < 4; ++M) {
-                *reinterpret_cast<uint4 *>(&E[M]) = xi[(8 + M) * 64 + lane];
-                const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&sm.Gam[buf3][16 * M + 4 * lg]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) O[M][r] *= scale * g4[r];
+                *reinterpret_cast<uint4 *>(&O[M]) = xi[M * 64 + lane];
+                *reinterpret_cast<uint4 *>(&E[M]) = xi[(4 + M) * 64 + lane];
             }
             pair_split(E[0], E[1], eh[0], el[0]);
             pair_split(E[2], E[3], eh[1], el[1]);
