@@ -398,6 +398,7 @@ struct alignas(16) StateSmem {
     float Gam[2][C];               // exp(G_i)
     float Gend[2][C];              // exp(G_63 - G_i)
     uint4 X[2][2][kXFrags][64];    // per chain wavefront and chunk parity
+    float Ost[2][C * 20];          // per helper: its fp32 output tile, token-major, for 16-byte stores
 };
 
 // Workgroup barrier for data exchanged through LDS only: waits for this
@@ -505,17 +506,6 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
                 }
             }
             uint4 *xo = &sm.X[buf][w][0][0];
-            // decays and this wavefront's v columns, read now for the X step
-            f32x4 gam[4], gnd[4];
-            bf16x4 vv[4];
-            const float gs = sm.Gam[buf][C - 1];  // exp(G_63), the chunk's state decay
-#pragma unroll
-            for (int M = 0; M < 4; ++M) {
-                gam[M] = *reinterpret_cast<const f32x4 *>(&sm.Gam[buf][16 * M + 4 * lg]);
-                gnd[M] = *reinterpret_cast<const f32x4 *>(&sm.Gend[buf][16 * M + 4 * lg]);
-                // V[16M + 4lg + r][16w + lr], r = 0..3
-                vv[M] = lds_read_tr(&sm.V[buf][(16 * M + 4 * lg + (lr >> 2)) * LDV + 16 * w + 4 * (lr & 3)]);
-            }
             // S as the B operand over key channels (hi, lo)
             bf16x8 SH[4], SL[4];
 #pragma unroll
@@ -551,6 +541,17 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
                 for (int M = 0; M < 4; ++M) QS[M] = mma(qa[cur][M], SH[kb], QS[M]);
 #pragma unroll
                 for (int M = 0; M < 4; ++M) QS[M] = mma(qa[cur][M], SL[kb], QS[M]);
+            }
+            // decays and this wavefront's v columns
+            f32x4 gam[4], gnd[4];
+            bf16x4 vv[4];
+            const float gs = sm.Gam[buf][C - 1];  // exp(G_63), the chunk's state decay
+#pragma unroll
+            for (int M = 0; M < 4; ++M) {
+                gam[M] = *reinterpret_cast<const f32x4 *>(&sm.Gam[buf][16 * M + 4 * lg]);
+                gnd[M] = *reinterpret_cast<const f32x4 *>(&sm.Gend[buf][16 * M + 4 * lg]);
+                // V[16M + 4lg + r][16w + lr], r = 0..3
+                vv[M] = lds_read_tr(&sm.V[buf][(16 * M + 4 * lg + (lr >> 2)) * LDV + 16 * w + 4 * (lr & 3)]);
             }
             // X = V - Gam P, rows 16M + 4lg + r; the read scale Gam Q S to the helper
             f32x4 Xv[4];
@@ -737,19 +738,32 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
             const size_t row0 = head0 + (size_t)t0 * H;
             constexpr int es = OUT_BF16 ? 2 : 4;
             const auto ro = rows_rsrc(static_cast<char *>(o) + row0 * DV * es, n, H * DV * es, DV * es);
+            if constexpr (OUT_BF16) {
 #pragma unroll
-            for (int M = 0; M < 4; ++M)
+                for (int M = 0; M < 4; ++M)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int off = ((16 * M + 4 * lg + r) * H * DV + jt + lr) * es;
-                    if constexpr (OUT_BF16) {
+                    for (int r = 0; r < 4; ++r) {
+                        const int off = ((16 * M + 4 * lg + r) * H * DV + jt + lr) * es;
                         const __bf16 hv = static_cast<__bf16>(O[M][r]);
                         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hv), ro, off, 0, 0);
-                    } else {
-                        const float val = O[M][r];
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, off, 0, 0);
                     }
+            } else {
+                // the tile through this wavefront's LDS area: one 16-byte store per
+                // lane covers 4 output columns (same wavefront, so no barrier)
+                float *ost = sm.Ost[vt];
+#pragma unroll
+                for (int M = 0; M < 4; ++M)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) ost[(16 * M + 4 * lg + r) * 20 + lr] = O[M][r];
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int row = 16 * it + (lane >> 2), c4 = 4 * (lane & 3);
+                    const uint4 val = *reinterpret_cast<const uint4 *>(&ost[row * 20 + c4]);
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, val), ro,
+                        (row * H * DV + jt + c4) * 4, 0, 0);
                 }
+            }
         };
         // step 0: stage chunk 0 (and 1); step c >= 1: outputs of chunk c-1
         load_stage(0);
