@@ -34,11 +34,11 @@ PEAK_HBM = 8000.0            # GB/s, MI355X HBM3E
 # file's sha256 differs, the figure is reported as null.
 MEASURED_TRAFFIC = {
     ("matrix", "state"): ("gated_delta_rule_26_amd/csrc/chunk_matrix.hip",
-                          "0ac215d329af0975541a7f07d6804b6edf633c6b28e0f4db9413bcd5d277cc6a",
-                          (148676.5 * 2.0 + 135267.9) * 1024),
+                          "89317b5477734d1bbd514c3fa74d190bfe1db742dadebc46582fc713799f5531",
+                          (148649.4 * 2.0 + 135174.4) * 1024),
     ("matrix", "intra"): ("gated_delta_rule_26_amd/csrc/chunk_matrix.hip",
-                          "0ac215d329af0975541a7f07d6804b6edf633c6b28e0f4db9413bcd5d277cc6a",
-                          (66888.5 * 2.0 + 100352.0) * 1024),
+                          "89317b5477734d1bbd514c3fa74d190bfe1db742dadebc46582fc713799f5531",
+                          (66891.4 * 2.0 + 100352.0) * 1024),
     ("decode", "step"): ("gated_delta_rule_26_amd/csrc/recurrent_step.hip",
                          "e7e419c4fce8d18e58aad36eae998f3c36e35efc9c754b1783925800a8b15b99",
                          (133011.2 * 2.0 + 264192.0) * 1024),
