@@ -35,94 +35,24 @@
 //    chain's Q S and E, passed through LDS.  One barrier per chunk; every LDS
 //    buffer that crosses it is doubled.
 //
-// Layout.  v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8(l/16)+e],
-// B[8(l/16)+e][l%16] (e = 0..7) and D[4(l/16)+r][l%16] (r = 0..3).  A
-// reduction may take its 32 terms (per 32-block) in any order shared by
-// both operands; here the 8 terms of lane group p = l/16 are indices
-// {4p..4p+3} and {16+4p..16+4p+3} of the block, which is exactly what two
-// stacked D tiles hold.  So a D tile (the state, X, E) is directly the B
-// operand of the next product, and the other operand (k, k^T, T'', A, q) is
-// stored or loaded in that permuted order.  The off-diagonal 16x16 blocks of
-// T use v_mfma_f32_16x16x4f32 (fp32 operands, same D layout).
-//
-// Precision.  Products of two exact bf16 inputs accumulate in fp32.  Every
-// fp32-derived operand (T'', A, S, X, E) is split into bf16 hi + lo and
-// multiplied as hi*x + lo*x (hi*hi + hi*lo + lo*hi when both sides are
-// split), which carries ~16 significant bits.
-#include "gdr_internal.h"
+// The operand layout (a D tile is directly the B operand of the next
+// product) and the bf16 hi/lo precision scheme are described in
+// matrix_common.h.
+#include "matrix_common.h"
 
 namespace gdr {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+using namespace mx;
 
-constexpr int C = kChunk;      // 64 tokens per chunk
-constexpr int DK = 128;
-constexpr int DV = 128;
-
-__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma32(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// Index, inside a 32-block, of term e (0..7) of lane group p (0..3).
-__host__ __device__ constexpr int kperm(int p, int e) { return e < 4 ? 4 * p + e : 12 + 4 * p + e; }
-
-// Two stacked D tiles (block rows 0..15 and 16..31) as one permuted operand,
-// split into bf16 hi and lo.
-__device__ __forceinline__ void pair_split(f32x4 t0, f32x4 t1, bf16x8 &hi, bf16x8 &lo) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        hi[r] = static_cast<__bf16>(t0[r]);
-        lo[r] = static_cast<__bf16>(t0[r] - static_cast<float>(hi[r]));
-        hi[4 + r] = static_cast<__bf16>(t1[r]);
-        lo[4 + r] = static_cast<__bf16>(t1[r] - static_cast<float>(hi[4 + r]));
-    }
-}
-
-// ---- per-chunk workspace record
-// T'' hi, T'' lo, A hi, A lo: each the six 16x32 operand fragments (M, kb) of
-// its lower triangle -- (0,0) (1,0) (2,0) (2,1) (3,0) (3,1), rows 16M ..
-// 16M+15, tokens 32kb .. 32kb+31 in the permuted order -- as 64 lanes x
-// 16 bytes; then, for the 64 tokens, Gam = exp(G) and Gend = exp(G_63 - G)
+// ---- per-chunk workspace record (scalar decay): the common head (T'' and A
+// fragments), then, for the 64 tokens, Gam = exp(G) and Gend = exp(G_63 - G)
 // (fp32), so the walk needs no exponentials.
-constexpr int kFragBytes = 64 * 16;
-constexpr int kRecTH = 0;
-constexpr int kRecTL = 6 * kFragBytes;
-constexpr int kRecAH = 12 * kFragBytes;
-constexpr int kRecAL = 18 * kFragBytes;
-constexpr int kRecGam = 24 * kFragBytes;
+constexpr int kRecGam = kRecHead;
 constexpr int kRecGend = kRecGam + C * 4;
 constexpr int kRecBytes = kRecGend + C * 4;  // 25088, a multiple of 256
-__host__ __device__ constexpr int lower_frag(int M, int kb) { return M < 2 ? M : 2 * M - 2 + kb; }
-__host__ __device__ constexpr int frag_M(int f) { return f < 2 ? f : 2 + ((f - 2) >> 1); }
-__host__ __device__ constexpr int frag_kb(int f) { return f < 2 ? 0 : (f - 2) & 1; }
-
-// Raw buffer resource over `rows` rows of `row_bytes` bytes spaced `stride`
-// bytes apart, starting at `base`: loads past the last row return zero and
-// stores past it are dropped, with no branch in the instruction stream
-// (0x00020000 is the gfx9-family descriptor word for untyped 32-bit data).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void *base, int rows, int stride, int row_bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (rows - 1) * stride + row_bytes,
-                                             0x00020000);
-}
-__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
 
 // ============================================================ intra kernel
-constexpr int kIntraThreads = 256;
-constexpr int LT = 20;                  // fp32 row stride of a 16x16 tile in LDS (16-byte aligned rows)
-constexpr int LQK = DK + 8;             // bf16 row stride of the staged q, k (token-major)
-constexpr int kTile = 16 * LT;          // floats per tile
-__host__ __device__ constexpr int tile_id(int I, int J) { return I * (I + 1) / 2 + J; }  // lower tiles 0..9
-__host__ __device__ constexpr int offdiag_id(int I, int J) { return I * (I - 1) / 2 + J; }  // J < I: 0..5
-
 // q and k are staged token-major for the K K^T and Q K^T products; the same
 // space then holds the lower 16x16 tiles of R, T and A.  T's diagonal blocks
 // overwrite R's (R_II is not needed once T_II is known; R_IJ with J < I is).
@@ -150,9 +80,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
     char *__restrict__ ws) {
     __shared__ IntraSmem sm;
     const int qk_stride = H * DK * 2;
-    auto Tb = [&](int I, int J) -> float * {  // block (I, J) of T, J <= I
-        return I == J ? &sm.u.t.R[tile_id(I, I) * kTile] : &sm.u.t.Toff[offdiag_id(I, J) * kTile];
-    };
+    const TriTiles tri{sm.u.t.R, sm.u.t.Toff, sm.u.t.A};
     const int seg = threadIdx.x & 15, i0 = threadIdx.x >> 4;
     const int lane0 = threadIdx.x & 63;
 
@@ -185,12 +113,8 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
-    const int c = ci % NC;
-    const int bh = ci / NC;
-    const int b = bh / H, h = bh % H;
-    const int t0 = c * C;
+    const int t0 = (ci % NC) * C;
     const int n = min(C, T - t0);
-    const size_t row0 = ((size_t)b * T + t0) * H + h;
     char *recb = ws + (size_t)ci * kRecBytes;
     __syncthreads();  // the previous chunk's tiles are no longer read
 
@@ -285,8 +209,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
             if (w >= 2) {
                 val = scale * dec * acc[t][r];
             } else {
-                float bi = sm.eta[i];
-                if constexpr (KZ) bi = i < n ? bi / (sm.kk[i] + eps) : 0.f;
+                const float bi = write_strength<KZ>(sm.eta, sm.kk, i, n, eps);
                 val = j < i ? bi * dec * acc[t][r] : 0.f;
             }
             dst[(4 * lg + r) * LT + lr] = val;
@@ -294,102 +217,14 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
     }
     __syncthreads();
 
-    // ---- T = (I + R)^{-1}: diagonal 16x16 blocks by forward substitution
-    // (one column per lane), then three levels of off-diagonal blocks on
-    // fp32 MFMA:  T_IJ = -T_II sum_{M=J}^{I-1} R_IM T_MJ
-    if (lane < 16) {
-        const int cc = lane;
-        float *blk = &sm.u.t.R[tile_id(w, w) * kTile];
-        float xcol[16];
-        f32x4 row[2][4];  // R row i (broadcast to every lane), the next row read ahead
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) row[0][q4] = *reinterpret_cast<const f32x4 *>(&blk[4 * q4]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int cur = i & 1;
-            if (i + 1 < 16) {
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    if (4 * q4 < i + 1) row[cur ^ 1][q4] = *reinterpret_cast<const f32x4 *>(&blk[(i + 1) * LT + 4 * q4]);
-            }
-            float a0 = i == cc ? 1.f : 0.f, a1 = 0.f;
-#pragma unroll
-            for (int m = 0; m < i; ++m) {
-                if (m & 1) a1 -= row[cur][m >> 2][m & 3] * xcol[m];
-                else a0 -= row[cur][m >> 2][m & 3] * xcol[m];
-            }
-            xcol[i] = i < cc ? 0.f : a0 + a1;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) blk[i * LT + cc] = xcol[i];
-    }
-    __syncthreads();
-    auto inverse_tile = [&](int I, int J) {
-        f32x4 P = {0.f, 0.f, 0.f, 0.f};
-        for (int M = J; M < I; ++M) {
-            const float *Rt = &sm.u.t.R[tile_id(I, M) * kTile];
-            const float *Tt = Tb(M, J);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) P = mma32(Rt[lr * LT + 4 * lg + s], Tt[(4 * lg + s) * LT + lr], P);
-        }
-        const float *Tii = Tb(I, I);
-        f32x4 out = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) out = mma32(Tii[lr * LT + 4 * lg + s], P[s], out);
-        float *dst = Tb(I, J);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(4 * lg + r) * LT + lr] = -out[r];
-    };
-    if (w < 3) inverse_tile(w + 1, w);
-    __syncthreads();
-    if (w < 2) inverse_tile(w + 2, w);
-    __syncthreads();
-    if (w == 0) inverse_tile(3, 0);
-    __syncthreads();
-
-    // ---- operand fragments: T'' = T Diag(beta) and A, lower triangle only,
-    // bf16 hi + lo.  Terms 0..3 of lane group p are tile columns 4p .. 4p+3
-    // of tile (M, 2kb), terms 4..7 the same columns of tile (M, 2kb + 1).
-    for (int u = tid; u < 2 * 6 * 64; u += kIntraThreads) {
-        const int mat = u / 384, f = (u >> 6) % 6, l = u & 63;
-        const int M = frag_M(f), kb = frag_kb(f), rr = l & 15, p = l >> 4;
-        bf16x8 hv, lv;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int J = 2 * kb + half;
-            f32x4 x4 = {0.f, 0.f, 0.f, 0.f};
-            if (J <= M) {
-                const float *tile = mat == 0 ? Tb(M, J) : &sm.u.t.A[tile_id(M, J) * kTile];
-                x4 = *reinterpret_cast<const f32x4 *>(&tile[rr * LT + 4 * p]);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int col = 4 * p + e;
-                float x = (J < M || (J == M && col <= rr)) ? x4[e] : 0.f;
-                if (mat == 0) {
-                    const int jt = 16 * J + col;
-                    float bj = sm.eta[jt];
-                    if constexpr (KZ) bj = jt < n ? bj / (sm.kk[jt] + eps) : 0.f;
-                    x *= bj;
-                }
-                hv[4 * half + e] = static_cast<__bf16>(x);
-                lv[4 * half + e] = static_cast<__bf16>(x - static_cast<float>(hv[4 * half + e]));
-            }
-        }
-        char *dst = recb + (mat == 0 ? kRecTH : kRecAH) + f * kFragBytes + l * 16;
-        *reinterpret_cast<bf16x8 *>(dst) = hv;
-        *reinterpret_cast<bf16x8 *>(dst + 6 * kFragBytes) = lv;
-    }
+    // ---- T = (I + R)^{-1}, then the T'' and A operand fragments
+    invert_unit_lower(tri, lane, w, lr, lg);
+    pack_T_A<KZ>(tri, sm.eta, sm.kk, n, eps, recb, tid);
     }  // chunk loop
 }
 
 // ============================================================ state kernel
-constexpr int kStateThreads = 256;  // chain wavefronts 0, 1; helper wavefronts 2, 3
-constexpr int BV = 32;              // value columns per workgroup
-constexpr int NS = DV / BV;         // workgroups per (sequence, head)
-constexpr int LDK = DK + 8;         // bf16 row stride of the token-major q, k
-constexpr int LDV = BV + 8;         // bf16 row stride of the token-major v slice
-constexpr int kXFrags = 8;          // chain -> helper: scale Gam Q S and E (4 fp32 tiles each)
+constexpr int LDK = DK + 8;  // bf16 row stride of the token-major q, k
 
 struct alignas(16) StateSmem {
     __bf16 K[2][C * LDK];          // k, token-major, key channels permuted within 32-blocks
@@ -400,26 +235,6 @@ struct alignas(16) StateSmem {
     uint4 X[2][2][kXFrags][64];    // per chain wavefront and chunk parity
     float Ost[2][C * 20];          // per helper: its fp32 output tile, token-major, for 16-byte stores
 };
-
-// Workgroup barrier for data exchanged through LDS only: waits for this
-// wavefront's LDS operations, not for its global loads, so loads issued for a
-// later chunk stay in flight across it (a full __syncthreads also waits for
-// every outstanding global load).  The memory clobber keeps the compiler from
-// moving LDS accesses across it.
-__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// ds_read_b64_tr_b16 (gfx950): every lane names 8 bytes (four bf16) of LDS;
-// within each group of 16 lanes, element e of lane i of the result is element
-// i % 4 of the 8 bytes named by lane 4e + i / 4 of the group.  So if lane j of
-// group p names elements c0 + 4 (j % 4) .. +3 of row r0 + 4p + j / 4 of a
-// row-major matrix, lane (i, p) receives rows r0 + 4p + e, e = 0..3, of column
-// c0 + i: a transposed 4x16 block, as MFMA fragments and D tiles hold it.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p) {
-    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4 *)(p));
-    return __builtin_bit_cast(bf16x4, r);
-}
 
 // Column, in the permuted token-major layout, of the 8-byte half hh (0, 1)
 // of key-channel segment seg (8 channels, 0..15).
@@ -435,19 +250,8 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
     float *__restrict__ s_final, int T, int H, int NC, int BH, float scale) {
     __shared__ StateSmem sm;
 
-    // XCD-aware placement: consecutive workgroup ids go to different XCDs, so
-    // the slices of one (sequence, head) get ids that are equal modulo 8 and
-    // share that XCD's L2 for q, k, v and the chunk records.
-    const int x = blockIdx.x;
     int bh, slice;
-    if ((BH & 7) == 0) {
-        const int xcd = x & 7, r = x >> 3;
-        bh = (r / NS) * 8 + xcd;
-        slice = r % NS;
-    } else {
-        bh = x / NS;
-        slice = x % NS;
-    }
+    state_slot(blockIdx.x, BH, bh, slice);
     const int b = bh / H, h = bh % H;
     const int j0 = slice * BV;
     const int tid = threadIdx.x;
@@ -711,59 +515,11 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
                 al[f] = *reinterpret_cast<const bf16x8 *>(rec + kRecAL + f * kFragBytes + lane * 16);
             }
         };
-        // outputs of chunk cp: O = (scale Gam Q S, from the chain) + A E; rows
-        // past the end of the sequence are dropped by the buffer bounds
+        // outputs of chunk cp: O = (scale Gam Q S, from the chain) + A E
         auto outputs = [&](int cp) __attribute__((always_inline)) {
-            const uint4 *xi = &sm.X[cp & 1][vt][0][0];
-            f32x4 O[4], E[4];
-            bf16x8 eh[2], el[2];
-#pragma unroll
-            for (int M = 0; M < 4; ++M) {
-                *reinterpret_cast<uint4 *>(&O[M]) = xi[M * 64 + lane];
-                *reinterpret_cast<uint4 *>(&E[M]) = xi[(4 + M) * 64 + lane];
-            }
-            pair_split(E[0], E[1], eh[0], el[0]);
-            pair_split(E[2], E[3], eh[1], el[1]);
-#pragma unroll
-            for (int M = 0; M < 4; ++M)
-#pragma unroll
-                for (int kb = 0; kb <= (M >> 1); ++kb) {
-                    const int f = lower_frag(M, kb);
-                    O[M] = mma(ah[f], eh[kb], O[M]);
-                    O[M] = mma(ah[f], el[kb], O[M]);
-                    O[M] = mma(al[f], eh[kb], O[M]);
-                }
             const int t0 = cp * C;
-            const int n = min(C, T - t0);
-            const size_t row0 = head0 + (size_t)t0 * H;
-            constexpr int es = OUT_BF16 ? 2 : 4;
-            const auto ro = rows_rsrc(static_cast<char *>(o) + row0 * DV * es, n, H * DV * es, DV * es);
-            if constexpr (OUT_BF16) {
-#pragma unroll
-                for (int M = 0; M < 4; ++M)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int off = ((16 * M + 4 * lg + r) * H * DV + jt + lr) * es;
-                        const __bf16 hv = static_cast<__bf16>(O[M][r]);
-                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hv), ro, off, 0, 0);
-                    }
-            } else {
-                // the tile through this wavefront's LDS area: one 16-byte store per
-                // lane covers 4 output columns (same wavefront, so no barrier)
-                float *ost = sm.Ost[vt];
-#pragma unroll
-                for (int M = 0; M < 4; ++M)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) ost[(16 * M + 4 * lg + r) * 20 + lr] = O[M][r];
-#pragma unroll
-                for (int it = 0; it < 4; ++it) {
-                    const int row = 16 * it + (lane >> 2), c4 = 4 * (lane & 3);
-                    const uint4 val = *reinterpret_cast<const uint4 *>(&ost[row * 20 + c4]);
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, val), ro,
-                        (row * H * DV + jt + c4) * 4, 0, 0);
-                }
-            }
+            chunk_outputs<OUT_BF16>(&sm.X[cp & 1][vt][0][0], ah, al, sm.Ost[vt], o, head0 + (size_t)t0 * H,
+                                    min(C, T - t0), H, jt, lane);
         };
         // step 0: stage chunk 0 (and 1); step c >= 1: outputs of chunk c-1
         load_stage(0);
@@ -787,21 +543,11 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
 }
 
 // ============================================================ launchers
-// Workgroups of the persistent intra kernel: four per compute unit (its LDS
-// allows four), or one per chunk when there are fewer chunks.
-int intra_grid(long total) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;
-    return (int)std::min<long>(total, 4L * cus);
-}
-
 template <bool KZ>
 hipError_t launch_intra(const ChunkArgs &a) {
     const long total = (long)a.B * a.H * a.NC;
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL((intra_matrix_kernel<KZ>), dim3(intra_grid(total)), dim3(kIntraThreads), 0, a.stream,
+    hipLaunchKernelGGL((intra_matrix_kernel<KZ>), dim3(intra_grid(total, 4)), dim3(kIntraThreads), 0, a.stream,
                        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), a.g, a.beta, a.T, a.H,
                        a.NC, (int)total, a.eps, a.scale, static_cast<char *>(a.ws));
     return hipGetLastError();
@@ -820,15 +566,22 @@ hipError_t launch_state(const ChunkArgs &a) {
 
 }  // namespace
 
-size_t chunk_matrix_workspace_bytes(int B, int H, int NC, int, int, bool) {
-    return (size_t)B * H * NC * kRecBytes;
+int mx::intra_grid(long total, int per_cu) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    return (int)std::min<long>(total, (long)per_cu * cus);
 }
 
-bool chunk_matrix_supported(int Dk, int Dv, bool qkv_bf16, bool per_channel) {
-    return qkv_bf16 && Dk == DK && Dv == DV && !per_channel;
+size_t chunk_matrix_workspace_bytes(int B, int H, int NC, int, int, bool per_channel) {
+    return per_channel ? chunk_matrix_pc_workspace_bytes(B, H, NC) : (size_t)B * H * NC * kRecBytes;
 }
+
+bool chunk_matrix_supported(int Dk, int Dv, bool qkv_bf16, bool) { return qkv_bf16 && Dk == DK && Dv == DV; }
 
 hipError_t launch_chunk_matrix(const ChunkArgs &a, int stage) {
+    if (a.per_channel) return launch_chunk_matrix_pc(a, stage);
     if (stage != 1) {
         const hipError_t e = a.kaczmarz ? launch_intra<true>(a) : launch_intra<false>(a);
         if (e != hipSuccess || stage == 0) return e;

@@ -47,6 +47,9 @@ hipError_t launch_chunk_vector(const ChunkArgs &a, int stage);
 size_t chunk_matrix_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel);
 bool chunk_matrix_supported(int Dk, int Dv, bool qkv_bf16, bool per_channel);
 hipError_t launch_chunk_matrix(const ChunkArgs &a, int stage);
+// Its per-channel-decay kernels (called by the two functions above).
+size_t chunk_matrix_pc_workspace_bytes(int B, int H, int NC);
+hipError_t launch_chunk_matrix_pc(const ChunkArgs &a, int stage);
 
 // T == 0: s_final = s0 (or zero).
 hipError_t launch_state_init(float *dst, const float *src, size_t n, hipStream_t stream);

@@ -63,7 +63,7 @@ extern "C" {
 /* algo: which kernels run the chunked path */
 #define GDR_ALGO_AUTO 0          /* matrix-core kernel where supported, else vector kernels */
 #define GDR_ALGO_VECTOR 1        /* fp32 vector-ALU kernels (any dtype, any mode) */
-#define GDR_ALGO_MATRIX 2        /* bf16 MFMA kernel: bf16 q/k/v, Dk = Dv = 128, scalar decay */
+#define GDR_ALGO_MATRIX 2        /* bf16 MFMA kernels: bf16 q/k/v, Dk = Dv = 128, either decay mode */
 
 typedef enum gdr_status {
     GDR_OK = 0,

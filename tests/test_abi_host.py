@@ -127,14 +127,20 @@ def test_matrix_algo_support_and_workspace():
     torch = __import__("torch")
     assert _ws(_desc(qkv_dtype=torch.float32, algo="matrix"))[0] == E["GDR_E_UNSUPPORTED"]
     assert _ws(_desc(Dk=64, Dv=64, algo="matrix"))[0] == E["GDR_E_UNSUPPORTED"]
-    assert _ws(_desc(per_channel=True, algo="matrix"))[0] == E["GDR_E_UNSUPPORTED"]
-    # matrix path, per chunk: T'' and A, each hi and lo, as six 1 KiB MFMA operand
-    # fragments, then two fp32 decay factors per token
     nc = (100 + 63) // 64
+    # scalar decay, per chunk: T'' and A, each hi and lo, as six 1 KiB MFMA
+    # operand fragments, then two fp32 decay factors per token
     assert _ws(_desc(algo="matrix")) == (0, 2 * 3 * nc * (4 * 6 * 1024 + 2 * 64 * 4))
     assert _ws(_desc(algo="auto")) == _ws(_desc(algo="matrix"))
-    rc, n = _ws(_desc(per_channel=True, algo="auto"))   # auto falls back to the vector path
-    assert rc == 0 and n > 0
+    # per-channel decay: the same head, then the decayed K, Q (for K S, Q S) and
+    # K (for the update), each hi and lo as sixteen 1 KiB fragments, and one
+    # fp32 chunk-end decay per key channel
+    pc = 4 * 6 * 1024 + 6 * 16 * 1024 + 128 * 4
+    assert _ws(_desc(per_channel=True, algo="matrix")) == (0, 2 * 3 * nc * pc)
+    assert _ws(_desc(per_channel=True, algo="auto")) == _ws(_desc(per_channel=True, algo="matrix"))
+    # auto falls back to the vector path where the matrix kernels do not apply
+    rc, n = _ws(_desc(Dk=64, Dv=64, per_channel=True, algo="auto"))
+    assert rc == 0 and (rc, n) == _ws(_desc(Dk=64, Dv=64, per_channel=True, algo="vector"))
 
 
 def test_step_validation_errors():
