@@ -22,10 +22,12 @@
 //    operand fragments, and exp(G_63).  The decayed operands are not exact in
 //    bf16, so every product with them is split (hi*hi + hi*lo + lo*hi).
 //  * state (one workgroup per (sequence, head, 32 value columns)): two chain
-//    wavefronts as for scalar decay; a copier wavefront moves the decayed
-//    operand fragments of a chunk from the record straight into LDS (global
-//    loads that write LDS, no registers) and stages v; an output wavefront
-//    forms O = Q~ S + A E one chunk behind.  Two barriers per chunk.
+//    wavefronts as for scalar decay; two helper wavefronts move the decayed
+//    operand fragments of a chunk from the record, and the v slice, straight
+//    into LDS (global loads that write LDS, no registers) and form
+//    O = Q~ S + A E one chunk behind.  Two barriers per chunk; key block 0 of
+//    K~, Q~ is double-buffered so that the copies split evenly between the
+//    two halves of a chunk.
 //
 // R and A with per-channel decay.  exp(G_i - G_j) does not factor into a row
 // term times a column term that is bounded for every i, j, so row block I
@@ -44,11 +46,12 @@ using namespace mx;
 
 // ---- per-chunk record (per-channel decay): the common head (T'' and A
 // fragments), then the decayed operands of the walk, each fragment 64 lanes x
-// 16 bytes: K~ hi, K~ lo, Q~ hi, Q~ lo (16 fragments each, f = 4M + kb: token
-// tile M, key block kb, term e of lane group p = key channel 32kb + kperm(p,e)),
-// K^ hi, K^ lo (16 fragments each, f = 2i + kb: key tile i, token block kb,
-// term e of lane group p = token 32kb + kperm(p,e)), then exp(G_63) per key
-// channel (fp32).
+// 16 bytes: K~ and Q~ as 64 fragments ordered by key block kb, then kind
+// (K~ hi, K~ lo, Q~ hi, Q~ lo), then token tile M (f = 16kb + 4kind + M; term
+// e of lane group p = key channel 32kb + kperm(p,e)), so each key block is
+// one contiguous 16 KiB group; K^ hi, K^ lo (16 fragments each, f = 2i + kb:
+// key tile i, token block kb, term e of lane group p = token 32kb +
+// kperm(p,e)); then exp(G_63) per key channel (fp32).
 constexpr int kPcKq = kRecHead;
 constexpr int kPcKu = kPcKq + 64 * kFragBytes;
 constexpr int kPcGend = kPcKu + 32 * kFragBytes;
@@ -191,13 +194,13 @@ __global__ __launch_bounds__(kIntraThreads, 2) void intra_pc_kernel(
             qx[4 + e] = scale * a1 * static_cast<float>(q1[e]);
         }
         bf16x8 hv, lv;
-        char *dst = recb + kPcKq + f * kFragBytes + l * 16;
+        char *dst = recb + kPcKq + (16 * kb + M) * kFragBytes + l * 16;
         split8(kx, hv, lv);
         *reinterpret_cast<bf16x8 *>(dst) = hv;
-        *reinterpret_cast<bf16x8 *>(dst + 16 * kFragBytes) = lv;
+        *reinterpret_cast<bf16x8 *>(dst + 4 * kFragBytes) = lv;
         split8(qx, hv, lv);
-        *reinterpret_cast<bf16x8 *>(dst + 32 * kFragBytes) = hv;
-        *reinterpret_cast<bf16x8 *>(dst + 48 * kFragBytes) = lv;
+        *reinterpret_cast<bf16x8 *>(dst + 8 * kFragBytes) = hv;
+        *reinterpret_cast<bf16x8 *>(dst + 12 * kFragBytes) = lv;
     }
     // K^: key channel 16i + l%16, tokens 32kb + kperm(p, e)
     for (int u = tid; u < 16 * 64; u += kIntraThreads) {
@@ -337,12 +340,14 @@ __global__ __launch_bounds__(kIntraThreads, 2) void intra_pc_kernel(
 
 // ============================================================ state kernel
 struct alignas(16) StatePcSmem {
-    uint4 Kq[64 * 64];           // K~ hi, K~ lo, Q~ hi, Q~ lo fragments of the current chunk
+    uint4 Kq0[2][16 * 64];       // key block 0 of K~, Q~ (hi, lo), by chunk parity
+    uint4 Kq123[48 * 64];        // key blocks 1..3 of K~, Q~ (hi, lo) of the current chunk
     uint4 Ku[32 * 64];           // K^ hi, K^ lo fragments of the current chunk
     float Gend[DK];              // exp(G_63) per key channel
-    __bf16 V[2][C * LDV];        // v slice, token-major
+    __bf16 V[2][C * BV];         // v slice, token-major, 64-byte rows
     uint4 X[2][2][kXFrags][64];  // per chain wavefront and chunk parity: Q~ S, then E
-    float Ost[C * 20];           // the output wavefront's fp32 tile, token-major, for 16-byte stores
+    float Ost[C * 20];           // a helper's fp32 output tile, token-major, for 16-byte stores (the
+                                 // helpers form outputs in turn, never at the same time)
 };
 
 // Global -> LDS copies without registers (global_load_lds, gfx950): every
@@ -350,7 +355,7 @@ struct alignas(16) StatePcSmem {
 // M0 + 16 lane (4 lane).  Issued from inline asm, which saves and restores M0:
 // the compiler then does not make later LDS accesses of this wavefront wait
 // for the copy (they touch other buffers); the copies complete at the
-// copier's explicit s_waitcnt vmcnt(0) before the barrier that publishes
+// helpers' explicit s_waitcnt vmcnt(0) before the barrier that publishes
 // them.  The hardware counts them in vmcnt, so the compiler's own wait counts
 // for other loads can only get stricter.  One wait state separates the M0
 // write from the copy that reads it.
@@ -369,14 +374,17 @@ __device__ __forceinline__ void lds_dma4(const void *src, unsigned lds) {
                  : "=&s"(saved) : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src) : "memory");
 }
 
-// PIECES 1 KiB pieces by one wavefront.
+// PIECES 1 KiB pieces, split over the two helper wavefronts (vt = 0, 1).
 template <int PIECES>
-__device__ __forceinline__ void copy_to_lds(const char *src, unsigned dst, int lane) {
+__device__ __forceinline__ void copy_to_lds(const char *src, unsigned dst, int vt, int lane) {
 #pragma unroll
-    for (int p = 0; p < PIECES; ++p) lds_dma16(src + p * 1024 + lane * 16, dst + p * 1024);
+    for (int j = 0; j < PIECES / 2; ++j) {
+        const int p = 2 * j + vt;
+        lds_dma16(src + p * 1024 + lane * 16, dst + p * 1024);
+    }
 }
 
-// Barrier after which data the copier moved into LDS is visible: waits for
+// Barrier after which data a helper moved into LDS is visible: waits for
 // all of this wavefront's global loads (those writing LDS included) and LDS
 // operations.
 __device__ __forceinline__ void barrier_after_loads() {
@@ -412,9 +420,9 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
     }
 
     // Per chunk c two barriers: A(c) after the chain has read K~, Q~ (the
-    // copier then moves chunk c+1's), B(c) at the end of the chunk (K^ and
-    // exp(G_63) of chunk c are moved between B(c-1) and A(c)).  Every role
-    // passes 2 NC + 2 barriers.
+    // helpers then move key blocks 1..3 of chunk c+1's), B(c) at the end of
+    // the chunk (K^, exp(G_63) of chunk c and key block 0 of chunk c+1 are
+    // moved between B(c-1) and A(c)).  Every role passes 2 NC + 3 barriers.
     if (w < 2) {
         // ================= chain wavefront: value columns jt .. jt+15
         const int jt = j0 + 16 * w;
@@ -454,7 +462,7 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
 #pragma unroll
             for (int m4 = 0; m4 < 4; ++m4)
 #pragma unroll
-                for (int M = 0; M < 4; ++M) fa[0][m4][M] = frag(sm.Kq, 16 * m4 + 4 * M);
+                for (int M = 0; M < 4; ++M) fa[0][m4][M] = frag(sm.Kq0[buf], 4 * m4 + M);
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const int cur = kb & 1;
@@ -462,7 +470,7 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
 #pragma unroll
                     for (int m4 = 0; m4 < 4; ++m4)
 #pragma unroll
-                        for (int M = 0; M < 4; ++M) fa[cur ^ 1][m4][M] = frag(sm.Kq, 16 * m4 + 4 * M + kb + 1);
+                        for (int M = 0; M < 4; ++M) fa[cur ^ 1][m4][M] = frag(sm.Kq123, 16 * kb + 4 * m4 + M);
                 }
 #pragma unroll
                 for (int M = 0; M < 4; ++M) {
@@ -477,13 +485,13 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
                     QS[M] = mma(fa[cur][3][M], SH[kb], QS[M]);
                 }
             }
-            barrier_lds();  // A(c): K~, Q~ of this chunk are no longer read
-            // X = V - K~ S (rows 16M + 4lg + r); Q~ S to the output wavefront
+            barrier_lds();  // A(c): key blocks 1..3 of K~, Q~ are no longer read
+            // X = V - K~ S (rows 16M + 4lg + r); Q~ S to the helper
             f32x4 Xv[4];
 #pragma unroll
             for (int M = 0; M < 4; ++M) {
                 // V[16M + 4lg + r][16w + lr], r = 0..3
-                const bf16x4 vv = lds_read_tr(&sm.V[buf][(16 * M + 4 * lg + (lr >> 2)) * LDV + 16 * w + 4 * (lr & 3)]);
+                const bf16x4 vv = lds_read_tr(&sm.V[buf][(16 * M + 4 * lg + (lr >> 2)) * BV + 16 * w + 4 * (lr & 3)]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) Xv[M][r] = static_cast<float>(vv[r]) - P[M][r];
                 xo[M * 64 + lane] = *reinterpret_cast<const uint4 *>(&QS[M]);
@@ -532,7 +540,8 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
             step(c + 1, tBh, tBl, tAh, tAl);
         }
         if (c < NC) step(c, tAh, tAl, tBh, tBl);
-        barrier_lds();  // the output wavefront finishes the last chunk
+        barrier_lds();  // the helpers finish the last chunk's outputs, in turn
+        barrier_lds();
         if (s_final) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -540,75 +549,73 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
                 for (int r = 0; r < 4; ++r)
                     s_final[sbase + (size_t)(16 * i + 4 * lg + r) * DV + jt + lr] = S[i][r];
         }
-    } else if (w == 2) {
-        // ================= copier wavefront: chunk operands and the v slice
-        // into LDS.  Its waits stall nothing else.
-        const size_t head0 = (size_t)b * T * H + h;  // row of token 0 of this head
-        const int v_stride = H * DV * 2;
-        uint4 vreg[4];
-        int v_off[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v_off[u] = (4 * (lane >> 2) + u) * v_stride + 2 * (j0 + 8 * (lane & 3));
-        auto load_v = [&](int cc) {  // rows past the end read as zero
-            const int t0 = cc * C;
-            const auto rv = rows_rsrc(v + (head0 + (size_t)t0 * H) * DV, min(C, T - t0), v_stride, DV * 2);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) vreg[u] = buf_ld16(rv, v_off[u]);
-        };
-        auto store_v = [&](int cc) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                *reinterpret_cast<uint4 *>(&sm.V[cc & 1][(4 * (lane >> 2) + u) * LDV + 8 * (lane & 3)]) = vreg[u];
-        };
-        const unsigned lds_kq = lds_addr(sm.Kq), lds_ku = lds_addr(sm.Ku), lds_gend = lds_addr(sm.Gend);
-        copy_to_lds<64>(recs + kPcKq, lds_kq, lane);
-        load_v(0);
-        store_v(0);
-        load_v(min(1, NC - 1));
-        barrier_after_loads();
-        for (int c = 0; c < NC; ++c) {
-            // chain: K~ S, Q~ S of chunk c
-            const char *rc = recs + (size_t)c * kPcBytes;
-            copy_to_lds<32>(rc + kPcKu, lds_ku, lane);
-            lds_dma4(rc + kPcGend + lane * 4, lds_gend);
-            lds_dma4(rc + kPcGend + 256 + lane * 4, lds_gend + 256);
-            if (c + 1 < NC) store_v(c + 1);
-            load_v(min(c + 2, NC - 1));
-            barrier_after_loads();  // A(c)
-            // chain: E and the state update of chunk c
-            copy_to_lds<64>(recs + (size_t)min(c + 1, NC - 1) * kPcBytes + kPcKq, lds_kq, lane);
-            barrier_after_loads();  // B(c)
-        }
-        barrier_lds();
     } else {
-        // ================= output wavefront: O = Q~ S + A E of chunk c-1 for
-        // the value columns of chain wavefront 0 (between B(c-1) and A(c)) and
-        // of chain wavefront 1 (between A(c) and B(c))
-        const size_t head0 = (size_t)b * T * H + h;
-        bf16x8 ah[6], al[6];
+        // ================= helper wavefronts (vt = 0, 1): both move the
+        // decayed operands and the v slice into LDS by global -> LDS copies,
+        // half each, and wait for them before each barrier; helper vt forms
+        // O = Q~ S + A E of chunk c-1 for the value columns of chain
+        // wavefront vt, helper 0 between B(c-1) and A(c), helper 1 between
+        // A(c) and B(c).
+        const int vt = __builtin_amdgcn_readfirstlane(w - 2);
+        const size_t head0 = (size_t)b * T * H + h;  // row of token 0 of this head
+        const unsigned lds_kq0 = lds_addr(sm.Kq0), lds_kq123 = lds_addr(sm.Kq123), lds_ku = lds_addr(sm.Ku);
+        const unsigned lds_gend = lds_addr(sm.Gend), lds_v = lds_addr(sm.V);
+        // v slice of chunk cc, 16 rows per copy (lane l: row l/4, 16-byte
+        // segment l%4); rows past the end repeat the last row (any finite
+        // value works there: those rows and columns of T'' and A are zero)
+        auto copy_v = [&](int cc) {
+            const int t0 = cc * C, n = min(C, T - t0);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int i = 2 * j + vt;
+                const int row = min(16 * i + (lane >> 2), n - 1);
+                lds_dma16(v + (head0 + (size_t)(t0 + row) * H) * DV + j0 + 8 * (lane & 3),
+                          lds_v + (cc & 1) * (C * BV * 2) + i * 1024);
+            }
+        };
+        auto kq0 = [&](int cc) { return lds_kq0 + (cc & 1) * (16 * 1024); };
+        bf16x8 ah[6], al[6], ahn[6], aln[6];
         auto load_out_ops = [&](int cc) {  // chunk cc's A fragments
             const char *rec = recs + (size_t)cc * kPcBytes;
 #pragma unroll
             for (int f = 0; f < 6; ++f) {
-                ah[f] = *reinterpret_cast<const bf16x8 *>(rec + kRecAH + f * kFragBytes + lane * 16);
-                al[f] = *reinterpret_cast<const bf16x8 *>(rec + kRecAL + f * kFragBytes + lane * 16);
+                ahn[f] = *reinterpret_cast<const bf16x8 *>(rec + kRecAH + f * kFragBytes + lane * 16);
+                aln[f] = *reinterpret_cast<const bf16x8 *>(rec + kRecAL + f * kFragBytes + lane * 16);
             }
         };
-        auto outputs = [&](int cp, int half) __attribute__((always_inline)) {
+        auto outputs = [&](int cp) __attribute__((always_inline)) {
             const int t0 = cp * C;
-            chunk_outputs<OUT_BF16>(&sm.X[cp & 1][half][0][0], ah, al, sm.Ost, o, head0 + (size_t)t0 * H,
-                                    min(C, T - t0), H, j0 + 16 * half, lane);
+            chunk_outputs<OUT_BF16>(&sm.X[cp & 1][vt][0][0], ah, al, sm.Ost, o,
+                                    head0 + (size_t)t0 * H, min(C, T - t0), H, j0 + 16 * vt, lane);
         };
-        barrier_lds();
+        copy_to_lds<16>(recs + kPcKq, kq0(0), vt, lane);
+        copy_to_lds<48>(recs + kPcKq + 16 * 1024, lds_kq123, vt, lane);
+        copy_v(0);
+        barrier_after_loads();
         for (int c = 0; c < NC; ++c) {
-            if (c >= 1) outputs(c - 1, 0);
-            barrier_lds();  // A(c)
-            if (c >= 1) outputs(c - 1, 1);
+            // chain: K~ S, Q~ S of chunk c (key block 0 from its own buffer)
+            const char *rc = recs + (size_t)c * kPcBytes;
+            const char *rn = recs + (size_t)min(c + 1, NC - 1) * kPcBytes;
             load_out_ops(c);
-            barrier_lds();  // B(c)
+            copy_to_lds<32>(rc + kPcKu, lds_ku, vt, lane);
+            lds_dma4(rc + kPcGend + vt * 256 + lane * 4, lds_gend + vt * 256);
+            copy_to_lds<16>(rn + kPcKq, kq0(c + 1), vt, lane);
+            if (c + 1 < NC) copy_v(c + 1);
+            if (vt == 0 && c >= 1) outputs(c - 1);
+            barrier_after_loads();  // A(c)
+            // chain: E and the state update of chunk c
+            copy_to_lds<48>(rn + kPcKq + 16 * 1024, lds_kq123, vt, lane);
+            if (vt == 1 && c >= 1) outputs(c - 1);
+#pragma unroll
+            for (int f = 0; f < 6; ++f) {
+                ah[f] = ahn[f];
+                al[f] = aln[f];
+            }
+            barrier_after_loads();  // B(c)
         }
-        outputs(NC - 1, 0);
-        outputs(NC - 1, 1);
+        if (vt == 0) outputs(NC - 1);
+        barrier_lds();
+        if (vt == 1) outputs(NC - 1);
         barrier_lds();
     }
 }
