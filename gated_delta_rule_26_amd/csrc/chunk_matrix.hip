@@ -27,13 +27,14 @@
 //    order.  Two "chain" wavefronts each own the fp32 state of 16 value
 //    columns in registers and do the dependent work of a chunk:
 //    P = K S, X = V - Gam P, E = T'' X, S <- gend S + K^T (Gend E).  Their
-//    operands stay in registers from one product to the next (see Layout),
-//    so a chunk needs no exchange between chain wavefronts.  They also form
+//    operands stay in registers from one product to the next (the layout in
+//    matrix_common.h), so a chunk needs no exchange between chain wavefronts.  They also form
 //    the read Q S, which shares the state operand with K S.  Two "helper"
 //    wavefronts stage the next chunk's q, k, v and decays in LDS and, one
 //    chunk behind, finish the outputs O = scale Gam (Q S) + A E from the
 //    chain's Q S and E, passed through LDS.  One barrier per chunk; every LDS
-//    buffer that crosses it is doubled.
+//    buffer that crosses it is doubled (exp(G) tripled: the helpers read it
+//    one chunk after the chain).
 //
 // The operand layout (a D tile is directly the B operand of the next
 // product) and the bf16 hi/lo precision scheme are described in
@@ -230,7 +231,7 @@ struct alignas(16) StateSmem {
     __bf16 K[2][C * LDK];          // k, token-major, key channels permuted within 32-blocks
     __bf16 Q[2][C * LDK];          // q, the same layout
     __bf16 V[2][C * LDV];          // v slice, token-major
-    float Gam[2][C];               // exp(G_i)
+    float Gam[3][C];               // exp(G_i); chunk c in buffer c % 3 (read one chunk later by the helpers)
     float Gend[2][C];              // exp(G_63 - G_i)
     uint4 X[2][2][kXFrags][64];    // per chain wavefront and chunk parity
     float Ost[2][C * 20];          // per helper: its fp32 output tile, token-major, for 16-byte stores
@@ -349,23 +350,22 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
             // decays and this wavefront's v columns
             f32x4 gam[4], gnd[4];
             bf16x4 vv[4];
-            const float gs = sm.Gam[buf][C - 1];  // exp(G_63), the chunk's state decay
+            const float *gamc = sm.Gam[c % 3];
+            const float gs = gamc[C - 1];  // exp(G_63), the chunk's state decay
 #pragma unroll
             for (int M = 0; M < 4; ++M) {
-                gam[M] = *reinterpret_cast<const f32x4 *>(&sm.Gam[buf][16 * M + 4 * lg]);
+                gam[M] = *reinterpret_cast<const f32x4 *>(&gamc[16 * M + 4 * lg]);
                 gnd[M] = *reinterpret_cast<const f32x4 *>(&sm.Gend[buf][16 * M + 4 * lg]);
                 // V[16M + 4lg + r][16w + lr], r = 0..3
                 vv[M] = lds_read_tr(&sm.V[buf][(16 * M + 4 * lg + (lr >> 2)) * LDV + 16 * w + 4 * (lr & 3)]);
             }
-            // X = V - Gam P, rows 16M + 4lg + r; the read scale Gam Q S to the helper
+            // X = V - Gam P, rows 16M + 4lg + r; the read Q S to the helper
+            // (which applies scale Gam)
             f32x4 Xv[4];
 #pragma unroll
             for (int M = 0; M < 4; ++M) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    Xv[M][r] = static_cast<float>(vv[M][r]) - gam[M][r] * P[M][r];
-                    QS[M][r] *= scale * gam[M][r];
-                }
+                for (int r = 0; r < 4; ++r) Xv[M][r] = static_cast<float>(vv[M][r]) - gam[M][r] * P[M][r];
                 xo[M * 64 + lane] = *reinterpret_cast<const uint4 *>(&QS[M]);
             }
             bf16x8 XH[2], XL[2];
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
                     *reinterpret_cast<uint4 *>(&sm.V[buf][(2 * tq + u) * LDV + 8 * sv]) = vreg[u];
             }
             if (ht < C) {
-                sm.Gam[buf][ht] = gam_reg;
+                sm.Gam[cc % 3][ht] = gam_reg;
                 sm.Gend[buf][ht] = gnd_reg;
             }
         };
@@ -515,11 +515,11 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
                 al[f] = *reinterpret_cast<const bf16x8 *>(rec + kRecAL + f * kFragBytes + lane * 16);
             }
         };
-        // outputs of chunk cp: O = (scale Gam Q S, from the chain) + A E
+        // outputs of chunk cp: O = scale Gam (Q S, from the chain) + A E
         auto outputs = [&](int cp) __attribute__((always_inline)) {
             const int t0 = cp * C;
-            chunk_outputs<OUT_BF16>(&sm.X[cp & 1][vt][0][0], ah, al, sm.Ost[vt], o, head0 + (size_t)t0 * H,
-                                    min(C, T - t0), H, jt, lane);
+            chunk_outputs<OUT_BF16, true>(&sm.X[cp & 1][vt][0][0], sm.Gam[cp % 3], scale, ah, al, sm.Ost[vt], o,
+                                          head0 + (size_t)t0 * H, min(C, T - t0), H, jt, lane);
         };
         // step 0: stage chunk 0 (and 1); step c >= 1: outputs of chunk c-1
         load_stage(0);

@@ -585,8 +585,8 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
         };
         auto outputs = [&](int cp) __attribute__((always_inline)) {
             const int t0 = cp * C;
-            chunk_outputs<OUT_BF16>(&sm.X[cp & 1][vt][0][0], ah, al, sm.Ost, o,
-                                    head0 + (size_t)t0 * H, min(C, T - t0), H, j0 + 16 * vt, lane);
+            chunk_outputs<OUT_BF16, false>(&sm.X[cp & 1][vt][0][0], nullptr, 1.f, ah, al, sm.Ost, o,
+                                           head0 + (size_t)t0 * H, min(C, T - t0), H, j0 + 16 * vt, lane);
         };
         copy_to_lds<16>(recs + kPcKq, kq0(0), vt, lane);
         copy_to_lds<48>(recs + kPcKq + 16 * 1024, lds_kq123, vt, lane);

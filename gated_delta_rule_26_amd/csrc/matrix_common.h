@@ -42,25 +42,39 @@ __device__ __forceinline__ f32x4 mma32(float a, float b, f32x4 c) {
 // Index, inside a 32-block, of term e (0..7) of lane group p (0..3).
 __host__ __device__ constexpr int kperm(int p, int e) { return e < 4 ? 4 * p + e : 12 + 4 * p + e; }
 
+// Two fp32 values as bf16 hi (round to nearest even) and lo (the rounded
+// residual), each pair packed in one 32-bit word: element 0 in the low half.
+// The hi values are recovered from the packed word by a shift and a mask,
+// so a pair costs two conversions, two bit operations and two subtractions.
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+    const bf16x2 h = {static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
+    hi = __builtin_bit_cast(uint32_t, h);
+    const bf16x2 l = {static_cast<__bf16>(x0 - __uint_as_float(hi << 16)),
+                      static_cast<__bf16>(x1 - __uint_as_float(hi & 0xffff0000u))};
+    lo = __builtin_bit_cast(uint32_t, l);
+}
+
 // Two stacked D tiles (block rows 0..15 and 16..31) as one permuted operand,
 // split into bf16 hi and lo.
 __device__ __forceinline__ void pair_split(f32x4 t0, f32x4 t1, bf16x8 &hi, bf16x8 &lo) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        hi[r] = static_cast<__bf16>(t0[r]);
-        lo[r] = static_cast<__bf16>(t0[r] - static_cast<float>(hi[r]));
-        hi[4 + r] = static_cast<__bf16>(t1[r]);
-        lo[4 + r] = static_cast<__bf16>(t1[r] - static_cast<float>(hi[4 + r]));
-    }
+    uint4 h, l;
+    split2(t0[0], t0[1], h.x, l.x);
+    split2(t0[2], t0[3], h.y, l.y);
+    split2(t1[0], t1[1], h.z, l.z);
+    split2(t1[2], t1[3], h.w, l.w);
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
 }
 
 // Eight fp32 values as bf16 hi + lo.
 __device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        hi[e] = static_cast<__bf16>(x[e]);
-        lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(hi[e]));
-    }
+    uint4 h, l;
+    split2(x[0], x[1], h.x, l.x);
+    split2(x[2], x[3], h.y, l.y);
+    split2(x[4], x[5], h.z, l.z);
+    split2(x[6], x[7], h.w, l.w);
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
 }
 
 // ---- per-chunk record, common head: T'' hi, T'' lo, A hi, A lo, each the six
@@ -254,14 +268,17 @@ __device__ __forceinline__ void state_slot(int x, int BH, int &bh, int &slice) {
 }
 
 // Outputs of one chunk on a helper wavefront: O = QS + A E, where QS (the
-// decayed, scaled read of the state) and E (fp32) come from the chain
-// wavefront of value columns jt .. jt+15 through LDS (xi: 8 tiles of 64 lanes
-// x 16 bytes) and ah, al are the A fragments.  Rows past the end of the
+// read of the state) and E (fp32) come from the chain wavefront of value
+// columns jt .. jt+15 through LDS (xi: 8 tiles of 64 lanes x 16 bytes) and
+// ah, al are the A fragments.  With ROW_SCALE, QS still lacks the output
+// scale and the decay of its token (row i is multiplied by scale
+// row_scale[i] here); otherwise it is final.  Rows past the end of the
 // sequence are dropped by the buffer bounds.  The fp32 tile goes through the
 // wavefront's own LDS area `ost` so that each lane stores 16-byte rows.
-template <bool OUT_BF16>
-__device__ __forceinline__ void chunk_outputs(const uint4 *xi, const bf16x8 *ah, const bf16x8 *al, float *ost,
-                                              void *o, size_t row0, int n, int H, int jt, int lane) {
+template <bool OUT_BF16, bool ROW_SCALE>
+__device__ __forceinline__ void chunk_outputs(const uint4 *xi, const float *row_scale, float scale,
+                                              const bf16x8 *ah, const bf16x8 *al, float *ost, void *o, size_t row0,
+                                              int n, int H, int jt, int lane) {
     const int lr = lane & 15, lg = lane >> 4;
     f32x4 O[4], E[4];
     bf16x8 eh[2], el[2];
@@ -269,6 +286,11 @@ __device__ __forceinline__ void chunk_outputs(const uint4 *xi, const bf16x8 *ah,
     for (int M = 0; M < 4; ++M) {
         *reinterpret_cast<uint4 *>(&O[M]) = xi[M * 64 + lane];
         *reinterpret_cast<uint4 *>(&E[M]) = xi[(4 + M) * 64 + lane];
+        if constexpr (ROW_SCALE) {
+            const f32x4 rs = *reinterpret_cast<const f32x4 *>(&row_scale[16 * M + 4 * lg]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O[M][r] *= scale * rs[r];
+        }
     }
     pair_split(E[0], E[1], eh[0], el[0]);
     pair_split(E[2], E[3], eh[1], el[1]);
