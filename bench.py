@@ -30,32 +30,43 @@ PEAK_HBM = 8000.0            # GB/s, MI355X HBM3E
 
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE (x2.0) + WRITE_SIZE (x1.0), scaled by a 1 GiB device
-# copy read in the same runs.  Each figure holds only for the kernel source it was measured on: when the
-# file's sha256 differs, the figure is reported as null.
+# copy read in the same runs, by (algorithm, kernel, workload).  Each figure holds only for the sources it
+# was measured on: when the sha256 of those files (concatenated in order) differs, it is reported as null.
+_SCALAR = ("gated_delta_rule_26_amd/csrc/chunk_matrix.hip", "gated_delta_rule_26_amd/csrc/matrix_common.h")
+_PER_CHANNEL = ("gated_delta_rule_26_amd/csrc/chunk_matrix_pc.hip", "gated_delta_rule_26_amd/csrc/matrix_common.h")
+_DECODE = ("gated_delta_rule_26_amd/csrc/recurrent_step.hip",)
 MEASURED_TRAFFIC = {
-    ("matrix", "state"): ("gated_delta_rule_26_amd/csrc/chunk_matrix.hip",
-                          "89317b5477734d1bbd514c3fa74d190bfe1db742dadebc46582fc713799f5531",
-                          (148649.4 * 2.0 + 135174.4) * 1024),
-    ("matrix", "intra"): ("gated_delta_rule_26_amd/csrc/chunk_matrix.hip",
-                          "89317b5477734d1bbd514c3fa74d190bfe1db742dadebc46582fc713799f5531",
-                          (66891.4 * 2.0 + 100352.0) * 1024),
-    ("decode", "step"): ("gated_delta_rule_26_amd/csrc/recurrent_step.hip",
-                         "e7e419c4fce8d18e58aad36eae998f3c36e35efc9c754b1783925800a8b15b99",
-                         (133011.2 * 2.0 + 264192.0) * 1024),
+    ("matrix", "state", "gdn_prefill"): (_SCALAR, "b6c217d8667d324d1fee1e26743024515a94bbeaaece3dcd9be2279e189ee20c",
+                                         (148653.9 * 2.0 + 135171.2) * 1024),
+    ("matrix", "intra", "gdn_prefill"): (_SCALAR, "b6c217d8667d324d1fee1e26743024515a94bbeaaece3dcd9be2279e189ee20c",
+                                         (66892.7 * 2.0 + 100352.0) * 1024),
+    ("matrix", "state", "kda_prefill"): (_PER_CHANNEL, "0e9f80c15c9123a5d79f953fd4cc9292bc9187820a1470dd1f83249232db0959",
+                                         (279754.2 * 2.0 + 133120.0) * 1024),
+    ("matrix", "intra", "kda_prefill"): (_PER_CHANNEL, "0e9f80c15c9123a5d79f953fd4cc9292bc9187820a1470dd1f83249232db0959",
+                                         (134538.2 * 2.0 + 493568.1) * 1024),
+    ("decode", "step", "decode"): (_DECODE, "e7e419c4fce8d18e58aad36eae998f3c36e35efc9c754b1783925800a8b15b99",
+                                   (133011.2 * 2.0 + 264192.0) * 1024),
 }
 
 
-def measured_traffic(path_kind: str, kernel: str):
-    """Counter-measured HBM bytes per launch, or None if not measured on the current source."""
+def sources_sha(files) -> str:
     import hashlib
-    entry = MEASURED_TRAFFIC.get((path_kind, kernel))
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(path_kind: str, kernel: str, workload: str):
+    """Counter-measured HBM bytes per launch, or None if not measured on the current sources."""
+    entry = MEASURED_TRAFFIC.get((path_kind, kernel, workload))
     if entry is None:
         return None
-    src, sha, nbytes = entry
+    files, sha, nbytes = entry
     try:
-        with open(os.path.join(ROOT, src), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != sha:
-                return None
+        if sources_sha(files) != sha:
+            return None
     except OSError:
         return None
     return nbytes
@@ -306,7 +317,7 @@ def main():
                    "B": w.B, "T": w.T, "H": w.H, "Dk": w.Dk, "Dv": w.Dv, "chunk": C,
                    "algo": algo, "o_dtype": args.o_dtype},
         "roofline": {"bound": bound, "kernel": f"{dom} ({algo} path)", "achieved": achieved, "peak": peak,
-                     "unit": unit, "frac": achieved / peak, "traffic": measured_traffic(algo, dom),
+                     "unit": unit, "frac": achieved / peak, "traffic": measured_traffic(algo, dom, w.name),
                      "alg_bytes_per_launch": dom_bytes, "alg_flops_per_launch": dom_flops,
                      "avg_launch_ms": dom_ms,
                      "mfma_view": {"achieved_tflops": mfma_view, "peak_tflops": PEAK_BF16_MFMA,
@@ -332,7 +343,7 @@ def main():
             "ms_per_step": dms, "ms_per_step_median": median(dec["step_ms"]),
             "tokens_per_s": wd.B / (dms * 1e-3),
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM, "unit": "GB/s",
-                         "frac": gbps / PEAK_HBM, "traffic": measured_traffic("decode", "step"),
+                         "frac": gbps / PEAK_HBM, "traffic": measured_traffic("decode", "step", "decode"),
                          "alg_bytes_per_launch": dbytes,
                          "avg_launch_ms": dms},
         }
