@@ -225,7 +225,11 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
 }
 
 // ============================================================ state kernel
-constexpr int LDK = DK + 8;  // bf16 row stride of the token-major q, k
+// bf16 row stride of the token-major q, k: 288 bytes keeps both the 16-byte
+// fragment reads and the transposing 8-byte reads of four rows free of LDS
+// bank conflicts (272 bytes costs the transposing reads a third more, 320
+// bytes doubles the 16-byte reads; measured on gfx950)
+constexpr int LDK = DK + 16;
 
 struct alignas(16) StateSmem {
     __bf16 K[2][C * LDK];          // k, token-major, key channels permuted within 32-blocks
