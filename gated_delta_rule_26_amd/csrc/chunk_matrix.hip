@@ -39,6 +39,8 @@
 // The operand layout (a D tile is directly the B operand of the next
 // product) and the bf16 hi/lo precision scheme are described in
 // matrix_common.h.
+#include <cmath>
+
 #include "matrix_common.h"
 
 namespace gdr {
@@ -248,31 +250,48 @@ __device__ __forceinline__ int kperm_col(int seg, int hh) {
     return 32 * (seg >> 2) + 8 * ((2 * s + hh) & 3) + 4 * (s >> 1);
 }
 
-template <bool OUT_BF16>
+// The walk over the chunks of G = BH * P groups (sequence, head, time
+// segment p): group g = bh * P + p covers chunks [p seg, min(NC, (p+1) seg)).
+// With P = 1 this is the whole sequence.
+//  * TRANSFER = false: s0 (or zero) holds the entering state of every group
+//    ([G][DK][DV]); the last segment of each sequence writes its final state
+//    to s_out[bh]; outputs are written.
+//  * TRANSFER = true: the group's chunk map S -> M S + N (substituting
+//    E = T''(V - Gam K S) into the chunk-end state, [P2] "KDA por chunks",
+//    chunk-end state): slices 0 .. NS-1 walk N (zero start, v), slices NS ..
+//    2NS-1 walk the columns of M (identity start, v = 0); N and M go to
+//    s_out[g][0] and s_out[g][1].  No outputs.
+template <bool OUT_BF16, bool TRANSFER>
 __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const char *__restrict__ ws, const float *__restrict__ s0, void *__restrict__ o,
-    float *__restrict__ s_final, int T, int H, int NC, int BH, float scale) {
+    float *__restrict__ s_out, int T, int H, int NC, int G, int P, int seg, float scale) {
     __shared__ StateSmem sm;
 
-    int bh, slice;
-    state_slot(blockIdx.x, BH, bh, slice);
+    int g, slice;
+    state_slot(blockIdx.x, G, TRANSFER ? 2 * NS : NS, g, slice);
+    const int bh = g / P, p = g % P;
+    const int kind = TRANSFER ? slice / NS : 0;  // transfer: 0 = N, 1 = M
+    const int c0 = p * seg;
+    const int nc = min(seg, NC - c0);            // chunks of this segment
     const int b = bh / H, h = bh % H;
-    const int j0 = slice * BV;
+    const int j0 = (slice % NS) * BV;
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
-    const char *recs = ws + (size_t)bh * NC * kRecBytes;
-    const size_t sbase = (size_t)bh * DK * DV;
+    const char *recs = ws + ((size_t)bh * NC + c0) * kRecBytes;
+    const float *s_in = TRANSFER || !s0 ? nullptr : s0 + (size_t)g * DK * DV;
+    float *s_end = TRANSFER ? s_out + ((size_t)g * 2 + kind) * DK * DV
+                            : (s_out && p == P - 1 ? s_out + (size_t)bh * DK * DV : nullptr);
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    if (NC == 0) {  // empty sequence: the final state is the initial one
-        if (s_final && w < 2) {
+    if (nc <= 0) {  // empty sequence: the final state is the initial one
+        if (s_end && w < 2) {
             const int jt = j0 + 16 * w;
             for (int i = 0; i < 8; ++i)
                 for (int r = 0; r < 4; ++r) {
-                    const size_t idx = sbase + (size_t)(16 * i + 4 * lg + r) * DV + jt + lr;
-                    s_final[idx] = s0 ? s0[idx] : 0.f;
+                    const size_t idx = (size_t)(16 * i + 4 * lg + r) * DV + jt + lr;
+                    s_end[idx] = s_in ? s_in[idx] : 0.f;
                 }
         }
         return;
@@ -292,8 +311,11 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                S[i][r] = s0 ? s0[sbase + (size_t)(16 * i + 4 * lg + r) * DV + jt + lr] : 0.f;
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * i + 4 * lg + r;
+                if constexpr (TRANSFER) S[i][r] = kind == 1 && row == jt + lr ? 1.f : 0.f;
+                else S[i][r] = s_in ? s_in[(size_t)row * DV + jt + lr] : 0.f;
+            }
         // T'' fragments of even chunks in tA, of odd chunks in tB: each chunk
         // loads the next one's into the other set (no register copies).
         bf16x8 tAh[6], tAl[6], tBh[6], tBl[6];
@@ -307,7 +329,7 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
             const int buf = c & 1;
             // next chunk's T'' fragments, in flight during this chunk
             {
-                const char *rn = recs + (size_t)min(c + 1, NC - 1) * kRecBytes;
+                const char *rn = recs + (size_t)min(c + 1, nc - 1) * kRecBytes;
 #pragma unroll
                 for (int f = 0; f < 6; ++f) {
                     thn[f] = *reinterpret_cast<const bf16x8 *>(rn + kRecTH + f * kFragBytes + lane * 16);
@@ -330,7 +352,7 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
 #pragma unroll
             for (int M = 0; M < 4; ++M) {
                 ka[0][M] = *reinterpret_cast<const bf16x8 *>(&sK[(16 * M + lr) * LDK + 8 * lg]);
-                qa[0][M] = *reinterpret_cast<const bf16x8 *>(&sQ[(16 * M + lr) * LDK + 8 * lg]);
+                if constexpr (!TRANSFER) qa[0][M] = *reinterpret_cast<const bf16x8 *>(&sQ[(16 * M + lr) * LDK + 8 * lg]);
             }
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
@@ -339,17 +361,20 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
 #pragma unroll
                     for (int M = 0; M < 4; ++M) {
                         ka[cur ^ 1][M] = *reinterpret_cast<const bf16x8 *>(&sK[(16 * M + lr) * LDK + 32 * (kb + 1) + 8 * lg]);
-                        qa[cur ^ 1][M] = *reinterpret_cast<const bf16x8 *>(&sQ[(16 * M + lr) * LDK + 32 * (kb + 1) + 8 * lg]);
+                        if constexpr (!TRANSFER)
+                            qa[cur ^ 1][M] = *reinterpret_cast<const bf16x8 *>(&sQ[(16 * M + lr) * LDK + 32 * (kb + 1) + 8 * lg]);
                     }
                 }
 #pragma unroll
                 for (int M = 0; M < 4; ++M) P[M] = mma(ka[cur][M], SH[kb], P[M]);
 #pragma unroll
                 for (int M = 0; M < 4; ++M) P[M] = mma(ka[cur][M], SL[kb], P[M]);
+                if constexpr (!TRANSFER) {  // the read Q S (no outputs in a transfer walk)
 #pragma unroll
-                for (int M = 0; M < 4; ++M) QS[M] = mma(qa[cur][M], SH[kb], QS[M]);
+                    for (int M = 0; M < 4; ++M) QS[M] = mma(qa[cur][M], SH[kb], QS[M]);
 #pragma unroll
-                for (int M = 0; M < 4; ++M) QS[M] = mma(qa[cur][M], SL[kb], QS[M]);
+                    for (int M = 0; M < 4; ++M) QS[M] = mma(qa[cur][M], SL[kb], QS[M]);
+                }
             }
             // decays and this wavefront's v columns
             f32x4 gam[4], gnd[4];
@@ -370,7 +395,7 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
             for (int M = 0; M < 4; ++M) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) Xv[M][r] = static_cast<float>(vv[M][r]) - gam[M][r] * P[M][r];
-                xo[M * 64 + lane] = *reinterpret_cast<const uint4 *>(&QS[M]);
+                if constexpr (!TRANSFER) xo[M * 64 + lane] = *reinterpret_cast<const uint4 *>(&QS[M]);
             }
             bf16x8 XH[2], XL[2];
             pair_split(Xv[0], Xv[1], XH[0], XL[0]);
@@ -405,7 +430,7 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
             f32x4 Ep[4];
 #pragma unroll
             for (int M = 0; M < 4; ++M) {
-                xo[(4 + M) * 64 + lane] = *reinterpret_cast<const uint4 *>(&E[M]);
+                if constexpr (!TRANSFER) xo[(4 + M) * 64 + lane] = *reinterpret_cast<const uint4 *>(&E[M]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) Ep[M][r] = E[M][r] * gnd[M][r];
             }
@@ -431,23 +456,22 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
         };
         barrier_lds();
         int c = 0;
-        for (; c + 1 < NC; c += 2) {
+        for (; c + 1 < nc; c += 2) {
             step(c, tAh, tAl, tBh, tBl);
             barrier_lds();
             step(c + 1, tBh, tBl, tAh, tAl);
             barrier_lds();
         }
-        if (c < NC) {
+        if (c < nc) {
             step(c, tAh, tAl, tBh, tBl);
             barrier_lds();
         }
-        barrier_lds();  // step NC: the helpers finish the last chunk's outputs
-        if (s_final) {
+        barrier_lds();  // step nc: the helpers finish the last chunk's outputs
+        if (s_end) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    s_final[sbase + (size_t)(16 * i + 4 * lg + r) * DV + jt + lr] = S[i][r];
+                for (int r = 0; r < 4; ++r) s_end[(size_t)(16 * i + 4 * lg + r) * DV + jt + lr] = S[i][r];
         }
     } else {
         // ================= helper wavefront: stages chunk c+1, outputs of chunk c-1
@@ -467,16 +491,16 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
 #pragma unroll
         for (int u = 0; u < 2; ++u) v_off[u] = (2 * (ht >> 2) + u) * v_stride + 2 * (j0 + 8 * (ht & 3));
         auto load_stage = [&](int cc) {  // chunk cc's q, k, v slice and G into registers
-            const int t0 = cc * C;
+            const int t0 = (c0 + cc) * C;
             const int n = min(C, T - t0);
             const size_t row0 = head0 + (size_t)t0 * H;
             const auto rk = rows_rsrc(k + row0 * DK, n, qk_stride, DK * 2);
             const auto rq = rows_rsrc(q + row0 * DK, n, qk_stride, DK * 2);
-            const auto rv = rows_rsrc(v + row0 * DV, n, v_stride, DV * 2);
+            const auto rv = rows_rsrc(v + row0 * DV, kind == 1 ? 0 : n, v_stride, DV * 2);  // M columns: v = 0
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 kreg[u] = buf_ld16(rk, qk_off[u]);
-                qreg[u] = buf_ld16(rq, qk_off[u]);
+                if constexpr (!TRANSFER) qreg[u] = buf_ld16(rq, qk_off[u]);
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) vreg[u] = buf_ld16(rv, v_off[u]);
@@ -496,7 +520,7 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
                 for (int hh = 0; hh < 2; ++hh) {
                     const int col = kperm_col(seg, hh);
                     *reinterpret_cast<uint2 *>(&sm.K[buf][i * LDK + col]) = kh[hh];
-                    *reinterpret_cast<uint2 *>(&sm.Q[buf][i * LDK + col]) = qh[hh];
+                    if constexpr (!TRANSFER) *reinterpret_cast<uint2 *>(&sm.Q[buf][i * LDK + col]) = qh[hh];
                 }
             }
             {
@@ -519,30 +543,78 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
                 al[f] = *reinterpret_cast<const bf16x8 *>(rec + kRecAL + f * kFragBytes + lane * 16);
             }
         };
-        // outputs of chunk cp: O = scale Gam (Q S, from the chain) + A E
+        // outputs of chunk cp: O = scale Gam (Q S, from the chain) + A E (none
+        // for a transfer walk)
         auto outputs = [&](int cp) __attribute__((always_inline)) {
-            const int t0 = cp * C;
-            chunk_outputs<OUT_BF16, true>(&sm.X[cp & 1][vt][0][0], sm.Gam[cp % 3], scale, ah, al, sm.Ost[vt], o,
-                                          head0 + (size_t)t0 * H, min(C, T - t0), H, jt, lane);
+            if constexpr (!TRANSFER) {
+                const int t0 = (c0 + cp) * C;
+                chunk_outputs<OUT_BF16, true>(&sm.X[cp & 1][vt][0][0], sm.Gam[cp % 3], scale, ah, al, sm.Ost[vt],
+                                              o, head0 + (size_t)t0 * H, min(C, T - t0), H, jt, lane);
+            }
+        };
+        auto load_outputs_operands = [&](int cc) {
+            if constexpr (!TRANSFER) load_out_ops(cc);
         };
         // step 0: stage chunk 0 (and 1); step c >= 1: outputs of chunk c-1
         load_stage(0);
         store_stage(0);
-        load_stage(min(1, NC - 1));
+        load_stage(min(1, nc - 1));
         barrier_lds();
-        if (NC > 1) store_stage(1);
-        load_stage(min(2, NC - 1));
-        load_out_ops(0);
+        if (nc > 1) store_stage(1);
+        load_stage(min(2, nc - 1));
+        load_outputs_operands(0);
         barrier_lds();
-        for (int c = 1; c < NC; ++c) {
-            if (c + 1 < NC) store_stage(c + 1);
-            load_stage(min(c + 2, NC - 1));
+        for (int c = 1; c < nc; ++c) {
+            if (c + 1 < nc) store_stage(c + 1);
+            load_stage(min(c + 2, nc - 1));
             outputs(c - 1);
-            load_out_ops(c);
+            load_outputs_operands(c);
             barrier_lds();
         }
-        outputs(NC - 1);
+        outputs(nc - 1);
         barrier_lds();
+    }
+}
+
+// ============================================================ segment combine
+// Entering state of every time segment of a sequence: S_0 = s0 (or zero),
+// S_{p+1} = M_p S_p + N_p, from the chunk maps of the transfer walk.  One
+// workgroup per (sequence, head); thread t forms row t / 8, columns
+// 16 (t % 8) .. +15 of each product in fp32 (M_p from memory, S_p in LDS).
+__global__ __launch_bounds__(1024) void segment_combine_kernel(const float *__restrict__ tr,
+                                                               const float *__restrict__ s0,
+                                                               float *__restrict__ seg_state, int P) {
+    __shared__ float Ss[DK * DV];
+    const int bh = blockIdx.x, t = threadIdx.x;
+    const int i = t >> 3, jb = 16 * (t & 7);
+    const size_t mat = (size_t)DK * DV;
+    const float *sin = s0 ? s0 + bh * mat : nullptr;
+    float *out0 = seg_state + (size_t)bh * P * mat;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+        const float x = sin ? sin[i * DV + jb + jj] : 0.f;
+        Ss[i * DV + jb + jj] = x;
+        out0[i * DV + jb + jj] = x;
+    }
+    for (int pp = 0; pp + 1 < P; ++pp) {
+        __syncthreads();
+        const float *N = tr + ((size_t)(bh * P + pp) * 2 + 0) * mat;
+        const float *M = tr + ((size_t)(bh * P + pp) * 2 + 1) * mat;
+        float acc[16];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) acc[jj] = N[i * DV + jb + jj];
+        for (int kk = 0; kk < DK; ++kk) {
+            const float m = M[i * DK + kk];
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) acc[jj] = fmaf(m, Ss[kk * DV + jb + jj], acc[jj]);
+        }
+        __syncthreads();
+        float *out = seg_state + ((size_t)bh * P + pp + 1) * mat;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+            Ss[i * DV + jb + jj] = acc[jj];
+            out[i * DV + jb + jj] = acc[jj];
+        }
     }
 }
 
@@ -557,14 +629,58 @@ hipError_t launch_intra(const ChunkArgs &a) {
     return hipGetLastError();
 }
 
+// Time segments of the walk.  Each walk is one workgroup per (group, 32 value
+// columns) and the walk is latency-bound, so a few long sequences leave most
+// compute units idle; splitting each sequence into P segments costs a
+// transfer walk of twice the columns plus a walk per segment, in
+// (ceil(2 P BH NS / CUs) + ceil(P BH NS / CUs)) / P of the single walk's
+// time.  P is the smallest power of two that minimises that (planned for
+// 256 compute units so that the workspace size does not depend on the
+// device), with at least 32 chunks per segment.
+int walk_segments(int BH, int NC) {
+    constexpr double kPlanCUs = 256.0;
+    int best = 1;
+    double best_cost = std::ceil(BH * NS / kPlanCUs);
+    for (int P = 2; P <= 16; P *= 2) {
+        if (NC < 32 * P) break;
+        const double cost = (std::ceil(2.0 * P * BH * NS / kPlanCUs) + std::ceil(1.0 * P * BH * NS / kPlanCUs)) / P;
+        if (cost < best_cost - 1e-9) {
+            best_cost = cost;
+            best = P;
+        }
+    }
+    return best;
+}
+
+size_t segment_bytes(int BH, int NC) {
+    const int P = walk_segments(BH, NC);
+    return P > 1 ? (size_t)BH * P * 3 * DK * DV * sizeof(float) : 0;
+}
+
 template <bool OB>
 hipError_t launch_state(const ChunkArgs &a) {
     const int BH = a.B * a.H;
-    const unsigned grid = (unsigned)(BH * NS);
-    hipLaunchKernelGGL((state_matrix_kernel<OB>), dim3(grid), dim3(kStateThreads), 0, a.stream,
-                       static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k),
-                       static_cast<const __bf16 *>(a.v), static_cast<const char *>(a.ws), a.s0, a.o, a.s_final,
-                       a.T, a.H, a.NC, BH, a.scale);
+    const int P = walk_segments(BH, a.NC);
+    const __bf16 *q = static_cast<const __bf16 *>(a.q), *k = static_cast<const __bf16 *>(a.k),
+                 *v = static_cast<const __bf16 *>(a.v);
+    const char *ws = static_cast<const char *>(a.ws);
+    if (P == 1) {
+        hipLaunchKernelGGL((state_matrix_kernel<OB, false>), dim3((unsigned)(BH * NS)), dim3(kStateThreads), 0,
+                           a.stream, q, k, v, ws, a.s0, a.o, a.s_final, a.T, a.H, a.NC, BH, 1, a.NC, a.scale);
+        return hipGetLastError();
+    }
+    // segments: chunk maps, entering states, then the walks with outputs
+    const int seg = (a.NC + P - 1) / P;
+    float *tr = reinterpret_cast<float *>(static_cast<char *>(a.ws) + (size_t)BH * a.NC * kRecBytes);
+    float *seg_state = tr + (size_t)BH * P * 2 * DK * DV;
+    hipLaunchKernelGGL((state_matrix_kernel<false, true>), dim3((unsigned)(BH * P * 2 * NS)), dim3(kStateThreads), 0,
+                       a.stream, q, k, v, ws, nullptr, nullptr, tr, a.T, a.H, a.NC, BH * P, P, seg, a.scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(segment_combine_kernel, dim3((unsigned)BH), dim3(1024), 0, a.stream, tr, a.s0, seg_state, P);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((state_matrix_kernel<OB, false>), dim3((unsigned)(BH * P * NS)), dim3(kStateThreads), 0,
+                       a.stream, q, k, v, ws, seg_state, a.o, a.s_final, a.T, a.H, a.NC, BH * P, P, seg, a.scale);
     return hipGetLastError();
 }
 
@@ -579,7 +695,8 @@ int mx::intra_grid(long total, int per_cu) {
 }
 
 size_t chunk_matrix_workspace_bytes(int B, int H, int NC, int, int, bool per_channel) {
-    return per_channel ? chunk_matrix_pc_workspace_bytes(B, H, NC) : (size_t)B * H * NC * kRecBytes;
+    return per_channel ? chunk_matrix_pc_workspace_bytes(B, H, NC)
+                       : (size_t)B * H * NC * kRecBytes + segment_bytes(B * H, NC);
 }
 
 bool chunk_matrix_supported(int Dk, int Dv, bool qkv_bf16, bool) { return qkv_bf16 && Dk == DK && Dv == DV; }

@@ -397,7 +397,7 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
     float *__restrict__ s_final, int T, int H, int NC, int BH) {
     __shared__ StatePcSmem sm;
     int bh, slice;
-    state_slot(blockIdx.x, BH, bh, slice);
+    state_slot(blockIdx.x, BH, NS, bh, slice);
     const int b = bh / H, h = bh % H;
     const int j0 = slice * BV;
     const int tid = threadIdx.x;

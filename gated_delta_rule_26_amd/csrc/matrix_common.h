@@ -95,9 +95,10 @@ __host__ __device__ constexpr int frag_kb(int f) { return f < 2 ? 0 : (f - 2) & 
 // bytes apart, starting at `base`: loads past the last row return zero and
 // stores past it are dropped, with no branch in the instruction stream
 // (0x00020000 is the gfx9-family descriptor word for untyped 32-bit data).
+// With rows <= 0 every load returns zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void *base, int rows, int stride, int row_bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (rows - 1) * stride + row_bytes,
-                                             0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                             rows > 0 ? (rows - 1) * stride + row_bytes : 0, 0x00020000);
 }
 __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
@@ -253,17 +254,17 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p) {
 }
 
 // XCD-aware placement of the state walk's workgroups: consecutive workgroup
-// ids go to different XCDs, so the slices of one (sequence, head) get ids
-// that are equal modulo 8 and share that XCD's L2 for q, k, v and the chunk
-// records.
-__device__ __forceinline__ void state_slot(int x, int BH, int &bh, int &slice) {
-    if ((BH & 7) == 0) {
+// ids go to different XCDs, so the nsl slices of one group (sequence, head,
+// time segment) get ids that are equal modulo 8 and share that XCD's L2 for
+// q, k, v and the chunk records.
+__device__ __forceinline__ void state_slot(int x, int groups, int nsl, int &g, int &slice) {
+    if ((groups & 7) == 0) {
         const int xcd = x & 7, r = x >> 3;
-        bh = (r / NS) * 8 + xcd;
-        slice = r % NS;
+        g = (r / nsl) * 8 + xcd;
+        slice = r % nsl;
     } else {
-        bh = x / NS;
-        slice = x % NS;
+        g = x / nsl;
+        slice = x % nsl;
     }
 }
 

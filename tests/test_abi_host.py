@@ -143,6 +143,20 @@ def test_matrix_algo_support_and_workspace():
     assert rc == 0 and (rc, n) == _ws(_desc(Dk=64, Dv=64, per_channel=True, algo="vector"))
 
 
+def test_long_sequence_workspace_includes_segment_states():
+    """A few long sequences are walked in time segments: the workspace adds,
+    per (sequence, head) and segment, the chunk map (two d_k x d_v fp32
+    matrices) and the entering state (one)."""
+    rec = 4 * 6 * 1024 + 2 * 64 * 4
+    # 16 heads x 2048 chunks: 4 segments
+    rc, n = _ws(_desc(B=1, T=131072, H=16, algo="matrix"))
+    assert rc == 0 and n == 16 * 2048 * rec + 16 * 4 * 3 * 128 * 128 * 4
+    # many heads or short sequences: a single walk
+    assert _ws(_desc(B=4, T=4096, H=16, algo="matrix")) == (0, 64 * 64 * rec)
+    assert _ws(_desc(B=1, T=64 * 127, H=1, algo="matrix")) == (0, 127 * rec)
+    assert _ws(_desc(B=1, T=64 * 128, H=1, algo="matrix")) == (0, 128 * rec + 1 * 4 * 3 * 128 * 128 * 4)
+
+
 def test_step_validation_errors():
     lib = gdr.load_library()
     d = _desc(T=1)

@@ -71,23 +71,25 @@ def test_chunk_mixed_widths(algo, D):
 
 
 @pytest.mark.parametrize("algo", ALGOS)
-def test_bf16_output_and_scale(algo):
-    x = _inputs(8, 2, 130, 2, 128, 128, "gdn", "bf16")
+@pytest.mark.parametrize("mode", ["gdn", "kda"])
+def test_bf16_output_and_scale(algo, mode):
+    x = _inputs(8, 2, 130, 2, 128, 128, mode, "bf16")
     sc = 128 ** -0.5
-    o, s = _gpu(x, "gdn", "bf16", algo=algo, o_dtype=torch.bfloat16, scale=sc)
-    o_ref, s_ref = _ref(x, "gdn", scale=sc)
+    o, s = _gpu(x, mode, "bf16", algo=algo, o_dtype=torch.bfloat16, scale=sc)
+    o_ref, s_ref = _ref(x, mode, scale=sc)
     eo = rel(host(o), o_ref)
-    print(f"bf16 output: rel o {eo:.2e}")
+    print(f"bf16 output {mode} {algo}: rel o {eo:.2e}")
     assert eo < TOL["bf16"] and rel(host(s), s_ref) < TOL["bf16"]
 
 
-def test_empty_and_zero_length():
-    x = _inputs(9, 2, 0, 2, 64, 64, "gdn", "bf16")
-    o, s = _gpu(x, "gdn", "bf16")
-    assert o.shape == (2, 0, 2, 64)
+@pytest.mark.parametrize("mode,D", [("gdn", 64), ("gdn", 128), ("kda", 128)])
+def test_empty_and_zero_length(mode, D):
+    x = _inputs(9, 2, 0, 2, D, D, mode, "bf16")
+    o, s = _gpu(x, mode, "bf16", algo="auto")
+    assert o.shape == (2, 0, 2, D)
     np.testing.assert_array_equal(host(s), x["s0"])
     x["s0"] = None
-    o, s = _gpu(x, "gdn", "bf16")
+    o, s = _gpu(x, mode, "bf16", algo="auto")
     assert not host(s).any()
     # B = 0 is a no-op
     x = _inputs(9, 1, 10, 1, 64, 64, "gdn", "bf16")
@@ -97,20 +99,22 @@ def test_empty_and_zero_length():
 
 
 @pytest.mark.parametrize("algo", ALGOS)
-def test_in_place_state_and_resume(algo):
-    x = _inputs(10, 2, 200, 2, 128, 128, "kla", "bf16")
-    o_full, s_full = _gpu(x, "kla", "bf16", algo=algo)
+@pytest.mark.parametrize("mode", ["kla", "kda"])
+def test_in_place_state_and_resume(algo, mode):
+    x = _inputs(10, 2, 200, 2, 128, 128, mode, "bf16")
+    o_full, s_full = _gpu(x, mode, "bf16", algo=algo)
     d = to_dev(x, "bf16")
     state = d["s0"].clone()
     outs = []
     for t0, t1 in [(0, 130), (130, 131), (131, 200)]:   # split mid-chunk, and a single token
         sl = {key: (d[key][:, t0:t1].contiguous() if key != "s0" else None) for key in d}
         o, _ = gdr.chunk_fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], s0=state, s_final=state,
-                             o_dtype=torch.float32, kaczmarz=True, eps=1e-6, algo=algo)
+                             o_dtype=torch.float32, eps=1e-6 if MODES[mode]["kaczmarz"] else 0.0,
+                             algo=algo, **MODES[mode])
         outs.append(o)
     torch.cuda.synchronize()
     o_split = torch.cat(outs, dim=1)
-    o_ref, s_ref = _ref(x, "kla")
+    o_ref, s_ref = _ref(x, mode)
     # both schedules meet the bar against the oracle; the vector path (fp32
     # throughout) also agrees with itself across chunk boundaries to 1e-5
     assert rel(host(o_split), o_ref) < TOL["bf16"] and rel(host(state), s_ref) < TOL["bf16"]
@@ -294,6 +298,25 @@ def test_matrix_chunk_counts_and_workgroup_mapping(B, H, T, mode):
     o_ref, s_ref = _ref(x, mode)
     eo, es = rel(host(o), o_ref), rel(host(s), s_ref)
     print(f"matrix {mode} B{B} H{H} T{T}: rel o {eo:.2e} S {es:.2e}")
+    assert eo < TOL["bf16"] and es < TOL["bf16"]
+
+
+@pytest.mark.parametrize("mode", ["gdn", "kla"])
+def test_matrix_walk_in_time_segments(mode):
+    """Few heads and long sequences: the walk runs as chunk maps per time
+    segment, their composition, and one walk per segment (4 segments of 33,
+    33, 33 and 30 chunks here, the last one partial).  Checked against the
+    oracle with an initial state updated in place."""
+    x = _inputs(3100, 1, 64 * 128 + 37, 2, 128, 128, mode, "bf16", with_s0=True)
+    d = to_dev(x, "bf16")
+    state = d["s0"].clone()
+    m = MODES[mode]
+    o, _ = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], s0=state, s_final=state,
+                         o_dtype=torch.float32, eps=1e-6 if m["kaczmarz"] else 0.0, algo="matrix", **m)
+    torch.cuda.synchronize()
+    o_ref, s_ref = _ref(x, mode)
+    eo, es = rel(host(o), o_ref), rel(host(state), s_ref)
+    print(f"segmented walk {mode}: rel o {eo:.2e} S {es:.2e}")
     assert eo < TOL["bf16"] and es < TOL["bf16"]
 
 
