@@ -72,7 +72,7 @@ struct alignas(16) IntraSmem {
         } t;
     } u;
     float G[C];                 // in-chunk cumulative log-decay
-    float eta[C];               // beta, or eta for the Kaczmarz step size (0 past the end)
+    float eta[C];               // beta, or eta for the Kaczmarz step size (0 past the end), then the write strengths
     float kk[C];                // |k_i|^2 (Kaczmarz only)
 };
 
@@ -195,6 +195,10 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
         }
     }
     __syncthreads();  // G, eta (and |k|^2) in LDS; q and k no longer read
+    if constexpr (KZ) {
+        write_strength<KZ>(sm.eta, sm.kk, n, eps, w, lane);
+        __syncthreads();
+    }
 
     // ---- decay (and beta for R) applied in fp32; R and A tiles to LDS
 #pragma unroll
@@ -212,8 +216,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
             if (w >= 2) {
                 val = scale * dec * acc[t][r];
             } else {
-                const float bi = write_strength<KZ>(sm.eta, sm.kk, i, n, eps);
-                val = j < i ? bi * dec * acc[t][r] : 0.f;
+                val = j < i ? sm.eta[i] * dec * acc[t][r] : 0.f;
             }
             dst[(4 * lg + r) * LT + lr] = val;
         }
@@ -222,7 +225,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
 
     // ---- T = (I + R)^{-1}, then the T'' and A operand fragments
     invert_unit_lower(tri, lane, w, lr, lg);
-    pack_T_A<KZ>(tri, sm.eta, sm.kk, n, eps, recb, tid);
+    pack_T_A(tri, sm.eta, recb, tid);
     }  // chunk loop
 }
 

@@ -74,7 +74,7 @@ struct alignas(16) IntraPcSmem {
         } t;
     } u;
     float G[C * LG];   // in-chunk cumulative log-decay, token-major
-    float eta[C];      // beta, or eta for the Kaczmarz step size (0 past the end)
+    float eta[C];      // beta, or eta for the Kaczmarz step size (0 past the end), then the write strengths
     float kk[C];       // |k_i|^2 (Kaczmarz only)
     float carry[DK];   // G of token 31, added to tokens 32 .. 63
     unsigned span[4];  // span_I as fp32 bits (>= 0, so integer order is float order)
@@ -172,6 +172,10 @@ __global__ __launch_bounds__(kIntraThreads, 2) void intra_pc_kernel(
         if (qd == 0) sm.kk[i] = s;
     }
     __syncthreads();  // G, spans, eta (and |k|^2) in LDS
+    if constexpr (KZ) {
+        write_strength<KZ>(sm.eta, sm.kk, n, eps, w, lane);
+        __syncthreads();
+    }
 
     // ---- decayed operands of the walk into the record
     // K~ and Q~: row i = 16M + l%16, key channels c0 .. c0+3 and c0+16 .. c0+19
@@ -323,7 +327,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void intra_pc_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = 16 * I + 4 * lg + r;
-            dR[(4 * lg + r) * LT + lr] = j < i ? write_strength<KZ>(sm.eta, sm.kk, i, n, eps) * aR[r] : 0.f;
+            dR[(4 * lg + r) * LT + lr] = j < i ? sm.eta[i] * aR[r] : 0.f;
             dA[(4 * lg + r) * LT + lr] = j <= i ? scale * aA[r] : 0.f;
         }
     };
@@ -334,7 +338,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void intra_pc_kernel(
 
     // ---- T = (I + R)^{-1}, then the T'' and A operand fragments
     invert_unit_lower(tri, lane, w, lr, lg);
-    pack_T_A<KZ>(tri, sm.eta, sm.kk, n, eps, recb, tid);
+    pack_T_A(tri, sm.eta, recb, tid);
     }  // chunk loop
 }
 

@@ -185,21 +185,22 @@ __device__ __forceinline__ void invert_unit_lower(const TriTiles &t, int lane, i
     __syncthreads();
 }
 
-// The write strength of token j: beta_j, or for the Kaczmarz step size
-// eta_j / (|k_j|^2 + eps) (zero past the end of a partial chunk).
+// The write strength of the chunk's tokens in place: beta stays; for the
+// Kaczmarz step size eta_j becomes eta_j / (|k_j|^2 + eps) (zero past the
+// end of a partial chunk).  One wavefront, one token per lane; the caller
+// synchronises before and after.
 template <bool KZ>
-__device__ __forceinline__ float write_strength(const float *eta, const float *kk, int j, int n, float eps) {
-    if constexpr (KZ) return j < n ? eta[j] / (kk[j] + eps) : 0.f;
-    else return eta[j];
+__device__ __forceinline__ void write_strength(float *eta, const float *kk, int n, float eps, int w, int lane) {
+    if constexpr (KZ) {
+        if (w == 0) eta[lane] = lane < n ? eta[lane] / (kk[lane] + eps) : 0.f;
+    }
 }
 
 // Operand fragments of T'' = T Diag(beta) and A, lower triangle only, bf16
-// hi + lo, into the record's head.  Terms 0..3 of lane group p are tile
-// columns 4p .. 4p+3 of tile (M, 2kb), terms 4..7 the same columns of tile
-// (M, 2kb + 1).
-template <bool KZ>
-__device__ __forceinline__ void pack_T_A(const TriTiles &t, const float *eta, const float *kk, int n, float eps,
-                                         char *recb, int tid) {
+// hi + lo, into the record's head (beta: the chunk's write strengths).
+// Terms 0..3 of lane group p are tile columns 4p .. 4p+3 of tile (M, 2kb),
+// terms 4..7 the same columns of tile (M, 2kb + 1).
+__device__ __forceinline__ void pack_T_A(const TriTiles &t, const float *beta, char *recb, int tid) {
     for (int u = tid; u < 2 * 6 * 64; u += kIntraThreads) {
         const int mat = u / 384, f = (u >> 6) % 6, l = u & 63;
         const int M = frag_M(f), kb = frag_kb(f), rr = l & 15, p = l >> 4;
@@ -216,7 +217,7 @@ __device__ __forceinline__ void pack_T_A(const TriTiles &t, const float *eta, co
             for (int e = 0; e < 4; ++e) {
                 const int col = 4 * p + e;
                 float x = (J < M || (J == M && col <= rr)) ? x4[e] : 0.f;
-                if (mat == 0) x *= write_strength<KZ>(eta, kk, 16 * J + col, n, eps);
+                if (mat == 0) x *= beta[16 * J + col];
                 hv[4 * half + e] = static_cast<__bf16>(x);
                 lv[4 * half + e] = static_cast<__bf16>(x - static_cast<float>(hv[4 * half + e]));
             }
