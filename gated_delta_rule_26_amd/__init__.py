@@ -28,6 +28,7 @@ library_path = os.path.join(_PKG, "libgdr.so")
 F32, BF16 = 0, 1
 DECAY_SCALAR, DECAY_PER_CHANNEL = 0, 1
 BETA_GIVEN, BETA_KACZMARZ = 0, 1
+DELTA_RULE, DELTA_OFF = 0, 1
 ALGOS = {"auto": 0, "vector": 1, "matrix": 2}
 STATUS = {0: "GDR_OK", -1: "GDR_E_NULL", -2: "GDR_E_SHAPE", -3: "GDR_E_UNSUPPORTED", -4: "GDR_E_ALIGN",
           -5: "GDR_E_WORKSPACE", -6: "GDR_E_HIP", -7: "GDR_E_ALIAS", -8: "GDR_E_MODE"}
@@ -49,7 +50,7 @@ class Desc(ctypes.Structure):
                 ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("qkv_dtype", ctypes.c_int32), ("o_dtype", ctypes.c_int32),
                 ("decay_mode", ctypes.c_int32), ("beta_mode", ctypes.c_int32),
-                ("algo", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("algo", ctypes.c_int32), ("delta_mode", ctypes.c_int32),
                 ("eps", ctypes.c_float), ("scale", ctypes.c_float)]
 
 
@@ -114,11 +115,11 @@ def _check_dev(name, t, device, dtype=None, shape=None):
 
 
 def make_desc(B, T, H, Dk, Dv, *, qkv_dtype, o_dtype, per_channel=False, kaczmarz=False, eps=0.0,
-              scale=1.0, algo="auto", chunk=64) -> Desc:
+              scale=1.0, algo="auto", chunk=64, delta_off=False) -> Desc:
     return Desc(B=B, T=T, H=H, Dk=Dk, Dv=Dv, chunk=chunk, qkv_dtype=_dtype_code(qkv_dtype),
                 o_dtype=_dtype_code(o_dtype), decay_mode=DECAY_PER_CHANNEL if per_channel else DECAY_SCALAR,
-                beta_mode=BETA_KACZMARZ if kaczmarz else BETA_GIVEN, algo=ALGOS[algo], reserved=0,
-                eps=float(eps), scale=float(scale))
+                beta_mode=BETA_KACZMARZ if kaczmarz else BETA_GIVEN, algo=ALGOS[algo],
+                delta_mode=DELTA_OFF if delta_off else DELTA_RULE, eps=float(eps), scale=float(scale))
 
 
 def chunk_fwd_workspace_size(desc: Desc) -> int:
@@ -131,12 +132,14 @@ def chunk_fwd_workspace_size(desc: Desc) -> int:
 
 def chunk_fwd(q, k, v, g, beta, *, per_channel: bool = False, kaczmarz: bool = False, eps: float = 0.0,
               scale: float = 1.0, s0=None, output_final_state: bool = True, s_final=None, o=None,
-              o_dtype=None, algo: str = "auto", workspace=None, stream=None, stage=None):
+              o_dtype=None, algo: str = "auto", workspace=None, stream=None, stage=None,
+              delta_off: bool = False):
     """Chunked forward pass (prefill) through ``gdr_chunk_fwd``.
 
     q, k [B,T,H,Dk] and v [B,T,H,Dv] in float32 or bfloat16; g float32
     [B,T,H] (scalar decay) or [B,T,H,Dk] (``per_channel``); beta float32
-    [B,T,H] (eta when ``kaczmarz``); s0 float32 [B,H,Dk,Dv] or None.
+    [B,T,H] (eta when ``kaczmarz``; None with ``delta_off``, the additive
+    write S = D S + k v^T); s0 float32 [B,H,Dk,Dv] or None.
     ``s_final`` may be ``s0`` itself for an in-place state update.
     Returns (o [B,T,H,Dv], s_final [B,H,Dk,Dv] or None).  The work is enqueued
     on ``stream`` (default: torch's current stream of q's device).  ``stage``
@@ -153,7 +156,10 @@ def chunk_fwd(q, k, v, g, beta, *, per_channel: bool = False, kaczmarz: bool = F
     _check_dev("k", k, dev, q.dtype, (B, T, H, Dk))
     _check_dev("v", v, dev, q.dtype, (B, T, H, Dv))
     _check_dev("g", g, dev, torch.float32, (B, T, H, Dk) if per_channel else (B, T, H))
-    _check_dev("beta", beta, dev, torch.float32, (B, T, H))
+    if delta_off:
+        beta = None
+    else:
+        _check_dev("beta", beta, dev, torch.float32, (B, T, H))
     if s0 is not None:
         _check_dev("s0", s0, dev, torch.float32, (B, H, Dk, Dv))
     o_dtype = o_dtype or q.dtype
@@ -166,7 +172,7 @@ def chunk_fwd(q, k, v, g, beta, *, per_channel: bool = False, kaczmarz: bool = F
     elif s_final is not None:
         _check_dev("s_final", s_final, dev, torch.float32, (B, H, Dk, Dv))
     desc = make_desc(B, T, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=o_dtype, per_channel=per_channel,
-                     kaczmarz=kaczmarz, eps=eps, scale=scale, algo=algo)
+                     kaczmarz=kaczmarz, eps=eps, scale=scale, algo=algo, delta_off=delta_off)
     need = chunk_fwd_workspace_size(desc)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -185,12 +191,13 @@ def chunk_fwd(q, k, v, g, beta, *, per_channel: bool = False, kaczmarz: bool = F
 
 
 def recurrent_step(q, k, v, g, beta, state, *, per_channel: bool = False, kaczmarz: bool = False,
-                   eps: float = 0.0, scale: float = 1.0, o=None, o_dtype=None, stream=None):
+                   eps: float = 0.0, scale: float = 1.0, o=None, o_dtype=None, stream=None,
+                   delta_off: bool = False):
     """One fused decode step through ``gdr_recurrent_step``.
 
     q, k [N,H,Dk], v [N,H,Dv] (float32 or bfloat16); g float32 [N,H] or
-    [N,H,Dk]; beta float32 [N,H]; state float32 [N,H,Dk,Dv], updated in
-    place.  Returns o [N,H,Dv].
+    [N,H,Dk]; beta float32 [N,H] (None with ``delta_off``); state float32
+    [N,H,Dk,Dv], updated in place.  Returns o [N,H,Dv].
     """
     lib = load_library()
     dev = q.device
@@ -202,7 +209,10 @@ def recurrent_step(q, k, v, g, beta, state, *, per_channel: bool = False, kaczma
     _check_dev("k", k, dev, q.dtype, (N, H, Dk))
     _check_dev("v", v, dev, q.dtype, (N, H, Dv))
     _check_dev("g", g, dev, torch.float32, (N, H, Dk) if per_channel else (N, H))
-    _check_dev("beta", beta, dev, torch.float32, (N, H))
+    if delta_off:
+        beta = None
+    else:
+        _check_dev("beta", beta, dev, torch.float32, (N, H))
     _check_dev("state", state, dev, torch.float32, (N, H, Dk, Dv))
     o_dtype = o_dtype or q.dtype
     if o is None:
@@ -210,7 +220,7 @@ def recurrent_step(q, k, v, g, beta, state, *, per_channel: bool = False, kaczma
     else:
         _check_dev("o", o, dev, o_dtype, (N, H, Dv))
     desc = make_desc(N, 1, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=o_dtype, per_channel=per_channel,
-                     kaczmarz=kaczmarz, eps=eps, scale=scale)
+                     kaczmarz=kaczmarz, eps=eps, scale=scale, delta_off=delta_off)
     st = stream if stream is not None else torch.cuda.current_stream(dev)
     rc = lib.gdr_recurrent_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                 _ptr(state), _ptr(o), ctypes.c_void_p(st.cuda_stream))

@@ -36,6 +36,12 @@
 //    buffer that crosses it is doubled (exp(G) tripled: the helpers read it
 //    one chunk after the chain).
 //
+// Without the delta rule (DELTA = false: the additive write S = D S + k v^T
+// of the textbook page's update table; linear attention, RetNet / Mamba-2)
+// there is no prediction and no solve: E = V, so the intra kernel forms only
+// A (no K K^T, no inverse, no T'' in the record) and the walk skips K S and
+// the T'' product.
+//
 // The operand layout (a D tile is directly the B operand of the next
 // product) and the bf16 hi/lo precision scheme are described in
 // matrix_common.h.
@@ -76,7 +82,7 @@ struct alignas(16) IntraSmem {
     float kk[C];                // |k_i|^2 (Kaczmarz only)
 };
 
-template <bool KZ>
+template <bool KZ, bool DELTA>
 __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, int T, int H, int NC, int total, float eps, float scale,
@@ -105,7 +111,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
             kv[it] = buf_ld16(rk, off);
         }
         gv = g[r0 + (size_t)min(lane0, nn - 1) * H];
-        ev = beta[r0 + (size_t)min(lane0, nn - 1) * H];
+        ev = DELTA ? beta[r0 + (size_t)min(lane0, nn - 1) * H] : 0.f;
     };
     prefetch(min((int)blockIdx.x, total - 1));
     for (int ci = blockIdx.x; ci < total; ci += gridDim.x) {
@@ -152,7 +158,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
     f32x4 acc[5];
 #pragma unroll
     for (int t = 0; t < 5; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
+    if (DELTA || w >= 2) {
         const __bf16 *X = w >= 2 ? sm.u.qk.Q : sm.u.qk.K;
         const __bf16 *Kt = sm.u.qk.K;
         auto fr = [&](const __bf16 *base, int row, int kb) {
@@ -200,9 +206,11 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
         __syncthreads();
     }
 
-    // ---- decay (and beta for R) applied in fp32; R and A tiles to LDS
+    // ---- decay (and beta for R) applied in fp32; R and A tiles to LDS (no R
+    // without the delta rule)
 #pragma unroll
     for (int t = 0; t < 5; ++t) {
+        if (!DELTA && w < 2) continue;
         const int I = tileI(t), J = tileJ(t);
         const int j = 16 * J + lr;
         const float gj = sm.G[j];
@@ -224,8 +232,8 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
     __syncthreads();
 
     // ---- T = (I + R)^{-1}, then the T'' and A operand fragments
-    invert_unit_lower(tri, lane, w, lr, lg);
-    pack_T_A(tri, sm.eta, recb, tid);
+    if constexpr (DELTA) invert_unit_lower(tri, lane, w, lr, lg);
+    pack_T_A<DELTA>(tri, sm.eta, recb, tid);
     }  // chunk loop
 }
 
@@ -264,7 +272,8 @@ __device__ __forceinline__ int kperm_col(int seg, int hh) {
 //    chunk-end state): slices 0 .. NS-1 walk N (zero start, v), slices NS ..
 //    2NS-1 walk the columns of M (identity start, v = 0); N and M go to
 //    s_out[g][0] and s_out[g][1].  No outputs.
-template <bool OUT_BF16, bool TRANSFER>
+// DELTA = false: E = V (no K S, no T''), records without T''.
+template <bool OUT_BF16, bool TRANSFER, bool DELTA>
 __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const char *__restrict__ ws, const float *__restrict__ s0, void *__restrict__ o,
@@ -322,16 +331,18 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
         // T'' fragments of even chunks in tA, of odd chunks in tB: each chunk
         // loads the next one's into the other set (no register copies).
         bf16x8 tAh[6], tAl[6], tBh[6], tBl[6];
+        if constexpr (DELTA) {
 #pragma unroll
-        for (int f = 0; f < 6; ++f) {
-            tAh[f] = *reinterpret_cast<const bf16x8 *>(recs + kRecTH + f * kFragBytes + lane * 16);
-            tAl[f] = *reinterpret_cast<const bf16x8 *>(recs + kRecTL + f * kFragBytes + lane * 16);
+            for (int f = 0; f < 6; ++f) {
+                tAh[f] = *reinterpret_cast<const bf16x8 *>(recs + kRecTH + f * kFragBytes + lane * 16);
+                tAl[f] = *reinterpret_cast<const bf16x8 *>(recs + kRecTL + f * kFragBytes + lane * 16);
+            }
         }
         auto step = [&](int c, const bf16x8 *th, const bf16x8 *tl, bf16x8 *thn, bf16x8 *tln)
                         __attribute__((always_inline)) {
             const int buf = c & 1;
             // next chunk's T'' fragments, in flight during this chunk
-            {
+            if constexpr (DELTA) {
                 const char *rn = recs + (size_t)min(c + 1, nc - 1) * kRecBytes;
 #pragma unroll
                 for (int f = 0; f < 6; ++f) {
@@ -354,7 +365,7 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
             bf16x8 ka[2][4], qa[2][4];
 #pragma unroll
             for (int M = 0; M < 4; ++M) {
-                ka[0][M] = *reinterpret_cast<const bf16x8 *>(&sK[(16 * M + lr) * LDK + 8 * lg]);
+                if constexpr (DELTA) ka[0][M] = *reinterpret_cast<const bf16x8 *>(&sK[(16 * M + lr) * LDK + 8 * lg]);
                 if constexpr (!TRANSFER) qa[0][M] = *reinterpret_cast<const bf16x8 *>(&sQ[(16 * M + lr) * LDK + 8 * lg]);
             }
 #pragma unroll
@@ -363,15 +374,18 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
                 if (kb + 1 < 4) {
 #pragma unroll
                     for (int M = 0; M < 4; ++M) {
-                        ka[cur ^ 1][M] = *reinterpret_cast<const bf16x8 *>(&sK[(16 * M + lr) * LDK + 32 * (kb + 1) + 8 * lg]);
+                        if constexpr (DELTA)
+                            ka[cur ^ 1][M] = *reinterpret_cast<const bf16x8 *>(&sK[(16 * M + lr) * LDK + 32 * (kb + 1) + 8 * lg]);
                         if constexpr (!TRANSFER)
                             qa[cur ^ 1][M] = *reinterpret_cast<const bf16x8 *>(&sQ[(16 * M + lr) * LDK + 32 * (kb + 1) + 8 * lg]);
                     }
                 }
+                if constexpr (DELTA) {
 #pragma unroll
-                for (int M = 0; M < 4; ++M) P[M] = mma(ka[cur][M], SH[kb], P[M]);
+                    for (int M = 0; M < 4; ++M) P[M] = mma(ka[cur][M], SH[kb], P[M]);
 #pragma unroll
-                for (int M = 0; M < 4; ++M) P[M] = mma(ka[cur][M], SL[kb], P[M]);
+                    for (int M = 0; M < 4; ++M) P[M] = mma(ka[cur][M], SL[kb], P[M]);
+                }
                 if constexpr (!TRANSFER) {  // the read Q S (no outputs in a transfer walk)
 #pragma unroll
                     for (int M = 0; M < 4; ++M) QS[M] = mma(qa[cur][M], SH[kb], QS[M]);
@@ -397,12 +411,15 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
 #pragma unroll
             for (int M = 0; M < 4; ++M) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Xv[M][r] = static_cast<float>(vv[M][r]) - gam[M][r] * P[M][r];
+                for (int r = 0; r < 4; ++r)
+                    Xv[M][r] = DELTA ? static_cast<float>(vv[M][r]) - gam[M][r] * P[M][r] : static_cast<float>(vv[M][r]);
                 if constexpr (!TRANSFER) xo[M * 64 + lane] = *reinterpret_cast<const uint4 *>(&QS[M]);
             }
             bf16x8 XH[2], XL[2];
-            pair_split(Xv[0], Xv[1], XH[0], XL[0]);
-            pair_split(Xv[2], Xv[3], XH[1], XL[1]);
+            if constexpr (DELTA) {
+                pair_split(Xv[0], Xv[1], XH[0], XL[0]);
+                pair_split(Xv[2], Xv[3], XH[1], XL[1]);
+            }
             // k^T fragments (key-channel tile i, token block kb) for the update,
             // read transposed from the token-major k: term e of lane group lg is
             // token 32kb + kperm(lg, e), key channel 16i + lr.  Tile 0 now.
@@ -416,17 +433,19 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
             bf16x8 kt[2][2];
             kt[0][0] = kt_frag(0, 0);
             kt[0][1] = kt_frag(0, 1);
-            // E = T'' X
+            // E = T'' X (E = X = V without the delta rule)
             f32x4 E[4];
 #pragma unroll
             for (int M = 0; M < 4; ++M) {
-                E[M] = zero4;
+                E[M] = DELTA ? zero4 : Xv[M];
+                if constexpr (DELTA) {
 #pragma unroll
-                for (int kb = 0; kb <= (M >> 1); ++kb) {
-                    const int f = lower_frag(M, kb);
-                    E[M] = mma(th[f], XH[kb], E[M]);
-                    E[M] = mma(th[f], XL[kb], E[M]);
-                    E[M] = mma(tl[f], XH[kb], E[M]);
+                    for (int kb = 0; kb <= (M >> 1); ++kb) {
+                        const int f = lower_frag(M, kb);
+                        E[M] = mma(th[f], XH[kb], E[M]);
+                        E[M] = mma(th[f], XL[kb], E[M]);
+                        E[M] = mma(tl[f], XH[kb], E[M]);
+                    }
                 }
             }
             // E to the helper; Gend E as the update's B operand
@@ -622,11 +641,11 @@ __global__ __launch_bounds__(1024) void segment_combine_kernel(const float *__re
 }
 
 // ============================================================ launchers
-template <bool KZ>
+template <bool KZ, bool DELTA>
 hipError_t launch_intra(const ChunkArgs &a) {
     const long total = (long)a.B * a.H * a.NC;
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL((intra_matrix_kernel<KZ>), dim3(intra_grid(total, 4)), dim3(kIntraThreads), 0, a.stream,
+    hipLaunchKernelGGL((intra_matrix_kernel<KZ, DELTA>), dim3(intra_grid(total, 4)), dim3(kIntraThreads), 0, a.stream,
                        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), a.g, a.beta, a.T, a.H,
                        a.NC, (int)total, a.eps, a.scale, static_cast<char *>(a.ws));
     return hipGetLastError();
@@ -660,7 +679,7 @@ size_t segment_bytes(int BH, int NC) {
     return P > 1 ? (size_t)BH * P * 3 * DK * DV * sizeof(float) : 0;
 }
 
-template <bool OB>
+template <bool OB, bool DELTA>
 hipError_t launch_state(const ChunkArgs &a) {
     const int BH = a.B * a.H;
     const int P = walk_segments(BH, a.NC);
@@ -668,7 +687,7 @@ hipError_t launch_state(const ChunkArgs &a) {
                  *v = static_cast<const __bf16 *>(a.v);
     const char *ws = static_cast<const char *>(a.ws);
     if (P == 1) {
-        hipLaunchKernelGGL((state_matrix_kernel<OB, false>), dim3((unsigned)(BH * NS)), dim3(kStateThreads), 0,
+        hipLaunchKernelGGL((state_matrix_kernel<OB, false, DELTA>), dim3((unsigned)(BH * NS)), dim3(kStateThreads), 0,
                            a.stream, q, k, v, ws, a.s0, a.o, a.s_final, a.T, a.H, a.NC, BH, 1, a.NC, a.scale);
         return hipGetLastError();
     }
@@ -676,13 +695,13 @@ hipError_t launch_state(const ChunkArgs &a) {
     const int seg = (a.NC + P - 1) / P;
     float *tr = reinterpret_cast<float *>(static_cast<char *>(a.ws) + (size_t)BH * a.NC * kRecBytes);
     float *seg_state = tr + (size_t)BH * P * 2 * DK * DV;
-    hipLaunchKernelGGL((state_matrix_kernel<false, true>), dim3((unsigned)(BH * P * 2 * NS)), dim3(kStateThreads), 0,
+    hipLaunchKernelGGL((state_matrix_kernel<false, true, DELTA>), dim3((unsigned)(BH * P * 2 * NS)), dim3(kStateThreads), 0,
                        a.stream, q, k, v, ws, nullptr, nullptr, tr, a.T, a.H, a.NC, BH * P, P, seg, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(segment_combine_kernel, dim3((unsigned)BH), dim3(1024), 0, a.stream, tr, a.s0, seg_state, P);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((state_matrix_kernel<OB, false>), dim3((unsigned)(BH * P * NS)), dim3(kStateThreads), 0,
+    hipLaunchKernelGGL((state_matrix_kernel<OB, false, DELTA>), dim3((unsigned)(BH * P * NS)), dim3(kStateThreads), 0,
                        a.stream, q, k, v, ws, seg_state, a.o, a.s_final, a.T, a.H, a.NC, BH * P, P, seg, a.scale);
     return hipGetLastError();
 }
@@ -707,10 +726,12 @@ bool chunk_matrix_supported(int Dk, int Dv, bool qkv_bf16, bool) { return qkv_bf
 hipError_t launch_chunk_matrix(const ChunkArgs &a, int stage) {
     if (a.per_channel) return launch_chunk_matrix_pc(a, stage);
     if (stage != 1) {
-        const hipError_t e = a.kaczmarz ? launch_intra<true>(a) : launch_intra<false>(a);
+        const hipError_t e = !a.delta ? launch_intra<false, false>(a)
+                             : a.kaczmarz ? launch_intra<true, true>(a) : launch_intra<false, true>(a);
         if (e != hipSuccess || stage == 0) return e;
     }
-    return a.o_bf16 ? launch_state<true>(a) : launch_state<false>(a);
+    if (!a.delta) return a.o_bf16 ? launch_state<true, false>(a) : launch_state<false, false>(a);
+    return a.o_bf16 ? launch_state<true, true>(a) : launch_state<false, true>(a);
 }
 
 }  // namespace gdr

@@ -14,6 +14,9 @@
 //   S   <- Diag(exp(G_63)) S + K^^T E                    chunk-end state
 // With one decay rate for all channels this is the scalar-decay form of
 // chunk_matrix.hip (there the factors multiply rows of K S and Q S instead).
+// Without the delta rule (DELTA = false: GLA's additive write
+// S = Diag(exp g) S + k v^T, textbook page, update table) E = V: no R, no
+// inverse and no T'' in the record, and the walk skips K~ S and T''.
 //
 // Two kernels, as for scalar decay:
 //  * intra (persistent, two workgroups per compute unit): the gate scan, R
@@ -80,7 +83,7 @@ struct alignas(16) IntraPcSmem {
     unsigned span[4];  // span_I as fp32 bits (>= 0, so integer order is float order)
 };
 
-template <bool KZ>
+template <bool KZ, bool DELTA>
 __global__ __launch_bounds__(kIntraThreads, 2) void intra_pc_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, int T, int H, int NC, int total, float eps, float scale,
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void intra_pc_kernel(
         }
 #pragma unroll
         for (int m = 0; m < 32; ++m) gv[m] = buf_ld4f(rg, (32 * gh + m) * g_stride + 4 * gc);
-        ev = beta[r0 + (size_t)min(lane0, nn - 1) * H];
+        ev = DELTA ? beta[r0 + (size_t)min(lane0, nn - 1) * H] : 0.f;
     };
     prefetch(min((int)blockIdx.x, total - 1));
     for (int ci = blockIdx.x; ci < total; ci += gridDim.x) {
@@ -272,9 +275,11 @@ __global__ __launch_bounds__(kIntraThreads, 2) void intra_pc_kernel(
         };
         auto both = [&](int t, const bf16x8 &kh, const bf16x8 &kl, const bf16x8 &qh, const bf16x8 &ql,
                         const bf16x8 &bh, const bf16x8 &bl) {
-            accR[t] = mma(kh, bh, accR[t]);
-            accR[t] = mma(kh, bl, accR[t]);
-            accR[t] = mma(kl, bh, accR[t]);
+            if constexpr (DELTA) {
+                accR[t] = mma(kh, bh, accR[t]);
+                accR[t] = mma(kh, bl, accR[t]);
+                accR[t] = mma(kl, bh, accR[t]);
+            }
             accA[t] = mma(qh, bh, accA[t]);
             accA[t] = mma(qh, bl, accA[t]);
             accA[t] = mma(ql, bh, accA[t]);
@@ -337,8 +342,8 @@ __global__ __launch_bounds__(kIntraThreads, 2) void intra_pc_kernel(
     __syncthreads();
 
     // ---- T = (I + R)^{-1}, then the T'' and A operand fragments
-    invert_unit_lower(tri, lane, w, lr, lg);
-    pack_T_A(tri, sm.eta, recb, tid);
+    if constexpr (DELTA) invert_unit_lower(tri, lane, w, lr, lg);
+    pack_T_A<DELTA>(tri, sm.eta, recb, tid);
     }  // chunk loop
 }
 
@@ -395,7 +400,7 @@ __device__ __forceinline__ void barrier_after_loads() {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool DELTA>
 __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
     const __bf16 *__restrict__ v, const char *__restrict__ ws, const float *__restrict__ s0, void *__restrict__ o,
     float *__restrict__ s_final, int T, int H, int NC, int BH) {
@@ -437,16 +442,18 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
             for (int r = 0; r < 4; ++r)
                 S[i][r] = s0 ? s0[sbase + (size_t)(16 * i + 4 * lg + r) * DV + jt + lr] : 0.f;
         bf16x8 tAh[6], tAl[6], tBh[6], tBl[6];
+        if constexpr (DELTA) {
 #pragma unroll
-        for (int f = 0; f < 6; ++f) {
-            tAh[f] = *reinterpret_cast<const bf16x8 *>(recs + kRecTH + f * kFragBytes + lane * 16);
-            tAl[f] = *reinterpret_cast<const bf16x8 *>(recs + kRecTL + f * kFragBytes + lane * 16);
+            for (int f = 0; f < 6; ++f) {
+                tAh[f] = *reinterpret_cast<const bf16x8 *>(recs + kRecTH + f * kFragBytes + lane * 16);
+                tAl[f] = *reinterpret_cast<const bf16x8 *>(recs + kRecTL + f * kFragBytes + lane * 16);
+            }
         }
         auto frag = [&](const uint4 *base, int f) { return __builtin_bit_cast(bf16x8, base[f * 64 + lane]); };
         auto step = [&](int c, const bf16x8 *th, const bf16x8 *tl, bf16x8 *thn, bf16x8 *tln)
                         __attribute__((always_inline)) {
             const int buf = c & 1;
-            {  // next chunk's T'' fragments, in flight during this chunk
+            if constexpr (DELTA) {  // next chunk's T'' fragments, in flight during this chunk
                 const char *rn = recs + (size_t)min(c + 1, NC - 1) * kPcBytes;
 #pragma unroll
                 for (int f = 0; f < 6; ++f) {
@@ -464,7 +471,7 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
             f32x4 QS[4] = {zero4, zero4, zero4, zero4};
             bf16x8 fa[2][4][4];  // [stage][K~ hi, K~ lo, Q~ hi, Q~ lo][M]
 #pragma unroll
-            for (int m4 = 0; m4 < 4; ++m4)
+            for (int m4 = DELTA ? 0 : 2; m4 < 4; ++m4)
 #pragma unroll
                 for (int M = 0; M < 4; ++M) fa[0][m4][M] = frag(sm.Kq0[buf], 4 * m4 + M);
 #pragma unroll
@@ -472,15 +479,17 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
                 const int cur = kb & 1;
                 if (kb + 1 < 4) {
 #pragma unroll
-                    for (int m4 = 0; m4 < 4; ++m4)
+                    for (int m4 = DELTA ? 0 : 2; m4 < 4; ++m4)
 #pragma unroll
                         for (int M = 0; M < 4; ++M) fa[cur ^ 1][m4][M] = frag(sm.Kq123, 16 * kb + 4 * m4 + M);
                 }
+                if constexpr (DELTA) {
 #pragma unroll
-                for (int M = 0; M < 4; ++M) {
-                    P[M] = mma(fa[cur][0][M], SH[kb], P[M]);
-                    P[M] = mma(fa[cur][0][M], SL[kb], P[M]);
-                    P[M] = mma(fa[cur][1][M], SH[kb], P[M]);
+                    for (int M = 0; M < 4; ++M) {
+                        P[M] = mma(fa[cur][0][M], SH[kb], P[M]);
+                        P[M] = mma(fa[cur][0][M], SL[kb], P[M]);
+                        P[M] = mma(fa[cur][1][M], SH[kb], P[M]);
+                    }
                 }
 #pragma unroll
                 for (int M = 0; M < 4; ++M) {
@@ -497,23 +506,27 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
                 // V[16M + 4lg + r][16w + lr], r = 0..3
                 const bf16x4 vv = lds_read_tr(&sm.V[buf][(16 * M + 4 * lg + (lr >> 2)) * BV + 16 * w + 4 * (lr & 3)]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Xv[M][r] = static_cast<float>(vv[r]) - P[M][r];
+                for (int r = 0; r < 4; ++r) Xv[M][r] = DELTA ? static_cast<float>(vv[r]) - P[M][r] : static_cast<float>(vv[r]);
                 xo[M * 64 + lane] = *reinterpret_cast<const uint4 *>(&QS[M]);
             }
             bf16x8 XH[2], XL[2];
-            pair_split(Xv[0], Xv[1], XH[0], XL[0]);
-            pair_split(Xv[2], Xv[3], XH[1], XL[1]);
-            // E = T'' X
+            if constexpr (DELTA) {
+                pair_split(Xv[0], Xv[1], XH[0], XL[0]);
+                pair_split(Xv[2], Xv[3], XH[1], XL[1]);
+            }
+            // E = T'' X (E = X = V without the delta rule)
             f32x4 E[4];
 #pragma unroll
             for (int M = 0; M < 4; ++M) {
-                E[M] = zero4;
+                E[M] = DELTA ? zero4 : Xv[M];
+                if constexpr (DELTA) {
 #pragma unroll
-                for (int kb = 0; kb <= (M >> 1); ++kb) {
-                    const int f = lower_frag(M, kb);
-                    E[M] = mma(th[f], XH[kb], E[M]);
-                    E[M] = mma(th[f], XL[kb], E[M]);
-                    E[M] = mma(tl[f], XH[kb], E[M]);
+                    for (int kb = 0; kb <= (M >> 1); ++kb) {
+                        const int f = lower_frag(M, kb);
+                        E[M] = mma(th[f], XH[kb], E[M]);
+                        E[M] = mma(th[f], XL[kb], E[M]);
+                        E[M] = mma(tl[f], XH[kb], E[M]);
+                    }
                 }
                 xo[(4 + M) * 64 + lane] = *reinterpret_cast<const uint4 *>(&E[M]);
             }
@@ -566,7 +579,9 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
         const unsigned lds_gend = lds_addr(sm.Gend), lds_v = lds_addr(sm.V);
         // v slice of chunk cc, 16 rows per copy (lane l: row l/4, 16-byte
         // segment l%4); rows past the end repeat the last row (any finite
-        // value works there: those rows and columns of T'' and A are zero)
+        // value works there: those rows and columns of T'' and A are zero,
+        // and so are those tokens' rows of K^, which meet them directly
+        // without the delta rule)
         auto copy_v = [&](int cc) {
             const int t0 = cc * C, n = min(C, T - t0);
 #pragma unroll
@@ -625,20 +640,20 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
 }
 
 // ============================================================ launchers
-template <bool KZ>
+template <bool KZ, bool DELTA>
 hipError_t launch_intra_pc(const ChunkArgs &a) {
     const long total = (long)a.B * a.H * a.NC;
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL((intra_pc_kernel<KZ>), dim3(intra_grid(total, 2)), dim3(kIntraThreads), 0, a.stream,
+    hipLaunchKernelGGL((intra_pc_kernel<KZ, DELTA>), dim3(intra_grid(total, 2)), dim3(kIntraThreads), 0, a.stream,
                        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), a.g, a.beta, a.T, a.H,
                        a.NC, (int)total, a.eps, a.scale, static_cast<char *>(a.ws));
     return hipGetLastError();
 }
 
-template <bool OB>
+template <bool OB, bool DELTA>
 hipError_t launch_state_pc(const ChunkArgs &a) {
     const int BH = a.B * a.H;
-    hipLaunchKernelGGL((state_pc_kernel<OB>), dim3((unsigned)(BH * NS)), dim3(kStateThreads), 0, a.stream,
+    hipLaunchKernelGGL((state_pc_kernel<OB, DELTA>), dim3((unsigned)(BH * NS)), dim3(kStateThreads), 0, a.stream,
                        static_cast<const __bf16 *>(a.v), static_cast<const char *>(a.ws), a.s0, a.o, a.s_final, a.T,
                        a.H, a.NC, BH);
     return hipGetLastError();
@@ -650,10 +665,12 @@ size_t chunk_matrix_pc_workspace_bytes(int B, int H, int NC) { return (size_t)B 
 
 hipError_t launch_chunk_matrix_pc(const ChunkArgs &a, int stage) {
     if (stage != 1) {
-        const hipError_t e = a.kaczmarz ? launch_intra_pc<true>(a) : launch_intra_pc<false>(a);
+        const hipError_t e = !a.delta ? launch_intra_pc<false, false>(a)
+                             : a.kaczmarz ? launch_intra_pc<true, true>(a) : launch_intra_pc<false, true>(a);
         if (e != hipSuccess || stage == 0) return e;
     }
-    return a.o_bf16 ? launch_state_pc<true>(a) : launch_state_pc<false>(a);
+    if (!a.delta) return a.o_bf16 ? launch_state_pc<true, false>(a) : launch_state_pc<false, false>(a);
+    return a.o_bf16 ? launch_state_pc<true, true>(a) : launch_state_pc<false, true>(a);
 }
 
 }  // namespace gdr

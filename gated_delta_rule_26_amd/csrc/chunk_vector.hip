@@ -17,6 +17,9 @@
 //   S_next  = Diag(exp G_{n-1}) S + (exp(G_{n-1} - G) o K)^T E.
 // Padded rows of a partial last chunk have k = q = v = 0, g = 0, beta = 0,
 // which makes them contribute nothing and keeps G_{63} = G_{n-1}.
+// Without the delta rule (the additive write S = D S + k v^T of the textbook
+// page's update table) R = 0, beta = 1 and W = 0, so E = U = V: the same
+// kernels with those three values.
 //
 // Two kernels: intra (one workgroup per (sequence, head, chunk), fully
 // parallel) writes W, U, A and G to the workspace; state (one workgroup per
@@ -50,7 +53,7 @@ template <int DK, int DV, bool PC, bool KZ, bool IN_BF16>
 __global__ __launch_bounds__(kThreads) void intra_vector_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, int T, int H, int NC, float eps,
-    float scale, float *__restrict__ wsW, float *__restrict__ wsU, float *__restrict__ wsA,
+    float scale, bool delta, float *__restrict__ wsW, float *__restrict__ wsU, float *__restrict__ wsA,
     float *__restrict__ wsG) {
     constexpr int GK = PC ? DK : 1;
     const int ci = blockIdx.x;  // (b*H + h)*NC + c
@@ -94,7 +97,9 @@ __global__ __launch_bounds__(kThreads) void intra_vector_kernel(
     if (tid >= kThreads - C) {  // the last wavefront prepares beta
         const int i = tid - (kThreads - C);
         float bv = 0.f;
-        if (i < n) {
+        if (i < n && !delta) {
+            bv = 1.f;
+        } else if (i < n) {
             const float given = beta[((size_t)b * T + t0 + i) * H + h];
             if constexpr (KZ) {
                 float kk = 0.f;
@@ -134,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void intra_vector_kernel(
                     a *= gam;
                 }
             }
-            sR[i][j] = j < i ? sBeta[i] * r : 0.f;
+            sR[i][j] = delta && j < i ? sBeta[i] * r : 0.f;
             Ag[j] = scale * a;
         }
     }
@@ -151,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void intra_vector_kernel(
             float rhs;
             if (isW) {
                 const float gi = PC ? sG[i][col] : sG[i][0];
-                rhs = sBeta[i] * __expf(gi) * sK[i][col];
+                rhs = delta ? sBeta[i] * __expf(gi) * sK[i][col] : 0.f;
             } else {
                 rhs = i < n ? sBeta[i] * load_in<IN_BF16>(v, (((size_t)b * T + t0 + i) * H + h) * DV + col)
                             : 0.f;
@@ -277,8 +282,8 @@ hipError_t launch_t(const ChunkArgs &a, int stage) {
     VecWs w = carve(a.ws, nchunks, DK, DV, PC);
     if (stage != 1) {
         hipLaunchKernelGGL((intra_vector_kernel<DK, DV, PC, KZ, IB>), dim3((unsigned)nchunks), dim3(kThreads), 0,
-                           a.stream, a.q, a.k, a.v, a.g, a.beta, a.T, a.H, a.NC, a.eps, a.scale, w.W, w.U, w.A,
-                           w.G);
+                           a.stream, a.q, a.k, a.v, a.g, a.beta, a.T, a.H, a.NC, a.eps, a.scale, a.delta, w.W, w.U,
+                           w.A, w.G);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || stage == 0) return e;
     }

@@ -39,14 +39,16 @@ struct Sizes {
 // (T = 1, no chunk constraint).
 int check_desc(const gdr_desc *d, bool step, Sizes *sz) {
     if (!d) return GDR_E_NULL;
-    if (d->reserved != 0) return GDR_E_MODE;
+    if (d->delta_mode != GDR_DELTA_RULE && d->delta_mode != GDR_DELTA_OFF) return GDR_E_MODE;
+    const bool delta = d->delta_mode == GDR_DELTA_RULE;  // beta_mode and eps matter only then
     if (d->qkv_dtype != GDR_F32 && d->qkv_dtype != GDR_BF16) return GDR_E_MODE;
     if (d->o_dtype != GDR_F32 && d->o_dtype != GDR_BF16) return GDR_E_MODE;
     if (d->decay_mode != GDR_DECAY_SCALAR && d->decay_mode != GDR_DECAY_PER_CHANNEL) return GDR_E_MODE;
-    if (d->beta_mode != GDR_BETA_GIVEN && d->beta_mode != GDR_BETA_KACZMARZ) return GDR_E_MODE;
+    if (delta && d->beta_mode != GDR_BETA_GIVEN && d->beta_mode != GDR_BETA_KACZMARZ) return GDR_E_MODE;
     if (d->algo != GDR_ALGO_AUTO && d->algo != GDR_ALGO_VECTOR && d->algo != GDR_ALGO_MATRIX) return GDR_E_MODE;
     if (!std::isfinite(d->scale)) return GDR_E_MODE;
-    if (d->beta_mode == GDR_BETA_KACZMARZ && !(std::isfinite(d->eps) && d->eps >= 0.f)) return GDR_E_MODE;
+    if (delta && d->beta_mode == GDR_BETA_KACZMARZ && !(std::isfinite(d->eps) && d->eps >= 0.f))
+        return GDR_E_MODE;
     const int T = step ? 1 : d->T;
     if (d->B < 0 || d->H < 0 || T < 0 || d->Dk < 0 || d->Dv < 0) return GDR_E_SHAPE;
     if (!(d->Dk == 64 || d->Dk == 128) || !(d->Dv == 64 || d->Dv == 128)) return GDR_E_UNSUPPORTED;
@@ -65,7 +67,7 @@ int check_desc(const gdr_desc *d, bool step, Sizes *sz) {
         sz->qk = qk;
         sz->v = vv;
         sz->g = d->decay_mode == GDR_DECAY_PER_CHANNEL ? qk : tok;
-        sz->beta = tok;
+        sz->beta = delta ? tok : 0;  // beta_or_eta is not read without the delta rule
         sz->state = st;
         sz->o = vv;
     }
@@ -145,9 +147,11 @@ int chunk_fwd_impl(int stage, const gdr_desc *d, const void *q, const void *k, c
     const size_t in_es = d->qkv_dtype == GDR_BF16 ? 2 : 4;
     const size_t out_es = d->o_dtype == GDR_BF16 ? 2 : 4;
     const bool have_tokens = d->T > 0;
+    const bool delta = d->delta_mode == GDR_DELTA_RULE;
+    if (!delta) beta_or_eta = nullptr;
 
     if (have_tokens) {
-        if (!q || !k || !v || !g || !beta_or_eta || !o) return GDR_E_NULL;
+        if (!q || !k || !v || !g || (delta && !beta_or_eta) || !o) return GDR_E_NULL;
         if (need > 0 && !workspace) return GDR_E_WORKSPACE;
         if (workspace_bytes < need) return GDR_E_WORKSPACE;
         if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return GDR_E_ALIGN;
@@ -184,7 +188,8 @@ int chunk_fwd_impl(int stage, const gdr_desc *d, const void *q, const void *k, c
     a.qkv_bf16 = d->qkv_dtype == GDR_BF16;
     a.o_bf16 = d->o_dtype == GDR_BF16;
     a.per_channel = pc;
-    a.kaczmarz = d->beta_mode == GDR_BETA_KACZMARZ;
+    a.delta = delta;
+    a.kaczmarz = delta && d->beta_mode == GDR_BETA_KACZMARZ;
     a.eps = a.kaczmarz ? d->eps : 0.f;
     a.scale = d->scale;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta_or_eta;
@@ -222,7 +227,9 @@ int gdr_recurrent_step(const gdr_desc *d, const void *q, const void *k, const vo
     const int rc = check_desc(d, true, &sz);
     if (rc != GDR_OK) return rc;
     if (d->B == 0 || d->H == 0) return GDR_OK;
-    if (!q || !k || !v || !g || !beta_or_eta || !state || !o) return GDR_E_NULL;
+    const bool delta = d->delta_mode == GDR_DELTA_RULE;
+    if (!delta) beta_or_eta = nullptr;
+    if (!q || !k || !v || !g || (delta && !beta_or_eta) || !state || !o) return GDR_E_NULL;
     const bool pc = d->decay_mode == GDR_DECAY_PER_CHANNEL;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(state, 16))
         return GDR_E_ALIGN;
@@ -242,7 +249,8 @@ int gdr_recurrent_step(const gdr_desc *d, const void *q, const void *k, const vo
     a.qkv_bf16 = d->qkv_dtype == GDR_BF16;
     a.o_bf16 = d->o_dtype == GDR_BF16;
     a.per_channel = pc;
-    a.kaczmarz = d->beta_mode == GDR_BETA_KACZMARZ;
+    a.delta = delta;
+    a.kaczmarz = delta && d->beta_mode == GDR_BETA_KACZMARZ;
     a.eps = a.kaczmarz ? d->eps : 0.f;
     a.scale = d->scale;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta_or_eta;

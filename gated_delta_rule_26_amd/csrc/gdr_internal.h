@@ -14,6 +14,7 @@ struct ChunkArgs {
     int B, T, H, Dk, Dv;
     int NC;                  // chunks per sequence, ceil(T / 64)
     bool qkv_bf16, o_bf16, per_channel, kaczmarz;
+    bool delta;              // false: additive write S = D S + k v^T (beta is NULL)
     float eps, scale;
     const void *q, *k, *v;
     const float *g, *beta;
@@ -28,6 +29,7 @@ struct ChunkArgs {
 struct StepArgs {
     int N, H, Dk, Dv;
     bool qkv_bf16, o_bf16, per_channel, kaczmarz;
+    bool delta;              // false: additive write S = D S + k v^T (beta is NULL)
     float eps, scale;
     const void *q, *k, *v;
     const float *g, *beta;

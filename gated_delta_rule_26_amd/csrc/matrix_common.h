@@ -197,11 +197,12 @@ __device__ __forceinline__ void write_strength(float *eta, const float *kk, int 
 }
 
 // Operand fragments of T'' = T Diag(beta) and A, lower triangle only, bf16
-// hi + lo, into the record's head (beta: the chunk's write strengths).
-// Terms 0..3 of lane group p are tile columns 4p .. 4p+3 of tile (M, 2kb),
-// terms 4..7 the same columns of tile (M, 2kb + 1).
+// hi + lo, into the record's head (beta: the chunk's write strengths; A only
+// when WITH_T is false).  Terms 0..3 of lane group p are tile columns
+// 4p .. 4p+3 of tile (M, 2kb), terms 4..7 the same columns of tile (M, 2kb + 1).
+template <bool WITH_T = true>
 __device__ __forceinline__ void pack_T_A(const TriTiles &t, const float *beta, char *recb, int tid) {
-    for (int u = tid; u < 2 * 6 * 64; u += kIntraThreads) {
+    for (int u = tid + (WITH_T ? 0 : 6 * 64); u < 2 * 6 * 64; u += kIntraThreads) {
         const int mat = u / 384, f = (u >> 6) % 6, l = u & 63;
         const int M = frag_M(f), kb = frag_kb(f), rr = l & 15, p = l >> 4;
         bf16x8 hv, lv;

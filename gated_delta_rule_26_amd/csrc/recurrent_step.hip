@@ -16,6 +16,11 @@
 // across the lanes of a wavefront with cross-lane swaps, then across the four
 // wavefronts through LDS.  The output uses o = scale (r + beta e (k.q)), so no
 // second pass over the state is needed.
+//
+// Without the delta rule (delta = false: linear attention, RetNet / Mamba-2,
+// GLA; textbook page, update table) the write is S = S~ + k v^T: the same
+// pass with e = v and beta = 1 (the prediction is formed and not used; the
+// pass is bound by the state's bytes either way) and beta never read.
 #include "gdr_internal.h"
 
 namespace gdr {
@@ -27,7 +32,7 @@ template <int DK, int DV, bool PC, bool KZ, bool IN_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ state,
-    void *__restrict__ o, float eps, float scale) {
+    void *__restrict__ o, float eps, float scale, bool delta) {
     constexpr int TPR = DV / 4;          // threads per state row (one float4 each)
     constexpr int RPP = kThreads / TPR;  // rows per pass of the workgroup
     constexpr int PASSES = DK / RPP;
@@ -74,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
         kk = wave_sum(kk);
         if (lane == 0) {
             s_kq = kq;
-            const float b = beta[nh];
+            const float b = delta ? beta[nh] : 1.f;
             s_beta = KZ ? b / (kk + eps) : b;
         }
     }
@@ -109,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
         R.x += b.x; R.y += b.y; R.z += b.z; R.w += b.w;
     }
     const float bt = s_beta;
-    const float4 e = make_float4(vv.x - P.x, vv.y - P.y, vv.z - P.z, vv.w - P.w);
+    const float4 e = delta ? make_float4(vv.x - P.x, vv.y - P.y, vv.z - P.z, vv.w - P.w) : vv;
 
     if (r0 == 0) {  // read after write: o = scale (S~^T q + beta e (k.q))
         const float bkq = bt * s_kq;
@@ -138,7 +143,8 @@ template <int DK, int DV, bool PC, bool KZ, bool IB, bool OB>
 hipError_t launch_t(const StepArgs &a) {
     const unsigned grid = static_cast<unsigned>(a.N) * static_cast<unsigned>(a.H);
     hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, PC, KZ, IB, OB>), dim3(grid), dim3(kThreads),
-                       0, a.stream, a.q, a.k, a.v, a.g, a.beta, a.state, a.o, a.eps, a.scale);
+                       0, a.stream, a.q, a.k, a.v, a.g, a.beta, a.state, a.o, a.eps, a.scale,
+                       a.delta);
     return hipGetLastError();
 }
 

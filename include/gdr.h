@@ -20,6 +20,13 @@
  * with beta_t given, or the Kaczmarz step beta_t = eta_t / (||k_t||^2 + eps)
  * (Kaczmarz page, "La Regola di Aggiornamento KLA").
  *
+ * With delta_mode = GDR_DELTA_OFF the prediction and the residual drop out
+ * and the write is the plain additive one, S_t = D_t S_{t-1} + k_t v_t^T,
+ * o_t = scale * S_t^T q_t: linear attention (D_t = I, g = 0), RetNet /
+ * Mamba-2 (scalar decay) and GLA (per-channel decay), the rows of the
+ * textbook page's update table whose transition is the decay alone.  No beta
+ * scales that write; beta_or_eta, beta_mode and eps are then ignored.
+ *
  * Two schedules of the same recurrence (blog summary, "Kernel Triton
  * recurrente fusionado" and "Pipeline Triton por chunks"): a chunked prefill
  * (gdr_chunk_fwd) and a fused single-token decode step (gdr_recurrent_step).
@@ -49,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 1
+#define GDR_ABI_VERSION 2
 
 /* decay_mode */
 #define GDR_DECAY_SCALAR 0       /* g is [.., H]: one log-decay per token and head */
@@ -57,6 +64,9 @@ extern "C" {
 /* beta_mode */
 #define GDR_BETA_GIVEN 0         /* beta_or_eta holds beta_t */
 #define GDR_BETA_KACZMARZ 1      /* beta_or_eta holds eta_t; beta_t = eta_t / (||k_t||^2 + eps) */
+/* delta_mode */
+#define GDR_DELTA_RULE 0         /* the (gated) delta rule above */
+#define GDR_DELTA_OFF 1          /* additive write S = D S + k v^T (no prediction, no beta) */
 /* dtypes of q, k, v (qkv_dtype) and of o (o_dtype) */
 #define GDR_F32 0
 #define GDR_BF16 1
@@ -90,8 +100,8 @@ typedef struct gdr_desc {
     int32_t decay_mode;  /* GDR_DECAY_* */
     int32_t beta_mode;   /* GDR_BETA_* */
     int32_t algo;        /* GDR_ALGO_*; gdr_recurrent_step ignores it */
-    int32_t reserved;    /* must be 0 */
-    float eps;           /* Kaczmarz stabiliser (>= 0); ignored for GDR_BETA_GIVEN */
+    int32_t delta_mode;  /* GDR_DELTA_*; 0 (the delta rule) in descriptors of ABI version 1 */
+    float eps;           /* Kaczmarz stabiliser (>= 0); ignored for GDR_BETA_GIVEN and GDR_DELTA_OFF */
     float scale;         /* output scale; 1 = the plain read, 1/sqrt(Dk) = KDA's read */
 } gdr_desc;
 
@@ -121,7 +131,7 @@ int gdr_chunk_fwd_workspace_size(const gdr_desc *desc, size_t *bytes);
  *   q, k        [B, T, H, Dk]  qkv_dtype, contiguous
  *   v           [B, T, H, Dv]  qkv_dtype, contiguous
  *   g           [B, T, H] (scalar decay) or [B, T, H, Dk] (per channel), fp32
- *   beta_or_eta [B, T, H] fp32
+ *   beta_or_eta [B, T, H] fp32 (may be NULL with GDR_DELTA_OFF)
  *   s0          [B, H, Dk, Dv] fp32 initial state, or NULL for zero
  *   o           [B, T, H, Dv]  o_dtype (written)
  *   s_final     [B, H, Dk, Dv] fp32 final state (written), or NULL; may be
@@ -170,7 +180,7 @@ int gdr_chunk_fwd_stage(int stage, const gdr_desc *desc,
  *   q, k        [N, H, Dk]  qkv_dtype
  *   v           [N, H, Dv]  qkv_dtype
  *   g           [N, H] or [N, H, Dk] fp32
- *   beta_or_eta [N, H] fp32
+ *   beta_or_eta [N, H] fp32 (may be NULL with GDR_DELTA_OFF)
  *   state       [N, H, Dk, Dv] fp32, read and updated in place
  *   o           [N, H, Dv] o_dtype (written)
  * desc->T and desc->chunk are ignored.  q, k, v, g, beta_or_eta must not

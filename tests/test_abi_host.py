@@ -43,7 +43,7 @@ def test_desc_layout_matches_header():
 
 def test_version_and_strings():
     lib = gdr.load_library()
-    assert lib.gdr_abi_version() == 1
+    assert lib.gdr_abi_version() == 2
     for code in gdr.STATUS:
         assert lib.gdr_status_string(code).decode().startswith(gdr.STATUS[code])
 
@@ -72,7 +72,7 @@ def test_workspace_size_query():
     assert _ws(_desc(chunk=32))[0] == E["GDR_E_UNSUPPORTED"]
     assert _ws(_desc(B=-1))[0] == E["GDR_E_SHAPE"]
     d = _desc()
-    d.reserved = 1
+    d.delta_mode = 2
     assert _ws(d)[0] == E["GDR_E_MODE"]
     d = _desc()
     d.decay_mode = 7
@@ -121,6 +121,29 @@ def test_chunk_validation_errors():
                                    wsb, None) == E["GDR_E_MODE"]
     assert lib.gdr_chunk_fwd_stage(0, ctypes.byref(d), None, P(2), P(3), P(4), P(5), None, P(6), P(7), P(8),
                                    wsb, None) == E["GDR_E_NULL"]
+
+
+def test_delta_off_ignores_beta_and_its_mode():
+    """Without the delta rule beta_or_eta is not read (it may be NULL) and
+    beta_mode and eps are ignored; everything else is validated as before."""
+    d = _desc(delta_off=True)
+    d.beta_mode = 9
+    d.eps = -1.0
+    assert _ws(d) == _ws(_desc())
+    # beta NULL passes the pointer checks: the call fails later, on the workspace
+    assert _call_chunk(d, b=None, ws=None) == E["GDR_E_WORKSPACE"]
+    assert _call_chunk(_desc(), b=None, ws=None) == E["GDR_E_NULL"]
+    # a beta pointer given anyway is ignored, even one that would alias o
+    assert _call_chunk(d, b=P(6), ws=None) == E["GDR_E_WORKSPACE"]
+    assert _call_chunk(d, q=None) == E["GDR_E_NULL"]
+    lib = gdr.load_library()
+    ds = _desc(T=1, delta_off=True)
+    call = lambda b, s: lib.gdr_recurrent_step(ctypes.byref(ds), P(1), P(2), P(3), P(4), b, s, P(7), None)
+    assert call(None, P(6, 4)) == E["GDR_E_ALIGN"]
+    assert call(None, None) == E["GDR_E_NULL"]
+    dr = _desc(T=1)
+    assert lib.gdr_recurrent_step(ctypes.byref(dr), P(1), P(2), P(3), P(4), None, P(6, 4), P(7),
+                                  None) == E["GDR_E_NULL"]
 
 
 def test_matrix_algo_support_and_workspace():

@@ -331,3 +331,91 @@ def test_kaczmarz_eps_zero_with_partial_chunk(algo):
     eo, es = rel(host(o), o_ref), rel(host(s), s_ref)
     print(f"kla eps=0 {algo}: rel o {eo:.2e} S {es:.2e}")
     assert eo < TOL["bf16"] and es < TOL["bf16"]
+
+
+# ------------------------------------------------------------ without the delta rule
+# The additive write S = D S + k v^T (no prediction, no beta): linear attention
+# (D = I), RetNet / Mamba-2 (scalar decay) and GLA (per-channel decay).
+NO_DELTA = {"linear": dict(per_channel=False), "retnet": dict(per_channel=False),
+            "gla": dict(per_channel=True)}
+
+
+def _no_delta_inputs(seed, B, T, H, D, variant, dtype, with_s0=True):
+    x = random_inputs(seed, B, T, H, D, D, dtype=dtype, per_channel=NO_DELTA[variant]["per_channel"],
+                      with_s0=with_s0)
+    if variant == "linear":
+        x["g"] = np.zeros_like(x["g"])
+    return x
+
+
+def _no_delta_run(x, variant, dtype, *, algo, o_dtype=torch.float32, scale=1.0, state=None):
+    d = to_dev(x, dtype)
+    s0 = d["s0"] if state is None else state
+    o, s = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], None, s0=s0, s_final=state, o_dtype=o_dtype,
+                         scale=scale, algo=algo, delta_off=True, **NO_DELTA[variant])
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.oracle_fwd(x["q"], x["k"], x["v"], x["g"], None, s0=x["s0"], scale=scale,
+                                     delta_off=True, **NO_DELTA[variant])
+    return o, s, o_ref, s_ref
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("variant", list(NO_DELTA))
+@pytest.mark.parametrize("T", [1, 64, 200])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_no_delta_parity(algo, variant, T, dtype, D):
+    _skip_unsupported(algo, "gdn", dtype, (D, D))
+    x = _no_delta_inputs(4000 + T, 2, T, 3, D, variant, dtype, with_s0=(T != 64))
+    o, s, o_ref, s_ref = _no_delta_run(x, variant, dtype, algo=algo)
+    eo, es = rel(host(o), o_ref), rel(host(s), s_ref)
+    print(f"no delta {variant} {algo} {dtype} T={T}: rel o {eo:.2e} S {es:.2e}")
+    assert eo < TOL[dtype] and es < TOL[dtype]
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("variant", ["retnet", "gla"])
+def test_no_delta_bf16_output_scale_and_beta_ignored(algo, variant):
+    """bf16 output with KDA's read scale; a beta tensor passed anyway (here
+    full of NaN) is not read."""
+    x = _no_delta_inputs(4100, 2, 150, 2, 128, variant, "bf16")
+    sc = 128 ** -0.5
+    o, s, o_ref, s_ref = _no_delta_run(x, variant, "bf16", algo=algo, o_dtype=torch.bfloat16, scale=sc)
+    assert rel(host(o), o_ref) < TOL["bf16"] and rel(host(s), s_ref) < TOL["bf16"]
+    d = to_dev(x, "bf16")
+    nan_beta = torch.full_like(d["beta"], float("nan"))
+    desc = gdr.make_desc(2, 150, 2, 128, 128, qkv_dtype=torch.bfloat16, o_dtype=torch.bfloat16,
+                         per_channel=NO_DELTA[variant]["per_channel"], scale=sc, algo=algo, delta_off=True)
+    ws = torch.empty(gdr.chunk_fwd_workspace_size(desc), dtype=torch.uint8, device=DEV)
+    o2 = torch.empty_like(o)
+    s2 = torch.empty_like(s)
+    lib = gdr.load_library()
+    import ctypes
+    rc = lib.gdr_chunk_fwd(ctypes.byref(desc), *[ctypes.c_void_p(t.data_ptr()) for t in
+                                                 (d["q"], d["k"], d["v"], d["g"], nan_beta, d["s0"], o2, s2, ws)],
+                           ws.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o) and torch.equal(s2, s)
+
+
+@pytest.mark.parametrize("variant", ["linear", "retnet"])
+def test_no_delta_walk_in_time_segments(variant):
+    """The time-segmented walk without the delta rule (the chunk map's M is
+    then the product of the chunk decays times I), state updated in place."""
+    x = _no_delta_inputs(4200, 1, 64 * 128 + 37, 2, 128, variant, "bf16")
+    if variant == "linear":  # keep the undecayed sums of 8229 writes moderate (a power of two: bf16 stays exact)
+        x["v"] = (x["v"] * 0.0625).astype(np.float32)
+    state = torch.from_numpy(x["s0"]).to(DEV)
+    o, _, o_ref, s_ref = _no_delta_run(x, variant, "bf16", algo="matrix", state=state)
+    eo, es = rel(host(o), o_ref), rel(host(state), s_ref)
+    print(f"segmented walk, no delta, {variant}: rel o {eo:.2e} S {es:.2e}")
+    assert eo < TOL["bf16"] and es < TOL["bf16"]
+
+
+@pytest.mark.parametrize("variant", list(NO_DELTA))
+def test_no_delta_matrix_close_to_vector_and_chunk_counts(variant):
+    x = _no_delta_inputs(4300, 3, 64 * 5 + 11, 3, 128, variant, "bf16")
+    om, sm, o_ref, s_ref = _no_delta_run(x, variant, "bf16", algo="matrix")
+    ov, sv, _, _ = _no_delta_run(x, variant, "bf16", algo="vector")
+    assert rel(host(om), host(ov)) < TOL["bf16"] and rel(host(sm), host(sv)) < TOL["bf16"]
+    assert rel(host(om), o_ref) < TOL["bf16"] and rel(host(sm), s_ref) < TOL["bf16"]

@@ -11,7 +11,7 @@ from tests.gpu_util import DEV, TOL, host, rel, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, steps, *, o_dtype=torch.float32, scale=1.0, kaczmarz=False):
+def _run(w, steps, *, o_dtype=torch.float32, scale=1.0, kaczmarz=False, delta_off=False, zero_gate=False):
     s0 = decode_state0(w)
     state = torch.from_numpy(s0).to(DEV)
     inputs, outs = [], []
@@ -19,16 +19,19 @@ def _run(w, steps, *, o_dtype=torch.float32, scale=1.0, kaczmarz=False):
         x = decode_step_inputs(w, t)
         if kaczmarz:
             x["beta"] = (x["beta"] * 1.5).astype(np.float32)   # eta
+        if zero_gate:
+            x["g"] = np.zeros_like(x["g"])
         inputs.append(x)
         d = to_dev(x, w.dtype)
-        o = gdr.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, per_channel=w.per_channel,
-                               kaczmarz=kaczmarz, eps=1e-6 if kaczmarz else 0.0, scale=scale, o_dtype=o_dtype)
+        o = gdr.recurrent_step(d["q"], d["k"], d["v"], d["g"], None if delta_off else d["beta"], state,
+                               per_channel=w.per_channel, kaczmarz=kaczmarz, eps=1e-6 if kaczmarz else 0.0,
+                               scale=scale, o_dtype=o_dtype, delta_off=delta_off)
         outs.append(host(o))
     torch.cuda.synchronize()
     st = {key: np.stack([x[key] for x in inputs]) for key in inputs[0]}
     o_ref, s_ref = oracle.oracle_decode(st["q"], st["k"], st["v"], st["g"], st["beta"], s0,
                                         per_channel=w.per_channel, kaczmarz=kaczmarz,
-                                        eps=1e-6 if kaczmarz else 0.0, scale=scale)
+                                        eps=1e-6 if kaczmarz else 0.0, scale=scale, delta_off=delta_off)
     return np.stack(outs), host(state), o_ref, s_ref
 
 
@@ -43,6 +46,17 @@ def test_decode_parity(D, mode, dtype):
     print(f"decode {mode} {dtype} D={D}: rel o {eo:.2e} S {es:.2e}")
     assert eo < TOL[dtype] and es < TOL[dtype]
     assert eo < 1e-5 and es < 1e-5          # fp32 arithmetic on exact inputs
+
+
+@pytest.mark.parametrize("variant", ["linear", "retnet", "gla"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_without_delta_rule(variant, dtype):
+    """The additive write S = D S + k v^T (no prediction, no beta) per step."""
+    w = WORKLOADS["decode"].scaled(B=5, H=3, dtype=dtype, decay="per_channel" if variant == "gla" else "scalar")
+    o, s, o_ref, s_ref = _run(w, 12, delta_off=True, zero_gate=variant == "linear", scale=0.5)
+    eo, es = rel(o, o_ref), rel(s, s_ref)
+    print(f"decode no delta {variant} {dtype}: rel o {eo:.2e} S {es:.2e}")
+    assert eo < 1e-5 and es < 1e-5
 
 
 def test_decode_bf16_output_and_scale():
