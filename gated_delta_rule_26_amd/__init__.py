@@ -10,6 +10,7 @@ built, importing works but every call raises ``GdrNotBuilt``.
 Entry points (same names as the C ABI):
   chunk_fwd(q, k, v, g, beta, ...)        -> (o, s_final)   chunked prefill
   recurrent_step(q, k, v, g, beta, state) -> o              one decode step (state in place)
+  recurrent_fwd(q, k, v, g, beta, state)  -> o              T tokens, recurrent (state in place)
   chunk_fwd_workspace_size(...)           -> bytes
 """
 from __future__ import annotations
@@ -19,7 +20,7 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_workspace_size", "GdrError", "GdrNotBuilt",
+__all__ = ["chunk_fwd", "recurrent_step", "recurrent_fwd", "chunk_fwd_workspace_size", "GdrError", "GdrNotBuilt",
            "library_path", "abi_version", "load_library", "Desc"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -80,6 +81,8 @@ def load_library(path: str | None = None):
     lib.gdr_chunk_fwd_stage.argtypes = [ctypes.c_int, D, V, V, V, V, V, V, V, V, V, ctypes.c_size_t, V]
     lib.gdr_recurrent_step.restype = ctypes.c_int
     lib.gdr_recurrent_step.argtypes = [D, V, V, V, V, V, V, V, V]
+    lib.gdr_recurrent_fwd.restype = ctypes.c_int
+    lib.gdr_recurrent_fwd.argtypes = [D, V, V, V, V, V, V, V, V]
     if path is None:
         _lib = lib
     return lib
@@ -226,4 +229,43 @@ def recurrent_step(q, k, v, g, beta, state, *, per_channel: bool = False, kaczma
                                 _ptr(state), _ptr(o), ctypes.c_void_p(st.cuda_stream))
     if rc != 0:
         raise GdrError(rc, "gdr_recurrent_step")
+    return o
+
+
+def recurrent_fwd(q, k, v, g, beta, state, *, per_channel: bool = False, kaczmarz: bool = False,
+                  eps: float = 0.0, scale: float = 1.0, o=None, o_dtype=None, stream=None,
+                  delta_off: bool = False):
+    """T recurrent tokens per sequence through ``gdr_recurrent_fwd``.
+
+    q, k [B,T,H,Dk], v [B,T,H,Dv] (float32 or bfloat16); g float32 [B,T,H]
+    or [B,T,H,Dk]; beta float32 [B,T,H] (None with ``delta_off``); state
+    float32 [B,H,Dk,Dv], updated in place.  Returns o [B,T,H,Dv].
+    """
+    lib = load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _check_dev("q", q, dev)
+    _check_dev("k", k, dev, q.dtype, (B, T, H, Dk))
+    _check_dev("v", v, dev, q.dtype, (B, T, H, Dv))
+    _check_dev("g", g, dev, torch.float32, (B, T, H, Dk) if per_channel else (B, T, H))
+    if delta_off:
+        beta = None
+    else:
+        _check_dev("beta", beta, dev, torch.float32, (B, T, H))
+    _check_dev("state", state, dev, torch.float32, (B, H, Dk, Dv))
+    o_dtype = o_dtype or q.dtype
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=o_dtype, device=dev)
+    else:
+        _check_dev("o", o, dev, o_dtype, (B, T, H, Dv))
+    desc = make_desc(B, T, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=o_dtype, per_channel=per_channel,
+                     kaczmarz=kaczmarz, eps=eps, scale=scale, delta_off=delta_off)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    rc = lib.gdr_recurrent_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(state), _ptr(o), ctypes.c_void_p(st.cuda_stream))
+    if rc != 0:
+        raise GdrError(rc, "gdr_recurrent_fwd")
     return o

@@ -35,9 +35,9 @@ struct Sizes {
     size_t qk, v, g, beta, state, o;  // element counts
 };
 
-// Shared descriptor validation.  `step` selects the recurrent-step reading
-// (T = 1, no chunk constraint).
-int check_desc(const gdr_desc *d, bool step, Sizes *sz) {
+// Shared descriptor validation.  `step` selects the recurrent readings (no
+// chunk constraint; T = 1 for the single step when `one_token`).
+int check_desc(const gdr_desc *d, bool step, Sizes *sz, bool one_token = true) {
     if (!d) return GDR_E_NULL;
     if (d->delta_mode != GDR_DELTA_RULE && d->delta_mode != GDR_DELTA_OFF) return GDR_E_MODE;
     const bool delta = d->delta_mode == GDR_DELTA_RULE;  // beta_mode and eps matter only then
@@ -49,7 +49,7 @@ int check_desc(const gdr_desc *d, bool step, Sizes *sz) {
     if (!std::isfinite(d->scale)) return GDR_E_MODE;
     if (delta && d->beta_mode == GDR_BETA_KACZMARZ && !(std::isfinite(d->eps) && d->eps >= 0.f))
         return GDR_E_MODE;
-    const int T = step ? 1 : d->T;
+    const int T = step && one_token ? 1 : d->T;
     if (d->B < 0 || d->H < 0 || T < 0 || d->Dk < 0 || d->Dv < 0) return GDR_E_SHAPE;
     if (!(d->Dk == 64 || d->Dk == 128) || !(d->Dv == 64 || d->Dv == 128)) return GDR_E_UNSUPPORTED;
     if (!step && d->chunk != gdr::kChunk) return GDR_E_UNSUPPORTED;
@@ -203,6 +203,47 @@ int chunk_fwd_impl(int stage, const gdr_desc *d, const void *q, const void *k, c
     return e == hipSuccess ? GDR_OK : GDR_E_HIP;
 }
 
+// The recurrent schedule: one token (gdr_recurrent_step, desc->T ignored) or
+// desc->T tokens per sequence (gdr_recurrent_fwd).
+int recurrent_impl(const gdr_desc *d, bool one_token, const void *q, const void *k, const void *v, const float *g,
+                   const float *beta_or_eta, float *state, void *o, void *stream) {
+    Sizes sz;
+    const int rc = check_desc(d, true, &sz, one_token);
+    if (rc != GDR_OK) return rc;
+    const int T = one_token ? 1 : d->T;
+    if (d->B == 0 || d->H == 0 || T == 0) return GDR_OK;
+    const bool delta = d->delta_mode == GDR_DELTA_RULE;
+    if (!delta) beta_or_eta = nullptr;
+    if (!q || !k || !v || !g || (delta && !beta_or_eta) || !state || !o) return GDR_E_NULL;
+    const bool pc = d->decay_mode == GDR_DECAY_PER_CHANNEL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(state, 16))
+        return GDR_E_ALIGN;
+    if (!aligned(g, pc ? 16 : 4) || !aligned(beta_or_eta, 4)) return GDR_E_ALIGN;
+    const size_t in_es = d->qkv_dtype == GDR_BF16 ? 2 : 4;
+    const size_t out_es = d->o_dtype == GDR_BF16 ? 2 : 4;
+    const Range rq = range_of(q, sz.qk * in_es), rk = range_of(k, sz.qk * in_es), rv = range_of(v, sz.v * in_es);
+    const Range rg = range_of(g, sz.g * 4), rb = range_of(beta_or_eta, sz.beta * 4);
+    const Range rs = range_of(state, sz.state * 4), ro = range_of(o, sz.o * out_es);
+    const Range ins[] = {rq, rk, rv, rg, rb};
+    for (const Range &r : ins)
+        if (overlap(r, rs) || overlap(r, ro)) return GDR_E_ALIAS;
+    if (overlap(rs, ro)) return GDR_E_ALIAS;
+
+    StepArgs a;
+    a.N = d->B; a.T = T; a.H = d->H; a.Dk = d->Dk; a.Dv = d->Dv;
+    a.qkv_bf16 = d->qkv_dtype == GDR_BF16;
+    a.o_bf16 = d->o_dtype == GDR_BF16;
+    a.per_channel = pc;
+    a.delta = delta;
+    a.kaczmarz = delta && d->beta_mode == GDR_BETA_KACZMARZ;
+    a.eps = a.kaczmarz ? d->eps : 0.f;
+    a.scale = d->scale;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta_or_eta;
+    a.state = state; a.o = o;
+    a.stream = static_cast<hipStream_t>(stream);
+    return gdr::launch_recurrent_step(a) == hipSuccess ? GDR_OK : GDR_E_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -223,40 +264,12 @@ int gdr_chunk_fwd_stage(int stage, const gdr_desc *d, const void *q, const void 
 
 int gdr_recurrent_step(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
                        const float *beta_or_eta, float *state, void *o, void *stream) {
-    Sizes sz;
-    const int rc = check_desc(d, true, &sz);
-    if (rc != GDR_OK) return rc;
-    if (d->B == 0 || d->H == 0) return GDR_OK;
-    const bool delta = d->delta_mode == GDR_DELTA_RULE;
-    if (!delta) beta_or_eta = nullptr;
-    if (!q || !k || !v || !g || (delta && !beta_or_eta) || !state || !o) return GDR_E_NULL;
-    const bool pc = d->decay_mode == GDR_DECAY_PER_CHANNEL;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(state, 16))
-        return GDR_E_ALIGN;
-    if (!aligned(g, pc ? 16 : 4) || !aligned(beta_or_eta, 4)) return GDR_E_ALIGN;
-    const size_t in_es = d->qkv_dtype == GDR_BF16 ? 2 : 4;
-    const size_t out_es = d->o_dtype == GDR_BF16 ? 2 : 4;
-    const Range rq = range_of(q, sz.qk * in_es), rk = range_of(k, sz.qk * in_es), rv = range_of(v, sz.v * in_es);
-    const Range rg = range_of(g, sz.g * 4), rb = range_of(beta_or_eta, sz.beta * 4);
-    const Range rs = range_of(state, sz.state * 4), ro = range_of(o, sz.o * out_es);
-    const Range ins[] = {rq, rk, rv, rg, rb};
-    for (const Range &r : ins)
-        if (overlap(r, rs) || overlap(r, ro)) return GDR_E_ALIAS;
-    if (overlap(rs, ro)) return GDR_E_ALIAS;
+    return recurrent_impl(d, true, q, k, v, g, beta_or_eta, state, o, stream);
+}
 
-    StepArgs a;
-    a.N = d->B; a.H = d->H; a.Dk = d->Dk; a.Dv = d->Dv;
-    a.qkv_bf16 = d->qkv_dtype == GDR_BF16;
-    a.o_bf16 = d->o_dtype == GDR_BF16;
-    a.per_channel = pc;
-    a.delta = delta;
-    a.kaczmarz = delta && d->beta_mode == GDR_BETA_KACZMARZ;
-    a.eps = a.kaczmarz ? d->eps : 0.f;
-    a.scale = d->scale;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta_or_eta;
-    a.state = state; a.o = o;
-    a.stream = static_cast<hipStream_t>(stream);
-    return gdr::launch_recurrent_step(a) == hipSuccess ? GDR_OK : GDR_E_HIP;
+int gdr_recurrent_fwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
+                      const float *beta_or_eta, float *state, void *o, void *stream) {
+    return recurrent_impl(d, false, q, k, v, g, beta_or_eta, state, o, stream);
 }
 
 }  // extern "C"

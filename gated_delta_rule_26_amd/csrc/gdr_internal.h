@@ -25,9 +25,9 @@ struct ChunkArgs {
     hipStream_t stream;
 };
 
-// Validated arguments of gdr_recurrent_step.
+// Validated arguments of gdr_recurrent_step (T = 1) and gdr_recurrent_fwd.
 struct StepArgs {
-    int N, H, Dk, Dv;
+    int N, T, H, Dk, Dv;
     bool qkv_bf16, o_bf16, per_channel, kaczmarz;
     bool delta;              // false: additive write S = D S + k v^T (beta is NULL)
     float eps, scale;
@@ -56,7 +56,7 @@ hipError_t launch_chunk_matrix_pc(const ChunkArgs &a, int stage);
 // T == 0: s_final = s0 (or zero).
 hipError_t launch_state_init(float *dst, const float *src, size_t n, hipStream_t stream);
 
-// Fused single-token recurrent step.
+// Fused recurrent steps over T >= 1 tokens per sequence.
 hipError_t launch_recurrent_step(const StepArgs &a);
 
 }  // namespace gdr

@@ -1,4 +1,5 @@
-// Fused single-token recurrent step of the gated delta rule (decode).
+// Fused recurrent schedule of the gated delta rule: decode (one token) and
+// short sequences (T tokens per sequence with the state kept in registers).
 //
 // Blog summary on the DeltaNet family, "Kernel Triton recurrente fusionado":
 // the recurrent schedule fuses decay, prediction, residual, rank-1 write and
@@ -17,6 +18,10 @@
 // wavefronts through LDS.  The output uses o = scale (r + beta e (k.q)), so no
 // second pass over the state is needed.
 //
+// A run of T tokens keeps the state in registers: it is read before the
+// first token and written after the last, and each token's q, k, v and gates
+// are loaded while the previous token is computed.  Decode is T = 1.
+//
 // Without the delta rule (delta = false: linear attention, RetNet / Mamba-2,
 // GLA; textbook page, update table) the write is S = S~ + k v^T: the same
 // pass with e = v and beta = 1 (the prediction is formed and not used; the
@@ -32,22 +37,26 @@ template <int DK, int DV, bool PC, bool KZ, bool IN_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ state,
-    void *__restrict__ o, float eps, float scale, bool delta) {
+    void *__restrict__ o, int T, int H, float eps, float scale, bool delta) {
     constexpr int TPR = DV / 4;          // threads per state row (one float4 each)
     constexpr int RPP = kThreads / TPR;  // rows per pass of the workgroup
     constexpr int PASSES = DK / RPP;
     static_assert(DK % RPP == 0, "state rows must tile the workgroup");
 
     const size_t nh = blockIdx.x;  // flattened (sequence, head)
+    const size_t n = nh / H, h = nh % H;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int c4 = tid % TPR;      // column quad owned by this thread
     const int r0 = tid / TPR;      // first row owned by this thread
 
-    __shared__ float sk[DK], sq[DK], sa[PC ? DK : 1];
-    __shared__ float4 red[2][4][TPR];
-    __shared__ float s_kq, s_beta;
+    // Per-token LDS is double-buffered by token parity: token t+1 fills its
+    // buffers while token t's are still read, so each token needs two
+    // barriers (inputs published; partial sums published).
+    __shared__ float sk[2][DK], sq[2][DK], sa[2][PC ? DK : 1];
+    __shared__ float4 red[2][2][4][TPR];
+    __shared__ float s_kq[2], s_beta[2];
 
     float *S = state + nh * DK * DV;
 
@@ -57,93 +66,113 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
     for (int p = 0; p < PASSES; ++p)
         s[p] = *reinterpret_cast<const float4 *>(S + (size_t)(p * RPP + r0) * DV + 4 * c4);
 
-    if (tid < DK) {
-        sk[tid] = load_in<IN_BF16>(k, nh * DK + tid);
-        sq[tid] = load_in<IN_BF16>(q, nh * DK + tid);
-        if constexpr (PC) sa[tid] = __expf(g[nh * DK + tid]);
-    }
-    const float4 vv = make_float4(load_in<IN_BF16>(v, nh * DV + 4 * c4 + 0),
-                                  load_in<IN_BF16>(v, nh * DV + 4 * c4 + 1),
-                                  load_in<IN_BF16>(v, nh * DV + 4 * c4 + 2),
-                                  load_in<IN_BF16>(v, nh * DV + 4 * c4 + 3));
-    const float a_scalar = PC ? 1.0f : __expf(g[nh]);
-    __syncthreads();
-
-    if (wave == 0) {
-        float kq = 0.f, kk = 0.f;
-        for (int i = lane; i < DK; i += 64) {
-            kq += sk[i] * sq[i];
-            kk += sk[i] * sk[i];
+    // token t of this (sequence, head): row (n T + t) H + h of q, k, v, g, beta
+    auto row_of = [&](int t) { return ((size_t)n * T + t) * H + h; };
+    float kin = 0.f, qin = 0.f, gin = 0.f, bin = 1.f, gsc = 0.f;
+    float4 vin;
+    auto fetch = [&](int t) {  // token t's inputs into registers
+        const size_t r = row_of(t);
+        if (tid < DK) {
+            kin = load_in<IN_BF16>(k, r * DK + tid);
+            qin = load_in<IN_BF16>(q, r * DK + tid);
+            if constexpr (PC) gin = g[r * DK + tid];
         }
-        kq = wave_sum(kq);
-        kk = wave_sum(kk);
-        if (lane == 0) {
-            s_kq = kq;
-            const float b = delta ? beta[nh] : 1.f;
-            s_beta = KZ ? b / (kk + eps) : b;
+        vin = make_float4(load_in<IN_BF16>(v, r * DV + 4 * c4 + 0), load_in<IN_BF16>(v, r * DV + 4 * c4 + 1),
+                          load_in<IN_BF16>(v, r * DV + 4 * c4 + 2), load_in<IN_BF16>(v, r * DV + 4 * c4 + 3));
+        if constexpr (!PC) gsc = g[r];
+        if (wave == 0 && delta) bin = beta[r];
+    };
+    if (T > 0) fetch(0);
+    for (int t = 0; t < T; ++t) {
+        const int b = t & 1;
+        if (tid < DK) {
+            sk[b][tid] = kin;
+            sq[b][tid] = qin;
+            if constexpr (PC) sa[b][tid] = __expf(gin);
+        }
+        const float4 vv = vin;
+        const float a_scalar = PC ? 1.0f : __expf(gsc);
+        const float bet = bin;
+        if (t + 1 < T) fetch(t + 1);  // next token's inputs, in flight during this one
+        __syncthreads();
+
+        if (wave == 0) {
+            float kq = 0.f, kk = 0.f;
+            for (int i = lane; i < DK; i += 64) {
+                kq += sk[b][i] * sq[b][i];
+                kk += sk[b][i] * sk[b][i];
+            }
+            kq = wave_sum(kq);
+            kk = wave_sum(kk);
+            if (lane == 0) {
+                s_kq[b] = kq;
+                s_beta[b] = KZ ? bet / (kk + eps) : bet;
+            }
+        }
+
+        // Column partial sums of the decayed state against k (prediction) and q (read).
+        float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = pk;
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            const int row = p * RPP + r0;
+            const float a = PC ? sa[b][row] : a_scalar;
+            const float ak = a * sk[b][row], aq = a * sq[b][row];
+            pk.x += ak * s[p].x; pk.y += ak * s[p].y; pk.z += ak * s[p].z; pk.w += ak * s[p].w;
+            pq.x += aq * s[p].x; pq.y += aq * s[p].y; pq.z += aq * s[p].z; pq.w += aq * s[p].w;
+        }
+#pragma unroll
+        for (int off = TPR; off < 64; off <<= 1) {
+            pk.x += __shfl_xor(pk.x, off, 64); pk.y += __shfl_xor(pk.y, off, 64);
+            pk.z += __shfl_xor(pk.z, off, 64); pk.w += __shfl_xor(pk.w, off, 64);
+            pq.x += __shfl_xor(pq.x, off, 64); pq.y += __shfl_xor(pq.y, off, 64);
+            pq.z += __shfl_xor(pq.z, off, 64); pq.w += __shfl_xor(pq.w, off, 64);
+        }
+        if (lane < TPR) {
+            red[b][0][wave][c4] = pk;
+            red[b][1][wave][c4] = pq;
+        }
+        __syncthreads();
+        float4 P = red[b][0][0][c4], R = red[b][1][0][c4];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+            const float4 x = red[b][0][w][c4], y = red[b][1][w][c4];
+            P.x += x.x; P.y += x.y; P.z += x.z; P.w += x.w;
+            R.x += y.x; R.y += y.y; R.z += y.z; R.w += y.w;
+        }
+        const float bt = s_beta[b];
+        const float4 e = delta ? make_float4(vv.x - P.x, vv.y - P.y, vv.z - P.z, vv.w - P.w) : vv;
+
+        if (r0 == 0) {  // read after write: o = scale (S~^T q + beta e (k.q))
+            const float bkq = bt * s_kq[b];
+            const size_t ob = row_of(t) * DV + 4 * c4;
+            store_out<OUT_BF16>(o, ob + 0, scale * (R.x + bkq * e.x));
+            store_out<OUT_BF16>(o, ob + 1, scale * (R.y + bkq * e.y));
+            store_out<OUT_BF16>(o, ob + 2, scale * (R.z + bkq * e.z));
+            store_out<OUT_BF16>(o, ob + 3, scale * (R.w + bkq * e.w));
+        }
+
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            const int row = p * RPP + r0;
+            const float a = PC ? sa[b][row] : a_scalar;
+            const float bk = bt * sk[b][row];
+            s[p].x = a * s[p].x + bk * e.x;
+            s[p].y = a * s[p].y + bk * e.y;
+            s[p].z = a * s[p].z + bk * e.z;
+            s[p].w = a * s[p].w + bk * e.w;
         }
     }
 
-    // Column partial sums of the decayed state against k (prediction) and q (read).
-    float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = pk;
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-        const int row = p * RPP + r0;
-        const float a = PC ? sa[row] : a_scalar;
-        const float ak = a * sk[row], aq = a * sq[row];
-        pk.x += ak * s[p].x; pk.y += ak * s[p].y; pk.z += ak * s[p].z; pk.w += ak * s[p].w;
-        pq.x += aq * s[p].x; pq.y += aq * s[p].y; pq.z += aq * s[p].z; pq.w += aq * s[p].w;
-    }
-#pragma unroll
-    for (int off = TPR; off < 64; off <<= 1) {
-        pk.x += __shfl_xor(pk.x, off, 64); pk.y += __shfl_xor(pk.y, off, 64);
-        pk.z += __shfl_xor(pk.z, off, 64); pk.w += __shfl_xor(pk.w, off, 64);
-        pq.x += __shfl_xor(pq.x, off, 64); pq.y += __shfl_xor(pq.y, off, 64);
-        pq.z += __shfl_xor(pq.z, off, 64); pq.w += __shfl_xor(pq.w, off, 64);
-    }
-    if (lane < TPR) {
-        red[0][wave][c4] = pk;
-        red[1][wave][c4] = pq;
-    }
-    __syncthreads();
-    float4 P = red[0][0][c4], R = red[1][0][c4];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) {
-        const float4 a = red[0][w][c4], b = red[1][w][c4];
-        P.x += a.x; P.y += a.y; P.z += a.z; P.w += a.w;
-        R.x += b.x; R.y += b.y; R.z += b.z; R.w += b.w;
-    }
-    const float bt = s_beta;
-    const float4 e = delta ? make_float4(vv.x - P.x, vv.y - P.y, vv.z - P.z, vv.w - P.w) : vv;
-
-    if (r0 == 0) {  // read after write: o = scale (S~^T q + beta e (k.q))
-        const float bkq = bt * s_kq;
-        const size_t ob = nh * DV + 4 * c4;
-        store_out<OUT_BF16>(o, ob + 0, scale * (R.x + bkq * e.x));
-        store_out<OUT_BF16>(o, ob + 1, scale * (R.y + bkq * e.y));
-        store_out<OUT_BF16>(o, ob + 2, scale * (R.z + bkq * e.z));
-        store_out<OUT_BF16>(o, ob + 3, scale * (R.w + bkq * e.w));
-    }
-
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-        const int row = p * RPP + r0;
-        const float a = PC ? sa[row] : a_scalar;
-        const float bk = bt * sk[row];
-        float4 ns;
-        ns.x = a * s[p].x + bk * e.x;
-        ns.y = a * s[p].y + bk * e.y;
-        ns.z = a * s[p].z + bk * e.z;
-        ns.w = a * s[p].w + bk * e.w;
-        *reinterpret_cast<float4 *>(S + (size_t)row * DV + 4 * c4) = ns;
-    }
+    for (int p = 0; p < PASSES; ++p)
+        *reinterpret_cast<float4 *>(S + (size_t)(p * RPP + r0) * DV + 4 * c4) = s[p];
 }
 
 template <int DK, int DV, bool PC, bool KZ, bool IB, bool OB>
 hipError_t launch_t(const StepArgs &a) {
     const unsigned grid = static_cast<unsigned>(a.N) * static_cast<unsigned>(a.H);
     hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, PC, KZ, IB, OB>), dim3(grid), dim3(kThreads),
-                       0, a.stream, a.q, a.k, a.v, a.g, a.beta, a.state, a.o, a.eps, a.scale,
+                       0, a.stream, a.q, a.k, a.v, a.g, a.beta, a.state, a.o, a.T, a.H, a.eps, a.scale,
                        a.delta);
     return hipGetLastError();
 }

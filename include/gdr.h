@@ -191,6 +191,30 @@ int gdr_recurrent_step(const gdr_desc *desc,
                        const float *g, const float *beta_or_eta,
                        float *state, void *o, void *stream);
 
+/*
+ * The fused recurrent schedule over desc->T tokens of B sequences (short
+ * prefills, several decode tokens at once): token after token as in
+ * gdr_recurrent_step, with the state read once before the first token and
+ * written once after the last (blog summary, "Kernel Triton recurrente
+ * fusionado", which puts the recurrent mode in charge of decode and short
+ * sequences).
+ *
+ *   q, k        [B, T, H, Dk]  qkv_dtype
+ *   v           [B, T, H, Dv]  qkv_dtype
+ *   g           [B, T, H] or [B, T, H, Dk] fp32
+ *   beta_or_eta [B, T, H] fp32 (may be NULL with GDR_DELTA_OFF)
+ *   state       [B, H, Dk, Dv] fp32, read and updated in place
+ *   o           [B, T, H, Dv] o_dtype (written)
+ * desc->chunk and desc->algo are ignored; T == 0, B == 0 or H == 0 is a
+ * no-op.  The same results as gdr_chunk_fwd with s0 = s_final = state, to
+ * rounding; the work is sequential in T, so long sequences belong on the
+ * chunked path.  Inputs must not overlap state or o.
+ */
+int gdr_recurrent_fwd(const gdr_desc *desc,
+                      const void *q, const void *k, const void *v,
+                      const float *g, const float *beta_or_eta,
+                      float *state, void *o, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,8 @@ def test_exports_every_declared_symbol():
     lib = gdr.load_library()
     names = declared_functions()
     assert names == sorted(["gdr_abi_version", "gdr_status_string", "gdr_chunk_fwd_workspace_size",
-                            "gdr_chunk_fwd", "gdr_chunk_fwd_stage", "gdr_recurrent_step"])
+                            "gdr_chunk_fwd", "gdr_chunk_fwd_stage", "gdr_recurrent_step",
+                            "gdr_recurrent_fwd"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -196,3 +197,25 @@ def test_step_validation_errors():
     bad = _desc()
     bad.o_dtype = 5
     assert call(desc=bad) == E["GDR_E_MODE"]
+
+
+def test_recurrent_fwd_validation_errors():
+    """T tokens per sequence: T is validated (the single step ignores it) and
+    the chunk length is not."""
+    lib = gdr.load_library()
+
+    def call(desc, q=P(1), k=P(2), v=P(3), g=P(4), b=P(5), s=P(6), o=P(7)):
+        return lib.gdr_recurrent_fwd(ctypes.byref(desc), q, k, v, g, b, s, o, None)
+
+    d = _desc(T=40, chunk=7)
+    assert call(d, q=None) == E["GDR_E_NULL"]
+    assert call(d, s=P(6, 4)) == E["GDR_E_ALIGN"]
+    assert call(d, o=P(2, 256)) == E["GDR_E_ALIAS"]
+    assert call(_desc(T=-1)) == E["GDR_E_SHAPE"]
+    assert call(_desc(T=5, Dk=96)) == E["GDR_E_UNSUPPORTED"]
+    # T = 0 (and B = 0) are no-ops that touch no pointer
+    assert call(_desc(T=0), q=None, s=None, o=None) == E["GDR_OK"]
+    assert call(_desc(B=0), q=None, s=None, o=None) == E["GDR_OK"]
+    # the single step ignores T
+    assert lib.gdr_recurrent_step(ctypes.byref(_desc(T=-5)), P(1), P(2), P(3), P(4), P(5), P(6, 4), P(7),
+                                  None) == E["GDR_E_ALIGN"]

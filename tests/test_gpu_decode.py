@@ -98,3 +98,77 @@ def test_decode_full_workload_sampled():
     eo, es = rel(o, o_ref[:, :, 0]), rel(s, s_ref[:, 0])
     print(f"decode full workload (48 sampled states): rel o {eo:.2e} S {es:.2e}")
     assert eo < TOL["bf16"] and es < TOL["bf16"]
+
+
+# ------------------------------------------------------------ T tokens per call
+from gdr_inputs import random_inputs  # noqa: E402
+
+RMODES = {"gdn": dict(per_channel=False, kaczmarz=False),
+          "kda": dict(per_channel=True, kaczmarz=False),
+          "kla": dict(per_channel=False, kaczmarz=True)}
+
+
+def _recurrent_fwd(x, dtype, mode, *, delta_off=False, scale=1.0, o_dtype=torch.float32):
+    m = RMODES[mode]
+    d = to_dev(x, dtype)
+    state = d["s0"].clone()
+    o = gdr.recurrent_fwd(d["q"], d["k"], d["v"], d["g"], None if delta_off else d["beta"], state,
+                          eps=1e-6 if m["kaczmarz"] else 0.0, scale=scale, o_dtype=o_dtype,
+                          delta_off=delta_off, **m)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.oracle_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], s0=x["s0"], scale=scale,
+                                     eps=1e-6 if m["kaczmarz"] else 0.0, delta_off=delta_off, **m)
+    return o, state, o_ref, s_ref
+
+
+@pytest.mark.parametrize("T", [1, 7, 40])
+@pytest.mark.parametrize("mode", ["gdn", "kda", "kla"])
+@pytest.mark.parametrize("dtype,D", [("bf16", (128, 128)), ("f32", (64, 128)), ("bf16", (128, 64))])
+def test_recurrent_fwd_parity(T, mode, dtype, D):
+    x = random_inputs(500 + T, 3, T, 2, D[0], D[1], dtype=dtype, per_channel=RMODES[mode]["per_channel"],
+                      kaczmarz=RMODES[mode]["kaczmarz"],
+                      key_norm="lognormal_norm" if mode == "kla" else "unit", with_s0=True)
+    o, s, o_ref, s_ref = _recurrent_fwd(x, dtype, mode)
+    eo, es = rel(host(o), o_ref), rel(host(s), s_ref)
+    print(f"recurrent fwd {mode} {dtype} D={D} T={T}: rel o {eo:.2e} S {es:.2e}")
+    assert eo < 1e-5 and es < 1e-5          # fp32 arithmetic on exact inputs
+
+
+@pytest.mark.parametrize("variant", ["retnet", "gla"])
+def test_recurrent_fwd_without_delta_rule_and_bf16_output(variant):
+    mode = "kda" if variant == "gla" else "gdn"
+    x = random_inputs(600, 2, 33, 3, 128, 128, dtype="bf16", per_channel=variant == "gla", with_s0=True)
+    o, s, o_ref, s_ref = _recurrent_fwd(x, "bf16", mode, delta_off=True, scale=128 ** -0.5,
+                                        o_dtype=torch.bfloat16)
+    assert rel(host(o), o_ref) < TOL["bf16"] and rel(host(s), s_ref) < 1e-5
+
+
+@pytest.mark.parametrize("mode", ["gdn", "kda"])
+def test_recurrent_fwd_equals_chunked_and_steps(mode):
+    """The same recurrence three ways: T = 100 tokens in one recurrent call,
+    one chunked call, and 100 single decode steps."""
+    T = 100
+    x = random_inputs(700, 2, T, 2, 128, 128, dtype="bf16", per_channel=RMODES[mode]["per_channel"],
+                      with_s0=True)
+    o_r, s_r, o_ref, s_ref = _recurrent_fwd(x, "bf16", mode)
+    d = to_dev(x, "bf16")
+    o_c, s_c = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], s0=d["s0"], o_dtype=torch.float32,
+                             algo="vector", **RMODES[mode])
+    state = d["s0"].clone()
+    o_s = torch.stack([gdr.recurrent_step(d["q"][:, t].contiguous(), d["k"][:, t].contiguous(),
+                                          d["v"][:, t].contiguous(), d["g"][:, t].contiguous(),
+                                          d["beta"][:, t].contiguous(), state, o_dtype=torch.float32,
+                                          **RMODES[mode]) for t in range(T)], dim=1)
+    torch.cuda.synchronize()
+    assert rel(host(o_r), host(o_c)) < 1e-5 and rel(host(s_r), host(s_c)) < 1e-5
+    assert torch.equal(o_r, o_s) and torch.equal(s_r, state)   # the same arithmetic, token by token
+    assert rel(host(o_r), o_ref) < 1e-5
+
+
+def test_recurrent_fwd_zero_tokens_is_a_no_op():
+    x = random_inputs(800, 2, 0, 2, 64, 64, dtype="bf16", with_s0=True)
+    d = to_dev(x, "bf16")
+    state = d["s0"].clone()
+    o = gdr.recurrent_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], state)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 0, 2, 64) and torch.equal(state, d["s0"])
