@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
   chunk_fwd(q, k, v, g, beta, ...)        -> (o, s_final)   chunked prefill
   recurrent_step(q, k, v, g, beta, state) -> o              one decode step (state in place)
   recurrent_fwd(q, k, v, g, beta, state)  -> o              T tokens, recurrent (state in place)
+  chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, ...) -> (o, s_final)   packed batch of sequences
   chunk_fwd_workspace_size(...)           -> bytes
 """
 from __future__ import annotations
@@ -20,7 +21,8 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "recurrent_step", "recurrent_fwd", "chunk_fwd_workspace_size", "GdrError", "GdrNotBuilt",
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "recurrent_step", "recurrent_fwd", "chunk_fwd_workspace_size",
+           "chunk_fwd_varlen_workspace_size", "GdrError", "GdrNotBuilt",
            "library_path", "abi_version", "load_library", "Desc"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +79,10 @@ def load_library(path: str | None = None):
     lib.gdr_chunk_fwd_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdr_chunk_fwd.restype = ctypes.c_int
     lib.gdr_chunk_fwd.argtypes = [D, V, V, V, V, V, V, V, V, V, ctypes.c_size_t, V]
+    lib.gdr_chunk_fwd_varlen_workspace_size.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_varlen_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_chunk_fwd_varlen.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_varlen.argtypes = [D, V, V, V, V, V, V, V, V, V, V, ctypes.c_size_t, V]
     lib.gdr_chunk_fwd_stage.restype = ctypes.c_int
     lib.gdr_chunk_fwd_stage.argtypes = [ctypes.c_int, D, V, V, V, V, V, V, V, V, V, ctypes.c_size_t, V]
     lib.gdr_recurrent_step.restype = ctypes.c_int
@@ -269,3 +275,68 @@ def recurrent_fwd(q, k, v, g, beta, state, *, per_channel: bool = False, kaczmar
     if rc != 0:
         raise GdrError(rc, "gdr_recurrent_fwd")
     return o
+
+
+def chunk_fwd_varlen_workspace_size(desc: Desc) -> int:
+    out = ctypes.c_size_t(0)
+    rc = load_library().gdr_chunk_fwd_varlen_workspace_size(ctypes.byref(desc), ctypes.byref(out))
+    if rc != 0:
+        raise GdrError(rc, "gdr_chunk_fwd_varlen_workspace_size")
+    return int(out.value)
+
+
+def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, *, per_channel: bool = False, kaczmarz: bool = False,
+                     eps: float = 0.0, scale: float = 1.0, s0=None, output_final_state: bool = True,
+                     s_final=None, o=None, o_dtype=None, algo: str = "auto", workspace=None, stream=None,
+                     delta_off: bool = False):
+    """Chunked forward pass over a packed batch through ``gdr_chunk_fwd_varlen``.
+
+    q, k [T,H,Dk], v [T,H,Dv] hold the tokens of N sequences back to back;
+    sequence n is tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 (cu_seqlens: int32
+    [N+1] on the device).  g float32 [T,H] or [T,H,Dk]; beta float32 [T,H]
+    (None with ``delta_off``); s0 float32 [N,H,Dk,Dv] or None.  Returns
+    (o [T,H,Dv], s_final [N,H,Dk,Dv] or None).
+    """
+    lib = load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _check_dev("cu_seqlens", cu_seqlens, dev, torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-d int32 tensor of N + 1 entries")
+    N = cu_seqlens.numel() - 1
+    _check_dev("q", q, dev)
+    _check_dev("k", k, dev, q.dtype, (T, H, Dk))
+    _check_dev("v", v, dev, q.dtype, (T, H, Dv))
+    _check_dev("g", g, dev, torch.float32, (T, H, Dk) if per_channel else (T, H))
+    if delta_off:
+        beta = None
+    else:
+        _check_dev("beta", beta, dev, torch.float32, (T, H))
+    if s0 is not None:
+        _check_dev("s0", s0, dev, torch.float32, (N, H, Dk, Dv))
+    o_dtype = o_dtype or q.dtype
+    if o is None:
+        o = torch.empty((T, H, Dv), dtype=o_dtype, device=dev)
+    else:
+        _check_dev("o", o, dev, o_dtype, (T, H, Dv))
+    if s_final is None and output_final_state:
+        s_final = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
+    elif s_final is not None:
+        _check_dev("s_final", s_final, dev, torch.float32, (N, H, Dk, Dv))
+    desc = make_desc(N, T, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=o_dtype, per_channel=per_channel,
+                     kaczmarz=kaczmarz, eps=eps, scale=scale, algo=algo, delta_off=delta_off)
+    need = chunk_fwd_varlen_workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _check_dev("workspace", workspace, dev, torch.uint8)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    rc = lib.gdr_chunk_fwd_varlen(ctypes.byref(desc), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                  _ptr(beta), _ptr(s0), _ptr(o), _ptr(s_final), _ptr(workspace),
+                                  workspace.numel(), ctypes.c_void_p(st.cuda_stream))
+    if rc != 0:
+        raise GdrError(rc, "gdr_chunk_fwd_varlen")
+    return o, s_final

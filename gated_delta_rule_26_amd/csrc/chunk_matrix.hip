@@ -86,8 +86,10 @@ template <bool KZ, bool DELTA>
 __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, int T, int H, int NC, int total, float eps, float scale,
-    char *__restrict__ ws) {
+    char *__restrict__ ws, SeqTable tb) {
     __shared__ IntraSmem sm;
+    if (tb.start) total = tb.cbase[tb.N] * H;  // packed batch: the chunks the table holds
+    if (total <= 0) return;
     const int qk_stride = H * DK * 2;
     const TriTiles tri{sm.u.t.R, sm.u.t.Toff, sm.u.t.A};
     const int seg = threadIdx.x & 15, i0 = threadIdx.x >> 4;
@@ -99,9 +101,9 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
     uint4 qv[4], kv[4];
     float gv, ev;
     auto prefetch = [&](int cj) {
-        const int cc = cj % NC, bhj = cj / NC;
-        const int tt = cc * C, nn = min(C, T - tt);
-        const size_t r0 = ((size_t)(bhj / H) * T + tt) * H + bhj % H;
+        size_t r0;
+        int nn;
+        chunk_place(cj, T, H, NC, tb, r0, nn);
         const auto rk = rows_rsrc(k + r0 * DK, nn, qk_stride, DK * 2);
         const auto rq = rows_rsrc(q + r0 * DK, nn, qk_stride, DK * 2);
 #pragma unroll
@@ -122,8 +124,9 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
-    const int t0 = (ci % NC) * C;
-    const int n = min(C, T - t0);
+    size_t r0_unused;
+    int n;
+    chunk_place(ci, T, H, NC, tb, r0_unused, n);
     char *recb = ws + (size_t)ci * kRecBytes;
     __syncthreads();  // the previous chunk's tiles are no longer read
 
@@ -277,7 +280,7 @@ template <bool OUT_BF16, bool TRANSFER, bool DELTA>
 __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const char *__restrict__ ws, const float *__restrict__ s0, void *__restrict__ o,
-    float *__restrict__ s_out, int T, int H, int NC, int G, int P, int seg, float scale) {
+    float *__restrict__ s_out, int T, int H, int NC, int G, int P, int seg, float scale, SeqTable tb) {
     __shared__ StateSmem sm;
 
     int g, slice;
@@ -285,13 +288,15 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
     const int bh = g / P, p = g % P;
     const int kind = TRANSFER ? slice / NS : 0;  // transfer: 0 = N, 1 = M
     const int c0 = p * seg;
-    const int nc = min(seg, NC - c0);            // chunks of this segment
-    const int b = bh / H, h = bh % H;
+    const WalkPlace wp = walk_place(bh, c0, seg, T, H, NC, tb, ws, kRecBytes);
+    const int nc = wp.nc;                        // chunks of this segment
+    const int L = wp.L;                          // tokens of this sequence
+    const size_t rstride = wp.rstride;           // bytes from one chunk's record to the next
     const int j0 = (slice % NS) * BV;
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
-    const char *recs = ws + ((size_t)bh * NC + c0) * kRecBytes;
+    const char *recs = wp.recs;
     const float *s_in = TRANSFER || !s0 ? nullptr : s0 + (size_t)g * DK * DV;
     float *s_end = TRANSFER ? s_out + ((size_t)g * 2 + kind) * DK * DV
                             : (s_out && p == P - 1 ? s_out + (size_t)bh * DK * DV : nullptr);
@@ -343,7 +348,7 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
             const int buf = c & 1;
             // next chunk's T'' fragments, in flight during this chunk
             if constexpr (DELTA) {
-                const char *rn = recs + (size_t)min(c + 1, nc - 1) * kRecBytes;
+                const char *rn = recs + (size_t)min(c + 1, nc - 1) * rstride;
 #pragma unroll
                 for (int f = 0; f < 6; ++f) {
                     thn[f] = *reinterpret_cast<const bf16x8 *>(rn + kRecTH + f * kFragBytes + lane * 16);
@@ -504,7 +509,7 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
         // bounds); T'' and A are zero in those rows and columns anyway.
         uint4 kreg[8], qreg[8], vreg[2];
         float gam_reg, gnd_reg;
-        const size_t head0 = (size_t)b * T * H + h;  // row of token 0 of this head
+        const size_t head0 = wp.head0;  // row of token 0 of this sequence and head
         const int qk_stride = H * DK * 2, v_stride = H * DV * 2;
         // byte offsets, inside a chunk, of this thread's q/k and v pieces
         int qk_off[8], v_off[2];
@@ -514,7 +519,7 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
         for (int u = 0; u < 2; ++u) v_off[u] = (2 * (ht >> 2) + u) * v_stride + 2 * (j0 + 8 * (ht & 3));
         auto load_stage = [&](int cc) {  // chunk cc's q, k, v slice and G into registers
             const int t0 = (c0 + cc) * C;
-            const int n = min(C, T - t0);
+            const int n = min(C, L - t0);
             const size_t row0 = head0 + (size_t)t0 * H;
             const auto rk = rows_rsrc(k + row0 * DK, n, qk_stride, DK * 2);
             const auto rq = rows_rsrc(q + row0 * DK, n, qk_stride, DK * 2);
@@ -526,7 +531,7 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) vreg[u] = buf_ld16(rv, v_off[u]);
-            const char *rec = recs + (size_t)cc * kRecBytes;
+            const char *rec = recs + (size_t)cc * rstride;
             gam_reg = reinterpret_cast<const float *>(rec + kRecGam)[ht & 63];
             gnd_reg = reinterpret_cast<const float *>(rec + kRecGend)[ht & 63];
         };
@@ -558,7 +563,7 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
         };
         bf16x8 ah[6], al[6];
         auto load_out_ops = [&](int cc) {  // chunk cc's A fragments
-            const char *rec = recs + (size_t)cc * kRecBytes;
+            const char *rec = recs + (size_t)cc * rstride;
 #pragma unroll
             for (int f = 0; f < 6; ++f) {
                 ah[f] = *reinterpret_cast<const bf16x8 *>(rec + kRecAH + f * kFragBytes + lane * 16);
@@ -571,7 +576,7 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
             if constexpr (!TRANSFER) {
                 const int t0 = (c0 + cp) * C;
                 chunk_outputs<OUT_BF16, true>(&sm.X[cp & 1][vt][0][0], sm.Gam[cp % 3], scale, ah, al, sm.Ost[vt],
-                                              o, head0 + (size_t)t0 * H, min(C, T - t0), H, jt, lane);
+                                              o, head0 + (size_t)t0 * H, min(C, L - t0), H, jt, lane);
             }
         };
         auto load_outputs_operands = [&](int cc) {
@@ -643,11 +648,11 @@ __global__ __launch_bounds__(1024) void segment_combine_kernel(const float *__re
 // ============================================================ launchers
 template <bool KZ, bool DELTA>
 hipError_t launch_intra(const ChunkArgs &a) {
-    const long total = (long)a.B * a.H * a.NC;
+    const long total = chunk_slots(a);
     if (total == 0) return hipSuccess;
     hipLaunchKernelGGL((intra_matrix_kernel<KZ, DELTA>), dim3(intra_grid(total, 4)), dim3(kIntraThreads), 0, a.stream,
                        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), a.g, a.beta, a.T, a.H,
-                       a.NC, (int)total, a.eps, a.scale, static_cast<char *>(a.ws));
+                       a.NC, (int)total, a.eps, a.scale, static_cast<char *>(a.ws), a.tab);
     return hipGetLastError();
 }
 
@@ -682,13 +687,14 @@ size_t segment_bytes(int BH, int NC) {
 template <bool OB, bool DELTA>
 hipError_t launch_state(const ChunkArgs &a) {
     const int BH = a.B * a.H;
-    const int P = walk_segments(BH, a.NC);
+    const int P = a.tab.start ? 1 : walk_segments(BH, a.NC);  // packed batches: one walk per sequence
     const __bf16 *q = static_cast<const __bf16 *>(a.q), *k = static_cast<const __bf16 *>(a.k),
                  *v = static_cast<const __bf16 *>(a.v);
     const char *ws = static_cast<const char *>(a.ws);
     if (P == 1) {
         hipLaunchKernelGGL((state_matrix_kernel<OB, false, DELTA>), dim3((unsigned)(BH * NS)), dim3(kStateThreads), 0,
-                           a.stream, q, k, v, ws, a.s0, a.o, a.s_final, a.T, a.H, a.NC, BH, 1, a.NC, a.scale);
+                           a.stream, q, k, v, ws, a.s0, a.o, a.s_final, a.T, a.H, a.NC, BH, 1, a.NC, a.scale,
+                           a.tab);
         return hipGetLastError();
     }
     // segments: chunk maps, entering states, then the walks with outputs
@@ -696,13 +702,15 @@ hipError_t launch_state(const ChunkArgs &a) {
     float *tr = reinterpret_cast<float *>(static_cast<char *>(a.ws) + (size_t)BH * a.NC * kRecBytes);
     float *seg_state = tr + (size_t)BH * P * 2 * DK * DV;
     hipLaunchKernelGGL((state_matrix_kernel<false, true, DELTA>), dim3((unsigned)(BH * P * 2 * NS)), dim3(kStateThreads), 0,
-                       a.stream, q, k, v, ws, nullptr, nullptr, tr, a.T, a.H, a.NC, BH * P, P, seg, a.scale);
+                       a.stream, q, k, v, ws, nullptr, nullptr, tr, a.T, a.H, a.NC, BH * P, P, seg, a.scale,
+                       SeqTable{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(segment_combine_kernel, dim3((unsigned)BH), dim3(1024), 0, a.stream, tr, a.s0, seg_state, P);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((state_matrix_kernel<OB, false, DELTA>), dim3((unsigned)(BH * P * NS)), dim3(kStateThreads), 0,
-                       a.stream, q, k, v, ws, seg_state, a.o, a.s_final, a.T, a.H, a.NC, BH * P, P, seg, a.scale);
+                       a.stream, q, k, v, ws, seg_state, a.o, a.s_final, a.T, a.H, a.NC, BH * P, P, seg, a.scale,
+                       SeqTable{});
     return hipGetLastError();
 }
 
@@ -716,9 +724,9 @@ int mx::intra_grid(long total, int per_cu) {
     return (int)std::min<long>(total, (long)per_cu * cus);
 }
 
-size_t chunk_matrix_workspace_bytes(int B, int H, int NC, int, int, bool per_channel) {
-    return per_channel ? chunk_matrix_pc_workspace_bytes(B, H, NC)
-                       : (size_t)B * H * NC * kRecBytes + segment_bytes(B * H, NC);
+size_t chunk_matrix_workspace_bytes(int B, int H, int NC, int, int, bool per_channel, bool packed) {
+    if (per_channel) return chunk_matrix_pc_workspace_bytes(B, H, NC);
+    return (size_t)B * H * NC * kRecBytes + (packed ? 0 : segment_bytes(B * H, NC));
 }
 
 bool chunk_matrix_supported(int Dk, int Dv, bool qkv_bf16, bool) { return qkv_bf16 && Dk == DK && Dv == DV; }

@@ -87,8 +87,10 @@ template <bool KZ, bool DELTA>
 __global__ __launch_bounds__(kIntraThreads, 2) void intra_pc_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, int T, int H, int NC, int total, float eps, float scale,
-    char *__restrict__ ws) {
+    char *__restrict__ ws, SeqTable tb) {
     __shared__ IntraPcSmem sm;
+    if (tb.start) total = tb.cbase[tb.N] * H;  // packed batch: the chunks the table holds
+    if (total <= 0) return;
     const int qk_stride = H * DK * 2, g_stride = H * DK * 4;
     const TriTiles tri{sm.u.t.R, sm.u.t.Toff, sm.u.t.A};
     const int seg = threadIdx.x & 15, i0 = threadIdx.x >> 4;
@@ -103,9 +105,9 @@ __global__ __launch_bounds__(kIntraThreads, 2) void intra_pc_kernel(
     float gv[32];
     float ev;
     auto prefetch = [&](int cj) {
-        const int cc = cj % NC, bhj = cj / NC;
-        const int tt = cc * C, nn = min(C, T - tt);
-        const size_t r0 = ((size_t)(bhj / H) * T + tt) * H + bhj % H;
+        size_t r0;
+        int nn;
+        chunk_place(cj, T, H, NC, tb, r0, nn);
         const auto rk = rows_rsrc(k + r0 * DK, nn, qk_stride, DK * 2);
         const auto rq = rows_rsrc(q + r0 * DK, nn, qk_stride, DK * 2);
         const auto rg = rows_rsrc(g + r0 * DK, nn, g_stride, DK * 4);
@@ -127,8 +129,9 @@ __global__ __launch_bounds__(kIntraThreads, 2) void intra_pc_kernel(
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
-    const int t0 = (ci % NC) * C;
-    const int n = min(C, T - t0);
+    size_t r0_unused;
+    int n;
+    chunk_place(ci, T, H, NC, tb, r0_unused, n);
     char *recb = ws + (size_t)ci * kPcBytes;
     __syncthreads();  // the previous chunk's tiles and G are no longer read
 
@@ -403,16 +406,19 @@ __device__ __forceinline__ void barrier_after_loads() {
 template <bool OUT_BF16, bool DELTA>
 __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
     const __bf16 *__restrict__ v, const char *__restrict__ ws, const float *__restrict__ s0, void *__restrict__ o,
-    float *__restrict__ s_final, int T, int H, int NC, int BH) {
+    float *__restrict__ s_final, int T_all, int H, int NC_all, int BH, SeqTable tb) {
     __shared__ StatePcSmem sm;
     int bh, slice;
     state_slot(blockIdx.x, BH, NS, bh, slice);
-    const int b = bh / H, h = bh % H;
+    const WalkPlace wp = walk_place(bh, 0, NC_all, T_all, H, NC_all, tb, ws, kPcBytes);
+    const int NC = wp.nc;                 // chunks of this sequence
+    const int T = wp.L;                   // tokens of this sequence
+    const size_t rstride = wp.rstride;    // bytes from one chunk's record to the next
     const int j0 = slice * BV;
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
-    const char *recs = ws + (size_t)bh * NC * kPcBytes;
+    const char *recs = wp.recs;
     const size_t sbase = (size_t)bh * DK * DV;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
@@ -454,7 +460,7 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
                         __attribute__((always_inline)) {
             const int buf = c & 1;
             if constexpr (DELTA) {  // next chunk's T'' fragments, in flight during this chunk
-                const char *rn = recs + (size_t)min(c + 1, NC - 1) * kPcBytes;
+                const char *rn = recs + (size_t)min(c + 1, NC - 1) * rstride;
 #pragma unroll
                 for (int f = 0; f < 6; ++f) {
                     thn[f] = *reinterpret_cast<const bf16x8 *>(rn + kRecTH + f * kFragBytes + lane * 16);
@@ -574,7 +580,7 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
         // wavefront vt, helper 0 between B(c-1) and A(c), helper 1 between
         // A(c) and B(c).
         const int vt = __builtin_amdgcn_readfirstlane(w - 2);
-        const size_t head0 = (size_t)b * T * H + h;  // row of token 0 of this head
+        const size_t head0 = wp.head0;  // row of token 0 of this sequence and head
         const unsigned lds_kq0 = lds_addr(sm.Kq0), lds_kq123 = lds_addr(sm.Kq123), lds_ku = lds_addr(sm.Ku);
         const unsigned lds_gend = lds_addr(sm.Gend), lds_v = lds_addr(sm.V);
         // v slice of chunk cc, 16 rows per copy (lane l: row l/4, 16-byte
@@ -595,7 +601,7 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
         auto kq0 = [&](int cc) { return lds_kq0 + (cc & 1) * (16 * 1024); };
         bf16x8 ah[6], al[6], ahn[6], aln[6];
         auto load_out_ops = [&](int cc) {  // chunk cc's A fragments
-            const char *rec = recs + (size_t)cc * kPcBytes;
+            const char *rec = recs + (size_t)cc * rstride;
 #pragma unroll
             for (int f = 0; f < 6; ++f) {
                 ahn[f] = *reinterpret_cast<const bf16x8 *>(rec + kRecAH + f * kFragBytes + lane * 16);
@@ -613,8 +619,8 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
         barrier_after_loads();
         for (int c = 0; c < NC; ++c) {
             // chain: K~ S, Q~ S of chunk c (key block 0 from its own buffer)
-            const char *rc = recs + (size_t)c * kPcBytes;
-            const char *rn = recs + (size_t)min(c + 1, NC - 1) * kPcBytes;
+            const char *rc = recs + (size_t)c * rstride;
+            const char *rn = recs + (size_t)min(c + 1, NC - 1) * rstride;
             load_out_ops(c);
             copy_to_lds<32>(rc + kPcKu, lds_ku, vt, lane);
             lds_dma4(rc + kPcGend + vt * 256 + lane * 4, lds_gend + vt * 256);
@@ -642,11 +648,11 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
 // ============================================================ launchers
 template <bool KZ, bool DELTA>
 hipError_t launch_intra_pc(const ChunkArgs &a) {
-    const long total = (long)a.B * a.H * a.NC;
+    const long total = chunk_slots(a);
     if (total == 0) return hipSuccess;
     hipLaunchKernelGGL((intra_pc_kernel<KZ, DELTA>), dim3(intra_grid(total, 2)), dim3(kIntraThreads), 0, a.stream,
                        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), a.g, a.beta, a.T, a.H,
-                       a.NC, (int)total, a.eps, a.scale, static_cast<char *>(a.ws));
+                       a.NC, (int)total, a.eps, a.scale, static_cast<char *>(a.ws), a.tab);
     return hipGetLastError();
 }
 
@@ -655,7 +661,7 @@ hipError_t launch_state_pc(const ChunkArgs &a) {
     const int BH = a.B * a.H;
     hipLaunchKernelGGL((state_pc_kernel<OB, DELTA>), dim3((unsigned)(BH * NS)), dim3(kStateThreads), 0, a.stream,
                        static_cast<const __bf16 *>(a.v), static_cast<const char *>(a.ws), a.s0, a.o, a.s_final, a.T,
-                       a.H, a.NC, BH);
+                       a.H, a.NC, BH, a.tab);
     return hipGetLastError();
 }
 

@@ -54,14 +54,24 @@ __global__ __launch_bounds__(kThreads) void intra_vector_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, int T, int H, int NC, float eps,
     float scale, bool delta, float *__restrict__ wsW, float *__restrict__ wsU, float *__restrict__ wsA,
-    float *__restrict__ wsG) {
+    float *__restrict__ wsG, SeqTable tb) {
     constexpr int GK = PC ? DK : 1;
-    const int ci = blockIdx.x;  // (b*H + h)*NC + c
-    const int c = ci % NC;
-    const int bh = ci / NC;
-    const int b = bh / H, h = bh % H;
-    const int t0 = c * C;
-    const int n = min(C, T - t0);
+    const int ci = blockIdx.x;  // (b*H + h)*NC + c; packed batches: u*H + h for chunk u of the table
+    if (tb.start && ci >= tb.cbase[tb.N] * H) return;  // past the chunks the table holds
+    size_t row0;  // [.., H, D] row of the chunk's token 0; token i is row row0 + i H
+    int n;
+    {
+        const int u = tb.start ? ci / H : 0, hh = tb.start ? ci % H : (ci / NC) % H;
+        const int b = ci / NC / H, c = ci % NC;
+        if (tb.start) {
+            const int t0 = tb.tok[u];
+            n = min(C, tb.start[tb.seq[u] + 1] - t0);
+            row0 = (size_t)t0 * H + hh;
+        } else {
+            n = min(C, T - c * C);
+            row0 = ((size_t)b * T + c * C) * H + hh;
+        }
+    }
     const int tid = threadIdx.x;
 
     __shared__ float sK[C][DK + 1];
@@ -72,17 +82,17 @@ __global__ __launch_bounds__(kThreads) void intra_vector_kernel(
 
     for (int idx = tid; idx < C * DK; idx += kThreads) {
         const int i = idx / DK, cc = idx % DK;
-        const size_t off = (((size_t)b * T + t0 + i) * H + h) * DK + cc;
+        const size_t off = (row0 + (size_t)i * H) * DK + cc;
         sK[i][cc] = i < n ? load_in<IN_BF16>(k, off) : 0.f;
         sQ[i][cc] = i < n ? load_in<IN_BF16>(q, off) : 0.f;
     }
     if constexpr (PC) {
         for (int idx = tid; idx < C * DK; idx += kThreads) {
             const int i = idx / DK, cc = idx % DK;
-            sG[i][cc] = i < n ? g[(((size_t)b * T + t0 + i) * H + h) * DK + cc] : 0.f;
+            sG[i][cc] = i < n ? g[(row0 + (size_t)i * H) * DK + cc] : 0.f;
         }
     } else {
-        if (tid < C) sG[tid][0] = tid < n ? g[((size_t)b * T + t0 + tid) * H + h] : 0.f;
+        if (tid < C) sG[tid][0] = tid < n ? g[row0 + (size_t)tid * H] : 0.f;
     }
     __syncthreads();
 
@@ -100,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void intra_vector_kernel(
         if (i < n && !delta) {
             bv = 1.f;
         } else if (i < n) {
-            const float given = beta[((size_t)b * T + t0 + i) * H + h];
+            const float given = beta[row0 + (size_t)i * H];
             if constexpr (KZ) {
                 float kk = 0.f;
                 for (int cc = 0; cc < DK; ++cc) kk += sK[i][cc] * sK[i][cc];
@@ -158,8 +168,7 @@ __global__ __launch_bounds__(kThreads) void intra_vector_kernel(
                 const float gi = PC ? sG[i][col] : sG[i][0];
                 rhs = delta ? sBeta[i] * __expf(gi) * sK[i][col] : 0.f;
             } else {
-                rhs = i < n ? sBeta[i] * load_in<IN_BF16>(v, (((size_t)b * T + t0 + i) * H + h) * DV + col)
-                            : 0.f;
+                rhs = i < n ? sBeta[i] * load_in<IN_BF16>(v, (row0 + (size_t)i * H) * DV + col) : 0.f;
             }
 #pragma unroll
             for (int j4 = 0; j4 < i / 4; ++j4) {
@@ -185,13 +194,31 @@ __global__ __launch_bounds__(kThreads) void state_vector_kernel(
     const void *__restrict__ q, const void *__restrict__ k, int T, int H, int NC,
     const float *__restrict__ wsW, const float *__restrict__ wsU, const float *__restrict__ wsA,
     const float *__restrict__ wsG, const float *__restrict__ s0, void *__restrict__ o,
-    float *__restrict__ s_final, float scale) {
+    float *__restrict__ s_final, float scale, SeqTable tb) {
     constexpr int GK = PC ? DK : 1;
     constexpr int NT = DV / kBV;
     const int tile = blockIdx.x % NT;
     const int bh = blockIdx.x / NT;
     const int b = bh / H, h = bh % H;
     const int j0 = tile * kBV;
+    // this sequence: [.., H, D] row of its token 0, its length and chunks, and
+    // the workspace index of its chunk c (first + c * cstep)
+    size_t head0, cfirst, cstep;
+    int L, nc;
+    if (tb.start) {
+        const int s = tb.start[b], cb = tb.cbase[b];
+        head0 = (size_t)s * H + h;
+        L = tb.start[b + 1] - s;
+        nc = tb.cbase[b + 1] - cb;
+        cfirst = (size_t)cb * H + h;
+        cstep = H;
+    } else {
+        head0 = (size_t)b * T * H + h;
+        L = T;
+        nc = NC;
+        cfirst = (size_t)bh * NC;
+        cstep = 1;
+    }
     const int tid = threadIdx.x;
     const int jj = tid % kBV;  // value column within the slice owned by this thread
     const int rr = tid / kBV;  // 0..7
@@ -208,10 +235,10 @@ __global__ __launch_bounds__(kThreads) void state_vector_kernel(
         sS[r][cc] = s0 ? s0[sbase + (size_t)r * DV + j0 + cc] : 0.f;
     }
 
-    for (int c = 0; c < NC; ++c) {
-        const size_t ci = (size_t)bh * NC + c;
+    for (int c = 0; c < nc; ++c) {
+        const size_t ci = cfirst + (size_t)c * cstep;
         const int t0 = c * C;
-        const int n = min(C, T - t0);
+        const int n = min(C, L - t0);
         const float *W = wsW + ci * C * DK;
         const float *U = wsU + ci * C * DV;
         const float *A = wsA + ci * C * C;
@@ -234,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void state_vector_kernel(
         for (int idx = tid; idx < C * DK; idx += kThreads) {
             const int i = idx / DK, cc = idx % DK;
             const float gi = PC ? sG[i][cc] : sG[i][0];
-            sX[i][cc] = i < n ? scale * __expf(gi) * load_in<IN_BF16>(q, (((size_t)b * T + t0 + i) * H + h) * DK + cc)
+            sX[i][cc] = i < n ? scale * __expf(gi) * load_in<IN_BF16>(q, (head0 + (size_t)(t0 + i) * H) * DK + cc)
                               : 0.f;
         }
         __syncthreads();
@@ -244,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void state_vector_kernel(
             float acc = 0.f;
             for (int cc = 0; cc < DK; ++cc) acc += sX[i][cc] * sS[cc][jj];
             for (int j = 0; j <= i; ++j) acc += sA[i][j] * sE[j][jj];
-            store_out<OUT_BF16>(o, (((size_t)b * T + t0 + i) * H + h) * DV + j0 + jj, acc);
+            store_out<OUT_BF16>(o, (head0 + (size_t)(t0 + i) * H) * DV + j0 + jj, acc);
         }
         __syncthreads();
 
@@ -253,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void state_vector_kernel(
             const int i = idx / DK, cc = idx % DK;
             const float gi = PC ? sG[i][cc] : sG[i][0];
             const float ge = PC ? sG[C - 1][cc] : sG[C - 1][0];
-            sX[i][cc] = i < n ? __expf(ge - gi) * load_in<IN_BF16>(k, (((size_t)b * T + t0 + i) * H + h) * DK + cc)
+            sX[i][cc] = i < n ? __expf(ge - gi) * load_in<IN_BF16>(k, (head0 + (size_t)(t0 + i) * H) * DK + cc)
                               : 0.f;
         }
         __syncthreads();
@@ -278,18 +305,18 @@ __global__ __launch_bounds__(kThreads) void state_vector_kernel(
 
 template <int DK, int DV, bool PC, bool KZ, bool IB, bool OB>
 hipError_t launch_t(const ChunkArgs &a, int stage) {
-    const size_t nchunks = (size_t)a.B * a.H * a.NC;
+    const size_t nchunks = (size_t)chunk_slots(a);
     VecWs w = carve(a.ws, nchunks, DK, DV, PC);
     if (stage != 1) {
         hipLaunchKernelGGL((intra_vector_kernel<DK, DV, PC, KZ, IB>), dim3((unsigned)nchunks), dim3(kThreads), 0,
                            a.stream, a.q, a.k, a.v, a.g, a.beta, a.T, a.H, a.NC, a.eps, a.scale, a.delta, w.W, w.U,
-                           w.A, w.G);
+                           w.A, w.G, a.tab);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || stage == 0) return e;
     }
     const unsigned grid = (unsigned)(a.B * a.H * (DV / kBV));
     hipLaunchKernelGGL((state_vector_kernel<DK, DV, PC, IB, OB>), dim3(grid), dim3(kThreads), 0, a.stream,
-                       a.q, a.k, a.T, a.H, a.NC, w.W, w.U, w.A, w.G, a.s0, a.o, a.s_final, a.scale);
+                       a.q, a.k, a.T, a.H, a.NC, w.W, w.U, w.A, w.G, a.s0, a.o, a.s_final, a.scale, a.tab);
     return hipGetLastError();
 }
 

@@ -36,8 +36,9 @@ struct Sizes {
 };
 
 // Shared descriptor validation.  `step` selects the recurrent readings (no
-// chunk constraint; T = 1 for the single step when `one_token`).
-int check_desc(const gdr_desc *d, bool step, Sizes *sz, bool one_token = true) {
+// chunk constraint; T = 1 for the single step when `one_token`); `packed`
+// the packed batch (B sequences sharing T tokens in all).
+int check_desc(const gdr_desc *d, bool step, Sizes *sz, bool one_token = true, bool packed = false) {
     if (!d) return GDR_E_NULL;
     if (d->delta_mode != GDR_DELTA_RULE && d->delta_mode != GDR_DELTA_OFF) return GDR_E_MODE;
     const bool delta = d->delta_mode == GDR_DELTA_RULE;  // beta_mode and eps matter only then
@@ -53,8 +54,9 @@ int check_desc(const gdr_desc *d, bool step, Sizes *sz, bool one_token = true) {
     if (d->B < 0 || d->H < 0 || T < 0 || d->Dk < 0 || d->Dv < 0) return GDR_E_SHAPE;
     if (!(d->Dk == 64 || d->Dk == 128) || !(d->Dv == 64 || d->Dv == 128)) return GDR_E_UNSUPPORTED;
     if (!step && d->chunk != gdr::kChunk) return GDR_E_UNSUPPORTED;
-    size_t tok = 1;  // B*T*H
-    if (!mul_ok(tok, (size_t)d->B) || !mul_ok(tok, (size_t)T) || !mul_ok(tok, (size_t)d->H)) return GDR_E_SHAPE;
+    size_t tok = 1;  // B*T*H (packed: T*H)
+    if (!mul_ok(tok, packed ? 1 : (size_t)d->B) || !mul_ok(tok, (size_t)T) || !mul_ok(tok, (size_t)d->H))
+        return GDR_E_SHAPE;
     size_t qk = tok, vv = tok, st = (size_t)d->B;
     if (!mul_ok(qk, (size_t)d->Dk) || !mul_ok(vv, (size_t)d->Dv)) return GDR_E_SHAPE;
     if (!mul_ok(st, (size_t)d->H) || !mul_ok(st, (size_t)d->Dk) || !mul_ok(st, (size_t)d->Dv)) return GDR_E_SHAPE;
@@ -84,18 +86,29 @@ bool matrix_path_available(const gdr_desc *d) {
                                        d->decay_mode == GDR_DECAY_PER_CHANNEL);
 }
 
-int chunk_workspace(const gdr_desc *d, size_t *bytes) {
-    const int NC = (d->T + gdr::kChunk - 1) / gdr::kChunk;
-    // one workgroup per (sequence, head, chunk): the grid must stay below 2^31
-    if ((size_t)d->B * d->H * (size_t)NC >= ((size_t)1 << 31)) return GDR_E_SHAPE;
+// Chunks per sequence (fixed length), or the chunk bound of a packed batch.
+long chunk_count(const gdr_desc *d, bool packed) {
+    return packed ? ((long)d->T + 63L * d->B) / gdr::kChunk : ((long)d->T + gdr::kChunk - 1) / gdr::kChunk;
+}
+
+// Workspace bytes; for a packed batch *table is the size of the sequence
+// table at its start (the records follow it).
+int chunk_workspace(const gdr_desc *d, bool packed, size_t *bytes, size_t *table = nullptr) {
+    const long NC = chunk_count(d, packed);
+    // one workgroup per (sequence, head, chunk) or (chunk, head): the grid must stay below 2^31
+    if ((size_t)(packed ? 1 : d->B) * d->H * (size_t)NC >= ((size_t)1 << 31)) return GDR_E_SHAPE;
     const bool pc = d->decay_mode == GDR_DECAY_PER_CHANNEL;
     int algo = resolve_algo(d);
     if (algo == GDR_ALGO_MATRIX && !matrix_path_available(d)) {
         if (d->algo == GDR_ALGO_MATRIX) return GDR_E_UNSUPPORTED;
         algo = GDR_ALGO_VECTOR;
     }
-    *bytes = algo == GDR_ALGO_MATRIX ? gdr::chunk_matrix_workspace_bytes(d->B, d->H, NC, d->Dk, d->Dv, pc)
-                                     : gdr::chunk_vector_workspace_bytes(d->B, d->H, NC, d->Dk, d->Dv, pc);
+    const int Bw = packed ? 1 : d->B;  // the records of a packed batch: NC chunks x H heads
+    const size_t tab = packed ? gdr::seq_table_bytes(d->B, (int)NC) : 0;
+    *bytes = tab + (algo == GDR_ALGO_MATRIX
+                        ? gdr::chunk_matrix_workspace_bytes(Bw, d->H, (int)NC, d->Dk, d->Dv, pc, packed)
+                        : gdr::chunk_vector_workspace_bytes(Bw, d->H, (int)NC, d->Dk, d->Dv, pc));
+    if (table) *table = tab;
     return GDR_OK;
 }
 
@@ -125,22 +138,31 @@ int gdr_chunk_fwd_workspace_size(const gdr_desc *desc, size_t *bytes) {
     Sizes sz;
     const int rc = check_desc(desc, false, &sz);
     if (rc != GDR_OK) return rc;
-    return chunk_workspace(desc, bytes);
+    return chunk_workspace(desc, false, bytes);
+}
+
+int gdr_chunk_fwd_varlen_workspace_size(const gdr_desc *desc, size_t *bytes) {
+    if (!bytes) return GDR_E_NULL;
+    Sizes sz;
+    const int rc = check_desc(desc, false, &sz, true, true);
+    if (rc != GDR_OK) return rc;
+    return chunk_workspace(desc, true, bytes);
 }
 
 }  // extern "C"
 
 namespace {
 
-// stage: -1 = the whole chunked pass, 0 = intra kernel, 1 = state kernel
-int chunk_fwd_impl(int stage, const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
-                   const float *beta_or_eta, const float *s0, void *o, float *s_final, void *workspace,
-                   size_t workspace_bytes, void *stream) {
+// stage: -1 = the whole chunked pass, 0 = intra kernel, 1 = state kernel.
+// cu_seqlens != NULL: a packed batch (the varlen entry point).
+int chunk_fwd_impl(int stage, const gdr_desc *d, const int32_t *cu_seqlens, const void *q, const void *k,
+                   const void *v, const float *g, const float *beta_or_eta, const float *s0, void *o,
+                   float *s_final, void *workspace, size_t workspace_bytes, void *stream, bool packed = false) {
     Sizes sz;
-    int rc = check_desc(d, false, &sz);
+    int rc = check_desc(d, false, &sz, true, packed);
     if (rc != GDR_OK) return rc;
-    size_t need = 0;
-    rc = chunk_workspace(d, &need);
+    size_t need = 0, table = 0;
+    rc = chunk_workspace(d, packed, &need, &table);
     if (rc != GDR_OK) return rc;
     if (d->B == 0 || d->H == 0) return GDR_OK;
     const bool pc = d->decay_mode == GDR_DECAY_PER_CHANNEL;
@@ -150,6 +172,8 @@ int chunk_fwd_impl(int stage, const gdr_desc *d, const void *q, const void *k, c
     const bool delta = d->delta_mode == GDR_DELTA_RULE;
     if (!delta) beta_or_eta = nullptr;
 
+    if (packed && !cu_seqlens) return GDR_E_NULL;
+    if (packed && !aligned(cu_seqlens, 4)) return GDR_E_ALIGN;
     if (have_tokens) {
         if (!q || !k || !v || !g || (delta && !beta_or_eta) || !o) return GDR_E_NULL;
         if (need > 0 && !workspace) return GDR_E_WORKSPACE;
@@ -167,7 +191,8 @@ int chunk_fwd_impl(int stage, const gdr_desc *d, const void *q, const void *k, c
     const Range rs0 = range_of(s0, s0 ? sz.state * 4 : 0);
     const Range rsf = range_of(s_final, s_final ? sz.state * 4 : 0);
     const Range rws = range_of(workspace, have_tokens ? need : 0);
-    const Range ins[] = {rq, rk, rv, rg, rb};
+    const Range rcu = range_of(cu_seqlens, packed ? ((size_t)d->B + 1) * 4 : 0);
+    const Range ins[] = {rq, rk, rv, rg, rb, rcu};
     for (const Range &r : ins) {
         if (have_tokens && (overlap(r, ro) || overlap(r, rws))) return GDR_E_ALIAS;
         if (overlap(r, rsf)) return GDR_E_ALIAS;
@@ -184,7 +209,7 @@ int chunk_fwd_impl(int stage, const gdr_desc *d, const void *q, const void *k, c
 
     ChunkArgs a;
     a.B = d->B; a.T = d->T; a.H = d->H; a.Dk = d->Dk; a.Dv = d->Dv;
-    a.NC = (d->T + gdr::kChunk - 1) / gdr::kChunk;
+    a.NC = (int)chunk_count(d, packed);
     a.qkv_bf16 = d->qkv_dtype == GDR_BF16;
     a.o_bf16 = d->o_dtype == GDR_BF16;
     a.per_channel = pc;
@@ -196,6 +221,12 @@ int chunk_fwd_impl(int stage, const gdr_desc *d, const void *q, const void *k, c
     a.s0 = s0; a.o = o; a.s_final = s_final;
     a.ws = workspace;
     a.stream = st;
+    if (packed) {  // the sequence table first; the records after it
+        if (gdr::launch_seq_table(cu_seqlens, d->B, d->T, workspace, st) != hipSuccess) return GDR_E_HIP;
+        a.tab = gdr::seq_table(workspace, d->B, a.NC);
+        a.tab.N = d->B;
+        a.ws = static_cast<char *>(workspace) + table;
+    }
     int algo = resolve_algo(d);
     if (algo == GDR_ALGO_MATRIX && !matrix_path_available(d)) algo = GDR_ALGO_VECTOR;
     const hipError_t e =
@@ -251,15 +282,23 @@ extern "C" {
 int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
                   const float *beta_or_eta, const float *s0, void *o, float *s_final, void *workspace,
                   size_t workspace_bytes, void *stream) {
-    return chunk_fwd_impl(-1, d, q, k, v, g, beta_or_eta, s0, o, s_final, workspace, workspace_bytes, stream);
+    return chunk_fwd_impl(-1, d, nullptr, q, k, v, g, beta_or_eta, s0, o, s_final, workspace, workspace_bytes,
+                          stream);
+}
+
+int gdr_chunk_fwd_varlen(const gdr_desc *d, const int32_t *cu_seqlens, const void *q, const void *k,
+                         const void *v, const float *g, const float *beta_or_eta, const float *s0, void *o,
+                         float *s_final, void *workspace, size_t workspace_bytes, void *stream) {
+    return chunk_fwd_impl(-1, d, cu_seqlens, q, k, v, g, beta_or_eta, s0, o, s_final, workspace, workspace_bytes,
+                          stream, true);
 }
 
 int gdr_chunk_fwd_stage(int stage, const gdr_desc *d, const void *q, const void *k, const void *v,
                         const float *g, const float *beta_or_eta, const float *s0, void *o, float *s_final,
                         void *workspace, size_t workspace_bytes, void *stream) {
     if (stage != GDR_STAGE_INTRA && stage != GDR_STAGE_STATE) return GDR_E_MODE;
-    return chunk_fwd_impl(stage, d, q, k, v, g, beta_or_eta, s0, o, s_final, workspace, workspace_bytes,
-                          stream);
+    return chunk_fwd_impl(stage, d, nullptr, q, k, v, g, beta_or_eta, s0, o, s_final, workspace,
+                          workspace_bytes, stream);
 }
 
 int gdr_recurrent_step(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,

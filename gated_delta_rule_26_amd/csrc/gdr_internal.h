@@ -9,10 +9,32 @@
 
 namespace gdr {
 
-// Validated arguments of gdr_chunk_fwd, as the launchers see them.
+constexpr int kChunk = 64;
+
+// The sequences of a variable-length (packed) batch, as device tables built
+// from cu_seqlens by launch_seq_table at the start of the workspace.  With
+// start == nullptr the batch has B sequences of T tokens each.
+struct SeqTable {
+    const int *start = nullptr;  // [N+1] first token of sequence n (clamped, non-decreasing; start[N] <= T)
+    const int *cbase = nullptr;  // [N+1] first chunk of sequence n; cbase[N] = number of chunks
+    const int *tok = nullptr;    // [chunk bound] first token of chunk u
+    const int *seq = nullptr;    // [chunk bound] sequence of chunk u
+    int N = 0;
+};
+// Chunk bound of N packed sequences of T tokens in all: floor((T + 63 N) / 64).
+int varlen_max_chunks(int N, int T);
+size_t seq_table_bytes(int N, int NCmax);
+SeqTable seq_table(void *ws, int N, int NCmax);
+hipError_t launch_seq_table(const int *cu, int N, int T, void *ws, hipStream_t stream);
+
+// Validated arguments of gdr_chunk_fwd, as the launchers see them.  For a
+// packed batch B = N sequences, T = tokens in all, NC = the chunk bound, ws
+// = the workspace after the table, and the records of chunk u of head h are
+// record u * H + h (for a fixed-length batch: (b * H + h) * NC + c).
 struct ChunkArgs {
     int B, T, H, Dk, Dv;
-    int NC;                  // chunks per sequence, ceil(T / 64)
+    int NC;                  // chunks per sequence, ceil(T / 64) (packed: the chunk bound)
+    SeqTable tab;            // packed batches only
     bool qkv_bf16, o_bf16, per_channel, kaczmarz;
     bool delta;              // false: additive write S = D S + k v^T (beta is NULL)
     float eps, scale;
@@ -24,6 +46,11 @@ struct ChunkArgs {
     void *ws;
     hipStream_t stream;
 };
+
+// Number of chunk records (chunks times heads) the kernels are launched for.
+inline long chunk_slots(const ChunkArgs &a) {
+    return a.tab.start ? (long)a.NC * a.H : (long)a.B * a.H * a.NC;
+}
 
 // Validated arguments of gdr_recurrent_step (T = 1) and gdr_recurrent_fwd.
 struct StepArgs {
@@ -38,15 +65,14 @@ struct StepArgs {
     hipStream_t stream;
 };
 
-constexpr int kChunk = 64;
-
 // Vector-ALU chunked path (fp32 arithmetic, any input dtype).
 size_t chunk_vector_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel);
 // stage: -1 = both kernels, 0 = intra kernel only, 1 = state kernel only
 hipError_t launch_chunk_vector(const ChunkArgs &a, int stage);
 
 // Matrix-core chunked path (bf16 MFMA with fp32 accumulation, bf16 inputs).
-size_t chunk_matrix_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel);
+// packed: records only (a packed batch is walked one sequence per walk, no time segments)
+size_t chunk_matrix_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel, bool packed);
 bool chunk_matrix_supported(int Dk, int Dv, bool qkv_bf16, bool per_channel);
 hipError_t launch_chunk_matrix(const ChunkArgs &a, int stage);
 // Its per-channel-decay kernels (called by the two functions above).

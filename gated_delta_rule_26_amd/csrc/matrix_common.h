@@ -109,6 +109,53 @@ __device__ __forceinline__ float buf_ld4f(__amdgpu_buffer_rsrc_t r, int off) {
 
 // ---- chunk triangle in LDS: 16x16 fp32 tiles, row stride LT
 constexpr int kIntraThreads = 256;
+
+// Chunk ci of the intra kernels' order: the [.., H, D] row of its first token
+// and its token count.  Fixed-length batch: ci = (b H + h) NC + c; packed
+// batch: ci = u H + h for chunk u of the table.
+__device__ __forceinline__ void chunk_place(int ci, int T, int H, int NC, const SeqTable &tb, size_t &row0, int &n) {
+    if (tb.start) {
+        const int u = ci / H, h = ci - u * H;
+        const int t0 = tb.tok[u];
+        n = min(C, tb.start[tb.seq[u] + 1] - t0);
+        row0 = (size_t)t0 * H + h;
+    } else {
+        const int c = ci % NC, bh = ci / NC;
+        const int t0 = c * C;
+        n = min(C, T - t0);
+        row0 = ((size_t)(bh / H) * T + t0) * H + bh % H;
+    }
+}
+
+// The chunks one walk covers: sequence `bh / H` (head bh % H), chunks c0 ..
+// c0 + nc - 1 of it, the [.., H, D] row of its token 0, its length L, and
+// the byte address and stride of its chunk records (rec_bytes each).
+struct WalkPlace {
+    size_t head0;
+    int L, nc;
+    const char *recs;
+    size_t rstride;
+};
+__device__ __forceinline__ WalkPlace walk_place(int bh, int c0, int seg, int T, int H, int NC, const SeqTable &tb,
+                                                const char *ws, size_t rec_bytes) {
+    const int b = bh / H, h = bh - b * H;
+    WalkPlace w;
+    if (tb.start) {
+        const int s = tb.start[b], cb = tb.cbase[b];
+        w.L = tb.start[b + 1] - s;
+        w.head0 = (size_t)s * H + h;
+        w.nc = min(seg, tb.cbase[b + 1] - cb - c0);
+        w.rstride = (size_t)H * rec_bytes;
+        w.recs = ws + ((size_t)(cb + c0) * H + h) * rec_bytes;
+    } else {
+        w.L = T;
+        w.head0 = (size_t)b * T * H + h;
+        w.nc = min(seg, NC - c0);
+        w.rstride = rec_bytes;
+        w.recs = ws + ((size_t)bh * NC + c0) * rec_bytes;
+    }
+    return w;
+}
 constexpr int LT = 20;           // fp32 row stride of a 16x16 tile in LDS (16-byte aligned rows)
 constexpr int LQK = DK + 8;      // bf16 row stride of the staged q, k (token-major)
 constexpr int kTile = 16 * LT;   // floats per tile

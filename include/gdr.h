@@ -149,6 +149,38 @@ int gdr_chunk_fwd(const gdr_desc *desc,
                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Chunked forward pass over a packed batch of sequences of different lengths
+ * (serving: prefills of several requests in one call; blog summary, "Pipeline
+ * Triton por chunks", on the chunk mode for prefill next to the recurrent one
+ * for decode).  desc->B is the number of sequences N and desc->T the number of
+ * tokens of all of them; sequence n holds tokens [cu_seqlens[n],
+ * cu_seqlens[n+1]) of the packed tensors and has its own state.
+ *
+ *   cu_seqlens  [N + 1] int32 in DEVICE memory, 0 = cu[0] <= ... <= cu[N] = T
+ *   q, k        [T, H, Dk]  qkv_dtype, contiguous
+ *   v           [T, H, Dv]  qkv_dtype, contiguous
+ *   g           [T, H] or [T, H, Dk] fp32
+ *   beta_or_eta [T, H] fp32 (may be NULL with GDR_DELTA_OFF)
+ *   s0, s_final [N, H, Dk, Dv] fp32 (as for gdr_chunk_fwd: s0 may be NULL,
+ *               s_final may be NULL or equal s0)
+ *   o           [T, H, Dv]  o_dtype (written for the tokens of the sequences)
+ *   workspace   at least gdr_chunk_fwd_varlen_workspace_size bytes
+ * Every sequence gives the results gdr_chunk_fwd gives for it alone.  The
+ * library does not read cu_seqlens on the host.  On the device, entries
+ * outside the form above never address memory out of bounds: each is clamped
+ * to [0, T] and raised to the largest entry before it (tokens outside every
+ * sequence are then not written).  Empty sequences are allowed (their final
+ * state is their initial one).  Long sequences are walked in one piece (no
+ * time segments).  cu_seqlens must not overlap o, s_final or the workspace.
+ */
+int gdr_chunk_fwd_varlen_workspace_size(const gdr_desc *desc, size_t *bytes);
+int gdr_chunk_fwd_varlen(const gdr_desc *desc, const int32_t *cu_seqlens,
+                         const void *q, const void *k, const void *v,
+                         const float *g, const float *beta_or_eta,
+                         const float *s0, void *o, float *s_final,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One stage of gdr_chunk_fwd, with the same arguments.  The chunked path is a
  * pipeline of two kernels (blog summary, "Pipeline Triton por chunks": an
  * intra-chunk kernel builds the in-chunk interaction matrices and the WY-like

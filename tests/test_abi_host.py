@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert names == sorted(["gdr_abi_version", "gdr_status_string", "gdr_chunk_fwd_workspace_size",
                             "gdr_chunk_fwd", "gdr_chunk_fwd_stage", "gdr_recurrent_step",
-                            "gdr_recurrent_fwd"])
+                            "gdr_recurrent_fwd", "gdr_chunk_fwd_varlen", "gdr_chunk_fwd_varlen_workspace_size"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -219,3 +219,41 @@ def test_recurrent_fwd_validation_errors():
     # the single step ignores T
     assert lib.gdr_recurrent_step(ctypes.byref(_desc(T=-5)), P(1), P(2), P(3), P(4), P(5), P(6, 4), P(7),
                                   None) == E["GDR_E_ALIGN"]
+
+
+def _ws_varlen(desc):
+    n = ctypes.c_size_t(0)
+    rc = gdr.load_library().gdr_chunk_fwd_varlen_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    return rc, n.value
+
+
+def test_varlen_workspace_and_validation():
+    """A packed batch of N sequences, T tokens in all: at most
+    floor((T + 63 N) / 64) chunks, each with one record per head, after a
+    table of 2 (N + 1) + 2 x chunks int32 rounded up to 256 bytes."""
+    N, T, H = 5, 1000, 3
+    nc = (T + 63 * N) // 64
+    table = -(-4 * (2 * (N + 1) + 2 * nc) // 256) * 256
+    rec = 4 * 6 * 1024 + 2 * 64 * 4
+    assert _ws_varlen(_desc(B=N, T=T, H=H, algo="matrix")) == (0, table + nc * H * rec)
+    pc = 4 * 6 * 1024 + 6 * 16 * 1024 + 128 * 4
+    assert _ws_varlen(_desc(B=N, T=T, H=H, per_channel=True, algo="matrix")) == (0, table + nc * H * pc)
+    # no time segments for packed batches, however long the sequence
+    assert _ws_varlen(_desc(B=1, T=131072, H=16, algo="matrix")) == (0, 256 * -(-4 * (4 + 2 * 2048) // 256)
+                                                                     + 2048 * 16 * rec)
+    lib = gdr.load_library()
+    d = _desc(B=N, T=T, H=H, algo="matrix")
+    wsb = _ws_varlen(d)[1]
+
+    def call(cu=P(10), q=P(1), ws=P(8), sf=P(7), desc=d):
+        return lib.gdr_chunk_fwd_varlen(ctypes.byref(desc), cu, q, P(2), P(3), P(4), P(5), None, P(6), sf, ws,
+                                        wsb, None)
+
+    assert call(cu=None) == E["GDR_E_NULL"]
+    assert call(cu=P(10, 2)) == E["GDR_E_ALIGN"]
+    assert call(cu=P(6, 64)) == E["GDR_E_ALIAS"]      # cu_seqlens inside o
+    assert call(cu=P(8, 64)) == E["GDR_E_ALIAS"]      # cu_seqlens inside the workspace
+    assert call(q=None) == E["GDR_E_NULL"]
+    assert call(ws=None) == E["GDR_E_WORKSPACE"]
+    # the packed token count is T (not B x T): q may be as small as T*H*Dk elements
+    assert call(desc=_desc(B=N, T=T, H=H, Dk=96, algo="matrix")) == E["GDR_E_UNSUPPORTED"]
