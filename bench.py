@@ -133,7 +133,7 @@ def cpu_baseline(w, x, heads=None):
             "seconds": dt, "cpu": platform.processor() or platform.machine()}
 
 
-def bench_prefill(w, steps, warmup, algo, o_dtype):
+def bench_prefill(w, steps, warmup, algo, o_dtype, cold_steps=0):
     import torch
     import gated_delta_rule_26_amd as gdr
     from gdr_inputs import prefill_inputs
@@ -180,8 +180,24 @@ def bench_prefill(w, steps, warmup, algo, o_dtype):
     intra_ms = [e[0].elapsed_time(e[1]) for e in evs]
     state_ms = [e[1].elapsed_time(e[2]) for e in evs]
     step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    # cold caches: before each of these steps a 512 MiB buffer is written, twice the 256 MB last-level
+    # (Infinity) cache, so the step's inputs come from HBM; events bracket the two kernels only
+    cold = None
+    if cold_steps > 0:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(cold_steps)]
+        for i in range(cold_steps):
+            scratch.fill_(i & 0xff)
+            step(cev[i])
+        torch.cuda.synchronize()
+        del scratch
+        cold = {"steps": cold_steps, "step_ms_median": median([e[0].elapsed_time(e[2]) for e in cev]),
+                "intra_ms_median": median([e[0].elapsed_time(e[1]) for e in cev]),
+                "state_ms_median": median([e[1].elapsed_time(e[2]) for e in cev]),
+                "flush": "512 MiB device buffer written before each step"}
     return {"wall_s": wall, "intra_ms": intra_ms, "state_ms": state_ms, "step_ms": step_ms, "inputs": x,
-            "o_bytes": 4 if odt == torch.float32 else 2, "in_bytes": 2 if qdt == torch.bfloat16 else 4}
+            "o_bytes": 4 if odt == torch.float32 else 2, "in_bytes": 2 if qdt == torch.bfloat16 else 4,
+            "cold": cold}
 
 
 def bench_decode(w, steps, distinct):
@@ -247,6 +263,8 @@ def main():
     ap.add_argument("--decode-distinct", type=int, default=16,
                     help="distinct decode-step inputs kept resident and cycled through")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="extra prefill steps, each after writing 512 MiB to evict the last-level cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (for rocprofv3 counter scaling)")
@@ -269,7 +287,7 @@ def main():
         sys.exit(3)
 
     w = WORKLOADS[args.workload]
-    pre = bench_prefill(w, args.steps, args.warmup, args.algo, args.o_dtype)
+    pre = bench_prefill(w, args.steps, args.warmup, args.algo, args.o_dtype, args.cold_steps)
     tok_heads = w.B * w.T * w.H
     ms_step = pre["wall_s"] / args.steps * 1e3
     value = w.B * w.T / (ms_step / 1e3)
@@ -331,6 +349,7 @@ def main():
                                    "frac": mfma_view / PEAK_BF16_MFMA}},
         "prefill": {"intra_ms": intra_ms, "state_ms": state_ms, "event_step_ms": event_step_ms,
                     "intra_ms_median": median(pre["intra_ms"]), "state_ms_median": median(pre["state_ms"]),
+                    "cold_cache": pre["cold"],
                     "alg_tflops": total_tflops, "frac_bf16_mfma_peak": total_tflops / PEAK_BF16_MFMA,
                     "alg_bytes": abytes, "alg_gbps": abytes / (event_step_ms * 1e-3) / 1e9,
                     "frac_hbm_peak": abytes / (event_step_ms * 1e-3) / 1e9 / PEAK_HBM,
