@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
   recurrent_step(q, k, v, g, beta, state) -> o              one decode step (state in place)
   recurrent_fwd(q, k, v, g, beta, state)  -> o              T tokens, recurrent (state in place)
   chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, ...) -> (o, s_final)   packed batch of sequences
+  chunk_bwd(q, k, v, g, beta, d_o, ...)   -> dict of gradients  backward pass (training)
   chunk_fwd_workspace_size(...)           -> bytes
 """
 from __future__ import annotations
@@ -21,7 +22,7 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "recurrent_step", "recurrent_fwd", "chunk_fwd_workspace_size",
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_bwd", "chunk_bwd_workspace_size", "recurrent_step", "recurrent_fwd", "chunk_fwd_workspace_size",
            "chunk_fwd_varlen_workspace_size", "GdrError", "GdrNotBuilt",
            "library_path", "abi_version", "load_library", "Desc"]
 
@@ -83,6 +84,10 @@ def load_library(path: str | None = None):
     lib.gdr_chunk_fwd_varlen_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdr_chunk_fwd_varlen.restype = ctypes.c_int
     lib.gdr_chunk_fwd_varlen.argtypes = [D, V, V, V, V, V, V, V, V, V, V, ctypes.c_size_t, V]
+    lib.gdr_chunk_bwd_workspace_size.restype = ctypes.c_int
+    lib.gdr_chunk_bwd_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_chunk_bwd.restype = ctypes.c_int
+    lib.gdr_chunk_bwd.argtypes = [D] + [V] * 15 + [ctypes.c_size_t, V]
     lib.gdr_chunk_fwd_stage.restype = ctypes.c_int
     lib.gdr_chunk_fwd_stage.argtypes = [ctypes.c_int, D, V, V, V, V, V, V, V, V, V, ctypes.c_size_t, V]
     lib.gdr_recurrent_step.restype = ctypes.c_int
@@ -340,3 +345,59 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, *, per_channel: bool = False,
     if rc != 0:
         raise GdrError(rc, "gdr_chunk_fwd_varlen")
     return o, s_final
+
+
+def chunk_bwd_workspace_size(desc: Desc) -> int:
+    out = ctypes.c_size_t(0)
+    rc = load_library().gdr_chunk_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(out))
+    if rc != 0:
+        raise GdrError(rc, "gdr_chunk_bwd_workspace_size")
+    return int(out.value)
+
+
+def chunk_bwd(q, k, v, g, beta, d_o, *, per_channel: bool = False, kaczmarz: bool = False, eps: float = 0.0,
+              scale: float = 1.0, s0=None, ds_final=None, need_ds0: bool = True, workspace=None, stream=None):
+    """Backward pass of ``chunk_fwd`` through ``gdr_chunk_bwd``.
+
+    Inputs as for chunk_fwd, plus d_o float32 [B,T,H,Dv] (dL/do) and
+    ds_final float32 [B,H,Dk,Dv] or None (dL/ds_final).  Returns a dict of
+    float32 tensors: dq, dk, dv, dg, dbeta (dL/deta with ``kaczmarz``) and
+    ds0 (None unless ``need_ds0``).
+    """
+    lib = load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _check_dev("q", q, dev)
+    _check_dev("k", k, dev, q.dtype, (B, T, H, Dk))
+    _check_dev("v", v, dev, q.dtype, (B, T, H, Dv))
+    gshape = (B, T, H, Dk) if per_channel else (B, T, H)
+    _check_dev("g", g, dev, torch.float32, gshape)
+    _check_dev("beta", beta, dev, torch.float32, (B, T, H))
+    _check_dev("d_o", d_o, dev, torch.float32, (B, T, H, Dv))
+    if s0 is not None:
+        _check_dev("s0", s0, dev, torch.float32, (B, H, Dk, Dv))
+    if ds_final is not None:
+        _check_dev("ds_final", ds_final, dev, torch.float32, (B, H, Dk, Dv))
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.empty((B, T, H, Dk), **f32), "dk": torch.empty((B, T, H, Dk), **f32),
+           "dv": torch.empty((B, T, H, Dv), **f32), "dg": torch.empty(gshape, **f32),
+           "dbeta": torch.empty((B, T, H), **f32),
+           "ds0": torch.empty((B, H, Dk, Dv), **f32) if need_ds0 else None}
+    desc = make_desc(B, T, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=torch.float32, per_channel=per_channel,
+                     kaczmarz=kaczmarz, eps=eps, scale=scale)
+    need = chunk_bwd_workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _check_dev("workspace", workspace, dev, torch.uint8)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    rc = lib.gdr_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0),
+                           _ptr(d_o), _ptr(ds_final), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                           _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["ds0"]), _ptr(workspace),
+                           workspace.numel(), ctypes.c_void_p(st.cuda_stream))
+    if rc != 0:
+        raise GdrError(rc, "gdr_chunk_bwd")
+    return out

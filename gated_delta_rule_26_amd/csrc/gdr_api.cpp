@@ -293,6 +293,80 @@ int gdr_chunk_fwd_varlen(const gdr_desc *d, const int32_t *cu_seqlens, const voi
                           stream, true);
 }
 
+int gdr_chunk_bwd_workspace_size(const gdr_desc *d, size_t *bytes) {
+    if (!bytes) return GDR_E_NULL;
+    Sizes sz;
+    const int rc = check_desc(d, false, &sz);
+    if (rc != GDR_OK) return rc;
+    if (d->delta_mode != GDR_DELTA_RULE) return GDR_E_UNSUPPORTED;
+    const long NC = chunk_count(d, false);
+    if ((size_t)d->B * d->H * (size_t)NC >= ((size_t)1 << 31)) return GDR_E_SHAPE;
+    *bytes = gdr::chunk_bwd_workspace_bytes(d->B, d->H, (int)NC, d->Dk, d->Dv,
+                                            d->decay_mode == GDR_DECAY_PER_CHANNEL);
+    return GDR_OK;
+}
+
+int gdr_chunk_bwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
+                  const float *beta_or_eta, const float *s0, const float *d_o, const float *ds_final, float *dq,
+                  float *dk, float *dv, float *dg, float *dbeta, float *ds0, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    Sizes sz;
+    int rc = check_desc(d, false, &sz);
+    if (rc != GDR_OK) return rc;
+    size_t need = 0;
+    rc = gdr_chunk_bwd_workspace_size(d, &need);
+    if (rc != GDR_OK) return rc;
+    if (d->B == 0 || d->H == 0) return GDR_OK;
+    const bool pc = d->decay_mode == GDR_DECAY_PER_CHANNEL;
+    const size_t in_es = d->qkv_dtype == GDR_BF16 ? 2 : 4;
+    const bool have_tokens = d->T > 0;
+    if (have_tokens) {
+        if (!q || !k || !v || !g || !beta_or_eta || !d_o || !dq || !dk || !dv || !dg || !dbeta) return GDR_E_NULL;
+        if (!workspace) return GDR_E_WORKSPACE;
+        if (workspace_bytes < need) return GDR_E_WORKSPACE;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d_o, 16) || !aligned(dq, 16) ||
+            !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 16))
+            return GDR_E_ALIGN;
+        if (!aligned(g, pc ? 16 : 4) || !aligned(dg, pc ? 16 : 4) || !aligned(beta_or_eta, 4) || !aligned(dbeta, 4))
+            return GDR_E_ALIGN;
+    }
+    if ((s0 && !aligned(s0, 16)) || (ds_final && !aligned(ds_final, 16)) || (ds0 && !aligned(ds0, 16)))
+        return GDR_E_ALIGN;
+    const size_t tq = have_tokens ? sz.qk * in_es : 0, tv = have_tokens ? sz.v * in_es : 0;
+    const Range ins[] = {range_of(q, tq), range_of(k, tq), range_of(v, tv),
+                         range_of(g, have_tokens ? sz.g * 4 : 0), range_of(beta_or_eta, have_tokens ? sz.beta * 4 : 0),
+                         range_of(d_o, have_tokens ? sz.o * 4 : 0), range_of(s0, s0 ? sz.state * 4 : 0),
+                         range_of(ds_final, ds_final ? sz.state * 4 : 0)};
+    const Range outs[] = {range_of(dq, have_tokens ? sz.qk * 4 : 0), range_of(dk, have_tokens ? sz.qk * 4 : 0),
+                          range_of(dv, have_tokens ? sz.v * 4 : 0), range_of(dg, have_tokens ? sz.g * 4 : 0),
+                          range_of(dbeta, have_tokens ? sz.beta * 4 : 0), range_of(ds0, ds0 ? sz.state * 4 : 0),
+                          range_of(workspace, have_tokens ? need : 0)};
+    for (const Range &o : outs) {
+        for (const Range &i : ins)
+            if (overlap(o, i)) return GDR_E_ALIAS;
+        for (const Range &o2 : outs)
+            if (&o2 != &o && overlap(o, o2)) return GDR_E_ALIAS;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!have_tokens) {  // the final state is the initial one: ds0 = ds_final
+        if (!ds0) return GDR_OK;
+        return gdr::launch_state_init(ds0, ds_final, sz.state, st) == hipSuccess ? GDR_OK : GDR_E_HIP;
+    }
+    gdr::BwdArgs a;
+    a.B = d->B; a.T = d->T; a.H = d->H; a.Dk = d->Dk; a.Dv = d->Dv;
+    a.NC = (int)chunk_count(d, false);
+    a.qkv_bf16 = d->qkv_dtype == GDR_BF16;
+    a.per_channel = pc;
+    a.kaczmarz = d->beta_mode == GDR_BETA_KACZMARZ;
+    a.eps = a.kaczmarz ? d->eps : 0.f;
+    a.scale = d->scale;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta_or_eta; a.s0 = s0; a.dO = d_o; a.ds_final = ds_final;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.ds0 = ds0;
+    a.ws = workspace;
+    a.stream = st;
+    return gdr::launch_chunk_bwd(a) == hipSuccess ? GDR_OK : GDR_E_HIP;
+}
+
 int gdr_chunk_fwd_stage(int stage, const gdr_desc *d, const void *q, const void *k, const void *v,
                         const float *g, const float *beta_or_eta, const float *s0, void *o, float *s_final,
                         void *workspace, size_t workspace_bytes, void *stream) {

@@ -79,6 +79,21 @@ hipError_t launch_chunk_matrix(const ChunkArgs &a, int stage);
 size_t chunk_matrix_pc_workspace_bytes(int B, int H, int NC);
 hipError_t launch_chunk_matrix_pc(const ChunkArgs &a, int stage);
 
+// Validated arguments of gdr_chunk_bwd (fixed-length batches, the delta rule).
+struct BwdArgs {
+    int B, T, H, Dk, Dv, NC;
+    bool qkv_bf16, per_channel, kaczmarz;
+    float eps, scale;
+    const void *q, *k, *v;
+    const float *g, *beta, *s0, *dO, *ds_final;  // s0, ds_final may be NULL (zero)
+    float *dq, *dk, *dv, *dg, *dbeta, *ds0;      // ds0 may be NULL
+    void *ws;
+    hipStream_t stream;
+};
+// Backward pass (fp32 vector kernels).
+size_t chunk_bwd_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel);
+hipError_t launch_chunk_bwd(const BwdArgs &a);
+
 // T == 0: s_final = s0 (or zero).
 hipError_t launch_state_init(float *dst, const float *src, size_t n, hipStream_t stream);
 

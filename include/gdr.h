@@ -181,6 +181,40 @@ int gdr_chunk_fwd_varlen(const gdr_desc *desc, const int32_t *cu_seqlens,
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Backward pass of gdr_chunk_fwd (training): the gradients of a loss L with
+ * respect to every input, given dL/do and dL/ds_final.  The pages derive no
+ * backward pass (the blog summary, "Pipeline Triton por chunks", calls the
+ * chunked mode the training mode); it is reverse-mode differentiation of the
+ * chunk algebra of gdr_chunk_fwd, with the chunk-entering states recomputed.
+ * fp32 vector kernels; the delta rule only (GDR_DELTA_OFF gives
+ * GDR_E_UNSUPPORTED); fixed-length batches; desc->algo and desc->o_dtype are
+ * ignored.
+ *
+ *   q, k, v, g, beta_or_eta, s0   as for gdr_chunk_fwd (s0 may be NULL)
+ *   d_o       [B, T, H, Dv] fp32, dL/do
+ *   ds_final  [B, H, Dk, Dv] fp32, dL/ds_final, or NULL for zero
+ *   dq, dk    [B, T, H, Dk] fp32 (written)
+ *   dv        [B, T, H, Dv] fp32 (written)
+ *   dg        shaped as g, fp32 (written)
+ *   dbeta     [B, T, H] fp32 (written): dL/dbeta, or dL/deta for the
+ *             Kaczmarz step size
+ *   ds0       [B, H, Dk, Dv] fp32 (written), or NULL
+ *   workspace at least gdr_chunk_bwd_workspace_size bytes (per chunk and
+ *             head: the entering state and its gradient, 2 Dk Dv fp32, and
+ *             about 100 KiB of per-chunk matrices)
+ * Outputs must not overlap inputs, each other or the workspace.  With
+ * T == 0 only ds0 is written (= ds_final, or zero).
+ */
+int gdr_chunk_bwd_workspace_size(const gdr_desc *desc, size_t *bytes);
+int gdr_chunk_bwd(const gdr_desc *desc,
+                  const void *q, const void *k, const void *v,
+                  const float *g, const float *beta_or_eta, const float *s0,
+                  const float *d_o, const float *ds_final,
+                  float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                  float *ds0, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/*
  * One stage of gdr_chunk_fwd, with the same arguments.  The chunked path is a
  * pipeline of two kernels (blog summary, "Pipeline Triton por chunks": an
  * intra-chunk kernel builds the in-chunk interaction matrices and the WY-like

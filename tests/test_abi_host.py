@@ -29,7 +29,8 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert names == sorted(["gdr_abi_version", "gdr_status_string", "gdr_chunk_fwd_workspace_size",
                             "gdr_chunk_fwd", "gdr_chunk_fwd_stage", "gdr_recurrent_step",
-                            "gdr_recurrent_fwd", "gdr_chunk_fwd_varlen", "gdr_chunk_fwd_varlen_workspace_size"])
+                            "gdr_recurrent_fwd", "gdr_chunk_fwd_varlen", "gdr_chunk_fwd_varlen_workspace_size",
+                            "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_size"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -257,3 +258,33 @@ def test_varlen_workspace_and_validation():
     assert call(ws=None) == E["GDR_E_WORKSPACE"]
     # the packed token count is T (not B x T): q may be as small as T*H*Dk elements
     assert call(desc=_desc(B=N, T=T, H=H, Dk=96, algo="matrix")) == E["GDR_E_UNSUPPORTED"]
+
+
+def test_backward_workspace_and_validation():
+    """Per chunk slot: T, A, M, dA, dT'' (64 x 64 fp32 each), G and dG (64 x
+    GK), GK, beta (64), the entering state and its gradient (Dk x Dv each)."""
+    lib = gdr.load_library()
+    n = ctypes.c_size_t(0)
+
+    def ws(desc):
+        rc = lib.gdr_chunk_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+        return rc, n.value
+
+    slots = 2 * 3 * 2
+    assert ws(_desc()) == (0, slots * 4 * (5 * 4096 + 2 * 64 + 1 + 64 + 2 * 128 * 128))
+    assert ws(_desc(per_channel=True)) == (0, slots * 4 * (5 * 4096 + 2 * 64 * 128 + 128 + 64 + 2 * 128 * 128))
+    assert ws(_desc(delta_off=True))[0] == E["GDR_E_UNSUPPORTED"]
+    d = _desc()
+    wsb = ws(d)[1]
+
+    def call(q=P(1), b=P(5), do=P(9), dq=P(10), dk=P(11), dv=P(12), dg=P(13), db=P(14), ds0=None, w=P(8)):
+        return lib.gdr_chunk_bwd(ctypes.byref(d), q, P(2), P(3), P(4), b, None, do, None, dq, dk, dv, dg, db, ds0,
+                                 w, wsb, None)
+
+    assert call(q=None) == E["GDR_E_NULL"]
+    assert call(b=None) == E["GDR_E_NULL"]
+    assert call(do=None) == E["GDR_E_NULL"]
+    assert call(w=None) == E["GDR_E_WORKSPACE"]
+    assert call(dq=P(10, 4)) == E["GDR_E_ALIGN"]
+    assert call(dk=P(10, 64)) == E["GDR_E_ALIAS"]    # dk inside dq
+    assert call(dv=P(3)) == E["GDR_E_ALIAS"]         # dv on top of v
