@@ -200,6 +200,38 @@ def bench_prefill(w, steps, warmup, algo, o_dtype, cold_steps=0):
             "cold": cold}
 
 
+def bench_backward(w, x, steps, warmup):
+    """The backward pass (gdr_chunk_bwd) on the prefill workload's inputs
+    with a seeded standard-normal dL/do; events around each call."""
+    import numpy as np
+    import torch
+    import gated_delta_rule_26_amd as gdr
+
+    dev = torch.device("cuda:0")
+    d = {}
+    for key in ("q", "k", "v", "g", "beta"):
+        t = torch.from_numpy(x[key]).to(dev)
+        d[key] = t.to(torch.bfloat16) if key in ("q", "k", "v") and w.dtype == "bf16" else t
+    rng = np.random.default_rng(12345)
+    d_o = torch.from_numpy(rng.standard_normal((w.B, w.T, w.H, w.Dv), dtype=np.float32)).to(dev)
+    desc = gdr.make_desc(w.B, w.T, w.H, w.Dk, w.Dv, qkv_dtype=d["q"].dtype, o_dtype=torch.float32,
+                         per_channel=w.per_channel, kaczmarz=w.kaczmarz, eps=w.eps)
+    ws = torch.empty(gdr.chunk_bwd_workspace_size(desc), dtype=torch.uint8, device=dev)
+    kw = dict(per_channel=w.per_channel, kaczmarz=w.kaczmarz, eps=w.eps, workspace=ws, need_ds0=False)
+    for _ in range(warmup):
+        gdr.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d_o, **kw)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
+        gdr.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d_o, **kw)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return {"ms_per_step_median": median(per), "ms_per_step": sum(per) / len(per),
+            "workspace_bytes": ws.numel(), "steps": steps}
+
+
 def bench_decode(w, steps, distinct):
     import torch
     import gated_delta_rule_26_amd as gdr
@@ -266,6 +298,8 @@ def main():
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra prefill steps, each after writing 512 MiB to evict the last-level cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=5,
+                    help="timed calls of the backward pass on the prefill workload (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (for rocprofv3 counter scaling)")
     args = ap.parse_args()
@@ -372,6 +406,15 @@ def main():
                          "frac": gbps / PEAK_HBM, "traffic": measured_traffic("decode", "step", "decode"),
                          "alg_bytes_per_launch": dbytes,
                          "avg_launch_ms": dms},
+        }
+
+    if args.backward_steps > 0:
+        bwd = bench_backward(w, pre["inputs"], args.backward_steps, 1)
+        out["backward"] = {
+            "workload": f"{w.name}: gdr_chunk_bwd on the same inputs, standard-normal dL/do, fp32 gradients "
+                        f"(vector fp32 kernels)",
+            **bwd,
+            "train_step_tokens_per_s": w.B * w.T / ((event_step_ms + bwd["ms_per_step"]) * 1e-3),
         }
 
     if args.calibrate_copy:
