@@ -53,6 +53,7 @@ struct BwdWs {
     float *S, *dS;                 // DK x DV: entering state; gradient of the chunk-end state
     float *dA, *dTT, *dG;          // C x C (two), C x GK
     float *dG63;                   // GK: the chunk-end decay's extra gradient (K^ and gam)
+    float *Kt, *Kh, *Qt;           // C x DK each: K~, K^, Q~ (decayed operands, fp32)
 };
 
 template <int DK, int DV, bool PC>
@@ -70,14 +71,18 @@ BwdWs carve_bwd(void *ws, size_t slots) {
     w.dA = p; p += slots * C * C;
     w.dTT = p; p += slots * C * C;
     w.dG = p; p += slots * C * GK;
-    w.dG63 = p;
+    w.dG63 = p; p += slots * GK;
+    w.Kt = p; p += slots * C * DK;
+    w.Kh = p; p += slots * C * DK;
+    w.Qt = p;
     return w;
 }
 
 template <int DK, int DV, bool PC>
 size_t bwd_bytes(size_t slots) {
     constexpr int GK = PC ? DK : 1;
-    return slots * sizeof(float) * ((size_t)5 * C * C + 2 * (size_t)C * GK + GK + C + 2 * (size_t)DK * DV);
+    return slots * sizeof(float) *
+           ((size_t)5 * C * C + 2 * (size_t)C * GK + GK + C + 2 * (size_t)DK * DV + 3 * (size_t)C * DK);
 }
 
 // chunk slot ci -> (b, h, c), token row of its token 0, token count
@@ -103,7 +108,8 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const void *__restri
                                                             int T, int H, int NC, float eps, float scale,
                                                             float *__restrict__ wT, float *__restrict__ wA,
                                                             float *__restrict__ wM, float *__restrict__ wG,
-                                                            float *__restrict__ wB) {
+                                                            float *__restrict__ wB, float *__restrict__ wKt,
+                                                            float *__restrict__ wKh, float *__restrict__ wQt) {
     constexpr int GK = PC ? DK : 1;
     const int ci = blockIdx.x;
     const Slot sl = slot_of(ci, T, H, NC);
@@ -115,15 +121,32 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const void *__restri
     __shared__ __align__(16) float sR[C][C];
     __shared__ float sBeta[C];
 
-    for (int idx = tid; idx < C * DK; idx += kThreads) {
-        const int i = idx / DK, cc = idx % DK;
-        const size_t off = (sl.row0 + (size_t)i * H) * DK + cc;
-        sK[i][cc] = i < n ? load_in<IN_BF16>(k, off) : 0.f;
-        sQ[i][cc] = i < n ? load_in<IN_BF16>(q, off) : 0.f;
-    }
-    for (int idx = tid; idx < C * GK; idx += kThreads) {
-        const int i = idx / GK, cc = idx % GK;
-        sG[i][cc] = i < n ? g[(sl.row0 + (size_t)i * H) * GK + cc] : 0.f;
+    {  // all loads in flight at once, then the LDS stores
+        constexpr int NE = C * DK / kThreads, NG = (C * GK + kThreads - 1) / kThreads;
+        float kr[NE], qr[NE], gr[NG];
+#pragma unroll
+        for (int u = 0; u < NE; ++u) {
+            const int idx = tid + u * kThreads, i = idx / DK, cc = idx % DK;
+            const size_t off = (sl.row0 + (size_t)i * H) * DK + cc;
+            kr[u] = i < n ? load_in<IN_BF16>(k, off) : 0.f;
+            qr[u] = i < n ? load_in<IN_BF16>(q, off) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < NG; ++u) {
+            const int idx = tid + u * kThreads, i = idx / GK, cc = idx % GK;
+            gr[u] = idx < C * GK && i < n ? g[(sl.row0 + (size_t)i * H) * GK + cc] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < NE; ++u) {
+            const int idx = tid + u * kThreads;
+            sK[idx / DK][idx % DK] = kr[u];
+            sQ[idx / DK][idx % DK] = qr[u];
+        }
+#pragma unroll
+        for (int u = 0; u < NG; ++u) {
+            const int idx = tid + u * kThreads;
+            if (idx < C * GK) sG[idx / GK][idx % GK] = gr[u];
+        }
     }
     __syncthreads();
     if (tid < GK) {  // in-chunk inclusive cumulative sum, one channel per thread
@@ -192,6 +215,16 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const void *__restri
     }
     for (int idx = tid; idx < C * GK; idx += kThreads) wG[(size_t)ci * C * GK + idx] = sG[idx / GK][idx % GK];
     if (tid < C) wB[(size_t)ci * C + tid] = sBeta[tid];
+    // the decayed operands: K~ = exp(G) k, K^ = exp(G_63 - G) k, Q~ = scale exp(G) q
+    for (int idx = tid; idx < C * DK; idx += kThreads) {
+        const int i = idx / DK, cc = idx % DK;
+        const float gi = PC ? sG[i][cc] : sG[i][0];
+        const float ge = PC ? sG[C - 1][cc] : sG[C - 1][0];
+        const float ei = __expf(gi);
+        wKt[(size_t)ci * C * DK + idx] = ei * sK[i][cc];
+        wKh[(size_t)ci * C * DK + idx] = __expf(ge - gi) * sK[i][cc];
+        wQt[(size_t)ci * C * DK + idx] = scale * ei * sQ[i][cc];
+    }
 }
 
 // decay factors of token i, channel cc from G in LDS
@@ -201,183 +234,235 @@ __device__ __forceinline__ float gval(const float (*sG)[GK], int i, int cc) {
 }
 
 // ============================================================ forward walk: entering states
+// Each chunk's operands (T, K~, K^, the v slice, beta, gam) are loaded into
+// registers one chunk ahead and moved to LDS at the start of the chunk.
 template <int DK, int DV, bool PC, bool IN_BF16>
-__global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__restrict__ k, const void *__restrict__ v,
-                                                              int T, int H, int NC, const float *__restrict__ wT,
+__global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__restrict__ v, int T, int H, int NC,
+                                                              const float *__restrict__ wT,
                                                               const float *__restrict__ wG,
                                                               const float *__restrict__ wB,
+                                                              const float *__restrict__ wKt,
+                                                              const float *__restrict__ wKh,
                                                               const float *__restrict__ s0, float *__restrict__ wS) {
     constexpr int GK = PC ? DK : 1;
     constexpr int NT = DV / kBV;
+    constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads, NVV = C * kBV / kThreads;
+    constexpr int RPW = kThreads / kBV;  // rows per pass of the workgroup
     const int tile = blockIdx.x % NT, bh = blockIdx.x / NT;
     const int b = bh / H, h = bh % H;
     const int j0 = tile * kBV;
     const int tid = threadIdx.x, jj = tid % kBV, rr = tid / kBV;
     __shared__ float sS[DK][kBV];
-    __shared__ float sK[C][DK + 1];   // K~, then K^
-    __shared__ float sX[C][kBV + 1];
+    __shared__ float sKt[C][DK + 1];
+    __shared__ float sKh[C][DK + 1];
+    __shared__ float sX[C][kBV + 1];  // V, then X
     __shared__ float sE[C][kBV + 1];
     __shared__ float sT[C][C + 1];
-    __shared__ float sG[C][GK];
-    __shared__ float sBeta[C];
+    __shared__ float sBeta[C], sGam[DK];
+
+    float rT[NTT], rKt[NKK], rKh[NKK], rV[NVV], rB = 0.f, rGam = 0.f;
+    auto fetch = [&](int c) {
+        const size_t ci = (size_t)bh * NC + c;
+        const int n = min(C, T - c * C);
+        const size_t row0 = ((size_t)b * T + (size_t)c * C) * H + h;
+#pragma unroll
+        for (int u = 0; u < NTT; ++u) rT[u] = wT[ci * C * C + tid + u * kThreads];
+#pragma unroll
+        for (int u = 0; u < NKK; ++u) {
+            rKt[u] = wKt[ci * C * DK + tid + u * kThreads];
+            rKh[u] = wKh[ci * C * DK + tid + u * kThreads];
+        }
+#pragma unroll
+        for (int u = 0; u < NVV; ++u) {
+            const int idx = tid + u * kThreads, i = idx / kBV, cc = idx % kBV;
+            rV[u] = i < n ? load_in<IN_BF16>(v, (row0 + (size_t)i * H) * DV + j0 + cc) : 0.f;
+        }
+        if (tid < C) rB = wB[ci * C + tid];
+        if (tid < DK) rGam = __expf(wG[ci * C * GK + (size_t)(C - 1) * GK + (PC ? tid : 0)]);
+    };
 
     const size_t sbase = (size_t)bh * DK * DV;
     for (int idx = tid; idx < DK * kBV; idx += kThreads) {
         const int r = idx / kBV, cc = idx % kBV;
         sS[r][cc] = s0 ? s0[sbase + (size_t)r * DV + j0 + cc] : 0.f;
     }
+    if (NC > 0) fetch(0);
     for (int c = 0; c < NC; ++c) {
         const size_t ci = (size_t)bh * NC + c;
-        const int n = min(C, T - c * C);
-        const size_t row0 = ((size_t)b * T + (size_t)c * C) * H + h;
-        __syncthreads();
+        __syncthreads();  // the previous chunk's reads are done
         float *Sg = wS + ci * DK * DV;
         for (int idx = tid; idx < DK * kBV; idx += kThreads) {
             const int r = idx / kBV, cc = idx % kBV;
             Sg[(size_t)r * DV + j0 + cc] = sS[r][cc];
         }
-        for (int idx = tid; idx < C * C; idx += kThreads) sT[idx / C][idx % C] = wT[ci * C * C + idx];
-        for (int idx = tid; idx < C * GK; idx += kThreads) sG[idx / GK][idx % GK] = wG[ci * C * GK + idx];
-        if (tid < C) sBeta[tid] = wB[ci * C + tid];
-        __syncthreads();
-        for (int idx = tid; idx < C * DK; idx += kThreads) {  // K~ = exp(G) k
-            const int i = idx / DK, cc = idx % DK;
-            sK[i][cc] = i < n ? __expf(gval<PC, GK>(sG, i, cc)) * load_in<IN_BF16>(k, (row0 + (size_t)i * H) * DK + cc)
-                              : 0.f;
+#pragma unroll
+        for (int u = 0; u < NTT; ++u) {
+            const int idx = tid + u * kThreads;
+            sT[idx / C][idx % C] = rT[u];
         }
+#pragma unroll
+        for (int u = 0; u < NKK; ++u) {
+            const int idx = tid + u * kThreads;
+            sKt[idx / DK][idx % DK] = rKt[u];
+            sKh[idx / DK][idx % DK] = rKh[u];
+        }
+#pragma unroll
+        for (int u = 0; u < NVV; ++u) {
+            const int idx = tid + u * kThreads;
+            sX[idx / kBV][idx % kBV] = rV[u];
+        }
+        if (tid < C) sBeta[tid] = rB;
+        if (tid < DK) sGam[tid] = rGam;
+        if (c + 1 < NC) fetch(c + 1);
         __syncthreads();
-        for (int i = rr; i < C; i += kThreads / kBV) {  // X = V - K~ S
-            float acc = i < n ? load_in<IN_BF16>(v, (row0 + (size_t)i * H) * DV + j0 + jj) : 0.f;
-            for (int cc = 0; cc < DK; ++cc) acc -= sK[i][cc] * sS[cc][jj];
+        // X = V - K~ S (each thread its own entries of sX)
+        for (int i = rr; i < C; i += RPW) {
+            float acc = sX[i][jj];
+            for (int cc = 0; cc < DK; ++cc) acc -= sKt[i][cc] * sS[cc][jj];
             sX[i][jj] = acc;
         }
         __syncthreads();
-        for (int i = rr; i < C; i += kThreads / kBV) {  // E = T Diag(beta) X
+        for (int i = rr; i < C; i += RPW) {  // E = T Diag(beta) X
             float acc = 0.f;
             for (int m = 0; m <= i; ++m) acc += sT[i][m] * sBeta[m] * sX[m][jj];
             sE[i][jj] = acc;
         }
-        for (int idx = tid; idx < C * DK; idx += kThreads) {  // K^ = exp(G_63 - G) k (sK not read above)
-            const int i = idx / DK, cc = idx % DK;
-            sK[i][cc] = i < n ? __expf(gval<PC, GK>(sG, C - 1, cc) - gval<PC, GK>(sG, i, cc)) *
-                                    load_in<IN_BF16>(k, (row0 + (size_t)i * H) * DK + cc)
-                              : 0.f;
-        }
         __syncthreads();
-        for (int r = rr; r < DK; r += kThreads / kBV) {  // S <- Diag(gam) S + K^' E
-            float acc = __expf(gval<PC, GK>(sG, C - 1, r)) * sS[r][jj];
-            for (int i = 0; i < C; ++i) acc += sK[i][r] * sE[i][jj];
-            sS[r][jj] = acc;
+        // S <- Diag(gam) S + K^' E (each thread its own entries)
+        constexpr int PER = DK / RPW;
+        float acc[PER];
+#pragma unroll
+        for (int p = 0; p < PER; ++p) acc[p] = sGam[rr + p * RPW] * sS[rr + p * RPW][jj];
+        for (int i = 0; i < C; ++i) {
+            const float e = sE[i][jj];
+#pragma unroll
+            for (int p = 0; p < PER; ++p) acc[p] += sKh[i][rr + p * RPW] * e;
         }
+#pragma unroll
+        for (int p = 0; p < PER; ++p) sS[rr + p * RPW][jj] = acc[p];
     }
 }
 
 // ============================================================ reverse walk: dS' per chunk
-template <int DK, int DV, bool PC, bool IN_BF16>
-__global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const void *__restrict__ q, const void *__restrict__ k,
-                                                               const float *__restrict__ dO, int T, int H, int NC,
-                                                               float scale, const float *__restrict__ wT,
+template <int DK, int DV, bool PC>
+__global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__restrict__ dO, int T, int H, int NC,
+                                                               const float *__restrict__ wT,
                                                                const float *__restrict__ wA,
                                                                const float *__restrict__ wG,
                                                                const float *__restrict__ wB,
+                                                               const float *__restrict__ wKt,
+                                                               const float *__restrict__ wKh,
+                                                               const float *__restrict__ wQt,
                                                                const float *__restrict__ ds_final,
                                                                float *__restrict__ wdS, float *__restrict__ ds0) {
     constexpr int GK = PC ? DK : 1;
     constexpr int NT = DV / kBV;
+    constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads, NVV = C * kBV / kThreads;
+    constexpr int RPW = kThreads / kBV;
     const int tile = blockIdx.x % NT, bh = blockIdx.x / NT;
     const int b = bh / H, h = bh % H;
     const int j0 = tile * kBV;
     const int tid = threadIdx.x, jj = tid % kBV, rr = tid / kBV;
     __shared__ float sdS[DK][kBV];
-    __shared__ float sK[C][DK + 1];   // K^, then K~, then Q~
+    __shared__ float sK1[C][DK + 1];  // K^, then Q~
+    __shared__ float sK2[C][DK + 1];  // K~
     __shared__ float sO[C][kBV + 1];  // dO slice
     __shared__ float sdE[C][kBV + 1];
     __shared__ float sdX[C][kBV + 1];
     __shared__ float sT[C][C + 1];
     __shared__ float sA[C][C + 1];
-    __shared__ float sG[C][GK];
-    __shared__ float sBeta[C];
+    __shared__ float sBeta[C], sGam[DK];
+
+    float rT[NTT], rA[NTT], rKt[NKK], rKh[NKK], rQt[NKK], rO[NVV], rB = 0.f, rGam = 0.f;
+    auto fetch = [&](int c) {
+        const size_t ci = (size_t)bh * NC + c;
+        const int n = min(C, T - c * C);
+        const size_t row0 = ((size_t)b * T + (size_t)c * C) * H + h;
+#pragma unroll
+        for (int u = 0; u < NTT; ++u) {
+            rT[u] = wT[ci * C * C + tid + u * kThreads];
+            rA[u] = wA[ci * C * C + tid + u * kThreads];
+        }
+#pragma unroll
+        for (int u = 0; u < NKK; ++u) {
+            rKt[u] = wKt[ci * C * DK + tid + u * kThreads];
+            rKh[u] = wKh[ci * C * DK + tid + u * kThreads];
+            rQt[u] = wQt[ci * C * DK + tid + u * kThreads];
+        }
+#pragma unroll
+        for (int u = 0; u < NVV; ++u) {
+            const int idx = tid + u * kThreads, i = idx / kBV, cc = idx % kBV;
+            rO[u] = i < n ? dO[(row0 + (size_t)i * H) * DV + j0 + cc] : 0.f;
+        }
+        if (tid < C) rB = wB[ci * C + tid];
+        if (tid < DK) rGam = __expf(wG[ci * C * GK + (size_t)(C - 1) * GK + (PC ? tid : 0)]);
+    };
 
     const size_t sbase = (size_t)bh * DK * DV;
     for (int idx = tid; idx < DK * kBV; idx += kThreads) {
         const int r = idx / kBV, cc = idx % kBV;
         sdS[r][cc] = ds_final ? ds_final[sbase + (size_t)r * DV + j0 + cc] : 0.f;
     }
-    constexpr int PER = DK * kBV / kThreads;  // dS entries per thread: rows rr + 8 p, column jj
+    constexpr int PER = DK / RPW;  // dS entries per thread: rows rr + RPW p, column jj
+    if (NC > 0) fetch(NC - 1);
     for (int c = NC - 1; c >= 0; --c) {
         const size_t ci = (size_t)bh * NC + c;
-        const int n = min(C, T - c * C);
-        const size_t row0 = ((size_t)b * T + (size_t)c * C) * H + h;
         __syncthreads();
         float *dSg = wdS + ci * DK * DV;
         for (int idx = tid; idx < DK * kBV; idx += kThreads) {
             const int r = idx / kBV, cc = idx % kBV;
             dSg[(size_t)r * DV + j0 + cc] = sdS[r][cc];
         }
-        for (int idx = tid; idx < C * C; idx += kThreads) {
-            sT[idx / C][idx % C] = wT[ci * C * C + idx];
-            sA[idx / C][idx % C] = wA[ci * C * C + idx];
+#pragma unroll
+        for (int u = 0; u < NTT; ++u) {
+            const int idx = tid + u * kThreads;
+            sT[idx / C][idx % C] = rT[u];
+            sA[idx / C][idx % C] = rA[u];
         }
-        for (int idx = tid; idx < C * GK; idx += kThreads) sG[idx / GK][idx % GK] = wG[ci * C * GK + idx];
-        if (tid < C) sBeta[tid] = wB[ci * C + tid];
-        for (int idx = tid; idx < C * kBV; idx += kThreads) {
-            const int i = idx / kBV, cc = idx % kBV;
-            sO[i][cc] = i < n ? dO[(row0 + (size_t)i * H) * DV + j0 + cc] : 0.f;
+#pragma unroll
+        for (int u = 0; u < NKK; ++u) {
+            const int idx = tid + u * kThreads;
+            sK1[idx / DK][idx % DK] = rKh[u];
+            sK2[idx / DK][idx % DK] = rKt[u];
         }
+#pragma unroll
+        for (int u = 0; u < NVV; ++u) {
+            const int idx = tid + u * kThreads;
+            sO[idx / kBV][idx % kBV] = rO[u];
+        }
+        if (tid < C) sBeta[tid] = rB;
+        if (tid < DK) sGam[tid] = rGam;
         __syncthreads();
-        for (int idx = tid; idx < C * DK; idx += kThreads) {  // K^
-            const int i = idx / DK, cc = idx % DK;
-            sK[i][cc] = i < n ? __expf(gval<PC, GK>(sG, C - 1, cc) - gval<PC, GK>(sG, i, cc)) *
-                                    load_in<IN_BF16>(k, (row0 + (size_t)i * H) * DK + cc)
-                              : 0.f;
-        }
-        __syncthreads();
-        for (int i = rr; i < C; i += kThreads / kBV) {  // dE = A' dO + K^ dS'
+        for (int i = rr; i < C; i += RPW) {  // dE = A' dO + K^ dS'
             float acc = 0.f;
             for (int m = i; m < C; ++m) acc += sA[m][i] * sO[m][jj];
-            for (int cc = 0; cc < DK; ++cc) acc += sK[i][cc] * sdS[cc][jj];
+            for (int cc = 0; cc < DK; ++cc) acc += sK1[i][cc] * sdS[cc][jj];
             sdE[i][jj] = acc;
         }
         __syncthreads();
-        for (int i = rr; i < C; i += kThreads / kBV) {  // dX = Diag(beta) T' dE
+        for (int i = rr; i < C; i += RPW) {  // dX = Diag(beta) T' dE
             float acc = 0.f;
             for (int m = i; m < C; ++m) acc += sT[m][i] * sdE[m][jj];
             sdX[i][jj] = sBeta[i] * acc;
         }
-        // dS = Diag(gam) dS' - K~' dX + Q~' dO, each thread its PER entries
+#pragma unroll
+        for (int u = 0; u < NKK; ++u) {  // K^ is no longer read: Q~ in its place
+            const int idx = tid + u * kThreads;
+            sK1[idx / DK][idx % DK] = rQt[u];
+        }
+        if (c > 0) fetch(c - 1);
+        __syncthreads();
+        // dS = Diag(gam) dS' - K~' dX + Q~' dO (each thread its own entries)
         float acc[PER];
 #pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int r = rr + p * (kThreads / kBV);
-            acc[p] = __expf(gval<PC, GK>(sG, C - 1, r)) * sdS[r][jj];
-        }
-        __syncthreads();  // sdX complete; sK (K^) no longer read
-        for (int idx = tid; idx < C * DK; idx += kThreads) {  // K~
-            const int i = idx / DK, cc = idx % DK;
-            sK[i][cc] = i < n ? __expf(gval<PC, GK>(sG, i, cc)) * load_in<IN_BF16>(k, (row0 + (size_t)i * H) * DK + cc)
-                              : 0.f;
-        }
-        __syncthreads();
+        for (int p = 0; p < PER; ++p) acc[p] = sGam[rr + p * RPW] * sdS[rr + p * RPW][jj];
         for (int i = 0; i < C; ++i) {
-            const float x = sdX[i][jj];
+            const float x = sdX[i][jj], o = sO[i][jj];
 #pragma unroll
-            for (int p = 0; p < PER; ++p) acc[p] -= sK[i][rr + p * (kThreads / kBV)] * x;
-        }
-        __syncthreads();
-        for (int idx = tid; idx < C * DK; idx += kThreads) {  // Q~
-            const int i = idx / DK, cc = idx % DK;
-            sK[i][cc] = i < n ? scale * __expf(gval<PC, GK>(sG, i, cc)) *
-                                    load_in<IN_BF16>(q, (row0 + (size_t)i * H) * DK + cc)
-                              : 0.f;
-        }
-        __syncthreads();
-        for (int i = 0; i < C; ++i) {
-            const float o = sO[i][jj];
-#pragma unroll
-            for (int p = 0; p < PER; ++p) acc[p] += sK[i][rr + p * (kThreads / kBV)] * o;
+            for (int p = 0; p < PER; ++p) acc[p] += sK1[i][rr + p * RPW] * o - sK2[i][rr + p * RPW] * x;
         }
 #pragma unroll
-        for (int p = 0; p < PER; ++p) sdS[rr + p * (kThreads / kBV)][jj] = acc[p];
+        for (int p = 0; p < PER; ++p) sdS[rr + p * RPW][jj] = acc[p];
     }
     __syncthreads();
     if (ds0) {
@@ -396,10 +481,13 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v, const float *__restrict__ dO,
     int T, int H, int NC, float scale, const float *__restrict__ wT, const float *__restrict__ wA,
     const float *__restrict__ wG, const float *__restrict__ wB, const float *__restrict__ wS,
-    const float *__restrict__ wdS, float *__restrict__ wdA, float *__restrict__ wdTT, float *__restrict__ wdG,
+    const float *__restrict__ wdS, const float *__restrict__ wKt, const float *__restrict__ wKh,
+    const float *__restrict__ wQt, float *__restrict__ wdA, float *__restrict__ wdTT, float *__restrict__ wdG,
     float *__restrict__ wdG63, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv) {
     constexpr int GK = PC ? DK : 1;
     constexpr int CPT = DK / 4;
+    constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads;
+    constexpr int NSS = DK * kBS / kThreads, NVS = C * kBS / kThreads;
     const int ci = blockIdx.x;
     const Slot sl = slot_of(ci, T, H, NC);
     const int n = sl.n;
@@ -422,18 +510,34 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
     const float *Gc = wG + (size_t)ci * C * GK;
     auto gget = [&](int r, int cc) { return Gc[r * GK + (PC ? cc : 0)]; };
 
-    for (int idx = tid; idx < C * C; idx += kThreads) {
-        sT[idx / C][idx % C] = wT[(size_t)ci * C * C + idx];
-        sA[idx / C][idx % C] = wA[(size_t)ci * C * C + idx];
+    {  // T, A, K~, K^: all loads in flight, then the LDS stores
+        float rT[NTT], rA[NTT], rKt[NKK], rKh[NKK];
+#pragma unroll
+        for (int u = 0; u < NTT; ++u) {
+            rT[u] = wT[(size_t)ci * C * C + tid + u * kThreads];
+            rA[u] = wA[(size_t)ci * C * C + tid + u * kThreads];
+        }
+#pragma unroll
+        for (int u = 0; u < NKK; ++u) {
+            rKt[u] = wKt[(size_t)ci * C * DK + tid + u * kThreads];
+            rKh[u] = wKh[(size_t)ci * C * DK + tid + u * kThreads];
+        }
+        if (tid < C) sBeta[tid] = wB[(size_t)ci * C + tid];
+#pragma unroll
+        for (int u = 0; u < NTT; ++u) {
+            const int idx = tid + u * kThreads;
+            sT[idx / C][idx % C] = rT[u];
+            sA[idx / C][idx % C] = rA[u];
+        }
+#pragma unroll
+        for (int u = 0; u < NKK; ++u) {
+            const int idx = tid + u * kThreads;
+            sKt[idx / DK][idx % DK] = rKt[u];
+            sKh[idx / DK][idx % DK] = rKh[u];
+        }
     }
-    if (tid < C) sBeta[tid] = wB[(size_t)ci * C + tid];
-    for (int idx = tid; idx < C * DK; idx += kThreads) {
-        const int r = idx / DK, cc = idx % DK;
-        const float kv = r < n ? load_in<IN_BF16>(k, (sl.row0 + (size_t)r * H) * DK + cc) : 0.f;
-        const float gi = gget(r, cc);
-        sKt[r][cc] = __expf(gi) * kv;
-        sKh[r][cc] = __expf(gget(C - 1, cc) - gi) * kv;
-    }
+    (void)k;
+    (void)q;
 
     float dQt[CPT], dKt[CPT], dKh[CPT], dAa[16], dTa[16];
 #pragma unroll
@@ -445,19 +549,39 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
     const float *Sg = wS + (size_t)ci * DK * DV;
     const float *dSg = wdS + (size_t)ci * DK * DV;
     const int oi = tid / 4, oj = (tid % 4) * 4;  // C x kBS products: row oi, columns oj .. oj+3
+    // the slice's S, dS', v and dO, loaded into registers one slice ahead
+    float rS[NSS], rdS[NSS], rV[NVS], rO[NVS];
+    auto fetch = [&](int j0) {
+#pragma unroll
+        for (int u = 0; u < NSS; ++u) {
+            const int idx = tid + u * kThreads, r = idx / kBS, cc = idx % kBS;
+            rS[u] = Sg[(size_t)r * DV + j0 + cc];
+            rdS[u] = dSg[(size_t)r * DV + j0 + cc];
+        }
+#pragma unroll
+        for (int u = 0; u < NVS; ++u) {
+            const int idx = tid + u * kThreads, r = idx / kBS, cc = idx % kBS;
+            const size_t row = sl.row0 + (size_t)r * H;
+            rV[u] = r < n ? load_in<IN_BF16>(v, row * DV + j0 + cc) : 0.f;
+            rO[u] = r < n ? dO[row * DV + j0 + cc] : 0.f;
+        }
+    };
+    fetch(0);
     for (int j0 = 0; j0 < DV; j0 += kBS) {
         __syncthreads();  // the previous slice is no longer read
-        for (int idx = tid; idx < DK * kBS; idx += kThreads) {
-            const int r = idx / kBS, cc = idx % kBS;
-            sS[r][cc] = Sg[(size_t)r * DV + j0 + cc];
-            sdS[r][cc] = dSg[(size_t)r * DV + j0 + cc];
+#pragma unroll
+        for (int u = 0; u < NSS; ++u) {
+            const int idx = tid + u * kThreads;
+            sS[idx / kBS][idx % kBS] = rS[u];
+            sdS[idx / kBS][idx % kBS] = rdS[u];
         }
-        for (int idx = tid; idx < C * kBS; idx += kThreads) {
-            const int r = idx / kBS, cc = idx % kBS;
-            const size_t row = sl.row0 + (size_t)r * H;
-            sX[r][cc] = r < n ? load_in<IN_BF16>(v, row * DV + j0 + cc) : 0.f;
-            sO[r][cc] = r < n ? dO[row * DV + j0 + cc] : 0.f;
+#pragma unroll
+        for (int u = 0; u < NVS; ++u) {
+            const int idx = tid + u * kThreads;
+            sX[idx / kBS][idx % kBS] = rV[u];
+            sO[idx / kBS][idx % kBS] = rO[u];
         }
+        if (j0 + kBS < DV) fetch(j0 + kBS);
         __syncthreads();
         {  // X = V - K~ S;  dE = A' dO + K^ dS'
             float x[4], de[4];
@@ -550,7 +674,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
         const int cc = cb + u;
         const float gi = gget(i, cc);
         const float ei = __expf(gi);
-        const float qt = valid ? scale * ei * load_in<IN_BF16>(q, rowi * DK + cc) : 0.f;
+        const float qt = wQt[((size_t)ci * C + i) * DK + cc];  // Q~ (zero past the end)
         const float kt = sKt[i][cc], kh = sKh[i][cc];
         if (valid) {
             dq[rowi * DK + cc] = scale * ei * dQt[u];
@@ -616,15 +740,37 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_b_kernel(
     float(*sY)[C + 1] = reinterpret_cast<float(*)[C + 1]>(smem + 2 * C * (C + 1));   // T' dT, then M
     const float *Tg = wT + (size_t)ci * C * C;
     const float *dAg = wdA + (size_t)ci * C * C, *dTg = wdTT + (size_t)ci * C * C;
-    for (int idx = tid; idx < C * C; idx += kThreads) {
-        const int r = idx / C, cc = idx % C;
-        sT[r][cc] = Tg[idx];
-        sD[r][cc] = cc <= r ? dAg[idx] : 0.f;
-        sX[r][cc] = cc <= r ? dTg[idx] : 0.f;  // dT''
-    }
-    for (int idx = tid; idx < C * GK; idx += kThreads) {
-        sG[idx / GK][idx % GK] = wG[(size_t)ci * C * GK + idx];
-        sdG[idx / GK][idx % GK] = wdG[(size_t)ci * C * GK + idx];
+    {  // all loads in flight, then the LDS stores
+        constexpr int NTT = C * C / kThreads, NG = (C * GK + kThreads - 1) / kThreads;
+        float rT[NTT], rD[NTT], rX[NTT], rG[NG], rdG[NG];
+#pragma unroll
+        for (int u = 0; u < NTT; ++u) {
+            const int idx = tid + u * kThreads;
+            rT[u] = Tg[idx];
+            rD[u] = dAg[idx];
+            rX[u] = dTg[idx];
+        }
+#pragma unroll
+        for (int u = 0; u < NG; ++u) {
+            const int idx = tid + u * kThreads;
+            rG[u] = idx < C * GK ? wG[(size_t)ci * C * GK + idx] : 0.f;
+            rdG[u] = idx < C * GK ? wdG[(size_t)ci * C * GK + idx] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < NTT; ++u) {
+            const int idx = tid + u * kThreads, r = idx / C, cc = idx % C;
+            sT[r][cc] = rT[u];
+            sD[r][cc] = cc <= r ? rD[u] : 0.f;
+            sX[r][cc] = cc <= r ? rX[u] : 0.f;  // dT''
+        }
+#pragma unroll
+        for (int u = 0; u < NG; ++u) {
+            const int idx = tid + u * kThreads;
+            if (idx < C * GK) {
+                sG[idx / GK][idx % GK] = rG[u];
+                sdG[idx / GK][idx % GK] = rdG[u];
+            }
+        }
     }
     if (tid < C) sBeta[tid] = wB[(size_t)ci * C + tid];
     __syncthreads();
@@ -687,11 +833,22 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_b_kernel(
     // ---- phase 2: raw k, q in LDS; pair terms per (channel, row group)
     float(*sK)[DK + 1] = reinterpret_cast<float(*)[DK + 1]>(smem);
     float(*sQ)[DK + 1] = reinterpret_cast<float(*)[DK + 1]>(smem + C * (DK + 1));
-    for (int idx = tid; idx < C * DK; idx += kThreads) {
-        const int r = idx / DK, cc = idx % DK;
-        const size_t off = (sl.row0 + (size_t)r * H) * DK + cc;
-        sK[r][cc] = r < n ? load_in<IN_BF16>(k, off) : 0.f;
-        sQ[r][cc] = r < n ? load_in<IN_BF16>(q, off) : 0.f;
+    {
+        constexpr int NKK = C * DK / kThreads;
+        float rk[NKK], rq[NKK];
+#pragma unroll
+        for (int u = 0; u < NKK; ++u) {
+            const int idx = tid + u * kThreads, r = idx / DK, cc = idx % DK;
+            const size_t off = (sl.row0 + (size_t)r * H) * DK + cc;
+            rk[u] = r < n ? load_in<IN_BF16>(k, off) : 0.f;
+            rq[u] = r < n ? load_in<IN_BF16>(q, off) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < NKK; ++u) {
+            const int idx = tid + u * kThreads;
+            sK[idx / DK][idx % DK] = rk[u];
+            sQ[idx / DK][idx % DK] = rq[u];
+        }
     }
     __syncthreads();
     if constexpr (KZ) {  // |k_i|^2
@@ -786,18 +943,18 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
     const unsigned nslot = (unsigned)slots;
     const unsigned nwalk = (unsigned)(a.B * a.H * (DV / kBV));
     hipLaunchKernelGGL((bwd_prep_kernel<DK, PC, KZ, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.q, a.k, a.g,
-                       a.beta, a.T, a.H, a.NC, a.eps, a.scale, w.T, w.A, w.M, w.G, w.beta);
+                       a.beta, a.T, a.H, a.NC, a.eps, a.scale, w.T, w.A, w.M, w.G, w.beta, w.Kt, w.Kh, w.Qt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_states_kernel<DK, DV, PC, IB>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.k, a.v, a.T,
-                       a.H, a.NC, w.T, w.G, w.beta, a.s0, w.S);
+    hipLaunchKernelGGL((bwd_states_kernel<DK, DV, PC, IB>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.v, a.T, a.H,
+                       a.NC, w.T, w.G, w.beta, w.Kt, w.Kh, a.s0, w.S);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dstates_kernel<DK, DV, PC, IB>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.q, a.k,
-                       a.dO, a.T, a.H, a.NC, a.scale, w.T, w.A, w.G, w.beta, a.ds_final, w.dS, a.ds0);
+    hipLaunchKernelGGL((bwd_dstates_kernel<DK, DV, PC>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.dO, a.T, a.H,
+                       a.NC, w.T, w.A, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.ds_final, w.dS, a.ds0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grads_a_kernel<DK, DV, PC, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.q, a.k, a.v,
-                       a.dO, a.T, a.H, a.NC, a.scale, w.T, w.A, w.G, w.beta, w.S, w.dS, w.dA, w.dTT, w.dG, w.dG63,
-                       a.dq, a.dk, a.dv);
+                       a.dO, a.T, a.H, a.NC, a.scale, w.T, w.A, w.G, w.beta, w.S, w.dS, w.Kt, w.Kh, w.Qt, w.dA,
+                       w.dTT, w.dG, w.dG63, a.dq, a.dk, a.dv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grads_b_kernel<DK, PC, KZ, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.q, a.k,
                        a.T, a.H, a.NC, a.eps, a.scale, w.T, w.M, w.G, w.beta, w.dA, w.dTT, w.dG, w.dG63, a.dq, a.dk,
