@@ -36,23 +36,23 @@ _SCALAR = ("gated_delta_rule_26_amd/csrc/chunk_matrix.hip", "gated_delta_rule_26
 _PER_CHANNEL = ("gated_delta_rule_26_amd/csrc/chunk_matrix_pc.hip", "gated_delta_rule_26_amd/csrc/matrix_common.h")
 _DECODE = ("gated_delta_rule_26_amd/csrc/recurrent_step.hip",)
 MEASURED_TRAFFIC = {
-    ("matrix", "state", "gdn_prefill"): (_SCALAR, "d5f304146f06db187036550dee6fa800673a3d151724e9a56f5c6c18f13d2392",
-                                         (148663.5 * 2.0 + 135184.3) * 1024),
-    ("matrix", "intra", "gdn_prefill"): (_SCALAR, "d5f304146f06db187036550dee6fa800673a3d151724e9a56f5c6c18f13d2392",
-                                         (66889.7 * 2.0 + 100352.0) * 1024),
-    ("matrix", "state", "kda_prefill"): (_PER_CHANNEL, "d3ffef5377de234eb23f03126f80e481098c995aa0ee25256dd443a54451cf18",
-                                         (279760.7 * 2.0 + 133120.2) * 1024),
-    ("matrix", "intra", "kda_prefill"): (_PER_CHANNEL, "d3ffef5377de234eb23f03126f80e481098c995aa0ee25256dd443a54451cf18",
-                                         (134559.9 * 2.0 + 493568.0) * 1024),
+    ("matrix", "state", "gdn_prefill"): (_SCALAR, "3816674dbd9be68a2cb4dd8f263a5947df263aeb667c55c2453a7b10aff555c6",
+                                         (148667.8 * 2.0 + 135172.3) * 1024),
+    ("matrix", "intra", "gdn_prefill"): (_SCALAR, "3816674dbd9be68a2cb4dd8f263a5947df263aeb667c55c2453a7b10aff555c6",
+                                         (66886.0 * 2.0 + 100352.0) * 1024),
+    ("matrix", "state", "kda_prefill"): (_PER_CHANNEL, "3823ccb93f5569591bf6f38465c39bdf55c2c4378189e604be4b583daa52f009",
+                                         (279778.8 * 2.0 + 133120.0) * 1024),
+    ("matrix", "intra", "kda_prefill"): (_PER_CHANNEL, "3823ccb93f5569591bf6f38465c39bdf55c2c4378189e604be4b583daa52f009",
+                                         (134573.2 * 2.0 + 493568.1) * 1024),
     # the state phase of the long sequence is three launches: the segment transfer walk, the
     # combine of the entering states and the per-segment walk
-    ("matrix", "state", "kla_prefill"): (_SCALAR, "d5f304146f06db187036550dee6fa800673a3d151724e9a56f5c6c18f13d2392",
-                                         (729216.7 * 2.0 + 8192.0 + 3091.1 * 2.0 + 4096.0
-                                          + 1225589.1 * 2.0 + 1049682.0) * 1024),
-    ("matrix", "intra", "kla_prefill"): (_SCALAR, "d5f304146f06db187036550dee6fa800673a3d151724e9a56f5c6c18f13d2392",
-                                         (656073.2 * 2.0 + 802816.0) * 1024),
-    ("decode", "step", "decode"): (_DECODE, "e7e419c4fce8d18e58aad36eae998f3c36e35efc9c754b1783925800a8b15b99",
-                                   (133011.2 * 2.0 + 264192.0) * 1024),
+    ("matrix", "state", "kla_prefill"): (_SCALAR, "3816674dbd9be68a2cb4dd8f263a5947df263aeb667c55c2453a7b10aff555c6",
+                                         (729217.3 * 2.0 + 8192.0 + 15398.6 * 2.0 + 4096.0
+                                          + 1190262.7 * 2.0 + 1049616.2) * 1024),
+    ("matrix", "intra", "kla_prefill"): (_SCALAR, "3816674dbd9be68a2cb4dd8f263a5947df263aeb667c55c2453a7b10aff555c6",
+                                         (656172.3 * 2.0 + 802816.0) * 1024),
+    ("decode", "step", "decode"): (_DECODE, "d95cdb4ade6f5f5e28c9f763a67dd8d994546380ce9e0a79ea14ec92052d8c69",
+                                   (132967.5 * 2.0 + 264192.0) * 1024),
 }
 
 

@@ -605,41 +605,55 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
 
 // ============================================================ segment combine
 // Entering state of every time segment of a sequence: S_0 = s0 (or zero),
-// S_{p+1} = M_p S_p + N_p, from the chunk maps of the transfer walk.  One
-// workgroup per (sequence, head); thread t forms row t / 8, columns
-// 16 (t % 8) .. +15 of each product in fp32 (M_p from memory, S_p in LDS).
-__global__ __launch_bounds__(1024) void segment_combine_kernel(const float *__restrict__ tr,
-                                                               const float *__restrict__ s0,
-                                                               float *__restrict__ seg_state, int P) {
-    __shared__ float Ss[DK * DV];
-    const int bh = blockIdx.x, t = threadIdx.x;
-    const int i = t >> 3, jb = 16 * (t & 7);
+// S_{p+1} = M_p S_p + N_p, from the chunk maps of the transfer walk.  The
+// columns of S are independent, so one workgroup takes (sequence, head, 16
+// value columns); per step it stages M_p in LDS (rows padded to 129 floats,
+// so the rows a wavefront reads fall in different banks), and thread t forms
+// row t / 2, columns 8 (t % 2) .. +7 of its slice in fp32.
+constexpr int kCombineCols = 16;
+__global__ __launch_bounds__(256) void segment_combine_kernel(const float *__restrict__ tr,
+                                                              const float *__restrict__ s0,
+                                                              float *__restrict__ seg_state, int P) {
+    constexpr int LM = DK + 1, NCS = DV / kCombineCols;
+    __shared__ float Ss[DK][kCombineCols];
+    __shared__ float Ms[DK * LM];
+    const int bh = blockIdx.x / NCS, cs = blockIdx.x % NCS;
+    const int t = threadIdx.x, i = t >> 1, jl = 8 * (t & 1), jb = cs * kCombineCols + jl;
     const size_t mat = (size_t)DK * DV;
     const float *sin = s0 ? s0 + bh * mat : nullptr;
     float *out0 = seg_state + (size_t)bh * P * mat;
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
+    for (int jj = 0; jj < 8; ++jj) {
         const float x = sin ? sin[i * DV + jb + jj] : 0.f;
-        Ss[i * DV + jb + jj] = x;
+        Ss[i][jl + jj] = x;
         out0[i * DV + jb + jj] = x;
     }
     for (int pp = 0; pp + 1 < P; ++pp) {
-        __syncthreads();
         const float *N = tr + ((size_t)(bh * P + pp) * 2 + 0) * mat;
         const float *M = tr + ((size_t)(bh * P + pp) * 2 + 1) * mat;
-        float acc[16];
+        constexpr int PER = DK * DK / 256;  // M entries per thread
+        float mr[PER], acc[8];
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) acc[jj] = N[i * DV + jb + jj];
+        for (int u = 0; u < PER; ++u) mr[u] = M[t + u * 256];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) acc[jj] = N[i * DV + jb + jj];
+        __syncthreads();  // the previous step's reads of Ms and Ss are done
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int idx = t + u * 256;
+            Ms[(idx / DK) * LM + idx % DK] = mr[u];
+        }
+        __syncthreads();
         for (int kk = 0; kk < DK; ++kk) {
-            const float m = M[i * DK + kk];
+            const float m = Ms[i * LM + kk];
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) acc[jj] = fmaf(m, Ss[kk * DV + jb + jj], acc[jj]);
+            for (int jj = 0; jj < 8; ++jj) acc[jj] = fmaf(m, Ss[kk][jl + jj], acc[jj]);
         }
         __syncthreads();
         float *out = seg_state + ((size_t)bh * P + pp + 1) * mat;
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-            Ss[i * DV + jb + jj] = acc[jj];
+        for (int jj = 0; jj < 8; ++jj) {
+            Ss[i][jl + jj] = acc[jj];
             out[i * DV + jb + jj] = acc[jj];
         }
     }
@@ -706,7 +720,8 @@ hipError_t launch_state(const ChunkArgs &a) {
                        SeqTable{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(segment_combine_kernel, dim3((unsigned)BH), dim3(1024), 0, a.stream, tr, a.s0, seg_state, P);
+    hipLaunchKernelGGL(segment_combine_kernel, dim3((unsigned)(BH * (DV / kCombineCols))), dim3(256), 0, a.stream, tr,
+                       a.s0, seg_state, P);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((state_matrix_kernel<OB, false, DELTA>), dim3((unsigned)(BH * P * NS)), dim3(kStateThreads), 0,
                        a.stream, q, k, v, ws, seg_state, a.o, a.s_final, a.T, a.H, a.NC, BH * P, P, seg, a.scale,
