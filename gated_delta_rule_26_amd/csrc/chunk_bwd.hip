@@ -233,9 +233,33 @@ __device__ __forceinline__ float gval(const float (*sG)[GK], int i, int cc) {
     return PC ? sG[i][cc] : sG[i][0];
 }
 
+// ============================================================ fp32 matrix-core tiles
+// v_mfma_f32_16x16x4_f32: lane l (lr = l % 16, lg = l / 16) gives A[lr][lg]
+// and B[lg][lr] of a 16 x 4 by 4 x 16 product and holds D[4 lg + r][lr] in
+// d[r].  A 16 x 16 tile with K = 4 m is m such steps; in step s lane l takes
+// reduction index k = 4 s + lg, so every k is taken once.  fp32 operands, fp32
+// accumulation: the same precision class as the vector-ALU products.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// LDS row strides (floats).  A row-indexed-by-lane read (rows lr, columns
+// lg) is free of bank conflicts at a stride of 2 mod 32, a column-indexed one
+// (rows lg, columns lr) at 16 mod 32; 18 serves both with at most two lanes
+// of a half-wavefront sharing a bank.
+constexpr int kLK = 130;  // C x DK operands read row-wise (K~ in X = V - K~ S, K^ in dE)
+constexpr int kLKT = 144; // C x DK operands read column-wise (K^' , K~', Q~')
+constexpr int kLT = 66;   // C x C read row-wise (T'' in E = T'' X)
+constexpr int kLTT = 80;  // C x C read column-wise (A', T'')
+constexpr int kLB = 48;   // B operands of 32 columns, read column-wise
+constexpr int kLS = 18;   // 16-column slices, read both ways
+
 // ============================================================ forward walk: entering states
-// Each chunk's operands (T, K~, K^, the v slice, beta, gam) are loaded into
-// registers one chunk ahead and moved to LDS at the start of the chunk.
+// One workgroup per (sequence, head, 32 value columns), four wavefronts.  Per
+// chunk: X = V - K~ S (wavefront w: rows 16w..16w+15), E = T'' X with T'' =
+// T Diag(beta), S <- Diag(gam) S + K^' E (wavefront w: state rows 16(w + 4t)..);
+// fp32 matrix-core tiles.  The chunk's operands are loaded into registers one
+// chunk ahead and moved to LDS at the start of the chunk.
 template <int DK, int DV, bool PC, bool IN_BF16>
 __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__restrict__ v, int T, int H, int NC,
                                                               const float *__restrict__ wT,
@@ -246,21 +270,23 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
                                                               const float *__restrict__ s0, float *__restrict__ wS) {
     constexpr int GK = PC ? DK : 1;
     constexpr int NT = DV / kBV;
-    constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads, NVV = C * kBV / kThreads;
-    constexpr int RPW = kThreads / kBV;  // rows per pass of the workgroup
+    constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads;
+    constexpr int SRB = DK / 64;  // state row blocks per wavefront
     const int tile = blockIdx.x % NT, bh = blockIdx.x / NT;
     const int b = bh / H, h = bh % H;
     const int j0 = tile * kBV;
-    const int tid = threadIdx.x, jj = tid % kBV, rr = tid / kBV;
-    __shared__ float sS[DK][kBV];
-    __shared__ float sKt[C][DK + 1];
-    __shared__ float sKh[C][DK + 1];
-    __shared__ float sX[C][kBV + 1];  // V, then X
-    __shared__ float sE[C][kBV + 1];
-    __shared__ float sT[C][C + 1];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    __shared__ float sS[DK * kLB];
+    __shared__ float sKt[C * kLK];
+    __shared__ float sKh[C * kLKT];
+    __shared__ float sT[C * kLT];     // T'' = T Diag(beta)
+    __shared__ float sX[C * kLB];
+    __shared__ float sE[C * kLB];
     __shared__ float sBeta[C], sGam[DK];
 
-    float rT[NTT], rKt[NKK], rKh[NKK], rV[NVV], rB = 0.f, rGam = 0.f;
+    float rT[NTT], rKt[NKK], rKh[NKK], rB = 0.f, rGam = 0.f;
+    f32x4 rV[2];  // the v slice in the layout of this wavefront's X tiles
     auto fetch = [&](int c) {
         const size_t ci = (size_t)bh * NC + c;
         const int n = min(C, T - c * C);
@@ -273,10 +299,12 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
             rKh[u] = wKh[ci * C * DK + tid + u * kThreads];
         }
 #pragma unroll
-        for (int u = 0; u < NVV; ++u) {
-            const int idx = tid + u * kThreads, i = idx / kBV, cc = idx % kBV;
-            rV[u] = i < n ? load_in<IN_BF16>(v, (row0 + (size_t)i * H) * DV + j0 + cc) : 0.f;
-        }
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * w + 4 * lg + r;
+                rV[J][r] = i < n ? load_in<IN_BF16>(v, (row0 + (size_t)i * H) * DV + j0 + 16 * J + lr) : 0.f;
+            }
         if (tid < C) rB = wB[ci * C + tid];
         if (tid < DK) rGam = __expf(wG[ci * C * GK + (size_t)(C - 1) * GK + (PC ? tid : 0)]);
     };
@@ -284,66 +312,86 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
     const size_t sbase = (size_t)bh * DK * DV;
     for (int idx = tid; idx < DK * kBV; idx += kThreads) {
         const int r = idx / kBV, cc = idx % kBV;
-        sS[r][cc] = s0 ? s0[sbase + (size_t)r * DV + j0 + cc] : 0.f;
+        sS[r * kLB + cc] = s0 ? s0[sbase + (size_t)r * DV + j0 + cc] : 0.f;
     }
     if (NC > 0) fetch(0);
     for (int c = 0; c < NC; ++c) {
         const size_t ci = (size_t)bh * NC + c;
-        __syncthreads();  // the previous chunk's reads are done
+        __syncthreads();  // the previous chunk's reads are done; sS holds the entering state
         float *Sg = wS + ci * DK * DV;
         for (int idx = tid; idx < DK * kBV; idx += kThreads) {
             const int r = idx / kBV, cc = idx % kBV;
-            Sg[(size_t)r * DV + j0 + cc] = sS[r][cc];
-        }
-#pragma unroll
-        for (int u = 0; u < NTT; ++u) {
-            const int idx = tid + u * kThreads;
-            sT[idx / C][idx % C] = rT[u];
-        }
-#pragma unroll
-        for (int u = 0; u < NKK; ++u) {
-            const int idx = tid + u * kThreads;
-            sKt[idx / DK][idx % DK] = rKt[u];
-            sKh[idx / DK][idx % DK] = rKh[u];
-        }
-#pragma unroll
-        for (int u = 0; u < NVV; ++u) {
-            const int idx = tid + u * kThreads;
-            sX[idx / kBV][idx % kBV] = rV[u];
+            Sg[(size_t)r * DV + j0 + cc] = sS[r * kLB + cc];
         }
         if (tid < C) sBeta[tid] = rB;
         if (tid < DK) sGam[tid] = rGam;
+#pragma unroll
+        for (int u = 0; u < NKK; ++u) {
+            const int idx = tid + u * kThreads;
+            sKt[(idx / DK) * kLK + idx % DK] = rKt[u];
+            sKh[(idx / DK) * kLKT + idx % DK] = rKh[u];
+        }
+        __syncthreads();  // sBeta
+#pragma unroll
+        for (int u = 0; u < NTT; ++u) {
+            const int idx = tid + u * kThreads, i = idx / C, m = idx % C;
+            sT[i * kLT + m] = rT[u] * sBeta[m];
+        }
+        f32x4 x[2] = {rV[0], rV[1]};
         if (c + 1 < NC) fetch(c + 1);
-        __syncthreads();
-        // X = V - K~ S (each thread its own entries of sX)
-        for (int i = rr; i < C; i += RPW) {
-            float acc = sX[i][jj];
-            for (int cc = 0; cc < DK; ++cc) acc -= sKt[i][cc] * sS[cc][jj];
-            sX[i][jj] = acc;
-        }
-        __syncthreads();
-        for (int i = rr; i < C; i += RPW) {  // E = T Diag(beta) X
-            float acc = 0.f;
-            for (int m = 0; m <= i; ++m) acc += sT[i][m] * sBeta[m] * sX[m][jj];
-            sE[i][jj] = acc;
-        }
-        __syncthreads();
-        // S <- Diag(gam) S + K^' E (each thread its own entries)
-        constexpr int PER = DK / RPW;
-        float acc[PER];
+        // X = V - K~ S (rows 16w ..)
+        for (int kk = 0; kk < DK; kk += 4) {
+            const float a = -sKt[(16 * w + lr) * kLK + kk + lg];
 #pragma unroll
-        for (int p = 0; p < PER; ++p) acc[p] = sGam[rr + p * RPW] * sS[rr + p * RPW][jj];
-        for (int i = 0; i < C; ++i) {
-            const float e = sE[i][jj];
-#pragma unroll
-            for (int p = 0; p < PER; ++p) acc[p] += sKh[i][rr + p * RPW] * e;
+            for (int J = 0; J < 2; ++J) x[J] = mfma4(a, sS[(kk + lg) * kLB + 16 * J + lr], x[J]);
         }
 #pragma unroll
-        for (int p = 0; p < PER; ++p) sS[rr + p * RPW][jj] = acc[p];
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sX[(16 * w + 4 * lg + r) * kLB + 16 * J + lr] = x[J][r];
+        __syncthreads();  // X, T''
+        f32x4 e[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        for (int kk = 0; kk < 16 * (w + 1); kk += 4) {  // T'' is lower triangular
+            const float a = sT[(16 * w + lr) * kLT + kk + lg];
+#pragma unroll
+            for (int J = 0; J < 2; ++J) e[J] = mfma4(a, sX[(kk + lg) * kLB + 16 * J + lr], e[J]);
+        }
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sE[(16 * w + 4 * lg + r) * kLB + 16 * J + lr] = e[J][r];
+        __syncthreads();  // E
+        // S <- Diag(gam) S + K^' E (this wavefront's state rows; nobody else reads them now)
+#pragma unroll
+        for (int t = 0; t < SRB; ++t) {
+            const int I = w + 4 * t;
+            f32x4 acc[2];
+#pragma unroll
+            for (int J = 0; J < 2; ++J)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * I + 4 * lg + r;
+                    acc[J][r] = sGam[row] * sS[row * kLB + 16 * J + lr];
+                }
+            for (int kk = 0; kk < C; kk += 4) {
+                const float a = sKh[(kk + lg) * kLKT + 16 * I + lr];
+#pragma unroll
+                for (int J = 0; J < 2; ++J) acc[J] = mfma4(a, sE[(kk + lg) * kLB + 16 * J + lr], acc[J]);
+            }
+#pragma unroll
+            for (int J = 0; J < 2; ++J)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sS[(16 * I + 4 * lg + r) * kLB + 16 * J + lr] = acc[J][r];
+        }
     }
 }
 
 // ============================================================ reverse walk: dS' per chunk
+// One workgroup per (sequence, head, 32 value columns), chunks in reverse.
+// Per chunk: dE = A' dO + K^ dS' and dX = transpose(T'') dE (wavefront w:
+// rows 16w..), dS = Diag(gam) dS' + Q~' dO - K~' dX (wavefront w: state rows
+// 16(w + 4t)..).  One LDS buffer holds K^ (row-wise reads), then Q~, then K~
+// (column-wise).
 template <int DK, int DV, bool PC>
 __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__restrict__ dO, int T, int H, int NC,
                                                                const float *__restrict__ wT,
@@ -358,23 +406,22 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
     constexpr int GK = PC ? DK : 1;
     constexpr int NT = DV / kBV;
     constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads, NVV = C * kBV / kThreads;
-    constexpr int RPW = kThreads / kBV;
+    constexpr int SRB = DK / 64;
     const int tile = blockIdx.x % NT, bh = blockIdx.x / NT;
     const int b = bh / H, h = bh % H;
     const int j0 = tile * kBV;
-    const int tid = threadIdx.x, jj = tid % kBV, rr = tid / kBV;
-    __shared__ float sdS[DK][kBV];
-    __shared__ float sK1[C][DK + 1];  // K^, then Q~
-    __shared__ float sK2[C][DK + 1];  // K~
-    __shared__ float sO[C][kBV + 1];  // dO slice
-    __shared__ float sdE[C][kBV + 1];
-    __shared__ float sdX[C][kBV + 1];
-    __shared__ float sT[C][C + 1];
-    __shared__ float sA[C][C + 1];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    __shared__ float sdS[DK * kLB];
+    __shared__ float sK[C * kLKT];   // K^ (stride kLK), then Q~, then K~ (stride kLKT)
+    __shared__ float sA[C * kLTT];
+    __shared__ float sT[C * kLTT];   // T'' = T Diag(beta)
+    __shared__ float sO[C * kLB];    // dO slice
+    __shared__ float sdE[C * kLB];   // dE, then dX
     __shared__ float sBeta[C], sGam[DK];
 
     float rT[NTT], rA[NTT], rKt[NKK], rKh[NKK], rQt[NKK], rO[NVV], rB = 0.f, rGam = 0.f;
-    auto fetch = [&](int c) {
+    auto fetch_a = [&](int c) {  // operands of dE, dX and the output gradient slice
         const size_t ci = (size_t)bh * NC + c;
         const int n = min(C, T - c * C);
         const size_t row0 = ((size_t)b * T + (size_t)c * C) * H + h;
@@ -384,11 +431,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
             rA[u] = wA[ci * C * C + tid + u * kThreads];
         }
 #pragma unroll
-        for (int u = 0; u < NKK; ++u) {
-            rKt[u] = wKt[ci * C * DK + tid + u * kThreads];
-            rKh[u] = wKh[ci * C * DK + tid + u * kThreads];
-            rQt[u] = wQt[ci * C * DK + tid + u * kThreads];
-        }
+        for (int u = 0; u < NKK; ++u) rKh[u] = wKh[ci * C * DK + tid + u * kThreads];
 #pragma unroll
         for (int u = 0; u < NVV; ++u) {
             const int idx = tid + u * kThreads, i = idx / kBV, cc = idx % kBV;
@@ -397,120 +440,182 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
         if (tid < C) rB = wB[ci * C + tid];
         if (tid < DK) rGam = __expf(wG[ci * C * GK + (size_t)(C - 1) * GK + (PC ? tid : 0)]);
     };
+    auto fetch_q = [&](int c) {
+#pragma unroll
+        for (int u = 0; u < NKK; ++u) rQt[u] = wQt[((size_t)bh * NC + c) * C * DK + tid + u * kThreads];
+    };
+    auto fetch_k = [&](int c) {
+#pragma unroll
+        for (int u = 0; u < NKK; ++u) rKt[u] = wKt[((size_t)bh * NC + c) * C * DK + tid + u * kThreads];
+    };
 
     const size_t sbase = (size_t)bh * DK * DV;
     for (int idx = tid; idx < DK * kBV; idx += kThreads) {
         const int r = idx / kBV, cc = idx % kBV;
-        sdS[r][cc] = ds_final ? ds_final[sbase + (size_t)r * DV + j0 + cc] : 0.f;
+        sdS[r * kLB + cc] = ds_final ? ds_final[sbase + (size_t)r * DV + j0 + cc] : 0.f;
     }
-    constexpr int PER = DK / RPW;  // dS entries per thread: rows rr + RPW p, column jj
-    if (NC > 0) fetch(NC - 1);
+    if (NC > 0) {
+        fetch_a(NC - 1);
+        fetch_q(NC - 1);
+        fetch_k(NC - 1);
+    }
     for (int c = NC - 1; c >= 0; --c) {
         const size_t ci = (size_t)bh * NC + c;
-        __syncthreads();
+        __syncthreads();  // sdS holds dS' of this chunk; the previous chunk's reads are done
         float *dSg = wdS + ci * DK * DV;
         for (int idx = tid; idx < DK * kBV; idx += kThreads) {
             const int r = idx / kBV, cc = idx % kBV;
-            dSg[(size_t)r * DV + j0 + cc] = sdS[r][cc];
+            dSg[(size_t)r * DV + j0 + cc] = sdS[r * kLB + cc];
         }
+        if (tid < C) sBeta[tid] = rB;
+        if (tid < DK) sGam[tid] = rGam;
 #pragma unroll
         for (int u = 0; u < NTT; ++u) {
             const int idx = tid + u * kThreads;
-            sT[idx / C][idx % C] = rT[u];
-            sA[idx / C][idx % C] = rA[u];
+            sA[(idx / C) * kLTT + idx % C] = rA[u];
         }
 #pragma unroll
         for (int u = 0; u < NKK; ++u) {
             const int idx = tid + u * kThreads;
-            sK1[idx / DK][idx % DK] = rKh[u];
-            sK2[idx / DK][idx % DK] = rKt[u];
+            sK[(idx / DK) * kLK + idx % DK] = rKh[u];
         }
 #pragma unroll
         for (int u = 0; u < NVV; ++u) {
             const int idx = tid + u * kThreads;
-            sO[idx / kBV][idx % kBV] = rO[u];
+            sO[(idx / kBV) * kLB + idx % kBV] = rO[u];
         }
-        if (tid < C) sBeta[tid] = rB;
-        if (tid < DK) sGam[tid] = rGam;
-        __syncthreads();
-        for (int i = rr; i < C; i += RPW) {  // dE = A' dO + K^ dS'
-            float acc = 0.f;
-            for (int m = i; m < C; ++m) acc += sA[m][i] * sO[m][jj];
-            for (int cc = 0; cc < DK; ++cc) acc += sK1[i][cc] * sdS[cc][jj];
-            sdE[i][jj] = acc;
+        __syncthreads();  // sBeta
+#pragma unroll
+        for (int u = 0; u < NTT; ++u) {
+            const int idx = tid + u * kThreads, i = idx / C, m = idx % C;
+            sT[i * kLTT + m] = rT[u] * sBeta[m];
         }
-        __syncthreads();
-        for (int i = rr; i < C; i += RPW) {  // dX = Diag(beta) T' dE
-            float acc = 0.f;
-            for (int m = i; m < C; ++m) acc += sT[m][i] * sdE[m][jj];
-            sdX[i][jj] = sBeta[i] * acc;
+        if (c > 0) fetch_a(c - 1);
+        // dE = A' dO + K^ dS' (rows 16w ..; the transpose of A is zero below the diagonal)
+        f32x4 de[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        for (int kk = 16 * w; kk < C; kk += 4) {
+            const float a = sA[(kk + lg) * kLTT + 16 * w + lr];
+#pragma unroll
+            for (int J = 0; J < 2; ++J) de[J] = mfma4(a, sO[(kk + lg) * kLB + 16 * J + lr], de[J]);
+        }
+        for (int kk = 0; kk < DK; kk += 4) {
+            const float a = sK[(16 * w + lr) * kLK + kk + lg];
+#pragma unroll
+            for (int J = 0; J < 2; ++J) de[J] = mfma4(a, sdS[(kk + lg) * kLB + 16 * J + lr], de[J]);
         }
 #pragma unroll
-        for (int u = 0; u < NKK; ++u) {  // K^ is no longer read: Q~ in its place
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sdE[(16 * w + 4 * lg + r) * kLB + 16 * J + lr] = de[J][r];
+        __syncthreads();  // dE, T''; K^ no longer read
+        // dX = transpose(T'') dE (upper triangular)
+        f32x4 dx[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        for (int kk = 16 * w; kk < C; kk += 4) {
+            const float a = sT[(kk + lg) * kLTT + 16 * w + lr];
+#pragma unroll
+            for (int J = 0; J < 2; ++J) dx[J] = mfma4(a, sdE[(kk + lg) * kLB + 16 * J + lr], dx[J]);
+        }
+#pragma unroll
+        for (int u = 0; u < NKK; ++u) {  // Q~ in K^'s place
             const int idx = tid + u * kThreads;
-            sK1[idx / DK][idx % DK] = rQt[u];
+            sK[(idx / DK) * kLKT + idx % DK] = rQt[u];
         }
-        if (c > 0) fetch(c - 1);
+        if (c > 0) fetch_q(c - 1);
+        __syncthreads();  // every dE read done; Q~ staged
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sdE[(16 * w + 4 * lg + r) * kLB + 16 * J + lr] = dx[J][r];
+        // dS = Diag(gam) dS' + Q~' dO ...
+        f32x4 acc[SRB][2];
+#pragma unroll
+        for (int t = 0; t < SRB; ++t) {
+            const int I = w + 4 * t;
+#pragma unroll
+            for (int J = 0; J < 2; ++J)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * I + 4 * lg + r;
+                    acc[t][J][r] = sGam[row] * sdS[row * kLB + 16 * J + lr];
+                }
+            for (int kk = 0; kk < C; kk += 4) {
+                const float a = sK[(kk + lg) * kLKT + 16 * I + lr];
+#pragma unroll
+                for (int J = 0; J < 2; ++J) acc[t][J] = mfma4(a, sO[(kk + lg) * kLB + 16 * J + lr], acc[t][J]);
+            }
+        }
+        __syncthreads();  // Q~ no longer read; dX visible
+#pragma unroll
+        for (int u = 0; u < NKK; ++u) {  // K~ in its place
+            const int idx = tid + u * kThreads;
+            sK[(idx / DK) * kLKT + idx % DK] = rKt[u];
+        }
+        if (c > 0) fetch_k(c - 1);
         __syncthreads();
-        // dS = Diag(gam) dS' - K~' dX + Q~' dO (each thread its own entries)
-        float acc[PER];
+        // ... - K~' dX
 #pragma unroll
-        for (int p = 0; p < PER; ++p) acc[p] = sGam[rr + p * RPW] * sdS[rr + p * RPW][jj];
-        for (int i = 0; i < C; ++i) {
-            const float x = sdX[i][jj], o = sO[i][jj];
+        for (int t = 0; t < SRB; ++t) {
+            const int I = w + 4 * t;
+            for (int kk = 0; kk < C; kk += 4) {
+                const float a = -sK[(kk + lg) * kLKT + 16 * I + lr];
 #pragma unroll
-            for (int p = 0; p < PER; ++p) acc[p] += sK1[i][rr + p * RPW] * o - sK2[i][rr + p * RPW] * x;
+                for (int J = 0; J < 2; ++J) acc[t][J] = mfma4(a, sdE[(kk + lg) * kLB + 16 * J + lr], acc[t][J]);
+            }
+#pragma unroll
+            for (int J = 0; J < 2; ++J)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sdS[(16 * I + 4 * lg + r) * kLB + 16 * J + lr] = acc[t][J][r];
         }
-#pragma unroll
-        for (int p = 0; p < PER; ++p) sdS[rr + p * RPW][jj] = acc[p];
     }
     __syncthreads();
     if (ds0) {
         for (int idx = tid; idx < DK * kBV; idx += kThreads) {
             const int r = idx / kBV, cc = idx % kBV;
-            ds0[sbase + (size_t)r * DV + j0 + cc] = sdS[r][cc];
+            ds0[sbase + (size_t)r * DV + j0 + cc] = sdS[r * kLB + cc];
         }
     }
 }
 
 // ============================================================ grads A: products over the value axis
-// Thread t owns row i = t / 4 of the C x DK accumulators (channels
-// (t % 4) CPT .. +CPT) and of the C x C accumulators (columns (t % 4) 16 .. +16).
+// One workgroup per chunk, four wavefronts; wavefront w owns rows 16w .. 16w+15
+// of every C-row product.  Over the value axis in slices of 16 columns:
+//   X = V - K~ S,  dE = A' dO + K^ dS',  E = T'' X,  dX = transpose(T'') dE (= dV),
+// and, accumulated over the slices in matrix-core accumulators,
+//   dQ~ += dO S',  dK~ -= dX S',  dK^ += E dS'',  dA += dO E',  dT'' += dE X'.
+// Then the parts of dq, dk, dG through K~, Q~, K^ and gam; dA and dT'' to the
+// workspace.  The slice operands are loaded one slice ahead.
 template <int DK, int DV, bool PC, bool IN_BF16>
 __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
-    const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v, const float *__restrict__ dO,
-    int T, int H, int NC, float scale, const float *__restrict__ wT, const float *__restrict__ wA,
-    const float *__restrict__ wG, const float *__restrict__ wB, const float *__restrict__ wS,
-    const float *__restrict__ wdS, const float *__restrict__ wKt, const float *__restrict__ wKh,
-    const float *__restrict__ wQt, float *__restrict__ wdA, float *__restrict__ wdTT, float *__restrict__ wdG,
-    float *__restrict__ wdG63, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv) {
+    const void *__restrict__ v, const float *__restrict__ dO, int T, int H, int NC, float scale,
+    const float *__restrict__ wT, const float *__restrict__ wA, const float *__restrict__ wG,
+    const float *__restrict__ wB, const float *__restrict__ wS, const float *__restrict__ wdS,
+    const float *__restrict__ wKt, const float *__restrict__ wKh, const float *__restrict__ wQt,
+    float *__restrict__ wdA, float *__restrict__ wdTT, float *__restrict__ wdG, float *__restrict__ wdG63,
+    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv) {
     constexpr int GK = PC ? DK : 1;
-    constexpr int CPT = DK / 4;
     constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads;
     constexpr int NSS = DK * kBS / kThreads, NVS = C * kBS / kThreads;
+    constexpr int JK = DK / 16;  // column tiles of the C x DK accumulators
     const int ci = blockIdx.x;
     const Slot sl = slot_of(ci, T, H, NC);
     const int n = sl.n;
-    const int tid = threadIdx.x;
-    const int i = tid >> 2, q4 = tid & 3;
-    const int cb = q4 * CPT;
-    __shared__ float sKt[C][DK + 1];     // K~
-    __shared__ float sKh[C][DK + 1];     // K^
-    __shared__ float sT[C][C + 1];
-    __shared__ float sA[C][C + 1];
-    __shared__ float sS[DK][kBS + 1];    // entering state, this slice
-    __shared__ float sdS[DK][kBS + 1];   // dS', this slice
-    __shared__ float sX[C][kBS + 1];     // V, then X
-    __shared__ float sO[C][kBS + 1];     // dO
-    __shared__ float sE[C][kBS + 1];
-    __shared__ float sdE[C][kBS + 1];
-    __shared__ float sdX[C][kBS + 1];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    __shared__ float sKt[C * kLK];
+    __shared__ float sKh[C * kLK];
+    __shared__ float sT[C * kLT];    // T'' = T Diag(beta)
+    __shared__ float sA[C * kLTT];
+    __shared__ float sS[DK * kLS];   // entering state, this slice
+    __shared__ float sdS[DK * kLS];  // dS', this slice
+    __shared__ float sO[C * kLS];
+    __shared__ float sX[C * kLS];
+    __shared__ float sE[C * kLS];
+    __shared__ float sdE[C * kLS];
+    __shared__ float sdX[C * kLS];
     __shared__ float sBeta[C];
-    // G of token r, channel cc (from the workspace: LDS holds the slices)
-    const float *Gc = wG + (size_t)ci * C * GK;
-    auto gget = [&](int r, int cc) { return Gc[r * GK + (PC ? cc : 0)]; };
+    __shared__ float sH[4][DK];      // per wavefront: column sums of dK^ K^
 
-    {  // T, A, K~, K^: all loads in flight, then the LDS stores
+    {  // T'', A, K~, K^: all loads in flight, then the LDS stores
         float rT[NTT], rA[NTT], rKt[NKK], rKh[NKK];
 #pragma unroll
         for (int u = 0; u < NTT; ++u) {
@@ -524,33 +629,32 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
         }
         if (tid < C) sBeta[tid] = wB[(size_t)ci * C + tid];
 #pragma unroll
-        for (int u = 0; u < NTT; ++u) {
-            const int idx = tid + u * kThreads;
-            sT[idx / C][idx % C] = rT[u];
-            sA[idx / C][idx % C] = rA[u];
-        }
-#pragma unroll
         for (int u = 0; u < NKK; ++u) {
             const int idx = tid + u * kThreads;
-            sKt[idx / DK][idx % DK] = rKt[u];
-            sKh[idx / DK][idx % DK] = rKh[u];
+            sKt[(idx / DK) * kLK + idx % DK] = rKt[u];
+            sKh[(idx / DK) * kLK + idx % DK] = rKh[u];
+        }
+        __syncthreads();  // sBeta
+#pragma unroll
+        for (int u = 0; u < NTT; ++u) {
+            const int idx = tid + u * kThreads, i = idx / C, m = idx % C;
+            sT[i * kLT + m] = rT[u] * sBeta[m];
+            sA[i * kLTT + m] = rA[u];
         }
     }
-    (void)k;
-    (void)q;
 
-    float dQt[CPT], dKt[CPT], dKh[CPT], dAa[16], dTa[16];
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 aQ[JK], aKt[JK], aKh[JK], aA[4], aT[4];
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) dQt[u] = dKt[u] = dKh[u] = 0.f;
+    for (int J = 0; J < JK; ++J) aQ[J] = aKt[J] = aKh[J] = z4;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) dAa[u] = dTa[u] = 0.f;
+    for (int J = 0; J < 4; ++J) aA[J] = aT[J] = z4;
     float dgam = 0.f;  // channel tid (tid < DK)
 
     const float *Sg = wS + (size_t)ci * DK * DV;
     const float *dSg = wdS + (size_t)ci * DK * DV;
-    const int oi = tid / 4, oj = (tid % 4) * 4;  // C x kBS products: row oi, columns oj .. oj+3
-    // the slice's S, dS', v and dO, loaded into registers one slice ahead
-    float rS[NSS], rdS[NSS], rV[NVS], rO[NVS];
+    float rS[NSS], rdS[NSS], rO[NVS];
+    f32x4 rV;  // the v slice in the layout of this wavefront's X tile
     auto fetch = [&](int j0) {
 #pragma unroll
         for (int u = 0; u < NSS; ++u) {
@@ -561,153 +665,153 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
 #pragma unroll
         for (int u = 0; u < NVS; ++u) {
             const int idx = tid + u * kThreads, r = idx / kBS, cc = idx % kBS;
-            const size_t row = sl.row0 + (size_t)r * H;
-            rV[u] = r < n ? load_in<IN_BF16>(v, row * DV + j0 + cc) : 0.f;
-            rO[u] = r < n ? dO[row * DV + j0 + cc] : 0.f;
+            rO[u] = r < n ? dO[(sl.row0 + (size_t)r * H) * DV + j0 + cc] : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * w + 4 * lg + r;
+            rV[r] = i < n ? load_in<IN_BF16>(v, (sl.row0 + (size_t)i * H) * DV + j0 + lr) : 0.f;
         }
     };
     fetch(0);
     for (int j0 = 0; j0 < DV; j0 += kBS) {
-        __syncthreads();  // the previous slice is no longer read
+        __syncthreads();  // the previous slice's reads are done
 #pragma unroll
         for (int u = 0; u < NSS; ++u) {
             const int idx = tid + u * kThreads;
-            sS[idx / kBS][idx % kBS] = rS[u];
-            sdS[idx / kBS][idx % kBS] = rdS[u];
+            sS[(idx / kBS) * kLS + idx % kBS] = rS[u];
+            sdS[(idx / kBS) * kLS + idx % kBS] = rdS[u];
         }
 #pragma unroll
         for (int u = 0; u < NVS; ++u) {
             const int idx = tid + u * kThreads;
-            sX[idx / kBS][idx % kBS] = rV[u];
-            sO[idx / kBS][idx % kBS] = rO[u];
+            sO[(idx / kBS) * kLS + idx % kBS] = rO[u];
         }
+        f32x4 x = rV;
         if (j0 + kBS < DV) fetch(j0 + kBS);
         __syncthreads();
-        {  // X = V - K~ S;  dE = A' dO + K^ dS'
-            float x[4], de[4];
+        // X = V - K~ S;  dE = A' dO + K^ dS'
+        f32x4 de = z4;
+        for (int kk = 0; kk < DK; kk += 4) {
+            x = mfma4(-sKt[(16 * w + lr) * kLK + kk + lg], sS[(kk + lg) * kLS + lr], x);
+            de = mfma4(sKh[(16 * w + lr) * kLK + kk + lg], sdS[(kk + lg) * kLS + lr], de);
+        }
+        for (int kk = 16 * w; kk < C; kk += 4) de = mfma4(sA[(kk + lg) * kLTT + 16 * w + lr], sO[(kk + lg) * kLS + lr], de);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                x[u] = sX[oi][oj + u];
-                de[u] = 0.f;
-            }
-            for (int cc = 0; cc < DK; ++cc) {
-                const float kt = sKt[oi][cc], kh = sKh[oi][cc];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    x[u] -= kt * sS[cc][oj + u];
-                    de[u] += kh * sdS[cc][oj + u];
-                }
-            }
-            for (int m = oi; m < C; ++m) {
-                const float a = sA[m][oi];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) de[u] += a * sO[m][oj + u];
-            }
-            __syncthreads();  // every thread has read V
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                sX[oi][oj + u] = x[u];
-                sdE[oi][oj + u] = de[u];
-            }
+        for (int r = 0; r < 4; ++r) {
+            sX[(16 * w + 4 * lg + r) * kLS + lr] = x[r];
+            sdE[(16 * w + 4 * lg + r) * kLS + lr] = de[r];
         }
         __syncthreads();
-        {  // E = T Diag(beta) X;  dX = Diag(beta) T' dE (= dV)
-            float e[4] = {0.f, 0.f, 0.f, 0.f}, dx[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int m = 0; m <= oi; ++m) {
-                const float t = sT[oi][m] * sBeta[m];
+        // E = T'' X (lower triangular);  dX = transpose(T'') dE (upper triangular)
+        f32x4 e = z4, dx = z4;
+        for (int kk = 0; kk < 16 * (w + 1); kk += 4) e = mfma4(sT[(16 * w + lr) * kLT + kk + lg], sX[(kk + lg) * kLS + lr], e);
+        for (int kk = 16 * w; kk < C; kk += 4) dx = mfma4(sT[(kk + lg) * kLT + 16 * w + lr], sdE[(kk + lg) * kLS + lr], dx);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) e[u] += t * sX[m][oj + u];
-            }
-            for (int m = oi; m < C; ++m) {
-                const float t = sT[m][oi];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) dx[u] += t * sdE[m][oj + u];
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                sE[oi][oj + u] = e[u];
-                sdX[oi][oj + u] = sBeta[oi] * dx[u];
-                if (oi < n) dv[(sl.row0 + (size_t)oi * H) * DV + j0 + oj + u] = sBeta[oi] * dx[u];
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * w + 4 * lg + r;
+            sE[i * kLS + lr] = e[r];
+            sdX[i * kLS + lr] = dx[r];
+            if (i < n) dv[(sl.row0 + (size_t)i * H) * DV + j0 + lr] = dx[r];
         }
         __syncthreads();
-        // accumulators of row i, one value column at a time
-        for (int jj = 0; jj < kBS; ++jj) {
-            const float o = sO[i][jj], x = sdX[i][jj], e = sE[i][jj], de = sdE[i][jj];
+        // accumulators of rows 16w .. (reduction over this slice's 16 value columns)
 #pragma unroll
-            for (int u = 0; u < CPT; ++u) {
-                const float sv = sS[cb + u][jj];
-                dQt[u] += o * sv;
-                dKt[u] -= x * sv;
-                dKh[u] += e * sdS[cb + u][jj];
+        for (int kk = 0; kk < kBS; kk += 4) {
+            const int ka = (16 * w + lr) * kLS + kk + lg;
+            const float ao = sO[ka], ax = -sdX[ka], ae = sE[ka], ade = sdE[ka];
+#pragma unroll
+            for (int J = 0; J < JK; ++J) {
+                const int kb = (16 * J + lr) * kLS + kk + lg;
+                const float bs = sS[kb];
+                aQ[J] = mfma4(ao, bs, aQ[J]);
+                aKt[J] = mfma4(ax, bs, aKt[J]);
+                aKh[J] = mfma4(ae, sdS[kb], aKh[J]);
             }
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int m = q4 * 16 + u;
-                dAa[u] += o * sE[m][jj];
-                dTa[u] += de * sX[m][jj];
+            for (int J = 0; J < 4; ++J) {
+                const int kb = (16 * J + lr) * kLS + kk + lg;
+                aA[J] = mfma4(ao, sE[kb], aA[J]);
+                aT[J] = mfma4(ade, sX[kb], aT[J]);
             }
         }
         if (tid < DK) {
             float s = 0.f;
 #pragma unroll
-            for (int jj = 0; jj < kBS; ++jj) s += sdS[tid][jj] * sS[tid][jj];
+            for (int cc = 0; cc < kBS; ++cc) s += sdS[tid * kLS + cc] * sS[tid * kLS + cc];
             dgam += s;
         }
     }
 
     // dA, dT'' (lower triangle incl. the diagonal) to the workspace
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-        const int m = q4 * 16 + u;
-        wdA[(size_t)ci * C * C + i * C + m] = m <= i ? dAa[u] : 0.f;
-        wdTT[(size_t)ci * C * C + i * C + m] = m <= i ? dTa[u] : 0.f;
-    }
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * w + 4 * lg + r, m = 16 * J + lr;
+            wdA[(size_t)ci * C * C + i * C + m] = m <= i ? aA[J][r] : 0.f;
+            wdTT[(size_t)ci * C * C + i * C + m] = m <= i ? aT[J][r] : 0.f;
+        }
     // parts of dq, dk through Q~, K~, K^ (rows past the end are not written);
     // parts of dG: dK~ K~ + dQ~ Q~ - dK^ K^; for G_63 also sum_i dK^ K^ + dgam gam
-    const bool valid = i < n;
-    const size_t rowi = sl.row0 + (size_t)i * H;
-    float gpart = 0.f;  // scalar decay: this thread's share of the sum over channels
-    float hh[CPT];      // dK^ K^ of row i, channels cb ..
+    const float *Gc = wG + (size_t)ci * C * GK;
+    float rowpart[4] = {0.f, 0.f, 0.f, 0.f};  // scalar decay: sums over this lane's channels
+    float colh[JK];                           // per channel 16J + lr: sum over this lane's rows of dK^ K^
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-        const int cc = cb + u;
-        const float gi = gget(i, cc);
-        const float ei = __expf(gi);
-        const float qt = wQt[((size_t)ci * C + i) * DK + cc];  // Q~ (zero past the end)
-        const float kt = sKt[i][cc], kh = sKh[i][cc];
-        if (valid) {
-            dq[rowi * DK + cc] = scale * ei * dQt[u];
-            dk[rowi * DK + cc] = ei * dKt[u] + __expf(gget(C - 1, cc) - gi) * dKh[u];
+    for (int J = 0; J < JK; ++J) {
+        colh[J] = 0.f;
+        const int ch = 16 * J + lr;
+        const float ge = Gc[(C - 1) * GK + (PC ? ch : 0)];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * w + 4 * lg + r;
+            const float gi = Gc[i * GK + (PC ? ch : 0)];
+            const float ei = __expf(gi);
+            const float kt = sKt[i * kLK + ch], kh = sKh[i * kLK + ch];
+            const float qt = wQt[((size_t)ci * C + i) * DK + ch];
+            if (i < n) {
+                const size_t off = (sl.row0 + (size_t)i * H) * DK + ch;
+                dq[off] = scale * ei * aQ[J][r];
+                dk[off] = ei * aKt[J][r] + __expf(ge - gi) * aKh[J][r];
+            }
+            const float part = aKt[J][r] * kt + aQ[J][r] * qt - aKh[J][r] * kh;
+            colh[J] += aKh[J][r] * kh;
+            if constexpr (PC) wdG[((size_t)ci * C + i) * GK + ch] = part;
+            else rowpart[r] += part;
         }
-        const float part = dKt[u] * kt + dQt[u] * qt - dKh[u] * kh;
-        hh[u] = dKh[u] * kh;
-        if constexpr (PC) wdG[((size_t)ci * C + i) * GK + cc] = part;
-        else gpart += part;
     }
-    if constexpr (!PC) {  // the four threads of row i are adjacent lanes
-        gpart += __shfl_xor(gpart, 1, 64);
-        gpart += __shfl_xor(gpart, 2, 64);
-        if (q4 == 0) wdG[(size_t)ci * C + i] = gpart;
-    }
-    // the chunk-end decay: per channel, the column sum of dK^ K^ (through LDS,
-    // fixed order) plus dgam gam; summed over channels for scalar decay
-    __syncthreads();  // sKt is no longer read
+    if constexpr (!PC) {  // sum over the 16 lanes of a row group (lr), then one lane writes each row
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) sKt[i][cb + u] = hh[u];
+        for (int r = 0; r < 4; ++r) {
+            float sum = rowpart[r];
+            sum += __shfl_xor(sum, 1, 64);
+            sum += __shfl_xor(sum, 2, 64);
+            sum += __shfl_xor(sum, 4, 64);
+            sum += __shfl_xor(sum, 8, 64);
+            if (lr == 0) wdG[(size_t)ci * C + 16 * w + 4 * lg + r] = sum;
+        }
+    }
+    // the chunk-end decay: per channel the column sum of dK^ K^ (lanes lg, then
+    // wavefronts, in a fixed order) plus dgam gam; summed over channels for scalar decay
+#pragma unroll
+    for (int J = 0; J < JK; ++J) {
+        float sum = colh[J];
+        sum += __shfl_xor(sum, 16, 64);
+        sum += __shfl_xor(sum, 32, 64);
+        if (lg == 0) sH[w][16 * J + lr] = sum;
+    }
     __syncthreads();
     if (tid < DK) {
-        float s = 0.f;
-        for (int r = 0; r < C; ++r) s += sKt[r][tid];
-        sKh[0][tid] = s + dgam * __expf(gget(C - 1, tid));
+        const float ge = Gc[(C - 1) * GK + (PC ? tid : 0)];
+        const float extra = ((sH[0][tid] + sH[1][tid]) + (sH[2][tid] + sH[3][tid])) + dgam * __expf(ge);
+        if constexpr (PC) wdG63[(size_t)ci * GK + tid] = extra;
+        else sH[0][tid] = extra;
     }
-    __syncthreads();
-    if constexpr (PC) {
-        if (tid < DK) wdG63[(size_t)ci * GK + tid] = sKh[0][tid];
-    } else {
+    if constexpr (!PC) {
+        __syncthreads();
         if (tid == 0) {
             float s = 0.f;
-            for (int cc = 0; cc < DK; ++cc) s += sKh[0][cc];
+            for (int cc = 0; cc < DK; ++cc) s += sH[0][cc];
             wdG63[ci] = s;
         }
     }
@@ -952,9 +1056,9 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
     hipLaunchKernelGGL((bwd_dstates_kernel<DK, DV, PC>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.dO, a.T, a.H,
                        a.NC, w.T, w.A, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.ds_final, w.dS, a.ds0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_grads_a_kernel<DK, DV, PC, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.q, a.k, a.v,
-                       a.dO, a.T, a.H, a.NC, a.scale, w.T, w.A, w.G, w.beta, w.S, w.dS, w.Kt, w.Kh, w.Qt, w.dA,
-                       w.dTT, w.dG, w.dG63, a.dq, a.dk, a.dv);
+    hipLaunchKernelGGL((bwd_grads_a_kernel<DK, DV, PC, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.v, a.dO, a.T,
+                       a.H, a.NC, a.scale, w.T, w.A, w.G, w.beta, w.S, w.dS, w.Kt, w.Kh, w.Qt, w.dA, w.dTT, w.dG,
+                       w.dG63, a.dq, a.dk, a.dv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grads_b_kernel<DK, PC, KZ, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.q, a.k,
                        a.T, a.H, a.NC, a.eps, a.scale, w.T, w.M, w.G, w.beta, w.dA, w.dTT, w.dG, w.dG63, a.dq, a.dk,
