@@ -412,7 +412,7 @@ def main():
         bwd = bench_backward(w, pre["inputs"], args.backward_steps, 1)
         out["backward"] = {
             "workload": f"{w.name}: gdr_chunk_bwd on the same inputs, standard-normal dL/do, fp32 gradients "
-                        f"(vector fp32 kernels)",
+                        f"(fp32 arithmetic, matrix-core tiles)",
             **bwd,
             "train_step_tokens_per_s": w.B * w.T / ((event_step_ms + bwd["ms_per_step"]) * 1e-3),
         }

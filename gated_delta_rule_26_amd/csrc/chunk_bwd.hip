@@ -1,4 +1,6 @@
-// Backward pass of the chunked forward pass (training), fp32 vector ALUs.
+// Backward pass of the chunked forward pass (training), fp32 arithmetic: the
+// products on fp32 matrix-core tiles (v_mfma_f32_16x16x4_f32), the rest on the
+// vector ALUs.
 //
 // The pages derive no backward pass (the blog summary on the DeltaNet family
 // calls the chunked mode the training mode, "Pipeline Triton por chunks"), so
@@ -101,6 +103,27 @@ __device__ __forceinline__ Slot slot_of(int ci, int T, int H, int NC) {
     return s;
 }
 
+// ============================================================ fp32 matrix-core tiles
+// v_mfma_f32_16x16x4_f32: lane l (lr = l % 16, lg = l / 16) gives A[lr][lg]
+// and B[lg][lr] of a 16 x 4 by 4 x 16 product and holds D[4 lg + r][lr] in
+// d[r].  A 16 x 16 tile with K = 4 m is m such steps; in step s lane l takes
+// reduction index k = 4 s + lg, so every k is taken once.  fp32 operands, fp32
+// accumulation: the same precision class as the vector-ALU products.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// LDS row strides (floats).  A row-indexed-by-lane read (rows lr, columns
+// lg) is free of bank conflicts at a stride of 2 mod 32, a column-indexed one
+// (rows lg, columns lr) at 16 mod 32; 18 serves both with at most two lanes
+// of a half-wavefront sharing a bank.
+constexpr int kLK = 130;  // C x DK operands read row-wise (K~ in X = V - K~ S, K^ in dE)
+constexpr int kLKT = 144; // C x DK operands read column-wise (K^' , K~', Q~')
+constexpr int kLT = 66;   // C x C read row-wise (T'' in E = T'' X)
+constexpr int kLTT = 80;  // C x C read column-wise (A', T'')
+constexpr int kLB = 48;   // B operands of 32 columns, read column-wise
+constexpr int kLS = 18;   // 16-column slices, read both ways
+
 // ============================================================ prep
 template <int DK, bool PC, bool KZ, bool IN_BF16>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const void *__restrict__ q, const void *__restrict__ k,
@@ -174,21 +197,42 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const void *__restri
     __syncthreads();
 
     float *Mg = wM + (size_t)ci * C * C, *Ag = wA + (size_t)ci * C * C;
-    {  // M (strictly lower), A (lower): thread -> row i, 16 columns
+    if constexpr (!PC) {
+        // scalar decay: K K' and Q K' on fp32 matrix-core tiles, then the one decay factor per
+        // pair; wavefront w takes tiles w, w + 4, w + 8, w + 12 of the list (lower tiles first)
+        const int lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+        for (int t = w; t < 16; t += 4) {
+            // tile t as 4 I + J in nibble t: the lower tiles (J <= I) row by row, then the upper ones
+            const int code = (int)((0xB76321FEDCA98540ull >> (4 * t)) & 15);
+            const int I = code >> 2, J = code & 3;
+            f32x4 mm = {0.f, 0.f, 0.f, 0.f}, aa = mm;
+            if (t < 10) {
+                for (int kk = 0; kk < DK; kk += 4) {
+                    const float kb = sK[16 * J + lr][kk + lg];
+                    mm = mfma4(sK[16 * I + lr][kk + lg], kb, mm);
+                    aa = mfma4(sQ[16 * I + lr][kk + lg], kb, aa);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * I + 4 * lg + r, j = 16 * J + lr;
+                const float pp = j <= i ? __expf(sG[i][0] - sG[j][0]) : 0.f;
+                const float m = j < i ? mm[r] * pp : 0.f;
+                Mg[i * C + j] = m;
+                Ag[i * C + j] = scale * aa[r] * pp;
+                sR[i][j] = sBeta[i] * m;
+            }
+        }
+    } else {  // M (strictly lower), A (lower): thread -> row i, 16 columns
         const int i = tid >> 2, jb = (tid & 3) * 16;
         for (int jj = 0; jj < 16; ++jj) {
             const int j = jb + jj;
             float r = 0.f, a = 0.f;
             if (j <= i) {
                 for (int cc = 0; cc < DK; ++cc) {
-                    const float p = PC ? __expf(sG[i][cc] - sG[j][cc]) : 1.f;
+                    const float p = __expf(sG[i][cc] - sG[j][cc]);
                     r += sK[i][cc] * sK[j][cc] * p;
                     a += sQ[i][cc] * sK[j][cc] * p;
-                }
-                if constexpr (!PC) {
-                    const float p = __expf(sG[i][0] - sG[j][0]);
-                    r *= p;
-                    a *= p;
                 }
             }
             const float m = j < i ? r : 0.f;
@@ -232,27 +276,6 @@ template <bool PC, int GK>
 __device__ __forceinline__ float gval(const float (*sG)[GK], int i, int cc) {
     return PC ? sG[i][cc] : sG[i][0];
 }
-
-// ============================================================ fp32 matrix-core tiles
-// v_mfma_f32_16x16x4_f32: lane l (lr = l % 16, lg = l / 16) gives A[lr][lg]
-// and B[lg][lr] of a 16 x 4 by 4 x 16 product and holds D[4 lg + r][lr] in
-// d[r].  A 16 x 16 tile with K = 4 m is m such steps; in step s lane l takes
-// reduction index k = 4 s + lg, so every k is taken once.  fp32 operands, fp32
-// accumulation: the same precision class as the vector-ALU products.
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-// LDS row strides (floats).  A row-indexed-by-lane read (rows lr, columns
-// lg) is free of bank conflicts at a stride of 2 mod 32, a column-indexed one
-// (rows lg, columns lr) at 16 mod 32; 18 serves both with at most two lanes
-// of a half-wavefront sharing a bank.
-constexpr int kLK = 130;  // C x DK operands read row-wise (K~ in X = V - K~ S, K^ in dE)
-constexpr int kLKT = 144; // C x DK operands read column-wise (K^' , K~', Q~')
-constexpr int kLT = 66;   // C x C read row-wise (T'' in E = T'' X)
-constexpr int kLTT = 80;  // C x C read column-wise (A', T'')
-constexpr int kLB = 48;   // B operands of 32 columns, read column-wise
-constexpr int kLS = 18;   // 16-column slices, read both ways
 
 // ============================================================ forward walk: entering states
 // One workgroup per (sequence, head, 32 value columns), four wavefronts.  Per
@@ -818,32 +841,49 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
 }
 
 // ============================================================ grads B: triangular algebra and pair terms
+// One workgroup per chunk, four wavefronts (wavefront w: rows 16w .. of the
+// C x C and C x DK products, on fp32 matrix-core tiles).  dbeta from dT'';
+// Y = T' dT, dR = -Y T' (strictly lower), dbeta += rowsum(dR o M), dM =
+// Diag(beta) dR.  The pair terms of M and A: for scalar decay P_ij =
+// exp(G_i - G_j) is one factor per pair, so with W1 = dM o P and W2 = scale
+// dA o P they are products, dk += W1 K + W1' K + W2' Q, dq += W2 K, and dG_i
+// = rowsum_i(Z) - colsum_i(Z) with Z = dM o M + dA o A; per-channel decay
+// takes them term by term per key channel.  Then the Kaczmarz step size and
+// the reverse cumulative sum of dG.
 template <int DK, bool PC, bool KZ, bool IN_BF16>
 __global__ __launch_bounds__(kThreads) void bwd_grads_b_kernel(
     const void *__restrict__ q, const void *__restrict__ k, int T, int H, int NC, float eps, float scale,
-    const float *__restrict__ wT, const float *__restrict__ wM, const float *__restrict__ wG,
-    const float *__restrict__ wB, const float *__restrict__ wdA, const float *__restrict__ wdTT,
-    const float *__restrict__ wdG, const float *__restrict__ wdG63, float *__restrict__ dq, float *__restrict__ dk,
-    float *__restrict__ dg, float *__restrict__ dbeta) {
+    const float *__restrict__ wT, const float *__restrict__ wM, const float *__restrict__ wA,
+    const float *__restrict__ wG, const float *__restrict__ wB, const float *__restrict__ wdA,
+    const float *__restrict__ wdTT, const float *__restrict__ wdG, const float *__restrict__ wdG63,
+    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dg, float *__restrict__ dbeta) {
     constexpr int GK = PC ? DK : 1;
-    constexpr int GROUPS = kThreads / DK;      // row groups per channel in the pair terms
+    constexpr int GROUPS = kThreads / DK;      // per-channel pair terms: row groups per channel
     constexpr int RPT = C / GROUPS;            // rows per thread
+    constexpr int LC = C + 1;                  // row stride of the C x C buffers
+    constexpr int LQ = DK + 1;                 // row stride of the C x DK buffers
+    constexpr int R0 = 0, R1 = C * LC, R2 = 2 * C * LC;  // three C x C regions
+    // per-channel decay: k and q over the C x C regions once those are free; scalar decay: W1, W2
+    // in regions 0 and 1, k from region 2 on, then q
+    constexpr int KOFF = PC ? 0 : R2, QOFF = KOFF + C * LQ;
+    constexpr int kSmem = QOFF + C * LQ > 3 * C * LC ? QOFF + C * LQ : 3 * C * LC;
     const int ci = blockIdx.x;
     const Slot sl = slot_of(ci, T, H, NC);
     const int n = sl.n;
-    const int tid = threadIdx.x;
-    // phase 1 buffers (C x C) and phase 2 buffers (C x DK) share the space
-    __shared__ float smem[3 * C * (C + 1) > 2 * C * (DK + 1) ? 3 * C * (C + 1) : 2 * C * (DK + 1)];
-    __shared__ float sD[C][C + 1];      // dA (j <= i) and, in the strict upper part, dM transposed
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    __shared__ float smem[kSmem];
+    __shared__ float sD[C * LC];        // dA (j <= i) and, in the strict upper part, dM transposed
     __shared__ float sG[C][GK];
     __shared__ float sBeta[C], sdBeta[C], sKK[C];
     __shared__ float sdG[C][GK];
 
-    float(*sT)[C + 1] = reinterpret_cast<float(*)[C + 1]>(smem);
-    float(*sX)[C + 1] = reinterpret_cast<float(*)[C + 1]>(smem + C * (C + 1));       // dT, then dR
-    float(*sY)[C + 1] = reinterpret_cast<float(*)[C + 1]>(smem + 2 * C * (C + 1));   // T' dT, then M
+    float *sT = smem + R0;   // T, then (scalar decay) A, then W1
+    float *sX = smem + R1;   // dT'', dT, dR, then (scalar decay) W2
+    float *sY = smem + R2;   // T' dT, then M
     const float *Tg = wT + (size_t)ci * C * C;
     const float *dAg = wdA + (size_t)ci * C * C, *dTg = wdTT + (size_t)ci * C * C;
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
     {  // all loads in flight, then the LDS stores
         constexpr int NTT = C * C / kThreads, NG = (C * GK + kThreads - 1) / kThreads;
         float rT[NTT], rD[NTT], rX[NTT], rG[NG], rdG[NG];
@@ -863,9 +903,9 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_b_kernel(
 #pragma unroll
         for (int u = 0; u < NTT; ++u) {
             const int idx = tid + u * kThreads, r = idx / C, cc = idx % C;
-            sT[r][cc] = rT[u];
-            sD[r][cc] = cc <= r ? rD[u] : 0.f;
-            sX[r][cc] = cc <= r ? rX[u] : 0.f;  // dT''
+            sT[r * LC + cc] = rT[u];
+            sD[r * LC + cc] = cc <= r ? rD[u] : 0.f;
+            sX[r * LC + cc] = cc <= r ? rX[u] : 0.f;  // dT''
         }
 #pragma unroll
         for (int u = 0; u < NG; ++u) {
@@ -883,61 +923,85 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_b_kernel(
     if (tid < C) {
         const int j = tid;
         float s = 0.f;
-        for (int r = j; r < C; ++r) s += sX[r][j] * sT[r][j];
+        for (int r = j; r < C; ++r) s += sX[r * LC + j] * sT[r * LC + j];
         sdBeta[j] = s;
     }
     __syncthreads();
     for (int idx = tid; idx < C * C; idx += kThreads) {
         const int r = idx / C, cc = idx % C;
-        sX[r][cc] *= sBeta[cc];
+        sX[r * LC + cc] *= sBeta[cc];
     }
     __syncthreads();
-    // Y = T' dT:  Y_ab = sum_i T_ia dT_ib
-    for (int idx = tid; idx < C * C; idx += kThreads) {
-        const int a = idx / C, bb = idx % C;
-        float s = 0.f;
-        for (int r = max(a, bb); r < C; ++r) s += sT[r][a] * sX[r][bb];
-        sY[a][bb] = s;
-    }
-    __syncthreads();
-    // dR = -Y T' (strictly lower):  dR_ab = -sum_m Y_am T_bm
-    float dr[C * C / kThreads];
+    {  // Y = T' dT (rows 16w ..)
+        f32x4 y[4] = {z4, z4, z4, z4};
+        for (int kk = 0; kk < C; kk += 4) {
+            const float a = sT[(kk + lg) * LC + 16 * w + lr];
 #pragma unroll
-    for (int u = 0; u < C * C / kThreads; ++u) {
-        const int idx = tid + u * kThreads;
-        const int a = idx / C, bb = idx % C;
-        float s = 0.f;
-        if (bb < a) {
-            for (int m = 0; m <= bb; ++m) s += sY[a][m] * sT[bb][m];
+            for (int J = 0; J < 4; ++J) y[J] = mfma4(a, sX[(kk + lg) * LC + 16 * J + lr], y[J]);
         }
-        dr[u] = -s;
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sY[(16 * w + 4 * lg + r) * LC + 16 * J + lr] = y[J][r];
     }
     __syncthreads();
+    f32x4 d[4] = {z4, z4, z4, z4};  // -dR = Y T' (rows 16w ..)
+    for (int kk = 0; kk < C; kk += 4) {
+        const float a = sY[(16 * w + lr) * LC + kk + lg];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) d[J] = mfma4(a, sT[(16 * J + lr) * LC + kk + lg], d[J]);
+    }
+    __syncthreads();  // Y, T and dT no longer read
     const float *Mg = wM + (size_t)ci * C * C;
 #pragma unroll
-    for (int u = 0; u < C * C / kThreads; ++u) {
-        const int idx = tid + u * kThreads;
-        sX[idx / C][idx % C] = dr[u];
-        sY[idx / C][idx % C] = Mg[idx];
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * w + 4 * lg + r, j = 16 * J + lr;
+            sX[i * LC + j] = j < i ? -d[J][r] : 0.f;  // dR, strictly lower
+        }
+    for (int idx = tid; idx < C * C; idx += kThreads) sY[(idx / C) * LC + idx % C] = Mg[idx];
+    if constexpr (!PC) {  // A for the pair terms of scalar decay, in T's place
+        const float *Ag = wA + (size_t)ci * C * C;
+        for (int idx = tid; idx < C * C; idx += kThreads) sT[(idx / C) * LC + idx % C] = Ag[idx];
     }
     __syncthreads();
     // dbeta_i += sum_{j<i} dR_ij M_ij;  dM_ij = beta_i dR_ij -> sD[j][i] (j < i)
     if (tid < C) {
         const int r = tid;
         float s = 0.f;
-        for (int cc = 0; cc < r; ++cc) s += sX[r][cc] * sY[r][cc];
+        for (int cc = 0; cc < r; ++cc) s += sX[r * LC + cc] * sY[r * LC + cc];
         sdBeta[r] += s;
     }
     for (int idx = tid; idx < C * C; idx += kThreads) {
         const int r = idx / C, cc = idx % C;
-        if (cc < r) sD[cc][r] = sBeta[r] * sX[r][cc];
+        if (cc < r) sD[cc * LC + r] = sBeta[r] * sX[r * LC + cc];
     }
     __syncthreads();
 
-    // ---- phase 2: raw k, q in LDS; pair terms per (channel, row group)
-    float(*sK)[DK + 1] = reinterpret_cast<float(*)[DK + 1]>(smem);
-    float(*sQ)[DK + 1] = reinterpret_cast<float(*)[DK + 1]>(smem + C * (DK + 1));
-    {
+    float(*sK)[LQ] = reinterpret_cast<float(*)[LQ]>(smem + KOFF);
+    float(*sQ)[LQ] = reinterpret_cast<float(*)[LQ]>(smem + QOFF);
+    if constexpr (!PC) {
+        // dG_i = rowsum_i(Z) - colsum_i(Z), Z = dM o M + dA o A (M in sY, A in sT)
+        if (tid < C) {
+            const int r = tid;
+            float s = 0.f;
+            for (int j = 0; j < r; ++j) s += sD[j * LC + r] * sY[r * LC + j];       // dM_rj M_rj
+            for (int j = 0; j <= r; ++j) s += sD[r * LC + j] * sT[r * LC + j];      // dA_rj A_rj
+            for (int i = r + 1; i < C; ++i) s -= sD[r * LC + i] * sY[i * LC + r];   // dM_ir M_ir
+            for (int i = r; i < C; ++i) s -= sD[i * LC + r] * sT[i * LC + r];       // dA_ir A_ir
+            sdG[r][0] += s;
+        }
+        __syncthreads();  // M, A no longer read
+        // W1 = dM o P (region 0), W2 = scale dA o P (region 1), P_ij = exp(G_i - G_j), j <= i
+        for (int idx = tid; idx < C * C; idx += kThreads) {
+            const int i = idx / C, j = idx % C;
+            const float p = j <= i ? __expf(sG[i][0] - sG[j][0]) : 0.f;
+            sT[i * LC + j] = j < i ? sD[j * LC + i] * p : 0.f;
+            sX[i * LC + j] = scale * sD[i * LC + j] * p;  // zero above the diagonal
+        }
+    }
+    {  // raw k, q
         constexpr int NKK = C * DK / kThreads;
         float rk[NKK], rq[NKK];
 #pragma unroll
@@ -963,64 +1027,78 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_b_kernel(
         }
         __syncthreads();
     }
-    const int cch = tid % DK, grp = tid / DK;
-    float pk[RPT], pq[RPT], pg[RPT];
-#pragma unroll
-    for (int u = 0; u < RPT; ++u) {
-        const int r = grp + u * GROUPS;  // rows of this thread (interleaved: the triangle is balanced)
-        const float gi = gval<PC, GK>(sG, r, cch);
-        const float ki = sK[r][cch], qi = sQ[r][cch];
-        float ak = 0.f, aq = 0.f, ag = 0.f;
-        // as the row of M and A: j <= i
-        for (int j = 0; j <= r; ++j) {
-            const float p = __expf(gi - gval<PC, GK>(sG, j, cch));
-            const float kj = sK[j][cch];
-            const float a = j < r ? sD[j][r] : 0.f;  // dM_ij
-            const float bq = scale * sD[r][j];       // scale dA_ij
-            ak += a * kj * p;
-            aq += bq * kj * p;
-            ag += (a * ki + bq * qi) * kj * p;
-        }
-        // as the column of M and A: i >= j (here j = r)
-        for (int i2 = r; i2 < C; ++i2) {
-            const float p = __expf(gval<PC, GK>(sG, i2, cch) - gi);
-            const float a = i2 > r ? sD[r][i2] : 0.f;  // dM_{i2, r}
-            const float bq = scale * sD[i2][r];        // scale dA_{i2, r}
-            const float w = (a * sK[i2][cch] + bq * sQ[i2][cch]) * p;
-            ak += w;
-            ag -= w * ki;
-        }
-        pk[u] = ak;
-        pq[u] = aq;
-        pg[u] = ag;
-    }
-    __syncthreads();  // sK, sQ are read below only at this thread's own entries
-    if constexpr (PC) {  // dG per channel: each thread its own entries
-#pragma unroll
-        for (int u = 0; u < RPT; ++u) sdG[grp + u * GROUPS][cch] += pg[u];
-    }
-    // dq, dk: add the parts written by grads A; the Kaczmarz step size
-#pragma unroll
-    for (int u = 0; u < RPT; ++u) {
-        const int r = grp + u * GROUPS;
-        if (r < n) {
-            const size_t off = (sl.row0 + (size_t)r * H) * DK + cch;
-            float dkv = dk[off] + pk[u];
-            if constexpr (KZ) dkv += -2.f * sBeta[r] * sdBeta[r] / (sKK[r] + eps) * sK[r][cch];
-            dk[off] = dkv;
-            dq[off] += pq[u];
-        }
-    }
     if constexpr (!PC) {
-        // scalar decay: dG_i = sum over channels; pg to LDS (sK space is free now), summed per row
-        __syncthreads();
+        // dk += W1 K + W1' K + W2' Q,  dq += W2 K (rows 16w .., all channels)
+        constexpr int JK = DK / 16;
+        f32x4 pk[JK], pq[JK];
 #pragma unroll
-        for (int u = 0; u < RPT; ++u) sK[grp + u * GROUPS][cch] = pg[u];
-        __syncthreads();
-        if (tid < C) {
-            float s = 0.f;
-            for (int cc = 0; cc < DK; ++cc) s += sK[tid][cc];
-            sdG[tid][0] += s;
+        for (int J = 0; J < JK; ++J) pk[J] = pq[J] = z4;
+        for (int kk = 0; kk < C; kk += 4) {
+            const float w1 = sT[(16 * w + lr) * LC + kk + lg], w1t = sT[(kk + lg) * LC + 16 * w + lr];
+            const float w2 = sX[(16 * w + lr) * LC + kk + lg], w2t = sX[(kk + lg) * LC + 16 * w + lr];
+#pragma unroll
+            for (int J = 0; J < JK; ++J) {
+                const float kb = sK[kk + lg][16 * J + lr], qb = sQ[kk + lg][16 * J + lr];
+                pk[J] = mfma4(w1, kb, pk[J]);
+                pk[J] = mfma4(w1t, kb, pk[J]);
+                pk[J] = mfma4(w2t, qb, pk[J]);
+                pq[J] = mfma4(w2, kb, pq[J]);
+            }
+        }
+#pragma unroll
+        for (int J = 0; J < JK; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * w + 4 * lg + r, ch = 16 * J + lr;
+                if (i < n) {
+                    const size_t off = (sl.row0 + (size_t)i * H) * DK + ch;
+                    float dkv = dk[off] + pk[J][r];
+                    if constexpr (KZ) dkv += -2.f * sBeta[i] * sdBeta[i] / (sKK[i] + eps) * sK[i][ch];
+                    dk[off] = dkv;
+                    dq[off] += pq[J][r];
+                }
+            }
+    } else {
+        const int cch = tid % DK, grp = tid / DK;
+        float pk[RPT], pq[RPT], pg[RPT];
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            const int r = grp + u * GROUPS;  // rows of this thread (interleaved: the triangle is balanced)
+            const float gi = sG[r][cch];
+            const float ki = sK[r][cch], qi = sQ[r][cch];
+            float ak = 0.f, aq = 0.f, ag = 0.f;
+            for (int j = 0; j <= r; ++j) {  // as the row of M and A: j <= i
+                const float p = __expf(gi - sG[j][cch]);
+                const float kj = sK[j][cch];
+                const float a = j < r ? sD[j * LC + r] : 0.f;  // dM_ij
+                const float bq = scale * sD[r * LC + j];       // scale dA_ij
+                ak += a * kj * p;
+                aq += bq * kj * p;
+                ag += (a * ki + bq * qi) * kj * p;
+            }
+            for (int i2 = r; i2 < C; ++i2) {  // as the column of M and A: i >= j (here j = r)
+                const float p = __expf(sG[i2][cch] - gi);
+                const float a = i2 > r ? sD[r * LC + i2] : 0.f;  // dM_{i2, r}
+                const float bq = scale * sD[i2 * LC + r];        // scale dA_{i2, r}
+                const float wv = (a * sK[i2][cch] + bq * sQ[i2][cch]) * p;
+                ak += wv;
+                ag -= wv * ki;
+            }
+            pk[u] = ak;
+            pq[u] = aq;
+            pg[u] = ag;
+        }
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            const int r = grp + u * GROUPS;
+            sdG[r][cch] += pg[u];  // each thread its own entries
+            if (r < n) {
+                const size_t off = (sl.row0 + (size_t)r * H) * DK + cch;
+                float dkv = dk[off] + pk[u];
+                if constexpr (KZ) dkv += -2.f * sBeta[r] * sdBeta[r] / (sKK[r] + eps) * sK[r][cch];
+                dk[off] = dkv;
+                dq[off] += pq[u];
+            }
         }
     }
     __syncthreads();
@@ -1061,8 +1139,8 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
                        w.dG63, a.dq, a.dk, a.dv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grads_b_kernel<DK, PC, KZ, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.q, a.k,
-                       a.T, a.H, a.NC, a.eps, a.scale, w.T, w.M, w.G, w.beta, w.dA, w.dTT, w.dG, w.dG63, a.dq, a.dk,
-                       a.dg, a.dbeta);
+                       a.T, a.H, a.NC, a.eps, a.scale, w.T, w.M, w.A, w.G, w.beta, w.dA, w.dTT, w.dG, w.dG63, a.dq,
+                       a.dk, a.dg, a.dbeta);
     return hipGetLastError();
 }
 
