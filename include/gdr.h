@@ -186,7 +186,7 @@ int gdr_chunk_fwd_varlen(const gdr_desc *desc, const int32_t *cu_seqlens,
  * backward pass (the blog summary, "Pipeline Triton por chunks", calls the
  * chunked mode the training mode); it is reverse-mode differentiation of the
  * chunk algebra of gdr_chunk_fwd, with the chunk-entering states recomputed.
- * fp32 vector kernels; the delta rule only (GDR_DELTA_OFF gives
+ * fp32 arithmetic (products on fp32 matrix-core tiles); the delta rule only (GDR_DELTA_OFF gives
  * GDR_E_UNSUPPORTED); fixed-length batches; desc->algo and desc->o_dtype are
  * ignored.
  *
@@ -201,7 +201,7 @@ int gdr_chunk_fwd_varlen(const gdr_desc *desc, const int32_t *cu_seqlens,
  *   ds0       [B, H, Dk, Dv] fp32 (written), or NULL
  *   workspace at least gdr_chunk_bwd_workspace_size bytes (per chunk and
  *             head: the entering state and its gradient, 2 Dk Dv fp32, and
- *             about 100 KiB of per-chunk matrices)
+ *             about 180 KiB of per-chunk matrices at Dk = 128)
  * Outputs must not overlap inputs, each other or the workspace.  With
  * T == 0 only ds0 is written (= ds_final, or zero).
  */

@@ -262,7 +262,8 @@ def test_varlen_workspace_and_validation():
 
 def test_backward_workspace_and_validation():
     """Per chunk slot: T, A, M, dA, dT'' (64 x 64 fp32 each), G and dG (64 x
-    GK), GK, beta (64), the entering state and its gradient (Dk x Dv each)."""
+    GK), GK, beta (64), the entering state and its gradient (Dk x Dv each),
+    and the decayed K~, K^, Q~ (64 x Dk each)."""
     lib = gdr.load_library()
     n = ctypes.c_size_t(0)
 
@@ -271,8 +272,9 @@ def test_backward_workspace_and_validation():
         return rc, n.value
 
     slots = 2 * 3 * 2
-    assert ws(_desc()) == (0, slots * 4 * (5 * 4096 + 2 * 64 + 1 + 64 + 2 * 128 * 128))
-    assert ws(_desc(per_channel=True)) == (0, slots * 4 * (5 * 4096 + 2 * 64 * 128 + 128 + 64 + 2 * 128 * 128))
+    assert ws(_desc()) == (0, slots * 4 * (5 * 4096 + 2 * 64 + 1 + 64 + 2 * 128 * 128 + 3 * 64 * 128))
+    assert ws(_desc(per_channel=True)) == (0, slots * 4 * (5 * 4096 + 2 * 64 * 128 + 128 + 64 + 2 * 128 * 128
+                                                           + 3 * 64 * 128))
     assert ws(_desc(delta_off=True))[0] == E["GDR_E_UNSUPPORTED"]
     d = _desc()
     wsb = ws(d)[1]
