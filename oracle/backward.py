@@ -30,10 +30,12 @@ def _t(a, requires_grad=True):
     return torch.tensor(np.asarray(a, dtype=np.float64), dtype=torch.float64, requires_grad=requires_grad)
 
 
-def forward_torch(q, k, v, g, beta, s0=None, *, per_channel=False, kaczmarz=False, eps=0.0, scale=1.0):
+def forward_torch(q, k, v, g, beta, s0=None, *, per_channel=False, kaczmarz=False, eps=0.0, scale=1.0,
+                  delta_off=False):
     """The token recurrence in float64 torch ops (differentiable).  Shapes as
     for oracle_fwd: q, k [B,T,H,Dk]; v [B,T,H,Dv]; g [B,T,H] or [B,T,H,Dk];
-    beta [B,T,H] (eta when kaczmarz); s0 [B,H,Dk,Dv] or None."""
+    beta [B,T,H] (eta when kaczmarz; unused with delta_off, the additive write
+    S = S~ + k v^T of the textbook page's update table); s0 [B,H,Dk,Dv] or None."""
     B, T, H, Dk = q.shape
     Dv = v.shape[3]
     S = s0 if s0 is not None else torch.zeros((B, H, Dk, Dv), dtype=torch.float64)
@@ -42,6 +44,10 @@ def forward_torch(q, k, v, g, beta, s0=None, *, per_channel=False, kaczmarz=Fals
         kt, qt, vt = k[:, t], q[:, t], v[:, t]            # [B,H,Dk], [B,H,Dk], [B,H,Dv]
         a = torch.exp(g[:, t])                             # [B,H] or [B,H,Dk]
         S = S * (a[..., :, None] if per_channel else a[..., None, None])   # forget: rows of S
+        if delta_off:
+            S = S + kt[..., :, None] * vt[..., None, :]
+            outs.append(scale * torch.einsum("bhij,bhi->bhj", S, qt))
+            continue
         if kaczmarz:
             bt = beta[:, t] / ((kt * kt).sum(-1) + eps)
         else:
@@ -55,13 +61,15 @@ def forward_torch(q, k, v, g, beta, s0=None, *, per_channel=False, kaczmarz=Fals
 
 
 def oracle_bwd(q, k, v, g, beta, do, *, ds_final=None, s0=None, per_channel=False, kaczmarz=False,
-               eps=0.0, scale=1.0):
+               eps=0.0, scale=1.0, delta_off=False):
     """Returns dict(dq, dk, dv, dg, dbeta, ds0) as float64 numpy arrays
-    (dbeta is d eta when kaczmarz; ds0 is None when s0 is None)."""
-    tq, tk, tv, tg, tb = _t(q), _t(k), _t(v), _t(g), _t(beta)
+    (dbeta is d eta when kaczmarz, None with delta_off; ds0 is None when s0
+    is None)."""
+    tq, tk, tv, tg = _t(q), _t(k), _t(v), _t(g)
+    tb = None if delta_off else _t(beta)
     ts0 = _t(s0)
     o, S = forward_torch(tq, tk, tv, tg, tb, ts0, per_channel=per_channel, kaczmarz=kaczmarz, eps=eps,
-                         scale=scale)
+                         scale=scale, delta_off=delta_off)
     loss = (o * _t(do, False)).sum()
     if ds_final is not None:
         loss = loss + (S * _t(ds_final, False)).sum()

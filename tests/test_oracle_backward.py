@@ -20,7 +20,7 @@ def _inputs(mode, seed=3):
     B, T, H, Dk, Dv = 1, 7, 2, 4, 3
     x = dict(q=_dyadic(rng, (B, T, H, Dk)), k=_dyadic(rng, (B, T, H, Dk), 0.5), v=_dyadic(rng, (B, T, H, Dv)),
              s0=_dyadic(rng, (B, H, Dk, Dv), 0.3))
-    gshape = (B, T, H, Dk) if mode == "kda" else (B, T, H)
+    gshape = (B, T, H, Dk) if mode in ("kda", "gla") else (B, T, H)
     x["g"] = -np.abs(_dyadic(rng, gshape, 0.3)) - 2.0 ** -5
     x["beta"] = np.abs(_dyadic(rng, (B, T, H), 0.4)) + 0.25
     x["do"] = _dyadic(rng, (B, T, H, Dv))
@@ -30,7 +30,9 @@ def _inputs(mode, seed=3):
 
 MODES = {"gdn": dict(per_channel=False, kaczmarz=False),
          "kda": dict(per_channel=True, kaczmarz=False),
-         "kla": dict(per_channel=False, kaczmarz=True, eps=0.125)}
+         "kla": dict(per_channel=False, kaczmarz=True, eps=0.125),
+         "retnet": dict(per_channel=False, delta_off=True),
+         "gla": dict(per_channel=True, delta_off=True)}
 
 
 def _loss(x, m, scale):
@@ -49,6 +51,8 @@ def test_gradients_match_finite_differences_of_the_c_oracle(mode):
     grads = oracle_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], ds_final=x["ds"], s0=x["s0"],
                        scale=scale, **m)
     names = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "beta": "dbeta", "s0": "ds0"}
+    if m.get("delta_off"):
+        del names["beta"]
     for key, gname in names.items():
         fd = np.zeros_like(x[key])
         for idx in np.ndindex(x[key].shape):
