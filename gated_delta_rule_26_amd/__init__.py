@@ -356,13 +356,14 @@ def chunk_bwd_workspace_size(desc: Desc) -> int:
 
 
 def chunk_bwd(q, k, v, g, beta, d_o, *, per_channel: bool = False, kaczmarz: bool = False, eps: float = 0.0,
-              scale: float = 1.0, s0=None, ds_final=None, need_ds0: bool = True, workspace=None, stream=None):
+              scale: float = 1.0, s0=None, ds_final=None, need_ds0: bool = True, workspace=None, stream=None,
+              delta_off: bool = False):
     """Backward pass of ``chunk_fwd`` through ``gdr_chunk_bwd``.
 
     Inputs as for chunk_fwd, plus d_o float32 [B,T,H,Dv] (dL/do) and
     ds_final float32 [B,H,Dk,Dv] or None (dL/ds_final).  Returns a dict of
-    float32 tensors: dq, dk, dv, dg, dbeta (dL/deta with ``kaczmarz``) and
-    ds0 (None unless ``need_ds0``).
+    float32 tensors: dq, dk, dv, dg, dbeta (dL/deta with ``kaczmarz``; None
+    with ``delta_off``) and ds0 (None unless ``need_ds0``).
     """
     lib = load_library()
     dev = q.device
@@ -375,7 +376,10 @@ def chunk_bwd(q, k, v, g, beta, d_o, *, per_channel: bool = False, kaczmarz: boo
     _check_dev("v", v, dev, q.dtype, (B, T, H, Dv))
     gshape = (B, T, H, Dk) if per_channel else (B, T, H)
     _check_dev("g", g, dev, torch.float32, gshape)
-    _check_dev("beta", beta, dev, torch.float32, (B, T, H))
+    if delta_off:
+        beta = None
+    else:
+        _check_dev("beta", beta, dev, torch.float32, (B, T, H))
     _check_dev("d_o", d_o, dev, torch.float32, (B, T, H, Dv))
     if s0 is not None:
         _check_dev("s0", s0, dev, torch.float32, (B, H, Dk, Dv))
@@ -384,10 +388,10 @@ def chunk_bwd(q, k, v, g, beta, d_o, *, per_channel: bool = False, kaczmarz: boo
     f32 = dict(dtype=torch.float32, device=dev)
     out = {"dq": torch.empty((B, T, H, Dk), **f32), "dk": torch.empty((B, T, H, Dk), **f32),
            "dv": torch.empty((B, T, H, Dv), **f32), "dg": torch.empty(gshape, **f32),
-           "dbeta": torch.empty((B, T, H), **f32),
+           "dbeta": None if delta_off else torch.empty((B, T, H), **f32),
            "ds0": torch.empty((B, H, Dk, Dv), **f32) if need_ds0 else None}
     desc = make_desc(B, T, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=torch.float32, per_channel=per_channel,
-                     kaczmarz=kaczmarz, eps=eps, scale=scale)
+                     kaczmarz=kaczmarz, eps=eps, scale=scale, delta_off=delta_off)
     need = chunk_bwd_workspace_size(desc)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

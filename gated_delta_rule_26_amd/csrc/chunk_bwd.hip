@@ -39,6 +39,9 @@
 //    cumulative sum; writes dq, dk, dg and dbeta.
 // Padded rows of a partial last chunk have k = q = v = g = beta = 0 and
 // dO = 0, so they contribute nothing.
+// Without the delta rule (delta = false: S = D S + k v^T) the same kernels run
+// with M = 0, beta = 1 (so T'' = I), X = V (no K~ S, no K~' dX) and no
+// gradient of beta.
 #include "gdr_internal.h"
 
 namespace gdr {
@@ -132,7 +135,8 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const void *__restri
                                                             float *__restrict__ wT, float *__restrict__ wA,
                                                             float *__restrict__ wM, float *__restrict__ wG,
                                                             float *__restrict__ wB, float *__restrict__ wKt,
-                                                            float *__restrict__ wKh, float *__restrict__ wQt) {
+                                                            float *__restrict__ wKh, float *__restrict__ wQt,
+                                                            bool delta) {
     constexpr int GK = PC ? DK : 1;
     const int ci = blockIdx.x;
     const Slot sl = slot_of(ci, T, H, NC);
@@ -182,7 +186,9 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const void *__restri
     if (tid >= kThreads - C) {
         const int i = tid - (kThreads - C);
         float bv = 0.f;
-        if (i < n) {
+        if (i < n && !delta) {
+            bv = 1.f;
+        } else if (i < n) {
             const float given = beta[sl.row0 + (size_t)i * H];
             if constexpr (KZ) {
                 float kk = 0.f;
@@ -217,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const void *__restri
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * I + 4 * lg + r, j = 16 * J + lr;
                 const float pp = j <= i ? __expf(sG[i][0] - sG[j][0]) : 0.f;
-                const float m = j < i ? mm[r] * pp : 0.f;
+                const float m = delta && j < i ? mm[r] * pp : 0.f;
                 Mg[i * C + j] = m;
                 Ag[i * C + j] = scale * aa[r] * pp;
                 sR[i][j] = sBeta[i] * m;
@@ -235,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const void *__restri
                     a += sQ[i][cc] * sK[j][cc] * p;
                 }
             }
-            const float m = j < i ? r : 0.f;
+            const float m = delta && j < i ? r : 0.f;
             Mg[i * C + j] = m;
             Ag[i * C + j] = j <= i ? scale * a : 0.f;
             sR[i][j] = sBeta[i] * m;
@@ -290,7 +296,8 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
                                                               const float *__restrict__ wB,
                                                               const float *__restrict__ wKt,
                                                               const float *__restrict__ wKh,
-                                                              const float *__restrict__ s0, float *__restrict__ wS) {
+                                                              const float *__restrict__ s0, float *__restrict__ wS,
+                                                              bool delta) {
     constexpr int GK = PC ? DK : 1;
     constexpr int NT = DV / kBV;
     constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads;
@@ -362,8 +369,8 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
         }
         f32x4 x[2] = {rV[0], rV[1]};
         if (c + 1 < NC) fetch(c + 1);
-        // X = V - K~ S (rows 16w ..)
-        for (int kk = 0; kk < DK; kk += 4) {
+        // X = V - K~ S (rows 16w ..; X = V without the delta rule)
+        for (int kk = 0; delta && kk < DK; kk += 4) {
             const float a = -sKt[(16 * w + lr) * kLK + kk + lg];
 #pragma unroll
             for (int J = 0; J < 2; ++J) x[J] = mfma4(a, sS[(kk + lg) * kLB + 16 * J + lr], x[J]);
@@ -425,7 +432,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
                                                                const float *__restrict__ wKh,
                                                                const float *__restrict__ wQt,
                                                                const float *__restrict__ ds_final,
-                                                               float *__restrict__ wdS, float *__restrict__ ds0) {
+                                                               float *__restrict__ wdS, float *__restrict__ ds0,
+                                                               bool delta) {
     constexpr int GK = PC ? DK : 1;
     constexpr int NT = DV / kBV;
     constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads, NVV = C * kBV / kThreads;
@@ -575,11 +583,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
         }
         if (c > 0) fetch_k(c - 1);
         __syncthreads();
-        // ... - K~' dX
+        // ... - K~' dX (not without the delta rule: X does not depend on S then)
 #pragma unroll
         for (int t = 0; t < SRB; ++t) {
             const int I = w + 4 * t;
-            for (int kk = 0; kk < C; kk += 4) {
+            for (int kk = 0; delta && kk < C; kk += 4) {
                 const float a = -sK[(kk + lg) * kLKT + 16 * I + lr];
 #pragma unroll
                 for (int J = 0; J < 2; ++J) acc[t][J] = mfma4(a, sdE[(kk + lg) * kLB + 16 * J + lr], acc[t][J]);
@@ -614,7 +622,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
     const float *__restrict__ wB, const float *__restrict__ wS, const float *__restrict__ wdS,
     const float *__restrict__ wKt, const float *__restrict__ wKh, const float *__restrict__ wQt,
     float *__restrict__ wdA, float *__restrict__ wdTT, float *__restrict__ wdG, float *__restrict__ wdG63,
-    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv) {
+    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv, bool delta) {
     constexpr int GK = PC ? DK : 1;
     constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads;
     constexpr int NSS = DK * kBS / kThreads, NVS = C * kBS / kThreads;
@@ -716,7 +724,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
         // X = V - K~ S;  dE = A' dO + K^ dS'
         f32x4 de = z4;
         for (int kk = 0; kk < DK; kk += 4) {
-            x = mfma4(-sKt[(16 * w + lr) * kLK + kk + lg], sS[(kk + lg) * kLS + lr], x);
+            if (delta) x = mfma4(-sKt[(16 * w + lr) * kLK + kk + lg], sS[(kk + lg) * kLS + lr], x);
             de = mfma4(sKh[(16 * w + lr) * kLK + kk + lg], sdS[(kk + lg) * kLS + lr], de);
         }
         for (int kk = 16 * w; kk < C; kk += 4) de = mfma4(sA[(kk + lg) * kLTT + 16 * w + lr], sO[(kk + lg) * kLS + lr], de);
@@ -742,7 +750,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
 #pragma unroll
         for (int kk = 0; kk < kBS; kk += 4) {
             const int ka = (16 * w + lr) * kLS + kk + lg;
-            const float ao = sO[ka], ax = -sdX[ka], ae = sE[ka], ade = sdE[ka];
+            // without the delta rule X does not depend on K~, and T'' (so beta) is fixed
+            const float ao = sO[ka], ax = delta ? -sdX[ka] : 0.f, ae = sE[ka], ade = delta ? sdE[ka] : 0.f;
 #pragma unroll
             for (int J = 0; J < JK; ++J) {
                 const int kb = (16 * J + lr) * kLS + kk + lg;
@@ -1110,7 +1119,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_b_kernel(
             if (r < n) dg[(sl.row0 + (size_t)r * H) * GK + tid] = run;
         }
     }
-    if (tid < C && tid < n) {
+    if (dbeta && tid < C && tid < n) {  // no beta without the delta rule
         float db = sdBeta[tid];
         if constexpr (KZ) db /= (sKK[tid] + eps);
         dbeta[sl.row0 + (size_t)tid * H] = db;
@@ -1125,18 +1134,18 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
     const unsigned nslot = (unsigned)slots;
     const unsigned nwalk = (unsigned)(a.B * a.H * (DV / kBV));
     hipLaunchKernelGGL((bwd_prep_kernel<DK, PC, KZ, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.q, a.k, a.g,
-                       a.beta, a.T, a.H, a.NC, a.eps, a.scale, w.T, w.A, w.M, w.G, w.beta, w.Kt, w.Kh, w.Qt);
+                       a.beta, a.T, a.H, a.NC, a.eps, a.scale, w.T, w.A, w.M, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.delta);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_states_kernel<DK, DV, PC, IB>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.v, a.T, a.H,
-                       a.NC, w.T, w.G, w.beta, w.Kt, w.Kh, a.s0, w.S);
+                       a.NC, w.T, w.G, w.beta, w.Kt, w.Kh, a.s0, w.S, a.delta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dstates_kernel<DK, DV, PC>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.dO, a.T, a.H,
-                       a.NC, w.T, w.A, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.ds_final, w.dS, a.ds0);
+                       a.NC, w.T, w.A, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.ds_final, w.dS, a.ds0, a.delta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grads_a_kernel<DK, DV, PC, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.v, a.dO, a.T,
                        a.H, a.NC, a.scale, w.T, w.A, w.G, w.beta, w.S, w.dS, w.Kt, w.Kh, w.Qt, w.dA, w.dTT, w.dG,
-                       w.dG63, a.dq, a.dk, a.dv);
+                       w.dG63, a.dq, a.dk, a.dv, a.delta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grads_b_kernel<DK, PC, KZ, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.q, a.k,
                        a.T, a.H, a.NC, a.eps, a.scale, w.T, w.M, w.A, w.G, w.beta, w.dA, w.dTT, w.dG, w.dG63, a.dq,

@@ -298,7 +298,6 @@ int gdr_chunk_bwd_workspace_size(const gdr_desc *d, size_t *bytes) {
     Sizes sz;
     const int rc = check_desc(d, false, &sz);
     if (rc != GDR_OK) return rc;
-    if (d->delta_mode != GDR_DELTA_RULE) return GDR_E_UNSUPPORTED;
     const long NC = chunk_count(d, false);
     if ((size_t)d->B * d->H * (size_t)NC >= ((size_t)1 << 31)) return GDR_E_SHAPE;
     *bytes = gdr::chunk_bwd_workspace_bytes(d->B, d->H, (int)NC, d->Dk, d->Dv,
@@ -320,8 +319,11 @@ int gdr_chunk_bwd(const gdr_desc *d, const void *q, const void *k, const void *v
     const bool pc = d->decay_mode == GDR_DECAY_PER_CHANNEL;
     const size_t in_es = d->qkv_dtype == GDR_BF16 ? 2 : 4;
     const bool have_tokens = d->T > 0;
+    const bool delta = d->delta_mode == GDR_DELTA_RULE;
+    if (!delta) beta_or_eta = dbeta = nullptr;  // no beta without the delta rule
     if (have_tokens) {
-        if (!q || !k || !v || !g || !beta_or_eta || !d_o || !dq || !dk || !dv || !dg || !dbeta) return GDR_E_NULL;
+        if (!q || !k || !v || !g || !d_o || !dq || !dk || !dv || !dg) return GDR_E_NULL;
+        if (delta && (!beta_or_eta || !dbeta)) return GDR_E_NULL;
         if (!workspace) return GDR_E_WORKSPACE;
         if (workspace_bytes < need) return GDR_E_WORKSPACE;
         if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d_o, 16) || !aligned(dq, 16) ||
@@ -357,7 +359,8 @@ int gdr_chunk_bwd(const gdr_desc *d, const void *q, const void *k, const void *v
     a.NC = (int)chunk_count(d, false);
     a.qkv_bf16 = d->qkv_dtype == GDR_BF16;
     a.per_channel = pc;
-    a.kaczmarz = d->beta_mode == GDR_BETA_KACZMARZ;
+    a.delta = delta;
+    a.kaczmarz = delta && d->beta_mode == GDR_BETA_KACZMARZ;
     a.eps = a.kaczmarz ? d->eps : 0.f;
     a.scale = d->scale;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta_or_eta; a.s0 = s0; a.dO = d_o; a.ds_final = ds_final;

@@ -79,10 +79,11 @@ hipError_t launch_chunk_matrix(const ChunkArgs &a, int stage);
 size_t chunk_matrix_pc_workspace_bytes(int B, int H, int NC);
 hipError_t launch_chunk_matrix_pc(const ChunkArgs &a, int stage);
 
-// Validated arguments of gdr_chunk_bwd (fixed-length batches, the delta rule).
+// Validated arguments of gdr_chunk_bwd (fixed-length batches).
 struct BwdArgs {
     int B, T, H, Dk, Dv, NC;
     bool qkv_bf16, per_channel, kaczmarz;
+    bool delta;                                  // false: additive write (beta and dbeta are NULL)
     float eps, scale;
     const void *q, *k, *v;
     const float *g, *beta, *s0, *dO, *ds_final;  // s0, ds_final may be NULL (zero)

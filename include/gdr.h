@@ -186,9 +186,9 @@ int gdr_chunk_fwd_varlen(const gdr_desc *desc, const int32_t *cu_seqlens,
  * backward pass (the blog summary, "Pipeline Triton por chunks", calls the
  * chunked mode the training mode); it is reverse-mode differentiation of the
  * chunk algebra of gdr_chunk_fwd, with the chunk-entering states recomputed.
- * fp32 arithmetic (products on fp32 matrix-core tiles); the delta rule only (GDR_DELTA_OFF gives
- * GDR_E_UNSUPPORTED); fixed-length batches; desc->algo and desc->o_dtype are
- * ignored.
+ * fp32 arithmetic (products on fp32 matrix-core tiles); fixed-length
+ * batches; desc->algo and desc->o_dtype are ignored.  With GDR_DELTA_OFF
+ * (the additive write) beta_or_eta and dbeta are ignored and may be NULL.
  *
  *   q, k, v, g, beta_or_eta, s0   as for gdr_chunk_fwd (s0 may be NULL)
  *   d_o       [B, T, H, Dv] fp32, dL/do
@@ -197,7 +197,7 @@ int gdr_chunk_fwd_varlen(const gdr_desc *desc, const int32_t *cu_seqlens,
  *   dv        [B, T, H, Dv] fp32 (written)
  *   dg        shaped as g, fp32 (written)
  *   dbeta     [B, T, H] fp32 (written): dL/dbeta, or dL/deta for the
- *             Kaczmarz step size
+ *             Kaczmarz step size (not written with GDR_DELTA_OFF)
  *   ds0       [B, H, Dk, Dv] fp32 (written), or NULL
  *   workspace at least gdr_chunk_bwd_workspace_size bytes (per chunk and
  *             head: the entering state and its gradient, 2 Dk Dv fp32, and

@@ -275,7 +275,7 @@ def test_backward_workspace_and_validation():
     assert ws(_desc()) == (0, slots * 4 * (5 * 4096 + 2 * 64 + 1 + 64 + 2 * 128 * 128 + 3 * 64 * 128))
     assert ws(_desc(per_channel=True)) == (0, slots * 4 * (5 * 4096 + 2 * 64 * 128 + 128 + 64 + 2 * 128 * 128
                                                            + 3 * 64 * 128))
-    assert ws(_desc(delta_off=True))[0] == E["GDR_E_UNSUPPORTED"]
+    assert ws(_desc(delta_off=True)) == ws(_desc())
     d = _desc()
     wsb = ws(d)[1]
 
@@ -285,8 +285,20 @@ def test_backward_workspace_and_validation():
 
     assert call(q=None) == E["GDR_E_NULL"]
     assert call(b=None) == E["GDR_E_NULL"]
+    assert call(db=None) == E["GDR_E_NULL"]
     assert call(do=None) == E["GDR_E_NULL"]
     assert call(w=None) == E["GDR_E_WORKSPACE"]
     assert call(dq=P(10, 4)) == E["GDR_E_ALIGN"]
     assert call(dk=P(10, 64)) == E["GDR_E_ALIAS"]    # dk inside dq
     assert call(dv=P(3)) == E["GDR_E_ALIAS"]         # dv on top of v
+
+
+def test_backward_without_delta_rule_needs_no_beta():
+    lib = gdr.load_library()
+    d = _desc(delta_off=True)
+    n = ctypes.c_size_t(0)
+    assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    # beta and dbeta NULL pass the pointer checks: the call fails later, on the workspace
+    rc = lib.gdr_chunk_bwd(ctypes.byref(d), P(1), P(2), P(3), P(4), None, None, P(9), None, P(10), P(11), P(12),
+                           P(13), None, None, None, n.value, None)
+    assert rc == E["GDR_E_WORKSPACE"]

@@ -87,3 +87,27 @@ def test_backward_deterministic_and_zero_length():
     r = gdr.chunk_bwd(z["q"], z["k"], z["v"], z["g"], z["beta"], z["do"], s0=z["s0"], ds_final=z["ds"])
     torch.cuda.synchronize()
     assert torch.equal(r["ds0"], d["ds"])
+
+
+@pytest.mark.parametrize("variant", ["linear", "retnet", "gla"])
+@pytest.mark.parametrize("T", [64, 150])
+def test_backward_without_delta_rule(variant, T):
+    """The additive write S = D S + k v^T (linear attention with g = 0,
+    RetNet / Mamba-2, GLA): every gradient but beta's."""
+    pc = variant == "gla"
+    x = random_inputs(6400 + T, 2, T, 2, 128, 128, dtype="bf16", per_channel=pc, with_s0=True)
+    if variant == "linear":
+        x["g"] = np.zeros_like(x["g"])
+    rng = np.random.default_rng(6401)
+    x["do"] = rng.standard_normal((2, T, 2, 128)).astype(np.float32)
+    x["ds"] = rng.standard_normal((2, 2, 128, 128)).astype(np.float32)
+    d = to_dev(x, "bf16")
+    g = gdr.chunk_bwd(d["q"], d["k"], d["v"], d["g"], None, d["do"], s0=d["s0"], ds_final=d["ds"],
+                      per_channel=pc, scale=0.5, delta_off=True)
+    torch.cuda.synchronize()
+    ref = oracle_bwd(x["q"], x["k"], x["v"], x["g"], None, x["do"], ds_final=x["ds"], s0=x["s0"], scale=0.5,
+                     per_channel=pc, delta_off=True)
+    assert g["dbeta"] is None
+    errs = {key: rel(host(g[key]), ref[key]) for key in ("dq", "dk", "dv", "dg", "ds0")}
+    print(f"backward no delta {variant} T={T}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert all(v < TOL_BWD for v in errs.values()), errs
