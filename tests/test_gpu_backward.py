@@ -111,3 +111,30 @@ def test_backward_without_delta_rule(variant, T):
     errs = {key: rel(host(g[key]), ref[key]) for key in ("dq", "dk", "dv", "dg", "ds0")}
     print(f"backward no delta {variant} T={T}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     assert all(v < TOL_BWD for v in errs.values()), errs
+
+
+@pytest.mark.parametrize("name,nheads", [("gdn_prefill", 2), ("kda_prefill", 1)])
+def test_backward_full_workload_sampled(name, nheads):
+    """The backward pass at the full size of a prefill workload (as the
+    benchmark runs it: zero initial state, a standard-normal dL/do), every
+    gradient of sampled (batch, head) pairs against the oracle run on that
+    pair alone."""
+    from gdr_inputs import WORKLOADS, prefill_inputs
+    w = WORKLOADS[name]
+    print(f"backward full workload {name}: inputs", flush=True)
+    x = prefill_inputs(w)
+    d = to_dev(x, w.dtype)
+    rng = np.random.default_rng(12345)
+    do = rng.standard_normal((w.B, w.T, w.H, w.Dv), dtype=np.float32)
+    m = dict(per_channel=w.per_channel, kaczmarz=w.kaczmarz, eps=w.eps)
+    g = gdr.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], torch.from_numpy(do).to(DEV), need_ds0=False, **m)
+    torch.cuda.synchronize()
+    pairs = np.random.default_rng(7).choice(w.B * w.H, nheads, replace=False)
+    for bh in pairs:
+        b, h = divmod(int(bh), w.H)
+        print(f"backward full workload {name}: oracle on (b={b}, h={h})", flush=True)
+        sl = {key: x[key][b:b + 1, :, h:h + 1] for key in ("q", "k", "v", "g", "beta")}
+        ref = oracle_bwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], do[b:b + 1, :, h:h + 1], **m)
+        errs = {key: rel(host(g[key][b:b + 1, :, h:h + 1]), ref[key]) for key in ("dq", "dk", "dv", "dg", "dbeta")}
+        print(f"backward full workload {name} (b={b}, h={h}): " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+        assert all(v < TOL_BWD for v in errs.values()), errs
