@@ -36,23 +36,37 @@ _SCALAR = ("gated_delta_rule_26_amd/csrc/chunk_matrix.hip", "gated_delta_rule_26
 _PER_CHANNEL = ("gated_delta_rule_26_amd/csrc/chunk_matrix_pc.hip", "gated_delta_rule_26_amd/csrc/matrix_common.h")
 _DECODE = ("gated_delta_rule_26_amd/csrc/recurrent_step.hip",)
 MEASURED_TRAFFIC = {
-    ("matrix", "state", "gdn_prefill"): (_SCALAR, "3816674dbd9be68a2cb4dd8f263a5947df263aeb667c55c2453a7b10aff555c6",
-                                         (148667.8 * 2.0 + 135172.3) * 1024),
-    ("matrix", "intra", "gdn_prefill"): (_SCALAR, "3816674dbd9be68a2cb4dd8f263a5947df263aeb667c55c2453a7b10aff555c6",
-                                         (66886.0 * 2.0 + 100352.0) * 1024),
+    ("matrix", "state", "gdn_prefill"): (_SCALAR, "f77615373beab2e05720a4e5c19567d55fd1c3473f3d8c9efe92c8b700ba44cb",
+                                         (148668.5 * 2.0 + 135171.9) * 1024),
+    ("matrix", "intra", "gdn_prefill"): (_SCALAR, "f77615373beab2e05720a4e5c19567d55fd1c3473f3d8c9efe92c8b700ba44cb",
+                                         (66883.1 * 2.0 + 100352.0) * 1024),
     ("matrix", "state", "kda_prefill"): (_PER_CHANNEL, "3823ccb93f5569591bf6f38465c39bdf55c2c4378189e604be4b583daa52f009",
                                          (279778.8 * 2.0 + 133120.0) * 1024),
     ("matrix", "intra", "kda_prefill"): (_PER_CHANNEL, "3823ccb93f5569591bf6f38465c39bdf55c2c4378189e604be4b583daa52f009",
                                          (134573.2 * 2.0 + 493568.1) * 1024),
     # the state phase of the long sequence is three launches: the segment transfer walk, the
     # combine of the entering states and the per-segment walk
-    ("matrix", "state", "kla_prefill"): (_SCALAR, "3816674dbd9be68a2cb4dd8f263a5947df263aeb667c55c2453a7b10aff555c6",
-                                         (729217.3 * 2.0 + 8192.0 + 15398.6 * 2.0 + 4096.0
-                                          + 1190262.7 * 2.0 + 1049616.2) * 1024),
-    ("matrix", "intra", "kla_prefill"): (_SCALAR, "3816674dbd9be68a2cb4dd8f263a5947df263aeb667c55c2453a7b10aff555c6",
-                                         (656172.3 * 2.0 + 802816.0) * 1024),
+    ("matrix", "state", "kla_prefill"): (_SCALAR, "f77615373beab2e05720a4e5c19567d55fd1c3473f3d8c9efe92c8b700ba44cb",
+                                         (730654.2 * 2.0 + 8192.0 + 15398.7 * 2.0 + 4096.0
+                                          + 1190824.8 * 2.0 + 1049621.2) * 1024),
+    ("matrix", "intra", "kla_prefill"): (_SCALAR, "f77615373beab2e05720a4e5c19567d55fd1c3473f3d8c9efe92c8b700ba44cb",
+                                         (656101.7 * 2.0 + 802816.0) * 1024),
     ("decode", "step", "decode"): (_DECODE, "d95cdb4ade6f5f5e28c9f763a67dd8d994546380ce9e0a79ea14ec92052d8c69",
                                    (132967.5 * 2.0 + 264192.0) * 1024),
+}
+
+
+# Matrix-core use of the dominant kernel from rocprofv3 counters: SQ_VALU_MFMA_BUSY_CYCLES over the kernel's
+# duration x 1024 SIMDs x the shader clock from GRBM_GUI_ACTIVE (per XCD), and the MFMA flops it issued
+# (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) per second.  The issued flops count every bf16 hi/lo product, so they
+# exceed the algorithmic flops.  (files, sha, busy fraction, issued TFLOP/s), as for the traffic.
+MEASURED_MFMA = {
+    ("matrix", "state", "gdn_prefill"): (_SCALAR, "f77615373beab2e05720a4e5c19567d55fd1c3473f3d8c9efe92c8b700ba44cb",
+                                         0.192, 454.0),
+    ("matrix", "state", "kda_prefill"): (_PER_CHANNEL, "3823ccb93f5569591bf6f38465c39bdf55c2c4378189e604be4b583daa52f009",
+                                         0.080, 197.4),
+    ("matrix", "state", "kla_prefill"): (_SCALAR, "f77615373beab2e05720a4e5c19567d55fd1c3473f3d8c9efe92c8b700ba44cb",
+                                         0.244, 539.0),   # transfer + combine + walk, by duration
 }
 
 
@@ -63,6 +77,21 @@ def sources_sha(files) -> str:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
+
+
+def measured_mfma(path_kind: str, kernel: str, workload: str):
+    """Counter-measured matrix-core busy fraction and issued TFLOP/s, or None if not measured on the current
+    sources."""
+    entry = MEASURED_MFMA.get((path_kind, kernel, workload))
+    if entry is None:
+        return None
+    files, sha, busy, issued = entry
+    try:
+        if sources_sha(files) != sha:
+            return None
+    except OSError:
+        return None
+    return {"counter_busy_frac": busy, "issued_tflops": issued}
 
 
 def measured_traffic(path_kind: str, kernel: str, workload: str):
@@ -380,7 +409,8 @@ def main():
                      "alg_bytes_per_launch": dom_bytes, "alg_flops_per_launch": dom_flops,
                      "avg_launch_ms": dom_ms,
                      "mfma_view": {"achieved_tflops": mfma_view, "peak_tflops": PEAK_BF16_MFMA,
-                                   "frac": mfma_view / PEAK_BF16_MFMA}},
+                                   "frac": mfma_view / PEAK_BF16_MFMA,
+                                   "counters": measured_mfma(algo, dom, w.name)}},
         "prefill": {"intra_ms": intra_ms, "state_ms": state_ms, "event_step_ms": event_step_ms,
                     "intra_ms_median": median(pre["intra_ms"]), "state_ms_median": median(pre["state_ms"]),
                     "cold_cache": pre["cold"],

@@ -46,6 +46,7 @@
 // product) and the bf16 hi/lo precision scheme are described in
 // matrix_common.h.
 #include <cmath>
+#include <type_traits>
 
 #include "matrix_common.h"
 
@@ -256,6 +257,13 @@ struct alignas(16) StateSmem {
     uint4 X[2][2][kXFrags][64];    // per chain wavefront and chunk parity
     float Ost[2][C * 20];          // per helper: its fp32 output tile, token-major, for 16-byte stores
 };
+// The transfer walk (no outputs, no Q S) needs only the k and v staging and the decays.
+struct alignas(16) TransferSmem {
+    __bf16 K[2][C * LDK];
+    __bf16 V[2][C * LDV];
+    float Gam[3][C];
+    float Gend[2][C];
+};
 
 // Column, in the permuted token-major layout, of the 8-byte half hh (0, 1)
 // of key-channel segment seg (8 channels, 0..15).
@@ -274,14 +282,15 @@ __device__ __forceinline__ int kperm_col(int seg, int hh) {
 //    E = T''(V - Gam K S) into the chunk-end state, [P2] "KDA por chunks",
 //    chunk-end state): slices 0 .. NS-1 walk N (zero start, v), slices NS ..
 //    2NS-1 walk the columns of M (identity start, v = 0); N and M go to
-//    s_out[g][0] and s_out[g][1].  No outputs.
+//    s_out[g][0] and s_out[g][1].  No outputs, so the LDS holds only the
+//    k, v staging and the decays (48 KB) and two workgroups share a unit.
 // DELTA = false: E = V (no K S, no T''), records without T''.
 template <bool OUT_BF16, bool TRANSFER, bool DELTA>
-__global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
+__global__ __launch_bounds__(kStateThreads, TRANSFER ? 2 : 1) void state_matrix_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const char *__restrict__ ws, const float *__restrict__ s0, void *__restrict__ o,
     float *__restrict__ s_out, int T, int H, int NC, int G, int P, int seg, float scale, SeqTable tb) {
-    __shared__ StateSmem sm;
+    __shared__ std::conditional_t<TRANSFER, TransferSmem, StateSmem> sm;
 
     int g, slice;
     state_slot(blockIdx.x, G, TRANSFER ? 2 * NS : NS, g, slice);
@@ -355,7 +364,8 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
                     tln[f] = *reinterpret_cast<const bf16x8 *>(rn + kRecTL + f * kFragBytes + lane * 16);
                 }
             }
-            uint4 *xo = &sm.X[buf][w][0][0];
+            uint4 *xo = nullptr;
+            if constexpr (!TRANSFER) xo = &sm.X[buf][w][0][0];
             // S as the B operand over key channels (hi, lo)
             bf16x8 SH[4], SL[4];
 #pragma unroll
@@ -366,7 +376,8 @@ __global__ __launch_bounds__(kStateThreads) void state_matrix_kernel(
             f32x4 P[4] = {zero4, zero4, zero4, zero4};
             f32x4 QS[4] = {zero4, zero4, zero4, zero4};
             const __bf16 *sK = sm.K[buf];
-            const __bf16 *sQ = sm.Q[buf];
+            const __bf16 *sQ = nullptr;
+            if constexpr (!TRANSFER) sQ = sm.Q[buf];
             bf16x8 ka[2][4], qa[2][4];
 #pragma unroll
             for (int M = 0; M < 4; ++M) {
@@ -673,9 +684,12 @@ hipError_t launch_intra(const ChunkArgs &a) {
 // Time segments of the walk.  Each walk is one workgroup per (group, 32 value
 // columns) and the walk is latency-bound, so a few long sequences leave most
 // compute units idle; splitting each sequence into P segments costs a
-// transfer walk of twice the columns plus a walk per segment, in
-// (ceil(2 P BH NS / CUs) + ceil(P BH NS / CUs)) / P of the single walk's
-// time.  P is the smallest power of two that minimises that (planned for
+// transfer walk of twice the columns plus a walk per segment.  The transfer
+// walk keeps no outputs and fits two workgroups per compute unit, and a round
+// of those takes about as long as a round of walks with outputs (one per
+// unit), so the cost is (ceil(2 P BH NS / 2 CUs) + ceil(P BH NS / CUs)) / P
+// of the single walk's time.  P is the smallest power of two that minimises
+// that (planned for
 // 256 compute units so that the workspace size does not depend on the
 // device), with at least 32 chunks per segment.
 int walk_segments(int BH, int NC) {
@@ -684,7 +698,8 @@ int walk_segments(int BH, int NC) {
     double best_cost = std::ceil(BH * NS / kPlanCUs);
     for (int P = 2; P <= 16; P *= 2) {
         if (NC < 32 * P) break;
-        const double cost = (std::ceil(2.0 * P * BH * NS / kPlanCUs) + std::ceil(1.0 * P * BH * NS / kPlanCUs)) / P;
+        const double cost =
+            (std::ceil(2.0 * P * BH * NS / (2 * kPlanCUs)) + std::ceil(1.0 * P * BH * NS / kPlanCUs)) / P;
         if (cost < best_cost - 1e-9) {
             best_cost = cost;
             best = P;
