@@ -186,29 +186,31 @@ def bench_prefill(w, steps, warmup, algo, o_dtype, cold_steps=0):
     kw = dict(per_channel=w.per_channel, kaczmarz=w.kaczmarz, eps=w.eps, o=o, s_final=s, o_dtype=odt,
               algo=algo, workspace=ws)
 
-    def step(events=None):
-        if events is not None:
-            events[0].record()
+    def step(mid=None, end=None):
         gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], stage=0, **kw)
-        if events is not None:
-            events[1].record()
+        if mid is not None:
+            mid.record()
         gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], stage=1, **kw)
-        if events is not None:
-            events[2].record()
+        if end is not None:
+            end.record()
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    # one event at each step boundary (the end of step i is the start of step i + 1) and one between the
+    # two kernels of each step
+    bnd = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    mid = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    bnd[0].record()
     for i in range(steps):
-        step(evs[i])
+        step(mid[i], bnd[i + 1])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    intra_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    state_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    intra_ms = [bnd[i].elapsed_time(mid[i]) for i in range(steps)]
+    state_ms = [mid[i].elapsed_time(bnd[i + 1]) for i in range(steps)]
+    step_ms = [bnd[i].elapsed_time(bnd[i + 1]) for i in range(steps)]
     # cold caches: before each of these steps a 512 MiB buffer is written, twice the 256 MB last-level
     # (Infinity) cache, so the step's inputs come from HBM; events bracket the two kernels only
     cold = None
@@ -217,7 +219,8 @@ def bench_prefill(w, steps, warmup, algo, o_dtype, cold_steps=0):
         cev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(cold_steps)]
         for i in range(cold_steps):
             scratch.fill_(i & 0xff)
-            step(cev[i])
+            cev[i][0].record()
+            step(cev[i][1], cev[i][2])
         torch.cuda.synchronize()
         del scratch
         cold = {"steps": cold_steps, "step_ms_median": median([e[0].elapsed_time(e[2]) for e in cev]),

@@ -43,6 +43,7 @@
 // with M = 0, beta = 1 (so T'' = I), X = V (no K~ S, no K~' dX) and no
 // gradient of beta.
 #include "gdr_internal.h"
+#include "matrix_common.h"
 
 namespace gdr {
 namespace {
@@ -128,25 +129,39 @@ constexpr int kLB = 48;   // B operands of 32 columns, read column-wise
 constexpr int kLS = 18;   // 16-column slices, read both ways
 
 // ============================================================ prep
+// One workgroup per chunk.  M and A on fp32 matrix-core tiles (wavefront w
+// takes lower tiles w, w + 4, w + 8 of the list; the upper tiles are zero).
+// Scalar decay: the products K K' and Q K', then the one decay factor of the
+// pair.  Per-channel decay: row block I takes the reference token r = 16 I
+// and the factors exp(G_ic - G_rc) (rows, <= 1) and exp(G_rc - G_jc)
+// (columns, <= 1 left of the diagonal) go into the operands; a diagonal
+// tile whose span max_c (G_rc - G_{r+15,c}) exceeds kSpanMax would overflow
+// the column factor and is summed term by term instead.  The decayed operands
+// K~, K^, Q~ are written next; then the LDS that held k and q holds R as
+// 16x16 tiles and T = (I + R)^-1 is formed by the block inverse of the
+// forward pass's intra kernel (forward substitution on the diagonal blocks,
+// matrix-core products for the others).
+constexpr float kSpanMax = 64.f;
+
 template <int DK, bool PC, bool KZ, bool IN_BF16>
-__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const void *__restrict__ q, const void *__restrict__ k,
-                                                            const float *__restrict__ g, const float *__restrict__ beta,
-                                                            int T, int H, int NC, float eps, float scale,
-                                                            float *__restrict__ wT, float *__restrict__ wA,
-                                                            float *__restrict__ wM, float *__restrict__ wG,
-                                                            float *__restrict__ wB, float *__restrict__ wKt,
-                                                            float *__restrict__ wKh, float *__restrict__ wQt,
-                                                            bool delta) {
+__global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
+    const void *__restrict__ q, const void *__restrict__ k, const float *__restrict__ g,
+    const float *__restrict__ beta, int T, int H, int NC, float eps, float scale, float *__restrict__ wT,
+    float *__restrict__ wA, float *__restrict__ wM, float *__restrict__ wG, float *__restrict__ wB,
+    float *__restrict__ wKt, float *__restrict__ wKh, float *__restrict__ wQt, bool delta) {
     constexpr int GK = PC ? DK : 1;
+    static_assert(2 * C * (DK + 1) >= 16 * mx::kTile, "the R and T tiles must fit where k and q were");
     const int ci = blockIdx.x;
     const Slot sl = slot_of(ci, T, H, NC);
     const int n = sl.n;
     const int tid = threadIdx.x;
-    __shared__ float sK[C][DK + 1];
-    __shared__ float sQ[C][DK + 1];
+    const int lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    __shared__ __align__(16) float sKQ[2][C][DK + 1];  // k, q; later the R and T tiles
+    float (*sK)[DK + 1] = sKQ[0];
+    float (*sQ)[DK + 1] = sKQ[1];
     __shared__ float sG[C][GK];
-    __shared__ __align__(16) float sR[C][C];
     __shared__ float sBeta[C];
+    __shared__ float sE[2][C];  // scalar decay: exp(G_i), exp(G_63 - G_i)
 
     {  // all loads in flight at once, then the LDS stores
         constexpr int NE = C * DK / kThreads, NG = (C * GK + kThreads - 1) / kThreads;
@@ -201,79 +216,113 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const void *__restri
         sBeta[i] = bv;
     }
     __syncthreads();
-
-    float *Mg = wM + (size_t)ci * C * C, *Ag = wA + (size_t)ci * C * C;
     if constexpr (!PC) {
-        // scalar decay: K K' and Q K' on fp32 matrix-core tiles, then the one decay factor per
-        // pair; wavefront w takes tiles w, w + 4, w + 8, w + 12 of the list (lower tiles first)
-        const int lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
-        for (int t = w; t < 16; t += 4) {
-            // tile t as 4 I + J in nibble t: the lower tiles (J <= I) row by row, then the upper ones
-            const int code = (int)((0xB76321FEDCA98540ull >> (4 * t)) & 15);
-            const int I = code >> 2, J = code & 3;
-            f32x4 mm = {0.f, 0.f, 0.f, 0.f}, aa = mm;
-            if (t < 10) {
+        if (tid < C) {
+            sE[0][tid] = __expf(sG[tid][0]);
+            sE[1][tid] = __expf(sG[C - 1][0] - sG[tid][0]);
+        }
+    }
+
+    // ---- M and A; this wavefront's R = Diag(beta) M values stay in registers
+    float *Mg = wM + (size_t)ci * C * C, *Ag = wA + (size_t)ci * C * C;
+    f32x4 rv[3];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+        const int t = w + 4 * s4;
+        // tile t as 4 I + J in nibble t: the lower tiles (J <= I) row by row, then the upper ones
+        const int code = (int)((0xB76321FEDCA98540ull >> (4 * t)) & 15);
+        const int I = code >> 2, J = code & 3;
+        f32x4 mm = {0.f, 0.f, 0.f, 0.f}, aa = mm;
+        if (t < 10) {
+            if constexpr (!PC) {
                 for (int kk = 0; kk < DK; kk += 4) {
                     const float kb = sK[16 * J + lr][kk + lg];
                     mm = mfma4(sK[16 * I + lr][kk + lg], kb, mm);
                     aa = mfma4(sQ[16 * I + lr][kk + lg], kb, aa);
                 }
-            }
+            } else {
+                const int r0 = 16 * I, ir = 16 * I + lr, jc = 16 * J + lr;
+                float span = 0.f;
+                if (I == J) {  // max over channels of G_r - G_{r+15}: a wavefront reduction
+                    for (int cc = lane; cc < DK; cc += 64) span = fmaxf(span, sG[r0][cc] - sG[r0 + 15][cc]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * I + 4 * lg + r, j = 16 * J + lr;
-                const float pp = j <= i ? __expf(sG[i][0] - sG[j][0]) : 0.f;
-                const float m = delta && j < i ? mm[r] * pp : 0.f;
-                Mg[i * C + j] = m;
-                Ag[i * C + j] = scale * aa[r] * pp;
-                sR[i][j] = sBeta[i] * m;
-            }
-        }
-    } else {  // M (strictly lower), A (lower): thread -> row i, 16 columns
-        const int i = tid >> 2, jb = (tid & 3) * 16;
-        for (int jj = 0; jj < 16; ++jj) {
-            const int j = jb + jj;
-            float r = 0.f, a = 0.f;
-            if (j <= i) {
-                for (int cc = 0; cc < DK; ++cc) {
-                    const float p = __expf(sG[i][cc] - sG[j][cc]);
-                    r += sK[i][cc] * sK[j][cc] * p;
-                    a += sQ[i][cc] * sK[j][cc] * p;
+                    for (int o = 32; o > 0; o >>= 1) span = fmaxf(span, __shfl_xor(span, o, 64));
+                }
+                if (span <= kSpanMax) {
+                    for (int kk = 0; kk < DK; kk += 4) {
+                        const int cc = kk + lg;
+                        const float er = __expf(sG[ir][cc] - sG[r0][cc]);
+                        const float kb = sK[jc][cc] * __expf(sG[r0][cc] - sG[jc][cc]);
+                        mm = mfma4(sK[ir][cc] * er, kb, mm);
+                        aa = mfma4(sQ[ir][cc] * er, kb, aa);
+                    }
+                } else {  // every entry j <= i directly
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 16 * I + 4 * lg + r;
+                        float sm_ = 0.f, sa = 0.f;
+                        if (jc <= i) {
+                            for (int cc = 0; cc < DK; ++cc) {
+                                const float d = __expf(sG[i][cc] - sG[jc][cc]) * sK[jc][cc];
+                                sm_ += d * sK[i][cc];
+                                sa += d * sQ[i][cc];
+                            }
+                        }
+                        mm[r] = sm_;
+                        aa[r] = sa;
+                    }
                 }
             }
-            const float m = delta && j < i ? r : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * I + 4 * lg + r, j = 16 * J + lr;
+            const float pp = PC ? (j <= i ? 1.f : 0.f) : (j <= i ? __expf(sG[i][0] - sG[j][0]) : 0.f);
+            const float m = delta && j < i ? mm[r] * pp : 0.f;
             Mg[i * C + j] = m;
-            Ag[i * C + j] = j <= i ? scale * a : 0.f;
-            sR[i][j] = sBeta[i] * m;
+            Ag[i * C + j] = scale * aa[r] * pp;
+            if (s4 < 3 && t < 10) rv[s4 < 3 ? s4 : 0][r] = sBeta[i] * m;
         }
-    }
-    __syncthreads();
-    // T = (I + R)^-1, one column per thread: x_i = [i == col] - sum_{m<i} R_im x_m
-    if (tid < C) {
-        const int col = tid;
-        float x[C];
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-            float acc = i == col ? 1.f : 0.f;
-#pragma unroll
-            for (int m = 0; m < i; ++m) acc -= sR[i][m] * x[m];
-            x[i] = acc;
-        }
-        float *Tg = wT + (size_t)ci * C * C;
-#pragma unroll
-        for (int i = 0; i < C; ++i) Tg[i * C + col] = x[i];
     }
     for (int idx = tid; idx < C * GK; idx += kThreads) wG[(size_t)ci * C * GK + idx] = sG[idx / GK][idx % GK];
     if (tid < C) wB[(size_t)ci * C + tid] = sBeta[tid];
     // the decayed operands: K~ = exp(G) k, K^ = exp(G_63 - G) k, Q~ = scale exp(G) q
     for (int idx = tid; idx < C * DK; idx += kThreads) {
         const int i = idx / DK, cc = idx % DK;
-        const float gi = PC ? sG[i][cc] : sG[i][0];
-        const float ge = PC ? sG[C - 1][cc] : sG[C - 1][0];
-        const float ei = __expf(gi);
+        float ei, eh;
+        if constexpr (PC) {
+            ei = __expf(sG[i][cc]);
+            eh = __expf(sG[C - 1][cc] - sG[i][cc]);
+        } else {
+            ei = sE[0][i];
+            eh = sE[1][i];
+        }
         wKt[(size_t)ci * C * DK + idx] = ei * sK[i][cc];
-        wKh[(size_t)ci * C * DK + idx] = __expf(ge - gi) * sK[i][cc];
+        wKh[(size_t)ci * C * DK + idx] = eh * sK[i][cc];
         wQt[(size_t)ci * C * DK + idx] = scale * ei * sQ[i][cc];
+    }
+    __syncthreads();  // k and q are no longer read
+
+    // ---- T = (I + R)^-1 on 16x16 tiles in the LDS of k and q
+    float *tiles = &sKQ[0][0][0];
+    const mx::TriTiles tri{tiles, tiles + 10 * mx::kTile, nullptr};
+#pragma unroll
+    for (int s4 = 0; s4 < 3; ++s4) {
+        const int t = w + 4 * s4;
+        if (t < 10) {
+            const int code = (int)((0xB76321FEDCA98540ull >> (4 * t)) & 15);
+            const int I = code >> 2, J = code & 3;
+            float *dst = &tri.R[mx::tile_id(I, J) * mx::kTile];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(4 * lg + r) * mx::LT + lr] = rv[s4][r];
+        }
+    }
+    __syncthreads();
+    mx::invert_unit_lower(tri, lane, w, lr, lg);  // ends with a barrier
+    float *Tg = wT + (size_t)ci * C * C;
+    for (int idx = tid; idx < C * C; idx += kThreads) {
+        const int i = idx / C, j = idx % C, I = i >> 4, J = j >> 4;
+        Tg[idx] = J <= I ? tri.Tb(I, J)[(i & 15) * mx::LT + (j & 15)] : 0.f;
     }
 }
 

@@ -254,9 +254,11 @@ struct alignas(16) StateSmem {
     __bf16 V[2][C * LDV];          // v slice, token-major
     float Gam[3][C];               // exp(G_i); chunk c in buffer c % 3 (read one chunk later by the helpers)
     float Gend[2][C];              // exp(G_63 - G_i)
-    uint4 X[2][2][kXFrags][64];    // per chain wavefront and chunk parity
-    float Ost[2][C * 20];          // per helper: its fp32 output tile, token-major, for 16-byte stores
+    uint4 X[2][2][kXFrags][64];    // per chunk parity and chain wavefront; once a helper has read its
+                                   // chunk's Q S and E, the same 8 KB hold its fp32 output tile
+                                   // (token-major, 20-float rows) for 16-byte stores
 };
+static_assert(C * 20 * sizeof(float) <= kXFrags * 64 * sizeof(uint4), "output tile must fit one X buffer");
 // The transfer walk (no outputs, no Q S) needs only the k and v staging and the decays.
 struct alignas(16) TransferSmem {
     __bf16 K[2][C * LDK];
@@ -586,7 +588,8 @@ __global__ __launch_bounds__(kStateThreads, TRANSFER ? 2 : 1) void state_matrix_
         auto outputs = [&](int cp) __attribute__((always_inline)) {
             if constexpr (!TRANSFER) {
                 const int t0 = (c0 + cp) * C;
-                chunk_outputs<OUT_BF16, true>(&sm.X[cp & 1][vt][0][0], sm.Gam[cp % 3], scale, ah, al, sm.Ost[vt],
+                uint4 *xv = &sm.X[cp & 1][vt][0][0];  // not written by the chain before the next barrier
+                chunk_outputs<OUT_BF16, true>(xv, sm.Gam[cp % 3], scale, ah, al, reinterpret_cast<float *>(xv),
                                               o, head0 + (size_t)t0 * H, min(C, L - t0), H, jt, lane);
             }
         };

@@ -324,7 +324,8 @@ __device__ __forceinline__ void state_slot(int x, int groups, int nsl, int &g, i
 // scale and the decay of its token (row i is multiplied by scale
 // row_scale[i] here); otherwise it is final.  Rows past the end of the
 // sequence are dropped by the buffer bounds.  The fp32 tile goes through the
-// wavefront's own LDS area `ost` so that each lane stores 16-byte rows.
+// LDS area `ost` (20-float rows, which may be xi itself) so that each lane
+// stores 16-byte rows.
 template <bool OUT_BF16, bool ROW_SCALE>
 __device__ __forceinline__ void chunk_outputs(const uint4 *xi, const float *row_scale, float scale,
                                               const bf16x8 *ah, const bf16x8 *al, float *ost, void *o, size_t row0,
@@ -342,6 +343,10 @@ __device__ __forceinline__ void chunk_outputs(const uint4 *xi, const float *row_
             for (int r = 0; r < 4; ++r) O[M][r] *= scale * rs[r];
         }
     }
+    // ost may overlay xi (a caller whose xi is free once read): no LDS store
+    // below may be moved above these loads (one wavefront's LDS operations
+    // complete in order, so the hardware keeps them apart).
+    __asm__ volatile("" ::: "memory");
     pair_split(E[0], E[1], eh[0], el[0]);
     pair_split(E[2], E[3], eh[1], el[1]);
 #pragma unroll
