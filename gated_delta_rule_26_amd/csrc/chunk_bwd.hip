@@ -905,8 +905,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
 // Diag(beta) dR.  The pair terms of M and A: for scalar decay P_ij =
 // exp(G_i - G_j) is one factor per pair, so with W1 = dM o P and W2 = scale
 // dA o P they are products, dk += W1 K + W1' K + W2' Q, dq += W2 K, and dG_i
-// = rowsum_i(Z) - colsum_i(Z) with Z = dM o M + dA o A; per-channel decay
-// takes them term by term per key channel.  Then the Kaczmarz step size and
+// = rowsum_i(Z) - colsum_i(Z) with Z = dM o M + dA o A; for per-channel decay
+// P is split at a reference token per row block, as in the prep kernel.  Then the Kaczmarz step size and
 // the reverse cumulative sum of dG.
 template <int DK, bool PC, bool KZ, bool IN_BF16>
 __global__ __launch_bounds__(kThreads) void bwd_grads_b_kernel(
@@ -916,8 +916,6 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_b_kernel(
     const float *__restrict__ wdTT, const float *__restrict__ wdG, const float *__restrict__ wdG63,
     float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dg, float *__restrict__ dbeta) {
     constexpr int GK = PC ? DK : 1;
-    constexpr int GROUPS = kThreads / DK;      // per-channel pair terms: row groups per channel
-    constexpr int RPT = C / GROUPS;            // rows per thread
     constexpr int LC = C + 1;                  // row stride of the C x C buffers
     constexpr int LQ = DK + 1;                 // row stride of the C x DK buffers
     constexpr int R0 = 0, R1 = C * LC, R2 = 2 * C * LC;  // three C x C regions
@@ -1117,47 +1115,116 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_b_kernel(
                 }
             }
     } else {
-        const int cch = tid % DK, grp = tid / DK;
-        float pk[RPT], pq[RPT], pg[RPT];
+        // Per-channel pair terms on matrix-core tiles.  Wavefront w takes the rows i of block w and all
+        // channels c:  U_ic = sum_{j<i} dM_ij k_jc P_ijc  and  V_ic = scale sum_{j<=i} dA_ij k_jc P_ijc  (its
+        // rows of M and A), and Cl_ic = sum_{i2>=i} (dM_{i2 i} k_{i2 c} + scale dA_{i2 i} q_{i2 c}) P_{i2 i c}
+        // (its columns); then dk += U + Cl, dq += V, dG += k (U - Cl) + q V.  P_ijc = exp(G_ic - G_jc) is
+        // split at the reference token r = 16 I of the row block I of i: exp(G_ic - G_rc) (<= 1) scales the
+        // product's rows (U, V) or operand (Cl), exp(G_rc - G_jc) its operand (U, V) or rows (Cl); both are
+        // <= 1 off the diagonal, and the diagonal block is summed term by term when its span would overflow.
+        constexpr int JC = DK / 16;
+        const f32x4 zero = z4;
+        f32x4 U[JC], V[JC], Cl[JC];
 #pragma unroll
-        for (int u = 0; u < RPT; ++u) {
-            const int r = grp + u * GROUPS;  // rows of this thread (interleaved: the triangle is balanced)
-            const float gi = sG[r][cch];
-            const float ki = sK[r][cch], qi = sQ[r][cch];
-            float ak = 0.f, aq = 0.f, ag = 0.f;
-            for (int j = 0; j <= r; ++j) {  // as the row of M and A: j <= i
-                const float p = __expf(gi - sG[j][cch]);
-                const float kj = sK[j][cch];
-                const float a = j < r ? sD[j * LC + r] : 0.f;  // dM_ij
-                const float bq = scale * sD[r * LC + j];       // scale dA_ij
-                ak += a * kj * p;
-                aq += bq * kj * p;
-                ag += (a * ki + bq * qi) * kj * p;
+        for (int jc = 0; jc < JC; ++jc) U[jc] = V[jc] = Cl[jc] = zero;
+        const int rw = 16 * w;  // first row of this wavefront's block
+        float span = 0.f;
+        for (int cc = lane; cc < DK; cc += 64) span = fmaxf(span, sG[rw][cc] - sG[rw + 15][cc]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) span = fmaxf(span, __shfl_xor(span, o, 64));
+        const bool direct = span > kSpanMax;
+        // U, V over the column blocks J <= w
+        for (int J = 0; J <= w; ++J) {
+            if (J == w && direct) continue;
+            for (int kk = 0; kk < 16; kk += 4) {
+                const int i = rw + lr, j = 16 * J + kk + lg;
+                const float a1 = j < i ? sD[j * LC + i] : 0.f;           // dM_ij
+                const float a2 = j <= i ? scale * sD[i * LC + j] : 0.f;  // scale dA_ij
+#pragma unroll
+                for (int jc = 0; jc < JC; ++jc) {
+                    const int c = 16 * jc + lr;
+                    const float b = sK[j][c] * __expf(sG[rw][c] - sG[j][c]);
+                    U[jc] = mfma4(a1, b, U[jc]);
+                    V[jc] = mfma4(a2, b, V[jc]);
+                }
             }
-            for (int i2 = r; i2 < C; ++i2) {  // as the column of M and A: i >= j (here j = r)
-                const float p = __expf(sG[i2][cch] - gi);
-                const float a = i2 > r ? sD[r * LC + i2] : 0.f;  // dM_{i2, r}
-                const float bq = scale * sD[i2 * LC + r];        // scale dA_{i2, r}
-                const float wv = (a * sK[i2][cch] + bq * sQ[i2][cch]) * p;
-                ak += wv;
-                ag -= wv * ki;
-            }
-            pk[u] = ak;
-            pq[u] = aq;
-            pg[u] = ag;
         }
 #pragma unroll
-        for (int u = 0; u < RPT; ++u) {
-            const int r = grp + u * GROUPS;
-            sdG[r][cch] += pg[u];  // each thread its own entries
-            if (r < n) {
-                const size_t off = (sl.row0 + (size_t)r * H) * DK + cch;
-                float dkv = dk[off] + pk[u];
-                if constexpr (KZ) dkv += -2.f * sBeta[r] * sdBeta[r] / (sKK[r] + eps) * sK[r][cch];
-                dk[off] = dkv;
-                dq[off] += pq[u];
+        for (int jc = 0; jc < JC; ++jc)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = rw + 4 * lg + r, c = 16 * jc + lr;
+                const float e = __expf(sG[i][c] - sG[rw][c]);
+                U[jc][r] *= e;
+                V[jc][r] *= e;
             }
+        // Cl over the row blocks I >= w
+        for (int I = w; I < 4; ++I) {
+            if (I == w && direct) continue;
+            const int ri = 16 * I;
+            f32x4 Ck[JC];
+#pragma unroll
+            for (int jc = 0; jc < JC; ++jc) Ck[jc] = zero;
+            for (int kk = 0; kk < 16; kk += 4) {
+                const int j = rw + lr, i = ri + kk + lg;
+                const float a1 = i > j ? sD[j * LC + i] : 0.f;           // dM_ij
+                const float a2 = i >= j ? scale * sD[i * LC + j] : 0.f;  // scale dA_ij
+#pragma unroll
+                for (int jc = 0; jc < JC; ++jc) {
+                    const int c = 16 * jc + lr;
+                    const float e = __expf(sG[i][c] - sG[ri][c]);
+                    Ck[jc] = mfma4(a1, sK[i][c] * e, Ck[jc]);
+                    Ck[jc] = mfma4(a2, sQ[i][c] * e, Ck[jc]);
+                }
+            }
+#pragma unroll
+            for (int jc = 0; jc < JC; ++jc)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = rw + 4 * lg + r, c = 16 * jc + lr;
+                    Cl[jc][r] += Ck[jc][r] * __expf(sG[ri][c] - sG[j][c]);
+                }
         }
+        if (direct) {  // the diagonal block term by term
+#pragma unroll
+            for (int jc = 0; jc < JC; ++jc)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = rw + 4 * lg + r, c = 16 * jc + lr;
+                    const float gi = sG[i][c];
+                    float u = 0.f, vq = 0.f, cl = 0.f;
+                    for (int j = rw; j < rw + 16; ++j) {
+                        if (j <= i) {  // i's row of M and A
+                            const float p = __expf(gi - sG[j][c]) * sK[j][c];
+                            if (j < i) u += sD[j * LC + i] * p;
+                            vq += scale * sD[i * LC + j] * p;
+                        }
+                        if (j >= i) {  // i's column
+                            const float p = __expf(sG[j][c] - gi);
+                            const float a = j > i ? sD[i * LC + j] * sK[j][c] : 0.f;
+                            cl += (a + scale * sD[j * LC + i] * sQ[j][c]) * p;
+                        }
+                    }
+                    U[jc][r] += u;
+                    V[jc][r] += vq;
+                    Cl[jc][r] += cl;
+                }
+        }
+#pragma unroll
+        for (int jc = 0; jc < JC; ++jc)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = rw + 4 * lg + r, c = 16 * jc + lr;
+                const float ki = sK[i][c];
+                sdG[i][c] += ki * (U[jc][r] - Cl[jc][r]) + sQ[i][c] * V[jc][r];  // each lane its own entries
+                if (i < n) {
+                    const size_t off = (sl.row0 + (size_t)i * H) * DK + c;
+                    float dkv = dk[off] + U[jc][r] + Cl[jc][r];
+                    if constexpr (KZ) dkv += -2.f * sBeta[i] * sdBeta[i] / (sKK[i] + eps) * ki;
+                    dk[off] = dkv;
+                    dq[off] += V[jc][r];
+                }
+            }
     }
     __syncthreads();
     // dg = reverse cumulative sum of dG over the chunk's tokens; dbeta (deta)
