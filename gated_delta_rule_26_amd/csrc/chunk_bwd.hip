@@ -909,7 +909,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
 // P is split at a reference token per row block, as in the prep kernel.  Then the Kaczmarz step size and
 // the reverse cumulative sum of dG.
 template <int DK, bool PC, bool KZ, bool IN_BF16>
-__global__ __launch_bounds__(kThreads) void bwd_grads_b_kernel(
+__global__ __launch_bounds__(kThreads, IN_BF16 && !PC ? 2 : 1) void bwd_grads_b_kernel(
     const void *__restrict__ q, const void *__restrict__ k, int T, int H, int NC, float eps, float scale,
     const float *__restrict__ wT, const float *__restrict__ wM, const float *__restrict__ wA,
     const float *__restrict__ wG, const float *__restrict__ wB, const float *__restrict__ wdA,
@@ -922,14 +922,21 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_b_kernel(
     // per-channel decay: k and q over the C x C regions once those are free; scalar decay: W1, W2
     // in regions 0 and 1, k from region 2 on, then q
     constexpr int KOFF = PC ? 0 : R2, QOFF = KOFF + C * LQ;
-    constexpr int kSmem = QOFF + C * LQ > 3 * C * LC ? QOFF + C * LQ : 3 * C * LC;
+    // scalar decay with bf16 inputs: dA / dM' is a fourth C x C region, and k, q (exact in bf16) are
+    // kept as bf16 over regions 2 and 3 once those are free, so two workgroups share a unit
+    constexpr bool KQ16 = IN_BF16 && !PC;
+    constexpr int LQB = DK + 16;  // bf16 row stride: rows 8 banks apart
+    constexpr int R3 = 3 * C * LC;
+    constexpr int KQ16_END = R2 + (C * LQB > 2 * C * LC ? C * LQB : 2 * C * LC);
+    constexpr int kSmem = KQ16 ? KQ16_END : (QOFF + C * LQ > 3 * C * LC ? QOFF + C * LQ : 3 * C * LC);
     const int ci = blockIdx.x;
     const Slot sl = slot_of(ci, T, H, NC);
     const int n = sl.n;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     __shared__ float smem[kSmem];
-    __shared__ float sD[C * LC];        // dA (j <= i) and, in the strict upper part, dM transposed
+    __shared__ float sDarr[KQ16 ? 1 : C * LC];
+    float *sD = KQ16 ? smem + R3 : sDarr;  // dA (j <= i) and, in the strict upper part, dM transposed
     __shared__ float sG[C][GK];
     __shared__ float sBeta[C], sdBeta[C], sKK[C];
     __shared__ float sdG[C][GK];
@@ -1037,6 +1044,25 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_b_kernel(
 
     float(*sK)[LQ] = reinterpret_cast<float(*)[LQ]>(smem + KOFF);
     float(*sQ)[LQ] = reinterpret_cast<float(*)[LQ]>(smem + QOFF);
+    __bf16 *sKb = reinterpret_cast<__bf16 *>(smem + R2), *sQb = sKb + C * LQB;
+    auto kv = [&](int r, int c) -> float {
+        if constexpr (KQ16) return static_cast<float>(sKb[r * LQB + c]);
+        else return sK[r][c];
+    };
+    auto qv = [&](int r, int c) -> float {
+        if constexpr (KQ16) return static_cast<float>(sQb[r * LQB + c]);
+        else return sQ[r][c];
+    };
+    // raw k, q: the loads are issued here and stored to LDS below
+    constexpr int NKK = C * DK / kThreads;
+    float rk[NKK], rq[NKK];
+#pragma unroll
+    for (int u = 0; u < NKK; ++u) {
+        const int idx = tid + u * kThreads, r = idx / DK, cc = idx % DK;
+        const size_t off = (sl.row0 + (size_t)r * H) * DK + cc;
+        rk[u] = r < n ? load_in<IN_BF16>(k, off) : 0.f;
+        rq[u] = r < n ? load_in<IN_BF16>(q, off) : 0.f;
+    }
     if constexpr (!PC) {
         // dG_i = rowsum_i(Z) - colsum_i(Z), Z = dM o M + dA o A (M in sY, A in sT)
         if (tid < C) {
@@ -1057,16 +1083,15 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_b_kernel(
             sX[i * LC + j] = scale * sD[i * LC + j] * p;  // zero above the diagonal
         }
     }
-    {  // raw k, q
-        constexpr int NKK = C * DK / kThreads;
-        float rk[NKK], rq[NKK];
+    if constexpr (KQ16) {
+        __syncthreads();  // M and dA / dM' are no longer read
 #pragma unroll
         for (int u = 0; u < NKK; ++u) {
-            const int idx = tid + u * kThreads, r = idx / DK, cc = idx % DK;
-            const size_t off = (sl.row0 + (size_t)r * H) * DK + cc;
-            rk[u] = r < n ? load_in<IN_BF16>(k, off) : 0.f;
-            rq[u] = r < n ? load_in<IN_BF16>(q, off) : 0.f;
+            const int idx = tid + u * kThreads;
+            sKb[(idx / DK) * LQB + idx % DK] = static_cast<__bf16>(rk[u]);
+            sQb[(idx / DK) * LQB + idx % DK] = static_cast<__bf16>(rq[u]);
         }
+    } else {
 #pragma unroll
         for (int u = 0; u < NKK; ++u) {
             const int idx = tid + u * kThreads;
@@ -1078,7 +1103,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_b_kernel(
     if constexpr (KZ) {  // |k_i|^2
         if (tid < C) {
             float s = 0.f;
-            for (int cc = 0; cc < DK; ++cc) s += sK[tid][cc] * sK[tid][cc];
+            for (int cc = 0; cc < DK; ++cc) s += kv(tid, cc) * kv(tid, cc);
             sKK[tid] = s;
         }
         __syncthreads();
@@ -1094,7 +1119,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_b_kernel(
             const float w2 = sX[(16 * w + lr) * LC + kk + lg], w2t = sX[(kk + lg) * LC + 16 * w + lr];
 #pragma unroll
             for (int J = 0; J < JK; ++J) {
-                const float kb = sK[kk + lg][16 * J + lr], qb = sQ[kk + lg][16 * J + lr];
+                const float kb = kv(kk + lg, 16 * J + lr), qb = qv(kk + lg, 16 * J + lr);
                 pk[J] = mfma4(w1, kb, pk[J]);
                 pk[J] = mfma4(w1t, kb, pk[J]);
                 pk[J] = mfma4(w2t, qb, pk[J]);
@@ -1109,7 +1134,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_b_kernel(
                 if (i < n) {
                     const size_t off = (sl.row0 + (size_t)i * H) * DK + ch;
                     float dkv = dk[off] + pk[J][r];
-                    if constexpr (KZ) dkv += -2.f * sBeta[i] * sdBeta[i] / (sKK[i] + eps) * sK[i][ch];
+                    if constexpr (KZ) dkv += -2.f * sBeta[i] * sdBeta[i] / (sKK[i] + eps) * kv(i, ch);
                     dk[off] = dkv;
                     dq[off] += pq[J][r];
                 }
