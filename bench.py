@@ -36,21 +36,21 @@ _SCALAR = ("gated_delta_rule_26_amd/csrc/chunk_matrix.hip", "gated_delta_rule_26
 _PER_CHANNEL = ("gated_delta_rule_26_amd/csrc/chunk_matrix_pc.hip", "gated_delta_rule_26_amd/csrc/matrix_common.h")
 _DECODE = ("gated_delta_rule_26_amd/csrc/recurrent_step.hip",)
 MEASURED_TRAFFIC = {
-    ("matrix", "state", "gdn_prefill"): (_SCALAR, "f77615373beab2e05720a4e5c19567d55fd1c3473f3d8c9efe92c8b700ba44cb",
-                                         (148668.5 * 2.0 + 135171.9) * 1024),
-    ("matrix", "intra", "gdn_prefill"): (_SCALAR, "f77615373beab2e05720a4e5c19567d55fd1c3473f3d8c9efe92c8b700ba44cb",
-                                         (66883.1 * 2.0 + 100352.0) * 1024),
-    ("matrix", "state", "kda_prefill"): (_PER_CHANNEL, "3823ccb93f5569591bf6f38465c39bdf55c2c4378189e604be4b583daa52f009",
-                                         (279778.8 * 2.0 + 133120.0) * 1024),
-    ("matrix", "intra", "kda_prefill"): (_PER_CHANNEL, "3823ccb93f5569591bf6f38465c39bdf55c2c4378189e604be4b583daa52f009",
-                                         (134573.2 * 2.0 + 493568.1) * 1024),
+    ("matrix", "state", "gdn_prefill"): (_SCALAR, "1201aa5d5a5c21bade99c648bf2f392684dd1b326e6f5069491ae747917431a3",
+                                         (148668.1 * 2.0 + 135172.0) * 1024),
+    ("matrix", "intra", "gdn_prefill"): (_SCALAR, "1201aa5d5a5c21bade99c648bf2f392684dd1b326e6f5069491ae747917431a3",
+                                         (66878.3 * 2.0 + 100352.0) * 1024),
+    ("matrix", "state", "kda_prefill"): (_PER_CHANNEL, "5fa637086ce22f9ad3197d83cf323512cc2301b645444e630104e2467b41a93b",
+                                         (279778.3 * 2.0 + 133120.0) * 1024),
+    ("matrix", "intra", "kda_prefill"): (_PER_CHANNEL, "5fa637086ce22f9ad3197d83cf323512cc2301b645444e630104e2467b41a93b",
+                                         (134565.2 * 2.0 + 493568.0) * 1024),
     # the state phase of the long sequence is three launches: the segment transfer walk, the
     # combine of the entering states and the per-segment walk
-    ("matrix", "state", "kla_prefill"): (_SCALAR, "f77615373beab2e05720a4e5c19567d55fd1c3473f3d8c9efe92c8b700ba44cb",
-                                         (730654.2 * 2.0 + 8192.0 + 15398.7 * 2.0 + 4096.0
-                                          + 1190824.8 * 2.0 + 1049621.2) * 1024),
-    ("matrix", "intra", "kla_prefill"): (_SCALAR, "f77615373beab2e05720a4e5c19567d55fd1c3473f3d8c9efe92c8b700ba44cb",
-                                         (656101.7 * 2.0 + 802816.0) * 1024),
+    ("matrix", "state", "kla_prefill"): (_SCALAR, "1201aa5d5a5c21bade99c648bf2f392684dd1b326e6f5069491ae747917431a3",
+                                         (732134.9 * 2.0 + 8192.0 + 15398.7 * 2.0 + 4096.0
+                                          + 1190090.9 * 2.0 + 1049605.1) * 1024),
+    ("matrix", "intra", "kla_prefill"): (_SCALAR, "1201aa5d5a5c21bade99c648bf2f392684dd1b326e6f5069491ae747917431a3",
+                                         (656170.9 * 2.0 + 802816.0) * 1024),
     ("decode", "step", "decode"): (_DECODE, "d95cdb4ade6f5f5e28c9f763a67dd8d994546380ce9e0a79ea14ec92052d8c69",
                                    (132967.5 * 2.0 + 264192.0) * 1024),
 }
@@ -61,12 +61,13 @@ MEASURED_TRAFFIC = {
 # (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) per second.  The issued flops count every bf16 hi/lo product, so they
 # exceed the algorithmic flops.  (files, sha, busy fraction, issued TFLOP/s), as for the traffic.
 MEASURED_MFMA = {
-    ("matrix", "state", "gdn_prefill"): (_SCALAR, "f77615373beab2e05720a4e5c19567d55fd1c3473f3d8c9efe92c8b700ba44cb",
-                                         0.192, 454.0),
-    ("matrix", "state", "kda_prefill"): (_PER_CHANNEL, "3823ccb93f5569591bf6f38465c39bdf55c2c4378189e604be4b583daa52f009",
-                                         0.080, 197.4),
-    ("matrix", "state", "kla_prefill"): (_SCALAR, "f77615373beab2e05720a4e5c19567d55fd1c3473f3d8c9efe92c8b700ba44cb",
-                                         0.244, 539.0),   # transfer + combine + walk, by duration
+    ("matrix", "state", "gdn_prefill"): (_SCALAR, "1201aa5d5a5c21bade99c648bf2f392684dd1b326e6f5069491ae747917431a3",
+                                         0.192, 452.1),
+    ("matrix", "state", "kda_prefill"): (_PER_CHANNEL, "5fa637086ce22f9ad3197d83cf323512cc2301b645444e630104e2467b41a93b",
+                                         0.080, 198.4),
+    # the long sequence: transfer + combine + walk, weighted by duration
+    ("matrix", "state", "kla_prefill"): (_SCALAR, "1201aa5d5a5c21bade99c648bf2f392684dd1b326e6f5069491ae747917431a3",
+                                         0.245, 537.3),
 }
 
 
