@@ -187,46 +187,47 @@ def bench_prefill(w, steps, warmup, algo, o_dtype, cold_steps=0):
     kw = dict(per_channel=w.per_channel, kaczmarz=w.kaczmarz, eps=w.eps, o=o, s_final=s, o_dtype=odt,
               algo=algo, workspace=ws)
 
-    def step(mid=None, end=None):
-        gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], stage=0, **kw)
-        if mid is not None:
-            mid.record()
-        gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], stage=1, **kw)
-        if end is not None:
-            end.record()
+    def step(ev=None):
+        gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], stage=0, events=ev and (ev[0], ev[1]), **kw)
+        gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], stage=1, events=ev and (ev[2], ev[3]), **kw)
+
+    def new_events(n):
+        # per step: the intra kernel's begin and end, the state phase's begin and end, recorded by the
+        # kernels themselves (gdr_chunk_fwd_stage_timed); each is recorded once here so that it exists
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+        for e in evs:
+            for x in e:
+                x.record()
+        return evs
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    # one event at each step boundary (the end of step i is the start of step i + 1) and one between the
-    # two kernels of each step
-    bnd = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    mid = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    evs = new_events(steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    bnd[0].record()
     for i in range(steps):
-        step(mid[i], bnd[i + 1])
+        step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    intra_ms = [bnd[i].elapsed_time(mid[i]) for i in range(steps)]
-    state_ms = [mid[i].elapsed_time(bnd[i + 1]) for i in range(steps)]
-    step_ms = [bnd[i].elapsed_time(bnd[i + 1]) for i in range(steps)]
+    intra_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    state_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
     # cold caches: before each of these steps a 512 MiB buffer is written, twice the 256 MB last-level
-    # (Infinity) cache, so the step's inputs come from HBM; events bracket the two kernels only
+    # (Infinity) cache, so the step's inputs come from HBM
     cold = None
     if cold_steps > 0:
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(cold_steps)]
+        cev = new_events(cold_steps)
+        torch.cuda.synchronize()
         for i in range(cold_steps):
             scratch.fill_(i & 0xff)
-            cev[i][0].record()
-            step(cev[i][1], cev[i][2])
+            step(cev[i])
         torch.cuda.synchronize()
         del scratch
-        cold = {"steps": cold_steps, "step_ms_median": median([e[0].elapsed_time(e[2]) for e in cev]),
+        cold = {"steps": cold_steps, "step_ms_median": median([e[0].elapsed_time(e[3]) for e in cev]),
                 "intra_ms_median": median([e[0].elapsed_time(e[1]) for e in cev]),
-                "state_ms_median": median([e[1].elapsed_time(e[2]) for e in cev]),
+                "state_ms_median": median([e[2].elapsed_time(e[3]) for e in cev]),
                 "flush": "512 MiB device buffer written before each step"}
     return {"wall_s": wall, "intra_ms": intra_ms, "state_ms": state_ms, "step_ms": step_ms, "inputs": x,
             "o_bytes": 4 if odt == torch.float32 else 2, "in_bytes": 2 if qdt == torch.bfloat16 else 4,

@@ -90,6 +90,8 @@ def load_library(path: str | None = None):
     lib.gdr_chunk_bwd.argtypes = [D] + [V] * 15 + [ctypes.c_size_t, V]
     lib.gdr_chunk_fwd_stage.restype = ctypes.c_int
     lib.gdr_chunk_fwd_stage.argtypes = [ctypes.c_int, D, V, V, V, V, V, V, V, V, V, ctypes.c_size_t, V]
+    lib.gdr_chunk_fwd_stage_timed.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_stage_timed.argtypes = [ctypes.c_int, D, V, V, V, V, V, V, V, V, V, ctypes.c_size_t, V, V, V]
     lib.gdr_recurrent_step.restype = ctypes.c_int
     lib.gdr_recurrent_step.argtypes = [D, V, V, V, V, V, V, V, V]
     lib.gdr_recurrent_fwd.restype = ctypes.c_int
@@ -147,7 +149,7 @@ def chunk_fwd_workspace_size(desc: Desc) -> int:
 def chunk_fwd(q, k, v, g, beta, *, per_channel: bool = False, kaczmarz: bool = False, eps: float = 0.0,
               scale: float = 1.0, s0=None, output_final_state: bool = True, s_final=None, o=None,
               o_dtype=None, algo: str = "auto", workspace=None, stream=None, stage=None,
-              delta_off: bool = False):
+              delta_off: bool = False, events=None):
     """Chunked forward pass (prefill) through ``gdr_chunk_fwd``.
 
     q, k [B,T,H,Dk] and v [B,T,H,Dv] in float32 or bfloat16; g float32
@@ -159,6 +161,9 @@ def chunk_fwd(q, k, v, g, beta, *, per_channel: bool = False, kaczmarz: bool = F
     on ``stream`` (default: torch's current stream of q's device).  ``stage``
     (0 = intra kernel, 1 = state kernel) runs one kernel of the pipeline
     through ``gdr_chunk_fwd_stage``; both stages must then share ``workspace``.
+    ``events`` (with ``stage``): a pair of torch.cuda.Event(enable_timing=True)
+    that have been recorded once (so that they exist); the stage's kernels
+    record them when they begin and end (``gdr_chunk_fwd_stage_timed``).
     """
     lib = load_library()
     dev = q.device
@@ -196,11 +201,18 @@ def chunk_fwd(q, k, v, g, beta, *, per_channel: bool = False, kaczmarz: bool = F
     args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(o),
             _ptr(s_final), _ptr(workspace), workspace.numel(), ctypes.c_void_p(st.cuda_stream))
     if stage is None:
-        rc = lib.gdr_chunk_fwd(*args)
+        if events is not None:
+            raise ValueError("events time one stage: pass stage=0 or 1")
+        rc, name = lib.gdr_chunk_fwd(*args), "gdr_chunk_fwd"
+    elif events is None:
+        rc, name = lib.gdr_chunk_fwd_stage(int(stage), *args), "gdr_chunk_fwd_stage"
     else:
-        rc = lib.gdr_chunk_fwd_stage(int(stage), *args)
+        e0, e1 = (ctypes.c_void_p(e.cuda_event) for e in events)
+        if not e0.value or not e1.value:
+            raise ValueError("record each event once before passing it")
+        rc, name = lib.gdr_chunk_fwd_stage_timed(int(stage), *args, e0, e1), "gdr_chunk_fwd_stage_timed"
     if rc != 0:
-        raise GdrError(rc, "gdr_chunk_fwd" if stage is None else "gdr_chunk_fwd_stage")
+        raise GdrError(rc, name)
     return o, s_final
 
 

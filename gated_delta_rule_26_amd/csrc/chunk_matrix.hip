@@ -678,9 +678,9 @@ template <bool KZ, bool DELTA>
 hipError_t launch_intra(const ChunkArgs &a) {
     const long total = chunk_slots(a);
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL((intra_matrix_kernel<KZ, DELTA>), dim3(intra_grid(total, 4)), dim3(kIntraThreads), 0, a.stream,
-                       static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), a.g, a.beta, a.T, a.H,
-                       a.NC, (int)total, a.eps, a.scale, static_cast<char *>(a.ws), a.tab);
+    GDR_LAUNCH((intra_matrix_kernel<KZ, DELTA>), dim3(intra_grid(total, 4)), dim3(kIntraThreads), a.stream, a.ev0,
+               a.ev1, static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), a.g, a.beta, a.T, a.H, a.NC,
+               (int)total, a.eps, a.scale, static_cast<char *>(a.ws), a.tab);
     return hipGetLastError();
 }
 
@@ -692,9 +692,8 @@ hipError_t launch_intra(const ChunkArgs &a) {
 // of those takes about as long as a round of walks with outputs (one per
 // unit), so the cost is (ceil(2 P BH NS / 2 CUs) + ceil(P BH NS / CUs)) / P
 // of the single walk's time.  P is the smallest power of two that minimises
-// that (planned for
-// 256 compute units so that the workspace size does not depend on the
-// device), with at least 32 chunks per segment.
+// that (planned for 256 compute units so that the workspace size does not
+// depend on the device), with at least 32 chunks per segment.
 int walk_segments(int BH, int NC) {
     constexpr double kPlanCUs = 256.0;
     int best = 1;
@@ -724,26 +723,25 @@ hipError_t launch_state(const ChunkArgs &a) {
                  *v = static_cast<const __bf16 *>(a.v);
     const char *ws = static_cast<const char *>(a.ws);
     if (P == 1) {
-        hipLaunchKernelGGL((state_matrix_kernel<OB, false, DELTA>), dim3((unsigned)(BH * NS)), dim3(kStateThreads), 0,
-                           a.stream, q, k, v, ws, a.s0, a.o, a.s_final, a.T, a.H, a.NC, BH, 1, a.NC, a.scale,
-                           a.tab);
+        GDR_LAUNCH((state_matrix_kernel<OB, false, DELTA>), dim3((unsigned)(BH * NS)), dim3(kStateThreads), a.stream,
+                   a.ev0, a.ev1, q, k, v, ws, a.s0, a.o, a.s_final, a.T, a.H, a.NC, BH, 1, a.NC, a.scale, a.tab);
         return hipGetLastError();
     }
     // segments: chunk maps, entering states, then the walks with outputs
     const int seg = (a.NC + P - 1) / P;
     float *tr = reinterpret_cast<float *>(static_cast<char *>(a.ws) + (size_t)BH * a.NC * kRecBytes);
     float *seg_state = tr + (size_t)BH * P * 2 * DK * DV;
-    hipLaunchKernelGGL((state_matrix_kernel<false, true, DELTA>), dim3((unsigned)(BH * P * 2 * NS)), dim3(kStateThreads), 0,
-                       a.stream, q, k, v, ws, nullptr, nullptr, tr, a.T, a.H, a.NC, BH * P, P, seg, a.scale,
-                       SeqTable{});
+    GDR_LAUNCH((state_matrix_kernel<false, true, DELTA>), dim3((unsigned)(BH * P * 2 * NS)), dim3(kStateThreads),
+               a.stream, a.ev0, nullptr, q, k, v, ws, nullptr, nullptr, tr, a.T, a.H, a.NC, BH * P, P, seg, a.scale,
+               SeqTable{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(segment_combine_kernel, dim3((unsigned)(BH * (DV / kCombineCols))), dim3(256), 0, a.stream, tr,
                        a.s0, seg_state, P);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((state_matrix_kernel<OB, false, DELTA>), dim3((unsigned)(BH * P * NS)), dim3(kStateThreads), 0,
-                       a.stream, q, k, v, ws, seg_state, a.o, a.s_final, a.T, a.H, a.NC, BH * P, P, seg, a.scale,
-                       SeqTable{});
+    GDR_LAUNCH((state_matrix_kernel<OB, false, DELTA>), dim3((unsigned)(BH * P * NS)), dim3(kStateThreads), a.stream,
+               nullptr, a.ev1, q, k, v, ws, seg_state, a.o, a.s_final, a.T, a.H, a.NC, BH * P, P, seg, a.scale,
+               SeqTable{});
     return hipGetLastError();
 }
 

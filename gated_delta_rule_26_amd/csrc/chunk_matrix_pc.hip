@@ -650,18 +650,18 @@ template <bool KZ, bool DELTA>
 hipError_t launch_intra_pc(const ChunkArgs &a) {
     const long total = chunk_slots(a);
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL((intra_pc_kernel<KZ, DELTA>), dim3(intra_grid(total, 2)), dim3(kIntraThreads), 0, a.stream,
-                       static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), a.g, a.beta, a.T, a.H,
-                       a.NC, (int)total, a.eps, a.scale, static_cast<char *>(a.ws), a.tab);
+    GDR_LAUNCH((intra_pc_kernel<KZ, DELTA>), dim3(intra_grid(total, 2)), dim3(kIntraThreads), a.stream, a.ev0, a.ev1,
+               static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), a.g, a.beta, a.T, a.H, a.NC,
+               (int)total, a.eps, a.scale, static_cast<char *>(a.ws), a.tab);
     return hipGetLastError();
 }
 
 template <bool OB, bool DELTA>
 hipError_t launch_state_pc(const ChunkArgs &a) {
     const int BH = a.B * a.H;
-    hipLaunchKernelGGL((state_pc_kernel<OB, DELTA>), dim3((unsigned)(BH * NS)), dim3(kStateThreads), 0, a.stream,
-                       static_cast<const __bf16 *>(a.v), static_cast<const char *>(a.ws), a.s0, a.o, a.s_final, a.T,
-                       a.H, a.NC, BH, a.tab);
+    GDR_LAUNCH((state_pc_kernel<OB, DELTA>), dim3((unsigned)(BH * NS)), dim3(kStateThreads), a.stream, a.ev0, a.ev1,
+               static_cast<const __bf16 *>(a.v), static_cast<const char *>(a.ws), a.s0, a.o, a.s_final, a.T, a.H, a.NC,
+               BH, a.tab);
     return hipGetLastError();
 }
 

@@ -154,10 +154,12 @@ int gdr_chunk_fwd_varlen_workspace_size(const gdr_desc *desc, size_t *bytes) {
 namespace {
 
 // stage: -1 = the whole chunked pass, 0 = intra kernel, 1 = state kernel.
-// cu_seqlens != NULL: a packed batch (the varlen entry point).
+// cu_seqlens != NULL: a packed batch (the varlen entry point).  ev0, ev1: a
+// timed stage (recorded when its first kernel begins and its last ends).
 int chunk_fwd_impl(int stage, const gdr_desc *d, const int32_t *cu_seqlens, const void *q, const void *k,
                    const void *v, const float *g, const float *beta_or_eta, const float *s0, void *o,
-                   float *s_final, void *workspace, size_t workspace_bytes, void *stream, bool packed = false) {
+                   float *s_final, void *workspace, size_t workspace_bytes, void *stream, bool packed = false,
+                   hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
     Sizes sz;
     int rc = check_desc(d, false, &sz, true, packed);
     if (rc != GDR_OK) return rc;
@@ -202,9 +204,15 @@ int chunk_fwd_impl(int stage, const gdr_desc *d, const int32_t *cu_seqlens, cons
     if (s0 && s_final && s0 != s_final && overlap(rs0, rsf)) return GDR_E_ALIAS;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
+    // a timed stage that does not go through the matrix-core launchers: the
+    // events bracket its launches on the stream
+    auto bracket = [&](hipEvent_t e) { return !e || hipEventRecord(e, st) == hipSuccess; };
     if (!have_tokens) {
-        if (stage == 0 || !s_final || s_final == s0) return GDR_OK;
-        return gdr::launch_state_init(s_final, s0, sz.state, st) == hipSuccess ? GDR_OK : GDR_E_HIP;
+        if (!bracket(ev0)) return GDR_E_HIP;
+        if (stage != 0 && s_final && s_final != s0 &&
+            gdr::launch_state_init(s_final, s0, sz.state, st) != hipSuccess)
+            return GDR_E_HIP;
+        return bracket(ev1) ? GDR_OK : GDR_E_HIP;
     }
 
     ChunkArgs a;
@@ -229,9 +237,14 @@ int chunk_fwd_impl(int stage, const gdr_desc *d, const int32_t *cu_seqlens, cons
     }
     int algo = resolve_algo(d);
     if (algo == GDR_ALGO_MATRIX && !matrix_path_available(d)) algo = GDR_ALGO_VECTOR;
-    const hipError_t e =
-        algo == GDR_ALGO_MATRIX ? gdr::launch_chunk_matrix(a, stage) : gdr::launch_chunk_vector(a, stage);
-    return e == hipSuccess ? GDR_OK : GDR_E_HIP;
+    if (algo == GDR_ALGO_MATRIX) {
+        a.ev0 = ev0;
+        a.ev1 = ev1;
+        return gdr::launch_chunk_matrix(a, stage) == hipSuccess ? GDR_OK : GDR_E_HIP;
+    }
+    if (!bracket(ev0)) return GDR_E_HIP;
+    if (gdr::launch_chunk_vector(a, stage) != hipSuccess) return GDR_E_HIP;
+    return bracket(ev1) ? GDR_OK : GDR_E_HIP;
 }
 
 // The recurrent schedule: one token (gdr_recurrent_step, desc->T ignored) or
@@ -376,6 +389,17 @@ int gdr_chunk_fwd_stage(int stage, const gdr_desc *d, const void *q, const void 
     if (stage != GDR_STAGE_INTRA && stage != GDR_STAGE_STATE) return GDR_E_MODE;
     return chunk_fwd_impl(stage, d, nullptr, q, k, v, g, beta_or_eta, s0, o, s_final, workspace,
                           workspace_bytes, stream);
+}
+
+int gdr_chunk_fwd_stage_timed(int stage, const gdr_desc *d, const void *q, const void *k, const void *v,
+                              const float *g, const float *beta_or_eta, const float *s0, void *o, float *s_final,
+                              void *workspace, size_t workspace_bytes, void *stream, void *start_event,
+                              void *stop_event) {
+    if (stage != GDR_STAGE_INTRA && stage != GDR_STAGE_STATE) return GDR_E_MODE;
+    if (!start_event || !stop_event) return GDR_E_NULL;
+    return chunk_fwd_impl(stage, d, nullptr, q, k, v, g, beta_or_eta, s0, o, s_final, workspace,
+                          workspace_bytes, stream, false, static_cast<hipEvent_t>(start_event),
+                          static_cast<hipEvent_t>(stop_event));
 }
 
 int gdr_recurrent_step(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,

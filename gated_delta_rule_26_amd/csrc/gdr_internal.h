@@ -1,6 +1,7 @@
 // Internal declarations shared by the libgdr sources (not part of the ABI).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -45,7 +46,19 @@ struct ChunkArgs {
     float *s_final;          // may be NULL
     void *ws;
     hipStream_t stream;
+    hipEvent_t ev0 = nullptr;  // a timed stage: recorded when its first kernel begins
+    hipEvent_t ev1 = nullptr;  //   and when its last kernel ends
 };
+
+// Kernel launch that records E0 when the kernel begins and E1 when it ends
+// (hipExtLaunchKernelGGL) if either is non-null; otherwise a plain launch.
+#define GDR_LAUNCH(K, GRID, BLOCK, STREAM, E0, E1, ...)                                        \
+    do {                                                                                       \
+        if ((E0) || (E1))                                                                      \
+            hipExtLaunchKernelGGL(K, GRID, BLOCK, 0, STREAM, E0, E1, 0, __VA_ARGS__);          \
+        else                                                                                   \
+            hipLaunchKernelGGL(K, GRID, BLOCK, 0, STREAM, __VA_ARGS__);                        \
+    } while (0)
 
 // Number of chunk records (chunks times heads) the kernels are launched for.
 inline long chunk_slots(const ChunkArgs &a) {

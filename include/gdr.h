@@ -238,6 +238,24 @@ int gdr_chunk_fwd_stage(int stage, const gdr_desc *desc,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gdr_chunk_fwd_stage with the stage's kernel time recorded, for measurement:
+ * start_event and stop_event are hipEvent_t handles created by the caller
+ * with timing enabled (both required, else GDR_E_NULL).  On the matrix-core
+ * path the stage's first kernel records start_event when it begins and its
+ * last kernel records stop_event when it ends (hipExtLaunchKernelGGL), so
+ * hipEventElapsedTime gives the kernels' time without the launch gap before
+ * them; on the other paths the events are recorded on the stream before and
+ * after the stage's launches.  Everything else (arguments, validation,
+ * results) is exactly gdr_chunk_fwd_stage.  The events are only written.
+ */
+int gdr_chunk_fwd_stage_timed(int stage, const gdr_desc *desc,
+                              const void *q, const void *k, const void *v,
+                              const float *g, const float *beta_or_eta,
+                              const float *s0, void *o, float *s_final,
+                              void *workspace, size_t workspace_bytes, void *stream,
+                              void *start_event, void *stop_event);
+
+/*
  * One fused recurrent step for B = N independent sequences (decode): the
  * seven steps above for a single token, with the state read once and written
  * once (blog summary, "Kernel Triton recurrente fusionado": decay, predict,

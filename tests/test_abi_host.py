@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
     lib = gdr.load_library()
     names = declared_functions()
     assert names == sorted(["gdr_abi_version", "gdr_status_string", "gdr_chunk_fwd_workspace_size",
-                            "gdr_chunk_fwd", "gdr_chunk_fwd_stage", "gdr_recurrent_step",
+                            "gdr_chunk_fwd", "gdr_chunk_fwd_stage", "gdr_chunk_fwd_stage_timed", "gdr_recurrent_step",
                             "gdr_recurrent_fwd", "gdr_chunk_fwd_varlen", "gdr_chunk_fwd_varlen_workspace_size",
                             "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_size"])
     for n in names:
@@ -123,6 +123,15 @@ def test_chunk_validation_errors():
                                    wsb, None) == E["GDR_E_MODE"]
     assert lib.gdr_chunk_fwd_stage(0, ctypes.byref(d), None, P(2), P(3), P(4), P(5), None, P(6), P(7), P(8),
                                    wsb, None) == E["GDR_E_NULL"]
+    # the timed stage: the same checks, and both events are required
+    assert lib.gdr_chunk_fwd_stage_timed(2, ctypes.byref(d), P(1), P(2), P(3), P(4), P(5), None, P(6), P(7),
+                                         P(8), wsb, None, P(10), P(11)) == E["GDR_E_MODE"]
+    assert lib.gdr_chunk_fwd_stage_timed(1, ctypes.byref(d), P(1), P(2), P(3), P(4), P(5), None, P(6), P(7),
+                                         P(8), wsb, None, None, P(11)) == E["GDR_E_NULL"]
+    assert lib.gdr_chunk_fwd_stage_timed(1, ctypes.byref(d), P(1), P(2), P(3), P(4), P(5), None, P(6), P(7),
+                                         P(8), wsb, None, P(10), None) == E["GDR_E_NULL"]
+    assert lib.gdr_chunk_fwd_stage_timed(0, ctypes.byref(d), None, P(2), P(3), P(4), P(5), None, P(6), P(7),
+                                         P(8), wsb, None, P(10), P(11)) == E["GDR_E_NULL"]
 
 
 def test_delta_off_ignores_beta_and_its_mode():
