@@ -94,6 +94,8 @@ def load_library(path: str | None = None):
     lib.gdr_chunk_fwd_stage_timed.argtypes = [ctypes.c_int, D, V, V, V, V, V, V, V, V, V, ctypes.c_size_t, V, V, V]
     lib.gdr_recurrent_step.restype = ctypes.c_int
     lib.gdr_recurrent_step.argtypes = [D, V, V, V, V, V, V, V, V]
+    lib.gdr_recurrent_step_timed.restype = ctypes.c_int
+    lib.gdr_recurrent_step_timed.argtypes = [D, V, V, V, V, V, V, V, V, V, V]
     lib.gdr_recurrent_fwd.restype = ctypes.c_int
     lib.gdr_recurrent_fwd.argtypes = [D, V, V, V, V, V, V, V, V]
     if path is None:
@@ -218,12 +220,14 @@ def chunk_fwd(q, k, v, g, beta, *, per_channel: bool = False, kaczmarz: bool = F
 
 def recurrent_step(q, k, v, g, beta, state, *, per_channel: bool = False, kaczmarz: bool = False,
                    eps: float = 0.0, scale: float = 1.0, o=None, o_dtype=None, stream=None,
-                   delta_off: bool = False):
+                   delta_off: bool = False, events=None):
     """One fused decode step through ``gdr_recurrent_step``.
 
     q, k [N,H,Dk], v [N,H,Dv] (float32 or bfloat16); g float32 [N,H] or
     [N,H,Dk]; beta float32 [N,H] (None with ``delta_off``); state float32
-    [N,H,Dk,Dv], updated in place.  Returns o [N,H,Dv].
+    [N,H,Dk,Dv], updated in place.  Returns o [N,H,Dv].  ``events``: a pair of
+    recorded torch.cuda.Event(enable_timing=True) that the step's kernel
+    records when it begins and ends (``gdr_recurrent_step_timed``).
     """
     lib = load_library()
     dev = q.device
@@ -248,10 +252,17 @@ def recurrent_step(q, k, v, g, beta, state, *, per_channel: bool = False, kaczma
     desc = make_desc(N, 1, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=o_dtype, per_channel=per_channel,
                      kaczmarz=kaczmarz, eps=eps, scale=scale, delta_off=delta_off)
     st = stream if stream is not None else torch.cuda.current_stream(dev)
-    rc = lib.gdr_recurrent_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                _ptr(state), _ptr(o), ctypes.c_void_p(st.cuda_stream))
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
+            ctypes.c_void_p(st.cuda_stream))
+    if events is None:
+        rc, name = lib.gdr_recurrent_step(*args), "gdr_recurrent_step"
+    else:
+        e0, e1 = (ctypes.c_void_p(e.cuda_event) for e in events)
+        if not e0.value or not e1.value:
+            raise ValueError("record each event once before passing it")
+        rc, name = lib.gdr_recurrent_step_timed(*args, e0, e1), "gdr_recurrent_step_timed"
     if rc != 0:
-        raise GdrError(rc, "gdr_recurrent_step")
+        raise GdrError(rc, name)
     return o
 
 

@@ -250,12 +250,18 @@ int chunk_fwd_impl(int stage, const gdr_desc *d, const int32_t *cu_seqlens, cons
 // The recurrent schedule: one token (gdr_recurrent_step, desc->T ignored) or
 // desc->T tokens per sequence (gdr_recurrent_fwd).
 int recurrent_impl(const gdr_desc *d, bool one_token, const void *q, const void *k, const void *v, const float *g,
-                   const float *beta_or_eta, float *state, void *o, void *stream) {
+                   const float *beta_or_eta, float *state, void *o, void *stream, hipEvent_t ev0 = nullptr,
+                   hipEvent_t ev1 = nullptr) {
     Sizes sz;
     const int rc = check_desc(d, true, &sz, one_token);
     if (rc != GDR_OK) return rc;
     const int T = one_token ? 1 : d->T;
-    if (d->B == 0 || d->H == 0 || T == 0) return GDR_OK;
+    if (d->B == 0 || d->H == 0 || T == 0) {  // nothing to launch: a timed call still records its events
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        if (ev0 && hipEventRecord(ev0, st) != hipSuccess) return GDR_E_HIP;
+        if (ev1 && hipEventRecord(ev1, st) != hipSuccess) return GDR_E_HIP;
+        return GDR_OK;
+    }
     const bool delta = d->delta_mode == GDR_DELTA_RULE;
     if (!delta) beta_or_eta = nullptr;
     if (!q || !k || !v || !g || (delta && !beta_or_eta) || !state || !o) return GDR_E_NULL;
@@ -285,6 +291,8 @@ int recurrent_impl(const gdr_desc *d, bool one_token, const void *q, const void 
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta_or_eta;
     a.state = state; a.o = o;
     a.stream = static_cast<hipStream_t>(stream);
+    a.ev0 = ev0;
+    a.ev1 = ev1;
     return gdr::launch_recurrent_step(a) == hipSuccess ? GDR_OK : GDR_E_HIP;
 }
 
@@ -405,6 +413,14 @@ int gdr_chunk_fwd_stage_timed(int stage, const gdr_desc *d, const void *q, const
 int gdr_recurrent_step(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
                        const float *beta_or_eta, float *state, void *o, void *stream) {
     return recurrent_impl(d, true, q, k, v, g, beta_or_eta, state, o, stream);
+}
+
+int gdr_recurrent_step_timed(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
+                             const float *beta_or_eta, float *state, void *o, void *stream, void *start_event,
+                             void *stop_event) {
+    if (!start_event || !stop_event) return GDR_E_NULL;
+    return recurrent_impl(d, true, q, k, v, g, beta_or_eta, state, o, stream, static_cast<hipEvent_t>(start_event),
+                          static_cast<hipEvent_t>(stop_event));
 }
 
 int gdr_recurrent_fwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,

@@ -76,6 +76,7 @@ struct StepArgs {
     float *state;
     void *o;
     hipStream_t stream;
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;  // a timed step: recorded when the kernel begins and ends
 };
 
 // Vector-ALU chunked path (fp32 arithmetic, any input dtype).

@@ -171,9 +171,8 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
 template <int DK, int DV, bool PC, bool KZ, bool IB, bool OB>
 hipError_t launch_t(const StepArgs &a) {
     const unsigned grid = static_cast<unsigned>(a.N) * static_cast<unsigned>(a.H);
-    hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, PC, KZ, IB, OB>), dim3(grid), dim3(kThreads),
-                       0, a.stream, a.q, a.k, a.v, a.g, a.beta, a.state, a.o, a.T, a.H, a.eps, a.scale,
-                       a.delta);
+    GDR_LAUNCH((recurrent_step_kernel<DK, DV, PC, KZ, IB, OB>), dim3(grid), dim3(kThreads), a.stream, a.ev0, a.ev1,
+               a.q, a.k, a.v, a.g, a.beta, a.state, a.o, a.T, a.H, a.eps, a.scale, a.delta);
     return hipGetLastError();
 }
 

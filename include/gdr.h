@@ -276,6 +276,20 @@ int gdr_recurrent_step(const gdr_desc *desc,
                        float *state, void *o, void *stream);
 
 /*
+ * gdr_recurrent_step with its kernel time recorded, for measurement: the
+ * step's kernel records start_event (a caller-created hipEvent_t with timing
+ * enabled) when it begins and stop_event when it ends (hipExtLaunchKernelGGL);
+ * both are required (else GDR_E_NULL).  With nothing to launch (B = 0 or
+ * H = 0) both are recorded on the stream.  Everything else is exactly
+ * gdr_recurrent_step.
+ */
+int gdr_recurrent_step_timed(const gdr_desc *desc,
+                             const void *q, const void *k, const void *v,
+                             const float *g, const float *beta_or_eta,
+                             float *state, void *o, void *stream,
+                             void *start_event, void *stop_event);
+
+/*
  * The fused recurrent schedule over desc->T tokens of B sequences (short
  * prefills, several decode tokens at once): token after token as in
  * gdr_recurrent_step, with the state read once before the first token and

@@ -29,6 +29,7 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert names == sorted(["gdr_abi_version", "gdr_status_string", "gdr_chunk_fwd_workspace_size",
                             "gdr_chunk_fwd", "gdr_chunk_fwd_stage", "gdr_chunk_fwd_stage_timed", "gdr_recurrent_step",
+                            "gdr_recurrent_step_timed",
                             "gdr_recurrent_fwd", "gdr_chunk_fwd_varlen", "gdr_chunk_fwd_varlen_workspace_size",
                             "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_size"])
     for n in names:
