@@ -88,6 +88,10 @@ def load_library(path: str | None = None):
     lib.gdr_chunk_bwd_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdr_chunk_bwd.restype = ctypes.c_int
     lib.gdr_chunk_bwd.argtypes = [D] + [V] * 15 + [ctypes.c_size_t, V]
+    lib.gdr_chunk_bwd_varlen_workspace_size.restype = ctypes.c_int
+    lib.gdr_chunk_bwd_varlen_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_chunk_bwd_varlen.restype = ctypes.c_int
+    lib.gdr_chunk_bwd_varlen.argtypes = [D] + [V] * 16 + [ctypes.c_size_t, V]
     lib.gdr_chunk_fwd_stage.restype = ctypes.c_int
     lib.gdr_chunk_fwd_stage.argtypes = [ctypes.c_int, D, V, V, V, V, V, V, V, V, V, ctypes.c_size_t, V]
     lib.gdr_chunk_fwd_stage_timed.restype = ctypes.c_int
@@ -427,4 +431,70 @@ def chunk_bwd(q, k, v, g, beta, d_o, *, per_channel: bool = False, kaczmarz: boo
                            workspace.numel(), ctypes.c_void_p(st.cuda_stream))
     if rc != 0:
         raise GdrError(rc, "gdr_chunk_bwd")
+    return out
+
+
+def chunk_bwd_varlen_workspace_size(desc: Desc) -> int:
+    out = ctypes.c_size_t(0)
+    rc = load_library().gdr_chunk_bwd_varlen_workspace_size(ctypes.byref(desc), ctypes.byref(out))
+    if rc != 0:
+        raise GdrError(rc, "gdr_chunk_bwd_varlen_workspace_size")
+    return int(out.value)
+
+
+def chunk_bwd_varlen(q, k, v, g, beta, d_o, cu_seqlens, *, per_channel: bool = False, kaczmarz: bool = False,
+                     eps: float = 0.0, scale: float = 1.0, s0=None, ds_final=None, need_ds0: bool = True,
+                     workspace=None, stream=None, delta_off: bool = False):
+    """Backward pass of ``chunk_fwd_varlen`` through ``gdr_chunk_bwd_varlen``.
+
+    Token tensors [T,H,..] of N packed sequences (cu_seqlens int32 [N+1] on
+    the device) as for chunk_fwd_varlen, d_o float32 [T,H,Dv]; s0, ds_final
+    float32 [N,H,Dk,Dv] or None.  Returns a dict of float32 tensors dq, dk, dv,
+    dg, dbeta (None with ``delta_off``) and ds0 (None unless ``need_ds0``);
+    gradients of tokens outside every sequence are left unwritten.
+    """
+    lib = load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _check_dev("cu_seqlens", cu_seqlens, dev, torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-d int32 tensor of N + 1 entries")
+    N = cu_seqlens.numel() - 1
+    _check_dev("q", q, dev)
+    _check_dev("k", k, dev, q.dtype, (T, H, Dk))
+    _check_dev("v", v, dev, q.dtype, (T, H, Dv))
+    gshape = (T, H, Dk) if per_channel else (T, H)
+    _check_dev("g", g, dev, torch.float32, gshape)
+    if delta_off:
+        beta = None
+    else:
+        _check_dev("beta", beta, dev, torch.float32, (T, H))
+    _check_dev("d_o", d_o, dev, torch.float32, (T, H, Dv))
+    if s0 is not None:
+        _check_dev("s0", s0, dev, torch.float32, (N, H, Dk, Dv))
+    if ds_final is not None:
+        _check_dev("ds_final", ds_final, dev, torch.float32, (N, H, Dk, Dv))
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.zeros((T, H, Dk), **f32), "dk": torch.zeros((T, H, Dk), **f32),
+           "dv": torch.zeros((T, H, Dv), **f32), "dg": torch.zeros(gshape, **f32),
+           "dbeta": None if delta_off else torch.zeros((T, H), **f32),
+           "ds0": torch.empty((N, H, Dk, Dv), **f32) if need_ds0 else None}
+    desc = make_desc(N, T, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=torch.float32, per_channel=per_channel,
+                     kaczmarz=kaczmarz, eps=eps, scale=scale, delta_off=delta_off)
+    need = chunk_bwd_varlen_workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _check_dev("workspace", workspace, dev, torch.uint8)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    rc = lib.gdr_chunk_bwd_varlen(ctypes.byref(desc), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                  _ptr(beta), _ptr(s0), _ptr(d_o), _ptr(ds_final), _ptr(out["dq"]),
+                                  _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
+                                  _ptr(out["ds0"]), _ptr(workspace), workspace.numel(),
+                                  ctypes.c_void_p(st.cuda_stream))
+    if rc != 0:
+        raise GdrError(rc, "gdr_chunk_bwd_varlen")
     return out

@@ -53,7 +53,7 @@ constexpr int kThreads = 256;
 constexpr int kBV = 32;  // value columns per walk workgroup
 constexpr int kBS = 16;  // value columns per slice of grads A
 
-// ---- workspace, per chunk slot ci = (b H + h) NC + c
+// ---- workspace, per chunk slot ci (fixed-length: (b H + h) NC + c; packed: u H + h)
 struct BwdWs {
     float *T, *A, *M, *G, *beta;   // C x C (three), C x GK, C
     float *S, *dS;                 // DK x DV: entering state; gradient of the chunk-end state
@@ -91,20 +91,69 @@ size_t bwd_bytes(size_t slots) {
            ((size_t)5 * C * C + 2 * (size_t)C * GK + GK + C + 2 * (size_t)DK * DV + 3 * (size_t)C * DK);
 }
 
-// chunk slot ci -> (b, h, c), token row of its token 0, token count
+// chunk slot ci -> token row of its token 0 and token count.  Fixed-length
+// batch: ci = (b H + h) NC + c; packed batch: ci = u H + h for chunk u of the
+// sequence table (its slots past the table's chunks are not used).
 struct Slot {
-    int b, h, c, n;
-    size_t row0;  // [B, T, H, .] row of token 0; token i is row0 + i H
+    int n;
+    size_t row0;  // [.., H, .] row of token 0; token i is row0 + i H
 };
-__device__ __forceinline__ Slot slot_of(int ci, int T, int H, int NC) {
+__device__ __forceinline__ Slot slot_of(int ci, int T, int H, int NC, const SeqTable &tb) {
     Slot s;
-    s.c = ci % NC;
-    const int bh = ci / NC;
-    s.b = bh / H;
-    s.h = bh % H;
-    s.n = min(C, T - s.c * C);
-    s.row0 = ((size_t)s.b * T + (size_t)s.c * C) * H + s.h;
+    if (tb.start) {
+        const int u = ci / H, h = ci - u * H;
+        const int t0 = tb.tok[u];
+        s.n = min(C, tb.start[tb.seq[u] + 1] - t0);
+        s.row0 = (size_t)t0 * H + h;
+    } else {
+        const int c = ci % NC, bh = ci / NC;
+        s.n = min(C, T - c * C);
+        s.row0 = ((size_t)(bh / H) * T + (size_t)c * C) * H + bh % H;
+    }
     return s;
+}
+// Chunk slots of a launch over every chunk: packed batches have fewer than
+// the grid (the chunk bound); the workgroups past them return.
+__device__ __forceinline__ bool slot_used(int ci, int H, const SeqTable &tb) {
+    return !tb.start || ci < tb.cbase[tb.N] * H;
+}
+
+// The chunks one walk covers: sequence b = bh / H, head h = bh % H; chunk c
+// of it has slot slot(c), token row row0(c) and count(c) tokens.
+struct BwdWalk {
+    SeqTable tb;
+    int nc, H, h, cb, tend, T;
+    size_t slot0, row00;  // fixed-length batch: slot and token row of chunk 0
+    __device__ __forceinline__ size_t slot(int c) const {
+        return tb.start ? (size_t)(cb + c) * H + h : slot0 + c;
+    }
+    __device__ __forceinline__ size_t row0(int c) const {
+        return tb.start ? (size_t)tb.tok[cb + c] * H + h : row00 + (size_t)c * C * H;
+    }
+    __device__ __forceinline__ int count(int c) const {
+        return tb.start ? min(C, tend - tb.tok[cb + c]) : min(C, T - c * C);
+    }
+};
+__device__ __forceinline__ BwdWalk bwd_walk(int bh, int T, int H, int NC, const SeqTable &tb) {
+    BwdWalk w;
+    w.tb = tb;
+    w.H = H;
+    w.h = bh % H;
+    w.T = T;
+    const int b = bh / H;
+    if (tb.start) {
+        w.cb = tb.cbase[b];
+        w.nc = tb.cbase[b + 1] - w.cb;
+        w.tend = tb.start[b + 1];
+        w.slot0 = w.row00 = 0;
+    } else {
+        w.cb = 0;
+        w.nc = NC;
+        w.tend = T;
+        w.slot0 = (size_t)bh * NC;
+        w.row00 = (size_t)b * T * H + w.h;
+    }
+    return w;
 }
 
 // ============================================================ fp32 matrix-core tiles
@@ -148,11 +197,12 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, int T, int H, int NC, float eps, float scale, float *__restrict__ wT,
     float *__restrict__ wA, float *__restrict__ wM, float *__restrict__ wG, float *__restrict__ wB,
-    float *__restrict__ wKt, float *__restrict__ wKh, float *__restrict__ wQt, bool delta) {
+    float *__restrict__ wKt, float *__restrict__ wKh, float *__restrict__ wQt, bool delta, SeqTable tb) {
     constexpr int GK = PC ? DK : 1;
     static_assert(2 * C * (DK + 1) >= 16 * mx::kTile, "the R and T tiles must fit where k and q were");
     const int ci = blockIdx.x;
-    const Slot sl = slot_of(ci, T, H, NC);
+    if (!slot_used(ci, H, tb)) return;
+    const Slot sl = slot_of(ci, T, H, NC, tb);
     const int n = sl.n;
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
@@ -346,13 +396,13 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
                                                               const float *__restrict__ wKt,
                                                               const float *__restrict__ wKh,
                                                               const float *__restrict__ s0, float *__restrict__ wS,
-                                                              bool delta) {
+                                                              bool delta, SeqTable tb) {
     constexpr int GK = PC ? DK : 1;
     constexpr int NT = DV / kBV;
     constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads;
     constexpr int SRB = DK / 64;  // state row blocks per wavefront
     const int tile = blockIdx.x % NT, bh = blockIdx.x / NT;
-    const int b = bh / H, h = bh % H;
+    const BwdWalk wk = bwd_walk(bh, T, H, NC, tb);
     const int j0 = tile * kBV;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -367,9 +417,9 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
     float rT[NTT], rKt[NKK], rKh[NKK], rB = 0.f, rGam = 0.f;
     f32x4 rV[2];  // the v slice in the layout of this wavefront's X tiles
     auto fetch = [&](int c) {
-        const size_t ci = (size_t)bh * NC + c;
-        const int n = min(C, T - c * C);
-        const size_t row0 = ((size_t)b * T + (size_t)c * C) * H + h;
+        const size_t ci = wk.slot(c);
+        const int n = wk.count(c);
+        const size_t row0 = wk.row0(c);
 #pragma unroll
         for (int u = 0; u < NTT; ++u) rT[u] = wT[ci * C * C + tid + u * kThreads];
 #pragma unroll
@@ -393,9 +443,9 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
         const int r = idx / kBV, cc = idx % kBV;
         sS[r * kLB + cc] = s0 ? s0[sbase + (size_t)r * DV + j0 + cc] : 0.f;
     }
-    if (NC > 0) fetch(0);
-    for (int c = 0; c < NC; ++c) {
-        const size_t ci = (size_t)bh * NC + c;
+    if (wk.nc > 0) fetch(0);
+    for (int c = 0; c < wk.nc; ++c) {
+        const size_t ci = wk.slot(c);
         __syncthreads();  // the previous chunk's reads are done; sS holds the entering state
         float *Sg = wS + ci * DK * DV;
         for (int idx = tid; idx < DK * kBV; idx += kThreads) {
@@ -417,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
             sT[i * kLT + m] = rT[u] * sBeta[m];
         }
         f32x4 x[2] = {rV[0], rV[1]};
-        if (c + 1 < NC) fetch(c + 1);
+        if (c + 1 < wk.nc) fetch(c + 1);
         // X = V - K~ S (rows 16w ..; X = V without the delta rule)
         for (int kk = 0; delta && kk < DK; kk += 4) {
             const float a = -sKt[(16 * w + lr) * kLK + kk + lg];
@@ -482,13 +532,13 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
                                                                const float *__restrict__ wQt,
                                                                const float *__restrict__ ds_final,
                                                                float *__restrict__ wdS, float *__restrict__ ds0,
-                                                               bool delta) {
+                                                               bool delta, SeqTable tb) {
     constexpr int GK = PC ? DK : 1;
     constexpr int NT = DV / kBV;
     constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads, NVV = C * kBV / kThreads;
     constexpr int SRB = DK / 64;
     const int tile = blockIdx.x % NT, bh = blockIdx.x / NT;
-    const int b = bh / H, h = bh % H;
+    const BwdWalk wk = bwd_walk(bh, T, H, NC, tb);
     const int j0 = tile * kBV;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -502,9 +552,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
 
     float rT[NTT], rA[NTT], rKt[NKK], rKh[NKK], rQt[NKK], rO[NVV], rB = 0.f, rGam = 0.f;
     auto fetch_a = [&](int c) {  // operands of dE, dX and the output gradient slice
-        const size_t ci = (size_t)bh * NC + c;
-        const int n = min(C, T - c * C);
-        const size_t row0 = ((size_t)b * T + (size_t)c * C) * H + h;
+        const size_t ci = wk.slot(c);
+        const int n = wk.count(c);
+        const size_t row0 = wk.row0(c);
 #pragma unroll
         for (int u = 0; u < NTT; ++u) {
             rT[u] = wT[ci * C * C + tid + u * kThreads];
@@ -522,11 +572,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
     };
     auto fetch_q = [&](int c) {
 #pragma unroll
-        for (int u = 0; u < NKK; ++u) rQt[u] = wQt[((size_t)bh * NC + c) * C * DK + tid + u * kThreads];
+        for (int u = 0; u < NKK; ++u) rQt[u] = wQt[wk.slot(c) * C * DK + tid + u * kThreads];
     };
     auto fetch_k = [&](int c) {
 #pragma unroll
-        for (int u = 0; u < NKK; ++u) rKt[u] = wKt[((size_t)bh * NC + c) * C * DK + tid + u * kThreads];
+        for (int u = 0; u < NKK; ++u) rKt[u] = wKt[wk.slot(c) * C * DK + tid + u * kThreads];
     };
 
     const size_t sbase = (size_t)bh * DK * DV;
@@ -534,13 +584,13 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
         const int r = idx / kBV, cc = idx % kBV;
         sdS[r * kLB + cc] = ds_final ? ds_final[sbase + (size_t)r * DV + j0 + cc] : 0.f;
     }
-    if (NC > 0) {
-        fetch_a(NC - 1);
-        fetch_q(NC - 1);
-        fetch_k(NC - 1);
+    if (wk.nc > 0) {
+        fetch_a(wk.nc - 1);
+        fetch_q(wk.nc - 1);
+        fetch_k(wk.nc - 1);
     }
-    for (int c = NC - 1; c >= 0; --c) {
-        const size_t ci = (size_t)bh * NC + c;
+    for (int c = wk.nc - 1; c >= 0; --c) {
+        const size_t ci = wk.slot(c);
         __syncthreads();  // sdS holds dS' of this chunk; the previous chunk's reads are done
         float *dSg = wdS + ci * DK * DV;
         for (int idx = tid; idx < DK * kBV; idx += kThreads) {
@@ -671,13 +721,14 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
     const float *__restrict__ wB, const float *__restrict__ wS, const float *__restrict__ wdS,
     const float *__restrict__ wKt, const float *__restrict__ wKh, const float *__restrict__ wQt,
     float *__restrict__ wdA, float *__restrict__ wdTT, float *__restrict__ wdG, float *__restrict__ wdG63,
-    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv, bool delta) {
+    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv, bool delta, SeqTable tb) {
     constexpr int GK = PC ? DK : 1;
     constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads;
     constexpr int NSS = DK * kBS / kThreads, NVS = C * kBS / kThreads;
     constexpr int JK = DK / 16;  // column tiles of the C x DK accumulators
     const int ci = blockIdx.x;
-    const Slot sl = slot_of(ci, T, H, NC);
+    if (!slot_used(ci, H, tb)) return;
+    const Slot sl = slot_of(ci, T, H, NC, tb);
     const int n = sl.n;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -914,7 +965,8 @@ __global__ __launch_bounds__(kThreads, IN_BF16 && !PC ? 2 : 1) void bwd_grads_b_
     const float *__restrict__ wT, const float *__restrict__ wM, const float *__restrict__ wA,
     const float *__restrict__ wG, const float *__restrict__ wB, const float *__restrict__ wdA,
     const float *__restrict__ wdTT, const float *__restrict__ wdG, const float *__restrict__ wdG63,
-    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dg, float *__restrict__ dbeta) {
+    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dg, float *__restrict__ dbeta,
+    SeqTable tb) {
     constexpr int GK = PC ? DK : 1;
     constexpr int LC = C + 1;                  // row stride of the C x C buffers
     constexpr int LQ = DK + 1;                 // row stride of the C x DK buffers
@@ -930,7 +982,8 @@ __global__ __launch_bounds__(kThreads, IN_BF16 && !PC ? 2 : 1) void bwd_grads_b_
     constexpr int KQ16_END = R2 + (C * LQB > 2 * C * LC ? C * LQB : 2 * C * LC);
     constexpr int kSmem = KQ16 ? KQ16_END : (QOFF + C * LQ > 3 * C * LC ? QOFF + C * LQ : 3 * C * LC);
     const int ci = blockIdx.x;
-    const Slot sl = slot_of(ci, T, H, NC);
+    if (!slot_used(ci, H, tb)) return;
+    const Slot sl = slot_of(ci, T, H, NC, tb);
     const int n = sl.n;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -1270,27 +1323,29 @@ __global__ __launch_bounds__(kThreads, IN_BF16 && !PC ? 2 : 1) void bwd_grads_b_
 // ============================================================ launch
 template <int DK, int DV, bool PC, bool KZ, bool IB>
 hipError_t launch_bwd_t(const BwdArgs &a) {
-    const size_t slots = (size_t)a.B * a.H * a.NC;
+    // packed batch: a.NC is the chunk bound of all sequences together
+    const size_t slots = (size_t)(a.tab.start ? 1 : a.B) * a.H * a.NC;
     BwdWs w = carve_bwd<DK, DV, PC>(a.ws, slots);
     const unsigned nslot = (unsigned)slots;
     const unsigned nwalk = (unsigned)(a.B * a.H * (DV / kBV));
     hipLaunchKernelGGL((bwd_prep_kernel<DK, PC, KZ, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.q, a.k, a.g,
-                       a.beta, a.T, a.H, a.NC, a.eps, a.scale, w.T, w.A, w.M, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.delta);
+                       a.beta, a.T, a.H, a.NC, a.eps, a.scale, w.T, w.A, w.M, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.delta,
+                       a.tab);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_states_kernel<DK, DV, PC, IB>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.v, a.T, a.H,
-                       a.NC, w.T, w.G, w.beta, w.Kt, w.Kh, a.s0, w.S, a.delta);
+                       a.NC, w.T, w.G, w.beta, w.Kt, w.Kh, a.s0, w.S, a.delta, a.tab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dstates_kernel<DK, DV, PC>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.dO, a.T, a.H,
-                       a.NC, w.T, w.A, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.ds_final, w.dS, a.ds0, a.delta);
+                       a.NC, w.T, w.A, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.ds_final, w.dS, a.ds0, a.delta, a.tab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grads_a_kernel<DK, DV, PC, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.v, a.dO, a.T,
                        a.H, a.NC, a.scale, w.T, w.A, w.G, w.beta, w.S, w.dS, w.Kt, w.Kh, w.Qt, w.dA, w.dTT, w.dG,
-                       w.dG63, a.dq, a.dk, a.dv, a.delta);
+                       w.dG63, a.dq, a.dk, a.dv, a.delta, a.tab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grads_b_kernel<DK, PC, KZ, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.q, a.k,
                        a.T, a.H, a.NC, a.eps, a.scale, w.T, w.M, w.A, w.G, w.beta, w.dA, w.dTT, w.dG, w.dG63, a.dq,
-                       a.dk, a.dg, a.dbeta);
+                       a.dk, a.dg, a.dbeta, a.tab);
     return hipGetLastError();
 }
 

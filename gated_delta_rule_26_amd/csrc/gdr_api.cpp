@@ -314,29 +314,42 @@ int gdr_chunk_fwd_varlen(const gdr_desc *d, const int32_t *cu_seqlens, const voi
                           stream, true);
 }
 
-int gdr_chunk_bwd_workspace_size(const gdr_desc *d, size_t *bytes) {
+// Workspace of the backward pass: for a packed batch the sequence table
+// first, then the per-chunk records of the chunk bound times H slots.
+static int bwd_workspace(const gdr_desc *d, bool packed, size_t *bytes, size_t *table) {
     if (!bytes) return GDR_E_NULL;
     Sizes sz;
-    const int rc = check_desc(d, false, &sz);
+    const int rc = check_desc(d, false, &sz, true, packed);
     if (rc != GDR_OK) return rc;
-    const long NC = chunk_count(d, false);
-    if ((size_t)d->B * d->H * (size_t)NC >= ((size_t)1 << 31)) return GDR_E_SHAPE;
-    *bytes = gdr::chunk_bwd_workspace_bytes(d->B, d->H, (int)NC, d->Dk, d->Dv,
-                                            d->decay_mode == GDR_DECAY_PER_CHANNEL);
+    const long NC = chunk_count(d, packed);
+    const int Bw = packed ? 1 : d->B;
+    if ((size_t)Bw * d->H * (size_t)NC >= ((size_t)1 << 31)) return GDR_E_SHAPE;
+    const size_t tab = packed ? gdr::seq_table_bytes(d->B, (int)NC) : 0;
+    *bytes = tab + gdr::chunk_bwd_workspace_bytes(Bw, d->H, (int)NC, d->Dk, d->Dv,
+                                                  d->decay_mode == GDR_DECAY_PER_CHANNEL);
+    if (table) *table = tab;
     return GDR_OK;
 }
 
-int gdr_chunk_bwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
-                  const float *beta_or_eta, const float *s0, const float *d_o, const float *ds_final, float *dq,
-                  float *dk, float *dv, float *dg, float *dbeta, float *ds0, void *workspace,
-                  size_t workspace_bytes, void *stream) {
+int gdr_chunk_bwd_workspace_size(const gdr_desc *d, size_t *bytes) { return bwd_workspace(d, false, bytes, nullptr); }
+
+int gdr_chunk_bwd_varlen_workspace_size(const gdr_desc *d, size_t *bytes) {
+    return bwd_workspace(d, true, bytes, nullptr);
+}
+
+static int chunk_bwd_impl(const gdr_desc *d, const int32_t *cu_seqlens, const void *q, const void *k,
+                          const void *v, const float *g, const float *beta_or_eta, const float *s0, const float *d_o,
+                          const float *ds_final, float *dq, float *dk, float *dv, float *dg, float *dbeta, float *ds0,
+                          void *workspace, size_t workspace_bytes, void *stream, bool packed) {
     Sizes sz;
-    int rc = check_desc(d, false, &sz);
+    int rc = check_desc(d, false, &sz, true, packed);
     if (rc != GDR_OK) return rc;
-    size_t need = 0;
-    rc = gdr_chunk_bwd_workspace_size(d, &need);
+    size_t need = 0, table = 0;
+    rc = bwd_workspace(d, packed, &need, &table);
     if (rc != GDR_OK) return rc;
     if (d->B == 0 || d->H == 0) return GDR_OK;
+    if (packed && !cu_seqlens) return GDR_E_NULL;
+    if (packed && !aligned(cu_seqlens, 4)) return GDR_E_ALIGN;
     const bool pc = d->decay_mode == GDR_DECAY_PER_CHANNEL;
     const size_t in_es = d->qkv_dtype == GDR_BF16 ? 2 : 4;
     const bool have_tokens = d->T > 0;
@@ -359,7 +372,8 @@ int gdr_chunk_bwd(const gdr_desc *d, const void *q, const void *k, const void *v
     const Range ins[] = {range_of(q, tq), range_of(k, tq), range_of(v, tv),
                          range_of(g, have_tokens ? sz.g * 4 : 0), range_of(beta_or_eta, have_tokens ? sz.beta * 4 : 0),
                          range_of(d_o, have_tokens ? sz.o * 4 : 0), range_of(s0, s0 ? sz.state * 4 : 0),
-                         range_of(ds_final, ds_final ? sz.state * 4 : 0)};
+                         range_of(ds_final, ds_final ? sz.state * 4 : 0),
+                         range_of(cu_seqlens, packed ? ((size_t)d->B + 1) * 4 : 0)};
     const Range outs[] = {range_of(dq, have_tokens ? sz.qk * 4 : 0), range_of(dk, have_tokens ? sz.qk * 4 : 0),
                           range_of(dv, have_tokens ? sz.v * 4 : 0), range_of(dg, have_tokens ? sz.g * 4 : 0),
                           range_of(dbeta, have_tokens ? sz.beta * 4 : 0), range_of(ds0, ds0 ? sz.state * 4 : 0),
@@ -377,7 +391,7 @@ int gdr_chunk_bwd(const gdr_desc *d, const void *q, const void *k, const void *v
     }
     gdr::BwdArgs a;
     a.B = d->B; a.T = d->T; a.H = d->H; a.Dk = d->Dk; a.Dv = d->Dv;
-    a.NC = (int)chunk_count(d, false);
+    a.NC = (int)chunk_count(d, packed);
     a.qkv_bf16 = d->qkv_dtype == GDR_BF16;
     a.per_channel = pc;
     a.delta = delta;
@@ -388,7 +402,29 @@ int gdr_chunk_bwd(const gdr_desc *d, const void *q, const void *k, const void *v
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.ds0 = ds0;
     a.ws = workspace;
     a.stream = st;
+    if (packed) {  // the sequence table first; the records after it
+        if (gdr::launch_seq_table(cu_seqlens, d->B, d->T, workspace, st) != hipSuccess) return GDR_E_HIP;
+        a.tab = gdr::seq_table(workspace, d->B, a.NC);
+        a.tab.N = d->B;
+        a.ws = static_cast<char *>(workspace) + table;
+    }
     return gdr::launch_chunk_bwd(a) == hipSuccess ? GDR_OK : GDR_E_HIP;
+}
+
+int gdr_chunk_bwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
+                  const float *beta_or_eta, const float *s0, const float *d_o, const float *ds_final, float *dq,
+                  float *dk, float *dv, float *dg, float *dbeta, float *ds0, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    return chunk_bwd_impl(d, nullptr, q, k, v, g, beta_or_eta, s0, d_o, ds_final, dq, dk, dv, dg, dbeta, ds0,
+                          workspace, workspace_bytes, stream, false);
+}
+
+int gdr_chunk_bwd_varlen(const gdr_desc *d, const int32_t *cu_seqlens, const void *q, const void *k, const void *v,
+                         const float *g, const float *beta_or_eta, const float *s0, const float *d_o,
+                         const float *ds_final, float *dq, float *dk, float *dv, float *dg, float *dbeta, float *ds0,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    return chunk_bwd_impl(d, cu_seqlens, q, k, v, g, beta_or_eta, s0, d_o, ds_final, dq, dk, dv, dg, dbeta, ds0,
+                          workspace, workspace_bytes, stream, true);
 }
 
 int gdr_chunk_fwd_stage(int stage, const gdr_desc *d, const void *q, const void *k, const void *v,

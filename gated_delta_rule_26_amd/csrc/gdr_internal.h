@@ -95,7 +95,8 @@ hipError_t launch_chunk_matrix_pc(const ChunkArgs &a, int stage);
 
 // Validated arguments of gdr_chunk_bwd (fixed-length batches).
 struct BwdArgs {
-    int B, T, H, Dk, Dv, NC;
+    int B, T, H, Dk, Dv, NC;     // packed batch: B = N sequences, T = tokens in all, NC = the chunk bound
+    SeqTable tab;                // packed batches only
     bool qkv_bf16, per_channel, kaczmarz;
     bool delta;                                  // false: additive write (beta and dbeta are NULL)
     float eps, scale;

@@ -187,7 +187,8 @@ int gdr_chunk_fwd_varlen(const gdr_desc *desc, const int32_t *cu_seqlens,
  * chunked mode the training mode); it is reverse-mode differentiation of the
  * chunk algebra of gdr_chunk_fwd, with the chunk-entering states recomputed.
  * fp32 arithmetic (products on fp32 matrix-core tiles); fixed-length
- * batches; desc->algo and desc->o_dtype are ignored.  With GDR_DELTA_OFF
+ * batches (packed ones: gdr_chunk_bwd_varlen below); desc->algo and
+ * desc->o_dtype are ignored.  With GDR_DELTA_OFF
  * (the additive write) beta_or_eta and dbeta are ignored and may be NULL.
  *
  *   q, k, v, g, beta_or_eta, s0   as for gdr_chunk_fwd (s0 may be NULL)
@@ -213,6 +214,29 @@ int gdr_chunk_bwd(const gdr_desc *desc,
                   float *dq, float *dk, float *dv, float *dg, float *dbeta,
                   float *ds0, void *workspace, size_t workspace_bytes,
                   void *stream);
+
+/*
+ * Backward pass of gdr_chunk_fwd_varlen: a packed batch of N = desc->B
+ * sequences of different lengths, desc->T tokens in all, sequence n holding
+ * tokens [cu_seqlens[n], cu_seqlens[n+1]) and its own state (training on
+ * packed sequences).  Tensors as for gdr_chunk_fwd_varlen: token tensors
+ * [T, H, ..] (q, k, v, g, beta_or_eta, d_o in; dq, dk, dv, dg, dbeta out),
+ * states [N, H, Dk, Dv] (s0 and ds_final in, may be NULL; ds0 out, may be
+ * NULL); cu_seqlens [N + 1] int32 in device memory, read on the device only,
+ * with entries clamped as gdr_chunk_fwd_varlen clamps them (gradients of
+ * tokens outside every sequence are not written).  Every sequence gets the
+ * gradients gdr_chunk_bwd gives for it alone.  The workspace holds the
+ * sequence table and the per-chunk records of floor((T + 63 N) / 64) chunks
+ * per head; cu_seqlens must not overlap an output or the workspace.
+ */
+int gdr_chunk_bwd_varlen_workspace_size(const gdr_desc *desc, size_t *bytes);
+int gdr_chunk_bwd_varlen(const gdr_desc *desc, const int32_t *cu_seqlens,
+                         const void *q, const void *k, const void *v,
+                         const float *g, const float *beta_or_eta, const float *s0,
+                         const float *d_o, const float *ds_final,
+                         float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                         float *ds0, void *workspace, size_t workspace_bytes,
+                         void *stream);
 
 /*
  * One stage of gdr_chunk_fwd, with the same arguments.  The chunked path is a

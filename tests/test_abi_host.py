@@ -31,7 +31,8 @@ def test_exports_every_declared_symbol():
                             "gdr_chunk_fwd", "gdr_chunk_fwd_stage", "gdr_chunk_fwd_stage_timed", "gdr_recurrent_step",
                             "gdr_recurrent_step_timed",
                             "gdr_recurrent_fwd", "gdr_chunk_fwd_varlen", "gdr_chunk_fwd_varlen_workspace_size",
-                            "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_size"])
+                            "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd_varlen",
+                            "gdr_chunk_bwd_varlen_workspace_size"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -312,3 +313,33 @@ def test_backward_without_delta_rule_needs_no_beta():
     rc = lib.gdr_chunk_bwd(ctypes.byref(d), P(1), P(2), P(3), P(4), None, None, P(9), None, P(10), P(11), P(12),
                            P(13), None, None, None, n.value, None)
     assert rc == E["GDR_E_WORKSPACE"]
+
+
+def test_backward_varlen_workspace_and_validation():
+    """A packed batch for the backward: the sequence table, then one backward
+    slot per head for each of the floor((T + 63 N) / 64) chunks."""
+    lib = gdr.load_library()
+    n = ctypes.c_size_t(0)
+
+    def ws(desc):
+        rc = lib.gdr_chunk_bwd_varlen_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+        return rc, n.value
+
+    N, T, H = 5, 1000, 3
+    nc = (T + 63 * N) // 64
+    table = -(-4 * (2 * (N + 1) + 2 * nc) // 256) * 256
+    slot = 4 * (5 * 4096 + 2 * 64 + 1 + 64 + 2 * 128 * 128 + 3 * 64 * 128)
+    assert ws(_desc(B=N, T=T, H=H)) == (0, table + nc * H * slot)
+    d = _desc(B=N, T=T, H=H)
+    wsb = ws(d)[1]
+
+    def call(cu=P(20), q=P(1), w=P(8), dq=P(10)):
+        return lib.gdr_chunk_bwd_varlen(ctypes.byref(d), cu, q, P(2), P(3), P(4), P(5), None, P(9), None, dq,
+                                        P(11), P(12), P(13), P(14), None, w, wsb, None)
+
+    assert call(cu=None) == E["GDR_E_NULL"]
+    assert call(cu=P(20, 2)) == E["GDR_E_ALIGN"]
+    assert call(cu=P(10, 64)) == E["GDR_E_ALIAS"]    # cu_seqlens inside dq
+    assert call(q=None) == E["GDR_E_NULL"]
+    assert call(w=None) == E["GDR_E_WORKSPACE"]
+
