@@ -102,6 +102,8 @@ def load_library(path: str | None = None):
     lib.gdr_recurrent_step_timed.argtypes = [D, V, V, V, V, V, V, V, V, V, V]
     lib.gdr_recurrent_fwd.restype = ctypes.c_int
     lib.gdr_recurrent_fwd.argtypes = [D, V, V, V, V, V, V, V, V]
+    lib.gdr_recurrent_fwd_varlen.restype = ctypes.c_int
+    lib.gdr_recurrent_fwd_varlen.argtypes = [D, V, V, V, V, V, V, V, V, V]
     if path is None:
         _lib = lib
     return lib
@@ -498,3 +500,49 @@ def chunk_bwd_varlen(q, k, v, g, beta, d_o, cu_seqlens, *, per_channel: bool = F
     if rc != 0:
         raise GdrError(rc, "gdr_chunk_bwd_varlen")
     return out
+
+
+def recurrent_fwd_varlen(q, k, v, g, beta, state, cu_seqlens, *, per_channel: bool = False,
+                         kaczmarz: bool = False, eps: float = 0.0, scale: float = 1.0, o=None, o_dtype=None,
+                         stream=None, delta_off: bool = False):
+    """Recurrent tokens of N packed sequences through ``gdr_recurrent_fwd_varlen``.
+
+    q, k [T,H,Dk], v [T,H,Dv] hold the tokens of N sequences back to back
+    (cu_seqlens int32 [N+1] on the device); g float32 [T,H] or [T,H,Dk]; beta
+    float32 [T,H] (None with ``delta_off``); state float32 [N,H,Dk,Dv],
+    updated in place.  Returns o [T,H,Dv] (tokens outside every sequence are
+    left unwritten).
+    """
+    lib = load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _check_dev("cu_seqlens", cu_seqlens, dev, torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-d int32 tensor of N + 1 entries")
+    N = cu_seqlens.numel() - 1
+    _check_dev("q", q, dev)
+    _check_dev("k", k, dev, q.dtype, (T, H, Dk))
+    _check_dev("v", v, dev, q.dtype, (T, H, Dv))
+    _check_dev("g", g, dev, torch.float32, (T, H, Dk) if per_channel else (T, H))
+    if delta_off:
+        beta = None
+    else:
+        _check_dev("beta", beta, dev, torch.float32, (T, H))
+    _check_dev("state", state, dev, torch.float32, (N, H, Dk, Dv))
+    o_dtype = o_dtype or q.dtype
+    if o is None:
+        o = torch.empty((T, H, Dv), dtype=o_dtype, device=dev)
+    else:
+        _check_dev("o", o, dev, o_dtype, (T, H, Dv))
+    desc = make_desc(N, T, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=o_dtype, per_channel=per_channel,
+                     kaczmarz=kaczmarz, eps=eps, scale=scale, delta_off=delta_off)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    rc = lib.gdr_recurrent_fwd_varlen(ctypes.byref(desc), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                      _ptr(beta), _ptr(state), _ptr(o), ctypes.c_void_p(st.cuda_stream))
+    if rc != 0:
+        raise GdrError(rc, "gdr_recurrent_fwd_varlen")
+    return o
+

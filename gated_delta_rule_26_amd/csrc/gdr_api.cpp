@@ -251,11 +251,15 @@ int chunk_fwd_impl(int stage, const gdr_desc *d, const int32_t *cu_seqlens, cons
 // desc->T tokens per sequence (gdr_recurrent_fwd).
 int recurrent_impl(const gdr_desc *d, bool one_token, const void *q, const void *k, const void *v, const float *g,
                    const float *beta_or_eta, float *state, void *o, void *stream, hipEvent_t ev0 = nullptr,
-                   hipEvent_t ev1 = nullptr) {
+                   hipEvent_t ev1 = nullptr, const int32_t *cu_seqlens = nullptr, bool packed = false) {
     Sizes sz;
-    const int rc = check_desc(d, true, &sz, one_token);
+    const int rc = check_desc(d, true, &sz, one_token, packed);
     if (rc != GDR_OK) return rc;
     const int T = one_token ? 1 : d->T;
+    if (d->B > 0 && d->H > 0 && packed) {
+        if (!cu_seqlens) return GDR_E_NULL;
+        if (!aligned(cu_seqlens, 4)) return GDR_E_ALIGN;
+    }
     if (d->B == 0 || d->H == 0 || T == 0) {  // nothing to launch: a timed call still records its events
         hipStream_t st = static_cast<hipStream_t>(stream);
         if (ev0 && hipEventRecord(ev0, st) != hipSuccess) return GDR_E_HIP;
@@ -274,7 +278,8 @@ int recurrent_impl(const gdr_desc *d, bool one_token, const void *q, const void 
     const Range rq = range_of(q, sz.qk * in_es), rk = range_of(k, sz.qk * in_es), rv = range_of(v, sz.v * in_es);
     const Range rg = range_of(g, sz.g * 4), rb = range_of(beta_or_eta, sz.beta * 4);
     const Range rs = range_of(state, sz.state * 4), ro = range_of(o, sz.o * out_es);
-    const Range ins[] = {rq, rk, rv, rg, rb};
+    const Range rcu = range_of(cu_seqlens, packed ? ((size_t)d->B + 1) * 4 : 0);
+    const Range ins[] = {rq, rk, rv, rg, rb, rcu};
     for (const Range &r : ins)
         if (overlap(r, rs) || overlap(r, ro)) return GDR_E_ALIAS;
     if (overlap(rs, ro)) return GDR_E_ALIAS;
@@ -293,6 +298,7 @@ int recurrent_impl(const gdr_desc *d, bool one_token, const void *q, const void 
     a.stream = static_cast<hipStream_t>(stream);
     a.ev0 = ev0;
     a.ev1 = ev1;
+    a.cu = packed ? cu_seqlens : nullptr;
     return gdr::launch_recurrent_step(a) == hipSuccess ? GDR_OK : GDR_E_HIP;
 }
 
@@ -462,6 +468,12 @@ int gdr_recurrent_step_timed(const gdr_desc *d, const void *q, const void *k, co
 int gdr_recurrent_fwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
                       const float *beta_or_eta, float *state, void *o, void *stream) {
     return recurrent_impl(d, false, q, k, v, g, beta_or_eta, state, o, stream);
+}
+
+int gdr_recurrent_fwd_varlen(const gdr_desc *d, const int32_t *cu_seqlens, const void *q, const void *k,
+                             const void *v, const float *g, const float *beta_or_eta, float *state, void *o,
+                             void *stream) {
+    return recurrent_impl(d, false, q, k, v, g, beta_or_eta, state, o, stream, nullptr, nullptr, cu_seqlens, true);
 }
 
 }  // extern "C"

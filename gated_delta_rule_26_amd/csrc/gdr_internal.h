@@ -77,6 +77,7 @@ struct StepArgs {
     void *o;
     hipStream_t stream;
     hipEvent_t ev0 = nullptr, ev1 = nullptr;  // a timed step: recorded when the kernel begins and ends
+    const int *cu = nullptr;  // packed batch: N + 1 token offsets (device), T = tokens in all
 };
 
 // Vector-ALU chunked path (fp32 arithmetic, any input dtype).

@@ -37,7 +37,7 @@ template <int DK, int DV, bool PC, bool KZ, bool IN_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ state,
-    void *__restrict__ o, int T, int H, float eps, float scale, bool delta) {
+    void *__restrict__ o, int T, int H, float eps, float scale, bool delta, const int *__restrict__ cu) {
     constexpr int TPR = DV / 4;          // threads per state row (one float4 each)
     constexpr int RPP = kThreads / TPR;  // rows per pass of the workgroup
     constexpr int PASSES = DK / RPP;
@@ -66,8 +66,21 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
     for (int p = 0; p < PASSES; ++p)
         s[p] = *reinterpret_cast<const float4 *>(S + (size_t)(p * RPP + r0) * DV + 4 * c4);
 
-    // token t of this (sequence, head): row (n T + t) H + h of q, k, v, g, beta
-    auto row_of = [&](int t) { return ((size_t)n * T + t) * H + h; };
+    // token t of this (sequence, head): row (n T + t) H + h of q, k, v, g,
+    // beta; in a packed batch (cu != NULL, T tokens in all) row (t0 + t) H + h
+    // for the sequence's first token t0, its tokens [cu[n], cu[n+1]) with each
+    // offset clamped to [0, T] and raised to the largest one before it
+    size_t first = (size_t)n * T;
+    if (cu) {
+        int m = 0, t0 = 0;
+        for (size_t i = 0; i <= n + 1; ++i) {
+            m = max(m, min(max(cu[i], 0), T));
+            if (i == n) t0 = m;
+        }
+        first = t0;
+        T = m - t0;
+    }
+    auto row_of = [&](int t) { return (first + t) * H + h; };
     float kin = 0.f, qin = 0.f, gin = 0.f, bin = 1.f, gsc = 0.f;
     float4 vin;
     auto fetch = [&](int t) {  // token t's inputs into registers
@@ -172,7 +185,7 @@ template <int DK, int DV, bool PC, bool KZ, bool IB, bool OB>
 hipError_t launch_t(const StepArgs &a) {
     const unsigned grid = static_cast<unsigned>(a.N) * static_cast<unsigned>(a.H);
     GDR_LAUNCH((recurrent_step_kernel<DK, DV, PC, KZ, IB, OB>), dim3(grid), dim3(kThreads), a.stream, a.ev0, a.ev1,
-               a.q, a.k, a.v, a.g, a.beta, a.state, a.o, a.T, a.H, a.eps, a.scale, a.delta);
+               a.q, a.k, a.v, a.g, a.beta, a.state, a.o, a.T, a.H, a.eps, a.scale, a.delta, a.cu);
     return hipGetLastError();
 }
 

@@ -337,6 +337,23 @@ int gdr_recurrent_fwd(const gdr_desc *desc,
                       const float *g, const float *beta_or_eta,
                       float *state, void *o, void *stream);
 
+/*
+ * gdr_recurrent_fwd over a packed batch (serving: a few tokens of each of N
+ * requests of different lengths in one call).  desc->B = N sequences,
+ * desc->T = tokens of all of them; sequence n is tokens [cu_seqlens[n],
+ * cu_seqlens[n+1]) of q, k, v [T, H, ..], g, beta_or_eta [T, H(, Dk)] and o
+ * [T, H, Dv], and owns state [n] of state [N, H, Dk, Dv] (updated in place).
+ * cu_seqlens [N + 1] int32 in device memory, read on the device only: each
+ * offset is clamped to [0, T] and raised to the largest one before it, so
+ * no entry addresses memory out of bounds (an empty sequence keeps its
+ * state; outputs of tokens outside every sequence are not written).
+ * cu_seqlens must not overlap state or o.
+ */
+int gdr_recurrent_fwd_varlen(const gdr_desc *desc, const int32_t *cu_seqlens,
+                             const void *q, const void *k, const void *v,
+                             const float *g, const float *beta_or_eta,
+                             float *state, void *o, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

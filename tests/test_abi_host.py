@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
                             "gdr_recurrent_step_timed",
                             "gdr_recurrent_fwd", "gdr_chunk_fwd_varlen", "gdr_chunk_fwd_varlen_workspace_size",
                             "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd_varlen",
-                            "gdr_chunk_bwd_varlen_workspace_size"])
+                            "gdr_chunk_bwd_varlen_workspace_size", "gdr_recurrent_fwd_varlen"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -342,4 +342,18 @@ def test_backward_varlen_workspace_and_validation():
     assert call(cu=P(10, 64)) == E["GDR_E_ALIAS"]    # cu_seqlens inside dq
     assert call(q=None) == E["GDR_E_NULL"]
     assert call(w=None) == E["GDR_E_WORKSPACE"]
+
+
+def test_recurrent_fwd_varlen_validation():
+    lib = gdr.load_library()
+    d = _desc(B=4, T=37, H=2)
+
+    def call(cu=P(20), q=P(1), st=P(7), o=P(6)):
+        return lib.gdr_recurrent_fwd_varlen(ctypes.byref(d), cu, q, P(2), P(3), P(4), P(5), st, o, None)
+
+    assert call(cu=None) == E["GDR_E_NULL"]
+    assert call(cu=P(20, 2)) == E["GDR_E_ALIGN"]
+    assert call(cu=P(7, 64)) == E["GDR_E_ALIAS"]     # cu_seqlens inside the state
+    assert call(q=None) == E["GDR_E_NULL"]
+    assert call(o=P(7)) == E["GDR_E_ALIAS"]          # o on top of the state
 

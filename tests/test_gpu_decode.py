@@ -5,7 +5,7 @@ import torch
 
 import gated_delta_rule_26_amd as gdr
 import oracle
-from gdr_inputs import WORKLOADS, decode_state0, decode_step_inputs
+from gdr_inputs import WORKLOADS, decode_state0, decode_step_inputs, random_inputs
 from tests.gpu_util import DEV, TOL, host, rel, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -172,3 +172,34 @@ def test_recurrent_fwd_zero_tokens_is_a_no_op():
     o = gdr.recurrent_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], state)
     torch.cuda.synchronize()
     assert o.shape == (2, 0, 2, 64) and torch.equal(state, d["s0"])
+
+
+@pytest.mark.parametrize("mode", ["gdn", "kda", "kla"])
+def test_recurrent_fwd_varlen_matches_each_sequence_alone(mode):
+    """Packed requests of different lengths (an empty one included) on the
+    recurrent schedule: each sequence's outputs and final state equal the
+    oracle's for that sequence alone."""
+    m = dict(per_channel=mode == "kda", kaczmarz=mode == "kla")
+    lens = [3, 0, 1, 17, 64, 5]
+    T, H, D = sum(lens), 2, 128
+    x = random_inputs(7400 + len(mode), 1, T, H, D, D, dtype="bf16",
+                      key_norm="lognormal_norm" if mode == "kla" else "unit", with_s0=False, **m)
+    x = {key: (val[0] if val is not None else None) for key, val in x.items()}
+    rng = np.random.default_rng(7401)
+    s0 = (rng.standard_normal((len(lens), H, D, D)) * 0.1).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    d = to_dev(x, "bf16")
+    state = torch.from_numpy(s0).to(DEV)
+    eps = 1e-6 if m["kaczmarz"] else 0.0
+    o = gdr.recurrent_fwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], state, torch.from_numpy(cu).to(DEV),
+                                 o_dtype=torch.float32, eps=eps, **m)
+    torch.cuda.synchronize()
+    for n in range(len(lens)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        sl = {key: x[key][None, a:b] for key in ("q", "k", "v", "g", "beta")}
+        o_ref, s_ref = oracle.oracle_fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], s0=s0[n:n + 1], eps=eps,
+                                         **m)
+        es = rel(host(state[n]), s_ref[0])
+        eo = rel(host(o[a:b]), o_ref[0]) if b > a else 0.0
+        print(f"recurrent varlen {mode} sequence {n} (length {b - a}): rel o {eo:.2e} S {es:.2e}")
+        assert eo < TOL["bf16"] and es < TOL["bf16"], (n, eo, es)
