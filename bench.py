@@ -51,8 +51,8 @@ MEASURED_TRAFFIC = {
                                           + 1190090.9 * 2.0 + 1049605.1) * 1024),
     ("matrix", "intra", "kla_prefill"): (_SCALAR, "1201aa5d5a5c21bade99c648bf2f392684dd1b326e6f5069491ae747917431a3",
                                          (656170.9 * 2.0 + 802816.0) * 1024),
-    ("decode", "step", "decode"): (_DECODE, "d95cdb4ade6f5f5e28c9f763a67dd8d994546380ce9e0a79ea14ec92052d8c69",
-                                   (132967.5 * 2.0 + 264192.0) * 1024),
+    ("decode", "step", "decode"): (_DECODE, "ff6af95675f820ab6aee79b825e824dd5de086030a6ac1b84f64cea9600f3e0a",
+                                   (132972.4 * 2.0 + 264192.0) * 1024),
 }
 
 
