@@ -36,21 +36,21 @@ _SCALAR = ("gated_delta_rule_26_amd/csrc/chunk_matrix.hip", "gated_delta_rule_26
 _PER_CHANNEL = ("gated_delta_rule_26_amd/csrc/chunk_matrix_pc.hip", "gated_delta_rule_26_amd/csrc/matrix_common.h")
 _DECODE = ("gated_delta_rule_26_amd/csrc/recurrent_step.hip",)
 MEASURED_TRAFFIC = {
-    ("matrix", "state", "gdn_prefill"): (_SCALAR, "1201aa5d5a5c21bade99c648bf2f392684dd1b326e6f5069491ae747917431a3",
-                                         (148668.1 * 2.0 + 135172.0) * 1024),
-    ("matrix", "intra", "gdn_prefill"): (_SCALAR, "1201aa5d5a5c21bade99c648bf2f392684dd1b326e6f5069491ae747917431a3",
-                                         (66878.3 * 2.0 + 100352.0) * 1024),
-    ("matrix", "state", "kda_prefill"): (_PER_CHANNEL, "5fa637086ce22f9ad3197d83cf323512cc2301b645444e630104e2467b41a93b",
-                                         (279778.3 * 2.0 + 133120.0) * 1024),
-    ("matrix", "intra", "kda_prefill"): (_PER_CHANNEL, "5fa637086ce22f9ad3197d83cf323512cc2301b645444e630104e2467b41a93b",
-                                         (134565.2 * 2.0 + 493568.0) * 1024),
+    ("matrix", "state", "gdn_prefill"): (_SCALAR, "4c7a4f5d2ac673e3b353b7d5545d145eaa2b619a18e3f53ced3437b273e43536",
+                                         (148668.0 * 2.0 + 135171.4) * 1024),
+    ("matrix", "intra", "gdn_prefill"): (_SCALAR, "4c7a4f5d2ac673e3b353b7d5545d145eaa2b619a18e3f53ced3437b273e43536",
+                                         (66815.8 * 2.0 + 100352.0) * 1024),
+    ("matrix", "state", "kda_prefill"): (_PER_CHANNEL, "c169a618a16b18c91e6fd2407dc6a11459d69f474008326c3e482928bc74c54c",
+                                         (279778.8 * 2.0 + 133120.0) * 1024),
+    ("matrix", "intra", "kda_prefill"): (_PER_CHANNEL, "c169a618a16b18c91e6fd2407dc6a11459d69f474008326c3e482928bc74c54c",
+                                         (134593.4 * 2.0 + 493568.1) * 1024),
     # the state phase of the long sequence is three launches: the segment transfer walk, the
     # combine of the entering states and the per-segment walk
-    ("matrix", "state", "kla_prefill"): (_SCALAR, "1201aa5d5a5c21bade99c648bf2f392684dd1b326e6f5069491ae747917431a3",
-                                         (732134.9 * 2.0 + 8192.0 + 15398.7 * 2.0 + 4096.0
-                                          + 1190090.9 * 2.0 + 1049605.1) * 1024),
-    ("matrix", "intra", "kla_prefill"): (_SCALAR, "1201aa5d5a5c21bade99c648bf2f392684dd1b326e6f5069491ae747917431a3",
-                                         (656170.9 * 2.0 + 802816.0) * 1024),
+    ("matrix", "state", "kla_prefill"): (_SCALAR, "4c7a4f5d2ac673e3b353b7d5545d145eaa2b619a18e3f53ced3437b273e43536",
+                                         (730910.4 * 2.0 + 8192.0 + 15398.6 * 2.0 + 4096.0
+                                          + 1190090.4 * 2.0 + 1049612.7) * 1024),
+    ("matrix", "intra", "kla_prefill"): (_SCALAR, "4c7a4f5d2ac673e3b353b7d5545d145eaa2b619a18e3f53ced3437b273e43536",
+                                         (656909.6 * 2.0 + 802816.0) * 1024),
     ("decode", "step", "decode"): (_DECODE, "ff6af95675f820ab6aee79b825e824dd5de086030a6ac1b84f64cea9600f3e0a",
                                    (132972.4 * 2.0 + 264192.0) * 1024),
 }
@@ -61,13 +61,13 @@ MEASURED_TRAFFIC = {
 # (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) per second.  The issued flops count every bf16 hi/lo product, so they
 # exceed the algorithmic flops.  (files, sha, busy fraction, issued TFLOP/s), as for the traffic.
 MEASURED_MFMA = {
-    ("matrix", "state", "gdn_prefill"): (_SCALAR, "1201aa5d5a5c21bade99c648bf2f392684dd1b326e6f5069491ae747917431a3",
-                                         0.192, 452.1),
-    ("matrix", "state", "kda_prefill"): (_PER_CHANNEL, "5fa637086ce22f9ad3197d83cf323512cc2301b645444e630104e2467b41a93b",
-                                         0.080, 198.4),
+    ("matrix", "state", "gdn_prefill"): (_SCALAR, "4c7a4f5d2ac673e3b353b7d5545d145eaa2b619a18e3f53ced3437b273e43536",
+                                         0.187, 452.2),
+    ("matrix", "state", "kda_prefill"): (_PER_CHANNEL, "c169a618a16b18c91e6fd2407dc6a11459d69f474008326c3e482928bc74c54c",
+                                         0.079, 197.2),
     # the long sequence: transfer + combine + walk, weighted by duration
-    ("matrix", "state", "kla_prefill"): (_SCALAR, "1201aa5d5a5c21bade99c648bf2f392684dd1b326e6f5069491ae747917431a3",
-                                         0.245, 537.3),
+    ("matrix", "state", "kla_prefill"): (_SCALAR, "4c7a4f5d2ac673e3b353b7d5545d145eaa2b619a18e3f53ced3437b273e43536",
+                                         0.243, 537.6),
 }
 
 
