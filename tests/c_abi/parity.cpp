@@ -2,7 +2,9 @@
 // device memory with the HIP runtime, calls libgdr through include/gdr.h and
 // checks the results against the fp64 oracle (liboracle, test
 // infrastructure).  Cases: chunked prefill with scalar decay (Gated DeltaNet)
-// and per-channel decay (KDA) on the matrix-core path, and one decode step.
+// and per-channel decay (KDA) on the matrix-core path, one decode step, and a
+// packed batch of sequences of different lengths (one empty) through the
+// chunked and the recurrent entry points for packed batches.
 // Inputs are seeded synthetic data drawn here with SplitMix64 (Steele, Lea
 // and Flood 2014) and Box-Muller normals; both sides read the same values.
 // Exit status 0 when every case is within the relative L2 bar for bf16
@@ -181,6 +183,58 @@ bool decode_case() {
     return eo < 2e-3 && es < 2e-3;
 }
 
+// Packed batch: N sequences with cu_seqlens in device memory, token tensors
+// [T, H, D], states [N, H, D, D]; each sequence against the oracle run on its
+// own tokens and initial state.
+bool varlen_case(bool recurrent) {
+    const int N = 4, H = 2, D = 128;
+    const std::vector<int32_t> cu = {0, 0, 70, 71, 200};  // lengths 0, 70, 1, 129
+    const int T = cu.back();
+    const Inputs x = make_inputs(recurrent ? 5 : 4, 1, T, H, D, false);
+    const std::vector<float> s0 = make_inputs(recurrent ? 7 : 6, N, 1, H, D, false).s0;  // [N, H, D, D]
+    gdr_desc d = make_desc(N, T, H, D, false, recurrent ? GDR_ALGO_AUTO : GDR_ALGO_MATRIX);
+    size_t ws_bytes = 0;
+    if (!recurrent && gdr_chunk_fwd_varlen_workspace_size(&d, &ws_bytes) != GDR_OK) return false;
+    Dev<uint16_t> q(x.q.size()), k(x.k.size()), v(x.v.size());
+    Dev<float> g(x.g.size()), beta(x.beta.size()), st(s0.size()), o((size_t)T * H * D), sf(s0.size());
+    Dev<int32_t> cud(cu.size());
+    Dev<unsigned char> ws(ws_bytes);
+    if (!q.p || !k.p || !v.p || !g.p || !beta.p || !st.p || !o.p || !sf.p || !cud.p || !ws.p) return false;
+    if (!q.put(x.q) || !k.put(x.k) || !v.put(x.v) || !g.put(x.g) || !beta.put(x.beta) || !st.put(s0) || !cud.put(cu))
+        return false;
+    const int rc = recurrent
+                       ? gdr_recurrent_fwd_varlen(&d, cud.p, q.p, k.p, v.p, g.p, beta.p, st.p, o.p, nullptr)
+                       : gdr_chunk_fwd_varlen(&d, cud.p, q.p, k.p, v.p, g.p, beta.p, st.p, o.p, sf.p, ws.p, ws_bytes,
+                                              nullptr);
+    if (rc != GDR_OK) {
+        std::fprintf(stderr, "varlen: %s\n", gdr_status_string(rc));
+        return false;
+    }
+    if (!hip_ok(hipDeviceSynchronize(), "sync")) return false;
+    std::vector<float> oh, sh;
+    if (!o.get(oh) || !(recurrent ? st.get(sh) : sf.get(sh))) return false;
+    bool ok = true;
+    const size_t ss = (size_t)H * D * D;
+    for (int n = 0; n < N; ++n) {
+        const long L = cu[n + 1] - cu[n];
+        const size_t t0 = (size_t)cu[n] * H * D;
+        std::vector<double> oref((size_t)L * H * D), sref(ss);
+        if (L > 0 && gdr_oracle_fwd(1, L, H, D, D, x.qf.data() + t0, x.kf.data() + t0, x.vf.data() + t0,
+                                    x.g.data() + (size_t)cu[n] * H, x.beta.data() + (size_t)cu[n] * H, 0, 0, 0.0,
+                                    1.0, 0, s0.data() + n * ss, oref.data(), sref.data(), nullptr, 0, 0) != 0)
+            return false;
+        if (L == 0)
+            for (size_t i = 0; i < ss; ++i) sref[i] = s0[n * ss + i];
+        const std::vector<float> on(oh.begin() + t0, oh.begin() + t0 + (size_t)L * H * D);
+        const std::vector<float> sn(sh.begin() + n * ss, sh.begin() + (n + 1) * ss);
+        const double eo = L > 0 ? rel_l2(on, oref) : 0.0, es = rel_l2(sn, sref);
+        std::printf("c-abi %s varlen, sequence %d (%ld tokens): rel-L2 o %.2e, S %.2e\n",
+                    recurrent ? "recurrent" : "chunked", n, L, eo, es);
+        ok = ok && eo < 2e-3 && es < 2e-3;
+    }
+    return ok;
+}
+
 }  // namespace
 
 int main() {
@@ -191,6 +245,8 @@ int main() {
     bool ok = prefill_case("prefill GDN B2 T200 H2 d128", false);
     ok = prefill_case("prefill KDA B2 T200 H2 d128", true) && ok;
     ok = decode_case() && ok;
+    ok = varlen_case(false) && ok;
+    ok = varlen_case(true) && ok;
     std::printf("c-abi: %s\n", ok ? "ok" : "FAILED");
     return ok ? 0 : 1;
 }

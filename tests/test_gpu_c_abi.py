@@ -16,4 +16,4 @@ def test_c_abi_program_matches_the_oracle():
     r = subprocess.run([BIN], capture_output=True, text=True, timeout=120)
     print(r.stdout + r.stderr)
     assert r.returncode == 0, r.stdout + r.stderr
-    assert r.stdout.count("rel-L2") == 3 and "c-abi: ok" in r.stdout
+    assert r.stdout.count("rel-L2") == 3 + 2 * 4 and "c-abi: ok" in r.stdout
