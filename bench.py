@@ -311,6 +311,111 @@ def bench_decode(w, steps, distinct):
     return {"wall_s": wall, "kernel_ms": kern, "step_ms": step}
 
 
+def serving_lengths(total, seed=2026, lo=64, hi=2048):
+    """A seeded serving mix: lengths log-uniform in [lo, hi] tokens, drawn until they cover `total`
+    tokens (the last one cut to fit)."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    lens = []
+    while sum(lens) < total:
+        lens.append(min(int(round(float(np.exp(rng.uniform(np.log(lo), np.log(hi)))))), total - sum(lens)))
+    return lens
+
+
+def _timed_calls(fn, steps, warmup):
+    """Mean and median ms per call over `steps` calls (events on torch's current stream, on which
+    the binding launches), after `warmup` calls."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
+        fn()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return sum(per) / len(per), median(per)
+
+
+def bench_next_rows(w, x, steps, warmup, recurrent_tokens=8):
+    """The serving and variant entry points on the prefill workload's tokens (whole calls, both
+    stages): a packed batch of a serving mix of lengths (gdr_chunk_fwd_varlen), the same batch
+    without the delta rule (gdr_chunk_fwd with delta_off), and T tokens per call on the recurrent
+    schedule for the decode workload's sequences (gdr_recurrent_fwd)."""
+    import torch
+    import gated_delta_rule_26_amd as gdr
+    from gdr_inputs import WORKLOADS, random_inputs
+
+    dev = torch.device("cuda:0")
+    d = {}
+    for key in ("q", "k", "v", "g", "beta"):
+        t = torch.from_numpy(x[key]).to(dev)
+        d[key] = t.to(torch.bfloat16) if key in ("q", "k", "v") and w.dtype == "bf16" else t
+    ntok = w.B * w.T
+    res = {}
+
+    # packed batch: the B*T tokens as one token axis, sequences of a serving mix
+    lens = serving_lengths(ntok)
+    cu = torch.tensor([0] + list(__import__("itertools").accumulate(lens)), dtype=torch.int32, device=dev)
+    pk = {key: val.reshape((ntok,) + tuple(val.shape[2:])) for key, val in d.items()}
+    N = len(lens)
+    desc = gdr.make_desc(N, ntok, w.H, w.Dk, w.Dv, qkv_dtype=pk["q"].dtype, o_dtype=torch.float32,
+                         per_channel=w.per_channel, kaczmarz=w.kaczmarz, eps=w.eps)
+    ws = torch.empty(max(1, gdr.chunk_fwd_varlen_workspace_size(desc)), dtype=torch.uint8, device=dev)
+    o = torch.empty((ntok, w.H, w.Dv), dtype=torch.float32, device=dev)
+    sf = torch.empty((N, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+    kw = dict(per_channel=w.per_channel, kaczmarz=w.kaczmarz, eps=w.eps, o=o, s_final=sf, workspace=ws,
+              o_dtype=torch.float32)
+    ms, med = _timed_calls(lambda: gdr.chunk_fwd_varlen(pk["q"], pk["k"], pk["v"], pk["g"], pk["beta"], cu,
+                                                        **kw), steps, warmup)
+    res["packed_batch"] = {
+        "entry": "gdr_chunk_fwd_varlen",
+        "workload": f"{w.name} tokens ({ntok} x H{w.H}) packed as {N} sequences, lengths log-uniform in "
+                    f"[64, 2048] (seed 2026; {min(lens)}..{max(lens)} tokens), fp32 output",
+        "sequences": N, "ms_per_call": ms, "ms_per_call_median": med, "tokens_per_s": ntok / (ms * 1e-3)}
+
+    # without the delta rule (the additive write, scalar decay: RetNet / Mamba-2 style), fixed length
+    o2 = torch.empty((w.B, w.T, w.H, w.Dv), dtype=torch.float32, device=dev)
+    s2 = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+    desc2 = gdr.make_desc(w.B, w.T, w.H, w.Dk, w.Dv, qkv_dtype=d["q"].dtype, o_dtype=torch.float32,
+                          per_channel=w.per_channel, delta_off=True)
+    ws2 = torch.empty(max(1, gdr.chunk_fwd_workspace_size(desc2)), dtype=torch.uint8, device=dev)
+    ms, med = _timed_calls(lambda: gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], None, per_channel=w.per_channel,
+                                                 delta_off=True, o=o2, o_dtype=torch.float32, s_final=s2,
+                                                 workspace=ws2),
+                           steps, warmup)
+    res["no_delta"] = {
+        "entry": "gdr_chunk_fwd (delta_off)",
+        "workload": f"{w.name} inputs, additive write S = D S + k v^T ({w.decay} decay), fp32 output",
+        "ms_per_call": ms, "ms_per_call_median": med, "tokens_per_s": ntok / (ms * 1e-3)}
+
+    # T tokens per call on the recurrent schedule (short prefills, several decode tokens)
+    wd = WORKLOADS["decode"]
+    T = recurrent_tokens
+    xr = random_inputs(77, wd.B, T, wd.H, wd.Dk, wd.Dv, dtype="bf16")
+    r = {key: torch.from_numpy(xr[key]).to(dev) for key in ("q", "k", "v", "g", "beta")}
+    for key in ("q", "k", "v"):
+        r[key] = r[key].to(torch.bfloat16)
+    gen = torch.Generator(device=dev).manual_seed(5)
+    state = torch.empty((wd.B, wd.H, wd.Dk, wd.Dv), dtype=torch.float32, device=dev).normal_(0.0, 0.02,
+                                                                                             generator=gen)
+    o3 = torch.empty((wd.B, T, wd.H, wd.Dv), dtype=torch.float32, device=dev)
+    ms, med = _timed_calls(lambda: gdr.recurrent_fwd(r["q"], r["k"], r["v"], r["g"], r["beta"], state, o=o3,
+                                                    o_dtype=torch.float32),
+                           steps, warmup)
+    nb = wd.B * wd.H * (2 * wd.Dk * wd.Dv * 4 + T * ((2 * wd.Dk + wd.Dv) * 2 + 8 + wd.Dv * 4))
+    res["recurrent_tokens"] = {
+        "entry": "gdr_recurrent_fwd",
+        "workload": f"{wd.B} sequences x H{wd.H}, {T} tokens per call, d_k=d_v={wd.Dk}, bf16 q/k/v, fp32 "
+                    f"state in place, scalar decay, given beta, fp32 output",
+        "ms_per_call": ms, "ms_per_call_median": med, "tokens_per_s": wd.B * T / (ms * 1e-3),
+        "roofline": {"bound": "hbm", "achieved": nb / (ms * 1e-3) / 1e9, "peak": PEAK_HBM, "unit": "GB/s",
+                     "frac": nb / (ms * 1e-3) / 1e9 / PEAK_HBM, "alg_bytes_per_call": nb}}
+    return res
+
+
 def calibrate_copy(nbytes=1 << 30, reps=3):
     """A plain device copy of known size, so that rocprofv3 byte counters of
     the same command can be scaled (FETCH_SIZE / WRITE_SIZE per dispatch)."""
@@ -346,6 +451,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=5,
                     help="timed calls of the backward pass on the prefill workload (0: skip)")
+    ap.add_argument("--next-rows-steps", type=int, default=5,
+                    help="timed calls of the packed-batch, no-delta and multi-token recurrent entry points (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (for rocprofv3 counter scaling)")
     args = ap.parse_args()
@@ -465,6 +572,9 @@ def main():
             **bwd,
             "train_step_tokens_per_s": w.B * w.T / ((event_step_ms + bwd["ms_per_step"]) * 1e-3),
         }
+
+    if args.next_rows_steps > 0 and not w.per_channel:
+        out["next_rows"] = bench_next_rows(w, pre["inputs"], args.next_rows_steps, 2)
 
     if args.calibrate_copy:
         out["calibration_copy_bytes"] = calibrate_copy()
