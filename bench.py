@@ -51,8 +51,8 @@ MEASURED_TRAFFIC = {
                                           + 1190090.4 * 2.0 + 1049612.7) * 1024),
     ("matrix", "intra", "kla_prefill"): (_SCALAR, "4c7a4f5d2ac673e3b353b7d5545d145eaa2b619a18e3f53ced3437b273e43536",
                                          (656909.6 * 2.0 + 802816.0) * 1024),
-    ("decode", "step", "decode"): (_DECODE, "ff6af95675f820ab6aee79b825e824dd5de086030a6ac1b84f64cea9600f3e0a",
-                                   (132972.4 * 2.0 + 264192.0) * 1024),
+    ("decode", "step", "decode"): (_DECODE, "2a51e82863d6794848b5853d96e23d47226519bfc4408e81297cd141dc4ceaee",
+                                   (132972.8 * 2.0 + 264192.0) * 1024),
 }
 
 
@@ -406,13 +406,19 @@ def bench_next_rows(w, x, steps, warmup, recurrent_tokens=8):
                                                     o_dtype=torch.float32),
                            steps, warmup)
     nb = wd.B * wd.H * (2 * wd.Dk * wd.Dv * 4 + T * ((2 * wd.Dk + wd.Dv) * 2 + 8 + wd.Dv * 4))
+    fl_rec = wd.B * wd.H * T * 6 * wd.Dk * wd.Dv
     res["recurrent_tokens"] = {
         "entry": "gdr_recurrent_fwd",
         "workload": f"{wd.B} sequences x H{wd.H}, {T} tokens per call, d_k=d_v={wd.Dk}, bf16 q/k/v, fp32 "
                     f"state in place, scalar decay, given beta, fp32 output",
         "ms_per_call": ms, "ms_per_call_median": med, "tokens_per_s": wd.B * T / (ms * 1e-3),
         "roofline": {"bound": "hbm", "achieved": nb / (ms * 1e-3) / 1e9, "peak": PEAK_HBM, "unit": "GB/s",
-                     "frac": nb / (ms * 1e-3) / 1e9 / PEAK_HBM, "alg_bytes_per_call": nb}}
+                     "frac": nb / (ms * 1e-3) / 1e9 / PEAK_HBM, "alg_bytes_per_call": nb,
+                     # per token and head three passes over the state (S~^T k, S~^T q, the rank-1
+                     # write), 2 flops per element each, on the fp32 vector ALUs
+                     "alu_view": {"alg_flops_per_call": fl_rec,
+                                  "achieved_tflops": fl_rec / (ms * 1e-3) / 1e12, "peak_tflops": PEAK_FP32_VALU,
+                                  "frac": fl_rec / (ms * 1e-3) / 1e12 / PEAK_FP32_VALU}}}
     return res
 
 

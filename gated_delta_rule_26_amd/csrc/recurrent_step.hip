@@ -19,8 +19,11 @@
 // second pass over the state is needed.
 //
 // A run of T tokens keeps the state in registers: it is read before the
-// first token and written after the last, and each token's q, k, v and gates
-// are loaded while the previous token is computed.  Decode is T = 1.
+// first token and written after the last.  The one-token kernel below loads
+// each token's q, k, v and gates while the previous token is computed (it is
+// launched for decode, T = 1); runs of several tokens take
+// recurrent_tokens_kernel, which stages the inputs of 16 tokens at a time in
+// LDS.
 //
 // Without the delta rule (delta = false: linear attention, RetNet / Mamba-2,
 // GLA; textbook page, update table) the write is S = S~ + k v^T: the same
@@ -181,11 +184,167 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
         *reinterpret_cast<float4 *>(S + (size_t)(p * RPP + r0) * DV + 4 * c4) = s[p];
 }
 
+// Several tokens per sequence: the same recurrence and thread layout, with
+// the tokens' inputs staged in LDS a block of kTokBlock tokens at a time (one
+// cooperative load per block, so no token waits on a global load), and one
+// barrier per token.  The per-token LDS that crosses that barrier (partial
+// sums, k.q, the write strength) is double-buffered by token parity: token
+// t+2 rewrites a buffer only after every thread has passed token t+1's
+// barrier, i.e. has finished reading token t's.
+constexpr int kTokBlock = 16;
+
+template <int DK, int DV, bool PC, bool KZ, bool IN_BF16, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads, 3) void recurrent_tokens_kernel(
+    const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ state,
+    void *__restrict__ o, int T, int H, float eps, float scale, bool delta, const int *__restrict__ cu) {
+    constexpr int TPR = DV / 4;
+    constexpr int RPP = kThreads / TPR;
+    constexpr int PASSES = DK / RPP;
+    static_assert(DK % RPP == 0, "state rows must tile the workgroup");
+
+    const size_t nh = blockIdx.x;
+    const size_t n = nh / H, h = nh % H;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int c4 = tid % TPR;
+    const int r0 = tid / TPR;
+
+    __shared__ float sk[kTokBlock][DK], sq[kTokBlock][DK], sa[PC ? kTokBlock : 1][DK];
+    __shared__ float4 sv[kTokBlock][TPR];
+    __shared__ float sgs[kTokBlock], sbt[kTokBlock];
+    __shared__ float4 red[2][2][4][TPR];
+    __shared__ float s_kq[2], s_beta[2];
+
+    float *S = state + nh * DK * DV;
+    float4 s[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+        s[p] = *reinterpret_cast<const float4 *>(S + (size_t)(p * RPP + r0) * DV + 4 * c4);
+
+    // token rows as in the one-token kernel (packed batches: offsets clamped
+    // to [0, T] and raised to the largest one before them)
+    size_t first = (size_t)n * T;
+    if (cu) {
+        int m = 0, t0 = 0;
+        for (size_t i = 0; i <= n + 1; ++i) {
+            m = max(m, min(max(cu[i], 0), T));
+            if (i == n) t0 = m;
+        }
+        first = t0;
+        T = m - t0;
+    }
+    auto row_of = [&](int t) { return (first + t) * H + h; };
+
+    for (int tb0 = 0; tb0 < T; tb0 += kTokBlock) {
+        const int nb = min(kTokBlock, T - tb0);
+        __syncthreads();  // the previous block's inputs are no longer read
+        for (int e = tid; e < nb * DK; e += kThreads) {
+            const int tt = e / DK, i = e % DK;
+            const size_t r = row_of(tb0 + tt);
+            sk[tt][i] = load_in<IN_BF16>(k, r * DK + i);
+            sq[tt][i] = load_in<IN_BF16>(q, r * DK + i);
+            if constexpr (PC) sa[tt][i] = __expf(g[r * DK + i]);
+        }
+        for (int e = tid; e < nb * TPR; e += kThreads) {
+            const int tt = e / TPR, j = e % TPR;
+            const size_t r = row_of(tb0 + tt);
+            sv[tt][j] = make_float4(load_in<IN_BF16>(v, r * DV + 4 * j + 0), load_in<IN_BF16>(v, r * DV + 4 * j + 1),
+                                    load_in<IN_BF16>(v, r * DV + 4 * j + 2), load_in<IN_BF16>(v, r * DV + 4 * j + 3));
+        }
+        if (tid < nb) {
+            const size_t r = row_of(tb0 + tid);
+            sgs[tid] = PC ? 1.0f : __expf(g[r]);
+            sbt[tid] = delta ? beta[r] : 1.0f;
+        }
+        __syncthreads();
+
+        for (int tt = 0; tt < nb; ++tt) {
+            const int t = tb0 + tt;
+            const int b = t & 1;
+            if (wave == 0) {
+                float kq = 0.f, kk = 0.f;
+                for (int i = lane; i < DK; i += 64) {
+                    kq += sk[tt][i] * sq[tt][i];
+                    kk += sk[tt][i] * sk[tt][i];
+                }
+                kq = wave_sum(kq);
+                kk = wave_sum(kk);
+                if (lane == 0) {
+                    s_kq[b] = kq;
+                    s_beta[b] = KZ ? sbt[tt] / (kk + eps) : sbt[tt];
+                }
+            }
+            const float a_scalar = sgs[tt];
+            float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = pk;
+#pragma unroll
+            for (int p = 0; p < PASSES; ++p) {
+                const int row = p * RPP + r0;
+                const float a = PC ? sa[tt][row] : a_scalar;
+                const float ak = a * sk[tt][row], aq = a * sq[tt][row];
+                pk.x += ak * s[p].x; pk.y += ak * s[p].y; pk.z += ak * s[p].z; pk.w += ak * s[p].w;
+                pq.x += aq * s[p].x; pq.y += aq * s[p].y; pq.z += aq * s[p].z; pq.w += aq * s[p].w;
+            }
+#pragma unroll
+            for (int off = TPR; off < 64; off <<= 1) {
+                pk.x += __shfl_xor(pk.x, off, 64); pk.y += __shfl_xor(pk.y, off, 64);
+                pk.z += __shfl_xor(pk.z, off, 64); pk.w += __shfl_xor(pk.w, off, 64);
+                pq.x += __shfl_xor(pq.x, off, 64); pq.y += __shfl_xor(pq.y, off, 64);
+                pq.z += __shfl_xor(pq.z, off, 64); pq.w += __shfl_xor(pq.w, off, 64);
+            }
+            if (lane < TPR) {
+                red[b][0][wave][c4] = pk;
+                red[b][1][wave][c4] = pq;
+            }
+            __syncthreads();
+            float4 P = red[b][0][0][c4], R = red[b][1][0][c4];
+#pragma unroll
+            for (int w = 1; w < 4; ++w) {
+                const float4 x = red[b][0][w][c4], y = red[b][1][w][c4];
+                P.x += x.x; P.y += x.y; P.z += x.z; P.w += x.w;
+                R.x += y.x; R.y += y.y; R.z += y.z; R.w += y.w;
+            }
+            const float bt = s_beta[b];
+            const float4 vv = sv[tt][c4];
+            const float4 e = delta ? make_float4(vv.x - P.x, vv.y - P.y, vv.z - P.z, vv.w - P.w) : vv;
+            if (r0 == 0) {  // read after write: o = scale (S~^T q + beta e (k.q))
+                const float bkq = bt * s_kq[b];
+                const size_t ob = row_of(t) * DV + 4 * c4;
+                store_out<OUT_BF16>(o, ob + 0, scale * (R.x + bkq * e.x));
+                store_out<OUT_BF16>(o, ob + 1, scale * (R.y + bkq * e.y));
+                store_out<OUT_BF16>(o, ob + 2, scale * (R.z + bkq * e.z));
+                store_out<OUT_BF16>(o, ob + 3, scale * (R.w + bkq * e.w));
+            }
+#pragma unroll
+            for (int p = 0; p < PASSES; ++p) {
+                const int row = p * RPP + r0;
+                const float a = PC ? sa[tt][row] : a_scalar;
+                const float bk = bt * sk[tt][row];
+                s[p].x = a * s[p].x + bk * e.x;
+                s[p].y = a * s[p].y + bk * e.y;
+                s[p].z = a * s[p].z + bk * e.z;
+                s[p].w = a * s[p].w + bk * e.w;
+            }
+        }
+    }
+
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+        *reinterpret_cast<float4 *>(S + (size_t)(p * RPP + r0) * DV + 4 * c4) = s[p];
+}
+
 template <int DK, int DV, bool PC, bool KZ, bool IB, bool OB>
 hipError_t launch_t(const StepArgs &a) {
     const unsigned grid = static_cast<unsigned>(a.N) * static_cast<unsigned>(a.H);
-    GDR_LAUNCH((recurrent_step_kernel<DK, DV, PC, KZ, IB, OB>), dim3(grid), dim3(kThreads), a.stream, a.ev0, a.ev1,
-               a.q, a.k, a.v, a.g, a.beta, a.state, a.o, a.T, a.H, a.eps, a.scale, a.delta, a.cu);
+    // one token per sequence (decode): the one-token kernel; more: tokens staged in LDS
+    const bool many = a.cu ? a.T > a.N : a.T > 1;
+    if (many)
+        GDR_LAUNCH((recurrent_tokens_kernel<DK, DV, PC, KZ, IB, OB>), dim3(grid), dim3(kThreads), a.stream, a.ev0,
+                   a.ev1, a.q, a.k, a.v, a.g, a.beta, a.state, a.o, a.T, a.H, a.eps, a.scale, a.delta, a.cu);
+    else
+        GDR_LAUNCH((recurrent_step_kernel<DK, DV, PC, KZ, IB, OB>), dim3(grid), dim3(kThreads), a.stream, a.ev0,
+                   a.ev1, a.q, a.k, a.v, a.g, a.beta, a.state, a.o, a.T, a.H, a.eps, a.scale, a.delta, a.cu);
     return hipGetLastError();
 }
 
