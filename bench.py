@@ -464,7 +464,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one MI355X; the path "
+        print(f"bench.py: --gpus {args.gpus} is not supported: bench.py measures one MI355X; the path "
               f"shards over independent (sequence, head) pairs, so N GPUs run N independent shares.",
               file=sys.stderr)
         sys.exit(2)
