@@ -8,8 +8,8 @@ step is timed beside it on the decode workload (256 sequences x 16 heads,
 d128, fp32 state updated in place).  Kernel times come from HIP events
 recorded on the stream the kernels are launched on (torch's current stream).
 
-Prints ONE JSON line.  ``--gpus`` above 1 is refused: this build runs on one
-GPU (the path shards over (sequence, head) pairs with no communication).
+Prints ONE JSON line.  ``--gpus`` above 1 is refused: the benchmark runs on
+one GPU (the path shards over (sequence, head) pairs with no communication).
 """
 from __future__ import annotations
 
