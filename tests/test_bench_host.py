@@ -1,0 +1,43 @@
+"""Host-side pieces of bench.py (no GPU): the refusal of several GPUs, the
+serving length mix, the algorithmic byte and flop counts, and the guard that
+drops counter figures measured on other kernel sources."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_several_gpus_are_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=60, cwd=ROOT)
+    assert r.returncode == 2 and "--gpus 2 is not supported" in r.stderr and r.stdout == ""
+
+
+def test_serving_lengths_cover_the_tokens_exactly_and_are_seeded():
+    for total in (1, 63, 16384, 131072):
+        lens = bench.serving_lengths(total)
+        assert sum(lens) == total and all(n >= 1 for n in lens)
+        assert all(n <= 2048 for n in lens)
+        assert lens == bench.serving_lengths(total)          # the same mix every run
+    assert bench.serving_lengths(16384) != bench.serving_lengths(16384, seed=1)
+
+
+def test_algorithmic_counts_at_d128():
+    # per token and head q, k, v in bf16 (768 B) and the fp32 output (512 B); per head the final state
+    assert bench.alg_bytes_state_kernel(4, 4096, 16, 128, 128, 2, 4) == 4 * 4096 * 16 * 1280 + 4 * 16 * 65536
+    assert bench.alg_bytes_state_kernel(4, 4096, 16, 128, 128, 2, 4) == 339_738_624
+    # decode: the state in and out plus one token's inputs and output, per (sequence, head)
+    assert bench.decode_bytes_per_step(256, 16, 128, 128) == 4096 * 132_360
+    fl = bench.alg_flops_per_token_head(128, 128)
+    assert fl["state"] == 6 * 128 * 128 + 65 * 128 and fl["total"] == fl["state"] + fl["intra"]
+
+
+def test_counter_figures_follow_their_sources():
+    # each recorded figure names the files it was measured on; a figure whose files changed is dropped
+    for key, (files, sha, _value) in bench.MEASURED_TRAFFIC.items():
+        assert all(os.path.exists(os.path.join(ROOT, f)) for f in files), key
+        expected = bench.measured_traffic(*key)
+        assert (expected is not None) == (bench.sources_sha(files) == sha), key
