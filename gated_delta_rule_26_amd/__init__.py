@@ -138,6 +138,23 @@ def _check_dev(name, t, device, dtype=None, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _stream(stream, dev):
+    """The stream the work is enqueued on: ``stream``, or torch's current stream of ``dev``."""
+    return stream if stream is not None else torch.cuda.current_stream(dev)
+
+
+def _used_on(st, dev, *tensors):
+    """Tensors allocated here come from the caching allocator's pool of the
+    current stream.  When the work runs on another stream, record that stream
+    on them, so that their memory is not handed out again (and overwritten)
+    before the work queued there has finished with it."""
+    if st.cuda_stream == torch.cuda.current_stream(dev).cuda_stream:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(st)
+
+
 def make_desc(B, T, H, Dk, Dv, *, qkv_dtype, o_dtype, per_channel=False, kaczmarz=False, eps=0.0,
               scale=1.0, algo="auto", chunk=64, delta_off=False) -> Desc:
     return Desc(B=B, T=T, H=H, Dk=Dk, Dv=Dv, chunk=chunk, qkv_dtype=_dtype_code(qkv_dtype),
@@ -189,13 +206,18 @@ def chunk_fwd(q, k, v, g, beta, *, per_channel: bool = False, kaczmarz: bool = F
         _check_dev("beta", beta, dev, torch.float32, (B, T, H))
     if s0 is not None:
         _check_dev("s0", s0, dev, torch.float32, (B, H, Dk, Dv))
+    if stage is not None and workspace is None:
+        raise ValueError("stage= runs one kernel of the pipeline: pass the workspace both stages share")
     o_dtype = o_dtype or q.dtype
+    fresh = []
     if o is None:
         o = torch.empty((B, T, H, Dv), dtype=o_dtype, device=dev)
+        fresh.append(o)
     else:
         _check_dev("o", o, dev, o_dtype, (B, T, H, Dv))
     if s_final is None and output_final_state:
         s_final = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+        fresh.append(s_final)
     elif s_final is not None:
         _check_dev("s_final", s_final, dev, torch.float32, (B, H, Dk, Dv))
     desc = make_desc(B, T, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=o_dtype, per_channel=per_channel,
@@ -203,9 +225,11 @@ def chunk_fwd(q, k, v, g, beta, *, per_channel: bool = False, kaczmarz: bool = F
     need = chunk_fwd_workspace_size(desc)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        fresh.append(workspace)
     else:
         _check_dev("workspace", workspace, dev, torch.uint8)
-    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    st = _stream(stream, dev)
+    _used_on(st, dev, *fresh)
     args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(o),
             _ptr(s_final), _ptr(workspace), workspace.numel(), ctypes.c_void_p(st.cuda_stream))
     if stage is None:
@@ -251,13 +275,15 @@ def recurrent_step(q, k, v, g, beta, state, *, per_channel: bool = False, kaczma
         _check_dev("beta", beta, dev, torch.float32, (N, H))
     _check_dev("state", state, dev, torch.float32, (N, H, Dk, Dv))
     o_dtype = o_dtype or q.dtype
-    if o is None:
+    fresh_o = o is None
+    if fresh_o:
         o = torch.empty((N, H, Dv), dtype=o_dtype, device=dev)
     else:
         _check_dev("o", o, dev, o_dtype, (N, H, Dv))
     desc = make_desc(N, 1, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=o_dtype, per_channel=per_channel,
                      kaczmarz=kaczmarz, eps=eps, scale=scale, delta_off=delta_off)
-    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    st = _stream(stream, dev)
+    _used_on(st, dev, o if fresh_o else None)
     args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
             ctypes.c_void_p(st.cuda_stream))
     if events is None:
@@ -297,13 +323,15 @@ def recurrent_fwd(q, k, v, g, beta, state, *, per_channel: bool = False, kaczmar
         _check_dev("beta", beta, dev, torch.float32, (B, T, H))
     _check_dev("state", state, dev, torch.float32, (B, H, Dk, Dv))
     o_dtype = o_dtype or q.dtype
-    if o is None:
+    fresh_o = o is None
+    if fresh_o:
         o = torch.empty((B, T, H, Dv), dtype=o_dtype, device=dev)
     else:
         _check_dev("o", o, dev, o_dtype, (B, T, H, Dv))
     desc = make_desc(B, T, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=o_dtype, per_channel=per_channel,
                      kaczmarz=kaczmarz, eps=eps, scale=scale, delta_off=delta_off)
-    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    st = _stream(stream, dev)
+    _used_on(st, dev, o if fresh_o else None)
     rc = lib.gdr_recurrent_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                _ptr(state), _ptr(o), ctypes.c_void_p(st.cuda_stream))
     if rc != 0:
@@ -352,22 +380,26 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, *, per_channel: bool = False,
     if s0 is not None:
         _check_dev("s0", s0, dev, torch.float32, (N, H, Dk, Dv))
     o_dtype = o_dtype or q.dtype
-    if o is None:
+    fresh_o = o is None
+    if fresh_o:
         o = torch.empty((T, H, Dv), dtype=o_dtype, device=dev)
     else:
         _check_dev("o", o, dev, o_dtype, (T, H, Dv))
-    if s_final is None and output_final_state:
+    fresh_s = s_final is None and output_final_state
+    if fresh_s:
         s_final = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
     elif s_final is not None:
         _check_dev("s_final", s_final, dev, torch.float32, (N, H, Dk, Dv))
     desc = make_desc(N, T, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=o_dtype, per_channel=per_channel,
                      kaczmarz=kaczmarz, eps=eps, scale=scale, algo=algo, delta_off=delta_off)
     need = chunk_fwd_varlen_workspace_size(desc)
-    if workspace is None:
+    fresh_ws = workspace is None
+    if fresh_ws:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     else:
         _check_dev("workspace", workspace, dev, torch.uint8)
-    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    st = _stream(stream, dev)
+    _used_on(st, dev, o if fresh_o else None, s_final if fresh_s else None, workspace if fresh_ws else None)
     rc = lib.gdr_chunk_fwd_varlen(ctypes.byref(desc), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                   _ptr(beta), _ptr(s0), _ptr(o), _ptr(s_final), _ptr(workspace),
                                   workspace.numel(), ctypes.c_void_p(st.cuda_stream))
@@ -422,11 +454,13 @@ def chunk_bwd(q, k, v, g, beta, d_o, *, per_channel: bool = False, kaczmarz: boo
     desc = make_desc(B, T, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=torch.float32, per_channel=per_channel,
                      kaczmarz=kaczmarz, eps=eps, scale=scale, delta_off=delta_off)
     need = chunk_bwd_workspace_size(desc)
-    if workspace is None:
+    fresh_ws = workspace is None
+    if fresh_ws:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     else:
         _check_dev("workspace", workspace, dev, torch.uint8)
-    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    st = _stream(stream, dev)
+    _used_on(st, dev, *out.values(), workspace if fresh_ws else None)
     rc = lib.gdr_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0),
                            _ptr(d_o), _ptr(ds_final), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
                            _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["ds0"]), _ptr(workspace),
@@ -487,11 +521,13 @@ def chunk_bwd_varlen(q, k, v, g, beta, d_o, cu_seqlens, *, per_channel: bool = F
     desc = make_desc(N, T, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=torch.float32, per_channel=per_channel,
                      kaczmarz=kaczmarz, eps=eps, scale=scale, delta_off=delta_off)
     need = chunk_bwd_varlen_workspace_size(desc)
-    if workspace is None:
+    fresh_ws = workspace is None
+    if fresh_ws:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     else:
         _check_dev("workspace", workspace, dev, torch.uint8)
-    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    st = _stream(stream, dev)
+    _used_on(st, dev, *out.values(), workspace if fresh_ws else None)
     rc = lib.gdr_chunk_bwd_varlen(ctypes.byref(desc), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                   _ptr(beta), _ptr(s0), _ptr(d_o), _ptr(ds_final), _ptr(out["dq"]),
                                   _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
@@ -533,13 +569,15 @@ def recurrent_fwd_varlen(q, k, v, g, beta, state, cu_seqlens, *, per_channel: bo
         _check_dev("beta", beta, dev, torch.float32, (T, H))
     _check_dev("state", state, dev, torch.float32, (N, H, Dk, Dv))
     o_dtype = o_dtype or q.dtype
-    if o is None:
+    fresh_o = o is None
+    if fresh_o:
         o = torch.empty((T, H, Dv), dtype=o_dtype, device=dev)
     else:
         _check_dev("o", o, dev, o_dtype, (T, H, Dv))
     desc = make_desc(N, T, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=o_dtype, per_channel=per_channel,
                      kaczmarz=kaczmarz, eps=eps, scale=scale, delta_off=delta_off)
-    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    st = _stream(stream, dev)
+    _used_on(st, dev, o if fresh_o else None)
     rc = lib.gdr_recurrent_fwd_varlen(ctypes.byref(desc), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                       _ptr(beta), _ptr(state), _ptr(o), ctypes.c_void_p(st.cuda_stream))
     if rc != 0:

@@ -9,6 +9,7 @@
 namespace {
 
 using gdr::ChunkArgs;
+constexpr size_t kChunkRows = gdr::kChunk;
 using gdr::StepArgs;
 
 struct Range {
@@ -65,6 +66,10 @@ int check_desc(const gdr_desc *d, bool step, Sizes *sz, bool one_token = true, b
     if (qk > lim || vv > lim || st > lim) return GDR_E_SHAPE;
     // grid-size limits of the launches (blocks per dimension < 2^31)
     if ((size_t)d->B * d->H * 2 >= ((size_t)1 << 31)) return GDR_E_SHAPE;
+    // the chunk kernels address the rows of one chunk ([64 tokens, H, D], up to 4-byte elements) with
+    // 32-bit byte offsets
+    if (!step && (size_t)kChunkRows * d->H * (size_t)(d->Dk > d->Dv ? d->Dk : d->Dv) * 4 >= ((size_t)1 << 31))
+        return GDR_E_SHAPE;
     if (sz) {
         sz->qk = qk;
         sz->v = vv;

@@ -36,6 +36,27 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// The token span [t0, end) of sequence n of a packed batch.  Its offsets are
+// cu[n] and cu[n+1], each clamped to [0, T] and raised to the largest offset
+// before it: t0 = max over i <= n of clamp(cu[i]), end = max(t0,
+// clamp(cu[n+1])).  The prefix maximum is a workgroup reduction (each thread
+// takes every kThreads-th offset, then the wavefronts and LDS), so a
+// workgroup reads about n / kThreads offsets per thread.  Every thread of the
+// workgroup must call it (it holds a barrier).
+__device__ __forceinline__ int2 packed_span(const int *__restrict__ cu, size_t n, int T, int *red) {
+    const int tid = threadIdx.x;
+    int m = 0;
+    for (size_t i = tid; i <= n; i += kThreads) m = max(m, min(max(cu[i], 0), T));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = max(m, __shfl_xor(m, off, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    int t0 = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) t0 = max(t0, red[w]);
+    return make_int2(t0, max(t0, min(max(cu[n + 1], 0), T)));
+}
+
 template <int DK, int DV, bool PC, bool KZ, bool IN_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
@@ -75,13 +96,10 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
     // offset clamped to [0, T] and raised to the largest one before it
     size_t first = (size_t)n * T;
     if (cu) {
-        int m = 0, t0 = 0;
-        for (size_t i = 0; i <= n + 1; ++i) {
-            m = max(m, min(max(cu[i], 0), T));
-            if (i == n) t0 = m;
-        }
-        first = t0;
-        T = m - t0;
+        __shared__ int red_cu[kThreads / 64];
+        const int2 span = packed_span(cu, n, T, red_cu);
+        first = span.x;
+        T = span.y - span.x;
     }
     auto row_of = [&](int t) { return (first + t) * H + h; };
     float kin = 0.f, qin = 0.f, gin = 0.f, bin = 1.f, gsc = 0.f;
@@ -227,13 +245,10 @@ __global__ __launch_bounds__(kThreads, 3) void recurrent_tokens_kernel(
     // to [0, T] and raised to the largest one before them)
     size_t first = (size_t)n * T;
     if (cu) {
-        int m = 0, t0 = 0;
-        for (size_t i = 0; i <= n + 1; ++i) {
-            m = max(m, min(max(cu[i], 0), T));
-            if (i == n) t0 = m;
-        }
-        first = t0;
-        T = m - t0;
+        __shared__ int red_cu[kThreads / 64];
+        const int2 span = packed_span(cu, n, T, red_cu);
+        first = span.x;
+        T = span.y - span.x;
     }
     auto row_of = [&](int t) { return (first + t) * H + h; };
 

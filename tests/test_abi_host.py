@@ -357,3 +357,20 @@ def test_recurrent_fwd_varlen_validation():
     assert call(q=None) == E["GDR_E_NULL"]
     assert call(o=P(7)) == E["GDR_E_ALIAS"]          # o on top of the state
 
+
+
+@pytest.mark.parametrize("D,h_max", [(128, 65535), (64, 131071)])
+def test_head_count_limit_of_the_chunk_kernels(D, h_max):
+    """The chunk kernels address the 64 token rows of a chunk ([64, H, D],
+    up to 4-byte elements) with 32-bit byte offsets: 64 H max(Dk, Dv) 4 must
+    stay below 2^31, else GDR_E_SHAPE (the recurrent entry points use 64-bit
+    offsets and have no such limit)."""
+    for algo in ("auto", "vector") + (("matrix",) if D == 128 else ()):   # the matrix path takes d128
+        assert _ws(_desc(B=1, T=64, H=h_max, Dk=D, Dv=D, algo=algo))[0] == 0
+        assert _ws(_desc(B=1, T=64, H=h_max + 1, Dk=D, Dv=D, algo=algo))[0] == E["GDR_E_SHAPE"]
+    n = ctypes.c_size_t(0)
+    bwd = gdr.load_library().gdr_chunk_bwd_workspace_size
+    assert bwd(ctypes.byref(_desc(B=1, T=64, H=h_max + 1, Dk=D, Dv=D)), ctypes.byref(n)) == E["GDR_E_SHAPE"]
+    # mixed widths: the wider one counts
+    assert _ws(_desc(B=1, T=64, H=65536, Dk=64, Dv=128))[0] == E["GDR_E_SHAPE"]
+    assert _ws(_desc(B=1, T=64, H=65535, Dk=64, Dv=128))[0] == 0

@@ -1,12 +1,13 @@
 """Chunked prefill on the GPU against the fp64 oracle: modes, dtypes, widths,
-ragged tails, edge cases, and the full benchmark workloads (sampled heads)."""
+ragged tails and edge cases (the full benchmark workloads, every head, are in
+test_gpu_full_workloads.py)."""
 import numpy as np
 import pytest
 import torch
 
 import gated_delta_rule_26_amd as gdr
 import oracle
-from gdr_inputs import WORKLOADS, prefill_inputs, random_inputs
+from gdr_inputs import random_inputs
 from tests.gpu_util import DEV, TOL, host, rel, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -251,42 +252,6 @@ def test_matrix_path_deterministic_and_close_to_vector_path(mode):
     assert eo < TOL["bf16"] and es < TOL["bf16"]
 
 
-# ------------------------------------------------------------ full workloads
-FULL = {
-    "gdn_tiny": dict(mode="gdn", heads=None),
-    "gdn_prefill": dict(mode="gdn", heads=8),
-    "kda_prefill": dict(mode="kda", heads=8),
-    "kla_prefill": dict(mode="kla", heads=2),
-}
-
-
-@pytest.mark.parametrize("name", list(FULL))
-def test_full_workload_sampled(name):
-    """Each prefill benchmark workload at full size, in the launch
-    configuration the benchmark times (auto algorithm, fp32 output), checked
-    on sampled (batch, head) pairs against the oracle."""
-    w = WORKLOADS[name]
-    spec = FULL[name]
-    print(f"full workload {name}: generating inputs", flush=True)
-    x = prefill_inputs(w)
-    d = to_dev(x, w.dtype)
-    m = MODES[spec["mode"]]
-    o, s = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], o_dtype=torch.float32,
-                         eps=w.eps, **m)
-    torch.cuda.synchronize()
-    nbh = w.B * w.H
-    heads = np.arange(nbh) if spec["heads"] is None else \
-        np.sort(np.random.default_rng(1).choice(nbh, spec["heads"], replace=False))
-    print(f"full workload {name}: oracle on {len(heads)} heads", flush=True)
-    o_ref, s_ref = oracle.oracle_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], eps=w.eps, heads=heads, **m)
-    hb, hh = heads // w.H, heads % w.H
-    o_g = o[torch.from_numpy(hb).to(DEV), :, torch.from_numpy(hh).to(DEV)].cpu().numpy()
-    s_g = s[torch.from_numpy(hb).to(DEV), torch.from_numpy(hh).to(DEV)].cpu().numpy()
-    eo, es = rel(o_g, o_ref[hb, :, hh]), rel(s_g, s_ref[hb, hh])
-    print(f"full workload {name}: rel o {eo:.2e} S {es:.2e}")
-    assert eo < TOL[w.dtype] and es < TOL[w.dtype]
-
-
 @pytest.mark.parametrize("mode", ["gdn", "kda"])
 @pytest.mark.parametrize("B,H,T", [(1, 8, 130), (3, 8, 70), (1, 2, 65), (2, 1, 129), (1, 2, 64 * 40 + 5)])
 def test_matrix_chunk_counts_and_workgroup_mapping(B, H, T, mode):
@@ -419,3 +384,41 @@ def test_no_delta_matrix_close_to_vector_and_chunk_counts(variant):
     ov, sv, _, _ = _no_delta_run(x, variant, "bf16", algo="vector")
     assert rel(host(om), host(ov)) < TOL["bf16"] and rel(host(sm), host(sv)) < TOL["bf16"]
     assert rel(host(om), o_ref) < TOL["bf16"] and rel(host(sm), s_ref) < TOL["bf16"]
+
+
+def test_side_stream_call_and_binding_allocations():
+    """Work enqueued on a caller's stream that is not torch's current stream.
+    The binding allocates o, the final state and the workspace from the
+    current stream's pool and releases the workspace on return; it records the
+    caller's stream on them, so memory the current stream allocates and fills
+    right after the call is not memory the kernels still use.  Results equal
+    the same call on the current stream, bit for bit."""
+    x = _inputs(17, 2, 900, 4, 128, 128, "gdn", "bf16")
+    d = to_dev(x, "bf16")
+    kw = dict(s0=d["s0"], o_dtype=torch.float32)
+    o_ref, s_ref = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], **kw)
+    st_ref = d["s0"].clone()
+    o1_ref = gdr.recurrent_step(d["q"][:, 0].contiguous(), d["k"][:, 0].contiguous(), d["v"][:, 0].contiguous(),
+                                d["g"][:, 0].contiguous(), d["beta"][:, 0].contiguous(), st_ref,
+                                o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    args1 = [d[key][:, 0].contiguous() for key in ("q", "k", "v", "g", "beta")]
+    st = d["s0"].clone()
+    torch.cuda.synchronize()
+    o, s = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], stream=side, **kw)
+    o1 = gdr.recurrent_step(*args1, st, o_dtype=torch.float32, stream=side)
+    scribble = [torch.full((1 << 22,), float("nan"), device=DEV) for _ in range(16)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    del scribble
+    assert torch.equal(o, o_ref) and torch.equal(s, s_ref)
+    assert torch.equal(o1, o1_ref) and torch.equal(st, st_ref)
+
+
+def test_one_stage_needs_the_shared_workspace():
+    x = _inputs(18, 1, 64, 1, 128, 128, "gdn", "bf16")
+    d = to_dev(x, "bf16")
+    with pytest.raises(ValueError):
+        gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], stage=1)
