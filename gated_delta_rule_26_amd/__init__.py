@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
   recurrent_fwd(q, k, v, g, beta, state)  -> o              T tokens, recurrent (state in place)
   chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, ...) -> (o, s_final)   packed batch of sequences
   chunk_bwd(q, k, v, g, beta, d_o, ...)   -> dict of gradients  backward pass (training)
+  chunk_fwd_noalloc(q, k, v, g, beta, o, ...) -> o         chunked prefill, no device allocation
   chunk_fwd_workspace_size(...)           -> bytes
 """
 from __future__ import annotations
@@ -22,7 +23,7 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_bwd", "chunk_bwd_workspace_size", "recurrent_step", "recurrent_fwd", "chunk_fwd_workspace_size",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_fwd_varlen", "chunk_bwd", "chunk_bwd_workspace_size", "recurrent_step", "recurrent_fwd", "chunk_fwd_workspace_size",
            "chunk_fwd_varlen_workspace_size", "GdrError", "GdrNotBuilt",
            "library_path", "abi_version", "load_library", "Desc"]
 
@@ -104,6 +105,8 @@ def load_library(path: str | None = None):
     lib.gdr_recurrent_fwd.argtypes = [D, V, V, V, V, V, V, V, V]
     lib.gdr_recurrent_fwd_varlen.restype = ctypes.c_int
     lib.gdr_recurrent_fwd_varlen.argtypes = [D, V, V, V, V, V, V, V, V, V]
+    lib.gdr_chunk_fwd_noalloc.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_noalloc.argtypes = [D, V, V, V, V, V, V, V, V, V]
     if path is None:
         _lib = lib
     return lib
@@ -584,3 +587,44 @@ def recurrent_fwd_varlen(q, k, v, g, beta, state, cu_seqlens, *, per_channel: bo
         raise GdrError(rc, "gdr_recurrent_fwd_varlen")
     return o
 
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # GDR_NOALLOC_SCRATCH_BYTES
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, o, *, s0=None, s_final=None, per_channel: bool = False,
+                      kaczmarz: bool = False, eps: float = 0.0, scale: float = 1.0, algo: str = "auto",
+                      stream=None, delta_off: bool = False):
+    """The chunked forward pass through ``gdr_chunk_fwd_noalloc``: the
+    workspace is the library's fixed device array, and nothing is allocated
+    here either, so the caller passes the output ``o`` [B,T,H,Dv] (its dtype
+    is the output dtype) and, if wanted, ``s_final`` (may be ``s0``).  Calls
+    on one GPU share that array: overlapping calls race.  Returns (o,
+    s_final)."""
+    lib = load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _check_dev("q", q, dev)
+    _check_dev("k", k, dev, q.dtype, (B, T, H, Dk))
+    _check_dev("v", v, dev, q.dtype, (B, T, H, Dv))
+    _check_dev("g", g, dev, torch.float32, (B, T, H, Dk) if per_channel else (B, T, H))
+    if delta_off:
+        beta = None
+    else:
+        _check_dev("beta", beta, dev, torch.float32, (B, T, H))
+    if s0 is not None:
+        _check_dev("s0", s0, dev, torch.float32, (B, H, Dk, Dv))
+    _check_dev("o", o, dev, None, (B, T, H, Dv))
+    if s_final is not None:
+        _check_dev("s_final", s_final, dev, torch.float32, (B, H, Dk, Dv))
+    desc = make_desc(B, T, H, Dk, Dv, qkv_dtype=q.dtype, o_dtype=o.dtype, per_channel=per_channel,
+                     kaczmarz=kaczmarz, eps=eps, scale=scale, algo=algo, delta_off=delta_off)
+    st = _stream(stream, dev)
+    rc = lib.gdr_chunk_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0),
+                                   _ptr(o), _ptr(s_final), ctypes.c_void_p(st.cuda_stream))
+    if rc != 0:
+        raise GdrError(rc, "gdr_chunk_fwd_noalloc")
+    return o, s_final

@@ -34,7 +34,9 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent) and
  *    are owned by the caller.  The library allocates nothing, frees nothing,
- *    never synchronises, and keeps no global state: it is reentrant.
+ *    never synchronises, and keeps no global state: it is reentrant.  The one
+ *    exception is gdr_chunk_fwd_noalloc, which takes its workspace from a
+ *    fixed device array of the library (see there).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  A
  *    GDR_OK return means the work is ENQUEUED on that stream, not finished.
  *  - Every argument is validated on the host before any HIP call.  A bad
@@ -353,6 +355,37 @@ int gdr_recurrent_fwd_varlen(const gdr_desc *desc, const int32_t *cu_seqlens,
                              const void *q, const void *k, const void *v,
                              const float *g, const float *beta_or_eta,
                              float *state, void *o, void *stream);
+
+/*
+ * gdr_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same pass, kernels, arithmetic and validation as gdr_chunk_fwd, with
+ * the workspace taken from a fixed scratch array of GDR_NOALLOC_SCRATCH_BYTES
+ * (128 MiB) that the library holds on each GPU it runs on until the process
+ * ends, instead of from the caller.  The caller still passes every input and
+ * output.  The call allocates and frees nothing.
+ *
+ *   Arguments as for gdr_chunk_fwd, without workspace and workspace_bytes.
+ *   Returns GDR_E_WORKSPACE (before any HIP call, nothing enqueued) when
+ *   gdr_chunk_fwd_workspace_size(desc) exceeds GDR_NOALLOC_SCRATCH_BYTES: it
+ *   covers for example B4 H16 T4096 d128 with scalar decay (98 MiB), or
+ *   about 5,300 (sequence, head, chunk) records on the matrix-core path with
+ *   scalar decay, 1,000 with per-channel decay.
+ *
+ * The scratch array of the calling thread's current device is used; `stream`
+ * must belong to that device.  Its device address is looked up on the first
+ * call on each device (hipGetSymbolAddress), so make that first call outside
+ * graph capture.  Every call on one GPU shares that GPU's array and the array
+ * keeps the last call's contents (the pass does not depend on them): calls
+ * that can overlap on one GPU (on different streams without ordering between
+ * them, or from several threads) race on it and must be serialised by the
+ * caller.
+ */
+#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int gdr_chunk_fwd_noalloc(const gdr_desc *desc,
+                          const void *q, const void *k, const void *v,
+                          const float *g, const float *beta_or_eta,
+                          const float *s0, void *o, float *s_final, void *stream);
 
 #ifdef __cplusplus
 }

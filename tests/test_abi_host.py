@@ -32,7 +32,8 @@ def test_exports_every_declared_symbol():
                             "gdr_recurrent_step_timed",
                             "gdr_recurrent_fwd", "gdr_chunk_fwd_varlen", "gdr_chunk_fwd_varlen_workspace_size",
                             "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd_varlen",
-                            "gdr_chunk_bwd_varlen_workspace_size", "gdr_recurrent_fwd_varlen"])
+                            "gdr_chunk_bwd_varlen_workspace_size", "gdr_recurrent_fwd_varlen",
+                            "gdr_chunk_fwd_noalloc"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -374,3 +375,26 @@ def test_head_count_limit_of_the_chunk_kernels(D, h_max):
     # mixed widths: the wider one counts
     assert _ws(_desc(B=1, T=64, H=65536, Dk=64, Dv=128))[0] == E["GDR_E_SHAPE"]
     assert _ws(_desc(B=1, T=64, H=65535, Dk=64, Dv=128))[0] == 0
+
+
+def test_noalloc_rejects_work_beyond_its_scratch_before_any_hip_call():
+    """gdr_chunk_fwd_noalloc checks the workspace the call needs against its
+    fixed scratch array (GDR_NOALLOC_SCRATCH_BYTES) before any HIP call: too
+    large returns GDR_E_WORKSPACE with nothing enqueued; a bad descriptor
+    returns the same status as gdr_chunk_fwd."""
+    import torch
+    lib = gdr.load_library()
+    text = open(HEADER).read()
+    assert "#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)" in text
+    assert gdr.NOALLOC_SCRATCH_BYTES == 128 << 20
+    big = _desc(B=4, T=8192, H=16, algo="matrix")
+    rc, need = _ws(big)
+    assert rc == 0 and need > gdr.NOALLOC_SCRATCH_BYTES
+    p = ctypes.c_void_p(16)
+    assert lib.gdr_chunk_fwd_noalloc(ctypes.byref(big), p, p, p, p, p, None, p, None, None) == E["GDR_E_WORKSPACE"]
+    bad = _desc(Dk=96)
+    assert lib.gdr_chunk_fwd_noalloc(ctypes.byref(bad), p, p, p, p, p, None, p, None, None) == E["GDR_E_UNSUPPORTED"]
+    assert lib.gdr_chunk_fwd_noalloc(None, p, p, p, p, p, None, p, None, None) == E["GDR_E_NULL"]
+    # the GDN prefill workload (B4 H16 T4096, scalar decay) fits
+    rc, need = _ws(_desc(B=4, T=4096, H=16, algo="matrix", qkv_dtype=torch.bfloat16))
+    assert rc == 0 and need <= gdr.NOALLOC_SCRATCH_BYTES
