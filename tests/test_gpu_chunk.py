@@ -253,11 +253,13 @@ def test_matrix_path_deterministic_and_close_to_vector_path(mode):
 
 
 @pytest.mark.parametrize("mode", ["gdn", "kda"])
-@pytest.mark.parametrize("B,H,T", [(1, 8, 130), (3, 8, 70), (1, 2, 65), (2, 1, 129), (1, 2, 64 * 40 + 5)])
+@pytest.mark.parametrize("B,H,T", [(1, 8, 130), (3, 8, 70), (1, 2, 65), (2, 1, 129), (1, 2, 64 * 40 + 5),
+                                   (5, 8, 130), (3, 11, 100)])
 def test_matrix_chunk_counts_and_workgroup_mapping(B, H, T, mode):
     """Matrix path: chunk counts that exercise the doubled LDS buffers and the
     loop tails (2, 3 and 41 chunks), and (sequence, head) counts that do and
-    do not divide by 8 (the XCD-aware workgroup mapping and its fallback)."""
+    do not divide by 8 (the XCD-aware workgroup mapping and its fallback),
+    and more walks (160, 132) than compute units."""
     x = _inputs(2000 + T + 7 * H + B, B, T, H, 128, 128, mode, "bf16", with_s0=True)
     o, s = _gpu(x, mode, "bf16", algo="matrix")
     o_ref, s_ref = _ref(x, mode)
