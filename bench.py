@@ -2,11 +2,18 @@
 """Benchmark of the gated delta-rule forward pass on one MI355X.
 
 A step is one chunked prefill over the Gated DeltaNet workload (B4 H16 T4096,
-d_k = d_v = 128, bf16 q/k/v, fp32 state, chunk 64): the intra-chunk kernel
-then the state/output kernel, with inputs resident in HBM.  The fused decode
-step is timed beside it on the decode workload (256 sequences x 16 heads,
-d128, fp32 state updated in place).  Kernel times come from HIP events
-recorded on the stream the kernels are launched on (torch's current stream).
+d_k = d_v = 128, bf16 q/k/v, fp32 state, bf16 output, chunk 64): the
+intra-chunk kernel then the state/output kernel, with the inputs resident in
+HBM and the 256 MB last-level (Infinity) cache flushed before each timed step
+by writing a 512 MiB buffer, so the step reads its inputs from HBM.  Kernel
+times come from HIP events the kernels record themselves
+(gdr_chunk_fwd_stage_timed: the first kernel records its begin, the last its
+end), on the stream they are launched on.  The same steps with warm caches,
+the fp32-output configuration, the other prefill workloads (tiny fp32, KDA
+per-channel decay, KLA long sequence), the fused decode step (256 sequences,
+and 512 sequences whose state is twice the last-level cache), the backward
+pass and the serving entry points are timed beside it, and the fp64 oracle on
+the host cores.
 
 Prints ONE JSON line.  ``--gpus`` above 1 is refused: the benchmark runs on
 one GPU (the path shards over (sequence, head) pairs with no communication).
@@ -27,32 +34,31 @@ C = 64
 PEAK_BF16_MFMA = 2500.0      # TFLOP/s, MI355X dense bf16
 PEAK_FP32_VALU = 157.3       # TFLOP/s, MI355X fp32 vector
 PEAK_HBM = 8000.0            # GB/s, MI355X HBM3E
+FLUSH_BYTES = 512 << 20      # twice the 256 MB last-level cache
 
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE (x2.0) + WRITE_SIZE (x1.0), scaled by a 1 GiB device
-# copy read in the same runs, by (algorithm, kernel, workload).  Each figure holds only for the sources it
-# was measured on: when the sha256 of those files (concatenated in order) differs, it is reported as null.
+# copy read in the same runs, by (algorithm, kernel, workload, output dtype).  Each figure holds only for
+# the sources it was measured on: when the sha256 of those files (concatenated in order) differs, it is
+# reported as null.
 _SCALAR = ("gated_delta_rule_26_amd/csrc/chunk_matrix.hip", "gated_delta_rule_26_amd/csrc/matrix_common.h")
 _PER_CHANNEL = ("gated_delta_rule_26_amd/csrc/chunk_matrix_pc.hip", "gated_delta_rule_26_amd/csrc/matrix_common.h")
 _DECODE = ("gated_delta_rule_26_amd/csrc/recurrent_step.hip",)
+_SHA_SCALAR = "4c7a4f5d2ac673e3b353b7d5545d145eaa2b619a18e3f53ced3437b273e43536"
+_SHA_PC = "c169a618a16b18c91e6fd2407dc6a11459d69f474008326c3e482928bc74c54c"
+_SHA_DECODE = "2a51e82863d6794848b5853d96e23d47226519bfc4408e81297cd141dc4ceaee"
 MEASURED_TRAFFIC = {
-    ("matrix", "state", "gdn_prefill"): (_SCALAR, "4c7a4f5d2ac673e3b353b7d5545d145eaa2b619a18e3f53ced3437b273e43536",
-                                         (148668.0 * 2.0 + 135171.4) * 1024),
-    ("matrix", "intra", "gdn_prefill"): (_SCALAR, "4c7a4f5d2ac673e3b353b7d5545d145eaa2b619a18e3f53ced3437b273e43536",
-                                         (66815.8 * 2.0 + 100352.0) * 1024),
-    ("matrix", "state", "kda_prefill"): (_PER_CHANNEL, "c169a618a16b18c91e6fd2407dc6a11459d69f474008326c3e482928bc74c54c",
-                                         (279778.8 * 2.0 + 133120.0) * 1024),
-    ("matrix", "intra", "kda_prefill"): (_PER_CHANNEL, "c169a618a16b18c91e6fd2407dc6a11459d69f474008326c3e482928bc74c54c",
-                                         (134593.4 * 2.0 + 493568.1) * 1024),
+    ("matrix", "state", "gdn_prefill", "f32"): (_SCALAR, _SHA_SCALAR, (148668.0 * 2.0 + 135171.4) * 1024),
+    ("matrix", "intra", "gdn_prefill", "f32"): (_SCALAR, _SHA_SCALAR, (66815.8 * 2.0 + 100352.0) * 1024),
+    ("matrix", "state", "kda_prefill", "f32"): (_PER_CHANNEL, _SHA_PC, (279778.8 * 2.0 + 133120.0) * 1024),
+    ("matrix", "intra", "kda_prefill", "f32"): (_PER_CHANNEL, _SHA_PC, (134593.4 * 2.0 + 493568.1) * 1024),
     # the state phase of the long sequence is three launches: the segment transfer walk, the
     # combine of the entering states and the per-segment walk
-    ("matrix", "state", "kla_prefill"): (_SCALAR, "4c7a4f5d2ac673e3b353b7d5545d145eaa2b619a18e3f53ced3437b273e43536",
-                                         (730910.4 * 2.0 + 8192.0 + 15398.6 * 2.0 + 4096.0
-                                          + 1190090.4 * 2.0 + 1049612.7) * 1024),
-    ("matrix", "intra", "kla_prefill"): (_SCALAR, "4c7a4f5d2ac673e3b353b7d5545d145eaa2b619a18e3f53ced3437b273e43536",
-                                         (656909.6 * 2.0 + 802816.0) * 1024),
-    ("decode", "step", "decode"): (_DECODE, "2a51e82863d6794848b5853d96e23d47226519bfc4408e81297cd141dc4ceaee",
-                                   (132972.8 * 2.0 + 264192.0) * 1024),
+    ("matrix", "state", "kla_prefill", "f32"): (_SCALAR, _SHA_SCALAR,
+                                                (730910.4 * 2.0 + 8192.0 + 15398.6 * 2.0 + 4096.0
+                                                 + 1190090.4 * 2.0 + 1049612.7) * 1024),
+    ("matrix", "intra", "kla_prefill", "f32"): (_SCALAR, _SHA_SCALAR, (656909.6 * 2.0 + 802816.0) * 1024),
+    ("decode", "step", "decode", "f32"): (_DECODE, _SHA_DECODE, (132972.8 * 2.0 + 264192.0) * 1024),
 }
 
 
@@ -61,13 +67,10 @@ MEASURED_TRAFFIC = {
 # (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) per second.  The issued flops count every bf16 hi/lo product, so they
 # exceed the algorithmic flops.  (files, sha, busy fraction, issued TFLOP/s), as for the traffic.
 MEASURED_MFMA = {
-    ("matrix", "state", "gdn_prefill"): (_SCALAR, "4c7a4f5d2ac673e3b353b7d5545d145eaa2b619a18e3f53ced3437b273e43536",
-                                         0.187, 452.2),
-    ("matrix", "state", "kda_prefill"): (_PER_CHANNEL, "c169a618a16b18c91e6fd2407dc6a11459d69f474008326c3e482928bc74c54c",
-                                         0.079, 197.2),
+    ("matrix", "state", "gdn_prefill", "f32"): (_SCALAR, _SHA_SCALAR, 0.187, 452.2),
+    ("matrix", "state", "kda_prefill", "f32"): (_PER_CHANNEL, _SHA_PC, 0.079, 197.2),
     # the long sequence: transfer + combine + walk, weighted by duration
-    ("matrix", "state", "kla_prefill"): (_SCALAR, "4c7a4f5d2ac673e3b353b7d5545d145eaa2b619a18e3f53ced3437b273e43536",
-                                         0.243, 537.6),
+    ("matrix", "state", "kla_prefill", "f32"): (_SCALAR, _SHA_SCALAR, 0.243, 537.6),
 }
 
 
@@ -80,33 +83,27 @@ def sources_sha(files) -> str:
     return h.hexdigest()
 
 
-def measured_mfma(path_kind: str, kernel: str, workload: str):
+def _current(entry):
+    if entry is None:
+        return None
+    files, sha = entry[0], entry[1]
+    try:
+        return entry if sources_sha(files) == sha else None
+    except OSError:
+        return None
+
+
+def measured_mfma(path_kind: str, kernel: str, workload: str, o_dtype: str = "f32"):
     """Counter-measured matrix-core busy fraction and issued TFLOP/s, or None if not measured on the current
     sources."""
-    entry = MEASURED_MFMA.get((path_kind, kernel, workload))
-    if entry is None:
-        return None
-    files, sha, busy, issued = entry
-    try:
-        if sources_sha(files) != sha:
-            return None
-    except OSError:
-        return None
-    return {"counter_busy_frac": busy, "issued_tflops": issued}
+    entry = _current(MEASURED_MFMA.get((path_kind, kernel, workload, o_dtype)))
+    return None if entry is None else {"counter_busy_frac": entry[2], "issued_tflops": entry[3]}
 
 
-def measured_traffic(path_kind: str, kernel: str, workload: str):
+def measured_traffic(path_kind: str, kernel: str, workload: str, o_dtype: str = "f32"):
     """Counter-measured HBM bytes per launch, or None if not measured on the current sources."""
-    entry = MEASURED_TRAFFIC.get((path_kind, kernel, workload))
-    if entry is None:
-        return None
-    files, sha, nbytes = entry
-    try:
-        if sources_sha(files) != sha:
-            return None
-    except OSError:
-        return None
-    return nbytes
+    entry = _current(MEASURED_TRAFFIC.get((path_kind, kernel, workload, o_dtype)))
+    return None if entry is None else entry[2]
 
 
 def alg_flops_per_token_head(dk: int, dv: int) -> dict:
@@ -146,44 +143,47 @@ def decode_bytes_per_step(N, H, dk, dv, in_bytes=2, out_bytes=4) -> float:
     return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * in_bytes + 8 + dv * out_bytes)
 
 
-def cpu_baseline(w, x, heads=None, min_seconds=10.0, max_passes=64):
-    """The fp64 oracle, as it stands, on the same prefill inputs: whole passes over the sampled
-    (batch, head) pairs, repeated until about min_seconds of wall time have passed, so that short
-    workloads are timed over a long enough window."""
-    import oracle
-    threads = oracle.max_threads()
-    nbh = w.B * w.H
-    heads = list(range(nbh)) if heads is None else heads
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.oracle_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], per_channel=w.per_channel,
-                          kaczmarz=w.kaczmarz, eps=w.eps, heads=heads, threads=threads)
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds or passes >= max_passes:
-            break
-    tok_heads = passes * len(heads) * w.T
-    return {"value": tok_heads / w.H / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{w.name}: {len(heads)} of {nbh} (batch, head) pairs, all {w.T} tokens each, fp64 "
-                      f"token recurrence, {passes} passes; {dt:.2f} s wall x {threads} threads; tokens/s "
-                      f"counts all {w.H} heads of a token",
-            "seconds": dt, "passes": passes, "cpu": platform.processor() or platform.machine()}
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
-def bench_prefill(w, steps, warmup, algo, o_dtype, cold_steps=0):
+def median(xs):
+    ys = sorted(xs)
+    return ys[len(ys) // 2] if ys else float("nan")
+
+
+def mean(xs):
+    return sum(xs) / len(xs) if xs else float("nan")
+
+
+def _to_device(x, w, dev):
     import torch
-    import gated_delta_rule_26_amd as gdr
-    from gdr_inputs import prefill_inputs
-
-    dev = torch.device("cuda:0")
-    x = prefill_inputs(w)
     d = {}
     for key, val in x.items():
         if val is None:
             continue
         t = torch.from_numpy(val).to(dev)
         d[key] = t.to(torch.bfloat16) if key in ("q", "k", "v") and w.dtype == "bf16" else t
+    return d
+
+
+def bench_prefill(w, x, steps, warmup, algo, o_dtype):
+    """Timed chunked passes of workload w on inputs x (numpy): `steps` with warm caches (wall clock
+    around them, and per-step events), then `steps` each after a cache flush (per-step events; the
+    flush is not inside the events).  Returns the per-step times and the last pass's o and final
+    state (on the device)."""
+    import torch
+    import gated_delta_rule_26_amd as gdr
+
+    dev = torch.device("cuda:0")
+    d = _to_device(x, w, dev)
     B, T, H, Dk, Dv = w.B, w.T, w.H, w.Dk, w.Dv
     odt = torch.float32 if o_dtype == "f32" else torch.bfloat16
     qdt = d["q"].dtype
@@ -204,9 +204,13 @@ def bench_prefill(w, steps, warmup, algo, o_dtype, cold_steps=0):
         # kernels themselves (gdr_chunk_fwd_stage_timed); each is recorded once here so that it exists
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
         for e in evs:
-            for x in e:
-                x.record()
+            for ev in e:
+                ev.record()
         return evs
+
+    def times(evs):
+        return {"intra": [e[0].elapsed_time(e[1]) for e in evs], "state": [e[2].elapsed_time(e[3]) for e in evs],
+                "step": [e[0].elapsed_time(e[3]) for e in evs]}
 
     for _ in range(warmup):
         step()
@@ -218,28 +222,82 @@ def bench_prefill(w, steps, warmup, algo, o_dtype, cold_steps=0):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    intra_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    state_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
-    # cold caches: before each of these steps a 512 MiB buffer is written, twice the 256 MB last-level
-    # (Infinity) cache, so the step's inputs come from HBM
-    cold = None
-    if cold_steps > 0:
-        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        cev = new_events(cold_steps)
-        torch.cuda.synchronize()
-        for i in range(cold_steps):
-            scratch.fill_(i & 0xff)
-            step(cev[i])
-        torch.cuda.synchronize()
-        del scratch
-        cold = {"steps": cold_steps, "step_ms_median": median([e[0].elapsed_time(e[3]) for e in cev]),
-                "intra_ms_median": median([e[0].elapsed_time(e[1]) for e in cev]),
-                "state_ms_median": median([e[2].elapsed_time(e[3]) for e in cev]),
-                "flush": "512 MiB device buffer written before each step"}
-    return {"wall_s": wall, "intra_ms": intra_ms, "state_ms": state_ms, "step_ms": step_ms, "inputs": x,
+    warm = times(evs)
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    cev = new_events(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        scratch.fill_(i & 0xff)
+        step(cev[i])
+    torch.cuda.synchronize()
+    cold_wall = time.perf_counter() - t0
+    del scratch
+    return {"warm": warm, "warm_wall_s": wall, "cold": times(cev), "cold_wall_s": cold_wall, "o": o, "s": s,
             "o_bytes": 4 if odt == torch.float32 else 2, "in_bytes": 2 if qdt == torch.bfloat16 else 4,
-            "cold": cold}
+            "workspace_bytes": ws.numel()}
+
+
+def resolve_algo(w, algo):
+    if algo != "auto":
+        return algo
+    return "matrix" if (w.dtype == "bf16" and w.Dk == 128 and w.Dv == 128 and gdr_matrix_ready(w.per_channel)) \
+        else "vector"
+
+
+def prefill_block(w, pre, algo, o_dtype):
+    """Throughput, per-kernel times and the roofline of the dominant kernel for one prefill
+    configuration, with the cold-cache step as the headline figure."""
+    tok_heads = w.B * w.T * w.H
+    fl = alg_flops_per_token_head(w.Dk, w.Dv)
+    cold, warm = pre["cold"], pre["warm"]
+    step_ms = mean(cold["step"])
+    intra_ms, state_ms = mean(cold["intra"]), mean(cold["state"])
+    dom = "state" if state_ms >= intra_ms else "intra"
+    dom_ms = state_ms if dom == "state" else intra_ms
+    dom_flops = fl[dom] * tok_heads
+    mfma_tflops = dom_flops / (dom_ms * 1e-3) / 1e12
+    # The pass's algorithmic intensity (~110 flop/B at d128 with fp32 o, ~135 with bf16 o) is below
+    # MI355X's ridge (2.5 PFLOP/s / 8 TB/s = 312 flop/B), so the roof that bounds the matrix path is
+    # HBM: the state kernel against its algorithmic bytes, with its MFMA fraction beside it.  The vector
+    # path (fp32 ALU) is bounded by its ALU peak.
+    if algo == "matrix" and dom == "state":
+        dom_bytes = alg_bytes_state_kernel(w.B, w.T, w.H, w.Dk, w.Dv, pre["in_bytes"], pre["o_bytes"])
+        achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM, "unit": "GB/s", "frac": achieved / PEAK_HBM,
+                "alg_bytes_per_launch": dom_bytes}
+    elif algo == "matrix":
+        roof = {"bound": "mfma", "achieved": mfma_tflops, "peak": PEAK_BF16_MFMA, "unit": "TFLOP/s",
+                "frac": mfma_tflops / PEAK_BF16_MFMA, "alg_bytes_per_launch": None}
+    else:
+        roof = {"bound": "alu", "achieved": mfma_tflops, "peak": PEAK_FP32_VALU, "unit": "TFLOP/s",
+                "frac": mfma_tflops / PEAK_FP32_VALU, "alg_bytes_per_launch": None}
+    roof.update({"kernel": f"{dom} ({algo} path)", "traffic": measured_traffic(algo, dom, w.name, o_dtype),
+                 "alg_flops_per_launch": dom_flops, "avg_launch_ms": dom_ms,
+                 "mfma_view": {"achieved_tflops": mfma_tflops, "peak_tflops": PEAK_BF16_MFMA,
+                               "frac": mfma_tflops / PEAK_BF16_MFMA,
+                               "counters": measured_mfma(algo, dom, w.name, o_dtype)}})
+    total_tflops = fl["total"] * tok_heads / (step_ms * 1e-3) / 1e12
+    abytes = alg_bytes_prefill(w.B, w.T, w.H, w.Dk, w.Dv, pre["in_bytes"], pre["o_bytes"], w.per_channel)
+    warm_ms = pre["warm_wall_s"] / len(warm["step"]) * 1e3
+    return {
+        "workload": f"{w.name}: chunked prefill B{w.B} H{w.H} T{w.T} d_k={w.Dk} d_v={w.Dv}, {w.dtype} q/k/v, "
+                    f"fp32 state, {o_dtype} output, chunk {C}, {w.decay} decay, {w.beta_mode} beta",
+        "algo": algo, "o_dtype": o_dtype,
+        "tokens_per_s": w.B * w.T / (step_ms * 1e-3), "ms_per_step": step_ms,
+        "ms_per_step_median": median(cold["step"]),
+        "intra_ms": intra_ms, "state_ms": state_ms,
+        "timing": "cold caches: 512 MiB written before each step (outside the events); events recorded by the "
+                  "first and last kernels of each stage",
+        "warm": {"ms_per_step_wall": warm_ms, "tokens_per_s_wall": w.B * w.T / (warm_ms * 1e-3),
+                 "event_step_ms": mean(warm["step"]), "intra_ms": mean(warm["intra"]),
+                 "state_ms": mean(warm["state"])},
+        "roofline": roof,
+        "alg_tflops": total_tflops, "frac_bf16_mfma_peak": total_tflops / PEAK_BF16_MFMA,
+        "alg_bytes": abytes, "alg_gbps": abytes / (step_ms * 1e-3) / 1e9,
+        "frac_hbm_peak": abytes / (step_ms * 1e-3) / 1e9 / PEAK_HBM,
+        "alg_flops_per_token_head": fl, "workspace_bytes": pre["workspace_bytes"],
+    }
 
 
 def bench_backward(w, x, steps, warmup):
@@ -250,10 +308,7 @@ def bench_backward(w, x, steps, warmup):
     import gated_delta_rule_26_amd as gdr
 
     dev = torch.device("cuda:0")
-    d = {}
-    for key in ("q", "k", "v", "g", "beta"):
-        t = torch.from_numpy(x[key]).to(dev)
-        d[key] = t.to(torch.bfloat16) if key in ("q", "k", "v") and w.dtype == "bf16" else t
+    d = _to_device({key: x[key] for key in ("q", "k", "v", "g", "beta")}, w, dev)
     rng = np.random.default_rng(12345)
     d_o = torch.from_numpy(rng.standard_normal((w.B, w.T, w.H, w.Dv), dtype=np.float32)).to(dev)
     desc = gdr.make_desc(w.B, w.T, w.H, w.Dk, w.Dv, qkv_dtype=d["q"].dtype, o_dtype=torch.float32,
@@ -270,27 +325,31 @@ def bench_backward(w, x, steps, warmup):
         evs[i + 1].record()
     torch.cuda.synchronize()
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
-    return {"ms_per_step_median": median(per), "ms_per_step": sum(per) / len(per),
+    return {"ms_per_step_median": median(per), "ms_per_step": mean(per),
             "workspace_bytes": ws.numel(), "steps": steps}
 
 
-def bench_decode(w, steps, distinct):
+def bench_decode(w, steps, distinct, warmup=10):
+    """`steps` fused decode steps on the state of w (updated in place), cycling `distinct` resident
+    inputs after `warmup` untimed steps.  Returns per-step kernel and begin-to-begin times, the
+    initial state, the inputs used in order and the final state and last output (device)."""
     import torch
     import gated_delta_rule_26_amd as gdr
     from gdr_inputs import decode_state0, decode_step_inputs
 
     dev = torch.device("cuda:0")
-    state = torch.from_numpy(decode_state0(w)).to(dev)
+    s0 = decode_state0(w)
+    state = torch.from_numpy(s0).to(dev)
+    host_inputs = [decode_step_inputs(w, i) for i in range(distinct)]
     inputs = []
-    for i in range(distinct):
-        x = decode_step_inputs(w, i)
+    for x in host_inputs:
         dd = {key: torch.from_numpy(val).to(dev) for key, val in x.items()}
         for key in ("q", "k", "v"):
             dd[key] = dd[key].to(torch.bfloat16)
         inputs.append(dd)
     o = torch.empty((w.B, w.H, w.Dv), dtype=torch.float32, device=dev)
     kw = dict(per_channel=w.per_channel, kaczmarz=w.kaczmarz, eps=w.eps, o=o, o_dtype=torch.float32)
-    for i in range(10):
+    for i in range(warmup):
         dd = inputs[i % distinct]
         gdr.recurrent_step(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], state, **kw)
     # per step the kernel's begin and end, recorded by the kernel (gdr_recurrent_step_timed); each
@@ -308,7 +367,27 @@ def bench_decode(w, steps, distinct):
     wall = time.perf_counter() - t0
     kern = [e[0].elapsed_time(e[1]) for e in evs]
     step = [evs[i][0].elapsed_time(evs[i + 1][0]) for i in range(steps - 1)]  # begin to begin
-    return {"wall_s": wall, "kernel_ms": kern, "step_ms": step}
+    order = [i % distinct for i in range(warmup)] + [i % distinct for i in range(steps)]
+    return {"wall_s": wall, "kernel_ms": kern, "step_ms": step, "s0": s0, "host_inputs": host_inputs,
+            "order": order, "state": state, "o": o}
+
+
+def decode_block(w, dec, steps, distinct, note):
+    dms = mean(dec["step_ms"])        # per-step latency: kernel begin to kernel begin
+    kms = mean(dec["kernel_ms"])      # the kernel alone
+    dbytes = decode_bytes_per_step(w.B, w.H, w.Dk, w.Dv)
+    gbps = dbytes / (kms * 1e-3) / 1e9
+    state_mib = w.B * w.H * w.Dk * w.Dv * 4 / 2 ** 20
+    return {
+        "workload": f"decode: {w.B} sequences x H{w.H}, d_k=d_v={w.Dk}, bf16 q/k/v, fp32 state in place "
+                    f"({state_mib:.0f} MiB{note}), scalar decay, given beta, fp32 output; {steps} steps cycling "
+                    f"{distinct} resident inputs",
+        "ms_per_step": dms, "ms_per_step_median": median(dec["step_ms"]), "tokens_per_s": w.B / (dms * 1e-3),
+        "state_gbps_per_step": dbytes / (dms * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM, "unit": "GB/s", "frac": gbps / PEAK_HBM,
+                     "traffic": measured_traffic("decode", "step", w.name, "f32") if w.name == "decode" else None,
+                     "alg_bytes_per_launch": dbytes, "avg_launch_ms": kms},
+    }
 
 
 def serving_lengths(total, seed=2026, lo=64, hi=2048):
@@ -336,7 +415,7 @@ def _timed_calls(fn, steps, warmup):
         evs[i + 1].record()
     torch.cuda.synchronize()
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
-    return sum(per) / len(per), median(per)
+    return mean(per), median(per)
 
 
 def bench_next_rows(w, x, steps, warmup, recurrent_tokens=8):
@@ -344,21 +423,19 @@ def bench_next_rows(w, x, steps, warmup, recurrent_tokens=8):
     stages): a packed batch of a serving mix of lengths (gdr_chunk_fwd_varlen), the same batch
     without the delta rule (gdr_chunk_fwd with delta_off), and T tokens per call on the recurrent
     schedule for the decode workload's sequences (gdr_recurrent_fwd)."""
+    import itertools
     import torch
     import gated_delta_rule_26_amd as gdr
     from gdr_inputs import WORKLOADS, random_inputs
 
     dev = torch.device("cuda:0")
-    d = {}
-    for key in ("q", "k", "v", "g", "beta"):
-        t = torch.from_numpy(x[key]).to(dev)
-        d[key] = t.to(torch.bfloat16) if key in ("q", "k", "v") and w.dtype == "bf16" else t
+    d = _to_device({key: x[key] for key in ("q", "k", "v", "g", "beta")}, w, dev)
     ntok = w.B * w.T
     res = {}
 
     # packed batch: the B*T tokens as one token axis, sequences of a serving mix
     lens = serving_lengths(ntok)
-    cu = torch.tensor([0] + list(__import__("itertools").accumulate(lens)), dtype=torch.int32, device=dev)
+    cu = torch.tensor([0] + list(itertools.accumulate(lens)), dtype=torch.int32, device=dev)
     pk = {key: val.reshape((ntok,) + tuple(val.shape[2:])) for key, val in d.items()}
     N = len(lens)
     desc = gdr.make_desc(N, ntok, w.H, w.Dk, w.Dv, qkv_dtype=pk["q"].dtype, o_dtype=torch.float32,
@@ -422,6 +499,32 @@ def bench_next_rows(w, x, steps, warmup, recurrent_tokens=8):
     return res
 
 
+def measured_peaks(reps=10):
+    """What this GPU reaches on plain library work, beside the spec peaks: a 1 GiB device-to-device
+    copy (bytes read + written per second) and a bf16 GEMM of 8192^3 through torch.matmul
+    (hipBLASLt), both timed with events after a warm-up."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = 1 << 30
+    a = torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    ms_copy, _ = _timed_calls(lambda: b.copy_(a), reps, 3)
+    del a, b
+    m = 8192
+    gen = torch.Generator(device=dev).manual_seed(3)
+    x = torch.randn((m, m), dtype=torch.bfloat16, device=dev, generator=gen)
+    y = torch.randn((m, m), dtype=torch.bfloat16, device=dev, generator=gen)
+    ms_mm, _ = _timed_calls(lambda: torch.matmul(x, y), reps, 3)
+    del x, y
+    torch.cuda.empty_cache()
+    copy_gbps = 2 * n / (ms_copy * 1e-3) / 1e9
+    gemm_tflops = 2 * m ** 3 / (ms_mm * 1e-3) / 1e12
+    return {"copy_gbps": copy_gbps, "copy_frac_of_spec": copy_gbps / PEAK_HBM,
+            "bf16_gemm_tflops": gemm_tflops, "bf16_gemm_frac_of_spec": gemm_tflops / PEAK_BF16_MFMA,
+            "how": "1 GiB torch copy_ (2 GiB moved per call); torch.matmul bf16 8192x8192x8192 (hipBLASLt); "
+                   f"mean of {reps} calls timed with events after 3 warm-up calls"}
+
+
 def calibrate_copy(nbytes=1 << 30, reps=3):
     """A plain device copy of known size, so that rocprofv3 byte counters of
     the same command can be scaled (FETCH_SIZE / WRITE_SIZE per dispatch)."""
@@ -434,9 +537,90 @@ def calibrate_copy(nbytes=1 << 30, reps=3):
     return nbytes
 
 
-def median(xs):
-    ys = sorted(xs)
-    return ys[len(ys) // 2] if ys else float("nan")
+def _rel_heads(gpu_o, ref_o, gpu_s, ref_s):
+    """Aggregate and largest per-(batch, head) relative L2 of o [B,T,H,Dv] and S [B,H,Dk,Dv]."""
+    import numpy as np
+    B, _, H = ref_o.shape[:3]
+    acc = np.zeros(4)
+    worst = [0.0, 0.0]
+    for b in range(B):
+        for h in range(H):
+            for i, (g, r) in enumerate(((gpu_o[b, :, h], ref_o[b, :, h]), (gpu_s[b, h], ref_s[b, h]))):
+                dd = np.asarray(g, dtype=np.float64) - r
+                d2, r2 = float(np.sum(dd * dd)), float(np.sum(r * r))
+                acc[2 * i] += d2
+                acc[2 * i + 1] += r2
+                worst[i] = max(worst[i], (d2 / r2) ** 0.5 if r2 > 0 else d2 ** 0.5)
+    return {"rel_l2_o": float((acc[0] / acc[1]) ** 0.5), "rel_l2_s": float((acc[2] / acc[3]) ** 0.5),
+            "worst_head_rel_l2_o": worst[0], "worst_head_rel_l2_s": worst[1]}
+
+
+def cpu_baseline(w, x, gpu_runs, decode_runs, min_seconds=8.0, max_passes=64):
+    """The fp64 oracle, as it stands, on the host cores.
+
+    * The headline figure: whole passes over every (batch, head) pair of the prefill workload w,
+      repeated until about min_seconds of wall time have passed; and one pass over a single pair on
+      one thread (the per-core rate).
+    * The same oracle on the other configurations timed in this run (one pass over every pair each,
+      a bounded sample of the decode workload's steps), whose results double as the parity of the
+      GPU outputs of this run: relative L2 over all heads and the worst single head.
+    """
+    import oracle
+    threads = oracle.max_threads()
+    nbh = w.B * w.H
+    heads = list(range(nbh))
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        ref_w = oracle.oracle_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], per_channel=w.per_channel,
+                                  kaczmarz=w.kaczmarz, eps=w.eps, heads=heads, threads=threads)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or passes >= max_passes:
+            break
+    t1 = time.perf_counter()
+    oracle.oracle_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], per_channel=w.per_channel, kaczmarz=w.kaczmarz,
+                      eps=w.eps, heads=[0], threads=1)
+    dt1 = time.perf_counter() - t1
+    out = {"value": passes * nbh * w.T / w.H / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{w.name}: {nbh} of {nbh} (batch, head) pairs, all {w.T} tokens each, fp64 token "
+                     f"recurrence, {passes} passes; {dt:.2f} s wall x {threads} threads; tokens/s counts all "
+                     f"{w.H} heads of a token",
+           "seconds": dt, "passes": passes, "cpu": cpu_model(),
+           "single_thread": {"token_heads_per_s": w.T / dt1, "seconds": dt1,
+                             "sample": f"{w.name}: (batch, head) pair 0, {w.T} tokens, 1 thread"},
+           "per_config": {}}
+    for name, (wc, xc, runs) in gpu_runs.items():
+        if wc is w:  # the timed passes above
+            ref, dt2 = ref_w, dt / passes
+        else:
+            t2 = time.perf_counter()
+            ref = oracle.oracle_fwd(xc["q"], xc["k"], xc["v"], xc["g"], xc["beta"], per_channel=wc.per_channel,
+                                    kaczmarz=wc.kaczmarz, eps=wc.eps, threads=threads)
+            dt2 = time.perf_counter() - t2
+        entry = {"oracle_seconds": dt2, "oracle_tokens_per_s": wc.B * wc.T / dt2}
+        for o_dtype, (o, s) in runs.items():
+            entry[f"parity_{o_dtype}_o"] = _rel_heads(o, ref[0], s, ref[1])
+        out["per_config"][name] = entry
+    if decode_runs:
+        import numpy as np
+        wd, dec = decode_runs
+        xs = [dec["host_inputs"][i] for i in dec["order"]]
+        st = {key: np.stack([xi[key] for xi in xs]) for key in xs[0]}
+        t2 = time.perf_counter()
+        o_ref, s_ref = oracle.oracle_decode(st["q"], st["k"], st["v"], st["g"], st["beta"], dec["s0"],
+                                            threads=threads)
+        dt2 = time.perf_counter() - t2
+        o_last = dec["o"].cpu().numpy()
+        s_gpu = dec["state"].cpu().numpy()
+        d_o = o_last - o_ref[-1]
+        d_s = s_gpu - s_ref
+        out["per_config"]["decode"] = {
+            "oracle_seconds": dt2, "oracle_tokens_per_s": wd.B * len(xs) / dt2,
+            "parity_f32_o": {"rel_l2_o_last_step": float(np.linalg.norm(d_o) / np.linalg.norm(o_ref[-1])),
+                             "rel_l2_s": float(np.linalg.norm(d_s) / np.linalg.norm(s_ref)),
+                             "steps": len(xs)}}
+    return out
 
 
 def main():
@@ -447,14 +631,16 @@ def main():
     ap.add_argument("--workload", default="gdn_prefill",
                     choices=["gdn_prefill", "kda_prefill", "kla_prefill", "gdn_tiny"])
     ap.add_argument("--algo", default="auto", choices=["auto", "vector", "matrix"])
-    ap.add_argument("--o-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--o-dtype", default="bf16", choices=["f32", "bf16"])
+    ap.add_argument("--other-configs", default="gdn_tiny,kda_prefill,kla_prefill",
+                    help="comma-separated prefill workloads timed beside the headline ('' for none)")
+    ap.add_argument("--other-steps", type=int, default=10, help="timed steps of each other configuration")
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--decode-distinct", type=int, default=16,
                     help="distinct decode-step inputs kept resident and cycled through")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cold-steps", type=int, default=10,
-                    help="extra prefill steps, each after writing 512 MiB to evict the last-level cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the copy and GEMM peak measurements")
     ap.add_argument("--backward-steps", type=int, default=5,
                     help="timed calls of the backward pass on the prefill workload (0: skip)")
     ap.add_argument("--next-rows-steps", type=int, default=5,
@@ -472,121 +658,101 @@ def main():
 
     import torch
     import gated_delta_rule_26_amd as gdr
-    from gdr_inputs import WORKLOADS
+    from gdr_inputs import WORKLOADS, prefill_inputs
 
     gdr.load_library()  # fail loudly if the HIP library is missing
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(3)
 
+    def host(t):
+        return t.float().cpu().numpy()
+
     w = WORKLOADS[args.workload]
-    pre = bench_prefill(w, args.steps, args.warmup, args.algo, args.o_dtype, args.cold_steps)
-    tok_heads = w.B * w.T * w.H
-    ms_step = pre["wall_s"] / args.steps * 1e3
-    value = w.B * w.T / (ms_step / 1e3)
-    fl = alg_flops_per_token_head(w.Dk, w.Dv)
-    intra_ms = sum(pre["intra_ms"]) / len(pre["intra_ms"])
-    state_ms = sum(pre["state_ms"]) / len(pre["state_ms"])
-    event_step_ms = sum(pre["step_ms"]) / len(pre["step_ms"])
-    algo = args.algo
-    if algo == "auto":
-        algo = "matrix" if (w.dtype == "bf16" and w.Dk == 128 and w.Dv == 128 and
-                            gdr_matrix_ready(w.per_channel)) else "vector"
-    dom = "state" if state_ms >= intra_ms else "intra"
-    dom_ms = state_ms if dom == "state" else intra_ms
-    dom_flops = fl[dom] * tok_heads
-    # The pass's algorithmic intensity (~110 flop/B at d128) is below MI355X's
-    # ridge (2.5 PFLOP/s / 8 TB/s = 312 flop/B), so the roof that bounds the
-    # matrix path is HBM: the state kernel against its algorithmic bytes.  The
-    # MFMA view of the same kernel is reported beside it.  The vector path
-    # (fp32 ALU) is bounded by its ALU peak.
-    if algo == "matrix" and dom == "state":
-        bound, peak, unit = "hbm", PEAK_HBM, "GB/s"
-        dom_bytes = alg_bytes_state_kernel(w.B, w.T, w.H, w.Dk, w.Dv, pre["in_bytes"], pre["o_bytes"])
-        achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    elif algo == "matrix":
-        bound, peak, unit = "mfma", PEAK_BF16_MFMA, "TFLOP/s"
-        dom_bytes = None
-        achieved = dom_flops / (dom_ms * 1e-3) / 1e12
-    else:
-        bound, peak, unit = "alu", PEAK_FP32_VALU, "TFLOP/s"
-        dom_bytes = None
-        achieved = dom_flops / (dom_ms * 1e-3) / 1e12
-    mfma_view = dom_flops / (dom_ms * 1e-3) / 1e12
-    total_tflops = fl["total"] * tok_heads / (event_step_ms * 1e-3) / 1e12
-    abytes = alg_bytes_prefill(w.B, w.T, w.H, w.Dk, w.Dv, pre["in_bytes"], pre["o_bytes"], w.per_channel)
+    x = prefill_inputs(w)
+    algo = resolve_algo(w, args.algo)
+    pre = bench_prefill(w, x, args.steps, args.warmup, algo, args.o_dtype)
+    head = prefill_block(w, pre, algo, args.o_dtype)
+    gpu_runs = {w.name: (w, x, {args.o_dtype: (host(pre["o"]), host(pre["s"]))})}
+    del pre
+    other_o = "f32" if args.o_dtype == "bf16" else "bf16"
+    pre2 = bench_prefill(w, x, args.other_steps, 2, algo, other_o)
+    gpu_runs[w.name][2][other_o] = (host(pre2["o"]), host(pre2["s"]))
+    beside = prefill_block(w, pre2, algo, other_o)
+    del pre2
+    torch.cuda.empty_cache()
 
     out = {
         "metric": "prefill tokens/s (chunkwise GDN, H16 d128, % MFMA peak) + decode HBM GB/s",
-        "value": value,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if algo == "matrix" else "f32",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: chunked prefill B{w.B} H{w.H} T{w.T} d_k={w.Dk} d_v={w.Dv}, "
-                               f"{w.dtype} q/k/v, fp32 state, {args.o_dtype} output, chunk {C}, "
-                               f"{w.decay} decay, {w.beta_mode} beta",
-                   "B": w.B, "T": w.T, "H": w.H, "Dk": w.Dk, "Dv": w.Dv, "chunk": C,
-                   "algo": algo, "o_dtype": args.o_dtype},
-        "roofline": {"bound": bound, "kernel": f"{dom} ({algo} path)", "achieved": achieved, "peak": peak,
-                     "unit": unit, "frac": achieved / peak, "traffic": measured_traffic(algo, dom, w.name),
-                     "alg_bytes_per_launch": dom_bytes, "alg_flops_per_launch": dom_flops,
-                     "avg_launch_ms": dom_ms,
-                     "mfma_view": {"achieved_tflops": mfma_view, "peak_tflops": PEAK_BF16_MFMA,
-                                   "frac": mfma_view / PEAK_BF16_MFMA,
-                                   "counters": measured_mfma(algo, dom, w.name)}},
-        "prefill": {"intra_ms": intra_ms, "state_ms": state_ms, "event_step_ms": event_step_ms,
-                    "intra_ms_median": median(pre["intra_ms"]), "state_ms_median": median(pre["state_ms"]),
-                    "cold_cache": pre["cold"],
-                    "alg_tflops": total_tflops, "frac_bf16_mfma_peak": total_tflops / PEAK_BF16_MFMA,
-                    "alg_bytes": abytes, "alg_gbps": abytes / (event_step_ms * 1e-3) / 1e9,
-                    "frac_hbm_peak": abytes / (event_step_ms * 1e-3) / 1e9 / PEAK_HBM,
-                    "alg_flops_per_token_head": fl},
+        "config": {"workload": head["workload"], "B": w.B, "T": w.T, "H": w.H, "Dk": w.Dk, "Dv": w.Dv,
+                   "chunk": C, "algo": algo, "o_dtype": args.o_dtype, "timing": head["timing"]},
+        "mfma_peak_frac": head["frac_bf16_mfma_peak"],
+        "roofline": head["roofline"],
+        "prefill": {key: head[key] for key in ("tokens_per_s", "ms_per_step", "ms_per_step_median", "intra_ms",
+                                               "state_ms", "warm", "alg_tflops", "frac_bf16_mfma_peak",
+                                               "alg_bytes", "alg_gbps", "frac_hbm_peak",
+                                               "alg_flops_per_token_head", "workspace_bytes")},
+        "prefill_other_output": beside,
+        "configs": {},
     }
 
+    for name in [n for n in args.other_configs.split(",") if n and n != w.name]:
+        wc = WORKLOADS[name]
+        xc = prefill_inputs(wc)
+        ac = resolve_algo(wc, args.algo)
+        od = "f32" if wc.dtype == "f32" else args.o_dtype
+        pc = bench_prefill(wc, xc, args.other_steps, 2, ac, od)
+        out["configs"][name] = prefill_block(wc, pc, ac, od)
+        gpu_runs[name] = (wc, xc, {od: (host(pc["o"]), host(pc["s"]))})
+        del pc
+        torch.cuda.empty_cache()
+
+    decode_runs = None
     if not args.no_decode:
         wd = WORKLOADS["decode"]
         dec = bench_decode(wd, args.decode_steps, args.decode_distinct)
-        dms = sum(dec["step_ms"]) / len(dec["step_ms"])        # per-step latency: kernel begin to kernel begin
-        kms = sum(dec["kernel_ms"]) / len(dec["kernel_ms"])    # the kernel alone
-        dbytes = decode_bytes_per_step(wd.B, wd.H, wd.Dk, wd.Dv)
-        gbps = dbytes / (kms * 1e-3) / 1e9
-        out["decode"] = {
-            "workload": f"decode: {wd.B} sequences x H{wd.H}, d_k=d_v={wd.Dk}, bf16 q/k/v, fp32 state in place, "
-                        f"scalar decay, given beta; {args.decode_steps} steps cycling {args.decode_distinct} "
-                        f"resident inputs",
-            "ms_per_step": dms, "ms_per_step_median": median(dec["step_ms"]),
-            "tokens_per_s": wd.B / (dms * 1e-3),
-            "state_gbps_per_step": dbytes / (dms * 1e-3) / 1e9,
-            "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM, "unit": "GB/s",
-                         "frac": gbps / PEAK_HBM, "traffic": measured_traffic("decode", "step", "decode"),
-                         "alg_bytes_per_launch": dbytes,
-                         "avg_launch_ms": kms},
-        }
+        out["decode"] = decode_block(wd, dec, args.decode_steps, args.decode_distinct,
+                                     ", the size of the 256 MB last-level cache")
+        decode_runs = (wd, dec)
+        # twice the sequences: a 512 MiB state the last-level cache cannot hold
+        wb = wd.scaled(name="decode_512", B=2 * wd.B)
+        decb = bench_decode(wb, args.decode_steps, args.decode_distinct)
+        out["decode_beyond_cache"] = decode_block(wb, decb, args.decode_steps, args.decode_distinct,
+                                                  ", twice the 256 MB last-level cache")
+        del decb
+        torch.cuda.empty_cache()
+
+    if not args.no_peaks:
+        out["peaks_measured"] = measured_peaks()
 
     if args.backward_steps > 0:
-        bwd = bench_backward(w, pre["inputs"], args.backward_steps, 1)
+        bwd = bench_backward(w, x, args.backward_steps, 1)
         out["backward"] = {
             "workload": f"{w.name}: gdr_chunk_bwd on the same inputs, standard-normal dL/do, fp32 gradients "
                         f"(fp32 arithmetic, matrix-core tiles)",
             **bwd,
-            "train_step_tokens_per_s": w.B * w.T / ((event_step_ms + bwd["ms_per_step"]) * 1e-3),
+            "train_step_tokens_per_s": w.B * w.T / ((head["warm"]["event_step_ms"] + bwd["ms_per_step"]) * 1e-3),
         }
 
     if args.next_rows_steps > 0 and not w.per_channel:
-        out["next_rows"] = bench_next_rows(w, pre["inputs"], args.next_rows_steps, 2)
+        out["next_rows"] = bench_next_rows(w, x, args.next_rows_steps, 2)
 
     if args.calibrate_copy:
         out["calibration_copy_bytes"] = calibrate_copy()
 
     if not args.no_cpu_baseline and rank == 0:
-        out["cpu_baseline"] = cpu_baseline(w, pre["inputs"])
+        out["cpu_baseline"] = cpu_baseline(w, x, gpu_runs, decode_runs)
 
     print(json.dumps(out), flush=True)
 

@@ -37,7 +37,12 @@ def test_algorithmic_counts_at_d128():
 
 def test_counter_figures_follow_their_sources():
     # each recorded figure names the files it was measured on; a figure whose files changed is dropped
-    for key, (files, sha, _value) in bench.MEASURED_TRAFFIC.items():
+    for key, (files, sha, *_value) in list(bench.MEASURED_TRAFFIC.items()) + list(bench.MEASURED_MFMA.items()):
         assert all(os.path.exists(os.path.join(ROOT, f)) for f in files), key
-        expected = bench.measured_traffic(*key)
-        assert (expected is not None) == (bench.sources_sha(files) == sha), key
+        fn = bench.measured_traffic if key in bench.MEASURED_TRAFFIC else bench.measured_mfma
+        assert (fn(*key) is not None) == (bench.sources_sha(files) == sha), key
+
+
+def test_cpu_model_is_named():
+    name = bench.cpu_model()
+    assert isinstance(name, str) and name and name != "x86_64"
