@@ -36,6 +36,18 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// The updated state goes back with non-temporal stores: it is not read again
+// within the call, and the next call usually comes after other work, so
+// keeping it in the caches only displaces other data.  Measured on the decode
+// workload, whose 256 MiB state fills the last-level cache: 83 us per step
+// against 80 us with ordinary stores; with 512 sequences (a 512 MiB state,
+// twice that cache) 164 us against 216 us.
+__device__ __forceinline__ void store_state(float *p, float4 v) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4 t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<f32x4 *>(p));
+}
+
 // The token span [t0, end) of sequence n of a packed batch.  Its offsets are
 // cu[n] and cu[n+1], each clamped to [0, T] and raised to the largest offset
 // before it: t0 = max over i <= n of clamp(cu[i]), end = max(t0,
@@ -199,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
 
 #pragma unroll
     for (int p = 0; p < PASSES; ++p)
-        *reinterpret_cast<float4 *>(S + (size_t)(p * RPP + r0) * DV + 4 * c4) = s[p];
+        store_state(S + (size_t)(p * RPP + r0) * DV + 4 * c4, s[p]);
 }
 
 // Several tokens per sequence: the same recurrence and thread layout, with
@@ -346,7 +358,7 @@ __global__ __launch_bounds__(kThreads, 3) void recurrent_tokens_kernel(
 
 #pragma unroll
     for (int p = 0; p < PASSES; ++p)
-        *reinterpret_cast<float4 *>(S + (size_t)(p * RPP + r0) * DV + 4 * c4) = s[p];
+        store_state(S + (size_t)(p * RPP + r0) * DV + 4 * c4, s[p]);
 }
 
 template <int DK, int DV, bool PC, bool KZ, bool IB, bool OB>
