@@ -41,24 +41,30 @@ FLUSH_BYTES = 512 << 20      # twice the 256 MB last-level cache
 # copy read in the same runs, by (algorithm, kernel, workload, output dtype).  Each figure holds only for
 # the sources it was measured on: when the sha256 of those files (concatenated in order) differs, it is
 # reported as null.
-_SCALAR = ("gated_delta_rule_26_amd/csrc/chunk_matrix.hip", "gated_delta_rule_26_amd/csrc/matrix_common.h")
-_PER_CHANNEL = ("gated_delta_rule_26_amd/csrc/chunk_matrix_pc.hip", "gated_delta_rule_26_amd/csrc/matrix_common.h")
-_DECODE = ("gated_delta_rule_26_amd/csrc/recurrent_step.hip",)
-_SHA_SCALAR = "4c7a4f5d2ac673e3b353b7d5545d145eaa2b619a18e3f53ced3437b273e43536"
-_SHA_PC = "c169a618a16b18c91e6fd2407dc6a11459d69f474008326c3e482928bc74c54c"
-_SHA_DECODE = "2a51e82863d6794848b5853d96e23d47226519bfc4408e81297cd141dc4ceaee"
+# The build script is part of each group: it holds the compiler options the kernels are built with.
+_BUILD = "gated_delta_rule_26_amd/build.py"
+_SCALAR = ("gated_delta_rule_26_amd/csrc/chunk_matrix.hip", "gated_delta_rule_26_amd/csrc/matrix_common.h", _BUILD)
+_PER_CHANNEL = ("gated_delta_rule_26_amd/csrc/chunk_matrix_pc.hip", "gated_delta_rule_26_amd/csrc/matrix_common.h",
+                _BUILD)
+_DECODE = ("gated_delta_rule_26_amd/csrc/recurrent_step.hip", _BUILD)
+_SHA_SCALAR = "ef1025a7ff7141b058181914da1c35a8bfa63d7e8722ed2218e50bed5ab5d14f"
+_SHA_PC = "9683e4bcf87c67802c147a54ca5d839a9bd664caa8790cb9148b98f6511a4a4f"
+_SHA_DECODE = "32418c0ee1020b20d96212e92a32fa306ea808bb4ec78f7b7f401d35e5af79d4"
 MEASURED_TRAFFIC = {
-    ("matrix", "state", "gdn_prefill", "f32"): (_SCALAR, _SHA_SCALAR, (148668.0 * 2.0 + 135171.4) * 1024),
-    ("matrix", "intra", "gdn_prefill", "f32"): (_SCALAR, _SHA_SCALAR, (66815.8 * 2.0 + 100352.0) * 1024),
-    ("matrix", "state", "kda_prefill", "f32"): (_PER_CHANNEL, _SHA_PC, (279778.8 * 2.0 + 133120.0) * 1024),
-    ("matrix", "intra", "kda_prefill", "f32"): (_PER_CHANNEL, _SHA_PC, (134593.4 * 2.0 + 493568.1) * 1024),
+    ("matrix", "state", "gdn_prefill", "bf16"): (_SCALAR, _SHA_SCALAR, (148650.2 * 2.0 + 69647.1) * 1024),
+    ("matrix", "intra", "gdn_prefill", "bf16"): (_SCALAR, _SHA_SCALAR, (66974.5 * 2.0 + 100352.0) * 1024),
+    ("matrix", "state", "gdn_prefill", "f32"): (_SCALAR, _SHA_SCALAR, (148651.3 * 2.0 + 135248.0) * 1024),
+    ("matrix", "intra", "gdn_prefill", "f32"): (_SCALAR, _SHA_SCALAR, (66974.5 * 2.0 + 100352.0) * 1024),
+    ("matrix", "state", "kda_prefill", "bf16"): (_PER_CHANNEL, _SHA_PC, (279780.9 * 2.0 + 93798.5) * 1024),
+    ("matrix", "intra", "kda_prefill", "bf16"): (_PER_CHANNEL, _SHA_PC, (134542.8 * 2.0 + 493568.1) * 1024),
     # the state phase of the long sequence is three launches: the segment transfer walk, the
     # combine of the entering states and the per-segment walk
-    ("matrix", "state", "kla_prefill", "f32"): (_SCALAR, _SHA_SCALAR,
-                                                (730910.4 * 2.0 + 8192.0 + 15398.6 * 2.0 + 4096.0
-                                                 + 1190090.4 * 2.0 + 1049612.7) * 1024),
-    ("matrix", "intra", "kla_prefill", "f32"): (_SCALAR, _SHA_SCALAR, (656909.6 * 2.0 + 802816.0) * 1024),
-    ("decode", "step", "decode", "f32"): (_DECODE, _SHA_DECODE, (132972.8 * 2.0 + 264192.0) * 1024),
+    ("matrix", "state", "kla_prefill", "bf16"): (_SCALAR, _SHA_SCALAR,
+                                                 (729892.0 * 2.0 + 8192.0 + 15398.6 * 2.0 + 4096.0
+                                                  + 1190075.7 * 2.0 + 525347.1) * 1024),
+    ("matrix", "intra", "kla_prefill", "bf16"): (_SCALAR, _SHA_SCALAR, (656322.9 * 2.0 + 802816.0) * 1024),
+    ("decode", "step", "decode", "f32"): (_DECODE, _SHA_DECODE, (132913.0 * 2.0 + 264729.0) * 1024),
+    ("decode", "step", "decode_512", "f32"): (_DECODE, _SHA_DECODE, (265782.2 * 2.0 + 529423.2) * 1024),
 }
 
 
@@ -67,10 +73,10 @@ MEASURED_TRAFFIC = {
 # (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) per second.  The issued flops count every bf16 hi/lo product, so they
 # exceed the algorithmic flops.  (files, sha, busy fraction, issued TFLOP/s), as for the traffic.
 MEASURED_MFMA = {
-    ("matrix", "state", "gdn_prefill", "f32"): (_SCALAR, _SHA_SCALAR, 0.187, 452.2),
-    ("matrix", "state", "kda_prefill", "f32"): (_PER_CHANNEL, _SHA_PC, 0.079, 197.2),
+    ("matrix", "state", "gdn_prefill", "bf16"): (_SCALAR, _SHA_SCALAR, 0.198, 478.2),
+    ("matrix", "state", "kda_prefill", "bf16"): (_PER_CHANNEL, _SHA_PC, 0.080, 199.2),
     # the long sequence: transfer + combine + walk, weighted by duration
-    ("matrix", "state", "kla_prefill", "f32"): (_SCALAR, _SHA_SCALAR, 0.243, 537.6),
+    ("matrix", "state", "kla_prefill", "bf16"): (_SCALAR, _SHA_SCALAR, 0.245, 556.5),
 }
 
 
@@ -385,7 +391,7 @@ def decode_block(w, dec, steps, distinct, note):
         "ms_per_step": dms, "ms_per_step_median": median(dec["step_ms"]), "tokens_per_s": w.B / (dms * 1e-3),
         "state_gbps_per_step": dbytes / (dms * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM, "unit": "GB/s", "frac": gbps / PEAK_HBM,
-                     "traffic": measured_traffic("decode", "step", w.name, "f32") if w.name == "decode" else None,
+                     "traffic": measured_traffic("decode", "step", w.name, "f32"),
                      "alg_bytes_per_launch": dbytes, "avg_launch_ms": kms},
     }
 
