@@ -1320,6 +1320,182 @@ __global__ __launch_bounds__(kThreads, IN_BF16 && !PC ? 2 : 1) void bwd_grads_b_
     }
 }
 
+// ============================================================ forward pass on fp32 tiles
+// The chunked forward pass for the inputs the bf16 matrix-core kernels do not
+// take (fp32 q/k/v, or d_k or d_v = 64): the prep kernel above forms the
+// per-chunk T, A and decayed operands, then this walk, which is the forward
+// walk above with the chunk's outputs O = Q~ S + A E formed before the state
+// moves on (Q~ S with the entering state, the diagonal of A kept: read after
+// write), and the final state written once instead of every entering state.
+// fp32 operands and accumulation throughout, as the vector-ALU kernels.
+// Q~ and A come straight from the workspace into registers at the start of
+// each chunk (the LDS holds the walk's own operands): lane (lr, lg) of
+// wavefront w holds row 16 w + lr of each, columns 16 t + 4 lg + e
+// (t = 0.., e = 0..3) as float4s, which is the reduction order of its
+// products: step (t, e) of a product takes reduction index 16 t + 4 lg + e
+// from lane group lg on both operands.
+template <int DK, int DV, bool PC, bool IN_BF16, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void fwd_tile_walk_kernel(
+    const void *__restrict__ v, int T, int H, int NC, const float *__restrict__ wT, const float *__restrict__ wA,
+    const float *__restrict__ wG, const float *__restrict__ wB, const float *__restrict__ wKt,
+    const float *__restrict__ wKh, const float *__restrict__ wQt, const float *__restrict__ s0,
+    void *__restrict__ o, float *__restrict__ s_final, bool delta, SeqTable tb) {
+    constexpr int GK = PC ? DK : 1;
+    constexpr int NT = DV / kBV;
+    constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads;
+    constexpr int SRB = DK / 64;  // state row blocks per wavefront
+    constexpr int NQ = DK / 16;   // float4 groups of a Q~ row per lane
+    const int tile = blockIdx.x % NT, bh = blockIdx.x / NT;
+    const BwdWalk wk = bwd_walk(bh, T, H, NC, tb);
+    const int j0 = tile * kBV;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    __shared__ float sS[DK * kLB];
+    __shared__ float sKt[C * kLK];
+    __shared__ float sKh[C * kLKT];
+    __shared__ float sT[C * kLT];     // T'' = T Diag(beta)
+    __shared__ float sX[C * kLB];
+    __shared__ float sE[C * kLB];
+    __shared__ float sBeta[C], sGam[DK];
+
+    float rT[NTT], rKt[NKK], rKh[NKK], rB = 0.f, rGam = 0.f;
+    f32x4 rV[2];  // the v slice in the layout of this wavefront's X tiles
+    auto fetch = [&](int c) {
+        const size_t ci = wk.slot(c);
+        const int n = wk.count(c);
+        const size_t row0 = wk.row0(c);
+#pragma unroll
+        for (int u = 0; u < NTT; ++u) rT[u] = wT[ci * C * C + tid + u * kThreads];
+#pragma unroll
+        for (int u = 0; u < NKK; ++u) {
+            rKt[u] = wKt[ci * C * DK + tid + u * kThreads];
+            rKh[u] = wKh[ci * C * DK + tid + u * kThreads];
+        }
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * w + 4 * lg + r;
+                rV[J][r] = i < n ? load_in<IN_BF16>(v, (row0 + (size_t)i * H) * DV + j0 + 16 * J + lr) : 0.f;
+            }
+        if (tid < C) rB = wB[ci * C + tid];
+        if (tid < DK) rGam = __expf(wG[ci * C * GK + (size_t)(C - 1) * GK + (PC ? tid : 0)]);
+    };
+
+    const size_t sbase = (size_t)bh * DK * DV;
+    for (int idx = tid; idx < DK * kBV; idx += kThreads) {
+        const int r = idx / kBV, cc = idx % kBV;
+        sS[r * kLB + cc] = s0 ? s0[sbase + (size_t)r * DV + j0 + cc] : 0.f;
+    }
+    if (wk.nc > 0) fetch(0);
+    for (int c = 0; c < wk.nc; ++c) {
+        const size_t ci = wk.slot(c);
+        const int n = wk.count(c);
+        const size_t row0 = wk.row0(c);
+        // this chunk's Q~ and A rows (only the blocks on or below the diagonal of A)
+        f32x4 rQ[NQ], rA[4];
+        const float *qrow = wQt + ci * C * DK + (size_t)(16 * w + lr) * DK + 4 * lg;
+        const float *arow = wA + ci * C * C + (size_t)(16 * w + lr) * C + 4 * lg;
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) rQ[t] = *reinterpret_cast<const f32x4 *>(qrow + 16 * t);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) rA[t] = t <= w ? *reinterpret_cast<const f32x4 *>(arow + 16 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
+        __syncthreads();  // the previous chunk's reads are done; sS holds the entering state
+        if (tid < C) sBeta[tid] = rB;
+        if (tid < DK) sGam[tid] = rGam;
+#pragma unroll
+        for (int u = 0; u < NKK; ++u) {
+            const int idx = tid + u * kThreads;
+            sKt[(idx / DK) * kLK + idx % DK] = rKt[u];
+            sKh[(idx / DK) * kLKT + idx % DK] = rKh[u];
+        }
+        __syncthreads();  // sBeta
+#pragma unroll
+        for (int u = 0; u < NTT; ++u) {
+            const int idx = tid + u * kThreads, i = idx / C, m = idx % C;
+            sT[i * kLT + m] = rT[u] * sBeta[m];
+        }
+        f32x4 x[2] = {rV[0], rV[1]};
+        if (c + 1 < wk.nc) fetch(c + 1);
+        // X = V - K~ S (rows 16w ..; X = V without the delta rule)
+        for (int kk = 0; delta && kk < DK; kk += 4) {
+            const float a = -sKt[(16 * w + lr) * kLK + kk + lg];
+#pragma unroll
+            for (int J = 0; J < 2; ++J) x[J] = mfma4(a, sS[(kk + lg) * kLB + 16 * J + lr], x[J]);
+        }
+        // the read of the entering state, Q~ S (rows 16w ..)
+        f32x4 oo[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int t = 0; t < NQ; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int J = 0; J < 2; ++J)
+                    oo[J] = mfma4(rQ[t][e], sS[(16 * t + 4 * lg + e) * kLB + 16 * J + lr], oo[J]);
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sX[(16 * w + 4 * lg + r) * kLB + 16 * J + lr] = x[J][r];
+        __syncthreads();  // X, T''
+        f32x4 e[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        for (int kk = 0; kk < 16 * (w + 1); kk += 4) {  // T'' is lower triangular
+            const float a = sT[(16 * w + lr) * kLT + kk + lg];
+#pragma unroll
+            for (int J = 0; J < 2; ++J) e[J] = mfma4(a, sX[(kk + lg) * kLB + 16 * J + lr], e[J]);
+        }
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sE[(16 * w + 4 * lg + r) * kLB + 16 * J + lr] = e[J][r];
+        __syncthreads();  // E
+        // the in-chunk read A E (A lower triangular, diagonal kept), then the outputs
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (t > w) break;
+#pragma unroll
+            for (int ee = 0; ee < 4; ++ee)
+#pragma unroll
+                for (int J = 0; J < 2; ++J)
+                    oo[J] = mfma4(rA[t][ee], sE[(16 * t + 4 * lg + ee) * kLB + 16 * J + lr], oo[J]);
+        }
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * w + 4 * lg + r;
+                if (i < n) store_out<OUT_BF16>(o, (row0 + (size_t)i * H) * DV + j0 + 16 * J + lr, oo[J][r]);
+            }
+        // S <- Diag(gam) S + K^' E (this wavefront's state rows; nobody else reads them now)
+#pragma unroll
+        for (int t = 0; t < SRB; ++t) {
+            const int I = w + 4 * t;
+            f32x4 acc[2];
+#pragma unroll
+            for (int J = 0; J < 2; ++J)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * I + 4 * lg + r;
+                    acc[J][r] = sGam[row] * sS[row * kLB + 16 * J + lr];
+                }
+            for (int kk = 0; kk < C; kk += 4) {
+                const float a = sKh[(kk + lg) * kLKT + 16 * I + lr];
+#pragma unroll
+                for (int J = 0; J < 2; ++J) acc[J] = mfma4(a, sE[(kk + lg) * kLB + 16 * J + lr], acc[J]);
+            }
+#pragma unroll
+            for (int J = 0; J < 2; ++J)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sS[(16 * I + 4 * lg + r) * kLB + 16 * J + lr] = acc[J][r];
+        }
+    }
+    if (!s_final) return;
+    __syncthreads();  // the last update's rows, from every wavefront
+    for (int idx = tid; idx < DK * kBV; idx += kThreads) {
+        const int r = idx / kBV, cc = idx % kBV;
+        s_final[sbase + (size_t)r * DV + j0 + cc] = sS[r * kLB + cc];
+    }
+}
+
 // ============================================================ launch
 template <int DK, int DV, bool PC, bool KZ, bool IB>
 hipError_t launch_bwd_t(const BwdArgs &a) {
@@ -1364,7 +1540,72 @@ hipError_t launch_bwd_d(const BwdArgs &a) {
     }
 }
 
+// ---- the forward pass on fp32 tiles: prep (stage 0), then the walk with outputs (stage 1).  Its
+// workspace is the prep kernel's part of the backward's: T, A, M, G, beta, K~, K^, Q~ per chunk slot.
+template <int DK, bool PC>
+size_t tile_fwd_bytes(size_t slots) {
+    constexpr int GK = PC ? DK : 1;
+    return slots * sizeof(float) * ((size_t)3 * C * C + (size_t)C * GK + C + 3 * (size_t)C * DK);
+}
+
+template <int DK, int DV, bool PC, bool KZ, bool IB, bool OB>
+hipError_t launch_tile_fwd_t(const ChunkArgs &a, int stage) {
+    constexpr int GK = PC ? DK : 1;
+    const size_t slots = (size_t)chunk_slots(a);
+    float *p = static_cast<float *>(a.ws);
+    float *wT = p, *wA = wT + slots * C * C, *wM = wA + slots * C * C, *wG = wM + slots * C * C;
+    float *wB = wG + slots * C * GK, *wKt = wB + slots * C, *wKh = wKt + slots * C * DK, *wQt = wKh + slots * C * DK;
+    if (stage != 1) {
+        GDR_LAUNCH((bwd_prep_kernel<DK, PC, KZ, IB>), dim3((unsigned)slots), dim3(kThreads), a.stream, a.ev0,
+                   stage == 0 ? a.ev1 : nullptr, a.q, a.k, a.g, a.beta, a.T, a.H, a.NC, a.eps, a.scale, wT, wA, wM, wG,
+                   wB, wKt, wKh, wQt, a.delta, a.tab);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess || stage == 0) return e;
+    }
+    const unsigned nwalk = (unsigned)(a.B * a.H * (DV / kBV));
+    GDR_LAUNCH((fwd_tile_walk_kernel<DK, DV, PC, IB, OB>), dim3(nwalk), dim3(kThreads), a.stream,
+               stage == 1 ? a.ev0 : nullptr, a.ev1, a.v, a.T, a.H, a.NC, wT, wA, wG, wB, wKt, wKh, wQt, a.s0, a.o,
+               a.s_final, a.delta, a.tab);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_tile_fwd_d(const ChunkArgs &a, int stage) {
+    const int key = (a.per_channel ? 8 : 0) | (a.kaczmarz ? 4 : 0) | (a.qkv_bf16 ? 2 : 0) | (a.o_bf16 ? 1 : 0);
+    switch (key) {
+        case 0: return launch_tile_fwd_t<DK, DV, false, false, false, false>(a, stage);
+        case 1: return launch_tile_fwd_t<DK, DV, false, false, false, true>(a, stage);
+        case 2: return launch_tile_fwd_t<DK, DV, false, false, true, false>(a, stage);
+        case 3: return launch_tile_fwd_t<DK, DV, false, false, true, true>(a, stage);
+        case 4: return launch_tile_fwd_t<DK, DV, false, true, false, false>(a, stage);
+        case 5: return launch_tile_fwd_t<DK, DV, false, true, false, true>(a, stage);
+        case 6: return launch_tile_fwd_t<DK, DV, false, true, true, false>(a, stage);
+        case 7: return launch_tile_fwd_t<DK, DV, false, true, true, true>(a, stage);
+        case 8: return launch_tile_fwd_t<DK, DV, true, false, false, false>(a, stage);
+        case 9: return launch_tile_fwd_t<DK, DV, true, false, false, true>(a, stage);
+        case 10: return launch_tile_fwd_t<DK, DV, true, false, true, false>(a, stage);
+        case 11: return launch_tile_fwd_t<DK, DV, true, false, true, true>(a, stage);
+        case 12: return launch_tile_fwd_t<DK, DV, true, true, false, false>(a, stage);
+        case 13: return launch_tile_fwd_t<DK, DV, true, true, false, true>(a, stage);
+        case 14: return launch_tile_fwd_t<DK, DV, true, true, true, false>(a, stage);
+        default: return launch_tile_fwd_t<DK, DV, true, true, true, true>(a, stage);
+    }
+}
+
 }  // namespace
+
+size_t chunk_tile_workspace_bytes(int B, int H, int NC, int Dk, int, bool per_channel) {
+    const size_t slots = (size_t)B * H * NC;
+    if (Dk == 128) return per_channel ? tile_fwd_bytes<128, true>(slots) : tile_fwd_bytes<128, false>(slots);
+    return per_channel ? tile_fwd_bytes<64, true>(slots) : tile_fwd_bytes<64, false>(slots);
+}
+
+hipError_t launch_chunk_tile(const ChunkArgs &a, int stage) {
+    if (a.Dk == 128 && a.Dv == 128) return launch_tile_fwd_d<128, 128>(a, stage);
+    if (a.Dk == 128 && a.Dv == 64) return launch_tile_fwd_d<128, 64>(a, stage);
+    if (a.Dk == 64 && a.Dv == 128) return launch_tile_fwd_d<64, 128>(a, stage);
+    return launch_tile_fwd_d<64, 64>(a, stage);
+}
 
 size_t chunk_bwd_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel) {
     const size_t slots = (size_t)B * H * NC;

@@ -755,14 +755,21 @@ int mx::intra_grid(long total, int per_cu) {
     return (int)std::min<long>(total, (long)per_cu * cus);
 }
 
-size_t chunk_matrix_workspace_bytes(int B, int H, int NC, int, int, bool per_channel, bool packed) {
+// The bf16 kernels of this file (and of chunk_matrix_pc.hip) take bf16 q/k/v at
+// d_k = d_v = 128; every other input runs on the fp32-tile kernels.
+static bool bf16_kernels(int Dk, int Dv, bool qkv_bf16) { return qkv_bf16 && Dk == DK && Dv == DV; }
+
+size_t chunk_matrix_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel, bool packed,
+                                    bool qkv_bf16) {
+    if (!bf16_kernels(Dk, Dv, qkv_bf16)) return chunk_tile_workspace_bytes(B, H, NC, Dk, Dv, per_channel);
     if (per_channel) return chunk_matrix_pc_workspace_bytes(B, H, NC);
     return (size_t)B * H * NC * kRecBytes + (packed ? 0 : segment_bytes(B * H, NC));
 }
 
-bool chunk_matrix_supported(int Dk, int Dv, bool qkv_bf16, bool) { return qkv_bf16 && Dk == DK && Dv == DV; }
+bool chunk_matrix_supported(int, int, bool, bool) { return true; }
 
 hipError_t launch_chunk_matrix(const ChunkArgs &a, int stage) {
+    if (!bf16_kernels(a.Dk, a.Dv, a.qkv_bf16)) return launch_chunk_tile(a, stage);
     if (a.per_channel) return launch_chunk_matrix_pc(a, stage);
     if (stage != 1) {
         const hipError_t e = !a.delta ? launch_intra<false, false>(a)

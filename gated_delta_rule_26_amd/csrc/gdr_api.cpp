@@ -81,10 +81,9 @@ int check_desc(const gdr_desc *d, bool step, Sizes *sz, bool one_token = true, b
     return GDR_OK;
 }
 
-int resolve_algo(const gdr_desc *d) {
-    if (d->algo == GDR_ALGO_AUTO) return d->qkv_dtype == GDR_BF16 ? GDR_ALGO_MATRIX : GDR_ALGO_VECTOR;
-    return d->algo;
-}
+// AUTO takes the matrix-core kernels: bf16 MFMA for bf16 q/k/v at d128, fp32
+// MFMA tiles for every other input.
+int resolve_algo(const gdr_desc *d) { return d->algo == GDR_ALGO_AUTO ? GDR_ALGO_MATRIX : d->algo; }
 
 bool matrix_path_available(const gdr_desc *d) {
     return gdr::chunk_matrix_supported(d->Dk, d->Dv, d->qkv_dtype == GDR_BF16,
@@ -111,7 +110,8 @@ int chunk_workspace(const gdr_desc *d, bool packed, size_t *bytes, size_t *table
     const int Bw = packed ? 1 : d->B;  // the records of a packed batch: NC chunks x H heads
     const size_t tab = packed ? gdr::seq_table_bytes(d->B, (int)NC) : 0;
     *bytes = tab + (algo == GDR_ALGO_MATRIX
-                        ? gdr::chunk_matrix_workspace_bytes(Bw, d->H, (int)NC, d->Dk, d->Dv, pc, packed)
+                        ? gdr::chunk_matrix_workspace_bytes(Bw, d->H, (int)NC, d->Dk, d->Dv, pc, packed,
+                                                            d->qkv_dtype == GDR_BF16)
                         : gdr::chunk_vector_workspace_bytes(Bw, d->H, (int)NC, d->Dk, d->Dv, pc));
     if (table) *table = tab;
     return GDR_OK;

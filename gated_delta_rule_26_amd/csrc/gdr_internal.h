@@ -85,11 +85,17 @@ size_t chunk_vector_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool p
 // stage: -1 = both kernels, 0 = intra kernel only, 1 = state kernel only
 hipError_t launch_chunk_vector(const ChunkArgs &a, int stage);
 
-// Matrix-core chunked path (bf16 MFMA with fp32 accumulation, bf16 inputs).
+// Matrix-core chunked path: bf16 MFMA with fp32 accumulation for bf16 inputs
+// at Dk = Dv = 128, fp32 MFMA tiles for every other input (see below).
 // packed: records only (a packed batch is walked one sequence per walk, no time segments)
-size_t chunk_matrix_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel, bool packed);
+size_t chunk_matrix_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel, bool packed,
+                                    bool qkv_bf16);
 bool chunk_matrix_supported(int Dk, int Dv, bool qkv_bf16, bool per_channel);
 hipError_t launch_chunk_matrix(const ChunkArgs &a, int stage);
+// Its fp32-tile kernels (fp32 q/k/v, or a width of 64): the backward pass's
+// per-chunk prep, then a walk that forms the outputs (chunk_bwd.hip).
+size_t chunk_tile_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel);
+hipError_t launch_chunk_tile(const ChunkArgs &a, int stage);
 // Its per-channel-decay kernels (called by the two functions above).
 size_t chunk_matrix_pc_workspace_bytes(int B, int H, int NC);
 hipError_t launch_chunk_matrix_pc(const ChunkArgs &a, int stage);

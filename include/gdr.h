@@ -73,9 +73,11 @@ extern "C" {
 #define GDR_F32 0
 #define GDR_BF16 1
 /* algo: which kernels run the chunked path */
-#define GDR_ALGO_AUTO 0          /* matrix-core kernel where supported, else vector kernels */
+#define GDR_ALGO_AUTO 0          /* the matrix-core kernels (GDR_ALGO_MATRIX) */
 #define GDR_ALGO_VECTOR 1        /* fp32 vector-ALU kernels (any dtype, any mode) */
-#define GDR_ALGO_MATRIX 2        /* bf16 MFMA kernels: bf16 q/k/v, Dk = Dv = 128, either decay mode */
+#define GDR_ALGO_MATRIX 2        /* matrix-core kernels: bf16 MFMA (bf16 operands split hi/lo, fp32
+                                    accumulation) for bf16 q/k/v at Dk = Dv = 128; fp32 MFMA tiles
+                                    (fp32 operands and accumulation) for every other dtype and width */
 
 typedef enum gdr_status {
     GDR_OK = 0,

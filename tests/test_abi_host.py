@@ -162,9 +162,16 @@ def test_delta_off_ignores_beta_and_its_mode():
 
 def test_matrix_algo_support_and_workspace():
     torch = __import__("torch")
-    assert _ws(_desc(qkv_dtype=torch.float32, algo="matrix"))[0] == E["GDR_E_UNSUPPORTED"]
-    assert _ws(_desc(Dk=64, Dv=64, algo="matrix"))[0] == E["GDR_E_UNSUPPORTED"]
     nc = (100 + 63) // 64
+    # fp32 q/k/v or a width of 64: the fp32-tile kernels, whose workspace per chunk and head is the
+    # backward's prep part: T, A, M (C x C), G (C, or C x Dk per channel), beta (C), K~, K^, Q~ (C x Dk)
+    def tile(Dk, pc):
+        return 4 * (3 * 64 * 64 + 64 * (Dk if pc else 1) + 64 + 3 * 64 * Dk)
+    for kw, Dk in ((dict(qkv_dtype=torch.float32), 128), (dict(Dk=64, Dv=64), 64), (dict(Dk=64, Dv=128), 64),
+                   (dict(Dk=128, Dv=64, qkv_dtype=torch.float32), 128)):
+        for pc in (False, True):
+            assert _ws(_desc(per_channel=pc, algo="matrix", **kw)) == (0, 2 * 3 * nc * tile(Dk, pc))
+            assert _ws(_desc(per_channel=pc, algo="auto", **kw)) == _ws(_desc(per_channel=pc, algo="matrix", **kw))
     # scalar decay, per chunk: T'' and A, each hi and lo, as six 1 KiB MFMA
     # operand fragments, then two fp32 decay factors per token
     assert _ws(_desc(algo="matrix")) == (0, 2 * 3 * nc * (4 * 6 * 1024 + 2 * 64 * 4))
@@ -175,9 +182,9 @@ def test_matrix_algo_support_and_workspace():
     pc = 4 * 6 * 1024 + 6 * 16 * 1024 + 128 * 4
     assert _ws(_desc(per_channel=True, algo="matrix")) == (0, 2 * 3 * nc * pc)
     assert _ws(_desc(per_channel=True, algo="auto")) == _ws(_desc(per_channel=True, algo="matrix"))
-    # auto falls back to the vector path where the matrix kernels do not apply
-    rc, n = _ws(_desc(Dk=64, Dv=64, per_channel=True, algo="auto"))
-    assert rc == 0 and (rc, n) == _ws(_desc(Dk=64, Dv=64, per_channel=True, algo="vector"))
+    # the vector kernels stay available on request, with their own workspace
+    rc, n = _ws(_desc(Dk=64, Dv=64, per_channel=True, algo="vector"))
+    assert rc == 0 and n > 0 and (rc, n) != _ws(_desc(Dk=64, Dv=64, per_channel=True, algo="auto"))
 
 
 def test_long_sequence_workspace_includes_segment_states():

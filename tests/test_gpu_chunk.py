@@ -19,9 +19,9 @@ ALGOS = ["vector", "matrix"]
 
 
 def _skip_unsupported(algo, mode, dtype, D):
-    """The matrix-core kernels cover bf16 inputs with d_k = d_v = 128."""
-    if algo == "matrix" and (dtype != "bf16" or tuple(D) != (128, 128)):
-        pytest.skip("matrix path: bf16, d128 only")
+    """Every combination runs on both paths: the matrix-core path takes bf16
+    inputs at d_k = d_v = 128 on its bf16 kernels and everything else on its
+    fp32-tile kernels."""
 
 
 def _inputs(seed, B, T, H, Dk, Dv, mode, dtype, with_s0=True, **kw):

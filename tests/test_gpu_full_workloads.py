@@ -16,8 +16,10 @@ recurrence.  Three bounds per workload, for outputs and final states alike:
 
 and a regression sentinel on the aggregate of the matrix-core path with fp32
 outputs (bf16 inputs), well below the bar and well above what it measures.
-The launch configuration is the one the benchmark times (algo auto, fp32
-output), plus bf16 outputs on the bf16 workloads.
+The launch configuration is the one the benchmark times (algo auto), with
+fp32 outputs and, on the bf16 workloads, bf16 outputs too.  The GDN and KDA
+prefill shapes also run with fp32 q/k/v (the fp32-tile kernels of the
+matrix-core path) against the fp32 bar.
 """
 import numpy as np
 import pytest
@@ -49,10 +51,22 @@ def _assert_bounds(r, tol):
     assert r["elem_o"] <= 1.0 and r["elem_s"] <= 1.0, r
 
 
+# the GDN and KDA prefill shapes with fp32 q/k/v (the fp32-tile kernels of the matrix-core path)
+FP32_SHAPES = {"gdn_prefill_f32": ("gdn_prefill", dict(dtype="f32")),
+               "kda_prefill_f32": ("kda_prefill", dict(dtype="f32"))}
+
+
+def _workload(name):
+    if name in FP32_SHAPES:
+        base, kw = FP32_SHAPES[name]
+        return WORKLOADS[base].scaled(name=name, **kw)
+    return WORKLOADS[name]
+
+
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["gdn_tiny", "gdn_prefill", "kda_prefill", "kla_prefill"])
+@pytest.mark.parametrize("name", ["gdn_tiny", "gdn_prefill", "kda_prefill", "kla_prefill", *FP32_SHAPES])
 def test_full_workload_every_head(name):
-    w = WORKLOADS[name]
+    w = _workload(name)
     print(f"{name}: generating inputs", flush=True)
     x = prefill_inputs(w)
     d = to_dev(x, w.dtype)
