@@ -637,6 +637,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gdn_prefill",
                     choices=["gdn_prefill", "kda_prefill", "kla_prefill", "gdn_tiny"])
+    ap.add_argument("--qkv-dtype", default=None, choices=["f32", "bf16"],
+                    help="store q, k, v of the headline workload in this dtype instead of its own")
     ap.add_argument("--algo", default="auto", choices=["auto", "vector", "matrix"])
     ap.add_argument("--o-dtype", default="bf16", choices=["f32", "bf16"])
     ap.add_argument("--other-configs", default="gdn_tiny,kda_prefill,kla_prefill",
@@ -676,6 +678,8 @@ def main():
         return t.float().cpu().numpy()
 
     w = WORKLOADS[args.workload]
+    if args.qkv_dtype and args.qkv_dtype != w.dtype:
+        w = w.scaled(name=f"{w.name}_{args.qkv_dtype}", dtype=args.qkv_dtype)
     x = prefill_inputs(w)
     algo = resolve_algo(w, args.algo)
     pre = bench_prefill(w, x, args.steps, args.warmup, algo, args.o_dtype)

@@ -48,6 +48,7 @@
 namespace gdr {
 namespace {
 
+using mx::state_slot;
 constexpr int C = kChunk;
 constexpr int kThreads = 256;
 constexpr int kBV = 32;  // value columns per walk workgroup
@@ -401,7 +402,10 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
     constexpr int NT = DV / kBV;
     constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads;
     constexpr int SRB = DK / 64;  // state row blocks per wavefront
-    const int tile = blockIdx.x % NT, bh = blockIdx.x / NT;
+    // XCD-aware placement: the value slices of one (sequence, head) share an XCD, so its L2 serves the
+    // chunk operands they all read
+    int bh, tile;
+    state_slot(blockIdx.x, gridDim.x / NT, NT, bh, tile);
     const BwdWalk wk = bwd_walk(bh, T, H, NC, tb);
     const int j0 = tile * kBV;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -537,7 +541,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
     constexpr int NT = DV / kBV;
     constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads, NVV = C * kBV / kThreads;
     constexpr int SRB = DK / 64;
-    const int tile = blockIdx.x % NT, bh = blockIdx.x / NT;
+    // XCD-aware placement: the value slices of one (sequence, head) share an XCD, so its L2 serves the
+    // chunk operands they all read
+    int bh, tile;
+    state_slot(blockIdx.x, gridDim.x / NT, NT, bh, tile);
     const BwdWalk wk = bwd_walk(bh, T, H, NC, tb);
     const int j0 = tile * kBV;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1345,7 +1352,10 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_walk_kernel(
     constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads;
     constexpr int SRB = DK / 64;  // state row blocks per wavefront
     constexpr int NQ = DK / 16;   // float4 groups of a Q~ row per lane
-    const int tile = blockIdx.x % NT, bh = blockIdx.x / NT;
+    // XCD-aware placement: the value slices of one (sequence, head) share an XCD, so its L2 serves the
+    // chunk operands they all read
+    int bh, tile;
+    state_slot(blockIdx.x, gridDim.x / NT, NT, bh, tile);
     const BwdWalk wk = bwd_walk(bh, T, H, NC, tb);
     const int j0 = tile * kBV;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
