@@ -262,13 +262,19 @@ def prefill_block(w, pre, algo, o_dtype):
     dom_ms = state_ms if dom == "state" else intra_ms
     dom_flops = fl[dom] * tok_heads
     mfma_tflops = dom_flops / (dom_ms * 1e-3) / 1e12
-    # bf16 inputs at d128 run on bf16 MFMA; fp32 inputs on fp32 MFMA tiles (peak 157.3 TFLOP/s)
-    mfma_peak = PEAK_BF16_MFMA if pre["in_bytes"] == 2 and w.Dk == 128 and w.Dv == 128 else PEAK_FP32_VALU
-    # The pass's algorithmic intensity (~110 flop/B at d128 with fp32 o, ~135 with bf16 o) is below
-    # MI355X's ridge (2.5 PFLOP/s / 8 TB/s = 312 flop/B), so the roof that bounds the matrix path is
+    # bf16 inputs at d128 run on bf16 MFMA; every other input on fp32 MFMA tiles, whose peak equals the
+    # fp32 vector peak on MI355X (157.3 TFLOP/s)
+    bf16_kernels = pre["in_bytes"] == 2 and w.Dk == 128 and w.Dv == 128
+    mfma_peak = PEAK_BF16_MFMA if bf16_kernels else PEAK_FP32_VALU
+    # The bf16 pass's algorithmic intensity (~110 flop/B at d128 with fp32 o, ~135 with bf16 o) is below
+    # MI355X's ridge (2.5 PFLOP/s / 8 TB/s = 312 flop/B), so the roof that bounds the bf16 matrix path is
     # HBM: the state kernel against its algorithmic bytes, with its MFMA fraction beside it.  The vector
     # path (fp32 ALU) is bounded by its ALU peak.
-    if algo == "matrix" and dom == "state":
+    if algo == "matrix" and not bf16_kernels:
+        # the fp32-tile kernels: 103 flop/B on fp32 data, above the fp32 matrix ridge (157.3 / 8 = 20 flop/B)
+        roof = {"bound": "mfma", "achieved": mfma_tflops, "peak": PEAK_FP32_VALU, "unit": "TFLOP/s",
+                "frac": mfma_tflops / PEAK_FP32_VALU, "alg_bytes_per_launch": None}
+    elif algo == "matrix" and dom == "state":
         dom_bytes = alg_bytes_state_kernel(w.B, w.T, w.H, w.Dk, w.Dv, pre["in_bytes"], pre["o_bytes"])
         achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM, "unit": "GB/s", "frac": achieved / PEAK_HBM,
