@@ -406,6 +406,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
     // chunk operands they all read
     int bh, tile;
     state_slot(blockIdx.x, gridDim.x / NT, NT, bh, tile);
+    bh = walk_seq(bh, H, tb);  // packed batches: longest sequences first
     const BwdWalk wk = bwd_walk(bh, T, H, NC, tb);
     const int j0 = tile * kBV;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -545,6 +546,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
     // chunk operands they all read
     int bh, tile;
     state_slot(blockIdx.x, gridDim.x / NT, NT, bh, tile);
+    bh = walk_seq(bh, H, tb);  // packed batches: longest sequences first
     const BwdWalk wk = bwd_walk(bh, T, H, NC, tb);
     const int j0 = tile * kBV;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1356,6 +1358,7 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_walk_kernel(
     // chunk operands they all read
     int bh, tile;
     state_slot(blockIdx.x, gridDim.x / NT, NT, bh, tile);
+    bh = walk_seq(bh, H, tb);  // packed batches: longest sequences first
     const BwdWalk wk = bwd_walk(bh, T, H, NC, tb);
     const int j0 = tile * kBV;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;

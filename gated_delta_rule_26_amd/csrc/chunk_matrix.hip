@@ -296,6 +296,7 @@ __global__ __launch_bounds__(kStateThreads, TRANSFER ? 2 : 1) void state_matrix_
 
     int g, slice;
     state_slot(blockIdx.x, G, TRANSFER ? 2 * NS : NS, g, slice);
+    g = walk_seq(g, H, tb);  // packed batches (P = 1): longest sequences first
     const int bh = g / P, p = g % P;
     const int kind = TRANSFER ? slice / NS : 0;  // transfer: 0 = N, 1 = M
     const int c0 = p * seg;

@@ -410,6 +410,7 @@ __global__ __launch_bounds__(kStateThreads) void state_pc_kernel(
     __shared__ StatePcSmem sm;
     int bh, slice;
     state_slot(blockIdx.x, BH, NS, bh, slice);
+    bh = walk_seq(bh, H, tb);  // packed batches: longest sequences first
     const WalkPlace wp = walk_place(bh, 0, NC_all, T_all, H, NC_all, tb, ws, kPcBytes);
     const int NC = wp.nc;                 // chunks of this sequence
     const int T = wp.L;                   // tokens of this sequence

@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void state_vector_kernel(
     constexpr int GK = PC ? DK : 1;
     constexpr int NT = DV / kBV;
     const int tile = blockIdx.x % NT;
-    const int bh = blockIdx.x / NT;
+    const int bh = walk_seq(blockIdx.x / NT, H, tb);  // packed batches: longest sequences first
     const int b = bh / H, h = bh % H;
     const int j0 = tile * kBV;
     // this sequence: [.., H, D] row of its token 0, its length and chunks, and

@@ -20,6 +20,7 @@ struct SeqTable {
     const int *cbase = nullptr;  // [N+1] first chunk of sequence n; cbase[N] = number of chunks
     const int *tok = nullptr;    // [chunk bound] first token of chunk u
     const int *seq = nullptr;    // [chunk bound] sequence of chunk u
+    const int *order = nullptr;  // [N] the sequence walked at rank r: longest first (see seq_table_kernel)
     int N = 0;
 };
 // Chunk bound of N packed sequences of T tokens in all: floor((T + 63 N) / 64).
@@ -151,6 +152,14 @@ template <bool BF16>
 __device__ __forceinline__ void store_out(void *p, size_t i, float x) {
     if constexpr (BF16) static_cast<uint16_t *>(p)[i] = f32_to_bf16_bits(x);
     else static_cast<float *>(p)[i] = x;
+}
+
+// The (sequence, head) that walk slot x (= rank * H + head) takes in a packed
+// batch: sequences in the table's walk order, longest first, so that the
+// longest walks are dispatched first; fixed-length batches (no table) and
+// the identity order leave x as it is.
+__device__ __forceinline__ int walk_seq(int x, int H, const SeqTable &tb) {
+    return tb.order ? tb.order[x / H] * H + x % H : x;
 }
 
 __device__ __forceinline__ float wave_sum(float x) {

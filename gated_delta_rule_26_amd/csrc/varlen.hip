@@ -36,7 +36,8 @@ __device__ int block_scan_excl(int x, int *tmp) {
 
 __global__ __launch_bounds__(kTabThreads) void seq_table_kernel(const int *__restrict__ cu, int N, int T,
                                                                 int *__restrict__ start, int *__restrict__ cbase,
-                                                                int *__restrict__ tok, int *__restrict__ seq) {
+                                                                int *__restrict__ tok, int *__restrict__ seq,
+                                                                int *__restrict__ order) {
     __shared__ int tmp[kTabThreads];
     const int t = threadIdx.x;
     // entries i0 .. i1-1 of the N + 1 boundaries belong to this thread
@@ -80,6 +81,33 @@ __global__ __launch_bounds__(kTabThreads) void seq_table_kernel(const int *__res
         tok[u] = start[lo] + (u - cbase[lo]) * kChunk;
         seq[u] = lo;
     }
+
+    // 4. the walk order: every walk of a sequence steps through its chunks one after the other, so
+    // the call lasts at least as long as the longest walk, and a long walk dispatched late makes it
+    // longer.  Sequences by chunk count, longest first, ties in sequence order: a bitonic sort of
+    // one key per thread (count above the low 10 bits, kTabThreads - 1 - n in them; padding -1,
+    // sorted last) for up to kTabThreads sequences; beyond that the sequence order itself.
+    if (N <= kTabThreads) {
+        __shared__ long long keys[kTabThreads];
+        keys[t] = t < N ? ((long long)((start[t + 1] - start[t] + kChunk - 1) / kChunk) << 10) | (kTabThreads - 1 - t)
+                        : -1;
+        for (int k = 2; k <= kTabThreads; k <<= 1)
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                __syncthreads();
+                const int ixj = t ^ j;
+                if (ixj > t) {
+                    const long long a = keys[t], b = keys[ixj];
+                    if ((t & k) == 0 ? a < b : a > b) {  // descending within blocks whose bit k is clear
+                        keys[t] = b;
+                        keys[ixj] = a;
+                    }
+                }
+            }
+        __syncthreads();
+        if (t < N) order[t] = kTabThreads - 1 - (int)(keys[t] & (kTabThreads - 1));
+    } else {
+        for (int n = t; n < N; n += kTabThreads) order[n] = n;
+    }
 }
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -88,8 +116,9 @@ constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int varlen_max_chunks(int N, int T) { return (int)(((long)T + 63L * N) / kChunk); }
 
+// Table layout (int32): start [N + 1], cbase [N + 1], tok [NCmax], seq [NCmax], order [N].
 size_t seq_table_bytes(int N, int NCmax) {
-    return align256(sizeof(int) * (2 * ((size_t)N + 1) + 2 * (size_t)NCmax));
+    return align256(sizeof(int) * (2 * ((size_t)N + 1) + 2 * (size_t)NCmax + (size_t)N));
 }
 
 SeqTable seq_table(void *ws, int N, int NCmax) {
@@ -99,6 +128,7 @@ SeqTable seq_table(void *ws, int N, int NCmax) {
     tb.cbase = p + (N + 1);
     tb.tok = p + 2 * (N + 1);
     tb.seq = p + 2 * (N + 1) + NCmax;
+    tb.order = p + 2 * (N + 1) + 2 * NCmax;
     return tb;
 }
 
@@ -106,7 +136,7 @@ hipError_t launch_seq_table(const int *cu, int N, int T, void *ws, hipStream_t s
     const int NCmax = varlen_max_chunks(N, T);
     int *p = static_cast<int *>(ws);
     hipLaunchKernelGGL(seq_table_kernel, dim3(1), dim3(kTabThreads), 0, stream, cu, N, T, p, p + (N + 1),
-                       p + 2 * (N + 1), p + 2 * (N + 1) + NCmax);
+                       p + 2 * (N + 1), p + 2 * (N + 1) + NCmax, p + 2 * (N + 1) + 2 * NCmax);
     return hipGetLastError();
 }
 

@@ -250,10 +250,10 @@ def _ws_varlen(desc):
 def test_varlen_workspace_and_validation():
     """A packed batch of N sequences, T tokens in all: at most
     floor((T + 63 N) / 64) chunks, each with one record per head, after a
-    table of 2 (N + 1) + 2 x chunks int32 rounded up to 256 bytes."""
+    table of 2 (N + 1) + 2 x chunks + N int32 rounded up to 256 bytes."""
     N, T, H = 5, 1000, 3
     nc = (T + 63 * N) // 64
-    table = -(-4 * (2 * (N + 1) + 2 * nc) // 256) * 256
+    table = -(-4 * (2 * (N + 1) + 2 * nc + N) // 256) * 256
     rec = 4 * 6 * 1024 + 2 * 64 * 4
     assert _ws_varlen(_desc(B=N, T=T, H=H, algo="matrix")) == (0, table + nc * H * rec)
     pc = 4 * 6 * 1024 + 6 * 16 * 1024 + 128 * 4
@@ -335,7 +335,7 @@ def test_backward_varlen_workspace_and_validation():
 
     N, T, H = 5, 1000, 3
     nc = (T + 63 * N) // 64
-    table = -(-4 * (2 * (N + 1) + 2 * nc) // 256) * 256
+    table = -(-4 * (2 * (N + 1) + 2 * nc + N) // 256) * 256
     slot = 4 * (5 * 4096 + 2 * 64 + 1 + 64 + 2 * 128 * 128 + 3 * 64 * 128)
     assert ws(_desc(B=N, T=T, H=H)) == (0, table + nc * H * slot)
     d = _desc(B=N, T=T, H=H)

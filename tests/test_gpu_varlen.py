@@ -139,3 +139,38 @@ def test_varlen_malformed_offsets_are_clamped(algo):
     o_bad, s_bad = _run(x, bad, "gdn", "bf16", algo=algo)
     o_ok, s_ok = _run(x, clamped, "gdn", "bf16", algo=algo)
     assert torch.equal(s_bad, s_ok) and torch.equal(o_bad, o_ok)
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_varlen_results_do_not_depend_on_the_walk_order(mode):
+    """The walks of a packed batch run longest sequence first.  A sequence's
+    outputs and final state are the same bits wherever it sits in the batch:
+    the batch and a permutation of it agree sequence by sequence."""
+    lens = [5, 300, 64, 0, 130, 1, 257, 64]
+    perm = [3, 1, 6, 0, 7, 5, 2, 4]
+    x, cu = _packed(5600 + len(mode), lens, 2, 128, mode, "bf16")
+    y = {key: np.concatenate([x[key][cu[n]:cu[n + 1]] for n in perm]) for key in ("q", "k", "v", "g", "beta")}
+    y["s0"] = x["s0"][perm]
+    cu_p = np.concatenate([[0], np.cumsum([lens[n] for n in perm])]).astype(np.int32)
+    o, s = _run(x, cu, mode, "bf16", algo="matrix")
+    o_p, s_p = _run(y, cu_p, mode, "bf16", algo="matrix")
+    for i, n in enumerate(perm):
+        assert torch.equal(s_p[i], s[n]), (mode, n)
+        assert torch.equal(o_p[cu_p[i]:cu_p[i + 1]], o[cu[n]:cu[n + 1]]), (mode, n)
+    o_ref, s_ref = _ref(x, cu, mode)
+    assert rel(host(o), o_ref) < TOL["bf16"] and rel(host(s), s_ref) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("algo", ["vector", "matrix"])
+def test_varlen_more_sequences_than_the_sorted_order(algo):
+    """1100 sequences: more than the table sorts into its longest-first order
+    (1024), so the walks run in sequence order; the results are the same."""
+    rng = np.random.default_rng(5700)
+    lens = [int(v) for v in rng.integers(0, 40, 1100)]
+    lens[17], lens[1099] = 200, 130
+    x, cu = _packed(5700, lens, 1, 128, "gdn", "bf16")
+    o, s = _run(x, cu, "gdn", "bf16", algo=algo)
+    o_ref, s_ref = _ref(x, cu, "gdn")
+    eo, es = rel(host(o), o_ref), rel(host(s), s_ref)
+    print(f"varlen 1100 sequences {algo}: rel o {eo:.2e} S {es:.2e}")
+    assert eo < TOL["bf16"] and es < TOL["bf16"]
