@@ -323,9 +323,10 @@ __device__ __forceinline__ void state_slot(int x, int groups, int nsl, int &g, i
 // ah, al are the A fragments.  With ROW_SCALE, QS still lacks the output
 // scale and the decay of its token (row i is multiplied by scale
 // row_scale[i] here); otherwise it is final.  Rows past the end of the
-// sequence are dropped by the buffer bounds.  The fp32 tile goes through the
-// LDS area `ost` (20-float rows, which may be xi itself) so that each lane
-// stores 16-byte rows.
+// sequence are dropped by the buffer bounds.  The output tile goes through
+// the LDS area `ost` (rows of 20 floats, or of 24 bf16 elements; it may be xi
+// itself, and holds at least 5,120 bytes) so that each lane stores 16-byte
+// pieces of rows.
 template <bool OUT_BF16, bool ROW_SCALE>
 __device__ __forceinline__ void chunk_outputs(const uint4 *xi, const float *row_scale, float scale,
                                               const bf16x8 *ah, const bf16x8 *al, float *ost, void *o, size_t row0,
@@ -361,14 +362,20 @@ __device__ __forceinline__ void chunk_outputs(const uint4 *xi, const float *row_
     constexpr int es = OUT_BF16 ? 2 : 4;
     const auto ro = rows_rsrc(static_cast<char *>(o) + row0 * DV * es, n, H * DV * es, DV * es);
     if constexpr (OUT_BF16) {
+        // the same through a bf16 tile (rows of 24 elements, 48 bytes): each
+        // lane stores two 16-byte half rows of 8 output columns
+        __bf16 *ob = reinterpret_cast<__bf16 *>(ost);
 #pragma unroll
         for (int M = 0; M < 4; ++M)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int off = ((16 * M + 4 * lg + r) * H * DV + jt + lr) * es;
-                const __bf16 hv = static_cast<__bf16>(O[M][r]);
-                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hv), ro, off, 0, 0);
-            }
+            for (int r = 0; r < 4; ++r) ob[(16 * M + 4 * lg + r) * 24 + lr] = static_cast<__bf16>(O[M][r]);
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int row = 32 * it + (lane >> 1), c8 = 8 * (lane & 1);
+            const uint4 val = *reinterpret_cast<const uint4 *>(&ob[row * 24 + c8]);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, val),
+                                                   ro, (row * H * DV + jt + c8) * es, 0, 0);
+        }
     } else {
         // one 16-byte store per lane covers 4 output columns (same wavefront,
         // so no barrier)
