@@ -120,39 +120,38 @@ __device__ __forceinline__ bool slot_used(int ci, int H, const SeqTable &tb) {
 }
 
 // The chunks one walk covers: sequence b = bh / H, head h = bh % H; chunk c
-// of it has slot slot(c), token row row0(c) and count(c) tokens.
+// of it has slot slot(c), token row row0(c) and count(c) tokens.  A
+// sequence's chunks are consecutive in its tokens and in the slot order
+// (stride 1 in a fixed-length batch, H in a packed one), so after the
+// sequence's start and end are read once these are arithmetic on scalars.
 struct BwdWalk {
-    SeqTable tb;
-    int nc, H, h, cb, tend, T;
-    size_t slot0, row00;  // fixed-length batch: slot and token row of chunk 0
-    __device__ __forceinline__ size_t slot(int c) const {
-        return tb.start ? (size_t)(cb + c) * H + h : slot0 + c;
-    }
-    __device__ __forceinline__ size_t row0(int c) const {
-        return tb.start ? (size_t)tb.tok[cb + c] * H + h : row00 + (size_t)c * C * H;
-    }
-    __device__ __forceinline__ int count(int c) const {
-        return tb.start ? min(C, tend - tb.tok[cb + c]) : min(C, T - c * C);
-    }
+    int nc;        // chunks of the sequence
+    int tok0, tend;  // its first token and one past its last (relative to its batch row)
+    size_t slot0, sstride;  // slot of chunk 0 and the slot stride
+    size_t row00, rstride;  // token row of chunk 0's first token and the row stride of a chunk
+    __device__ __forceinline__ size_t slot(int c) const { return slot0 + (size_t)c * sstride; }
+    __device__ __forceinline__ size_t row0(int c) const { return row00 + (size_t)c * rstride; }
+    __device__ __forceinline__ int count(int c) const { return min(C, tend - (tok0 + c * C)); }
 };
 __device__ __forceinline__ BwdWalk bwd_walk(int bh, int T, int H, int NC, const SeqTable &tb) {
     BwdWalk w;
-    w.tb = tb;
-    w.H = H;
-    w.h = bh % H;
-    w.T = T;
-    const int b = bh / H;
+    const int b = bh / H, h = bh % H;
+    w.rstride = (size_t)C * H;
     if (tb.start) {
-        w.cb = tb.cbase[b];
-        w.nc = tb.cbase[b + 1] - w.cb;
+        const int cb = tb.cbase[b];
+        w.nc = tb.cbase[b + 1] - cb;
+        w.tok0 = tb.start[b];
         w.tend = tb.start[b + 1];
-        w.slot0 = w.row00 = 0;
+        w.slot0 = (size_t)cb * H + h;
+        w.sstride = H;
+        w.row00 = (size_t)w.tok0 * H + h;
     } else {
-        w.cb = 0;
         w.nc = NC;
+        w.tok0 = 0;
         w.tend = T;
         w.slot0 = (size_t)bh * NC;
-        w.row00 = (size_t)b * T * H + w.h;
+        w.sstride = 1;
+        w.row00 = (size_t)b * T * H + h;
     }
     return w;
 }
@@ -167,6 +166,49 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+// One element of a token-major input through a raw buffer resource (rows past
+// the resource's end read as zero, with no branch), at element offset `off`.
+template <bool BF16>
+__device__ __forceinline__ float buf_in(__amdgpu_buffer_rsrc_t r, int off) {
+    if constexpr (BF16) return bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off * 2, 0, 0));
+    else return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off * 4, 0, 0));
+}
+using mx::barrier_lds;
+using mx::rows_rsrc;
+// A value the same in every lane, in scalar registers (so that a buffer
+// resource built from it is uniform and needs no per-lane loop).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ size_t uniform(size_t x) {
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)x);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(x >> 32));
+    return ((size_t)hi << 32) | lo;
+}
+
+// Workgroup barrier that first waits until at most N of this wavefront's
+// vector memory operations are outstanding (its global-to-LDS copies
+// included) and its LDS operations are done.
+template <int N>
+__device__ __forceinline__ void barrier_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+// Rows w, w + 4, .. of a C x NCOL fp32 matrix (row-major, in global memory)
+// to LDS rows LD floats apart, 64 values per copy instruction.
+// (A rolled loop: unrolled, the compiler would keep every copy's address live.)
+template <int NCOL, int LD>
+__device__ __forceinline__ void dma_rows(const float *src, float *dst, int w, int lane) {
+    const float *s = src + w * NCOL + lane;
+    unsigned d = mx::lds_addr(dst + w * LD);
+#pragma unroll 1
+    for (int i = 0; i < C / 4; ++i) {
+#pragma unroll
+        for (int hh = 0; hh < NCOL / 64; ++hh) mx::lds_dma4(s + 64 * hh, d + 256 * hh);
+        s += 4 * NCOL;
+        d += 16 * LD;
+    }
+}
+
 // LDS row strides (floats).  A row-indexed-by-lane read (rows lr, columns
 // lg) is free of bank conflicts at a stride of 2 mod 32, a column-indexed one
 // (rows lg, columns lr) at 16 mod 32; 18 serves both with at most two lanes
@@ -176,7 +218,7 @@ constexpr int kLKT = 144; // C x DK operands read column-wise (K^' , K~', Q~')
 constexpr int kLT = 66;   // C x C read row-wise (T'' in E = T'' X)
 constexpr int kLTT = 80;  // C x C read column-wise (A', T'')
 constexpr int kLB = 48;   // B operands of 32 columns, read column-wise
-constexpr int kLS = 18;   // 16-column slices, read both ways
+constexpr int kLS = 20;   // 16-column slices, read both ways and as float4 rows (16-byte aligned)
 
 // ============================================================ prep
 // One workgroup per chunk.  M and A on fp32 matrix-core tiles (wavefront w
@@ -384,11 +426,24 @@ __device__ __forceinline__ float gval(const float (*sG)[GK], int i, int cc) {
 }
 
 // ============================================================ forward walk: entering states
-// One workgroup per (sequence, head, 32 value columns), four wavefronts.  Per
-// chunk: X = V - K~ S (wavefront w: rows 16w..16w+15), E = T'' X with T'' =
-// T Diag(beta), S <- Diag(gam) S + K^' E (wavefront w: state rows 16(w + 4t)..);
-// fp32 matrix-core tiles.  The chunk's operands are loaded into registers one
-// chunk ahead and moved to LDS at the start of the chunk.
+// One workgroup per (sequence, head, 32 value columns), four wavefronts in two
+// pairs; pair p owns value columns j0 + 16p .. +15 and its wavefront h owns
+// key channels h DK/2 .. of the state, kept in registers in the layout of a
+// product's D tile.  That layout is also the B operand of the next product
+// when the reduction runs over the tile's rows with index 16 t + 4 lg + e
+// (step e of block t, lane group lg), so the state, X and E pass from one
+// product to the next without leaving the registers.  Per chunk:
+//   P_h = K~[:, half h] S_h          (each wavefront its half of the channels)
+//   X = V - (P_0 + P_1)              (the pair exchanges P through LDS)
+//   E = T (beta X)                   (= T'' X; both wavefronts of the pair)
+//   S_h <- Diag(gam_h) S_h + K^[:, half h]' E.
+// The A operands come from LDS: rows of K~ and T as float4 (four steps of one
+// lane group), columns of K^ one value per step.  The operands move from the
+// workspace to LDS by global-to-LDS copies (no registers), each buffer refilled
+// for the next chunk as soon as this chunk is done with it: K~ after the
+// exchange barrier, T, K^, beta and G_63 after the chunk's last barrier; each
+// barrier first waits for the copies issued before the previous one.  Only v
+// goes through registers, one chunk ahead.
 template <int DK, int DV, bool PC, bool IN_BF16>
 __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__restrict__ v, int T, int H, int NC,
                                                               const float *__restrict__ wT,
@@ -400,8 +455,10 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
                                                               bool delta, SeqTable tb) {
     constexpr int GK = PC ? DK : 1;
     constexpr int NT = DV / kBV;
-    constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads;
-    constexpr int SRB = DK / 64;  // state row blocks per wavefront
+    constexpr int HK = DK / 2, NTH = HK / 16;  // channels per wavefront of a pair, their 16-blocks
+    constexpr int LKR = DK + 8;                // K~: rows read as float4
+    constexpr int LKC = DK + 4;                // K^: columns read one value per lane
+    constexpr int LTR = C + 8;                 // T: rows read as float4
     // XCD-aware placement: the value slices of one (sequence, head) share an XCD, so its L2 serves the
     // chunk operands they all read
     int bh, tile;
@@ -411,121 +468,128 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
     const int j0 = tile * kBV;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
-    __shared__ float sS[DK * kLB];
-    __shared__ float sKt[C * kLK];
-    __shared__ float sKh[C * kLKT];
-    __shared__ float sT[C * kLT];     // T'' = T Diag(beta)
-    __shared__ float sX[C * kLB];
-    __shared__ float sE[C * kLB];
-    __shared__ float sBeta[C], sGam[DK];
+    const int p = w >> 1, h = w & 1;
+    const int jc = j0 + 16 * p + lr;  // this lane's value column
+    const int kh0 = h * HK;           // first key channel of this wavefront's half
+    __shared__ float sKt[C * LKR];
+    __shared__ float sKh[C * LKC];
+    __shared__ float sT[C * LTR];
+    __shared__ float sB[C];            // beta of the chunk's tokens
+    __shared__ float sG[DK];           // G_63 per channel (scalar decay: the one value, repeated)
+    __shared__ f32x4 sP[2][2][4][64];  // per pair and half: the partial K~ S tiles
 
-    float rT[NTT], rKt[NKK], rKh[NKK], rB = 0.f, rGam = 0.f;
-    f32x4 rV[2];  // the v slice in the layout of this wavefront's X tiles
-    auto fetch = [&](int c) {
-        const size_t ci = wk.slot(c);
-        const int n = wk.count(c);
-        const size_t row0 = wk.row0(c);
+    auto copy_kt = [&](size_t ci) __attribute__((always_inline)) {
+        dma_rows<DK, LKR>(wKt + ci * C * DK, sKt, w, lane);
+    };
+    auto copy_rest = [&](size_t ci) __attribute__((always_inline)) {
+        dma_rows<C, LTR>(wT + ci * C * C, sT, w, lane);
+        dma_rows<DK, LKC>(wKh + ci * C * DK, sKh, w, lane);
+        if (w == 0) mx::lds_dma4(wB + ci * C + lane, mx::lds_addr(sB));
+        if (w >= 1 && w <= DK / 64)
+            mx::lds_dma4(wG + ci * C * GK + (size_t)(C - 1) * GK + (PC ? 64 * (w - 1) + lane : 0),
+                         mx::lds_addr(sG + 64 * (w - 1)));
+    };
+    f32x4 gV[4];  // v of a chunk: rows 16 M + 4 lg + r, column jc
+    auto load_v = [&](int c) __attribute__((always_inline)) {
+        const int n = uniform(wk.count(c));
+        const size_t row0 = uniform(wk.row0(c));
+        constexpr int es = IN_BF16 ? 2 : 4;
+        const auto rv = rows_rsrc(static_cast<const char *>(v) + row0 * DV * es, n, H * DV * es, DV * es);
 #pragma unroll
-        for (int u = 0; u < NTT; ++u) rT[u] = wT[ci * C * C + tid + u * kThreads];
+        for (int M = 0; M < 4; ++M)
 #pragma unroll
-        for (int u = 0; u < NKK; ++u) {
-            rKt[u] = wKt[ci * C * DK + tid + u * kThreads];
-            rKh[u] = wKh[ci * C * DK + tid + u * kThreads];
-        }
-#pragma unroll
-        for (int J = 0; J < 2; ++J)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * w + 4 * lg + r;
-                rV[J][r] = i < n ? load_in<IN_BF16>(v, (row0 + (size_t)i * H) * DV + j0 + 16 * J + lr) : 0.f;
-            }
-        if (tid < C) rB = wB[ci * C + tid];
-        if (tid < DK) rGam = __expf(wG[ci * C * GK + (size_t)(C - 1) * GK + (PC ? tid : 0)]);
+            for (int r = 0; r < 4; ++r) gV[M][r] = buf_in<IN_BF16>(rv, (16 * M + 4 * lg + r) * H * DV + jc);
     };
 
     const size_t sbase = (size_t)bh * DK * DV;
-    for (int idx = tid; idx < DK * kBV; idx += kThreads) {
-        const int r = idx / kBV, cc = idx % kBV;
-        sS[r * kLB + cc] = s0 ? s0[sbase + (size_t)r * DV + j0 + cc] : 0.f;
+    f32x4 sv[NTH];  // S[kh0 + 16 t + 4 lg + e][jc]
+#pragma unroll
+    for (int t = 0; t < NTH; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[t][e] = s0 ? s0[sbase + (size_t)(kh0 + 16 * t + 4 * lg + e) * DV + jc] : 0.f;
+    if (wk.nc <= 0) return;
+    {
+        const size_t c0 = uniform(wk.slot(0));
+        copy_kt(c0);
+        copy_rest(c0);
+        load_v(0);
+        barrier_vm<0>();
     }
-    if (wk.nc > 0) fetch(0);
     for (int c = 0; c < wk.nc; ++c) {
-        const size_t ci = wk.slot(c);
-        __syncthreads();  // the previous chunk's reads are done; sS holds the entering state
+        const size_t ci = uniform(wk.slot(c));
+        const bool more = c + 1 < wk.nc;
+        const size_t cn = uniform(wk.slot(more ? c + 1 : c));
+        // the state entering this chunk, to the workspace
         float *Sg = wS + ci * DK * DV;
-        for (int idx = tid; idx < DK * kBV; idx += kThreads) {
-            const int r = idx / kBV, cc = idx % kBV;
-            Sg[(size_t)r * DV + j0 + cc] = sS[r * kLB + cc];
-        }
-        if (tid < C) sBeta[tid] = rB;
-        if (tid < DK) sGam[tid] = rGam;
 #pragma unroll
-        for (int u = 0; u < NKK; ++u) {
-            const int idx = tid + u * kThreads;
-            sKt[(idx / DK) * kLK + idx % DK] = rKt[u];
-            sKh[(idx / DK) * kLKT + idx % DK] = rKh[u];
-        }
-        __syncthreads();  // sBeta
+        for (int t = 0; t < NTH; ++t)
 #pragma unroll
-        for (int u = 0; u < NTT; ++u) {
-            const int idx = tid + u * kThreads, i = idx / C, m = idx % C;
-            sT[i * kLT + m] = rT[u] * sBeta[m];
-        }
-        f32x4 x[2] = {rV[0], rV[1]};
-        if (c + 1 < wk.nc) fetch(c + 1);
-        // X = V - K~ S (rows 16w ..; X = V without the delta rule)
-        for (int kk = 0; delta && kk < DK; kk += 4) {
-            const float a = -sKt[(16 * w + lr) * kLK + kk + lg];
+            for (int e = 0; e < 4; ++e) Sg[(size_t)(kh0 + 16 * t + 4 * lg + e) * DV + jc] = sv[t][e];
+        // P_h = K~[:, half h] S_h (X = V without the delta rule)
+        f32x4 pp[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        if (delta) {
 #pragma unroll
-            for (int J = 0; J < 2; ++J) x[J] = mfma4(a, sS[(kk + lg) * kLB + 16 * J + lr], x[J]);
-        }
+            for (int t = 0; t < NTH; ++t)
 #pragma unroll
-        for (int J = 0; J < 2; ++J)
+                for (int M = 0; M < 4; ++M) {
+                    const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&sKt[(16 * M + lr) * LKR + kh0 + 16 * t + 4 * lg]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sX[(16 * w + 4 * lg + r) * kLB + 16 * J + lr] = x[J][r];
-        __syncthreads();  // X, T''
-        f32x4 e[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        for (int kk = 0; kk < 16 * (w + 1); kk += 4) {  // T'' is lower triangular
-            const float a = sT[(16 * w + lr) * kLT + kk + lg];
-#pragma unroll
-            for (int J = 0; J < 2; ++J) e[J] = mfma4(a, sX[(kk + lg) * kLB + 16 * J + lr], e[J]);
-        }
-#pragma unroll
-        for (int J = 0; J < 2; ++J)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sE[(16 * w + 4 * lg + r) * kLB + 16 * J + lr] = e[J][r];
-        __syncthreads();  // E
-        // S <- Diag(gam) S + K^' E (this wavefront's state rows; nobody else reads them now)
-#pragma unroll
-        for (int t = 0; t < SRB; ++t) {
-            const int I = w + 4 * t;
-            f32x4 acc[2];
-#pragma unroll
-            for (int J = 0; J < 2; ++J)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * I + 4 * lg + r;
-                    acc[J][r] = sGam[row] * sS[row * kLB + 16 * J + lr];
+                    for (int e = 0; e < 4; ++e) pp[M] = mfma4(a4[e], sv[t][e], pp[M]);
                 }
-            for (int kk = 0; kk < C; kk += 4) {
-                const float a = sKh[(kk + lg) * kLKT + 16 * I + lr];
-#pragma unroll
-                for (int J = 0; J < 2; ++J) acc[J] = mfma4(a, sE[(kk + lg) * kLB + 16 * J + lr], acc[J]);
-            }
-#pragma unroll
-            for (int J = 0; J < 2; ++J)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sS[(16 * I + 4 * lg + r) * kLB + 16 * J + lr] = acc[J][r];
         }
+#pragma unroll
+        for (int M = 0; M < 4; ++M) sP[p][h][M][lane] = pp[M];
+        barrier_vm<0>();  // partial tiles; this chunk's T, K^, beta, G_63 have landed; K~ is free
+        f32x4 x[4];
+#pragma unroll
+        for (int M = 0; M < 4; ++M) x[M] = gV[M] - (pp[M] + sP[p][h ^ 1][M][lane]);  // the same sum in both
+        if (more) copy_kt(cn);
+        load_v(more ? c + 1 : c);  // the last 16 loads: the barrier below may leave them in flight
+        // E = T (beta X) (T lower triangular)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] *= *reinterpret_cast<const f32x4 *>(&sB[16 * t + 4 * lg]);
+        f32x4 e4[4];
+#pragma unroll
+        for (int M = 0; M < 4; ++M) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t <= M; ++t) {
+                const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&sT[(16 * M + lr) * LTR + 16 * t + 4 * lg]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc = mfma4(a4[e], x[t][e], acc);
+            }
+            e4[M] = acc;
+        }
+        // S_h <- Diag(gam) S_h + K^[:, half h]' E
+#pragma unroll
+        for (int J = 0; J < NTH; ++J) {
+            f32x4 acc;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = __expf(sG[PC ? kh0 + 16 * J + 4 * lg + e : 0]) * sv[J][e];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc = mfma4(sKh[(16 * t + 4 * lg + e) * LKC + kh0 + 16 * J + lr], e4[t][e], acc);
+            sv[J] = acc;
+        }
+        barrier_vm<16>();  // the next chunk's K~ has landed; T, K^, beta, G_63 are free
+        if (more) copy_rest(cn);
     }
 }
 
 // ============================================================ reverse walk: dS' per chunk
-// One workgroup per (sequence, head, 32 value columns), chunks in reverse.
-// Per chunk: dE = A' dO + K^ dS' and dX = transpose(T'') dE (wavefront w:
-// rows 16w..), dS = Diag(gam) dS' + Q~' dO - K~' dX (wavefront w: state rows
-// 16(w + 4t)..).  One LDS buffer holds K^ (row-wise reads), then Q~, then K~
-// (column-wise).
+// One workgroup per (sequence, head, 32 value columns), chunks in reverse, in
+// the layout of the forward walk above: pair p owns value columns j0 + 16p ..
+// +15, its wavefront h key channels h DK/2 .. of dS' (in registers).  Per
+// chunk, with dO (this lane's column, rows as a D tile) in registers:
+//   dE = K^ dS' + A' dO   (the pair sums its halves of the channel reduction
+//                          through LDS; wavefront h adds A' dO on token tiles
+//                          h and 3 - h)
+//   dX = T''' dE          (both wavefronts of the pair)
+//   dS_h = Diag(gam_h) dS'_h + Q~[:, half h]' dO - K~[:, half h]' dX.
+// Rows of K^ are read from LDS as float4, the columns of A, T'', Q~ and K~ one
+// value per lane and step.  Loads and barriers as in the forward walk.
 template <int DK, int DV, bool PC>
 __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__restrict__ dO, int T, int H, int NC,
                                                                const float *__restrict__ wT,
@@ -540,8 +604,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
                                                                bool delta, SeqTable tb) {
     constexpr int GK = PC ? DK : 1;
     constexpr int NT = DV / kBV;
-    constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads, NVV = C * kBV / kThreads;
-    constexpr int SRB = DK / 64;
+    constexpr int HK = DK / 2, NTH = HK / 16;
+    constexpr int LKR = DK + 8;  // K^: rows read as float4
+    constexpr int LKC = DK + 4;  // Q~, K~: columns read one value per lane (4 lane groups in 4 bank quarters)
+    constexpr int LTC = C + 4;   // A, T'': columns
+    constexpr int NK4 = C * DK / 4 / kThreads, NT4 = C * C / 4 / kThreads;
     // XCD-aware placement: the value slices of one (sequence, head) share an XCD, so its L2 serves the
     // chunk operands they all read
     int bh, tile;
@@ -551,167 +618,153 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
     const int j0 = tile * kBV;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
-    __shared__ float sdS[DK * kLB];
-    __shared__ float sK[C * kLKT];   // K^ (stride kLK), then Q~, then K~ (stride kLKT)
-    __shared__ float sA[C * kLTT];
-    __shared__ float sT[C * kLTT];   // T'' = T Diag(beta)
-    __shared__ float sO[C * kLB];    // dO slice
-    __shared__ float sdE[C * kLB];   // dE, then dX
-    __shared__ float sBeta[C], sGam[DK];
+    const int p = w >> 1, h = w & 1;
+    const int jc = j0 + 16 * p + lr;
+    const int kh0 = h * HK;
+    __shared__ float sKh[C * LKR];
+    __shared__ float sQt[C * LKC];
+    __shared__ float sKt[C * LKC];
+    __shared__ float sA[C * LTC];
+    __shared__ float sT[C * LTC];      // T'' = T Diag(beta)
+    __shared__ float sGam[DK];
+    __shared__ f32x4 sP[2][2][4][64];  // per pair and half: the partial dE tiles
 
-    float rT[NTT], rA[NTT], rKt[NKK], rKh[NKK], rQt[NKK], rO[NVV], rB = 0.f, rGam = 0.f;
-    auto fetch_a = [&](int c) {  // operands of dE, dX and the output gradient slice
-        const size_t ci = wk.slot(c);
-        const int n = wk.count(c);
-        const size_t row0 = wk.row0(c);
+    f32x4 gKh[NK4], gQt[NK4], gKt[NK4], gT[NT4], gA[NT4], gB;
+    f32x4 gO[4];  // dO of the fetched chunk: rows 16 t + 4 lg + e, column jc
+    float gGam = 0.f;
+    auto fetch = [&](int c) {
+        const size_t ci = uniform(wk.slot(c));
+        const int n = uniform(wk.count(c));
+        const size_t row0 = uniform(wk.row0(c));
+        const f32x4 *kh4 = reinterpret_cast<const f32x4 *>(wKh + ci * C * DK);
+        const f32x4 *qt4 = reinterpret_cast<const f32x4 *>(wQt + ci * C * DK);
+        const f32x4 *kt4 = reinterpret_cast<const f32x4 *>(wKt + ci * C * DK);
+        const f32x4 *t4 = reinterpret_cast<const f32x4 *>(wT + ci * C * C);
+        const f32x4 *a4 = reinterpret_cast<const f32x4 *>(wA + ci * C * C);
 #pragma unroll
-        for (int u = 0; u < NTT; ++u) {
-            rT[u] = wT[ci * C * C + tid + u * kThreads];
-            rA[u] = wA[ci * C * C + tid + u * kThreads];
+        for (int u = 0; u < NK4; ++u) {
+            gKh[u] = kh4[tid + u * kThreads];
+            gQt[u] = qt4[tid + u * kThreads];
+            gKt[u] = kt4[tid + u * kThreads];
         }
 #pragma unroll
-        for (int u = 0; u < NKK; ++u) rKh[u] = wKh[ci * C * DK + tid + u * kThreads];
-#pragma unroll
-        for (int u = 0; u < NVV; ++u) {
-            const int idx = tid + u * kThreads, i = idx / kBV, cc = idx % kBV;
-            rO[u] = i < n ? dO[(row0 + (size_t)i * H) * DV + j0 + cc] : 0.f;
+        for (int u = 0; u < NT4; ++u) {
+            gT[u] = t4[tid + u * kThreads];
+            gA[u] = a4[tid + u * kThreads];
         }
-        if (tid < C) rB = wB[ci * C + tid];
-        if (tid < DK) rGam = __expf(wG[ci * C * GK + (size_t)(C - 1) * GK + (PC ? tid : 0)]);
-    };
-    auto fetch_q = [&](int c) {
+        gB = reinterpret_cast<const f32x4 *>(wB + ci * C)[tid % (C / 4)];
+        gGam = __expf(wG[ci * C * GK + (size_t)(C - 1) * GK + (PC ? tid % DK : 0)]);
+        const auto ro = rows_rsrc(dO + row0 * DV, n, H * DV * 4, DV * 4);
 #pragma unroll
-        for (int u = 0; u < NKK; ++u) rQt[u] = wQt[wk.slot(c) * C * DK + tid + u * kThreads];
-    };
-    auto fetch_k = [&](int c) {
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int u = 0; u < NKK; ++u) rKt[u] = wKt[wk.slot(c) * C * DK + tid + u * kThreads];
+            for (int e = 0; e < 4; ++e) gO[t][e] = buf_in<false>(ro, (16 * t + 4 * lg + e) * H * DV + jc);
+    };
+    auto stage_rows = [&](float *dst, int ld, const f32x4 *src, int cols, int count) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < count; ++u) {
+            const int idx4 = tid + u * kThreads, row = idx4 / (cols / 4), c4 = idx4 % (cols / 4);
+            *reinterpret_cast<f32x4 *>(&dst[row * ld + 4 * c4]) = src[u];
+        }
     };
 
     const size_t sbase = (size_t)bh * DK * DV;
-    for (int idx = tid; idx < DK * kBV; idx += kThreads) {
-        const int r = idx / kBV, cc = idx % kBV;
-        sdS[r * kLB + cc] = ds_final ? ds_final[sbase + (size_t)r * DV + j0 + cc] : 0.f;
-    }
-    if (wk.nc > 0) {
-        fetch_a(wk.nc - 1);
-        fetch_q(wk.nc - 1);
-        fetch_k(wk.nc - 1);
-    }
+    f32x4 dsv[NTH];  // dS'[kh0 + 16 t + 4 lg + e][jc]
+#pragma unroll
+    for (int t = 0; t < NTH; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            dsv[t][e] = ds_final ? ds_final[sbase + (size_t)(kh0 + 16 * t + 4 * lg + e) * DV + jc] : 0.f;
+    if (wk.nc > 0) fetch(wk.nc - 1);
     for (int c = wk.nc - 1; c >= 0; --c) {
-        const size_t ci = wk.slot(c);
-        __syncthreads();  // sdS holds dS' of this chunk; the previous chunk's reads are done
+        const size_t ci = uniform(wk.slot(c));
+        barrier_lds();  // the previous chunk's LDS reads are done
+        stage_rows(sKh, LKR, gKh, DK, NK4);
+        stage_rows(sQt, LKC, gQt, DK, NK4);
+        stage_rows(sKt, LKC, gKt, DK, NK4);
+        stage_rows(sA, LTC, gA, C, NT4);
+#pragma unroll
+        for (int u = 0; u < NT4; ++u) {
+            const int idx4 = tid + u * kThreads, row = idx4 / (C / 4), c4 = idx4 % (C / 4);
+            *reinterpret_cast<f32x4 *>(&sT[row * LTC + 4 * c4]) = gT[u] * gB;
+        }
+        if (tid < DK) sGam[tid] = gGam;
+        const f32x4 ov[4] = {gO[0], gO[1], gO[2], gO[3]};
+        // dS' of this chunk to the workspace (before the next loads, as in the forward walk)
         float *dSg = wdS + ci * DK * DV;
-        for (int idx = tid; idx < DK * kBV; idx += kThreads) {
-            const int r = idx / kBV, cc = idx % kBV;
-            dSg[(size_t)r * DV + j0 + cc] = sdS[r * kLB + cc];
-        }
-        if (tid < C) sBeta[tid] = rB;
-        if (tid < DK) sGam[tid] = rGam;
 #pragma unroll
-        for (int u = 0; u < NTT; ++u) {
-            const int idx = tid + u * kThreads;
-            sA[(idx / C) * kLTT + idx % C] = rA[u];
-        }
+        for (int t = 0; t < NTH; ++t)
 #pragma unroll
-        for (int u = 0; u < NKK; ++u) {
-            const int idx = tid + u * kThreads;
-            sK[(idx / DK) * kLK + idx % DK] = rKh[u];
-        }
+            for (int e = 0; e < 4; ++e) dSg[(size_t)(kh0 + 16 * t + 4 * lg + e) * DV + jc] = dsv[t][e];
+        fetch(max(c - 1, 0));
+        barrier_lds();  // the chunk's operands are in LDS
+        // partial dE: K^[:, half h] dS'_h ...
+        f32x4 pp[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int u = 0; u < NVV; ++u) {
-            const int idx = tid + u * kThreads;
-            sO[(idx / kBV) * kLB + idx % kBV] = rO[u];
-        }
-        __syncthreads();  // sBeta
+        for (int t = 0; t < NTH; ++t)
 #pragma unroll
-        for (int u = 0; u < NTT; ++u) {
-            const int idx = tid + u * kThreads, i = idx / C, m = idx % C;
-            sT[i * kLTT + m] = rT[u] * sBeta[m];
-        }
-        if (c > 0) fetch_a(c - 1);
-        // dE = A' dO + K^ dS' (rows 16w ..; the transpose of A is zero below the diagonal)
-        f32x4 de[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        for (int kk = 16 * w; kk < C; kk += 4) {
-            const float a = sA[(kk + lg) * kLTT + 16 * w + lr];
+            for (int M = 0; M < 4; ++M) {
+                const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&sKh[(16 * M + lr) * LKR + kh0 + 16 * t + 4 * lg]);
 #pragma unroll
-            for (int J = 0; J < 2; ++J) de[J] = mfma4(a, sO[(kk + lg) * kLB + 16 * J + lr], de[J]);
-        }
-        for (int kk = 0; kk < DK; kk += 4) {
-            const float a = sK[(16 * w + lr) * kLK + kk + lg];
-#pragma unroll
-            for (int J = 0; J < 2; ++J) de[J] = mfma4(a, sdS[(kk + lg) * kLB + 16 * J + lr], de[J]);
-        }
-#pragma unroll
-        for (int J = 0; J < 2; ++J)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sdE[(16 * w + 4 * lg + r) * kLB + 16 * J + lr] = de[J][r];
-        __syncthreads();  // dE, T''; K^ no longer read
-        // dX = transpose(T'') dE (upper triangular)
-        f32x4 dx[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        for (int kk = 16 * w; kk < C; kk += 4) {
-            const float a = sT[(kk + lg) * kLTT + 16 * w + lr];
-#pragma unroll
-            for (int J = 0; J < 2; ++J) dx[J] = mfma4(a, sdE[(kk + lg) * kLB + 16 * J + lr], dx[J]);
-        }
-#pragma unroll
-        for (int u = 0; u < NKK; ++u) {  // Q~ in K^'s place
-            const int idx = tid + u * kThreads;
-            sK[(idx / DK) * kLKT + idx % DK] = rQt[u];
-        }
-        if (c > 0) fetch_q(c - 1);
-        __syncthreads();  // every dE read done; Q~ staged
-#pragma unroll
-        for (int J = 0; J < 2; ++J)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sdE[(16 * w + 4 * lg + r) * kLB + 16 * J + lr] = dx[J][r];
-        // dS = Diag(gam) dS' + Q~' dO ...
-        f32x4 acc[SRB][2];
-#pragma unroll
-        for (int t = 0; t < SRB; ++t) {
-            const int I = w + 4 * t;
-#pragma unroll
-            for (int J = 0; J < 2; ++J)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * I + 4 * lg + r;
-                    acc[t][J][r] = sGam[row] * sdS[row * kLB + 16 * J + lr];
-                }
-            for (int kk = 0; kk < C; kk += 4) {
-                const float a = sK[(kk + lg) * kLKT + 16 * I + lr];
-#pragma unroll
-                for (int J = 0; J < 2; ++J) acc[t][J] = mfma4(a, sO[(kk + lg) * kLB + 16 * J + lr], acc[t][J]);
+                for (int e = 0; e < 4; ++e) pp[M] = mfma4(a4[e], dsv[t][e], pp[M]);
             }
+        // ... + A' dO on token tiles h and 3 - h (A' upper triangular: blocks t >= M)
+        auto adO = [&](f32x4 &acc, int M) __attribute__((always_inline)) {
+#pragma unroll
+            for (int t = M; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc = mfma4(sA[(16 * t + 4 * lg + e) * LTC + 16 * M + lr], ov[t][e], acc);
+        };
+        if (h == 0) {
+            adO(pp[0], 0);
+            adO(pp[3], 3);
+        } else {
+            adO(pp[1], 1);
+            adO(pp[2], 2);
         }
-        __syncthreads();  // Q~ no longer read; dX visible
 #pragma unroll
-        for (int u = 0; u < NKK; ++u) {  // K~ in its place
-            const int idx = tid + u * kThreads;
-            sK[(idx / DK) * kLKT + idx % DK] = rKt[u];
+        for (int M = 0; M < 4; ++M) sP[p][h][M][lane] = pp[M];
+        barrier_lds();  // both partial tiles of each pair
+        f32x4 de[4];
+#pragma unroll
+        for (int M = 0; M < 4; ++M) de[M] = pp[M] + sP[p][h ^ 1][M][lane];  // the same sum in both
+        // dX = T''' dE (T''' upper triangular)
+        f32x4 dx[4];
+#pragma unroll
+        for (int M = 0; M < 4; ++M) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = M; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc = mfma4(sT[(16 * t + 4 * lg + e) * LTC + 16 * M + lr], de[t][e], acc);
+            dx[M] = acc;
         }
-        if (c > 0) fetch_k(c - 1);
-        __syncthreads();
-        // ... - K~' dX (not without the delta rule: X does not depend on S then)
+        // dS_h = Diag(gam) dS'_h + Q~[:, half h]' dO - K~[:, half h]' dX (no K~ term without the delta
+        // rule: X does not depend on S then)
 #pragma unroll
-        for (int t = 0; t < SRB; ++t) {
-            const int I = w + 4 * t;
-            for (int kk = 0; delta && kk < C; kk += 4) {
-                const float a = -sK[(kk + lg) * kLKT + 16 * I + lr];
+        for (int J = 0; J < NTH; ++J) {
+            const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&sGam[kh0 + 16 * J + 4 * lg]);
+            f32x4 acc = g4 * dsv[J];
 #pragma unroll
-                for (int J = 0; J < 2; ++J) acc[t][J] = mfma4(a, sdE[(kk + lg) * kLB + 16 * J + lr], acc[t][J]);
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc = mfma4(sQt[(16 * t + 4 * lg + e) * LKC + kh0 + 16 * J + lr], ov[t][e], acc);
+            if (delta) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc = mfma4(-sKt[(16 * t + 4 * lg + e) * LKC + kh0 + 16 * J + lr], dx[t][e], acc);
             }
-#pragma unroll
-            for (int J = 0; J < 2; ++J)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sdS[(16 * I + 4 * lg + r) * kLB + 16 * J + lr] = acc[t][J][r];
+            dsv[J] = acc;
         }
     }
-    __syncthreads();
     if (ds0) {
-        for (int idx = tid; idx < DK * kBV; idx += kThreads) {
-            const int r = idx / kBV, cc = idx % kBV;
-            ds0[sbase + (size_t)r * DV + j0 + cc] = sdS[r * kLB + cc];
-        }
+#pragma unroll
+        for (int t = 0; t < NTH; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ds0[sbase + (size_t)(kh0 + 16 * t + 4 * lg + e) * DV + jc] = dsv[t][e];
     }
 }
 
@@ -795,6 +848,16 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
     const float *dSg = wdS + (size_t)ci * DK * DV;
     float rS[NSS], rdS[NSS], rO[NVS];
     f32x4 rV;  // the v slice in the layout of this wavefront's X tile
+    // The slice loop's barriers wait for LDS operations only, so the next
+    // slice's loads stay in flight across them; every load and store in the
+    // loop is issued unconditionally (buffer bounds drop the rows past the
+    // chunk's end), which keeps the compiler's wait counts exact.
+    const size_t row0u = uniform(sl.row0);
+    const int nu = uniform(n);
+    constexpr int es = IN_BF16 ? 2 : 4;
+    const auto r_o = rows_rsrc(dO + row0u * DV, nu, H * DV * 4, DV * 4);
+    const auto r_v = rows_rsrc(static_cast<const char *>(v) + row0u * DV * es, nu, H * DV * es, DV * es);
+    const auto r_dv = rows_rsrc(dv + row0u * DV, nu, H * DV * 4, DV * 4);
     auto fetch = [&](int j0) {
 #pragma unroll
         for (int u = 0; u < NSS; ++u) {
@@ -805,17 +868,14 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
 #pragma unroll
         for (int u = 0; u < NVS; ++u) {
             const int idx = tid + u * kThreads, r = idx / kBS, cc = idx % kBS;
-            rO[u] = r < n ? dO[(sl.row0 + (size_t)r * H) * DV + j0 + cc] : 0.f;
+            rO[u] = buf_in<false>(r_o, r * H * DV + j0 + cc);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * w + 4 * lg + r;
-            rV[r] = i < n ? load_in<IN_BF16>(v, (sl.row0 + (size_t)i * H) * DV + j0 + lr) : 0.f;
-        }
+        for (int r = 0; r < 4; ++r) rV[r] = buf_in<IN_BF16>(r_v, (16 * w + 4 * lg + r) * H * DV + j0 + lr);
     };
     fetch(0);
     for (int j0 = 0; j0 < DV; j0 += kBS) {
-        __syncthreads();  // the previous slice's reads are done
+        barrier_lds();  // the previous slice's reads are done
 #pragma unroll
         for (int u = 0; u < NSS; ++u) {
             const int idx = tid + u * kThreads;
@@ -828,8 +888,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
             sO[(idx / kBS) * kLS + idx % kBS] = rO[u];
         }
         f32x4 x = rV;
-        if (j0 + kBS < DV) fetch(j0 + kBS);
-        __syncthreads();
+        fetch(min(j0 + kBS, DV - kBS));
+        barrier_lds();
         // X = V - K~ S;  dE = A' dO + K^ dS'
         f32x4 de = z4;
         for (int kk = 0; kk < DK; kk += 4) {
@@ -842,7 +902,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
             sX[(16 * w + 4 * lg + r) * kLS + lr] = x[r];
             sdE[(16 * w + 4 * lg + r) * kLS + lr] = de[r];
         }
-        __syncthreads();
+        barrier_lds();
         // E = T'' X (lower triangular);  dX = transpose(T'') dE (upper triangular)
         f32x4 e = z4, dx = z4;
         for (int kk = 0; kk < 16 * (w + 1); kk += 4) e = mfma4(sT[(16 * w + lr) * kLT + kk + lg], sX[(kk + lg) * kLS + lr], e);
@@ -852,28 +912,43 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
             const int i = 16 * w + 4 * lg + r;
             sE[i * kLS + lr] = e[r];
             sdX[i * kLS + lr] = dx[r];
-            if (i < n) dv[(sl.row0 + (size_t)i * H) * DV + j0 + lr] = dx[r];
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dx[r]), r_dv,
+                                                  (i * H * DV + j0 + lr) * 4, 0, 0);
         }
-        __syncthreads();
-        // accumulators of rows 16w .. (reduction over this slice's 16 value columns)
-#pragma unroll
-        for (int kk = 0; kk < kBS; kk += 4) {
-            const int ka = (16 * w + lr) * kLS + kk + lg;
+        barrier_lds();
+        // accumulators of rows 16w .. (reduction over this slice's 16 value
+        // columns; step e of lane group lg takes column 4 lg + e, so each
+        // operand row gives a lane its four values as one float4)
+        {
+            const int ka = (16 * w + lr) * kLS + 4 * lg;
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
             // without the delta rule X does not depend on K~, and T'' (so beta) is fixed
-            const float ao = sO[ka], ax = delta ? -sdX[ka] : 0.f, ae = sE[ka], ade = delta ? sdE[ka] : 0.f;
+            const f32x4 ao = *reinterpret_cast<const f32x4 *>(&sO[ka]);
+            const f32x4 ae = *reinterpret_cast<const f32x4 *>(&sE[ka]);
+            const f32x4 ax = delta ? -*reinterpret_cast<const f32x4 *>(&sdX[ka]) : z;
+            const f32x4 ade = delta ? *reinterpret_cast<const f32x4 *>(&sdE[ka]) : z;
 #pragma unroll
             for (int J = 0; J < JK; ++J) {
-                const int kb = (16 * J + lr) * kLS + kk + lg;
-                const float bs = sS[kb];
-                aQ[J] = mfma4(ao, bs, aQ[J]);
-                aKt[J] = mfma4(ax, bs, aKt[J]);
-                aKh[J] = mfma4(ae, sdS[kb], aKh[J]);
+                const int kb = (16 * J + lr) * kLS + 4 * lg;
+                const f32x4 bs = *reinterpret_cast<const f32x4 *>(&sS[kb]);
+                const f32x4 bd = *reinterpret_cast<const f32x4 *>(&sdS[kb]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    aQ[J] = mfma4(ao[e], bs[e], aQ[J]);
+                    aKt[J] = mfma4(ax[e], bs[e], aKt[J]);
+                    aKh[J] = mfma4(ae[e], bd[e], aKh[J]);
+                }
             }
 #pragma unroll
             for (int J = 0; J < 4; ++J) {
-                const int kb = (16 * J + lr) * kLS + kk + lg;
-                aA[J] = mfma4(ao, sE[kb], aA[J]);
-                aT[J] = mfma4(ade, sX[kb], aT[J]);
+                const int kb = (16 * J + lr) * kLS + 4 * lg;
+                const f32x4 be = *reinterpret_cast<const f32x4 *>(&sE[kb]);
+                const f32x4 bx = *reinterpret_cast<const f32x4 *>(&sX[kb]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    aA[J] = mfma4(ao[e], be[e], aA[J]);
+                    aT[J] = mfma4(ade[e], bx[e], aT[J]);
+                }
             }
         }
         if (tid < DK) {

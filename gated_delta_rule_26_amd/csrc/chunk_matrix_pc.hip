@@ -362,30 +362,6 @@ struct alignas(16) StatePcSmem {
                                  // helpers form outputs in turn, never at the same time)
 };
 
-// Global -> LDS copies without registers (global_load_lds, gfx950): every
-// lane moves 16 (or 4) bytes from its own global address to LDS address
-// M0 + 16 lane (4 lane).  Issued from inline asm, which saves and restores M0:
-// the compiler then does not make later LDS accesses of this wavefront wait
-// for the copy (they touch other buffers); the copies complete at the
-// helpers' explicit s_waitcnt vmcnt(0) before the barrier that publishes
-// them.  The hardware counts them in vmcnt, so the compiler's own wait counts
-// for other loads can only get stricter.  One wait state separates the M0
-// write from the copy that reads it.
-__device__ __forceinline__ unsigned lds_addr(const void *p) {
-    return __builtin_amdgcn_readfirstlane(
-        static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)(p))));
-}
-__device__ __forceinline__ void lds_dma16(const void *src, unsigned lds) {
-    int saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src) : "memory");
-}
-__device__ __forceinline__ void lds_dma4(const void *src, unsigned lds) {
-    int saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src) : "memory");
-}
-
 // PIECES 1 KiB pieces, split over the two helper wavefronts (vt = 0, 1).
 template <int PIECES>
 __device__ __forceinline__ void copy_to_lds(const char *src, unsigned dst, int vt, int lane) {

@@ -302,6 +302,30 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p) {
     return __builtin_bit_cast(bf16x4, r);
 }
 
+// Global -> LDS copies without registers (global_load_lds, gfx950): every
+// lane moves 16 (or 4) bytes from its own global address to LDS address
+// M0 + 16 lane (4 lane).  Issued from inline asm, which saves and restores M0:
+// the compiler then does not make later LDS accesses of this wavefront wait
+// for the copy (they touch other buffers); the copies complete at an explicit
+// s_waitcnt vmcnt before the barrier that publishes them.  The hardware
+// counts them in vmcnt, so the compiler's own wait counts for other loads can
+// only get stricter.  One wait state separates the M0 write from the copy
+// that reads it.
+__device__ __forceinline__ unsigned lds_addr(const void *p) {
+    return __builtin_amdgcn_readfirstlane(
+        static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)(p))));
+}
+__device__ __forceinline__ void lds_dma16(const void *src, unsigned lds) {
+    int saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const void *src, unsigned lds) {
+    int saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src) : "memory");
+}
+
 // XCD-aware placement of the state walk's workgroups: consecutive workgroup
 // ids go to different XCDs, so the nsl slices of one group (sequence, head,
 // time segment) get ids that are equal modulo 8 and share that XCD's L2 for
