@@ -256,31 +256,68 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
     __shared__ float sBeta[C];
     __shared__ float sE[2][C];  // scalar decay: exp(G_i), exp(G_63 - G_i)
 
-    {  // all loads in flight at once, then the LDS stores
-        constexpr int NE = C * DK / kThreads, NG = (C * GK + kThreads - 1) / kThreads;
-        float kr[NE], qr[NE], gr[NG];
+    {  // all loads in flight at once (16 bytes per lane, rows past the chunk's end read as zero through
+       // the buffer bounds), then the LDS stores
+        constexpr int es = IN_BF16 ? 2 : 4, EPL = 16 / es;   // input elements per 16-byte load
+        constexpr int NL = C * DK / EPL / kThreads;           // loads per thread and matrix
+        constexpr int NG4 = (C * GK / 4 + kThreads - 1) / kThreads;
+        const size_t row0u = uniform(sl.row0);
+        const int nu = uniform(n);
+        const auto rk = rows_rsrc(static_cast<const char *>(k) + row0u * DK * es, nu, H * DK * es, DK * es);
+        const auto rq = rows_rsrc(static_cast<const char *>(q) + row0u * DK * es, nu, H * DK * es, DK * es);
+        const auto rg = rows_rsrc(g + row0u * GK, nu, H * GK * 4, GK * 4);
+        uint4 kr[NL], qr[NL];
+        f32x4 gr[NG4];
 #pragma unroll
-        for (int u = 0; u < NE; ++u) {
-            const int idx = tid + u * kThreads, i = idx / DK, cc = idx % DK;
-            const size_t off = (sl.row0 + (size_t)i * H) * DK + cc;
-            kr[u] = i < n ? load_in<IN_BF16>(k, off) : 0.f;
-            qr[u] = i < n ? load_in<IN_BF16>(q, off) : 0.f;
+        for (int u = 0; u < NL; ++u) {
+            const int idx = tid + u * kThreads, i = idx / (DK / EPL), c0 = (idx % (DK / EPL)) * EPL;
+            kr[u] = mx::buf_ld16(rk, (i * H * DK + c0) * es);
+            qr[u] = mx::buf_ld16(rq, (i * H * DK + c0) * es);
         }
 #pragma unroll
-        for (int u = 0; u < NG; ++u) {
-            const int idx = tid + u * kThreads, i = idx / GK, cc = idx % GK;
-            gr[u] = idx < C * GK && i < n ? g[(sl.row0 + (size_t)i * H) * GK + cc] : 0.f;
+        for (int u = 0; u < NG4; ++u) {
+            const int idx4 = tid + u * kThreads, i = idx4 / ((GK + 3) / 4), c0 = (idx4 % ((GK + 3) / 4)) * 4;
+            if constexpr (PC) {
+                gr[u] = __builtin_bit_cast(f32x4, mx::buf_ld16(rg, (i * H * GK + c0) * 4));
+            } else {  // one value per token: thread i < C takes token i
+                gr[u] = f32x4{idx4 < C ? mx::buf_ld4f(rg, idx4 * H * 4) : 0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        auto unpack = [&](const uint4 &r, float *dst) __attribute__((always_inline)) {
+            const unsigned wd[4] = {r.x, r.y, r.z, r.w};
+            if constexpr (IN_BF16) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    dst[2 * e] = __uint_as_float(wd[e] << 16);
+                    dst[2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[e] = __uint_as_float(wd[e]);
+            }
+        };
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+            const int idx = tid + u * kThreads, i = idx / (DK / EPL), c0 = (idx % (DK / EPL)) * EPL;
+            float kv[EPL], qv[EPL];
+            unpack(kr[u], kv);
+            unpack(qr[u], qv);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                sK[i][c0 + e] = kv[e];
+                sQ[i][c0 + e] = qv[e];
+            }
         }
 #pragma unroll
-        for (int u = 0; u < NE; ++u) {
-            const int idx = tid + u * kThreads;
-            sK[idx / DK][idx % DK] = kr[u];
-            sQ[idx / DK][idx % DK] = qr[u];
-        }
+        for (int u = 0; u < NG4; ++u) {
+            const int idx4 = tid + u * kThreads;
+            if constexpr (PC) {
+                const int i = idx4 / (GK / 4), c0 = (idx4 % (GK / 4)) * 4;
 #pragma unroll
-        for (int u = 0; u < NG; ++u) {
-            const int idx = tid + u * kThreads;
-            if (idx < C * GK) sG[idx / GK][idx % GK] = gr[u];
+                for (int e = 0; e < 4; ++e) sG[i][c0 + e] = gr[u][e];
+            } else {
+                if (idx4 < C) sG[idx4][0] = gr[u][0];
+            }
         }
     }
     __syncthreads();
@@ -379,20 +416,29 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
     }
     for (int idx = tid; idx < C * GK; idx += kThreads) wG[(size_t)ci * C * GK + idx] = sG[idx / GK][idx % GK];
     if (tid < C) wB[(size_t)ci * C + tid] = sBeta[tid];
-    // the decayed operands: K~ = exp(G) k, K^ = exp(G_63 - G) k, Q~ = scale exp(G) q
-    for (int idx = tid; idx < C * DK; idx += kThreads) {
-        const int i = idx / DK, cc = idx % DK;
-        float ei, eh;
-        if constexpr (PC) {
-            ei = __expf(sG[i][cc]);
-            eh = __expf(sG[C - 1][cc] - sG[i][cc]);
-        } else {
-            ei = sE[0][i];
-            eh = sE[1][i];
+    // the decayed operands: K~ = exp(G) k, K^ = exp(G_63 - G) k, Q~ = scale exp(G) q (four channels
+    // per thread and step, 16-byte stores)
+    for (int idx4 = tid; idx4 < C * DK / 4; idx4 += kThreads) {
+        const int i = idx4 / (DK / 4), c0 = (idx4 % (DK / 4)) * 4;
+        f32x4 kt, kh, qt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int cc = c0 + e;
+            float ei, eh;
+            if constexpr (PC) {
+                ei = __expf(sG[i][cc]);
+                eh = __expf(sG[C - 1][cc] - sG[i][cc]);
+            } else {
+                ei = sE[0][i];
+                eh = sE[1][i];
+            }
+            kt[e] = ei * sK[i][cc];
+            kh[e] = eh * sK[i][cc];
+            qt[e] = scale * ei * sQ[i][cc];
         }
-        wKt[(size_t)ci * C * DK + idx] = ei * sK[i][cc];
-        wKh[(size_t)ci * C * DK + idx] = eh * sK[i][cc];
-        wQt[(size_t)ci * C * DK + idx] = scale * ei * sQ[i][cc];
+        reinterpret_cast<f32x4 *>(wKt + (size_t)ci * C * DK)[idx4] = kt;
+        reinterpret_cast<f32x4 *>(wKh + (size_t)ci * C * DK)[idx4] = kh;
+        reinterpret_cast<f32x4 *>(wQt + (size_t)ci * C * DK)[idx4] = qt;
     }
     __syncthreads();  // k and q are no longer read
 
@@ -413,9 +459,11 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
     __syncthreads();
     mx::invert_unit_lower(tri, lane, w, lr, lg);  // ends with a barrier
     float *Tg = wT + (size_t)ci * C * C;
-    for (int idx = tid; idx < C * C; idx += kThreads) {
-        const int i = idx / C, j = idx % C, I = i >> 4, J = j >> 4;
-        Tg[idx] = J <= I ? tri.Tb(I, J)[(i & 15) * mx::LT + (j & 15)] : 0.f;
+    for (int idx4 = tid; idx4 < C * C / 4; idx4 += kThreads) {  // 16-byte stores
+        const int i = idx4 / (C / 4), j = (idx4 % (C / 4)) * 4, I = i >> 4, J = j >> 4;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        reinterpret_cast<f32x4 *>(Tg)[idx4] =
+            J <= I ? *reinterpret_cast<const f32x4 *>(&tri.Tb(I, J)[(i & 15) * mx::LT + (j & 15)]) : z;
     }
 }
 
