@@ -175,6 +175,20 @@ __device__ __forceinline__ float buf_in(__amdgpu_buffer_rsrc_t r, int off) {
 }
 using mx::barrier_lds;
 using mx::rows_rsrc;
+// The input elements in 16 loaded bytes, as fp32: eight bf16 or four fp32.
+template <bool BF16>
+__device__ __forceinline__ void unpack16(const uint4 &r, float *dst) {
+    const unsigned wd[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (BF16) {
+            dst[2 * e] = __uint_as_float(wd[e] << 16);
+            dst[2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
+        } else {
+            dst[e] = __uint_as_float(wd[e]);
+        }
+    }
+}
 // A value the same in every lane, in scalar registers (so that a buffer
 // resource built from it is uniform and needs no per-lane loop).
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -283,25 +297,12 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
                 gr[u] = f32x4{idx4 < C ? mx::buf_ld4f(rg, idx4 * H * 4) : 0.f, 0.f, 0.f, 0.f};
             }
         }
-        auto unpack = [&](const uint4 &r, float *dst) __attribute__((always_inline)) {
-            const unsigned wd[4] = {r.x, r.y, r.z, r.w};
-            if constexpr (IN_BF16) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    dst[2 * e] = __uint_as_float(wd[e] << 16);
-                    dst[2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dst[e] = __uint_as_float(wd[e]);
-            }
-        };
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
             const int idx = tid + u * kThreads, i = idx / (DK / EPL), c0 = (idx % (DK / EPL)) * EPL;
             float kv[EPL], qv[EPL];
-            unpack(kr[u], kv);
-            unpack(qr[u], qv);
+            unpack16<IN_BF16>(kr[u], kv);
+            unpack16<IN_BF16>(qr[u], qv);
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
                 sK[i][c0 + e] = kv[e];
@@ -856,31 +857,41 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
     __shared__ float sBeta[C];
     __shared__ float sH[4][DK];      // per wavefront: column sums of dK^ K^
 
-    {  // T'', A, K~, K^: all loads in flight, then the LDS stores
-        float rT[NTT], rA[NTT], rKt[NKK], rKh[NKK];
+    {  // T'', A, K~, K^: all loads in flight (16 bytes per lane), then the LDS stores
+        f32x4 rT[NTT / 4], rA[NTT / 4], rKt[NKK / 4], rKh[NKK / 4];
+        const f32x4 *t4 = reinterpret_cast<const f32x4 *>(wT + (size_t)ci * C * C);
+        const f32x4 *a4 = reinterpret_cast<const f32x4 *>(wA + (size_t)ci * C * C);
+        const f32x4 *kt4 = reinterpret_cast<const f32x4 *>(wKt + (size_t)ci * C * DK);
+        const f32x4 *kh4 = reinterpret_cast<const f32x4 *>(wKh + (size_t)ci * C * DK);
 #pragma unroll
-        for (int u = 0; u < NTT; ++u) {
-            rT[u] = wT[(size_t)ci * C * C + tid + u * kThreads];
-            rA[u] = wA[(size_t)ci * C * C + tid + u * kThreads];
+        for (int u = 0; u < NTT / 4; ++u) {
+            rT[u] = t4[tid + u * kThreads];
+            rA[u] = a4[tid + u * kThreads];
         }
 #pragma unroll
-        for (int u = 0; u < NKK; ++u) {
-            rKt[u] = wKt[(size_t)ci * C * DK + tid + u * kThreads];
-            rKh[u] = wKh[(size_t)ci * C * DK + tid + u * kThreads];
+        for (int u = 0; u < NKK / 4; ++u) {
+            rKt[u] = kt4[tid + u * kThreads];
+            rKh[u] = kh4[tid + u * kThreads];
         }
         if (tid < C) sBeta[tid] = wB[(size_t)ci * C + tid];
 #pragma unroll
-        for (int u = 0; u < NKK; ++u) {
-            const int idx = tid + u * kThreads;
-            sKt[(idx / DK) * kLK + idx % DK] = rKt[u];
-            sKh[(idx / DK) * kLK + idx % DK] = rKh[u];
+        for (int u = 0; u < NKK / 4; ++u) {
+            const int idx = 4 * (tid + u * kThreads), i = idx / DK, cc = idx % DK;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sKt[i * kLK + cc + e] = rKt[u][e];
+                sKh[i * kLK + cc + e] = rKh[u][e];
+            }
         }
         __syncthreads();  // sBeta
 #pragma unroll
-        for (int u = 0; u < NTT; ++u) {
-            const int idx = tid + u * kThreads, i = idx / C, m = idx % C;
-            sT[i * kLT + m] = rT[u] * sBeta[m];
-            sA[i * kLTT + m] = rA[u];
+        for (int u = 0; u < NTT / 4; ++u) {
+            const int idx = 4 * (tid + u * kThreads), i = idx / C, m = idx % C;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sT[i * kLT + m + e] = rT[u][e] * sBeta[m + e];
+                sA[i * kLTT + m + e] = rA[u][e];
+            }
         }
     }
 
@@ -894,7 +905,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
 
     const float *Sg = wS + (size_t)ci * DK * DV;
     const float *dSg = wdS + (size_t)ci * DK * DV;
-    float rS[NSS], rdS[NSS], rO[NVS];
+    f32x4 rS[NSS / 4], rdS[NSS / 4], rO[NVS / 4];  // this thread's four-column pieces of the slice
     f32x4 rV;  // the v slice in the layout of this wavefront's X tile
     // The slice loop's barriers wait for LDS operations only, so the next
     // slice's loads stay in flight across them; every load and store in the
@@ -908,15 +919,15 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
     const auto r_dv = rows_rsrc(dv + row0u * DV, nu, H * DV * 4, DV * 4);
     auto fetch = [&](int j0) {
 #pragma unroll
-        for (int u = 0; u < NSS; ++u) {
-            const int idx = tid + u * kThreads, r = idx / kBS, cc = idx % kBS;
-            rS[u] = Sg[(size_t)r * DV + j0 + cc];
-            rdS[u] = dSg[(size_t)r * DV + j0 + cc];
+        for (int u = 0; u < NSS / 4; ++u) {
+            const int idx = 4 * (tid + u * kThreads), r = idx / kBS, cc = idx % kBS;
+            rS[u] = *reinterpret_cast<const f32x4 *>(&Sg[(size_t)r * DV + j0 + cc]);
+            rdS[u] = *reinterpret_cast<const f32x4 *>(&dSg[(size_t)r * DV + j0 + cc]);
         }
 #pragma unroll
-        for (int u = 0; u < NVS; ++u) {
-            const int idx = tid + u * kThreads, r = idx / kBS, cc = idx % kBS;
-            rO[u] = buf_in<false>(r_o, r * H * DV + j0 + cc);
+        for (int u = 0; u < NVS / 4; ++u) {
+            const int idx = 4 * (tid + u * kThreads), r = idx / kBS, cc = idx % kBS;
+            rO[u] = __builtin_bit_cast(f32x4, mx::buf_ld16(r_o, (r * H * DV + j0 + cc) * 4));
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) rV[r] = buf_in<IN_BF16>(r_v, (16 * w + 4 * lg + r) * H * DV + j0 + lr);
@@ -925,15 +936,15 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
     for (int j0 = 0; j0 < DV; j0 += kBS) {
         barrier_lds();  // the previous slice's reads are done
 #pragma unroll
-        for (int u = 0; u < NSS; ++u) {
-            const int idx = tid + u * kThreads;
-            sS[(idx / kBS) * kLS + idx % kBS] = rS[u];
-            sdS[(idx / kBS) * kLS + idx % kBS] = rdS[u];
+        for (int u = 0; u < NSS / 4; ++u) {
+            const int idx = 4 * (tid + u * kThreads);
+            *reinterpret_cast<f32x4 *>(&sS[(idx / kBS) * kLS + idx % kBS]) = rS[u];
+            *reinterpret_cast<f32x4 *>(&sdS[(idx / kBS) * kLS + idx % kBS]) = rdS[u];
         }
 #pragma unroll
-        for (int u = 0; u < NVS; ++u) {
-            const int idx = tid + u * kThreads;
-            sO[(idx / kBS) * kLS + idx % kBS] = rO[u];
+        for (int u = 0; u < NVS / 4; ++u) {
+            const int idx = 4 * (tid + u * kThreads);
+            *reinterpret_cast<f32x4 *>(&sO[(idx / kBS) * kLS + idx % kBS]) = rO[u];
         }
         f32x4 x = rV;
         fetch(min(j0 + kBS, DV - kBS));
@@ -1238,15 +1249,21 @@ __global__ __launch_bounds__(kThreads, IN_BF16 && !PC ? 2 : 1) void bwd_grads_b_
         if constexpr (KQ16) return static_cast<float>(sQb[r * LQB + c]);
         else return sQ[r][c];
     };
-    // raw k, q: the loads are issued here and stored to LDS below
-    constexpr int NKK = C * DK / kThreads;
-    float rk[NKK], rq[NKK];
+    // raw k, q: the loads (16 bytes per lane, rows past the chunk's end zero through the buffer bounds)
+    // are issued here and stored to LDS below
+    constexpr int es = IN_BF16 ? 2 : 4, EPL = 16 / es, NL = C * DK / EPL / kThreads;
+    uint4 rk[NL], rq[NL];
+    {
+        const size_t row0u = uniform(sl.row0);
+        const int nu = uniform(n);
+        const auto rkb = rows_rsrc(static_cast<const char *>(k) + row0u * DK * es, nu, H * DK * es, DK * es);
+        const auto rqb = rows_rsrc(static_cast<const char *>(q) + row0u * DK * es, nu, H * DK * es, DK * es);
 #pragma unroll
-    for (int u = 0; u < NKK; ++u) {
-        const int idx = tid + u * kThreads, r = idx / DK, cc = idx % DK;
-        const size_t off = (sl.row0 + (size_t)r * H) * DK + cc;
-        rk[u] = r < n ? load_in<IN_BF16>(k, off) : 0.f;
-        rq[u] = r < n ? load_in<IN_BF16>(q, off) : 0.f;
+        for (int u = 0; u < NL; ++u) {
+            const int idx = tid + u * kThreads, r = idx / (DK / EPL), c0 = (idx % (DK / EPL)) * EPL;
+            rk[u] = mx::buf_ld16(rkb, (r * H * DK + c0) * es);
+            rq[u] = mx::buf_ld16(rqb, (r * H * DK + c0) * es);
+        }
     }
     if constexpr (!PC) {
         // dG_i = rowsum_i(Z) - colsum_i(Z), Z = dM o M + dA o A (M in sY, A in sT)
@@ -1271,17 +1288,23 @@ __global__ __launch_bounds__(kThreads, IN_BF16 && !PC ? 2 : 1) void bwd_grads_b_
     if constexpr (KQ16) {
         __syncthreads();  // M and dA / dM' are no longer read
 #pragma unroll
-        for (int u = 0; u < NKK; ++u) {
-            const int idx = tid + u * kThreads;
-            sKb[(idx / DK) * LQB + idx % DK] = static_cast<__bf16>(rk[u]);
-            sQb[(idx / DK) * LQB + idx % DK] = static_cast<__bf16>(rq[u]);
+        for (int u = 0; u < NL; ++u) {  // the bf16 rows as loaded (16-byte aligned: 288-byte rows)
+            const int idx = tid + u * kThreads, r = idx / (DK / EPL), c0 = (idx % (DK / EPL)) * EPL;
+            *reinterpret_cast<uint4 *>(&sKb[r * LQB + c0]) = rk[u];
+            *reinterpret_cast<uint4 *>(&sQb[r * LQB + c0]) = rq[u];
         }
     } else {
 #pragma unroll
-        for (int u = 0; u < NKK; ++u) {
-            const int idx = tid + u * kThreads;
-            sK[idx / DK][idx % DK] = rk[u];
-            sQ[idx / DK][idx % DK] = rq[u];
+        for (int u = 0; u < NL; ++u) {
+            const int idx = tid + u * kThreads, r = idx / (DK / EPL), c0 = (idx % (DK / EPL)) * EPL;
+            float kf[EPL], qf[EPL];
+            unpack16<IN_BF16>(rk[u], kf);
+            unpack16<IN_BF16>(rq[u], qf);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                sK[r][c0 + e] = kf[e];
+                sQ[r][c0 + e] = qf[e];
+            }
         }
     }
     __syncthreads();
