@@ -632,13 +632,15 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
 // the layout of the forward walk above: pair p owns value columns j0 + 16p ..
 // +15, its wavefront h key channels h DK/2 .. of dS' (in registers).  Per
 // chunk, with dO (this lane's column, rows as a D tile) in registers:
-//   dE = K^ dS' + A' dO   (the pair sums its halves of the channel reduction
-//                          through LDS; wavefront h adds A' dO on token tiles
-//                          h and 3 - h)
-//   dX = T''' dE          (both wavefronts of the pair)
+//   P_h = K^[:, half h] dS'_h            (the pair sums the halves through LDS)
+//   dE = P_0 + P_1 + A' dO
+//   dX = Diag(beta) T' dE                (= T''' dE; both wavefronts of the pair)
 //   dS_h = Diag(gam_h) dS'_h + Q~[:, half h]' dO - K~[:, half h]' dX.
-// Rows of K^ are read from LDS as float4, the columns of A, T'', Q~ and K~ one
-// value per lane and step.  Loads and barriers as in the forward walk.
+// Rows of K^ are read from LDS as float4, the columns of A, T, Q~ and K~ one
+// value per lane and step.  The operands move to LDS by global-to-LDS copies
+// as in the forward walk: K^ and A after the exchange barrier, T, Q~, K~, beta
+// and G_63 after the chunk's last barrier; dO goes through registers one chunk
+// ahead.
 template <int DK, int DV, bool PC>
 __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__restrict__ dO, int T, int H, int NC,
                                                                const float *__restrict__ wT,
@@ -656,8 +658,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
     constexpr int HK = DK / 2, NTH = HK / 16;
     constexpr int LKR = DK + 8;  // K^: rows read as float4
     constexpr int LKC = DK + 4;  // Q~, K~: columns read one value per lane (4 lane groups in 4 bank quarters)
-    constexpr int LTC = C + 4;   // A, T'': columns
-    constexpr int NK4 = C * DK / 4 / kThreads, NT4 = C * C / 4 / kThreads;
+    constexpr int LTC = C + 4;   // A, T: columns
     // XCD-aware placement: the value slices of one (sequence, head) share an XCD, so its L2 serves the
     // chunk operands they all read
     int bh, tile;
@@ -674,47 +675,33 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
     __shared__ float sQt[C * LKC];
     __shared__ float sKt[C * LKC];
     __shared__ float sA[C * LTC];
-    __shared__ float sT[C * LTC];      // T'' = T Diag(beta)
-    __shared__ float sGam[DK];
+    __shared__ float sT[C * LTC];
+    __shared__ float sB[C];            // beta of the chunk's tokens
+    __shared__ float sG[DK];           // G_63 per channel (scalar decay: the one value, repeated)
     __shared__ f32x4 sP[2][2][4][64];  // per pair and half: the partial dE tiles
 
-    f32x4 gKh[NK4], gQt[NK4], gKt[NK4], gT[NT4], gA[NT4], gB;
-    f32x4 gO[4];  // dO of the fetched chunk: rows 16 t + 4 lg + e, column jc
-    float gGam = 0.f;
-    auto fetch = [&](int c) {
-        const size_t ci = uniform(wk.slot(c));
+    auto copy_ka = [&](size_t ci) __attribute__((always_inline)) {
+        dma_rows<DK, LKR>(wKh + ci * C * DK, sKh, w, lane);
+        dma_rows<C, LTC>(wA + ci * C * C, sA, w, lane);
+    };
+    auto copy_rest = [&](size_t ci) __attribute__((always_inline)) {
+        dma_rows<C, LTC>(wT + ci * C * C, sT, w, lane);
+        dma_rows<DK, LKC>(wQt + ci * C * DK, sQt, w, lane);
+        dma_rows<DK, LKC>(wKt + ci * C * DK, sKt, w, lane);
+        if (w == 0) mx::lds_dma4(wB + ci * C + lane, mx::lds_addr(sB));
+        if (w >= 1 && w <= DK / 64)
+            mx::lds_dma4(wG + ci * C * GK + (size_t)(C - 1) * GK + (PC ? 64 * (w - 1) + lane : 0),
+                         mx::lds_addr(sG + 64 * (w - 1)));
+    };
+    f32x4 gO[4];  // dO of a chunk: rows 16 t + 4 lg + e, column jc
+    auto load_do = [&](int c) __attribute__((always_inline)) {
         const int n = uniform(wk.count(c));
         const size_t row0 = uniform(wk.row0(c));
-        const f32x4 *kh4 = reinterpret_cast<const f32x4 *>(wKh + ci * C * DK);
-        const f32x4 *qt4 = reinterpret_cast<const f32x4 *>(wQt + ci * C * DK);
-        const f32x4 *kt4 = reinterpret_cast<const f32x4 *>(wKt + ci * C * DK);
-        const f32x4 *t4 = reinterpret_cast<const f32x4 *>(wT + ci * C * C);
-        const f32x4 *a4 = reinterpret_cast<const f32x4 *>(wA + ci * C * C);
-#pragma unroll
-        for (int u = 0; u < NK4; ++u) {
-            gKh[u] = kh4[tid + u * kThreads];
-            gQt[u] = qt4[tid + u * kThreads];
-            gKt[u] = kt4[tid + u * kThreads];
-        }
-#pragma unroll
-        for (int u = 0; u < NT4; ++u) {
-            gT[u] = t4[tid + u * kThreads];
-            gA[u] = a4[tid + u * kThreads];
-        }
-        gB = reinterpret_cast<const f32x4 *>(wB + ci * C)[tid % (C / 4)];
-        gGam = __expf(wG[ci * C * GK + (size_t)(C - 1) * GK + (PC ? tid % DK : 0)]);
         const auto ro = rows_rsrc(dO + row0 * DV, n, H * DV * 4, DV * 4);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) gO[t][e] = buf_in<false>(ro, (16 * t + 4 * lg + e) * H * DV + jc);
-    };
-    auto stage_rows = [&](float *dst, int ld, const f32x4 *src, int cols, int count) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < count; ++u) {
-            const int idx4 = tid + u * kThreads, row = idx4 / (cols / 4), c4 = idx4 % (cols / 4);
-            *reinterpret_cast<f32x4 *>(&dst[row * ld + 4 * c4]) = src[u];
-        }
     };
 
     const size_t sbase = (size_t)bh * DK * DV;
@@ -724,30 +711,24 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             dsv[t][e] = ds_final ? ds_final[sbase + (size_t)(kh0 + 16 * t + 4 * lg + e) * DV + jc] : 0.f;
-    if (wk.nc > 0) fetch(wk.nc - 1);
+    if (wk.nc > 0) {
+        const size_t cl = uniform(wk.slot(wk.nc - 1));
+        copy_ka(cl);
+        copy_rest(cl);
+        load_do(wk.nc - 1);
+        barrier_vm<0>();
+    }
     for (int c = wk.nc - 1; c >= 0; --c) {
         const size_t ci = uniform(wk.slot(c));
-        barrier_lds();  // the previous chunk's LDS reads are done
-        stage_rows(sKh, LKR, gKh, DK, NK4);
-        stage_rows(sQt, LKC, gQt, DK, NK4);
-        stage_rows(sKt, LKC, gKt, DK, NK4);
-        stage_rows(sA, LTC, gA, C, NT4);
-#pragma unroll
-        for (int u = 0; u < NT4; ++u) {
-            const int idx4 = tid + u * kThreads, row = idx4 / (C / 4), c4 = idx4 % (C / 4);
-            *reinterpret_cast<f32x4 *>(&sT[row * LTC + 4 * c4]) = gT[u] * gB;
-        }
-        if (tid < DK) sGam[tid] = gGam;
-        const f32x4 ov[4] = {gO[0], gO[1], gO[2], gO[3]};
-        // dS' of this chunk to the workspace (before the next loads, as in the forward walk)
+        const bool more = c > 0;
+        const size_t cn = uniform(wk.slot(more ? c - 1 : c));
+        // dS' of this chunk to the workspace
         float *dSg = wdS + ci * DK * DV;
 #pragma unroll
         for (int t = 0; t < NTH; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) dSg[(size_t)(kh0 + 16 * t + 4 * lg + e) * DV + jc] = dsv[t][e];
-        fetch(max(c - 1, 0));
-        barrier_lds();  // the chunk's operands are in LDS
-        // partial dE: K^[:, half h] dS'_h ...
+        // P_h = K^[:, half h] dS'_h
         f32x4 pp[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int t = 0; t < NTH; ++t)
@@ -757,27 +738,26 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
 #pragma unroll
                 for (int e = 0; e < 4; ++e) pp[M] = mfma4(a4[e], dsv[t][e], pp[M]);
             }
-        // ... + A' dO on token tiles h and 3 - h (A' upper triangular: blocks t >= M)
-        auto adO = [&](f32x4 &acc, int M) __attribute__((always_inline)) {
+#pragma unroll
+        for (int M = 0; M < 4; ++M) sP[p][h][M][lane] = pp[M];
+        barrier_vm<0>();  // partial tiles; this chunk's T, Q~, K~, beta, G_63 and dO have landed
+        const f32x4 ov[4] = {gO[0], gO[1], gO[2], gO[3]};
+        // dE = P_0 + P_1 + A' dO (A' upper triangular: blocks t >= M); A is read before K^ and A are
+        // refilled below, so the copies wait for these reads
+        f32x4 de[4];
+#pragma unroll
+        for (int M = 0; M < 4; ++M) {
+            f32x4 acc = pp[M] + sP[p][h ^ 1][M][lane];  // the same sum in both
 #pragma unroll
             for (int t = M; t < 4; ++t)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc = mfma4(sA[(16 * t + 4 * lg + e) * LTC + 16 * M + lr], ov[t][e], acc);
-        };
-        if (h == 0) {
-            adO(pp[0], 0);
-            adO(pp[3], 3);
-        } else {
-            adO(pp[1], 1);
-            adO(pp[2], 2);
+            de[M] = acc;
         }
-#pragma unroll
-        for (int M = 0; M < 4; ++M) sP[p][h][M][lane] = pp[M];
-        barrier_lds();  // both partial tiles of each pair
-        f32x4 de[4];
-#pragma unroll
-        for (int M = 0; M < 4; ++M) de[M] = pp[M] + sP[p][h ^ 1][M][lane];  // the same sum in both
-        // dX = T''' dE (T''' upper triangular)
+        barrier_vm<0>();  // every wavefront's reads of K^ and A are done
+        if (more) copy_ka(cn);
+        load_do(more ? c - 1 : c);  // the last 16 loads: the barrier below may leave them in flight
+        // dX = Diag(beta) T' dE (T' upper triangular)
         f32x4 dx[4];
 #pragma unroll
         for (int M = 0; M < 4; ++M) {
@@ -786,14 +766,15 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
             for (int t = M; t < 4; ++t)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc = mfma4(sT[(16 * t + 4 * lg + e) * LTC + 16 * M + lr], de[t][e], acc);
-            dx[M] = acc;
+            dx[M] = acc * *reinterpret_cast<const f32x4 *>(&sB[16 * M + 4 * lg]);
         }
         // dS_h = Diag(gam) dS'_h + Q~[:, half h]' dO - K~[:, half h]' dX (no K~ term without the delta
         // rule: X does not depend on S then)
 #pragma unroll
         for (int J = 0; J < NTH; ++J) {
-            const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&sGam[kh0 + 16 * J + 4 * lg]);
-            f32x4 acc = g4 * dsv[J];
+            f32x4 acc;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = __expf(sG[PC ? kh0 + 16 * J + 4 * lg + e : 0]) * dsv[J][e];
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -808,6 +789,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
             }
             dsv[J] = acc;
         }
+        barrier_vm<16>();  // the previous chunk's K^ and A have landed; T, Q~, K~, beta, G_63 are free
+        if (more) copy_rest(cn);
     }
     if (ds0) {
 #pragma unroll

@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
     int n;
     chunk_place(ci, T, H, NC, tb, r0_unused, n);
     char *recb = ws + (size_t)ci * kRecBytes;
-    __syncthreads();  // the previous chunk's tiles are no longer read
+    barrier_lds();  // the previous chunk's tiles are no longer read
 
     // ---- gates of token `lane`: cumulative log-decay and beta (eta)
     float Gl = lane < n ? gv : 0.f;
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
         *reinterpret_cast<uint4 *>(&sm.u.qk.K[(i0 + 16 * it) * LQK + 8 * seg]) = kv[it];
     }
     prefetch(min(ci + (int)gridDim.x, total - 1));
-    __syncthreads();
+    barrier_lds();
 
     // ---- K K^T (wavefronts 0, 1) and Q K^T (2, 3) on the lower tiles: even
     // wavefronts take row blocks {0, 3}, odd ones {1, 2}
@@ -204,10 +204,10 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
             }
         }
     }
-    __syncthreads();  // G, eta (and |k|^2) in LDS; q and k no longer read
+    barrier_lds();  // G, eta (and |k|^2) in LDS; q and k no longer read
     if constexpr (KZ) {
         write_strength<KZ>(sm.eta, sm.kk, n, eps, w, lane);
-        __syncthreads();
+        barrier_lds();
     }
 
     // ---- decay (and beta for R) applied in fp32; R and A tiles to LDS (no R
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
             dst[(4 * lg + r) * LT + lr] = val;
         }
     }
-    __syncthreads();
+    barrier_lds();
 
     // ---- T = (I + R)^{-1}, then the T'' and A operand fragments
     if constexpr (DELTA) invert_unit_lower(tri, lane, w, lr, lg);

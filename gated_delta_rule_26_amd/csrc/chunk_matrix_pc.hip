@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void intra_pc_kernel(
     int n;
     chunk_place(ci, T, H, NC, tb, r0_unused, n);
     char *recb = ws + (size_t)ci * kPcBytes;
-    __syncthreads();  // the previous chunk's tiles and G are no longer read
+    barrier_lds();  // the previous chunk's tiles and G are no longer read
 
     // ---- gates: thread (gc, gh) scans tokens 32gh .. 32gh+31 of key channel gc
     float gl[32];
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void intra_pc_kernel(
         *reinterpret_cast<uint4 *>(&sm.u.qk.K[(i0 + 16 * it) * LQK + 8 * seg]) = kv[it];
     }
     prefetch(min(ci + (int)gridDim.x, total - 1));
-    __syncthreads();
+    barrier_lds();
 
     if (gh == 1) {
         const float cr = sm.carry[gc];
@@ -177,10 +177,10 @@ __global__ __launch_bounds__(kIntraThreads, 2) void intra_pc_kernel(
         s += __shfl_xor(s, 2, 64);
         if (qd == 0) sm.kk[i] = s;
     }
-    __syncthreads();  // G, spans, eta (and |k|^2) in LDS
+    barrier_lds();  // G, spans, eta (and |k|^2) in LDS
     if constexpr (KZ) {
         write_strength<KZ>(sm.eta, sm.kk, n, eps, w, lane);
-        __syncthreads();
+        barrier_lds();
     }
 
     // ---- decayed operands of the walk into the record
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void intra_pc_kernel(
         if (__uint_as_float(sm.span[Ia]) > kSpanMax) direct_tile(Ia, accR[1], accA[1]);
         if (__uint_as_float(sm.span[Ib]) > kSpanMax) direct_tile(Ib, accR[2], accA[2]);
     }
-    __syncthreads();  // q, k no longer read: the tiles may overwrite them
+    barrier_lds();  // q, k no longer read: the tiles may overwrite them
 
     // ---- beta (R) and the output scale (A); strictly lower R, lower A
     auto put = [&](int I, int J, const f32x4 &aR, const f32x4 &aA) {
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void intra_pc_kernel(
     put(Ia, J0, accR[0], accA[0]);
     put(Ia, J0 + 1, accR[1], accA[1]);
     if (three) put(Ib, Ib, accR[2], accA[2]);
-    __syncthreads();
+    barrier_lds();
 
     // ---- T = (I + R)^{-1}, then the T'' and A operand fragments
     if constexpr (DELTA) invert_unit_lower(tri, lane, w, lr, lg);

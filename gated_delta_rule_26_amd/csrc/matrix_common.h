@@ -174,6 +174,13 @@ struct TriTiles {
     }
 };
 
+// Workgroup barrier for data exchanged through LDS only: waits for this
+// wavefront's LDS operations, not for its global loads, so loads issued for a
+// later chunk stay in flight across it (a full __syncthreads also waits for
+// every outstanding global load).  The memory clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // T = (I + R)^{-1} for the unit lower-triangular I + R of one chunk, by all
 // 256 threads: the 16x16 diagonal blocks by forward substitution (wavefront w
 // takes block w, one column per lane, rows read ahead with 16-byte reads),
@@ -207,7 +214,7 @@ __device__ __forceinline__ void invert_unit_lower(const TriTiles &t, int lane, i
 #pragma unroll
         for (int i = 0; i < 16; ++i) blk[i * LT + cc] = xcol[i];
     }
-    __syncthreads();
+    barrier_lds();
     auto inverse_tile = [&](int I, int J) {
         f32x4 P = {0.f, 0.f, 0.f, 0.f};
         for (int M = J; M < I; ++M) {
@@ -225,11 +232,11 @@ __device__ __forceinline__ void invert_unit_lower(const TriTiles &t, int lane, i
         for (int r = 0; r < 4; ++r) dst[(4 * lg + r) * LT + lr] = -out[r];
     };
     if (w < 3) inverse_tile(w + 1, w);
-    __syncthreads();
+    barrier_lds();
     if (w < 2) inverse_tile(w + 2, w);
-    __syncthreads();
+    barrier_lds();
     if (w == 0) inverse_tile(3, 0);
-    __syncthreads();
+    barrier_lds();
 }
 
 // The write strength of the chunk's tokens in place: beta stays; for the
@@ -283,12 +290,6 @@ constexpr int NS = DV / BV;         // workgroups per (sequence, head)
 constexpr int LDV = BV + 8;         // bf16 row stride of the token-major v slice
 constexpr int kXFrags = 8;          // chain -> helper: the read Q S and E (4 fp32 tiles each)
 
-// Workgroup barrier for data exchanged through LDS only: waits for this
-// wavefront's LDS operations, not for its global loads, so loads issued for a
-// later chunk stay in flight across it (a full __syncthreads also waits for
-// every outstanding global load).  The memory clobber keeps the compiler from
-// moving LDS accesses across it.
-__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // ds_read_b64_tr_b16 (gfx950): every lane names 8 bytes (four bf16) of LDS;
 // within each group of 16 lanes, element e of lane i of the result is element
