@@ -223,16 +223,14 @@ __device__ __forceinline__ void dma_rows(const float *src, float *dst, int w, in
     }
 }
 
-// LDS row strides (floats).  A row-indexed-by-lane read (rows lr, columns
-// lg) is free of bank conflicts at a stride of 2 mod 32, a column-indexed one
-// (rows lg, columns lr) at 16 mod 32; 18 serves both with at most two lanes
-// of a half-wavefront sharing a bank.
+// LDS row strides (floats) of the fp32-tile forward walk.  A
+// row-indexed-by-lane read (rows lr, columns lg) is free of bank conflicts at
+// a stride of 2 mod 32, a column-indexed one (rows lg, columns lr) at 16 mod
+// 32.
 constexpr int kLK = 130;  // C x DK operands read row-wise (K~ in X = V - K~ S, K^ in dE)
 constexpr int kLKT = 144; // C x DK operands read column-wise (K^' , K~', Q~')
 constexpr int kLT = 66;   // C x C read row-wise (T'' in E = T'' X)
-constexpr int kLTT = 80;  // C x C read column-wise (A', T'')
 constexpr int kLB = 48;   // B operands of 32 columns, read column-wise
-constexpr int kLS = 20;   // 16-column slices, read both ways and as float4 rows (16-byte aligned)
 
 // ============================================================ prep
 // One workgroup per chunk.  M and A on fp32 matrix-core tiles (wavefront w
@@ -807,7 +805,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
 // and, accumulated over the slices in matrix-core accumulators,
 //   dQ~ += dO S',  dK~ -= dX S',  dK^ += E dS'',  dA += dO E',  dT'' += dE X'.
 // Then the parts of dq, dk, dG through K~, Q~, K^ and gam; dA and dT'' to the
-// workspace.  The slice operands are loaded one slice ahead.
+// workspace.  Every product takes reduction index 16 t + 4 lg + e in step
+// (t, e) from lane group lg, so that each operand gives a lane its four values
+// as one float4 of a row: the wavefront's rows of K~ and K^ stay in registers
+// in that order, and the LDS holds the other operands in the orientation that
+// makes the reduction index run along rows (T'' and its transpose, A
+// transposed, the slices of S, dS' and dO both ways, X and dE both ways).  The
+// slice operands are loaded one slice ahead; the barriers wait for LDS
+// operations only, so those loads stay in flight across them.
 template <int DK, int DV, bool PC, bool IN_BF16>
 __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
     const void *__restrict__ v, const float *__restrict__ dO, int T, int H, int NC, float scale,
@@ -817,63 +822,62 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
     float *__restrict__ wdA, float *__restrict__ wdTT, float *__restrict__ wdG, float *__restrict__ wdG63,
     float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv, bool delta, SeqTable tb) {
     constexpr int GK = PC ? DK : 1;
-    constexpr int NTT = C * C / kThreads, NKK = C * DK / kThreads;
-    constexpr int NSS = DK * kBS / kThreads, NVS = C * kBS / kThreads;
-    constexpr int JK = DK / 16;  // column tiles of the C x DK accumulators
+    constexpr int JK = DK / 16;   // column tiles of the C x DK accumulators, and reduction blocks over channels
+    constexpr int LR = kBS + 4;   // rows of a 16-column slice (16-byte aligned)
+    constexpr int LSt = DK + 4;   // rows of a transposed DK x 16 slice
+    constexpr int LCt = C + 4;    // rows of C x C operands and of transposed C x 16 tiles
+    constexpr int NT4 = C * C / 4 / kThreads;       // float4s per thread of a C x C operand
+    constexpr int NS4 = DK * kBS / 4 / kThreads;    // float4s per thread of a DK x 16 slice
     const int ci = blockIdx.x;
     if (!slot_used(ci, H, tb)) return;
     const Slot sl = slot_of(ci, T, H, NC, tb);
     const int n = sl.n;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
-    __shared__ float sKt[C * kLK];
-    __shared__ float sKh[C * kLK];
-    __shared__ float sT[C * kLT];    // T'' = T Diag(beta)
-    __shared__ float sA[C * kLTT];
-    __shared__ float sS[DK * kLS];   // entering state, this slice
-    __shared__ float sdS[DK * kLS];  // dS', this slice
-    __shared__ float sO[C * kLS];
-    __shared__ float sX[C * kLS];
-    __shared__ float sE[C * kLS];
-    __shared__ float sdE[C * kLS];
-    __shared__ float sdX[C * kLS];
+    __shared__ float sT[C * LCt];     // T'' = T Diag(beta)
+    __shared__ float sTt[C * LCt];    // transpose(T'')
+    __shared__ float sAt[C * LCt];    // transpose(A)
+    __shared__ float sS[DK * LR], sdS[DK * LR];         // slices of S and dS', channel rows
+    __shared__ float sSt[kBS * LSt], sdSt[kBS * LSt];   // the same, column rows
+    __shared__ float sO[C * LR], sOt[kBS * LCt];        // slice of dO, token rows and column rows
+    __shared__ float sX[C * LR], sXt[kBS * LCt];
+    __shared__ float sdE[C * LR], sdEt[kBS * LCt];
+    __shared__ float sE[C * LR], sdX[C * LR];
     __shared__ float sBeta[C];
-    __shared__ float sH[4][DK];      // per wavefront: column sums of dK^ K^
+    __shared__ float sH[4][DK];       // per wavefront: column sums of dK^ K^
 
-    {  // T'', A, K~, K^: all loads in flight (16 bytes per lane), then the LDS stores
-        f32x4 rT[NTT / 4], rA[NTT / 4], rKt[NKK / 4], rKh[NKK / 4];
+    // this wavefront's rows of K~ and K^: kt[t][e] = K~[16w + lr][16t + 4lg + e]
+    f32x4 kt[JK], kh[JK];
+    {
+        const float *ktr = wKt + ((size_t)ci * C + 16 * w + lr) * DK + 4 * lg;
+        const float *khr = wKh + ((size_t)ci * C + 16 * w + lr) * DK + 4 * lg;
+#pragma unroll
+        for (int t = 0; t < JK; ++t) {
+            kt[t] = *reinterpret_cast<const f32x4 *>(ktr + 16 * t);
+            kh[t] = *reinterpret_cast<const f32x4 *>(khr + 16 * t);
+        }
+    }
+    {  // T'' both ways and A transposed: all loads in flight (16 bytes per lane), then the LDS stores
+        f32x4 rT[NT4], rA[NT4];
         const f32x4 *t4 = reinterpret_cast<const f32x4 *>(wT + (size_t)ci * C * C);
         const f32x4 *a4 = reinterpret_cast<const f32x4 *>(wA + (size_t)ci * C * C);
-        const f32x4 *kt4 = reinterpret_cast<const f32x4 *>(wKt + (size_t)ci * C * DK);
-        const f32x4 *kh4 = reinterpret_cast<const f32x4 *>(wKh + (size_t)ci * C * DK);
 #pragma unroll
-        for (int u = 0; u < NTT / 4; ++u) {
+        for (int u = 0; u < NT4; ++u) {
             rT[u] = t4[tid + u * kThreads];
             rA[u] = a4[tid + u * kThreads];
         }
-#pragma unroll
-        for (int u = 0; u < NKK / 4; ++u) {
-            rKt[u] = kt4[tid + u * kThreads];
-            rKh[u] = kh4[tid + u * kThreads];
-        }
+        // the columns of this thread's pieces: beta[m0 .. m0 + 3]
+        const f32x4 b4 = reinterpret_cast<const f32x4 *>(wB + (size_t)ci * C)[tid % (C / 4)];
         if (tid < C) sBeta[tid] = wB[(size_t)ci * C + tid];
 #pragma unroll
-        for (int u = 0; u < NKK / 4; ++u) {
-            const int idx = 4 * (tid + u * kThreads), i = idx / DK, cc = idx % DK;
+        for (int u = 0; u < NT4; ++u) {
+            const int idx4 = tid + u * kThreads, i = idx4 / (C / 4), m0 = (idx4 % (C / 4)) * 4;
+            const f32x4 tt = rT[u] * b4;
+            *reinterpret_cast<f32x4 *>(&sT[i * LCt + m0]) = tt;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                sKt[i * kLK + cc + e] = rKt[u][e];
-                sKh[i * kLK + cc + e] = rKh[u][e];
-            }
-        }
-        __syncthreads();  // sBeta
-#pragma unroll
-        for (int u = 0; u < NTT / 4; ++u) {
-            const int idx = 4 * (tid + u * kThreads), i = idx / C, m = idx % C;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sT[i * kLT + m + e] = rT[u][e] * sBeta[m + e];
-                sA[i * kLTT + m + e] = rA[u][e];
+                sTt[(m0 + e) * LCt + i] = tt[e];
+                sAt[(m0 + e) * LCt + i] = rA[u][e];
             }
         }
     }
@@ -888,90 +892,119 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
 
     const float *Sg = wS + (size_t)ci * DK * DV;
     const float *dSg = wdS + (size_t)ci * DK * DV;
-    f32x4 rS[NSS / 4], rdS[NSS / 4], rO[NVS / 4];  // this thread's four-column pieces of the slice
-    f32x4 rV;  // the v slice in the layout of this wavefront's X tile
-    // The slice loop's barriers wait for LDS operations only, so the next
-    // slice's loads stay in flight across them; every load and store in the
-    // loop is issued unconditionally (buffer bounds drop the rows past the
-    // chunk's end), which keeps the compiler's wait counts exact.
     const size_t row0u = uniform(sl.row0);
     const int nu = uniform(n);
     constexpr int es = IN_BF16 ? 2 : 4;
     const auto r_o = rows_rsrc(dO + row0u * DV, nu, H * DV * 4, DV * 4);
     const auto r_v = rows_rsrc(static_cast<const char *>(v) + row0u * DV * es, nu, H * DV * es, DV * es);
     const auto r_dv = rows_rsrc(dv + row0u * DV, nu, H * DV * 4, DV * 4);
-    auto fetch = [&](int j0) {
+    f32x4 rS[NS4], rdS[NS4], rO;  // this thread's four-column pieces of the slice
+    f32x4 rV;                      // v in the layout of this wavefront's X tile
+    // every load and store in the slice loop is issued unconditionally (buffer bounds drop the rows past
+    // the chunk's end), which keeps the compiler's wait counts exact
+    auto fetch = [&](int j0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < NSS / 4; ++u) {
-            const int idx = 4 * (tid + u * kThreads), r = idx / kBS, cc = idx % kBS;
-            rS[u] = *reinterpret_cast<const f32x4 *>(&Sg[(size_t)r * DV + j0 + cc]);
-            rdS[u] = *reinterpret_cast<const f32x4 *>(&dSg[(size_t)r * DV + j0 + cc]);
+        for (int u = 0; u < NS4; ++u) {
+            const int idx4 = tid + u * kThreads, r = idx4 / (kBS / 4), c0 = (idx4 % (kBS / 4)) * 4;
+            rS[u] = *reinterpret_cast<const f32x4 *>(&Sg[(size_t)r * DV + j0 + c0]);
+            rdS[u] = *reinterpret_cast<const f32x4 *>(&dSg[(size_t)r * DV + j0 + c0]);
         }
-#pragma unroll
-        for (int u = 0; u < NVS / 4; ++u) {
-            const int idx = 4 * (tid + u * kThreads), r = idx / kBS, cc = idx % kBS;
-            rO[u] = __builtin_bit_cast(f32x4, mx::buf_ld16(r_o, (r * H * DV + j0 + cc) * 4));
+        {
+            const int r = tid / (kBS / 4), c0 = (tid % (kBS / 4)) * 4;  // C x 16 = 256 float4s
+            rO = __builtin_bit_cast(f32x4, mx::buf_ld16(r_o, (r * H * DV + j0 + c0) * 4));
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) rV[r] = buf_in<IN_BF16>(r_v, (16 * w + 4 * lg + r) * H * DV + j0 + lr);
     };
     fetch(0);
     for (int j0 = 0; j0 < DV; j0 += kBS) {
-        barrier_lds();  // the previous slice's reads are done
+        barrier_lds();  // the previous slice's reads are done (and, first time, T'', A staged)
 #pragma unroll
-        for (int u = 0; u < NSS / 4; ++u) {
-            const int idx = 4 * (tid + u * kThreads);
-            *reinterpret_cast<f32x4 *>(&sS[(idx / kBS) * kLS + idx % kBS]) = rS[u];
-            *reinterpret_cast<f32x4 *>(&sdS[(idx / kBS) * kLS + idx % kBS]) = rdS[u];
-        }
+        for (int u = 0; u < NS4; ++u) {
+            const int idx4 = tid + u * kThreads, r = idx4 / (kBS / 4), c0 = (idx4 % (kBS / 4)) * 4;
+            *reinterpret_cast<f32x4 *>(&sS[r * LR + c0]) = rS[u];
+            *reinterpret_cast<f32x4 *>(&sdS[r * LR + c0]) = rdS[u];
 #pragma unroll
-        for (int u = 0; u < NVS / 4; ++u) {
-            const int idx = 4 * (tid + u * kThreads);
-            *reinterpret_cast<f32x4 *>(&sO[(idx / kBS) * kLS + idx % kBS]) = rO[u];
+            for (int e = 0; e < 4; ++e) {
+                sSt[(c0 + e) * LSt + r] = rS[u][e];
+                sdSt[(c0 + e) * LSt + r] = rdS[u][e];
+            }
         }
-        f32x4 x = rV;
+        {
+            const int r = tid / (kBS / 4), c0 = (tid % (kBS / 4)) * 4;
+            *reinterpret_cast<f32x4 *>(&sO[r * LR + c0]) = rO;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sOt[(c0 + e) * LCt + r] = rO[e];
+        }
+        const f32x4 vv = rV;
         fetch(min(j0 + kBS, DV - kBS));
         barrier_lds();
-        // X = V - K~ S;  dE = A' dO + K^ dS'
-        f32x4 de = z4;
-        for (int kk = 0; kk < DK; kk += 4) {
-            if (delta) x = mfma4(-sKt[(16 * w + lr) * kLK + kk + lg], sS[(kk + lg) * kLS + lr], x);
-            de = mfma4(sKh[(16 * w + lr) * kLK + kk + lg], sdS[(kk + lg) * kLS + lr], de);
+        // X = V - K~ S;  dE = K^ dS' + A' dO (A' upper triangular: token blocks t >= w)
+        f32x4 x = z4, de = z4;
+#pragma unroll
+        for (int t = 0; t < JK; ++t) {
+            const f32x4 bs = *reinterpret_cast<const f32x4 *>(&sSt[lr * LSt + 16 * t + 4 * lg]);
+            const f32x4 bd = *reinterpret_cast<const f32x4 *>(&sdSt[lr * LSt + 16 * t + 4 * lg]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x = mfma4(kt[t][e], bs[e], x);
+                de = mfma4(kh[t][e], bd[e], de);
+            }
         }
-        for (int kk = 16 * w; kk < C; kk += 4) de = mfma4(sA[(kk + lg) * kLTT + 16 * w + lr], sO[(kk + lg) * kLS + lr], de);
+        x = delta ? vv - x : vv;  // without the delta rule X = V
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (t < w) continue;
+            const f32x4 aa = *reinterpret_cast<const f32x4 *>(&sAt[(16 * w + lr) * LCt + 16 * t + 4 * lg]);
+            const f32x4 bo = *reinterpret_cast<const f32x4 *>(&sOt[lr * LCt + 16 * t + 4 * lg]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) de = mfma4(aa[e], bo[e], de);
+        }
+        *reinterpret_cast<f32x4 *>(&sXt[lr * LCt + 16 * w + 4 * lg]) = x;
+        *reinterpret_cast<f32x4 *>(&sdEt[lr * LCt + 16 * w + 4 * lg]) = de;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            sX[(16 * w + 4 * lg + r) * kLS + lr] = x[r];
-            sdE[(16 * w + 4 * lg + r) * kLS + lr] = de[r];
+            sX[(16 * w + 4 * lg + r) * LR + lr] = x[r];
+            sdE[(16 * w + 4 * lg + r) * LR + lr] = de[r];
         }
         barrier_lds();
-        // E = T'' X (lower triangular);  dX = transpose(T'') dE (upper triangular)
-        f32x4 e = z4, dx = z4;
-        for (int kk = 0; kk < 16 * (w + 1); kk += 4) e = mfma4(sT[(16 * w + lr) * kLT + kk + lg], sX[(kk + lg) * kLS + lr], e);
-        for (int kk = 16 * w; kk < C; kk += 4) dx = mfma4(sT[(kk + lg) * kLT + 16 * w + lr], sdE[(kk + lg) * kLS + lr], dx);
+        // E = T'' X (token blocks t <= w);  dX = transpose(T'') dE (blocks t >= w)
+        f32x4 ee = z4, dx = z4;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (t <= w) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(&sT[(16 * w + lr) * LCt + 16 * t + 4 * lg]);
+                const f32x4 b = *reinterpret_cast<const f32x4 *>(&sXt[lr * LCt + 16 * t + 4 * lg]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ee = mfma4(a[e], b[e], ee);
+            }
+            if (t >= w) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(&sTt[(16 * w + lr) * LCt + 16 * t + 4 * lg]);
+                const f32x4 b = *reinterpret_cast<const f32x4 *>(&sdEt[lr * LCt + 16 * t + 4 * lg]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dx = mfma4(a[e], b[e], dx);
+            }
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = 16 * w + 4 * lg + r;
-            sE[i * kLS + lr] = e[r];
-            sdX[i * kLS + lr] = dx[r];
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dx[r]), r_dv,
-                                                  (i * H * DV + j0 + lr) * 4, 0, 0);
+            sE[i * LR + lr] = ee[r];
+            sdX[i * LR + lr] = dx[r];
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dx[r]), r_dv, (i * H * DV + j0 + lr) * 4, 0, 0);
         }
         barrier_lds();
-        // accumulators of rows 16w .. (reduction over this slice's 16 value
-        // columns; step e of lane group lg takes column 4 lg + e, so each
-        // operand row gives a lane its four values as one float4)
+        // accumulators of rows 16w .. (reduction over this slice's 16 value columns; step e of lane
+        // group lg takes column 4 lg + e)
         {
-            const int ka = (16 * w + lr) * kLS + 4 * lg;
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            const int ka = (16 * w + lr) * LR + 4 * lg;
             // without the delta rule X does not depend on K~, and T'' (so beta) is fixed
             const f32x4 ao = *reinterpret_cast<const f32x4 *>(&sO[ka]);
             const f32x4 ae = *reinterpret_cast<const f32x4 *>(&sE[ka]);
-            const f32x4 ax = delta ? -*reinterpret_cast<const f32x4 *>(&sdX[ka]) : z;
-            const f32x4 ade = delta ? *reinterpret_cast<const f32x4 *>(&sdE[ka]) : z;
+            const f32x4 ax = delta ? -*reinterpret_cast<const f32x4 *>(&sdX[ka]) : z4;
+            const f32x4 ade = delta ? *reinterpret_cast<const f32x4 *>(&sdE[ka]) : z4;
 #pragma unroll
             for (int J = 0; J < JK; ++J) {
-                const int kb = (16 * J + lr) * kLS + 4 * lg;
+                const int kb = (16 * J + lr) * LR + 4 * lg;
                 const f32x4 bs = *reinterpret_cast<const f32x4 *>(&sS[kb]);
                 const f32x4 bd = *reinterpret_cast<const f32x4 *>(&sdS[kb]);
 #pragma unroll
@@ -983,7 +1016,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
             }
 #pragma unroll
             for (int J = 0; J < 4; ++J) {
-                const int kb = (16 * J + lr) * kLS + 4 * lg;
+                const int kb = (16 * J + lr) * LR + 4 * lg;
                 const f32x4 be = *reinterpret_cast<const f32x4 *>(&sE[kb]);
                 const f32x4 bx = *reinterpret_cast<const f32x4 *>(&sX[kb]);
 #pragma unroll
@@ -994,10 +1027,12 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
             }
         }
         if (tid < DK) {
-            float s = 0.f;
+            const f32x4 *s4 = reinterpret_cast<const f32x4 *>(&sS[tid * LR]);
+            const f32x4 *d4 = reinterpret_cast<const f32x4 *>(&sdS[tid * LR]);
+            f32x4 acc = z4;
 #pragma unroll
-            for (int cc = 0; cc < kBS; ++cc) s += sdS[tid * kLS + cc] * sS[tid * kLS + cc];
-            dgam += s;
+            for (int q = 0; q < kBS / 4; ++q) acc += d4[q] * s4[q];
+            dgam += (acc[0] + acc[1]) + (acc[2] + acc[3]);
         }
     }
 
@@ -1025,15 +1060,15 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
             const int i = 16 * w + 4 * lg + r;
             const float gi = Gc[i * GK + (PC ? ch : 0)];
             const float ei = __expf(gi);
-            const float kt = sKt[i * kLK + ch], kh = sKh[i * kLK + ch];
+            const float ktv = wKt[((size_t)ci * C + i) * DK + ch], khv = wKh[((size_t)ci * C + i) * DK + ch];
             const float qt = wQt[((size_t)ci * C + i) * DK + ch];
             if (i < n) {
                 const size_t off = (sl.row0 + (size_t)i * H) * DK + ch;
                 dq[off] = scale * ei * aQ[J][r];
                 dk[off] = ei * aKt[J][r] + __expf(ge - gi) * aKh[J][r];
             }
-            const float part = aKt[J][r] * kt + aQ[J][r] * qt - aKh[J][r] * kh;
-            colh[J] += aKh[J][r] * kh;
+            const float part = aKt[J][r] * ktv + aQ[J][r] * qt - aKh[J][r] * khv;
+            colh[J] += aKh[J][r] * khv;
             if constexpr (PC) wdG[((size_t)ci * C + i) * GK + ch] = part;
             else rowpart[r] += part;
         }
