@@ -1197,11 +1197,13 @@ __global__ __launch_bounds__(kThreads, IN_BF16 && !PC ? 2 : 1) void bwd_grads_b_
     __syncthreads();
     if (tid < GK) sdG[C - 1][tid] += wdG63[(size_t)ci * GK + tid];  // the chunk-end decay's extra
     // dbeta_j = sum_i dT''_ij T_ij; then dT = dT'' Diag(beta)
-    if (tid < C) {
-        const int j = tid;
+    {  // four lanes per column (every fourth row each), then a sum over the quad
+        const int j = tid >> 2, q = tid & 3;
         float s = 0.f;
-        for (int r = j; r < C; ++r) s += sX[r * LC + j] * sT[r * LC + j];
-        sdBeta[j] = s;
+        for (int r = j + q; r < C; r += 4) s += sX[r * LC + j] * sT[r * LC + j];
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        if (q == 0) sdBeta[j] = s;
     }
     __syncthreads();
     for (int idx = tid; idx < C * C; idx += kThreads) {
@@ -1244,11 +1246,13 @@ __global__ __launch_bounds__(kThreads, IN_BF16 && !PC ? 2 : 1) void bwd_grads_b_
     }
     __syncthreads();
     // dbeta_i += sum_{j<i} dR_ij M_ij;  dM_ij = beta_i dR_ij -> sD[j][i] (j < i)
-    if (tid < C) {
-        const int r = tid;
+    {  // four lanes per row, then a sum over the quad
+        const int r = tid >> 2, q = tid & 3;
         float s = 0.f;
-        for (int cc = 0; cc < r; ++cc) s += sX[r * LC + cc] * sY[r * LC + cc];
-        sdBeta[r] += s;
+        for (int cc = q; cc < r; cc += 4) s += sX[r * LC + cc] * sY[r * LC + cc];
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        if (q == 0) sdBeta[r] += s;
     }
     for (int idx = tid; idx < C * C; idx += kThreads) {
         const int r = idx / C, cc = idx % C;
@@ -1285,14 +1289,16 @@ __global__ __launch_bounds__(kThreads, IN_BF16 && !PC ? 2 : 1) void bwd_grads_b_
     }
     if constexpr (!PC) {
         // dG_i = rowsum_i(Z) - colsum_i(Z), Z = dM o M + dA o A (M in sY, A in sT)
-        if (tid < C) {
-            const int r = tid;
+        {  // four lanes per token r (every fourth term each), then a sum over the quad
+            const int r = tid >> 2, q = tid & 3;
             float s = 0.f;
-            for (int j = 0; j < r; ++j) s += sD[j * LC + r] * sY[r * LC + j];       // dM_rj M_rj
-            for (int j = 0; j <= r; ++j) s += sD[r * LC + j] * sT[r * LC + j];      // dA_rj A_rj
-            for (int i = r + 1; i < C; ++i) s -= sD[r * LC + i] * sY[i * LC + r];   // dM_ir M_ir
-            for (int i = r; i < C; ++i) s -= sD[i * LC + r] * sT[i * LC + r];       // dA_ir A_ir
-            sdG[r][0] += s;
+            for (int j = q; j < r; j += 4) s += sD[j * LC + r] * sY[r * LC + j];              // dM_rj M_rj
+            for (int j = q; j <= r; j += 4) s += sD[r * LC + j] * sT[r * LC + j];             // dA_rj A_rj
+            for (int i = r + 1 + q; i < C; i += 4) s -= sD[r * LC + i] * sY[i * LC + r];      // dM_ir M_ir
+            for (int i = r + q; i < C; i += 4) s -= sD[i * LC + r] * sT[i * LC + r];          // dA_ir A_ir
+            s += __shfl_xor(s, 1, 64);
+            s += __shfl_xor(s, 2, 64);
+            if (q == 0) sdG[r][0] += s;
         }
         __syncthreads();  // M, A no longer read
         // W1 = dM o P (region 0), W2 = scale dA o P (region 1), P_ij = exp(G_i - G_j), j <= i
@@ -1327,10 +1333,13 @@ __global__ __launch_bounds__(kThreads, IN_BF16 && !PC ? 2 : 1) void bwd_grads_b_
     }
     __syncthreads();
     if constexpr (KZ) {  // |k_i|^2
-        if (tid < C) {
+        {  // four lanes per token, then a sum over the quad
+            const int r = tid >> 2, q = tid & 3;
             float s = 0.f;
-            for (int cc = 0; cc < DK; ++cc) s += kv(tid, cc) * kv(tid, cc);
-            sKK[tid] = s;
+            for (int cc = q; cc < DK; cc += 4) s += kv(r, cc) * kv(r, cc);
+            s += __shfl_xor(s, 1, 64);
+            s += __shfl_xor(s, 2, 64);
+            if (q == 0) sKK[r] = s;
         }
         __syncthreads();
     }
@@ -1340,16 +1349,45 @@ __global__ __launch_bounds__(kThreads, IN_BF16 && !PC ? 2 : 1) void bwd_grads_b_
         f32x4 pk[JK], pq[JK];
 #pragma unroll
         for (int J = 0; J < JK; ++J) pk[J] = pq[J] = z4;
-        for (int kk = 0; kk < C; kk += 4) {
-            const float w1 = sT[(16 * w + lr) * LC + kk + lg], w1t = sT[(kk + lg) * LC + 16 * w + lr];
-            const float w2 = sX[(16 * w + lr) * LC + kk + lg], w2t = sX[(kk + lg) * LC + 16 * w + lr];
+        if constexpr (KQ16) {
+            // token j = 16 t + 4 lg + e in step (t, e): the four tokens of a lane group are one
+            // transposing read of the bf16 rows of k and q (rows 16 t + 4 lg + e, column 16 J + lr), and
+            // W1 + W1' is formed once per operand
 #pragma unroll
-            for (int J = 0; J < JK; ++J) {
-                const float kb = kv(kk + lg, 16 * J + lr), qb = qv(kk + lg, 16 * J + lr);
-                pk[J] = mfma4(w1, kb, pk[J]);
-                pk[J] = mfma4(w1t, kb, pk[J]);
-                pk[J] = mfma4(w2t, qb, pk[J]);
-                pq[J] = mfma4(w2, kb, pq[J]);
+            for (int t = 0; t < 4; ++t) {
+                float ak[4], aq[4], ad[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 16 * t + 4 * lg + e;
+                    ak[e] = sT[(16 * w + lr) * LC + j] + sT[j * LC + 16 * w + lr];  // W1 + W1'
+                    aq[e] = sX[j * LC + 16 * w + lr];                                 // W2'
+                    ad[e] = sX[(16 * w + lr) * LC + j];                               // W2
+                }
+#pragma unroll
+                for (int J = 0; J < JK; ++J) {
+                    const int at = (16 * t + 4 * lg + (lr >> 2)) * LQB + 16 * J + 4 * (lr & 3);
+                    const mx::bf16x4 k4 = mx::lds_read_tr(&sKb[at]);
+                    const mx::bf16x4 q4 = mx::lds_read_tr(&sQb[at]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float kb = static_cast<float>(k4[e]), qb = static_cast<float>(q4[e]);
+                        pk[J] = mfma4(ak[e], kb, pk[J]);
+                        pk[J] = mfma4(aq[e], qb, pk[J]);
+                        pq[J] = mfma4(ad[e], kb, pq[J]);
+                    }
+                }
+            }
+        } else {
+            for (int kk = 0; kk < C; kk += 4) {
+                const float w1 = sT[(16 * w + lr) * LC + kk + lg], w1t = sT[(kk + lg) * LC + 16 * w + lr];
+                const float w2 = sX[(16 * w + lr) * LC + kk + lg], w2t = sX[(kk + lg) * LC + 16 * w + lr];
+#pragma unroll
+                for (int J = 0; J < JK; ++J) {
+                    const float kb = kv(kk + lg, 16 * J + lr), qb = qv(kk + lg, 16 * J + lr);
+                    pk[J] = mfma4(w1 + w1t, kb, pk[J]);
+                    pk[J] = mfma4(w2t, qb, pk[J]);
+                    pq[J] = mfma4(w2, kb, pq[J]);
+                }
             }
         }
 #pragma unroll
@@ -1479,12 +1517,22 @@ __global__ __launch_bounds__(kThreads, IN_BF16 && !PC ? 2 : 1) void bwd_grads_b_
     }
     __syncthreads();
     // dg = reverse cumulative sum of dG over the chunk's tokens; dbeta (deta)
-    if (tid < GK) {
-        float run = 0.f;
-        for (int r = C - 1; r >= 0; --r) {
-            run += sdG[r][tid];
-            if (r < n) dg[(sl.row0 + (size_t)r * H) * GK + tid] = run;
+    if constexpr (PC) {  // one channel per thread
+        if (tid < GK) {
+            float run = 0.f;
+            for (int r = C - 1; r >= 0; --r) {
+                run += sdG[r][tid];
+                if (r < n) dg[(sl.row0 + (size_t)r * H) * GK + tid] = run;
+            }
         }
+    } else if (w == 0) {  // one token per lane: a suffix sum across the wavefront
+        float run = sdG[lane][0];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float up = __shfl_down(run, off, 64);
+            if (lane + off < 64) run += up;
+        }
+        if (lane < n) dg[sl.row0 + (size_t)lane * H] = run;
     }
     if (dbeta && tid < C && tid < n) {  // no beta without the delta rule
         float db = sdBeta[tid];
