@@ -320,12 +320,32 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
         }
     }
     __syncthreads();
-    if (tid < GK) {  // in-chunk inclusive cumulative sum, one channel per thread
-        float run = 0.f;
-        for (int i = 0; i < C; ++i) {
-            run += sG[i][tid];
-            sG[i][tid] = run;
+    __shared__ float sKn[KZ ? C : 1];  // |k_i|^2 (Kaczmarz step size)
+    if constexpr (KZ) {  // four lanes per token, then a sum over the quad
+        const int r = tid >> 2, q = tid & 3;
+        float sq = 0.f;
+        for (int cc = q; cc < DK; cc += 4) sq += sK[r][cc] * sK[r][cc];
+        sq += __shfl_xor(sq, 1, 64);
+        sq += __shfl_xor(sq, 2, 64);
+        if (q == 0) sKn[r] = sq;
+        barrier_lds();
+    }
+    if constexpr (PC) {  // in-chunk inclusive cumulative sum, one channel per thread
+        if (tid < GK) {
+            float run = 0.f;
+            for (int i = 0; i < C; ++i) {
+                run += sG[i][tid];
+                sG[i][tid] = run;
+            }
         }
+    } else if (w == 0) {  // one token per lane: an inclusive scan across the wavefront
+        float run = sG[lane][0];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float up = __shfl_up(run, off, 64);
+            if (lane >= off) run += up;
+        }
+        sG[lane][0] = run;
     }
     if (tid >= kThreads - C) {
         const int i = tid - (kThreads - C);
@@ -335,9 +355,7 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
         } else if (i < n) {
             const float given = beta[sl.row0 + (size_t)i * H];
             if constexpr (KZ) {
-                float kk = 0.f;
-                for (int cc = 0; cc < DK; ++cc) kk += sK[i][cc] * sK[i][cc];
-                bv = given / (kk + eps);
+                bv = given / (sKn[i] + eps);
             } else {
                 bv = given;
             }
@@ -1100,12 +1118,14 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
         if constexpr (PC) wdG63[(size_t)ci * GK + tid] = extra;
         else sH[0][tid] = extra;
     }
-    if constexpr (!PC) {
+    if constexpr (!PC) {  // the sum over channels, on one wavefront
         __syncthreads();
-        if (tid == 0) {
+        if (w == 0) {
             float s = 0.f;
-            for (int cc = 0; cc < DK; ++cc) s += sH[0][cc];
-            wdG63[ci] = s;
+            for (int cc = lane; cc < DK; cc += 64) s += sH[0][cc];
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+            if (lane == 0) wdG63[ci] = s;
         }
     }
 }
