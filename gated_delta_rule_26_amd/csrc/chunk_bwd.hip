@@ -223,6 +223,34 @@ __device__ __forceinline__ void dma_rows(const float *src, float *dst, int w, in
     }
 }
 
+// Swizzled fp32 matrices in LDS, rows of NCOL values (no padding): the
+// 16-byte piece q of row r sits at piece q ^ (r % 16).  A float4 read of the
+// same four columns of 16 consecutive rows, and a one-value read of four rows
+// 4 apart by 16 consecutive columns, then fall in distinct banks, and the rows
+// stay contiguous, so 1 KiB global-to-LDS copies fill them.
+template <int NCOL>
+__device__ __forceinline__ int lds_swz(int r, int col) {
+    return r * NCOL + ((((col >> 2) ^ (r & 15))) << 2) + (col & 3);
+}
+// Copy instructions per wavefront for one C x NCOL matrix.
+template <int NCOL>
+constexpr int swz_copies() { return C * NCOL * 4 / 1024 / 4; }
+// A C x NCOL fp32 matrix (row-major, in global memory) into LDS in the
+// swizzled layout: 1 KiB per copy instruction (lane l moves the 16 bytes that
+// belong at piece l of it), instructions w, w + 4, .. on wavefront w.
+template <int NCOL>
+__device__ __forceinline__ void dma_swz(const float *src, float *dst, int w, int lane) {
+    constexpr int RPI = 1024 / (NCOL * 4);  // rows per instruction
+    constexpr int SPR = NCOL / 4;           // 16-byte pieces per row
+    static_assert(SPR >= 16 && C % RPI == 0, "the swizzle needs at least 16 pieces per row");
+    const int rr = lane / SPR, q = lane % SPR;
+#pragma unroll
+    for (int i = 0; i < C / RPI / 4; ++i) {
+        const int ins = 4 * i + w, row = ins * RPI + rr;
+        mx::lds_dma16(src + row * NCOL + 4 * (q ^ (row & 15)), mx::lds_addr(dst + ins * 256));
+    }
+}
+
 // LDS row strides (floats) of the fp32-tile forward walk.  A
 // row-indexed-by-lane read (rows lr, columns lg) is free of bank conflicts at
 // a stride of 2 mod 32, a column-indexed one (rows lg, columns lr) at 16 mod
@@ -503,12 +531,14 @@ __device__ __forceinline__ float gval(const float (*sG)[GK], int i, int cc) {
 //   E = T (beta X)                   (= T'' X; both wavefronts of the pair)
 //   S_h <- Diag(gam_h) S_h + K^[:, half h]' E.
 // The A operands come from LDS: rows of K~ and T as float4 (four steps of one
-// lane group), columns of K^ one value per step.  The operands move from the
-// workspace to LDS by global-to-LDS copies (no registers), each buffer refilled
-// for the next chunk as soon as this chunk is done with it: K~ after the
-// exchange barrier, T, K^, beta and G_63 after the chunk's last barrier; each
-// barrier first waits for the copies issued before the previous one.  Only v
-// goes through registers, one chunk ahead.
+// lane group), columns of K^ one value per step, in the swizzled layout of
+// lds_swz.  The operands move from the workspace to LDS by 1 KiB
+// global-to-LDS copies (no registers): K~, T, beta and G_63 of the next chunk
+// into the other half of double buffers at the start of a chunk, K^ of this
+// chunk into its single buffer at the same time (used last, in the update).
+// Per chunk three barriers: the pair exchange; before the update, after this
+// chunk's K^ has landed; at the end, after the next chunk's operands have.
+// Only v goes through registers, one chunk ahead.
 template <int DK, int DV, bool PC, bool IN_BF16>
 __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__restrict__ v, int T, int H, int NC,
                                                               const float *__restrict__ wT,
@@ -521,9 +551,8 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
     constexpr int GK = PC ? DK : 1;
     constexpr int NT = DV / kBV;
     constexpr int HK = DK / 2, NTH = HK / 16;  // channels per wavefront of a pair, their 16-blocks
-    constexpr int LKR = DK + 8;                // K~: rows read as float4
-    constexpr int LKC = DK + 4;                // K^: columns read one value per lane
-    constexpr int LTR = C + 8;                 // T: rows read as float4
+    // copy instructions per wavefront issued after K^'s: K~ and T of the next chunk and one small copy
+    constexpr int kAfterKh = swz_copies<DK>() + swz_copies<C>() + 1;
     // XCD-aware placement: the value slices of one (sequence, head) share an XCD, so its L2 serves the
     // chunk operands they all read
     int bh, tile;
@@ -536,23 +565,23 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
     const int p = w >> 1, h = w & 1;
     const int jc = j0 + 16 * p + lr;  // this lane's value column
     const int kh0 = h * HK;           // first key channel of this wavefront's half
-    __shared__ float sKt[C * LKR];
-    __shared__ float sKh[C * LKC];
-    __shared__ float sT[C * LTR];
-    __shared__ float sB[C];            // beta of the chunk's tokens
-    __shared__ float sG[DK];           // G_63 per channel (scalar decay: the one value, repeated)
-    __shared__ f32x4 sP[2][2][4][64];  // per pair and half: the partial K~ S tiles
+    __shared__ __align__(16) float sKt[2][C * DK];
+    __shared__ __align__(16) float sT[2][C * C];
+    __shared__ __align__(16) float sKh[C * DK];
+    __shared__ __align__(16) float sB[2][C];    // beta of the chunk's tokens
+    __shared__ __align__(16) float sG[2][DK];   // G_63 per channel (scalar decay: the one value, repeated)
+    __shared__ f32x4 sP[2][2][4][64];           // per pair and half: the partial K~ S tiles
 
-    auto copy_kt = [&](size_t ci) __attribute__((always_inline)) {
-        dma_rows<DK, LKR>(wKt + ci * C * DK, sKt, w, lane);
-    };
-    auto copy_rest = [&](size_t ci) __attribute__((always_inline)) {
-        dma_rows<C, LTR>(wT + ci * C * C, sT, w, lane);
-        dma_rows<DK, LKC>(wKh + ci * C * DK, sKh, w, lane);
-        if (w == 0) mx::lds_dma4(wB + ci * C + lane, mx::lds_addr(sB));
-        if (w >= 1 && w <= DK / 64)
+    // the next chunk's K~, T, beta and G_63 into buffer `b` (one small copy per wavefront: beta on
+    // wavefronts 0 and 3, G_63 in 64-channel pieces on 1 and 2, beta again when there is one piece)
+    auto copy_next = [&](size_t ci, int b) __attribute__((always_inline)) {
+        dma_swz<DK>(wKt + ci * C * DK, sKt[b], w, lane);
+        dma_swz<C>(wT + ci * C * C, sT[b], w, lane);
+        if (w == 1 || (w == 2 && DK > 64))
             mx::lds_dma4(wG + ci * C * GK + (size_t)(C - 1) * GK + (PC ? 64 * (w - 1) + lane : 0),
-                         mx::lds_addr(sG + 64 * (w - 1)));
+                         mx::lds_addr(sG[b] + 64 * (w - 1)));
+        else
+            mx::lds_dma4(wB + ci * C + lane, mx::lds_addr(sB[b]));
     };
     f32x4 gV[4];  // v of a chunk: rows 16 M + 4 lg + r, column jc
     auto load_v = [&](int c) __attribute__((always_inline)) {
@@ -573,73 +602,78 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
 #pragma unroll
         for (int e = 0; e < 4; ++e) sv[t][e] = s0 ? s0[sbase + (size_t)(kh0 + 16 * t + 4 * lg + e) * DV + jc] : 0.f;
     if (wk.nc <= 0) return;
-    {
-        const size_t c0 = uniform(wk.slot(0));
-        copy_kt(c0);
-        copy_rest(c0);
-        load_v(0);
-        barrier_vm<0>();
-    }
+    copy_next(uniform(wk.slot(0)), 0);
+    load_v(0);
+    barrier_vm<0>();
     for (int c = 0; c < wk.nc; ++c) {
+        const int b = c & 1;
         const size_t ci = uniform(wk.slot(c));
         const bool more = c + 1 < wk.nc;
         const size_t cn = uniform(wk.slot(more ? c + 1 : c));
+        const f32x4 vv[4] = {gV[0], gV[1], gV[2], gV[3]};
         // the state entering this chunk, to the workspace
         float *Sg = wS + ci * DK * DV;
 #pragma unroll
         for (int t = 0; t < NTH; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) Sg[(size_t)(kh0 + 16 * t + 4 * lg + e) * DV + jc] = sv[t][e];
+        load_v(more ? c + 1 : c);
+        dma_swz<DK>(wKh + ci * C * DK, sKh, w, lane);  // this chunk's K^ (its buffer's last reader was the previous update)
+        if (more) copy_next(cn, b ^ 1);
         // P_h = K~[:, half h] S_h (X = V without the delta rule)
+        const float *kt = sKt[b];
         f32x4 pp[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         if (delta) {
 #pragma unroll
             for (int t = 0; t < NTH; ++t)
 #pragma unroll
                 for (int M = 0; M < 4; ++M) {
-                    const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&sKt[(16 * M + lr) * LKR + kh0 + 16 * t + 4 * lg]);
+                    const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&kt[lds_swz<DK>(16 * M + lr, kh0 + 16 * t + 4 * lg)]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) pp[M] = mfma4(a4[e], sv[t][e], pp[M]);
                 }
         }
 #pragma unroll
         for (int M = 0; M < 4; ++M) sP[p][h][M][lane] = pp[M];
-        barrier_vm<0>();  // partial tiles; this chunk's T, K^, beta, G_63 have landed; K~ is free
+        barrier_lds();  // both partial tiles of each pair
         f32x4 x[4];
 #pragma unroll
-        for (int M = 0; M < 4; ++M) x[M] = gV[M] - (pp[M] + sP[p][h ^ 1][M][lane]);  // the same sum in both
-        if (more) copy_kt(cn);
-        load_v(more ? c + 1 : c);  // the last 16 loads: the barrier below may leave them in flight
+        for (int M = 0; M < 4; ++M) x[M] = vv[M] - (pp[M] + sP[p][h ^ 1][M][lane]);  // the same sum in both
         // E = T (beta X) (T lower triangular)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) x[t] *= *reinterpret_cast<const f32x4 *>(&sB[16 * t + 4 * lg]);
+        for (int t = 0; t < 4; ++t) x[t] *= *reinterpret_cast<const f32x4 *>(&sB[b][16 * t + 4 * lg]);
+        const float *tt = sT[b];
         f32x4 e4[4];
 #pragma unroll
         for (int M = 0; M < 4; ++M) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int t = 0; t <= M; ++t) {
-                const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&sT[(16 * M + lr) * LTR + 16 * t + 4 * lg]);
+                const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&tt[lds_swz<C>(16 * M + lr, 16 * t + 4 * lg)]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc = mfma4(a4[e], x[t][e], acc);
             }
             e4[M] = acc;
         }
+        // this chunk's K^ has landed (the next chunk's copies, issued after it, may still be in flight)
+        if (more) barrier_vm<kAfterKh>();
+        else barrier_vm<0>();
         // S_h <- Diag(gam) S_h + K^[:, half h]' E
 #pragma unroll
         for (int J = 0; J < NTH; ++J) {
             f32x4 acc;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = __expf(sG[PC ? kh0 + 16 * J + 4 * lg + e : 0]) * sv[J][e];
+            for (int e = 0; e < 4; ++e) acc[e] = __expf(sG[b][PC ? kh0 + 16 * J + 4 * lg + e : 0]) * sv[J][e];
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    acc = mfma4(sKh[(16 * t + 4 * lg + e) * LKC + kh0 + 16 * J + lr], e4[t][e], acc);
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * t + 4 * lg + e;
+                    acc = mfma4(sKh[lds_swz<DK>(row, kh0 + 16 * J + lr)], e4[t][e], acc);
+                }
             sv[J] = acc;
         }
-        barrier_vm<16>();  // the next chunk's K~ has landed; T, K^, beta, G_63 are free
-        if (more) copy_rest(cn);
+        barrier_vm<0>();  // the next chunk's K~, T, beta, G_63 have landed; K^ is free
     }
 }
 
