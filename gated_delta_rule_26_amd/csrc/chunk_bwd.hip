@@ -850,6 +850,209 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
     }
 }
 
+// ---- reverse walk, scalar decay with bf16 q and k
+// The reverse walk above for scalar decay and bf16 inputs.  There
+// K~ = exp(G) k, K^ = exp(G_63 - G) k and Q~ = scale exp(G) q are k and q
+// scaled per token, so the walk stages the chunk's bf16 k and q (exact) and
+// applies the token factors to the other operand of each product or to its
+// result:
+//   P_h = k[:, half h] dS'_h,   dE = exp(G_63 - G) (P_0 + P_1) + A' dO,
+//   dX = Diag(beta) T' dE,
+//   dS_h = gam dS'_h + q[:, half h]' (scale exp(G) dO) - k[:, half h]' (exp(G) dX).
+// Rows of k are read as 8-byte pieces (a lane group's four bf16), columns of
+// q and k by transposing reads (tokens 16 t + 4 lg + e of one column in one
+// read).  With bf16 k and q every operand of the previous chunk fits a second
+// buffer, so it is staged while this chunk is processed: A, T, G and beta by
+// global-to-LDS copies, k and q through registers, dO through registers.
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void bwd_dstates_kq16_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const float *__restrict__ dO, int T, int H, int NC,
+    float scale, const float *__restrict__ wT, const float *__restrict__ wA, const float *__restrict__ wG,
+    const float *__restrict__ wB, const float *__restrict__ ds_final, float *__restrict__ wdS,
+    float *__restrict__ ds0, bool delta, SeqTable tb) {
+    constexpr int NT = DV / kBV;
+    constexpr int HK = DK / 2, NTH = HK / 16;
+    constexpr int LKB = DK + 16;                // bf16 row stride of k and q (rows 8 banks apart)
+    constexpr int LTC = C + 4;                  // A, T: columns read one value per lane
+    constexpr int NKQ = C * DK / 8 / kThreads;  // 16-byte pieces per thread of the chunk's k (and of q)
+    // XCD-aware placement: the value slices of one (sequence, head) share an XCD, so its L2 serves the
+    // chunk operands they all read
+    int bh, tile;
+    state_slot(blockIdx.x, gridDim.x / NT, NT, bh, tile);
+    bh = walk_seq(bh, H, tb);  // packed batches: longest sequences first
+    const BwdWalk wk = bwd_walk(bh, T, H, NC, tb);
+    const int j0 = tile * kBV;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int p = w >> 1, h = w & 1;
+    const int jc = j0 + 16 * p + lr;
+    const int kh0 = h * HK;
+    __shared__ __align__(16) __bf16 sK[2][C * LKB];
+    __shared__ __align__(16) __bf16 sQ[2][C * LKB];
+    __shared__ float sA[2][C * LTC];
+    __shared__ float sT[2][C * LTC];
+    __shared__ __align__(16) float sGc[2][C];  // in-chunk cumulative log-decay per token
+    __shared__ __align__(16) float sB[2][C];   // beta
+    __shared__ f32x4 sP[2][2][4][64];          // per pair and half: the partial k dS' tiles
+
+    auto copy_at = [&](size_t ci, int b) __attribute__((always_inline)) {  // A, T, G, beta into buffer b
+        dma_rows<C, LTC>(wA + ci * C * C, sA[b], w, lane);
+        dma_rows<C, LTC>(wT + ci * C * C, sT[b], w, lane);
+        if (w == 0) mx::lds_dma4(wG + ci * C + lane, mx::lds_addr(sGc[b]));
+        else if (w == 1) mx::lds_dma4(wB + ci * C + lane, mx::lds_addr(sB[b]));
+    };
+    uint4 gk[NKQ], gq[NKQ];  // a chunk's k and q, this thread's 16-byte pieces
+    auto load_kq = [&](int c) __attribute__((always_inline)) {
+        const int n = uniform(wk.count(c));
+        const size_t row0 = uniform(wk.row0(c));
+        const auto rk = rows_rsrc(k + row0 * DK, n, H * DK * 2, DK * 2);
+        const auto rq = rows_rsrc(q + row0 * DK, n, H * DK * 2, DK * 2);
+#pragma unroll
+        for (int u = 0; u < NKQ; ++u) {
+            const int idx = tid + u * kThreads, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
+            gk[u] = mx::buf_ld16(rk, (r * H * DK + c8) * 2);
+            gq[u] = mx::buf_ld16(rq, (r * H * DK + c8) * 2);
+        }
+    };
+    auto store_kq = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < NKQ; ++u) {
+            const int idx = tid + u * kThreads, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
+            *reinterpret_cast<uint4 *>(&sK[b][r * LKB + c8]) = gk[u];
+            *reinterpret_cast<uint4 *>(&sQ[b][r * LKB + c8]) = gq[u];
+        }
+    };
+    f32x4 gO[4];  // dO of a chunk: rows 16 t + 4 lg + e, column jc
+    auto load_do = [&](int c) __attribute__((always_inline)) {
+        const int n = uniform(wk.count(c));
+        const size_t row0 = uniform(wk.row0(c));
+        const auto ro = rows_rsrc(dO + row0 * DV, n, H * DV * 4, DV * 4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gO[t][e] = buf_in<false>(ro, (16 * t + 4 * lg + e) * H * DV + jc);
+    };
+    auto bf16lo = [](unsigned x) { return __uint_as_float(x << 16); };
+    auto bf16hi = [](unsigned x) { return __uint_as_float(x & 0xffff0000u); };
+
+    const size_t sbase = (size_t)bh * DK * DV;
+    f32x4 dsv[NTH];  // dS'[kh0 + 16 t + 4 lg + e][jc]
+#pragma unroll
+    for (int t = 0; t < NTH; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            dsv[t][e] = ds_final ? ds_final[sbase + (size_t)(kh0 + 16 * t + 4 * lg + e) * DV + jc] : 0.f;
+    if (wk.nc > 0) {
+        const int cl = wk.nc - 1;
+        copy_at(uniform(wk.slot(cl)), cl & 1);
+        load_kq(cl);
+        load_do(cl);
+        store_kq(cl & 1);
+        barrier_vm<0>();
+    }
+    for (int c = wk.nc - 1; c >= 0; --c) {
+        const int b = c & 1, nb = b ^ 1;
+        const size_t ci = uniform(wk.slot(c));
+        const bool more = c > 0;
+        const size_t cn = uniform(wk.slot(more ? c - 1 : c));
+        const f32x4 ov[4] = {gO[0], gO[1], gO[2], gO[3]};  // this chunk's dO (loaded a chunk ago)
+        // dS' of this chunk to the workspace
+        float *dSg = wdS + ci * DK * DV;
+#pragma unroll
+        for (int t = 0; t < NTH; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dSg[(size_t)(kh0 + 16 * t + 4 * lg + e) * DV + jc] = dsv[t][e];
+        // the previous chunk's operands (buffer nb was last read in the iteration before this one)
+        if (more) copy_at(cn, nb);
+        load_kq(more ? c - 1 : c);
+        load_do(more ? c - 1 : c);
+        // P_h = k[:, half h] dS'_h
+        const __bf16 *kb = sK[b];
+        f32x4 pp[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int t = 0; t < NTH; ++t)
+#pragma unroll
+            for (int M = 0; M < 4; ++M) {
+                const uint2 raw = *reinterpret_cast<const uint2 *>(&kb[(16 * M + lr) * LKB + kh0 + 16 * t + 4 * lg]);
+                const float a4[4] = {bf16lo(raw.x), bf16hi(raw.x), bf16lo(raw.y), bf16hi(raw.y)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pp[M] = mfma4(a4[e], dsv[t][e], pp[M]);
+            }
+#pragma unroll
+        for (int M = 0; M < 4; ++M) sP[p][h][M][lane] = pp[M];
+        barrier_lds();  // both partial tiles of each pair
+        // token factors of this lane's rows 16 M + 4 lg + r: exp(G) and exp(G_63 - G)
+        const float gend = sGc[b][C - 1];
+        f32x4 fe[4], fh[4];
+#pragma unroll
+        for (int M = 0; M < 4; ++M) {
+            const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&sGc[b][16 * M + 4 * lg]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                fe[M][r] = __expf(g4[r]);
+                fh[M][r] = __expf(gend - g4[r]);
+            }
+        }
+        // dE = exp(G_63 - G) (P_0 + P_1) + A' dO (A' upper triangular: blocks t >= M)
+        f32x4 de[4];
+#pragma unroll
+        for (int M = 0; M < 4; ++M) {
+            f32x4 acc = fh[M] * (pp[M] + sP[p][h ^ 1][M][lane]);  // the same in both
+#pragma unroll
+            for (int t = M; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc = mfma4(sA[b][(16 * t + 4 * lg + e) * LTC + 16 * M + lr], ov[t][e], acc);
+            de[M] = acc;
+        }
+        // dX = Diag(beta) T' dE (T' upper triangular)
+        f32x4 dx[4];
+#pragma unroll
+        for (int M = 0; M < 4; ++M) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = M; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc = mfma4(sT[b][(16 * t + 4 * lg + e) * LTC + 16 * M + lr], de[t][e], acc);
+            dx[M] = acc * *reinterpret_cast<const f32x4 *>(&sB[b][16 * M + 4 * lg]);
+        }
+        // dS_h = gam dS'_h + q[:, half h]' (scale exp(G) dO) - k[:, half h]' (exp(G) dX) (no k term without
+        // the delta rule: X does not depend on S then)
+        f32x4 os[4], xs[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            os[t] = scale * fe[t] * ov[t];
+            xs[t] = -(fe[t] * dx[t]);
+        }
+        const float gam = __expf(gend);
+        const __bf16 *qb = sQ[b];
+#pragma unroll
+        for (int J = 0; J < NTH; ++J) {
+            f32x4 acc = gam * dsv[J];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int at = (16 * t + 4 * lg + (lr >> 2)) * LKB + kh0 + 16 * J + 4 * (lr & 3);
+                const mx::bf16x4 q4 = mx::lds_read_tr(&qb[at]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc = mfma4(static_cast<float>(q4[e]), os[t][e], acc);
+                if (delta) {
+                    const mx::bf16x4 k4 = mx::lds_read_tr(&kb[at]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc = mfma4(static_cast<float>(k4[e]), xs[t][e], acc);
+                }
+            }
+            dsv[J] = acc;
+        }
+        store_kq(nb);      // the previous chunk's k and q (the compiler waits for their loads)
+        barrier_vm<16>();  // its A, T, G, beta copies and k, q have landed (its dO may still be in flight)
+    }
+    if (ds0) {
+#pragma unroll
+        for (int t = 0; t < NTH; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ds0[sbase + (size_t)(kh0 + 16 * t + 4 * lg + e) * DV + jc] = dsv[t][e];
+    }
+}
+
 // ============================================================ grads A: products over the value axis
 // One workgroup per chunk, four wavefronts; wavefront w owns rows 16w .. 16w+15
 // of every C-row product.  Over the value axis in slices of 16 columns:
@@ -1791,8 +1994,13 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
     hipLaunchKernelGGL((bwd_states_kernel<DK, DV, PC, IB>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.v, a.T, a.H,
                        a.NC, w.T, w.G, w.beta, w.Kt, w.Kh, a.s0, w.S, a.delta, a.tab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dstates_kernel<DK, DV, PC>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.dO, a.T, a.H,
-                       a.NC, w.T, w.A, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.ds_final, w.dS, a.ds0, a.delta, a.tab);
+    if constexpr (!PC && IB)  // scalar decay with bf16 inputs: the walk on k and q themselves
+        hipLaunchKernelGGL((bwd_dstates_kq16_kernel<DK, DV>), dim3(nwalk), dim3(kThreads), 0, a.stream,
+                           static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), a.dO, a.T, a.H, a.NC,
+                           a.scale, w.T, w.A, w.G, w.beta, a.ds_final, w.dS, a.ds0, a.delta, a.tab);
+    else
+        hipLaunchKernelGGL((bwd_dstates_kernel<DK, DV, PC>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.dO, a.T,
+                           a.H, a.NC, w.T, w.A, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.ds_final, w.dS, a.ds0, a.delta, a.tab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grads_a_kernel<DK, DV, PC, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.v, a.dO, a.T,
                        a.H, a.NC, a.scale, w.T, w.A, w.G, w.beta, w.S, w.dS, w.Kt, w.Kh, w.Qt, w.dA, w.dTT, w.dG,
