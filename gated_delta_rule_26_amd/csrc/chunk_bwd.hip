@@ -60,11 +60,16 @@ struct BwdWs {
     float *S, *dS;                 // DK x DV: entering state; gradient of the chunk-end state
     float *dA, *dTT, *dG;          // C x C (two), C x GK
     float *dG63;                   // GK: the chunk-end decay's extra gradient (K^ and gam)
-    float *Kt, *Kh, *Qt;           // C x DK each: K~, K^, Q~ (decayed operands, fp32)
+    float *Kt, *Kh, *Qt;           // C x DK each: K~, K^, Q~ (decayed operands, fp32), or null
 };
 
+// Whether the decayed operands are stored: not for scalar decay with bf16
+// inputs, whose kernels form them from k and q (exact in bf16) and the token
+// factors where they use them.
+constexpr bool bwd_stores_ops(bool per_channel, bool qkv_bf16) { return per_channel || !qkv_bf16; }
+
 template <int DK, int DV, bool PC>
-BwdWs carve_bwd(void *ws, size_t slots) {
+BwdWs carve_bwd(void *ws, size_t slots, bool ops) {
     constexpr int GK = PC ? DK : 1;
     float *p = static_cast<float *>(ws);
     BwdWs w;
@@ -79,17 +84,20 @@ BwdWs carve_bwd(void *ws, size_t slots) {
     w.dTT = p; p += slots * C * C;
     w.dG = p; p += slots * C * GK;
     w.dG63 = p; p += slots * GK;
-    w.Kt = p; p += slots * C * DK;
-    w.Kh = p; p += slots * C * DK;
-    w.Qt = p;
+    w.Kt = w.Kh = w.Qt = nullptr;
+    if (ops) {
+        w.Kt = p; p += slots * C * DK;
+        w.Kh = p; p += slots * C * DK;
+        w.Qt = p;
+    }
     return w;
 }
 
 template <int DK, int DV, bool PC>
-size_t bwd_bytes(size_t slots) {
+size_t bwd_bytes(size_t slots, bool ops) {
     constexpr int GK = PC ? DK : 1;
     return slots * sizeof(float) *
-           ((size_t)5 * C * C + 2 * (size_t)C * GK + GK + C + 2 * (size_t)DK * DV + 3 * (size_t)C * DK);
+           ((size_t)5 * C * C + 2 * (size_t)C * GK + GK + C + 2 * (size_t)DK * DV + (ops ? 3 * (size_t)C * DK : 0));
 }
 
 // chunk slot ci -> token row of its token 0 and token count.  Fixed-length
@@ -462,8 +470,8 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
     for (int idx = tid; idx < C * GK; idx += kThreads) wG[(size_t)ci * C * GK + idx] = sG[idx / GK][idx % GK];
     if (tid < C) wB[(size_t)ci * C + tid] = sBeta[tid];
     // the decayed operands: K~ = exp(G) k, K^ = exp(G_63 - G) k, Q~ = scale exp(G) q (four channels
-    // per thread and step, 16-byte stores)
-    for (int idx4 = tid; idx4 < C * DK / 4; idx4 += kThreads) {
+    // per thread and step, 16-byte stores), when the caller keeps them
+    for (int idx4 = tid; wKt && idx4 < C * DK / 4; idx4 += kThreads) {
         const int i = idx4 / (DK / 4), c0 = (idx4 % (DK / 4)) * 4;
         f32x4 kt, kh, qt;
 #pragma unroll
@@ -674,6 +682,176 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
             sv[J] = acc;
         }
         barrier_vm<0>();  // the next chunk's K~, T, beta, G_63 have landed; K^ is free
+    }
+}
+
+// ---- forward walk, scalar decay with bf16 q and k
+// The forward walk above for scalar decay and bf16 inputs: K~ = exp(G) k and
+// K^ = exp(G_63 - G) k are k scaled per token, so the walk stages the chunk's
+// bf16 k (exact) and applies the token factors to the product's result or to
+// the other operand:
+//   P_h = k[:, half h] S_h,   X = V - exp(G) (P_0 + P_1),   E = T (beta X),
+//   S_h <- gam S_h + k[:, half h]' (exp(G_63 - G) E).
+// Rows of k are read as 8-byte pieces, its columns by transposing reads.
+// Every operand of the next chunk is staged while this chunk is processed
+// (double buffers): T, G and beta by global-to-LDS copies, k and v through
+// registers.  (With the decayed operands in the workspace the fp32 walk above
+// is faster, 380 against 396 us on the GDN workload; this one runs when they
+// are not stored.)
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void bwd_states_kq16_kernel(const __bf16 *__restrict__ v,
+                                                                   const __bf16 *__restrict__ k, int T, int H, int NC,
+                                                                   const float *__restrict__ wT,
+                                                                   const float *__restrict__ wG,
+                                                                   const float *__restrict__ wB,
+                                                                   const float *__restrict__ s0, float *__restrict__ wS,
+                                                                   bool delta, SeqTable tb) {
+    constexpr int NT = DV / kBV;
+    constexpr int HK = DK / 2, NTH = HK / 16;
+    constexpr int LKB = DK + 16;                // bf16 row stride of k (rows 8 banks apart)
+    constexpr int LTR = C + 8;                  // T: rows read as float4
+    constexpr int NKQ = C * DK / 8 / kThreads;  // 16-byte pieces per thread of the chunk's k
+    // XCD-aware placement: the value slices of one (sequence, head) share an XCD, so its L2 serves the
+    // chunk operands they all read
+    int bh, tile;
+    state_slot(blockIdx.x, gridDim.x / NT, NT, bh, tile);
+    bh = walk_seq(bh, H, tb);  // packed batches: longest sequences first
+    const BwdWalk wk = bwd_walk(bh, T, H, NC, tb);
+    const int j0 = tile * kBV;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int p = w >> 1, h = w & 1;
+    const int jc = j0 + 16 * p + lr;
+    const int kh0 = h * HK;
+    __shared__ __align__(16) __bf16 sK[2][C * LKB];
+    __shared__ __align__(16) float sT[2][C * LTR];
+    __shared__ __align__(16) float sGc[2][C];  // in-chunk cumulative log-decay per token
+    __shared__ __align__(16) float sB[2][C];   // beta
+    __shared__ f32x4 sP[2][2][4][64];          // per pair and half: the partial k S tiles
+
+    auto copy_at = [&](size_t ci, int b) __attribute__((always_inline)) {  // T, G, beta into buffer b
+        dma_rows<C, LTR>(wT + ci * C * C, sT[b], w, lane);
+        if (w == 0) mx::lds_dma4(wG + ci * C + lane, mx::lds_addr(sGc[b]));
+        else if (w == 1) mx::lds_dma4(wB + ci * C + lane, mx::lds_addr(sB[b]));
+    };
+    uint4 gk[NKQ];  // a chunk's k, this thread's 16-byte pieces
+    f32x4 gV[4];    // v of a chunk: rows 16 M + 4 lg + r, column jc
+    auto load_kv = [&](int c) __attribute__((always_inline)) {
+        const int n = uniform(wk.count(c));
+        const size_t row0 = uniform(wk.row0(c));
+        const auto rk = rows_rsrc(k + row0 * DK, n, H * DK * 2, DK * 2);
+#pragma unroll
+        for (int u = 0; u < NKQ; ++u) {
+            const int idx = tid + u * kThreads, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
+            gk[u] = mx::buf_ld16(rk, (r * H * DK + c8) * 2);
+        }
+        const auto rv = rows_rsrc(v + row0 * DV, n, H * DV * 2, DV * 2);
+#pragma unroll
+        for (int M = 0; M < 4; ++M)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gV[M][r] = buf_in<true>(rv, (16 * M + 4 * lg + r) * H * DV + jc);
+    };
+    auto store_k = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < NKQ; ++u) {
+            const int idx = tid + u * kThreads, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
+            *reinterpret_cast<uint4 *>(&sK[b][r * LKB + c8]) = gk[u];
+        }
+    };
+    auto bf16lo = [](unsigned x) { return __uint_as_float(x << 16); };
+    auto bf16hi = [](unsigned x) { return __uint_as_float(x & 0xffff0000u); };
+
+    const size_t sbase = (size_t)bh * DK * DV;
+    f32x4 sv[NTH];  // S[kh0 + 16 t + 4 lg + e][jc]
+#pragma unroll
+    for (int t = 0; t < NTH; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[t][e] = s0 ? s0[sbase + (size_t)(kh0 + 16 * t + 4 * lg + e) * DV + jc] : 0.f;
+    if (wk.nc <= 0) return;
+    copy_at(uniform(wk.slot(0)), 0);
+    load_kv(0);
+    store_k(0);
+    barrier_vm<0>();
+    for (int c = 0; c < wk.nc; ++c) {
+        const int b = c & 1, nb = b ^ 1;
+        const size_t ci = uniform(wk.slot(c));
+        const bool more = c + 1 < wk.nc;
+        const size_t cn = uniform(wk.slot(more ? c + 1 : c));
+        const f32x4 vv[4] = {gV[0], gV[1], gV[2], gV[3]};  // this chunk's v (loaded a chunk ago)
+        // the state entering this chunk, to the workspace
+        float *Sg = wS + ci * DK * DV;
+#pragma unroll
+        for (int t = 0; t < NTH; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Sg[(size_t)(kh0 + 16 * t + 4 * lg + e) * DV + jc] = sv[t][e];
+        // the next chunk's operands (buffer nb was last read in the iteration before this one)
+        if (more) copy_at(cn, nb);
+        load_kv(more ? c + 1 : c);
+        // P_h = k[:, half h] S_h
+        const __bf16 *kb = sK[b];
+        f32x4 pp[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        if (delta) {
+#pragma unroll
+            for (int t = 0; t < NTH; ++t)
+#pragma unroll
+                for (int M = 0; M < 4; ++M) {
+                    const uint2 raw = *reinterpret_cast<const uint2 *>(&kb[(16 * M + lr) * LKB + kh0 + 16 * t + 4 * lg]);
+                    const float a4[4] = {bf16lo(raw.x), bf16hi(raw.x), bf16lo(raw.y), bf16hi(raw.y)};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pp[M] = mfma4(a4[e], sv[t][e], pp[M]);
+                }
+        }
+#pragma unroll
+        for (int M = 0; M < 4; ++M) sP[p][h][M][lane] = pp[M];
+        barrier_lds();  // both partial tiles of each pair
+        // token factors of this lane's rows 16 M + 4 lg + r: exp(G) and exp(G_63 - G)
+        const float gend = sGc[b][C - 1];
+        f32x4 fe[4], fh[4];
+#pragma unroll
+        for (int M = 0; M < 4; ++M) {
+            const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&sGc[b][16 * M + 4 * lg]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                fe[M][r] = __expf(g4[r]);
+                fh[M][r] = __expf(gend - g4[r]);
+            }
+        }
+        // X = V - exp(G) (P_0 + P_1), then beta X
+        f32x4 x[4];
+#pragma unroll
+        for (int M = 0; M < 4; ++M)
+            x[M] = (vv[M] - fe[M] * (pp[M] + sP[p][h ^ 1][M][lane])) *
+                   *reinterpret_cast<const f32x4 *>(&sB[b][16 * M + 4 * lg]);  // the same in both
+        // E = T (beta X) (T lower triangular), then exp(G_63 - G) E for the update
+        const float *tt = sT[b];
+        f32x4 es[4];
+#pragma unroll
+        for (int M = 0; M < 4; ++M) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t <= M; ++t) {
+                const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&tt[(16 * M + lr) * LTR + 16 * t + 4 * lg]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc = mfma4(a4[e], x[t][e], acc);
+            }
+            es[M] = fh[M] * acc;
+        }
+        // S_h <- gam S_h + k[:, half h]' (exp(G_63 - G) E)
+        const float gam = __expf(gend);
+#pragma unroll
+        for (int J = 0; J < NTH; ++J) {
+            f32x4 acc = gam * sv[J];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const mx::bf16x4 k4 =
+                    mx::lds_read_tr(&kb[(16 * t + 4 * lg + (lr >> 2)) * LKB + kh0 + 16 * J + 4 * (lr & 3)]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc = mfma4(static_cast<float>(k4[e]), es[t][e], acc);
+            }
+            sv[J] = acc;
+        }
+        store_k(nb);       // the next chunk's k (the compiler waits for its loads)
+        barrier_vm<16>();  // its T, G, beta copies and k have landed (its v may still be in flight)
     }
 }
 
@@ -1067,15 +1245,17 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kq16_kernel(
 // makes the reduction index run along rows (T'' and its transpose, A
 // transposed, the slices of S, dS' and dO both ways, X and dE both ways).  The
 // slice operands are loaded one slice ahead; the barriers wait for LDS
-// operations only, so those loads stay in flight across them.
-template <int DK, int DV, bool PC, bool IN_BF16>
+// operations only, so those loads stay in flight across them.  With KQ (scalar
+// decay, bf16 inputs) K~, K^ and Q~ are not in the workspace: their values are
+// formed here from k, q and the token factors, as the prep kernel forms them.
+template <int DK, int DV, bool PC, bool IN_BF16, bool KQ>
 __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
     const void *__restrict__ v, const float *__restrict__ dO, int T, int H, int NC, float scale,
     const float *__restrict__ wT, const float *__restrict__ wA, const float *__restrict__ wG,
     const float *__restrict__ wB, const float *__restrict__ wS, const float *__restrict__ wdS,
     const float *__restrict__ wKt, const float *__restrict__ wKh, const float *__restrict__ wQt,
-    float *__restrict__ wdA, float *__restrict__ wdTT, float *__restrict__ wdG, float *__restrict__ wdG63,
-    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv, bool delta, SeqTable tb) {
+    const __bf16 *__restrict__ kin, const __bf16 *__restrict__ qin, float *__restrict__ wdA,
+    float *__restrict__ wdTT, float *__restrict__ wdG, float *__restrict__ wdG63, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv, bool delta, SeqTable tb) {
     constexpr int GK = PC ? DK : 1;
     constexpr int JK = DK / 16;   // column tiles of the C x DK accumulators, and reduction blocks over channels
     constexpr int LR = kBS + 4;   // rows of a 16-column slice (16-byte aligned)
@@ -1103,7 +1283,21 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
 
     // this wavefront's rows of K~ and K^: kt[t][e] = K~[16w + lr][16t + 4lg + e]
     f32x4 kt[JK], kh[JK];
-    {
+    if constexpr (KQ) {  // exp(G_r) k_r and exp(G_63 - G_r) k_r, k read 8 bytes (four bf16) at a time
+        static_assert(!PC && IN_BF16, "k and q scaled per token: scalar decay, bf16 inputs");
+        const int r = 16 * w + lr;
+        const float gr = wG[(size_t)ci * C + r], gend = wG[(size_t)ci * C + C - 1];
+        const float fe = __expf(gr), fh = __expf(gend - gr);
+        const auto rk = rows_rsrc(kin + uniform(sl.row0) * DK, uniform(n), H * DK * 2, DK * 2);
+#pragma unroll
+        for (int t = 0; t < JK; ++t) {
+            const auto raw = __builtin_amdgcn_raw_buffer_load_b64(rk, (r * H * DK + 16 * t + 4 * lg) * 2, 0, 0);
+            const f32x4 k4 = {__uint_as_float(raw[0] << 16), __uint_as_float(raw[0] & 0xffff0000u),
+                              __uint_as_float(raw[1] << 16), __uint_as_float(raw[1] & 0xffff0000u)};
+            kt[t] = fe * k4;
+            kh[t] = fh * k4;
+        }
+    } else {
         const float *ktr = wKt + ((size_t)ci * C + 16 * w + lr) * DK + 4 * lg;
         const float *khr = wKh + ((size_t)ci * C + 16 * w + lr) * DK + 4 * lg;
 #pragma unroll
@@ -1304,6 +1498,9 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
     // parts of dG: dK~ K~ + dQ~ Q~ - dK^ K^; for G_63 also sum_i dK^ K^ + dgam gam
     const float *Gc = wG + (size_t)ci * C * GK;
     float rowpart[4] = {0.f, 0.f, 0.f, 0.f};  // scalar decay: sums over this lane's channels
+    [[maybe_unused]] const size_t kq0 = KQ ? uniform(sl.row0) * DK : 0;
+    [[maybe_unused]] const auto rkq = rows_rsrc(kin + kq0, KQ ? uniform(n) : 0, H * DK * 2, DK * 2);
+    [[maybe_unused]] const auto rqq = rows_rsrc(qin + kq0, KQ ? uniform(n) : 0, H * DK * 2, DK * 2);
     float colh[JK];                           // per channel 16J + lr: sum over this lane's rows of dK^ K^
 #pragma unroll
     for (int J = 0; J < JK; ++J) {
@@ -1315,8 +1512,17 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
             const int i = 16 * w + 4 * lg + r;
             const float gi = Gc[i * GK + (PC ? ch : 0)];
             const float ei = __expf(gi);
-            const float ktv = wKt[((size_t)ci * C + i) * DK + ch], khv = wKh[((size_t)ci * C + i) * DK + ch];
-            const float qt = wQt[((size_t)ci * C + i) * DK + ch];
+            float ktv, khv, qt;
+            if constexpr (KQ) {
+                const float kv = buf_in<true>(rkq, i * H * DK + ch), qv = buf_in<true>(rqq, i * H * DK + ch);
+                ktv = ei * kv;
+                khv = __expf(ge - gi) * kv;
+                qt = scale * ei * qv;
+            } else {
+                ktv = wKt[((size_t)ci * C + i) * DK + ch];
+                khv = wKh[((size_t)ci * C + i) * DK + ch];
+                qt = wQt[((size_t)ci * C + i) * DK + ch];
+            }
             if (i < n) {
                 const size_t off = (sl.row0 + (size_t)i * H) * DK + ch;
                 dq[off] = scale * ei * aQ[J][r];
@@ -1983,7 +2189,8 @@ template <int DK, int DV, bool PC, bool KZ, bool IB>
 hipError_t launch_bwd_t(const BwdArgs &a) {
     // packed batch: a.NC is the chunk bound of all sequences together
     const size_t slots = (size_t)(a.tab.start ? 1 : a.B) * a.H * a.NC;
-    BwdWs w = carve_bwd<DK, DV, PC>(a.ws, slots);
+    constexpr bool ops = bwd_stores_ops(PC, IB);  // K~, K^, Q~ in the workspace
+    BwdWs w = carve_bwd<DK, DV, PC>(a.ws, slots, ops);
     const unsigned nslot = (unsigned)slots;
     const unsigned nwalk = (unsigned)(a.B * a.H * (DV / kBV));
     hipLaunchKernelGGL((bwd_prep_kernel<DK, PC, KZ, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.q, a.k, a.g,
@@ -1991,10 +2198,15 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
                        a.tab);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_states_kernel<DK, DV, PC, IB>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.v, a.T, a.H,
-                       a.NC, w.T, w.G, w.beta, w.Kt, w.Kh, a.s0, w.S, a.delta, a.tab);
+    if constexpr (ops)
+        hipLaunchKernelGGL((bwd_states_kernel<DK, DV, PC, IB>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.v, a.T,
+                           a.H, a.NC, w.T, w.G, w.beta, w.Kt, w.Kh, a.s0, w.S, a.delta, a.tab);
+    else
+        hipLaunchKernelGGL((bwd_states_kq16_kernel<DK, DV>), dim3(nwalk), dim3(kThreads), 0, a.stream,
+                           static_cast<const __bf16 *>(a.v), static_cast<const __bf16 *>(a.k), a.T, a.H, a.NC, w.T,
+                           w.G, w.beta, a.s0, w.S, a.delta, a.tab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if constexpr (!PC && IB)  // scalar decay with bf16 inputs: the walk on k and q themselves
+    if constexpr (!ops)  // scalar decay with bf16 inputs: the walk on k and q themselves
         hipLaunchKernelGGL((bwd_dstates_kq16_kernel<DK, DV>), dim3(nwalk), dim3(kThreads), 0, a.stream,
                            static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), a.dO, a.T, a.H, a.NC,
                            a.scale, w.T, w.A, w.G, w.beta, a.ds_final, w.dS, a.ds0, a.delta, a.tab);
@@ -2002,9 +2214,10 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
         hipLaunchKernelGGL((bwd_dstates_kernel<DK, DV, PC>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.dO, a.T,
                            a.H, a.NC, w.T, w.A, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.ds_final, w.dS, a.ds0, a.delta, a.tab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_grads_a_kernel<DK, DV, PC, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.v, a.dO, a.T,
-                       a.H, a.NC, a.scale, w.T, w.A, w.G, w.beta, w.S, w.dS, w.Kt, w.Kh, w.Qt, w.dA, w.dTT, w.dG,
-                       w.dG63, a.dq, a.dk, a.dv, a.delta, a.tab);
+    hipLaunchKernelGGL((bwd_grads_a_kernel<DK, DV, PC, IB, !ops>), dim3(nslot), dim3(kThreads), 0, a.stream, a.v,
+                       a.dO, a.T, a.H, a.NC, a.scale, w.T, w.A, w.G, w.beta, w.S, w.dS, w.Kt, w.Kh, w.Qt,
+                       static_cast<const __bf16 *>(a.k), static_cast<const __bf16 *>(a.q), w.dA, w.dTT, w.dG, w.dG63,
+                       a.dq, a.dk, a.dv, a.delta, a.tab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grads_b_kernel<DK, PC, KZ, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.q, a.k,
                        a.T, a.H, a.NC, a.eps, a.scale, w.T, w.M, w.A, w.G, w.beta, w.dA, w.dTT, w.dG, w.dG63, a.dq,
@@ -2094,12 +2307,16 @@ hipError_t launch_chunk_tile(const ChunkArgs &a, int stage) {
     return launch_tile_fwd_d<64, 64>(a, stage);
 }
 
-size_t chunk_bwd_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel) {
+size_t chunk_bwd_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel, bool qkv_bf16) {
     const size_t slots = (size_t)B * H * NC;
-    if (Dk == 128 && Dv == 128) return per_channel ? bwd_bytes<128, 128, true>(slots) : bwd_bytes<128, 128, false>(slots);
-    if (Dk == 128 && Dv == 64) return per_channel ? bwd_bytes<128, 64, true>(slots) : bwd_bytes<128, 64, false>(slots);
-    if (Dk == 64 && Dv == 128) return per_channel ? bwd_bytes<64, 128, true>(slots) : bwd_bytes<64, 128, false>(slots);
-    return per_channel ? bwd_bytes<64, 64, true>(slots) : bwd_bytes<64, 64, false>(slots);
+    const bool ops = bwd_stores_ops(per_channel, qkv_bf16);
+    if (Dk == 128 && Dv == 128)
+        return per_channel ? bwd_bytes<128, 128, true>(slots, ops) : bwd_bytes<128, 128, false>(slots, ops);
+    if (Dk == 128 && Dv == 64)
+        return per_channel ? bwd_bytes<128, 64, true>(slots, ops) : bwd_bytes<128, 64, false>(slots, ops);
+    if (Dk == 64 && Dv == 128)
+        return per_channel ? bwd_bytes<64, 128, true>(slots, ops) : bwd_bytes<64, 128, false>(slots, ops);
+    return per_channel ? bwd_bytes<64, 64, true>(slots, ops) : bwd_bytes<64, 64, false>(slots, ops);
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs &a) {

@@ -337,7 +337,8 @@ static int bwd_workspace(const gdr_desc *d, bool packed, size_t *bytes, size_t *
     if ((size_t)Bw * d->H * (size_t)NC >= ((size_t)1 << 31)) return GDR_E_SHAPE;
     const size_t tab = packed ? gdr::seq_table_bytes(d->B, (int)NC) : 0;
     *bytes = tab + gdr::chunk_bwd_workspace_bytes(Bw, d->H, (int)NC, d->Dk, d->Dv,
-                                                  d->decay_mode == GDR_DECAY_PER_CHANNEL);
+                                                  d->decay_mode == GDR_DECAY_PER_CHANNEL,
+                                                  d->qkv_dtype == GDR_BF16);
     if (table) *table = tab;
     return GDR_OK;
 }

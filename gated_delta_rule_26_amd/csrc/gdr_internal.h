@@ -115,7 +115,7 @@ struct BwdArgs {
     hipStream_t stream;
 };
 // Backward pass (fp32 vector kernels).
-size_t chunk_bwd_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel);
+size_t chunk_bwd_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel, bool qkv_bf16);
 hipError_t launch_chunk_bwd(const BwdArgs &a);
 
 // T == 0: s_final = s0 (or zero).

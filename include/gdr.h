@@ -206,7 +206,8 @@ int gdr_chunk_fwd_varlen(const gdr_desc *desc, const int32_t *cu_seqlens,
  *   ds0       [B, H, Dk, Dv] fp32 (written), or NULL
  *   workspace at least gdr_chunk_bwd_workspace_size bytes (per chunk and
  *             head: the entering state and its gradient, 2 Dk Dv fp32, and
- *             about 180 KiB of per-chunk matrices at Dk = 128)
+ *             about 80 KiB of per-chunk matrices; with per-channel decay or
+ *             fp32 q, k also the decayed keys and queries, 3 x 64 x Dk fp32)
  * Outputs must not overlap inputs, each other or the workspace.  With
  * T == 0 only ds0 is written (= ds_final, or zero).
  */
