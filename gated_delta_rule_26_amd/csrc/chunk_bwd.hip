@@ -61,18 +61,29 @@ struct BwdWs {
     float *dA, *dTT, *dG;          // C x C (two), C x GK
     float *dG63;                   // GK: the chunk-end decay's extra gradient (K^ and gam)
     float *Kt, *Kh, *Qt;           // C x DK each: K~, K^, Q~ (decayed operands, fp32), or null
+    void *rec;                     // the forward intra kernel's chunk records (bf16 walk), or null
 };
 
 // Whether the decayed operands are stored: not for scalar decay with bf16
 // inputs, whose kernels form them from k and q (exact in bf16) and the token
 // factors where they use them.
 constexpr bool bwd_stores_ops(bool per_channel, bool qkv_bf16) { return per_channel || !qkv_bf16; }
+// Whether the entering states come from the forward pass's bf16 walk (bf16
+// products with hi/lo split fp32 operands, as the forward pass computes them):
+// scalar decay with bf16 inputs at d_k = d_v = 128.  Its chunk records lead
+// the workspace.
+constexpr bool bwd_walk16(bool ops, int Dk, int Dv) { return !ops && Dk == 128 && Dv == 128; }
 
 template <int DK, int DV, bool PC>
 BwdWs carve_bwd(void *ws, size_t slots, bool ops) {
     constexpr int GK = PC ? DK : 1;
-    float *p = static_cast<float *>(ws);
     BwdWs w;
+    w.rec = nullptr;
+    if (bwd_walk16(ops, DK, DV)) {
+        w.rec = ws;
+        ws = static_cast<char *>(ws) + chunk_states_record_bytes((long)slots);
+    }
+    float *p = static_cast<float *>(ws);
     w.T = p; p += slots * C * C;
     w.A = p; p += slots * C * C;
     w.M = p; p += slots * C * C;
@@ -97,7 +108,8 @@ template <int DK, int DV, bool PC>
 size_t bwd_bytes(size_t slots, bool ops) {
     constexpr int GK = PC ? DK : 1;
     return slots * sizeof(float) *
-           ((size_t)5 * C * C + 2 * (size_t)C * GK + GK + C + 2 * (size_t)DK * DV + (ops ? 3 * (size_t)C * DK : 0));
+               ((size_t)5 * C * C + 2 * (size_t)C * GK + GK + C + 2 * (size_t)DK * DV + (ops ? 3 * (size_t)C * DK : 0)) +
+           (bwd_walk16(ops, DK, DV) ? chunk_states_record_bytes((long)slots) : 0);
 }
 
 // chunk slot ci -> token row of its token 0 and token count.  Fixed-length
@@ -2198,7 +2210,30 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
                        a.tab);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if constexpr (ops)
+    if constexpr (bwd_walk16(ops, DK, DV)) {  // the forward pass's records and bf16 walk
+        ChunkArgs f{};
+        f.B = a.B;
+        f.T = a.T;
+        f.H = a.H;
+        f.Dk = DK;
+        f.Dv = DV;
+        f.NC = a.NC;
+        f.tab = a.tab;
+        f.qkv_bf16 = true;
+        f.kaczmarz = a.kaczmarz;
+        f.delta = a.delta;
+        f.eps = a.eps;
+        f.scale = a.scale;
+        f.q = a.q;
+        f.k = a.k;
+        f.v = a.v;
+        f.g = a.g;
+        f.beta = a.beta;
+        f.s0 = a.s0;
+        f.ws = w.rec;
+        f.stream = a.stream;
+        if ((e = launch_chunk_states(f, w.S)) != hipSuccess) return e;
+    } else if constexpr (ops)
         hipLaunchKernelGGL((bwd_states_kernel<DK, DV, PC, IB>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.v, a.T,
                            a.H, a.NC, w.T, w.G, w.beta, w.Kt, w.Kh, a.s0, w.S, a.delta, a.tab);
     else

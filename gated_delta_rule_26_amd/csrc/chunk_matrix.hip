@@ -286,19 +286,24 @@ __device__ __forceinline__ int kperm_col(int seg, int hh) {
 //    2NS-1 walk the columns of M (identity start, v = 0); N and M go to
 //    s_out[g][0] and s_out[g][1].  No outputs, so the LDS holds only the
 //    k, v staging and the decays (48 KB) and two workgroups share a unit.
+//  * STATES (with TRANSFER's staging, P = 1): the walk of S itself from s0
+//    (or zero), no outputs; the state entering every chunk goes to s_out at
+//    the chunk's record index ([DK][DV] each), for the backward pass.
 // DELTA = false: E = V (no K S, no T''), records without T''.
-template <bool OUT_BF16, bool TRANSFER, bool DELTA>
+template <bool OUT_BF16, bool TRANSFER, bool DELTA, bool STATES = false>
 __global__ __launch_bounds__(kStateThreads, TRANSFER ? 2 : 1) void state_matrix_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const char *__restrict__ ws, const float *__restrict__ s0, void *__restrict__ o,
     float *__restrict__ s_out, int T, int H, int NC, int G, int P, int seg, float scale, SeqTable tb) {
+    static_assert(!STATES || TRANSFER, "the states walk uses the transfer walk's staging");
+    constexpr bool MAPS = TRANSFER && !STATES;  // the walk of a chunk map
     __shared__ std::conditional_t<TRANSFER, TransferSmem, StateSmem> sm;
 
     int g, slice;
-    state_slot(blockIdx.x, G, TRANSFER ? 2 * NS : NS, g, slice);
+    state_slot(blockIdx.x, G, MAPS ? 2 * NS : NS, g, slice);
     g = walk_seq(g, H, tb);  // packed batches (P = 1): longest sequences first
     const int bh = g / P, p = g % P;
-    const int kind = TRANSFER ? slice / NS : 0;  // transfer: 0 = N, 1 = M
+    const int kind = MAPS ? slice / NS : 0;      // transfer: 0 = N, 1 = M
     const int c0 = p * seg;
     const WalkPlace wp = walk_place(bh, c0, seg, T, H, NC, tb, ws, kRecBytes);
     const int nc = wp.nc;                        // chunks of this segment
@@ -309,9 +314,12 @@ __global__ __launch_bounds__(kStateThreads, TRANSFER ? 2 : 1) void state_matrix_
     const int lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const char *recs = wp.recs;
-    const float *s_in = TRANSFER || !s0 ? nullptr : s0 + (size_t)g * DK * DV;
-    float *s_end = TRANSFER ? s_out + ((size_t)g * 2 + kind) * DK * DV
-                            : (s_out && p == P - 1 ? s_out + (size_t)bh * DK * DV : nullptr);
+    const float *s_in = MAPS || !s0 ? nullptr : s0 + (size_t)g * DK * DV;
+    float *s_end = STATES ? nullptr
+                   : TRANSFER ? s_out + ((size_t)g * 2 + kind) * DK * DV
+                              : (s_out && p == P - 1 ? s_out + (size_t)bh * DK * DV : nullptr);
+    // STATES: record index of the segment's first chunk and from one chunk to the next
+    const size_t slot0 = (size_t)(recs - ws) / kRecBytes, slot_step = rstride / kRecBytes;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     if (nc <= 0) {  // empty sequence: the final state is the initial one
@@ -342,7 +350,7 @@ __global__ __launch_bounds__(kStateThreads, TRANSFER ? 2 : 1) void state_matrix_
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * i + 4 * lg + r;
-                if constexpr (TRANSFER) S[i][r] = kind == 1 && row == jt + lr ? 1.f : 0.f;
+                if constexpr (MAPS) S[i][r] = kind == 1 && row == jt + lr ? 1.f : 0.f;
                 else S[i][r] = s_in ? s_in[(size_t)row * DV + jt + lr] : 0.f;
             }
         // T'' fragments of even chunks in tA, of odd chunks in tB: each chunk
@@ -358,6 +366,13 @@ __global__ __launch_bounds__(kStateThreads, TRANSFER ? 2 : 1) void state_matrix_
         auto step = [&](int c, const bf16x8 *th, const bf16x8 *tl, bf16x8 *thn, bf16x8 *tln)
                         __attribute__((always_inline)) {
             const int buf = c & 1;
+            if constexpr (STATES) {  // the state entering chunk c
+                float *Sc = s_out + (slot0 + (size_t)c * slot_step) * (DK * DV);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Sc[(size_t)(16 * i + 4 * lg + r) * DV + jt + lr] = S[i][r];
+            }
             // next chunk's T'' fragments, in flight during this chunk
             if constexpr (DELTA) {
                 const char *rn = recs + (size_t)min(c + 1, nc - 1) * rstride;
@@ -746,7 +761,29 @@ hipError_t launch_state(const ChunkArgs &a) {
     return hipGetLastError();
 }
 
+// The backward pass's walk: one workgroup per (sequence, head, 32 value
+// columns), every chunk of the sequence, the entering states to `states`.
+template <bool DELTA>
+hipError_t launch_states_walk(const ChunkArgs &a, float *states) {
+    const int BH = a.B * a.H;
+    GDR_LAUNCH((state_matrix_kernel<false, true, DELTA, true>), dim3((unsigned)(BH * NS)), dim3(kStateThreads),
+               a.stream, nullptr, nullptr, static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k),
+               static_cast<const __bf16 *>(a.v), static_cast<const char *>(a.ws), a.s0, nullptr, states, a.T, a.H,
+               a.NC, BH, 1, a.NC, a.scale, a.tab);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+size_t chunk_states_record_bytes(long slots) { return (size_t)slots * kRecBytes; }
+
+hipError_t launch_chunk_states(const ChunkArgs &a, float *states) {
+    if (chunk_slots(a) == 0) return hipSuccess;
+    const hipError_t e = !a.delta ? launch_intra<false, false>(a)
+                         : a.kaczmarz ? launch_intra<true, true>(a) : launch_intra<false, true>(a);
+    if (e != hipSuccess) return e;
+    return a.delta ? launch_states_walk<true>(a, states) : launch_states_walk<false>(a, states);
+}
 
 int mx::intra_grid(long total, int per_cu) {
     int dev = 0, cus = 0;

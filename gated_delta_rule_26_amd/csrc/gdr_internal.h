@@ -97,6 +97,12 @@ hipError_t launch_chunk_matrix(const ChunkArgs &a, int stage);
 // per-chunk prep, then a walk that forms the outputs (chunk_bwd.hip).
 size_t chunk_tile_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel);
 hipError_t launch_chunk_tile(const ChunkArgs &a, int stage);
+// The state entering every chunk, for the backward pass (bf16 inputs at
+// Dk = Dv = 128, scalar decay): the intra kernel's records into a.ws
+// (chunk_states_record_bytes), then the bf16 walk without outputs, the states
+// to `states` at the records' indices ([Dk][Dv] fp32 each).
+size_t chunk_states_record_bytes(long slots);
+hipError_t launch_chunk_states(const ChunkArgs &a, float *states);
 // Its per-channel-decay kernels (called by the two functions above).
 size_t chunk_matrix_pc_workspace_bytes(int B, int H, int NC);
 hipError_t launch_chunk_matrix_pc(const ChunkArgs &a, int stage);
