@@ -81,7 +81,7 @@ BwdWs carve_bwd(void *ws, size_t slots, bool ops) {
     w.rec = nullptr;
     if (bwd_walk16(ops, DK, DV)) {
         w.rec = ws;
-        ws = static_cast<char *>(ws) + chunk_states_record_bytes((long)slots);
+        ws = static_cast<char *>(ws) + slots * mx::kRecBytes;
     }
     float *p = static_cast<float *>(ws);
     w.T = p; p += slots * C * C;
@@ -109,7 +109,7 @@ size_t bwd_bytes(size_t slots, bool ops) {
     constexpr int GK = PC ? DK : 1;
     return slots * sizeof(float) *
                ((size_t)5 * C * C + 2 * (size_t)C * GK + GK + C + 2 * (size_t)DK * DV + (ops ? 3 * (size_t)C * DK : 0)) +
-           (bwd_walk16(ops, DK, DV) ? chunk_states_record_bytes((long)slots) : 0);
+           (bwd_walk16(ops, DK, DV) ? slots * mx::kRecBytes : 0);
 }
 
 // chunk slot ci -> token row of its token 0 and token count.  Fixed-length
@@ -292,7 +292,9 @@ constexpr int kLB = 48;   // B operands of 32 columns, read column-wise
 // K~, K^, Q~ are written next; then the LDS that held k and q holds R as
 // 16x16 tiles and T = (I + R)^-1 is formed by the block inverse of the
 // forward pass's intra kernel (forward substitution on the diagonal blocks,
-// matrix-core products for the others).
+// matrix-core products for the others).  With `rec` (scalar decay) the chunk
+// record of the forward pass's bf16 walk is written too, from the same T and
+// A: T'' and A as bf16 hi/lo operand fragments, exp(G) and exp(G_63 - G).
 constexpr float kSpanMax = 64.f;
 
 template <int DK, bool PC, bool KZ, bool IN_BF16>
@@ -300,9 +302,10 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, int T, int H, int NC, float eps, float scale, float *__restrict__ wT,
     float *__restrict__ wA, float *__restrict__ wM, float *__restrict__ wG, float *__restrict__ wB,
-    float *__restrict__ wKt, float *__restrict__ wKh, float *__restrict__ wQt, bool delta, SeqTable tb) {
+    float *__restrict__ wKt, float *__restrict__ wKh, float *__restrict__ wQt, char *__restrict__ rec, bool delta,
+    SeqTable tb) {
     constexpr int GK = PC ? DK : 1;
-    static_assert(2 * C * (DK + 1) >= 16 * mx::kTile, "the R and T tiles must fit where k and q were");
+    static_assert(2 * C * (DK + 1) >= 26 * mx::kTile, "the R, T and A tiles must fit where k and q were");
     const int ci = blockIdx.x;
     if (!slot_used(ci, H, tb)) return;
     const Slot sl = slot_of(ci, T, H, NC, tb);
@@ -420,7 +423,7 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
 
     // ---- M and A; this wavefront's R = Diag(beta) M values stay in registers
     float *Mg = wM + (size_t)ci * C * C, *Ag = wA + (size_t)ci * C * C;
-    f32x4 rv[3];
+    f32x4 rv[3], av[3];  // this wavefront's lower tiles of R and (for the record) A
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
         const int t = w + 4 * s4;
@@ -476,7 +479,10 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
             const float m = delta && j < i ? mm[r] * pp : 0.f;
             Mg[i * C + j] = m;
             Ag[i * C + j] = scale * aa[r] * pp;
-            if (s4 < 3 && t < 10) rv[s4 < 3 ? s4 : 0][r] = sBeta[i] * m;
+            if (s4 < 3 && t < 10) {
+                rv[s4 < 3 ? s4 : 0][r] = sBeta[i] * m;
+                av[s4 < 3 ? s4 : 0][r] = scale * aa[r] * pp;
+            }
         }
     }
     for (int idx = tid; idx < C * GK; idx += kThreads) wG[(size_t)ci * C * GK + idx] = sG[idx / GK][idx % GK];
@@ -509,7 +515,7 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
 
     // ---- T = (I + R)^-1 on 16x16 tiles in the LDS of k and q
     float *tiles = &sKQ[0][0][0];
-    const mx::TriTiles tri{tiles, tiles + 10 * mx::kTile, nullptr};
+    const mx::TriTiles tri{tiles, tiles + 10 * mx::kTile, tiles + 16 * mx::kTile};
 #pragma unroll
     for (int s4 = 0; s4 < 3; ++s4) {
         const int t = w + 4 * s4;
@@ -519,10 +525,25 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
             float *dst = &tri.R[mx::tile_id(I, J) * mx::kTile];
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(4 * lg + r) * mx::LT + lr] = rv[s4][r];
+            if (!PC && rec) {
+                float *da = &tri.A[mx::tile_id(I, J) * mx::kTile];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) da[(4 * lg + r) * mx::LT + lr] = av[s4][r];
+            }
         }
     }
     __syncthreads();
     mx::invert_unit_lower(tri, lane, w, lr, lg);  // ends with a barrier
+    if constexpr (!PC) {
+        if (rec) {  // the forward walk's record of this chunk
+            char *recb = rec + (size_t)ci * mx::kRecBytes;
+            mx::pack_T_A<true>(tri, sBeta, recb, tid);
+            if (tid < C) {
+                reinterpret_cast<float *>(recb + mx::kRecGam)[tid] = sE[0][tid];
+                reinterpret_cast<float *>(recb + mx::kRecGend)[tid] = sE[1][tid];
+            }
+        }
+    }
     float *Tg = wT + (size_t)ci * C * C;
     for (int idx4 = tid; idx4 < C * C / 4; idx4 += kThreads) {  // 16-byte stores
         const int i = idx4 / (C / 4), j = (idx4 % (C / 4)) * 4, I = i >> 4, J = j >> 4;
@@ -2206,11 +2227,11 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
     const unsigned nslot = (unsigned)slots;
     const unsigned nwalk = (unsigned)(a.B * a.H * (DV / kBV));
     hipLaunchKernelGGL((bwd_prep_kernel<DK, PC, KZ, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.q, a.k, a.g,
-                       a.beta, a.T, a.H, a.NC, a.eps, a.scale, w.T, w.A, w.M, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.delta,
-                       a.tab);
+                       a.beta, a.T, a.H, a.NC, a.eps, a.scale, w.T, w.A, w.M, w.G, w.beta, w.Kt, w.Kh, w.Qt,
+                       static_cast<char *>(w.rec), a.delta, a.tab);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if constexpr (bwd_walk16(ops, DK, DV)) {  // the forward pass's records and bf16 walk
+    if constexpr (bwd_walk16(ops, DK, DV)) {  // the forward pass's bf16 walk over the records prep wrote
         ChunkArgs f{};
         f.B = a.B;
         f.T = a.T;
@@ -2293,7 +2314,7 @@ hipError_t launch_tile_fwd_t(const ChunkArgs &a, int stage) {
     if (stage != 1) {
         GDR_LAUNCH((bwd_prep_kernel<DK, PC, KZ, IB>), dim3((unsigned)slots), dim3(kThreads), a.stream, a.ev0,
                    stage == 0 ? a.ev1 : nullptr, a.q, a.k, a.g, a.beta, a.T, a.H, a.NC, a.eps, a.scale, wT, wA, wM, wG,
-                   wB, wKt, wKh, wQt, a.delta, a.tab);
+                   wB, wKt, wKh, wQt, nullptr, a.delta, a.tab);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess || stage == 0) return e;
     }

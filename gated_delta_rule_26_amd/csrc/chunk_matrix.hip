@@ -55,12 +55,9 @@ namespace {
 
 using namespace mx;
 
-// ---- per-chunk workspace record (scalar decay): the common head (T'' and A
-// fragments), then, for the 64 tokens, Gam = exp(G) and Gend = exp(G_63 - G)
-// (fp32), so the walk needs no exponentials.
-constexpr int kRecGam = kRecHead;
-constexpr int kRecGend = kRecGam + C * 4;
-constexpr int kRecBytes = kRecGend + C * 4;  // 25088, a multiple of 256
+// The per-chunk workspace record of scalar decay (kRecBytes, matrix_common.h):
+// the T'' and A fragments, then exp(G) and exp(G_63 - G) of the 64 tokens, so
+// the walk needs no exponentials.
 
 // ============================================================ intra kernel
 // q and k are staged token-major for the K K^T and Q K^T products; the same
@@ -765,6 +762,7 @@ hipError_t launch_state(const ChunkArgs &a) {
 // columns), every chunk of the sequence, the entering states to `states`.
 template <bool DELTA>
 hipError_t launch_states_walk(const ChunkArgs &a, float *states) {
+    if (chunk_slots(a) == 0) return hipSuccess;
     const int BH = a.B * a.H;
     GDR_LAUNCH((state_matrix_kernel<false, true, DELTA, true>), dim3((unsigned)(BH * NS)), dim3(kStateThreads),
                a.stream, nullptr, nullptr, static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k),
@@ -775,13 +773,7 @@ hipError_t launch_states_walk(const ChunkArgs &a, float *states) {
 
 }  // namespace
 
-size_t chunk_states_record_bytes(long slots) { return (size_t)slots * kRecBytes; }
-
 hipError_t launch_chunk_states(const ChunkArgs &a, float *states) {
-    if (chunk_slots(a) == 0) return hipSuccess;
-    const hipError_t e = !a.delta ? launch_intra<false, false>(a)
-                         : a.kaczmarz ? launch_intra<true, true>(a) : launch_intra<false, true>(a);
-    if (e != hipSuccess) return e;
     return a.delta ? launch_states_walk<true>(a, states) : launch_states_walk<false>(a, states);
 }
 

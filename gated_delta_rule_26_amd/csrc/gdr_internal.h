@@ -98,10 +98,10 @@ hipError_t launch_chunk_matrix(const ChunkArgs &a, int stage);
 size_t chunk_tile_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel);
 hipError_t launch_chunk_tile(const ChunkArgs &a, int stage);
 // The state entering every chunk, for the backward pass (bf16 inputs at
-// Dk = Dv = 128, scalar decay): the intra kernel's records into a.ws
-// (chunk_states_record_bytes), then the bf16 walk without outputs, the states
-// to `states` at the records' indices ([Dk][Dv] fp32 each).
-size_t chunk_states_record_bytes(long slots);
+// Dk = Dv = 128, scalar decay): the bf16 walk without outputs over the chunk
+// records at a.ws (mx::kRecBytes each, in the intra kernel's format, written
+// by the caller), the states to `states` at the records' indices ([Dk][Dv]
+// fp32 each).
 hipError_t launch_chunk_states(const ChunkArgs &a, float *states);
 // Its per-channel-decay kernels (called by the two functions above).
 size_t chunk_matrix_pc_workspace_bytes(int B, int H, int NC);

@@ -87,6 +87,12 @@ constexpr int kRecTL = 6 * kFragBytes;
 constexpr int kRecAH = 12 * kFragBytes;
 constexpr int kRecAL = 18 * kFragBytes;
 constexpr int kRecHead = 24 * kFragBytes;
+// The record of scalar decay: the head, then exp(G_i) and exp(G_63 - G_i) of
+// the 64 tokens (fp32; past the end of a partial chunk G stays at its last
+// value).  Written by the forward intra kernel and by the backward's prep.
+constexpr int kRecGam = kRecHead;
+constexpr int kRecGend = kRecGam + C * 4;
+constexpr int kRecBytes = kRecGend + C * 4;  // 25088, a multiple of 256
 __host__ __device__ constexpr int lower_frag(int M, int kb) { return M < 2 ? M : 2 * M - 2 + kb; }
 __host__ __device__ constexpr int frag_M(int f) { return f < 2 ? f : 2 + ((f - 2) >> 1); }
 __host__ __device__ constexpr int frag_kb(int f) { return f < 2 ? 0 : (f - 2) & 1; }
