@@ -54,6 +54,41 @@ constexpr int kThreads = 256;
 constexpr int kBV = 32;  // value columns per walk workgroup
 constexpr int kBS = 16;  // value columns per slice of grads A
 
+// ---- the reverse record of the bf16 reverse walk (bwd_dstates_bf16_kernel), per chunk slot
+constexpr int kRevTH = 0;                    // T''' hi, lo; A' hi, lo: six fragments each
+constexpr int kRevTL = 6 * mx::kFragBytes;
+constexpr int kRevAH = 12 * mx::kFragBytes;
+constexpr int kRevAL = 18 * mx::kFragBytes;
+constexpr int kRevBytes = 24 * mx::kFragBytes;
+// Upper-triangular fragment f (M, kb): rows 16 M .. of a 64 x 64 matrix, columns 32 kb + kperm(p, e).
+__host__ __device__ constexpr int upper_frag(int M, int kb) { return M < 2 ? 2 * M + kb : M + 2; }
+__host__ __device__ constexpr int ufrag_M(int f) { return f < 4 ? f >> 1 : f - 2; }
+__host__ __device__ constexpr int ufrag_kb(int f) { return f < 4 ? f & 1 : 1; }
+
+// The reverse record of one chunk from prep's tiles: T''' = Diag(beta) T' and A' as bf16 hi/lo A-operand
+// fragments of their upper triangles.
+__device__ __forceinline__ void pack_reverse(const mx::TriTiles &t, const float *beta, char *dst, int tid) {
+    for (int u = tid; u < 2 * 6 * 64; u += kThreads) {
+        const int mat = u / 384, f = (u >> 6) % 6, l = u & 63;
+        const int i = 16 * ufrag_M(f) + (l & 15), p = l >> 4, kb = ufrag_kb(f);
+        mx::bf16x8 hv, lv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int j = 32 * kb + mx::kperm(p, e);
+            float x = 0.f;
+            if (j >= i) {
+                const int I = i >> 4, J = j >> 4, at = (j & 15) * mx::LT + (i & 15);
+                x = mat == 0 ? t.Tb(J, I)[at] * beta[i] : t.A[mx::tile_id(J, I) * mx::kTile + at];
+            }
+            hv[e] = static_cast<__bf16>(x);
+            lv[e] = static_cast<__bf16>(x - static_cast<float>(hv[e]));
+        }
+        char *d = dst + (mat == 0 ? kRevTH : kRevAH) + f * mx::kFragBytes + l * 16;
+        *reinterpret_cast<mx::bf16x8 *>(d) = hv;
+        *reinterpret_cast<mx::bf16x8 *>(d + 6 * mx::kFragBytes) = lv;
+    }
+}
+
 // ---- workspace, per chunk slot ci (fixed-length: (b H + h) NC + c; packed: u H + h)
 struct BwdWs {
     float *T, *A, *M, *G, *beta;   // C x C (three), C x GK, C
@@ -61,7 +96,8 @@ struct BwdWs {
     float *dA, *dTT, *dG;          // C x C (two), C x GK
     float *dG63;                   // GK: the chunk-end decay's extra gradient (K^ and gam)
     float *Kt, *Kh, *Qt;           // C x DK each: K~, K^, Q~ (decayed operands, fp32), or null
-    void *rec;                     // the forward intra kernel's chunk records (bf16 walk), or null
+    void *rec;                     // the bf16 walks' chunk records (forward, then reverse), or null
+    void *rrev;
 };
 
 // Whether the decayed operands are stored: not for scalar decay with bf16
@@ -78,10 +114,11 @@ template <int DK, int DV, bool PC>
 BwdWs carve_bwd(void *ws, size_t slots, bool ops) {
     constexpr int GK = PC ? DK : 1;
     BwdWs w;
-    w.rec = nullptr;
+    w.rec = w.rrev = nullptr;
     if (bwd_walk16(ops, DK, DV)) {
         w.rec = ws;
-        ws = static_cast<char *>(ws) + slots * mx::kRecBytes;
+        w.rrev = static_cast<char *>(ws) + slots * mx::kRecBytes;
+        ws = static_cast<char *>(w.rrev) + slots * kRevBytes;
     }
     float *p = static_cast<float *>(ws);
     w.T = p; p += slots * C * C;
@@ -109,7 +146,7 @@ size_t bwd_bytes(size_t slots, bool ops) {
     constexpr int GK = PC ? DK : 1;
     return slots * sizeof(float) *
                ((size_t)5 * C * C + 2 * (size_t)C * GK + GK + C + 2 * (size_t)DK * DV + (ops ? 3 * (size_t)C * DK : 0)) +
-           (bwd_walk16(ops, DK, DV) ? slots * mx::kRecBytes : 0);
+           (bwd_walk16(ops, DK, DV) ? slots * (mx::kRecBytes + kRevBytes) : 0);
 }
 
 // chunk slot ci -> token row of its token 0 and token count.  Fixed-length
@@ -302,8 +339,8 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, int T, int H, int NC, float eps, float scale, float *__restrict__ wT,
     float *__restrict__ wA, float *__restrict__ wM, float *__restrict__ wG, float *__restrict__ wB,
-    float *__restrict__ wKt, float *__restrict__ wKh, float *__restrict__ wQt, char *__restrict__ rec, bool delta,
-    SeqTable tb) {
+    float *__restrict__ wKt, float *__restrict__ wKh, float *__restrict__ wQt, char *__restrict__ rec,
+    char *__restrict__ rrev, bool delta, SeqTable tb) {
     constexpr int GK = PC ? DK : 1;
     static_assert(2 * C * (DK + 1) >= 26 * mx::kTile, "the R, T and A tiles must fit where k and q were");
     const int ci = blockIdx.x;
@@ -542,6 +579,7 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
                 reinterpret_cast<float *>(recb + mx::kRecGam)[tid] = sE[0][tid];
                 reinterpret_cast<float *>(recb + mx::kRecGend)[tid] = sE[1][tid];
             }
+            if (rrev) pack_reverse(tri, sBeta, rrev + (size_t)ci * kRevBytes, tid);
         }
     }
     float *Tg = wT + (size_t)ci * C * C;
@@ -1261,6 +1299,312 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kq16_kernel(
         for (int t = 0; t < NTH; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) ds0[sbase + (size_t)(kh0 + 16 * t + 4 * lg + e) * DV + jc] = dsv[t][e];
+    }
+}
+
+// ---- the same walk on bf16 tiles (scalar decay, bf16 inputs, d_k = d_v = 128), as the forward pass's
+// walk computes the states: bf16 products with every fp32 operand split into hi + lo (matrix_common.h).
+// Per chunk c, from the last, with dS' the gradient of its end state (stored first):
+//   P = k dS',  dE = A' dO + Diag(exp(G_63 - G)) P,  dX = T''' dE,
+//   dS = exp(G_63) dS' + q' (scale Diag(exp(G)) dO) - k' (Diag(exp(G)) dX)
+// (dS is the earlier chunk's dS').  One workgroup per (sequence, head, 32 value columns), chunks in
+// reverse.  Chain wavefronts 0, 1 keep dS of 16 value columns in registers as D tiles, the B operand of
+// the next product, and do the dependent products: k dS' (k rows from LDS in the permuted channel
+// order), T''' dE (upper-triangular fragments from the reverse record, loaded a chunk ahead) and the
+// update (k' by transposing LDS reads).  Helper wavefronts 2, 3 stage k, q and the decays in LDS and,
+// one chunk ahead of their chain wavefront, form the chain-independent A' dO (4 token tiles) and
+// q'(scale exp(G) dO) (8 channel tiles), which reach the chain through LDS.  One barrier per chunk;
+// q is staged one chunk earlier than k (the helpers read it before the chain reads k).
+struct alignas(16) RevSmem {
+    __bf16 K[2][C * (mx::DK + 16)];  // k, token-major, channels permuted (chunk parity)
+    __bf16 Q[2][C * (mx::DK + 16)];  // q, the same
+    f32x4 At[2][2][4][64];           // A' dO per chunk parity and chain wavefront, 4 token tiles
+    f32x4 Qd[2][2][8][64];           // q'(scale exp(G) dO), 8 channel tiles
+    float Gam[2][C], Gend[2][C];     // exp(G_i), exp(G_63 - G_i)
+};
+
+template <bool DELTA>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dstates_bf16_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const float *__restrict__ dO, int T, int H, int NC,
+    float scale, const char *__restrict__ rec, const char *__restrict__ rrev, const float *__restrict__ ds_final,
+    float *__restrict__ wdS, float *__restrict__ ds0, SeqTable tb) {
+    using mx::bf16x8;
+    constexpr int DK = mx::DK, DV = mx::DV, LDK = DK + 16, NT = DV / kBV;
+    __shared__ RevSmem sm;
+    int bh, tile;
+    state_slot(blockIdx.x, gridDim.x / NT, NT, bh, tile);
+    bh = walk_seq(bh, H, tb);
+    const BwdWalk wk = bwd_walk(bh, T, H, NC, tb);
+    const int nc = wk.nc, L = nc - 1;
+    const int j0 = tile * kBV;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+
+    if (w < 2) {
+        // ================= chain wavefront: value columns jt .. jt+15
+        const int jt = j0 + 16 * w;
+        f32x4 S[8];  // dS'[16 i + 4 lg + r][jt + lr]
+        const float *sfin = ds_final ? ds_final + (size_t)bh * DK * DV : nullptr;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[i][r] = sfin ? sfin[(size_t)(16 * i + 4 * lg + r) * DV + jt + lr] : 0.f;
+        if (nc > 0) {
+            // T''' fragments of even chunks in tA, of odd ones in tB (each step loads the next)
+            bf16x8 tAh[6], tAl[6], tBh[6], tBl[6];
+            auto load_t = [&](int c, bf16x8 *th, bf16x8 *tl) __attribute__((always_inline)) {
+                if constexpr (DELTA) {
+                    const char *r = rrev + wk.slot(max(c, 0)) * kRevBytes;
+#pragma unroll
+                    for (int f = 0; f < 6; ++f) {
+                        th[f] = *reinterpret_cast<const bf16x8 *>(r + kRevTH + f * mx::kFragBytes + lane * 16);
+                        tl[f] = *reinterpret_cast<const bf16x8 *>(r + kRevTL + f * mx::kFragBytes + lane * 16);
+                    }
+                }
+            };
+            if (L & 1) load_t(L, tBh, tBl);
+            else load_t(L, tAh, tAl);
+            auto step = [&](int c, const bf16x8 *th, const bf16x8 *tl, bf16x8 *thn, bf16x8 *tln)
+                            __attribute__((always_inline)) {
+                const int buf = c & 1;
+                {  // the gradient of chunk c's end state
+                    float *d = wdS + wk.slot(c) * DK * DV;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) d[(size_t)(16 * i + 4 * lg + r) * DV + jt + lr] = S[i][r];
+                }
+                load_t(c - 1, thn, tln);
+                const float gs = sm.Gam[buf][C - 1];
+                bf16x8 PH[2], PL[2];  // -exp(G) dX as the update's B operand
+                if constexpr (DELTA) {
+                    bf16x8 SH[4], SL[4];
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb) mx::pair_split(S[2 * kb], S[2 * kb + 1], SH[kb], SL[kb]);
+                    // P = k dS' (token tile M); the next 32 channels' k fragments read during the products
+                    const __bf16 *sK = sm.K[buf];
+                    f32x4 P[4] = {z4, z4, z4, z4};
+                    bf16x8 ka[2][4];
+#pragma unroll
+                    for (int M = 0; M < 4; ++M) ka[0][M] = *reinterpret_cast<const bf16x8 *>(&sK[(16 * M + lr) * LDK + 8 * lg]);
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb) {
+                        const int cur = kb & 1;
+                        if (kb + 1 < 4) {
+#pragma unroll
+                            for (int M = 0; M < 4; ++M)
+                                ka[cur ^ 1][M] = *reinterpret_cast<const bf16x8 *>(
+                                    &sK[(16 * M + lr) * LDK + 32 * (kb + 1) + 8 * lg]);
+                        }
+#pragma unroll
+                        for (int M = 0; M < 4; ++M) P[M] = mx::mma(ka[cur][M], SH[kb], P[M]);
+#pragma unroll
+                        for (int M = 0; M < 4; ++M) P[M] = mx::mma(ka[cur][M], SL[kb], P[M]);
+                    }
+                    // dE = A' dO + exp(G_63 - G) P
+                    f32x4 dE[4];
+#pragma unroll
+                    for (int M = 0; M < 4; ++M) {
+                        const f32x4 gnd = *reinterpret_cast<const f32x4 *>(&sm.Gend[buf][16 * M + 4 * lg]);
+                        const f32x4 at = sm.At[buf][w][M][lane];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) dE[M][r] = at[r] + gnd[r] * P[M][r];
+                    }
+                    bf16x8 EH[2], EL[2];
+                    mx::pair_split(dE[0], dE[1], EH[0], EL[0]);
+                    mx::pair_split(dE[2], dE[3], EH[1], EL[1]);
+                    // dX = T''' dE (upper triangle: token blocks kb >= M / 2), then -exp(G) dX
+                    f32x4 Ep[4];
+#pragma unroll
+                    for (int M = 0; M < 4; ++M) {
+                        f32x4 dx = z4;
+#pragma unroll
+                        for (int kb = M >> 1; kb < 2; ++kb) {
+                            const int f = upper_frag(M, kb);
+                            dx = mx::mma(th[f], EH[kb], dx);
+                            dx = mx::mma(th[f], EL[kb], dx);
+                            dx = mx::mma(tl[f], EH[kb], dx);
+                        }
+                        const f32x4 gm = *reinterpret_cast<const f32x4 *>(&sm.Gam[buf][16 * M + 4 * lg]);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) Ep[M][r] = -gm[r] * dx[r];
+                    }
+                    mx::pair_split(Ep[0], Ep[1], PH[0], PL[0]);
+                    mx::pair_split(Ep[2], Ep[3], PH[1], PL[1]);
+                }
+                // dS = exp(G_63) dS' + q'(scale exp(G) dO) - k'(exp(G) dX), key-channel tile i
+                const __bf16 *sK = sm.K[buf];
+                bf16x8 kt[2][2];
+                if constexpr (DELTA) {
+                    kt[0][0] = mx::kt_operand(sK, LDK, 0, 0, lr, lg);
+                    kt[0][1] = mx::kt_operand(sK, LDK, 0, 1, lr, lg);
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int cur = i & 1;
+                    if (DELTA && i + 1 < 8) {
+                        kt[cur ^ 1][0] = mx::kt_operand(sK, LDK, i + 1, 0, lr, lg);
+                        kt[cur ^ 1][1] = mx::kt_operand(sK, LDK, i + 1, 1, lr, lg);
+                    }
+                    f32x4 acc = S[i] * gs + sm.Qd[buf][w][i][lane];
+                    if constexpr (DELTA) {
+                        acc = mx::mma(kt[cur][0], PH[0], acc);
+                        acc = mx::mma(kt[cur][0], PL[0], acc);
+                        acc = mx::mma(kt[cur][1], PH[1], acc);
+                        acc = mx::mma(kt[cur][1], PL[1], acc);
+                    }
+                    S[i] = acc;
+                }
+            };
+            barrier_lds();
+            barrier_lds();
+            int c = L;
+            if (L & 1) {  // odd chunks use tB: the last chunk first when it is odd
+                step(c, tBh, tBl, tAh, tAl);
+                barrier_lds();
+                --c;
+            }
+            for (; c >= 2; c -= 2) {
+                step(c, tAh, tAl, tBh, tBl);
+                barrier_lds();
+                step(c - 1, tBh, tBl, tAh, tAl);
+                barrier_lds();
+            }
+            step(0, tAh, tAl, tBh, tBl);
+            barrier_lds();
+        }
+        if (ds0) {  // the gradient of the initial state
+            float *d = ds0 + (size_t)bh * DK * DV;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) d[(size_t)(16 * i + 4 * lg + r) * DV + jt + lr] = S[i][r];
+        }
+    } else if (nc > 0) {
+        // ================= helper wavefront: stages k, q; A' dO and q'(scale exp(G) dO) a chunk ahead
+        const int vt = w - 2, jt = j0 + 16 * vt, ht = tid - 128;
+        const int qk_stride = H * DK * 2;
+        uint4 kreg[8], qreg[8];
+        float gam_reg = 0.f, gnd_reg = 0.f;
+        f32x4 dor[4], gmr[4];   // dO[16 t + 4 lg + e][jt + lr] and exp(G) of those tokens
+        bf16x8 ath[6], atl[6];  // A' fragments
+        auto qk_rsrc = [&](const __bf16 *base, int c) __attribute__((always_inline)) {
+            return rows_rsrc(base + uniform(wk.row0(c)) * DK, uniform(wk.count(c)), qk_stride, DK * 2);
+        };
+        auto load_k = [&](int c) __attribute__((always_inline)) {
+            c = max(c, 0);
+            const auto rk = qk_rsrc(k, c);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) kreg[u] = mx::buf_ld16(rk, (8 * (ht >> 4) + u) * qk_stride + 16 * (ht & 15));
+            const char *r = rec + wk.slot(c) * mx::kRecBytes;
+            gam_reg = reinterpret_cast<const float *>(r + mx::kRecGam)[ht & 63];
+            gnd_reg = reinterpret_cast<const float *>(r + mx::kRecGend)[ht & 63];
+        };
+        auto load_q = [&](int c) __attribute__((always_inline)) {
+            const auto rq = qk_rsrc(q, max(c, 0));
+#pragma unroll
+            for (int u = 0; u < 8; ++u) qreg[u] = mx::buf_ld16(rq, (8 * (ht >> 4) + u) * qk_stride + 16 * (ht & 15));
+        };
+        auto load_d = [&](int c) __attribute__((always_inline)) {
+            c = max(c, 0);
+            const auto ro = rows_rsrc(dO + uniform(wk.row0(c)) * DV, uniform(wk.count(c)), H * DV * 4, DV * 4);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dor[t][e] = buf_in<false>(ro, (16 * t + 4 * lg + e) * H * DV + jt + lr);
+            const char *r = rec + wk.slot(c) * mx::kRecBytes;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) gmr[t] = *reinterpret_cast<const f32x4 *>(r + mx::kRecGam + (16 * t + 4 * lg) * 4);
+            if constexpr (DELTA) {
+                const char *rr = rrev + wk.slot(c) * kRevBytes;
+#pragma unroll
+                for (int f = 0; f < 6; ++f) {
+                    ath[f] = *reinterpret_cast<const bf16x8 *>(rr + kRevAH + f * mx::kFragBytes + lane * 16);
+                    atl[f] = *reinterpret_cast<const bf16x8 *>(rr + kRevAL + f * mx::kFragBytes + lane * 16);
+                }
+            }
+        };
+        // into the buffers of chunk parity b (the data: the chunk last loaded)
+        auto store_rows = [&](__bf16 *dst, const uint4 *src) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = 8 * (ht >> 4) + u;
+                const uint2 *h2 = reinterpret_cast<const uint2 *>(&src[u]);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    *reinterpret_cast<uint2 *>(&dst[i * LDK + mx::kperm_col(ht & 15, hh)]) = h2[hh];
+            }
+        };
+        auto store_k = [&](int b) __attribute__((always_inline)) {
+            store_rows(sm.K[b], kreg);
+            if (ht < C) {
+                sm.Gam[b][ht] = gam_reg;
+                sm.Gend[b][ht] = gnd_reg;
+            }
+        };
+        auto store_q = [&](int b) __attribute__((always_inline)) { store_rows(sm.Q[b], qreg); };
+        // A' dO and q'(scale exp(G) dO) of the chunk whose dO was last loaded, q in Q[b], to buffers b
+        auto compute = [&](int b) __attribute__((always_inline)) {
+            if constexpr (DELTA) {
+                bf16x8 OH[2], OL[2];
+                mx::pair_split(dor[0], dor[1], OH[0], OL[0]);
+                mx::pair_split(dor[2], dor[3], OH[1], OL[1]);
+#pragma unroll
+                for (int M = 0; M < 4; ++M) {
+                    f32x4 acc = z4;
+#pragma unroll
+                    for (int kb = M >> 1; kb < 2; ++kb) {
+                        const int f = upper_frag(M, kb);
+                        acc = mx::mma(ath[f], OH[kb], acc);
+                        acc = mx::mma(ath[f], OL[kb], acc);
+                        acc = mx::mma(atl[f], OH[kb], acc);
+                    }
+                    sm.At[b][vt][M][lane] = acc;
+                }
+            }
+            f32x4 sd[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) sd[t] = scale * gmr[t] * dor[t];
+            bf16x8 DH[2], DL[2];
+            mx::pair_split(sd[0], sd[1], DH[0], DL[0]);
+            mx::pair_split(sd[2], sd[3], DH[1], DL[1]);
+            const __bf16 *sQ = sm.Q[b];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const bf16x8 q0 = mx::kt_operand(sQ, LDK, i, 0, lr, lg), q1 = mx::kt_operand(sQ, LDK, i, 1, lr, lg);
+                f32x4 acc = mx::mma(q0, DH[0], z4);
+                acc = mx::mma(q0, DL[0], acc);
+                acc = mx::mma(q1, DH[1], acc);
+                acc = mx::mma(q1, DL[1], acc);
+                sm.Qd[b][vt][i][lane] = acc;
+            }
+        };
+        // before the first barrier: k, q of chunk L staged; then q of L - 1 and dO of L loaded
+        load_k(L);
+        load_q(L);
+        store_k(L & 1);
+        store_q(L & 1);
+        load_q(L - 1);
+        load_d(L);
+        barrier_lds();
+        // before the second: chunk L's products; q of L - 1 staged
+        compute(L & 1);
+        store_q((L - 1) & 1);
+        load_k(L - 1);
+        load_q(L - 2);
+        load_d(L - 1);
+        barrier_lds();
+        // during the chain's step on chunk c: k of c - 1 and q of c - 2 staged, chunk c - 1's products
+        for (int c = L; c >= 0; --c) {
+            store_k((c - 1) & 1);
+            store_q((c - 2) & 1);
+            compute((c - 1) & 1);
+            load_k(c - 2);
+            load_q(c - 3);
+            load_d(c - 2);
+            barrier_lds();
+        }
     }
 }
 
@@ -2228,7 +2572,7 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
     const unsigned nwalk = (unsigned)(a.B * a.H * (DV / kBV));
     hipLaunchKernelGGL((bwd_prep_kernel<DK, PC, KZ, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.q, a.k, a.g,
                        a.beta, a.T, a.H, a.NC, a.eps, a.scale, w.T, w.A, w.M, w.G, w.beta, w.Kt, w.Kh, w.Qt,
-                       static_cast<char *>(w.rec), a.delta, a.tab);
+                       static_cast<char *>(w.rec), static_cast<char *>(w.rrev), a.delta, a.tab);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (bwd_walk16(ops, DK, DV)) {  // the forward pass's bf16 walk over the records prep wrote
@@ -2262,7 +2606,16 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
                            static_cast<const __bf16 *>(a.v), static_cast<const __bf16 *>(a.k), a.T, a.H, a.NC, w.T,
                            w.G, w.beta, a.s0, w.S, a.delta, a.tab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if constexpr (!ops)  // scalar decay with bf16 inputs: the walk on k and q themselves
+    if constexpr (bwd_walk16(ops, DK, DV)) {  // bf16 tiles, the records prep wrote
+        const __bf16 *qb = static_cast<const __bf16 *>(a.q), *kb = static_cast<const __bf16 *>(a.k);
+        const char *rec = static_cast<const char *>(w.rec), *rrev = static_cast<const char *>(w.rrev);
+        if (a.delta)
+            hipLaunchKernelGGL((bwd_dstates_bf16_kernel<true>), dim3(nwalk), dim3(kThreads), 0, a.stream, qb, kb, a.dO,
+                               a.T, a.H, a.NC, a.scale, rec, rrev, a.ds_final, w.dS, a.ds0, a.tab);
+        else
+            hipLaunchKernelGGL((bwd_dstates_bf16_kernel<false>), dim3(nwalk), dim3(kThreads), 0, a.stream, qb, kb,
+                               a.dO, a.T, a.H, a.NC, a.scale, rec, rrev, a.ds_final, w.dS, a.ds0, a.tab);
+    } else if constexpr (!ops)  // scalar decay with bf16 inputs: the walk on k and q themselves
         hipLaunchKernelGGL((bwd_dstates_kq16_kernel<DK, DV>), dim3(nwalk), dim3(kThreads), 0, a.stream,
                            static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), a.dO, a.T, a.H, a.NC,
                            a.scale, w.T, w.A, w.G, w.beta, a.ds_final, w.dS, a.ds0, a.delta, a.tab);
@@ -2314,7 +2667,7 @@ hipError_t launch_tile_fwd_t(const ChunkArgs &a, int stage) {
     if (stage != 1) {
         GDR_LAUNCH((bwd_prep_kernel<DK, PC, KZ, IB>), dim3((unsigned)slots), dim3(kThreads), a.stream, a.ev0,
                    stage == 0 ? a.ev1 : nullptr, a.q, a.k, a.g, a.beta, a.T, a.H, a.NC, a.eps, a.scale, wT, wA, wM, wG,
-                   wB, wKt, wKh, wQt, nullptr, a.delta, a.tab);
+                   wB, wKt, wKh, wQt, nullptr, nullptr, a.delta, a.tab);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess || stage == 0) return e;
     }

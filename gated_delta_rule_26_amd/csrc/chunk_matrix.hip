@@ -264,13 +264,6 @@ struct alignas(16) TransferSmem {
     float Gend[2][C];
 };
 
-// Column, in the permuted token-major layout, of the 8-byte half hh (0, 1)
-// of key-channel segment seg (8 channels, 0..15).
-__device__ __forceinline__ int kperm_col(int seg, int hh) {
-    const int s = seg & 3;
-    return 32 * (seg >> 2) + 8 * ((2 * s + hh) & 3) + 4 * (s >> 1);
-}
-
 // The walk over the chunks of G = BH * P groups (sequence, head, time
 // segment p): group g = bh * P + p covers chunks [p seg, min(NC, (p+1) seg)).
 // With P = 1 this is the whole sequence.
@@ -454,13 +447,7 @@ __global__ __launch_bounds__(kStateThreads, TRANSFER ? 2 : 1) void state_matrix_
             // k^T fragments (key-channel tile i, token block kb) for the update,
             // read transposed from the token-major k: term e of lane group lg is
             // token 32kb + kperm(lg, e), key channel 16i + lr.  Tile 0 now.
-            auto kt_frag = [&](int i, int kb) {
-                const int col = 32 * (i >> 1) + 8 * (lr & 3) + 4 * (i & 1);  // 16i + 4(lr%4), permuted
-                const int row = 32 * kb + 4 * lg + (lr >> 2);
-                const bf16x4 a = lds_read_tr(&sK[row * LDK + col]);
-                const bf16x4 c = lds_read_tr(&sK[(row + 16) * LDK + col]);
-                return bf16x8{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
-            };
+            auto kt_frag = [&](int i, int kb) { return kt_operand(sK, LDK, i, kb, lr, lg); };
             bf16x8 kt[2][2];
             kt[0][0] = kt_frag(0, 0);
             kt[0][1] = kt_frag(0, 1);

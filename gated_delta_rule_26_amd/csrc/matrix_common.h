@@ -309,6 +309,26 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p) {
     return __builtin_bit_cast(bf16x4, r);
 }
 
+// k and q staged token-major in LDS (rows of ld bf16) with the key channels
+// of each 32-block permuted, so that a 16-byte read at row r, column 32 kb +
+// 8 p holds channels 32 kb + kperm(p, 0..7): the A operand of a product over
+// key channels.  kperm_col: the column of the 8-byte half hh (0, 1) of key
+// channel segment seg (8 channels, 0..15).
+__device__ __forceinline__ int kperm_col(int seg, int hh) {
+    const int s = seg & 3;
+    return 32 * (seg >> 2) + 8 * ((2 * s + hh) & 3) + 4 * (s >> 1);
+}
+// The transposed A operand of that layout (key channel tile i, token block
+// kb): term e of lane group lg is token 32 kb + kperm(lg, e), key channel
+// 16 i + lr, by transposing reads.
+__device__ __forceinline__ bf16x8 kt_operand(const __bf16 *s, int ld, int i, int kb, int lr, int lg) {
+    const int col = 32 * (i >> 1) + 8 * (lr & 3) + 4 * (i & 1);  // 16 i + 4 (lr % 4), permuted
+    const int row = 32 * kb + 4 * lg + (lr >> 2);
+    const bf16x4 a = lds_read_tr(&s[row * ld + col]);
+    const bf16x4 c = lds_read_tr(&s[(row + 16) * ld + col]);
+    return bf16x8{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+}
+
 // Global -> LDS copies without registers (global_load_lds, gfx950): every
 // lane moves 16 (or 4) bytes from its own global address to LDS address
 // M0 + 16 lane (4 lane).  Issued from inline asm, which saves and restores M0:
