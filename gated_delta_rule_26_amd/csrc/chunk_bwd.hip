@@ -1950,6 +1950,322 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
     }
 }
 
+// ---- grads A on bf16 tiles (scalar decay, bf16 inputs, d_k = d_v = 128): the products of the kernel
+// above with every fp32 operand split into bf16 hi + lo (hi*hi + hi*lo + lo*hi; k and v exact), in
+// slices of 32 value columns.  A slice's operands live in LDS as bf16 hi and lo arrays in [value][row]
+// orientation (the S and dS' slices: rows = key channels; dO, X, dE, E, dX: rows = tokens), so that a
+// product reducing over rows reads its B operand with plain 8-byte reads (rows_operand) and one reducing
+// over the 32 values reads its operands with transposing reads (vals_operand).  This wavefront's rows of
+// k (A operand over channels, exact), of T'' (lower) and of T''' and A' (upper) stay in registers, the
+// fragments from the walks' records.  Four barriers per slice: slice operands staged; X, dE; E, dX; the
+// value-axis accumulations done.
+constexpr int kSW = 32;           // value columns per slice
+constexpr int kLSK = mx::DK + 8;  // bf16 pitch of the [value][channel] arrays
+constexpr int kLST = C + 8;       // bf16 pitch of the [value][token] arrays
+
+struct alignas(16) GradsSmem {
+    __bf16 S[2][kSW * kLSK], dS[2][kSW * kLSK];  // [hi, lo][value][channel]
+    __bf16 O[2][kSW * kLST], X[2][kSW * kLST], dE[2][kSW * kLST], E[2][kSW * kLST], dX[2][kSW * kLST];
+    float gsum[mx::DK];  // per key channel: sum over values of dS' S
+    float H[4][mx::DK];  // per wavefront: column sums of dK^ K^
+};
+
+// B operand reducing over the rows of a [value][row] array: value column 16 vt + lr, rows 32 kb + kperm(lg, e).
+__device__ __forceinline__ mx::bf16x8 rows_operand(const __bf16 *s, int ld, int vt, int kb, int lr, int lg) {
+    const __bf16 *p = s + (16 * vt + lr) * ld + 32 * kb + 4 * lg;
+    const uint2 a = *reinterpret_cast<const uint2 *>(p), b = *reinterpret_cast<const uint2 *>(p + 16);
+    return __builtin_bit_cast(mx::bf16x8, uint4{a.x, a.y, b.x, b.y});
+}
+// Operand reducing over the slice's values: row 16 m + lr of a [value][row] array, values kperm(lg, e)
+// (the A operand of rows 16 m .., or the B operand of their transpose).
+__device__ __forceinline__ mx::bf16x8 vals_operand(const __bf16 *s, int ld, int m, int lr, int lg) {
+    const __bf16 *p = s + (4 * lg + (lr >> 2)) * ld + 16 * m + 4 * (lr & 3);
+    const mx::bf16x4 a = mx::lds_read_tr(p), c = mx::lds_read_tr(p + 16 * ld);
+    return mx::bf16x8{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+}
+// A D tile (rows 16 m + 4 lg + r, value column 16 vt + lr) into a [value][row] array as bf16 hi and lo.
+__device__ __forceinline__ void store_tile(__bf16 *hi, __bf16 *lo, int m, int vt, f32x4 d, int lr, int lg) {
+    uint32_t h0, l0, h1, l1;
+    mx::split2(d[0], d[1], h0, l0);
+    mx::split2(d[2], d[3], h1, l1);
+    const int off = (16 * vt + lr) * kLST + 16 * m + 4 * lg;
+    *reinterpret_cast<uint2 *>(hi + off) = uint2{h0, h1};
+    *reinterpret_cast<uint2 *>(lo + off) = uint2{l0, l1};
+}
+__device__ __forceinline__ f32x4 mma3(mx::bf16x8 ah, mx::bf16x8 al, mx::bf16x8 bh, mx::bf16x8 bl, f32x4 c) {
+    c = mx::mma(ah, bh, c);
+    c = mx::mma(ah, bl, c);
+    return mx::mma(al, bh, c);
+}
+__device__ __forceinline__ mx::bf16x8 neg8(mx::bf16x8 x) {
+    uint4 u = __builtin_bit_cast(uint4, x);
+    u.x ^= 0x80008000u;
+    u.y ^= 0x80008000u;
+    u.z ^= 0x80008000u;
+    u.w ^= 0x80008000u;
+    return __builtin_bit_cast(mx::bf16x8, u);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void bwd_grads_a16_kernel(
+    const __bf16 *__restrict__ v, const float *__restrict__ dO, const __bf16 *__restrict__ kin,
+    const __bf16 *__restrict__ qin, int T, int H, int NC, float scale, const float *__restrict__ wG,
+    const char *__restrict__ rec, const char *__restrict__ rrev, const float *__restrict__ wS,
+    const float *__restrict__ wdS, float *__restrict__ wdA, float *__restrict__ wdTT, float *__restrict__ wdG,
+    float *__restrict__ wdG63, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv, bool delta,
+    SeqTable tb) {
+    using mx::bf16x8;
+    constexpr int DK = mx::DK, DV = mx::DV, JK = DK / 16;
+    const int ci = blockIdx.x;
+    if (!slot_used(ci, H, tb)) return;
+    const Slot sl = slot_of(ci, T, H, NC, tb);
+    const int n = sl.n;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    __shared__ GradsSmem sm;
+    const size_t row0u = uniform(sl.row0);
+    const int nu = uniform(n);
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+
+    // this wavefront's k rows as the A operand over channels: kA[kb] = k[16 w + lr][32 kb + kperm(lg, e)]
+    bf16x8 kA[4];
+    {
+        const auto rk = rows_rsrc(kin + row0u * DK, nu, H * DK * 2, DK * 2);
+        const int base = (16 * w + lr) * H * DK + 4 * lg;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const auto a = __builtin_amdgcn_raw_buffer_load_b64(rk, (base + 32 * kb) * 2, 0, 0);
+            const auto b = __builtin_amdgcn_raw_buffer_load_b64(rk, (base + 32 * kb + 16) * 2, 0, 0);
+            kA[kb] = __builtin_bit_cast(bf16x8, uint4{a[0], a[1], b[0], b[1]});
+        }
+    }
+    // token factors of this lane's D-tile rows and the record fragments of rows 16 w ..: T'' (lower,
+    // token blocks kb <= w / 2), T''' and A' (upper, kb >= w / 2); every load issued, unused ones unread
+    const char *rc = rec + (size_t)ci * mx::kRecBytes;
+    const char *rr = rrev + (size_t)ci * kRevBytes;
+    const f32x4 gam = *reinterpret_cast<const f32x4 *>(rc + mx::kRecGam + (16 * w + 4 * lg) * 4);
+    const f32x4 gnd = *reinterpret_cast<const f32x4 *>(rc + mx::kRecGend + (16 * w + 4 * lg) * 4);
+    bf16x8 tlh[2], tll[2], tuh[2], tul[2], auh[2], aul[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int fl = mx::lower_frag(w, min(kb, w >> 1)), fu = upper_frag(w, max(kb, w >> 1));
+        tlh[kb] = *reinterpret_cast<const bf16x8 *>(rc + mx::kRecTH + fl * mx::kFragBytes + lane * 16);
+        tll[kb] = *reinterpret_cast<const bf16x8 *>(rc + mx::kRecTL + fl * mx::kFragBytes + lane * 16);
+        tuh[kb] = *reinterpret_cast<const bf16x8 *>(rr + kRevTH + fu * mx::kFragBytes + lane * 16);
+        tul[kb] = *reinterpret_cast<const bf16x8 *>(rr + kRevTL + fu * mx::kFragBytes + lane * 16);
+        auh[kb] = *reinterpret_cast<const bf16x8 *>(rr + kRevAH + fu * mx::kFragBytes + lane * 16);
+        aul[kb] = *reinterpret_cast<const bf16x8 *>(rr + kRevAL + fu * mx::kFragBytes + lane * 16);
+    }
+
+    f32x4 aQ[JK], aKt[JK], aKh[JK], aA[4], aT[4];
+#pragma unroll
+    for (int J = 0; J < JK; ++J) aQ[J] = aKt[J] = aKh[J] = z4;
+#pragma unroll
+    for (int J = 0; J < 4; ++J) aA[J] = aT[J] = z4;
+
+    // slice loads: thread t takes value column j0 + (t % 32); for S and dS' key channels 16 (t / 32) + m,
+    // for dO tokens 8 (t / 32) + m; v in this wavefront's D-tile layout
+    const int sv = tid & 31, sg = tid >> 5;
+    const float *Sg = wS + (size_t)ci * DK * DV, *dSg = wdS + (size_t)ci * DK * DV;
+    const auto r_o = rows_rsrc(dO + row0u * DV, nu, H * DV * 4, DV * 4);
+    const auto r_v = rows_rsrc(v + row0u * DV, nu, H * DV * 2, DV * 2);
+    const auto r_dv = rows_rsrc(dv + row0u * DV, nu, H * DV * 4, DV * 4);
+    float rS[16], rdS[16], rO[8], gpart[16];
+    f32x4 rV[2];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) gpart[m] = 0.f;
+    auto fetch = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            rS[m] = Sg[(16 * sg + m) * DV + j0 + sv];
+            rdS[m] = dSg[(16 * sg + m) * DV + j0 + sv];
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) rO[m] = buf_in<false>(r_o, (8 * sg + m) * H * DV + j0 + sv);
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rV[vt][r] = buf_in<true>(r_v, (16 * w + 4 * lg + r) * H * DV + j0 + 16 * vt + lr);
+    };
+    fetch(0);
+    for (int j0 = 0; j0 < DV; j0 += kSW) {
+        if (j0) barrier_lds();  // the previous slice's operands are no longer read
+        // ---- the slice's S, dS' and dO to LDS as bf16 hi, lo; the next slice's loads
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) {
+            uint32_t h0, l0, h1, l1;
+            const int off = sv * kLSK + 16 * sg + 4 * m4;
+            mx::split2(rS[4 * m4], rS[4 * m4 + 1], h0, l0);
+            mx::split2(rS[4 * m4 + 2], rS[4 * m4 + 3], h1, l1);
+            *reinterpret_cast<uint2 *>(&sm.S[0][off]) = uint2{h0, h1};
+            *reinterpret_cast<uint2 *>(&sm.S[1][off]) = uint2{l0, l1};
+            mx::split2(rdS[4 * m4], rdS[4 * m4 + 1], h0, l0);
+            mx::split2(rdS[4 * m4 + 2], rdS[4 * m4 + 3], h1, l1);
+            *reinterpret_cast<uint2 *>(&sm.dS[0][off]) = uint2{h0, h1};
+            *reinterpret_cast<uint2 *>(&sm.dS[1][off]) = uint2{l0, l1};
+        }
+#pragma unroll
+        for (int m = 0; m < 16; ++m) gpart[m] += rdS[m] * rS[m];
+#pragma unroll
+        for (int m4 = 0; m4 < 2; ++m4) {
+            uint32_t h0, l0, h1, l1;
+            const int off = sv * kLST + 8 * sg + 4 * m4;
+            mx::split2(rO[4 * m4], rO[4 * m4 + 1], h0, l0);
+            mx::split2(rO[4 * m4 + 2], rO[4 * m4 + 3], h1, l1);
+            *reinterpret_cast<uint2 *>(&sm.O[0][off]) = uint2{h0, h1};
+            *reinterpret_cast<uint2 *>(&sm.O[1][off]) = uint2{l0, l1};
+        }
+        const f32x4 vv[2] = {rV[0], rV[1]};
+        fetch(min(j0 + kSW, DV - kSW));
+        barrier_lds();
+        // ---- X = V - exp(G) (k S),  dE = exp(G_63 - G) (k dS') + A' dO  (two value tiles)
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt) {
+            f32x4 ps = z4, pd = z4;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                if (delta) {
+                    ps = mx::mma(kA[kb], rows_operand(sm.S[0], kLSK, vt, kb, lr, lg), ps);
+                    ps = mx::mma(kA[kb], rows_operand(sm.S[1], kLSK, vt, kb, lr, lg), ps);
+                }
+                pd = mx::mma(kA[kb], rows_operand(sm.dS[0], kLSK, vt, kb, lr, lg), pd);
+                pd = mx::mma(kA[kb], rows_operand(sm.dS[1], kLSK, vt, kb, lr, lg), pd);
+            }
+            f32x4 de = gnd * pd;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                if (kb >= (w >> 1))
+                    de = mma3(auh[kb], aul[kb], rows_operand(sm.O[0], kLST, vt, kb, lr, lg),
+                              rows_operand(sm.O[1], kLST, vt, kb, lr, lg), de);
+            const f32x4 x = vv[vt] - gam * ps;
+            store_tile(sm.X[0], sm.X[1], w, vt, x, lr, lg);
+            store_tile(sm.dE[0], sm.dE[1], w, vt, de, lr, lg);
+        }
+        barrier_lds();
+        // ---- E = T'' X (token blocks kb <= w / 2),  dX = T''' dE (kb >= w / 2) = dV
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt) {
+            f32x4 ee = z4, dx = z4;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (kb <= (w >> 1))
+                    ee = mma3(tlh[kb], tll[kb], rows_operand(sm.X[0], kLST, vt, kb, lr, lg),
+                              rows_operand(sm.X[1], kLST, vt, kb, lr, lg), ee);
+                if (kb >= (w >> 1))
+                    dx = mma3(tuh[kb], tul[kb], rows_operand(sm.dE[0], kLST, vt, kb, lr, lg),
+                              rows_operand(sm.dE[1], kLST, vt, kb, lr, lg), dx);
+            }
+            store_tile(sm.E[0], sm.E[1], w, vt, ee, lr, lg);
+            store_tile(sm.dX[0], sm.dX[1], w, vt, dx, lr, lg);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dx[r]), r_dv,
+                                                      ((16 * w + 4 * lg + r) * H * DV + j0 + 16 * vt + lr) * 4, 0, 0);
+        }
+        barrier_lds();
+        // ---- over the slice's values: dQ~ += dO S',  dK~ -= dX S',  dK^ += E dS'',  dA += dO E',  dT'' += dE X'
+        {
+            const bf16x8 oh = vals_operand(sm.O[0], kLST, w, lr, lg), ol = vals_operand(sm.O[1], kLST, w, lr, lg);
+            const bf16x8 eh = vals_operand(sm.E[0], kLST, w, lr, lg), el = vals_operand(sm.E[1], kLST, w, lr, lg);
+            const bf16x8 xh = neg8(vals_operand(sm.dX[0], kLST, w, lr, lg));
+            const bf16x8 xl = neg8(vals_operand(sm.dX[1], kLST, w, lr, lg));
+            const bf16x8 dh = vals_operand(sm.dE[0], kLST, w, lr, lg), dl = vals_operand(sm.dE[1], kLST, w, lr, lg);
+#pragma unroll
+            for (int J = 0; J < JK; ++J) {
+                const bf16x8 sh = vals_operand(sm.S[0], kLSK, J, lr, lg), slo = vals_operand(sm.S[1], kLSK, J, lr, lg);
+                const bf16x8 th = vals_operand(sm.dS[0], kLSK, J, lr, lg), tl = vals_operand(sm.dS[1], kLSK, J, lr, lg);
+                aQ[J] = mma3(oh, ol, sh, slo, aQ[J]);
+                if (delta) aKt[J] = mma3(xh, xl, sh, slo, aKt[J]);
+                aKh[J] = mma3(eh, el, th, tl, aKh[J]);
+            }
+#pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                if (J > w) continue;
+                aA[J] = mma3(oh, ol, vals_operand(sm.E[0], kLST, J, lr, lg), vals_operand(sm.E[1], kLST, J, lr, lg),
+                             aA[J]);
+                if (delta)
+                    aT[J] = mma3(dh, dl, vals_operand(sm.X[0], kLST, J, lr, lg), vals_operand(sm.X[1], kLST, J, lr, lg),
+                                 aT[J]);
+            }
+        }
+    }
+    // dgam per channel: the sums over this thread's value column, then over the 32 columns (half a wavefront)
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        float s = gpart[m];
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) s += __shfl_xor(s, o, 64);
+        gpart[m] = s;
+    }
+    if (sv == 0) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m) sm.gsum[16 * sg + m] = gpart[m];
+    }
+
+    // dA, dT'' (lower triangle incl. the diagonal) to the workspace
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * w + 4 * lg + r, m = 16 * J + lr;
+            wdA[(size_t)ci * C * C + i * C + m] = m <= i ? aA[J][r] : 0.f;
+            wdTT[(size_t)ci * C * C + i * C + m] = m <= i ? aT[J][r] : 0.f;
+        }
+    // parts of dq, dk through Q~, K~, K^ (rows past the end are not written); parts of dG:
+    // dK~ K~ + dQ~ Q~ - dK^ K^ over the channels; for G_63 also sum_i dK^ K^ + dgam gam
+    const float *Gc = wG + (size_t)ci * C;
+    const float ge = Gc[C - 1];
+    const auto rkq = rows_rsrc(kin + row0u * DK, nu, H * DK * 2, DK * 2);
+    const auto rqq = rows_rsrc(qin + row0u * DK, nu, H * DK * 2, DK * 2);
+    float rowpart[4] = {0.f, 0.f, 0.f, 0.f};
+    float colh[JK];
+#pragma unroll
+    for (int J = 0; J < JK; ++J) {
+        colh[J] = 0.f;
+        const int ch = 16 * J + lr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * w + 4 * lg + r;
+            const float ei = gam[r], eh = gnd[r];
+            const float kv = buf_in<true>(rkq, i * H * DK + ch), qv = buf_in<true>(rqq, i * H * DK + ch);
+            if (i < n) {
+                const size_t off = (sl.row0 + (size_t)i * H) * DK + ch;
+                dq[off] = scale * ei * aQ[J][r];
+                dk[off] = ei * aKt[J][r] + eh * aKh[J][r];
+            }
+            const float khv = eh * kv;
+            rowpart[r] += aKt[J][r] * (ei * kv) + aQ[J][r] * (scale * ei * qv) - aKh[J][r] * khv;
+            colh[J] += aKh[J][r] * khv;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {  // sum over the 16 lanes of a row group, then one lane writes each row
+        float sum = rowpart[r];
+        sum += __shfl_xor(sum, 1, 64);
+        sum += __shfl_xor(sum, 2, 64);
+        sum += __shfl_xor(sum, 4, 64);
+        sum += __shfl_xor(sum, 8, 64);
+        if (lr == 0) wdG[(size_t)ci * C + 16 * w + 4 * lg + r] = sum;
+    }
+#pragma unroll
+    for (int J = 0; J < JK; ++J) {
+        float sum = colh[J];
+        sum += __shfl_xor(sum, 16, 64);
+        sum += __shfl_xor(sum, 32, 64);
+        if (lg == 0) sm.H[w][16 * J + lr] = sum;
+    }
+    __syncthreads();
+    if (tid < DK)
+        sm.H[0][tid] = ((sm.H[0][tid] + sm.H[1][tid]) + (sm.H[2][tid] + sm.H[3][tid])) + sm.gsum[tid] * __expf(ge);
+    __syncthreads();
+    if (w == 0) {  // the sum over channels
+        float s = 0.f;
+        for (int cc = lane; cc < DK; cc += 64) s += sm.H[0][cc];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+        if (lane == 0) wdG63[ci] = s;
+    }
+}
+
 // ============================================================ grads B: triangular algebra and pair terms
 // One workgroup per chunk, four wavefronts (wavefront w: rows 16w .. of the
 // C x C and C x DK products, on fp32 matrix-core tiles).  dbeta from dT'';
@@ -2623,10 +2939,17 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
         hipLaunchKernelGGL((bwd_dstates_kernel<DK, DV, PC>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.dO, a.T,
                            a.H, a.NC, w.T, w.A, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.ds_final, w.dS, a.ds0, a.delta, a.tab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_grads_a_kernel<DK, DV, PC, IB, !ops>), dim3(nslot), dim3(kThreads), 0, a.stream, a.v,
-                       a.dO, a.T, a.H, a.NC, a.scale, w.T, w.A, w.G, w.beta, w.S, w.dS, w.Kt, w.Kh, w.Qt,
-                       static_cast<const __bf16 *>(a.k), static_cast<const __bf16 *>(a.q), w.dA, w.dTT, w.dG, w.dG63,
-                       a.dq, a.dk, a.dv, a.delta, a.tab);
+    if constexpr (bwd_walk16(ops, DK, DV))
+        hipLaunchKernelGGL(bwd_grads_a16_kernel, dim3(nslot), dim3(kThreads), 0, a.stream,
+                           static_cast<const __bf16 *>(a.v), a.dO, static_cast<const __bf16 *>(a.k),
+                           static_cast<const __bf16 *>(a.q), a.T, a.H, a.NC, a.scale, w.G,
+                           static_cast<const char *>(w.rec), static_cast<const char *>(w.rrev), w.S, w.dS, w.dA, w.dTT,
+                           w.dG, w.dG63, a.dq, a.dk, a.dv, a.delta, a.tab);
+    else
+        hipLaunchKernelGGL((bwd_grads_a_kernel<DK, DV, PC, IB, !ops>), dim3(nslot), dim3(kThreads), 0, a.stream,
+                           a.v, a.dO, a.T, a.H, a.NC, a.scale, w.T, w.A, w.G, w.beta, w.S, w.dS, w.Kt, w.Kh, w.Qt,
+                           static_cast<const __bf16 *>(a.k), static_cast<const __bf16 *>(a.q), w.dA, w.dTT, w.dG,
+                           w.dG63, a.dq, a.dk, a.dv, a.delta, a.tab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grads_b_kernel<DK, PC, KZ, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.q, a.k,
                        a.T, a.H, a.NC, a.eps, a.scale, w.T, w.M, w.A, w.G, w.beta, w.dA, w.dTT, w.dG, w.dG63, a.dq,

@@ -14,9 +14,22 @@ pytestmark = pytest.mark.gpu
 MODES = {"gdn": dict(per_channel=False, kaczmarz=False),
          "kda": dict(per_channel=True, kaczmarz=False),
          "kla": dict(per_channel=False, kaczmarz=True)}
-# fp32 arithmetic on inputs that are exact in fp32, the bar of the fp32
-# forward path (measured: 1e-7 .. 2e-6 relative L2 on these cases)
+# fp32 arithmetic on inputs that are exact in fp32 (fp32 inputs, per-channel
+# decay, d = 64): the bar of the fp32 forward path (measured: 1e-7 .. 5e-7
+# relative L2 on these cases)
 TOL_BWD = 1e-5
+# bf16 inputs with scalar decay at d_k = d_v = 128 run on bf16 tiles, as the
+# forward pass's matrix path does: a product of fp32 values taken as bf16
+# hi/lo pairs (hi*hi + hi*lo + lo*hi) keeps about 16 significant bits, so each
+# is exact to about 2^-16 = 1.5e-5 relative at worst.  The bar for bf16
+# inputs is the forward pass's, 2e-3; this is a 1e-4 sentinel under it
+# (measured: 2e-6 .. 3e-5, the largest on a one-token sequence's dg).
+TOL_BWD16 = 1e-4
+
+
+def _tol(mode, dtype, D=(128, 128)):
+    tile16 = dtype == "bf16" and D == (128, 128) and mode not in ("kda", "gla")
+    return TOL_BWD16 if tile16 else TOL_BWD
 
 
 def _case(seed, B, T, H, D, mode, dtype, *, with_ds=True):
@@ -47,7 +60,7 @@ def test_backward_parity(T, mode):
     x = _case(6000 + T, 2, T, 2, (128, 128), mode, "bf16")
     errs = _run(x, mode, "bf16")
     print(f"backward {mode} T={T}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
-    assert all(v < TOL_BWD for v in errs.values()), errs
+    assert all(v < _tol(mode, "bf16") for v in errs.values()), errs
 
 
 @pytest.mark.parametrize("D", [(64, 64), (64, 128), (128, 64)])
@@ -56,7 +69,7 @@ def test_backward_widths_fp32_inputs_and_scale(D, mode):
     x = _case(6100, 1, 90, 3, D, mode, "f32")
     errs = _run(x, mode, "f32", scale=D[0] ** -0.5)
     print(f"backward {mode} D={D} f32: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
-    assert all(v < TOL_BWD for v in errs.values()), errs
+    assert all(v < _tol(mode, "f32", D) for v in errs.values()), errs
 
 
 @pytest.mark.parametrize("mode", ["gdn", "kda"])
@@ -70,7 +83,7 @@ def test_backward_strong_decay_and_no_final_gradient(mode):
     x["g"] = g
     errs = _run(x, mode, "bf16")
     print(f"backward strong decay {mode}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
-    assert all(v < TOL_BWD for v in errs.values()), errs
+    assert all(v < _tol(mode, "bf16") for v in errs.values()), errs
 
 
 def test_backward_deterministic_and_zero_length():
@@ -110,7 +123,7 @@ def test_backward_without_delta_rule(variant, T):
     assert g["dbeta"] is None
     errs = {key: rel(host(g[key]), ref[key]) for key in ("dq", "dk", "dv", "dg", "ds0")}
     print(f"backward no delta {variant} T={T}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
-    assert all(v < TOL_BWD for v in errs.values()), errs
+    assert all(v < _tol(variant, "bf16") for v in errs.values()), errs
 
 
 @pytest.mark.parametrize("name,nheads", [("gdn_prefill", 2), ("kda_prefill", 1)])
@@ -137,7 +150,7 @@ def test_backward_full_workload_sampled(name, nheads):
         ref = oracle_bwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], do[b:b + 1, :, h:h + 1], **m)
         errs = {key: rel(host(g[key][b:b + 1, :, h:h + 1]), ref[key]) for key in ("dq", "dk", "dv", "dg", "dbeta")}
         print(f"backward full workload {name} (b={b}, h={h}): " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
-        assert all(v < TOL_BWD for v in errs.values()), errs
+        assert all(v < _tol("kda" if w.per_channel else "gdn", w.dtype) for v in errs.values()), errs
 
 
 def _packed_case(seed, lens, H, D, mode):
@@ -182,4 +195,4 @@ def test_backward_varlen_matches_each_sequence_alone(mode):
         errs["ds0"] = rel(host(g["ds0"][n]), ref["ds0"][0])
         print(f"backward varlen {mode} sequence {n} (length {b - a}): "
               + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
-        assert all(v < TOL_BWD for v in errs.values()), (n, errs)
+        assert all(v < _tol(mode, "bf16") for v in errs.values()), (n, errs)
