@@ -1952,32 +1952,37 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
 
 // ---- grads A on bf16 tiles (scalar decay, bf16 inputs, d_k = d_v = 128): the products of the kernel
 // above with every fp32 operand split into bf16 hi + lo (hi*hi + hi*lo + lo*hi; k and v exact), in
-// slices of 32 value columns.  A slice's operands live in LDS as bf16 hi and lo arrays in [value][row]
-// orientation (the S and dS' slices: rows = key channels; dO, X, dE, E, dX: rows = tokens), so that a
-// product reducing over rows reads its B operand with plain 8-byte reads (rows_operand) and one reducing
-// over the 32 values reads its operands with transposing reads (vals_operand).  This wavefront's rows of
+// slices of 32 value columns.  A slice's operands live in LDS as bf16 hi and lo arrays: the S, dS' and dO
+// slices as they are in memory ([row][value], 16-byte loads), X, dE, E and dX, which arrive as D tiles, in
+// [value][row] orientation.  Every operand read is then one of two kinds: 8-byte reads along an array's
+// rows (rows_operand), or transposing reads across them (vals_operand), whichever orientation the product
+// reduces over.  This wavefront's rows of
 // k (A operand over channels, exact), of T'' (lower) and of T''' and A' (upper) stay in registers, the
 // fragments from the walks' records.  Four barriers per slice: slice operands staged; X, dE; E, dX; the
-// value-axis accumulations done.
+// value-axis accumulations done.  Eight wavefronts: wavefront w takes token rows 16 (w % 4) .., value
+// tile w / 4 of each slice's 32 columns, channel tiles 4 (w / 4) .. of the value-axis accumulations, and
+// dA (w < 4) or dT'' (w >= 4).
 constexpr int kSW = 32;           // value columns per slice
-constexpr int kLSK = mx::DK + 8;  // bf16 pitch of the [value][channel] arrays
+constexpr int kLSV = kSW + 8;     // bf16 pitch of the [row][value] arrays
 constexpr int kLST = C + 8;       // bf16 pitch of the [value][token] arrays
 
 struct alignas(16) GradsSmem {
-    __bf16 S[2][kSW * kLSK], dS[2][kSW * kLSK];  // [hi, lo][value][channel]
-    __bf16 O[2][kSW * kLST], X[2][kSW * kLST], dE[2][kSW * kLST], E[2][kSW * kLST], dX[2][kSW * kLST];
+    __bf16 S[2][mx::DK * kLSV], dS[2][mx::DK * kLSV];  // [hi, lo][key channel][value]
+    __bf16 O[2][C * kLSV];                              // [hi, lo][token][value]
+    __bf16 X[2][kSW * kLST], dE[2][kSW * kLST], E[2][kSW * kLST], dX[2][kSW * kLST];  // [hi, lo][value][token]
     float gsum[mx::DK];  // per key channel: sum over values of dS' S
-    float H[4][mx::DK];  // per wavefront: column sums of dK^ K^
+    float H[4][mx::DK];  // per token block: column sums of dK^ K^
+    float rowp[2][C];    // per half of the channels: the token rows' parts of dG
 };
 
-// B operand reducing over the rows of a [value][row] array: value column 16 vt + lr, rows 32 kb + kperm(lg, e).
+// Along the rows of an array (pitch ld): row 16 vt + lr, columns 32 kb + kperm(lg, e).
 __device__ __forceinline__ mx::bf16x8 rows_operand(const __bf16 *s, int ld, int vt, int kb, int lr, int lg) {
     const __bf16 *p = s + (16 * vt + lr) * ld + 32 * kb + 4 * lg;
     const uint2 a = *reinterpret_cast<const uint2 *>(p), b = *reinterpret_cast<const uint2 *>(p + 16);
     return __builtin_bit_cast(mx::bf16x8, uint4{a.x, a.y, b.x, b.y});
 }
-// Operand reducing over the slice's values: row 16 m + lr of a [value][row] array, values kperm(lg, e)
-// (the A operand of rows 16 m .., or the B operand of their transpose).
+// Across the rows, by transposing reads: column 16 m + lr, rows kperm(lg, e) of the 32 from s.  As an A
+// operand, rows 16 m .. of the transpose; as a B operand, reduction over the rows.
 __device__ __forceinline__ mx::bf16x8 vals_operand(const __bf16 *s, int ld, int m, int lr, int lg) {
     const __bf16 *p = s + (4 * lg + (lr >> 2)) * ld + 16 * m + 4 * (lr & 3);
     const mx::bf16x4 a = mx::lds_read_tr(p), c = mx::lds_read_tr(p + 16 * ld);
@@ -2006,7 +2011,9 @@ __device__ __forceinline__ mx::bf16x8 neg8(mx::bf16x8 x) {
     return __builtin_bit_cast(mx::bf16x8, u);
 }
 
-__global__ __launch_bounds__(kThreads, 1) void bwd_grads_a16_kernel(
+constexpr int kThreads16 = 512;  // eight wavefronts
+
+__global__ __launch_bounds__(kThreads16, 1) void bwd_grads_a16_kernel(
     const __bf16 *__restrict__ v, const float *__restrict__ dO, const __bf16 *__restrict__ kin,
     const __bf16 *__restrict__ qin, int T, int H, int NC, float scale, const float *__restrict__ wG,
     const char *__restrict__ rec, const char *__restrict__ rrev, const float *__restrict__ wS,
@@ -2014,12 +2021,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grads_a16_kernel(
     float *__restrict__ wdG63, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv, bool delta,
     SeqTable tb) {
     using mx::bf16x8;
-    constexpr int DK = mx::DK, DV = mx::DV, JK = DK / 16;
+    constexpr int DK = mx::DK, DV = mx::DV, JH = DK / 32;  // channel tiles per half
     const int ci = blockIdx.x;
     if (!slot_used(ci, H, tb)) return;
     const Slot sl = slot_of(ci, T, H, NC, tb);
     const int n = sl.n;
-    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w = wv & 3, h = wv >> 2;  // token rows 16 w .., value tile h of a slice, channel tiles 4 h ..
     const int lr = lane & 15, lg = lane >> 4;
     __shared__ GradsSmem sm;
     const size_t row0u = uniform(sl.row0);
@@ -2056,94 +2064,83 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grads_a16_kernel(
         aul[kb] = *reinterpret_cast<const bf16x8 *>(rr + kRevAL + fu * mx::kFragBytes + lane * 16);
     }
 
-    f32x4 aQ[JK], aKt[JK], aKh[JK], aA[4], aT[4];
+    // channel tiles 4 h + J of dQ~, dK~, dK^; dA (h = 0) or dT'' (h = 1), token tiles J <= w
+    f32x4 aQ[JH], aKt[JH], aKh[JH], aM[4];
 #pragma unroll
-    for (int J = 0; J < JK; ++J) aQ[J] = aKt[J] = aKh[J] = z4;
+    for (int J = 0; J < JH; ++J) aQ[J] = aKt[J] = aKh[J] = z4;
 #pragma unroll
-    for (int J = 0; J < 4; ++J) aA[J] = aT[J] = z4;
+    for (int J = 0; J < 4; ++J) aM[J] = z4;
 
-    // slice loads: thread t takes value column j0 + (t % 32); for S and dS' key channels 16 (t / 32) + m,
-    // for dO tokens 8 (t / 32) + m; v in this wavefront's D-tile layout
-    const int sv = tid & 31, sg = tid >> 5;
+    // slice loads, 16 bytes per lane: thread t takes values j0 + 4 (t % 8) .. +3 of key channels t / 8 and
+    // 64 + t / 8 (S, dS') and of token t / 8 (dO); v in this wavefront's D-tile layout (value tile h)
+    const int sq = 4 * (tid & 7), sr = tid >> 3;
     const float *Sg = wS + (size_t)ci * DK * DV, *dSg = wdS + (size_t)ci * DK * DV;
     const auto r_o = rows_rsrc(dO + row0u * DV, nu, H * DV * 4, DV * 4);
     const auto r_v = rows_rsrc(v + row0u * DV, nu, H * DV * 2, DV * 2);
     const auto r_dv = rows_rsrc(dv + row0u * DV, nu, H * DV * 4, DV * 4);
-    float rS[16], rdS[16], rO[8], gpart[16];
-    f32x4 rV[2];
-#pragma unroll
-    for (int m = 0; m < 16; ++m) gpart[m] = 0.f;
+    f32x4 rS[2], rdS[2], rO, rV;
+    float gpart[2] = {0.f, 0.f};
     auto fetch = [&](int j0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            rS[m] = Sg[(16 * sg + m) * DV + j0 + sv];
-            rdS[m] = dSg[(16 * sg + m) * DV + j0 + sv];
+        for (int u = 0; u < 2; ++u) {
+            rS[u] = *reinterpret_cast<const f32x4 *>(&Sg[(sr + 64 * u) * DV + j0 + sq]);
+            rdS[u] = *reinterpret_cast<const f32x4 *>(&dSg[(sr + 64 * u) * DV + j0 + sq]);
         }
+        rO = __builtin_bit_cast(f32x4, mx::buf_ld16(r_o, (sr * H * DV + j0 + sq) * 4));
 #pragma unroll
-        for (int m = 0; m < 8; ++m) rO[m] = buf_in<false>(r_o, (8 * sg + m) * H * DV + j0 + sv);
-#pragma unroll
-        for (int vt = 0; vt < 2; ++vt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) rV[vt][r] = buf_in<true>(r_v, (16 * w + 4 * lg + r) * H * DV + j0 + 16 * vt + lr);
+        for (int r = 0; r < 4; ++r) rV[r] = buf_in<true>(r_v, (16 * w + 4 * lg + r) * H * DV + j0 + 16 * h + lr);
+    };
+    auto stage4 = [&](__bf16 *hi, __bf16 *lo, int off, f32x4 x) __attribute__((always_inline)) {
+        uint32_t h0, l0, h1, l1;
+        mx::split2(x[0], x[1], h0, l0);
+        mx::split2(x[2], x[3], h1, l1);
+        *reinterpret_cast<uint2 *>(hi + off) = uint2{h0, h1};
+        *reinterpret_cast<uint2 *>(lo + off) = uint2{l0, l1};
     };
     fetch(0);
     for (int j0 = 0; j0 < DV; j0 += kSW) {
         if (j0) barrier_lds();  // the previous slice's operands are no longer read
         // ---- the slice's S, dS' and dO to LDS as bf16 hi, lo; the next slice's loads
 #pragma unroll
-        for (int m4 = 0; m4 < 4; ++m4) {
-            uint32_t h0, l0, h1, l1;
-            const int off = sv * kLSK + 16 * sg + 4 * m4;
-            mx::split2(rS[4 * m4], rS[4 * m4 + 1], h0, l0);
-            mx::split2(rS[4 * m4 + 2], rS[4 * m4 + 3], h1, l1);
-            *reinterpret_cast<uint2 *>(&sm.S[0][off]) = uint2{h0, h1};
-            *reinterpret_cast<uint2 *>(&sm.S[1][off]) = uint2{l0, l1};
-            mx::split2(rdS[4 * m4], rdS[4 * m4 + 1], h0, l0);
-            mx::split2(rdS[4 * m4 + 2], rdS[4 * m4 + 3], h1, l1);
-            *reinterpret_cast<uint2 *>(&sm.dS[0][off]) = uint2{h0, h1};
-            *reinterpret_cast<uint2 *>(&sm.dS[1][off]) = uint2{l0, l1};
+        for (int u = 0; u < 2; ++u) {
+            const int off = (sr + 64 * u) * kLSV + sq;
+            stage4(sm.S[0], sm.S[1], off, rS[u]);
+            stage4(sm.dS[0], sm.dS[1], off, rdS[u]);
+            const f32x4 pr = rdS[u] * rS[u];
+            gpart[u] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
         }
-#pragma unroll
-        for (int m = 0; m < 16; ++m) gpart[m] += rdS[m] * rS[m];
-#pragma unroll
-        for (int m4 = 0; m4 < 2; ++m4) {
-            uint32_t h0, l0, h1, l1;
-            const int off = sv * kLST + 8 * sg + 4 * m4;
-            mx::split2(rO[4 * m4], rO[4 * m4 + 1], h0, l0);
-            mx::split2(rO[4 * m4 + 2], rO[4 * m4 + 3], h1, l1);
-            *reinterpret_cast<uint2 *>(&sm.O[0][off]) = uint2{h0, h1};
-            *reinterpret_cast<uint2 *>(&sm.O[1][off]) = uint2{l0, l1};
-        }
-        const f32x4 vv[2] = {rV[0], rV[1]};
+        stage4(sm.O[0], sm.O[1], sr * kLSV + sq, rO);
+        const f32x4 vv = rV;
         fetch(min(j0 + kSW, DV - kSW));
         barrier_lds();
-        // ---- X = V - exp(G) (k S),  dE = exp(G_63 - G) (k dS') + A' dO  (two value tiles)
-#pragma unroll
-        for (int vt = 0; vt < 2; ++vt) {
+        // ---- X = V - exp(G) (k S),  dE = exp(G_63 - G) (k dS') + A' dO  (value tile h)
+        {
+            const int vt = h;
             f32x4 ps = z4, pd = z4;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
+                const int rb = 32 * kb * kLSV;  // key channels 32 kb ..
                 if (delta) {
-                    ps = mx::mma(kA[kb], rows_operand(sm.S[0], kLSK, vt, kb, lr, lg), ps);
-                    ps = mx::mma(kA[kb], rows_operand(sm.S[1], kLSK, vt, kb, lr, lg), ps);
+                    ps = mx::mma(kA[kb], vals_operand(sm.S[0] + rb, kLSV, vt, lr, lg), ps);
+                    ps = mx::mma(kA[kb], vals_operand(sm.S[1] + rb, kLSV, vt, lr, lg), ps);
                 }
-                pd = mx::mma(kA[kb], rows_operand(sm.dS[0], kLSK, vt, kb, lr, lg), pd);
-                pd = mx::mma(kA[kb], rows_operand(sm.dS[1], kLSK, vt, kb, lr, lg), pd);
+                pd = mx::mma(kA[kb], vals_operand(sm.dS[0] + rb, kLSV, vt, lr, lg), pd);
+                pd = mx::mma(kA[kb], vals_operand(sm.dS[1] + rb, kLSV, vt, lr, lg), pd);
             }
             f32x4 de = gnd * pd;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
                 if (kb >= (w >> 1))
-                    de = mma3(auh[kb], aul[kb], rows_operand(sm.O[0], kLST, vt, kb, lr, lg),
-                              rows_operand(sm.O[1], kLST, vt, kb, lr, lg), de);
-            const f32x4 x = vv[vt] - gam * ps;
+                    de = mma3(auh[kb], aul[kb], vals_operand(sm.O[0] + 32 * kb * kLSV, kLSV, vt, lr, lg),
+                              vals_operand(sm.O[1] + 32 * kb * kLSV, kLSV, vt, lr, lg), de);
+            const f32x4 x = vv - gam * ps;
             store_tile(sm.X[0], sm.X[1], w, vt, x, lr, lg);
             store_tile(sm.dE[0], sm.dE[1], w, vt, de, lr, lg);
         }
         barrier_lds();
-        // ---- E = T'' X (token blocks kb <= w / 2),  dX = T''' dE (kb >= w / 2) = dV
-#pragma unroll
-        for (int vt = 0; vt < 2; ++vt) {
+        // ---- E = T'' X (token blocks kb <= w / 2),  dX = T''' dE (kb >= w / 2) = dV  (value tile h)
+        {
+            const int vt = h;
             f32x4 ee = z4, dx = z4;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -2162,66 +2159,69 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grads_a16_kernel(
                                                       ((16 * w + 4 * lg + r) * H * DV + j0 + 16 * vt + lr) * 4, 0, 0);
         }
         barrier_lds();
-        // ---- over the slice's values: dQ~ += dO S',  dK~ -= dX S',  dK^ += E dS'',  dA += dO E',  dT'' += dE X'
+        // ---- over the slice's values: dQ~ += dO S',  dK~ -= dX S',  dK^ += E dS'' (channel tiles 4 h ..);
+        // dA += dO E' (h = 0) or dT'' += dE X' (h = 1)
         {
-            const bf16x8 oh = vals_operand(sm.O[0], kLST, w, lr, lg), ol = vals_operand(sm.O[1], kLST, w, lr, lg);
+            const bf16x8 oh = rows_operand(sm.O[0], kLSV, w, 0, lr, lg), ol = rows_operand(sm.O[1], kLSV, w, 0, lr, lg);
             const bf16x8 eh = vals_operand(sm.E[0], kLST, w, lr, lg), el = vals_operand(sm.E[1], kLST, w, lr, lg);
             const bf16x8 xh = neg8(vals_operand(sm.dX[0], kLST, w, lr, lg));
             const bf16x8 xl = neg8(vals_operand(sm.dX[1], kLST, w, lr, lg));
-            const bf16x8 dh = vals_operand(sm.dE[0], kLST, w, lr, lg), dl = vals_operand(sm.dE[1], kLST, w, lr, lg);
 #pragma unroll
-            for (int J = 0; J < JK; ++J) {
-                const bf16x8 sh = vals_operand(sm.S[0], kLSK, J, lr, lg), slo = vals_operand(sm.S[1], kLSK, J, lr, lg);
-                const bf16x8 th = vals_operand(sm.dS[0], kLSK, J, lr, lg), tl = vals_operand(sm.dS[1], kLSK, J, lr, lg);
+            for (int J = 0; J < JH; ++J) {
+                const int jc = JH * h + J;
+                const bf16x8 sh = rows_operand(sm.S[0], kLSV, jc, 0, lr, lg), slo = rows_operand(sm.S[1], kLSV, jc, 0, lr, lg);
+                const bf16x8 th = rows_operand(sm.dS[0], kLSV, jc, 0, lr, lg), tl = rows_operand(sm.dS[1], kLSV, jc, 0, lr, lg);
                 aQ[J] = mma3(oh, ol, sh, slo, aQ[J]);
                 if (delta) aKt[J] = mma3(xh, xl, sh, slo, aKt[J]);
                 aKh[J] = mma3(eh, el, th, tl, aKh[J]);
             }
+            if (h == 0) {
 #pragma unroll
-            for (int J = 0; J < 4; ++J) {
-                if (J > w) continue;
-                aA[J] = mma3(oh, ol, vals_operand(sm.E[0], kLST, J, lr, lg), vals_operand(sm.E[1], kLST, J, lr, lg),
-                             aA[J]);
-                if (delta)
-                    aT[J] = mma3(dh, dl, vals_operand(sm.X[0], kLST, J, lr, lg), vals_operand(sm.X[1], kLST, J, lr, lg),
-                                 aT[J]);
+                for (int J = 0; J < 4; ++J)
+                    if (J <= w)
+                        aM[J] = mma3(oh, ol, vals_operand(sm.E[0], kLST, J, lr, lg),
+                                     vals_operand(sm.E[1], kLST, J, lr, lg), aM[J]);
+            } else if (delta) {
+                const bf16x8 dh = vals_operand(sm.dE[0], kLST, w, lr, lg), dl = vals_operand(sm.dE[1], kLST, w, lr, lg);
+#pragma unroll
+                for (int J = 0; J < 4; ++J)
+                    if (J <= w)
+                        aM[J] = mma3(dh, dl, vals_operand(sm.X[0], kLST, J, lr, lg),
+                                     vals_operand(sm.X[1], kLST, J, lr, lg), aM[J]);
             }
         }
     }
-    // dgam per channel: the sums over this thread's value column, then over the 32 columns (half a wavefront)
+    // dgam per channel: this thread's sums over its values, then over the eight threads of a channel
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        float s = gpart[m];
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) s += __shfl_xor(s, o, 64);
-        gpart[m] = s;
-    }
-    if (sv == 0) {
-#pragma unroll
-        for (int m = 0; m < 16; ++m) sm.gsum[16 * sg + m] = gpart[m];
+    for (int u = 0; u < 2; ++u) {
+        float s = gpart[u];
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        s += __shfl_xor(s, 4, 64);
+        if (sq == 0) sm.gsum[sr + 64 * u] = s;
     }
 
-    // dA, dT'' (lower triangle incl. the diagonal) to the workspace
+    // dA (h = 0) or dT'' (h = 1), lower triangle incl. the diagonal, to the workspace
+    float *dM = (h == 0 ? wdA : wdTT) + (size_t)ci * C * C;
 #pragma unroll
     for (int J = 0; J < 4; ++J)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = 16 * w + 4 * lg + r, m = 16 * J + lr;
-            wdA[(size_t)ci * C * C + i * C + m] = m <= i ? aA[J][r] : 0.f;
-            wdTT[(size_t)ci * C * C + i * C + m] = m <= i ? aT[J][r] : 0.f;
+            dM[i * C + m] = m <= i ? aM[J][r] : 0.f;
         }
-    // parts of dq, dk through Q~, K~, K^ (rows past the end are not written); parts of dG:
+    // parts of dq, dk through Q~, K~, K^, channel tiles 4 h .. (rows past the end are not written); of dG:
     // dK~ K~ + dQ~ Q~ - dK^ K^ over the channels; for G_63 also sum_i dK^ K^ + dgam gam
     const float *Gc = wG + (size_t)ci * C;
     const float ge = Gc[C - 1];
     const auto rkq = rows_rsrc(kin + row0u * DK, nu, H * DK * 2, DK * 2);
     const auto rqq = rows_rsrc(qin + row0u * DK, nu, H * DK * 2, DK * 2);
     float rowpart[4] = {0.f, 0.f, 0.f, 0.f};
-    float colh[JK];
+    float colh[JH];
 #pragma unroll
-    for (int J = 0; J < JK; ++J) {
+    for (int J = 0; J < JH; ++J) {
         colh[J] = 0.f;
-        const int ch = 16 * J + lr;
+        const int ch = 16 * (JH * h + J) + lr;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = 16 * w + 4 * lg + r;
@@ -2238,26 +2238,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grads_a16_kernel(
         }
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {  // sum over the 16 lanes of a row group, then one lane writes each row
+    for (int r = 0; r < 4; ++r) {  // sum over the 16 lanes of a row group; the halves meet in LDS
         float sum = rowpart[r];
         sum += __shfl_xor(sum, 1, 64);
         sum += __shfl_xor(sum, 2, 64);
         sum += __shfl_xor(sum, 4, 64);
         sum += __shfl_xor(sum, 8, 64);
-        if (lr == 0) wdG[(size_t)ci * C + 16 * w + 4 * lg + r] = sum;
+        if (lr == 0) sm.rowp[h][16 * w + 4 * lg + r] = sum;
     }
 #pragma unroll
-    for (int J = 0; J < JK; ++J) {
+    for (int J = 0; J < JH; ++J) {
         float sum = colh[J];
         sum += __shfl_xor(sum, 16, 64);
         sum += __shfl_xor(sum, 32, 64);
-        if (lg == 0) sm.H[w][16 * J + lr] = sum;
+        if (lg == 0) sm.H[w][16 * (JH * h + J) + lr] = sum;
     }
     __syncthreads();
+    if (tid < C) wdG[(size_t)ci * C + tid] = sm.rowp[0][tid] + sm.rowp[1][tid];
     if (tid < DK)
         sm.H[0][tid] = ((sm.H[0][tid] + sm.H[1][tid]) + (sm.H[2][tid] + sm.H[3][tid])) + sm.gsum[tid] * __expf(ge);
     __syncthreads();
-    if (w == 0) {  // the sum over channels
+    if (wv == 0) {  // the sum over channels
         float s = 0.f;
         for (int cc = lane; cc < DK; cc += 64) s += sm.H[0][cc];
 #pragma unroll
@@ -2940,7 +2941,7 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
                            a.H, a.NC, w.T, w.A, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.ds_final, w.dS, a.ds0, a.delta, a.tab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if constexpr (bwd_walk16(ops, DK, DV))
-        hipLaunchKernelGGL(bwd_grads_a16_kernel, dim3(nslot), dim3(kThreads), 0, a.stream,
+        hipLaunchKernelGGL(bwd_grads_a16_kernel, dim3(nslot), dim3(kThreads16), 0, a.stream,
                            static_cast<const __bf16 *>(a.v), a.dO, static_cast<const __bf16 *>(a.k),
                            static_cast<const __bf16 *>(a.q), a.T, a.H, a.NC, a.scale, w.G,
                            static_cast<const char *>(w.rec), static_cast<const char *>(w.rrev), w.S, w.dS, w.dA, w.dTT,
