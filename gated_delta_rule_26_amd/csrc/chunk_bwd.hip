@@ -1966,13 +1966,25 @@ constexpr int kSW = 32;           // value columns per slice
 constexpr int kLSV = kSW + 8;     // bf16 pitch of the [row][value] arrays
 constexpr int kLST = C + 8;       // bf16 pitch of the [value][token] arrays
 
+constexpr int kLCB = C + 1;       // fp32 pitch of the C x C arrays of the triangular algebra
+constexpr int kLQB = mx::DK + 16;  // bf16 pitch of k and q there
+
 struct alignas(16) GradsSmem {
-    __bf16 S[2][mx::DK * kLSV], dS[2][mx::DK * kLSV];  // [hi, lo][key channel][value]
-    __bf16 O[2][C * kLSV];                              // [hi, lo][token][value]
-    __bf16 X[2][kSW * kLST], dE[2][kSW * kLST], E[2][kSW * kLST], dX[2][kSW * kLST];  // [hi, lo][value][token]
+    union {
+        struct {  // the value-axis products
+            __bf16 S[2][mx::DK * kLSV], dS[2][mx::DK * kLSV];  // [hi, lo][key channel][value]
+            __bf16 O[2][C * kLSV];                              // [hi, lo][token][value]
+            __bf16 X[2][kSW * kLST], dE[2][kSW * kLST], E[2][kSW * kLST], dX[2][kSW * kLST];  // [value][token]
+        } a;
+        struct {  // the triangular algebra and the pair terms
+            float T[C * kLCB], X[C * kLCB], Y[C * kLCB], D[C * kLCB], M[C * kLCB], A[C * kLCB];
+            __bf16 K[C * kLQB], Q[C * kLQB];
+        } b;
+    } u;
     float gsum[mx::DK];  // per key channel: sum over values of dS' S
     float H[4][mx::DK];  // per token block: column sums of dK^ K^
     float rowp[2][C];    // per half of the channels: the token rows' parts of dG
+    float G[C], beta[C], dbeta[C], kk[C], dG[C];
 };
 
 // Along the rows of an array (pitch ld): row 16 vt + lr, columns 32 kb + kperm(lg, e).
@@ -2013,12 +2025,13 @@ __device__ __forceinline__ mx::bf16x8 neg8(mx::bf16x8 x) {
 
 constexpr int kThreads16 = 512;  // eight wavefronts
 
-__global__ __launch_bounds__(kThreads16, 1) void bwd_grads_a16_kernel(
+__global__ __launch_bounds__(kThreads16, 1) void bwd_grads16_kernel(
     const __bf16 *__restrict__ v, const float *__restrict__ dO, const __bf16 *__restrict__ kin,
-    const __bf16 *__restrict__ qin, int T, int H, int NC, float scale, const float *__restrict__ wG,
-    const char *__restrict__ rec, const char *__restrict__ rrev, const float *__restrict__ wS,
-    const float *__restrict__ wdS, float *__restrict__ wdA, float *__restrict__ wdTT, float *__restrict__ wdG,
-    float *__restrict__ wdG63, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv, bool delta,
+    const __bf16 *__restrict__ qin, int T, int H, int NC, float eps, float scale, const float *__restrict__ wT,
+    const float *__restrict__ wM, const float *__restrict__ wA, const float *__restrict__ wG,
+    const float *__restrict__ wB, const char *__restrict__ rec, const char *__restrict__ rrev,
+    const float *__restrict__ wS, const float *__restrict__ wdS, float *__restrict__ dq, float *__restrict__ dk,
+    float *__restrict__ dv, float *__restrict__ dg, float *__restrict__ dbeta, bool delta, bool kaczmarz,
     SeqTable tb) {
     using mx::bf16x8;
     constexpr int DK = mx::DK, DV = mx::DV, JH = DK / 32;  // channel tiles per half
@@ -2104,12 +2117,12 @@ __global__ __launch_bounds__(kThreads16, 1) void bwd_grads_a16_kernel(
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int off = (sr + 64 * u) * kLSV + sq;
-            stage4(sm.S[0], sm.S[1], off, rS[u]);
-            stage4(sm.dS[0], sm.dS[1], off, rdS[u]);
+            stage4(sm.u.a.S[0], sm.u.a.S[1], off, rS[u]);
+            stage4(sm.u.a.dS[0], sm.u.a.dS[1], off, rdS[u]);
             const f32x4 pr = rdS[u] * rS[u];
             gpart[u] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
         }
-        stage4(sm.O[0], sm.O[1], sr * kLSV + sq, rO);
+        stage4(sm.u.a.O[0], sm.u.a.O[1], sr * kLSV + sq, rO);
         const f32x4 vv = rV;
         fetch(min(j0 + kSW, DV - kSW));
         barrier_lds();
@@ -2121,21 +2134,21 @@ __global__ __launch_bounds__(kThreads16, 1) void bwd_grads_a16_kernel(
             for (int kb = 0; kb < 4; ++kb) {
                 const int rb = 32 * kb * kLSV;  // key channels 32 kb ..
                 if (delta) {
-                    ps = mx::mma(kA[kb], vals_operand(sm.S[0] + rb, kLSV, vt, lr, lg), ps);
-                    ps = mx::mma(kA[kb], vals_operand(sm.S[1] + rb, kLSV, vt, lr, lg), ps);
+                    ps = mx::mma(kA[kb], vals_operand(sm.u.a.S[0] + rb, kLSV, vt, lr, lg), ps);
+                    ps = mx::mma(kA[kb], vals_operand(sm.u.a.S[1] + rb, kLSV, vt, lr, lg), ps);
                 }
-                pd = mx::mma(kA[kb], vals_operand(sm.dS[0] + rb, kLSV, vt, lr, lg), pd);
-                pd = mx::mma(kA[kb], vals_operand(sm.dS[1] + rb, kLSV, vt, lr, lg), pd);
+                pd = mx::mma(kA[kb], vals_operand(sm.u.a.dS[0] + rb, kLSV, vt, lr, lg), pd);
+                pd = mx::mma(kA[kb], vals_operand(sm.u.a.dS[1] + rb, kLSV, vt, lr, lg), pd);
             }
             f32x4 de = gnd * pd;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
                 if (kb >= (w >> 1))
-                    de = mma3(auh[kb], aul[kb], vals_operand(sm.O[0] + 32 * kb * kLSV, kLSV, vt, lr, lg),
-                              vals_operand(sm.O[1] + 32 * kb * kLSV, kLSV, vt, lr, lg), de);
+                    de = mma3(auh[kb], aul[kb], vals_operand(sm.u.a.O[0] + 32 * kb * kLSV, kLSV, vt, lr, lg),
+                              vals_operand(sm.u.a.O[1] + 32 * kb * kLSV, kLSV, vt, lr, lg), de);
             const f32x4 x = vv - gam * ps;
-            store_tile(sm.X[0], sm.X[1], w, vt, x, lr, lg);
-            store_tile(sm.dE[0], sm.dE[1], w, vt, de, lr, lg);
+            store_tile(sm.u.a.X[0], sm.u.a.X[1], w, vt, x, lr, lg);
+            store_tile(sm.u.a.dE[0], sm.u.a.dE[1], w, vt, de, lr, lg);
         }
         barrier_lds();
         // ---- E = T'' X (token blocks kb <= w / 2),  dX = T''' dE (kb >= w / 2) = dV  (value tile h)
@@ -2145,14 +2158,14 @@ __global__ __launch_bounds__(kThreads16, 1) void bwd_grads_a16_kernel(
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 if (kb <= (w >> 1))
-                    ee = mma3(tlh[kb], tll[kb], rows_operand(sm.X[0], kLST, vt, kb, lr, lg),
-                              rows_operand(sm.X[1], kLST, vt, kb, lr, lg), ee);
+                    ee = mma3(tlh[kb], tll[kb], rows_operand(sm.u.a.X[0], kLST, vt, kb, lr, lg),
+                              rows_operand(sm.u.a.X[1], kLST, vt, kb, lr, lg), ee);
                 if (kb >= (w >> 1))
-                    dx = mma3(tuh[kb], tul[kb], rows_operand(sm.dE[0], kLST, vt, kb, lr, lg),
-                              rows_operand(sm.dE[1], kLST, vt, kb, lr, lg), dx);
+                    dx = mma3(tuh[kb], tul[kb], rows_operand(sm.u.a.dE[0], kLST, vt, kb, lr, lg),
+                              rows_operand(sm.u.a.dE[1], kLST, vt, kb, lr, lg), dx);
             }
-            store_tile(sm.E[0], sm.E[1], w, vt, ee, lr, lg);
-            store_tile(sm.dX[0], sm.dX[1], w, vt, dx, lr, lg);
+            store_tile(sm.u.a.E[0], sm.u.a.E[1], w, vt, ee, lr, lg);
+            store_tile(sm.u.a.dX[0], sm.u.a.dX[1], w, vt, dx, lr, lg);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dx[r]), r_dv,
@@ -2162,15 +2175,15 @@ __global__ __launch_bounds__(kThreads16, 1) void bwd_grads_a16_kernel(
         // ---- over the slice's values: dQ~ += dO S',  dK~ -= dX S',  dK^ += E dS'' (channel tiles 4 h ..);
         // dA += dO E' (h = 0) or dT'' += dE X' (h = 1)
         {
-            const bf16x8 oh = rows_operand(sm.O[0], kLSV, w, 0, lr, lg), ol = rows_operand(sm.O[1], kLSV, w, 0, lr, lg);
-            const bf16x8 eh = vals_operand(sm.E[0], kLST, w, lr, lg), el = vals_operand(sm.E[1], kLST, w, lr, lg);
-            const bf16x8 xh = neg8(vals_operand(sm.dX[0], kLST, w, lr, lg));
-            const bf16x8 xl = neg8(vals_operand(sm.dX[1], kLST, w, lr, lg));
+            const bf16x8 oh = rows_operand(sm.u.a.O[0], kLSV, w, 0, lr, lg), ol = rows_operand(sm.u.a.O[1], kLSV, w, 0, lr, lg);
+            const bf16x8 eh = vals_operand(sm.u.a.E[0], kLST, w, lr, lg), el = vals_operand(sm.u.a.E[1], kLST, w, lr, lg);
+            const bf16x8 xh = neg8(vals_operand(sm.u.a.dX[0], kLST, w, lr, lg));
+            const bf16x8 xl = neg8(vals_operand(sm.u.a.dX[1], kLST, w, lr, lg));
 #pragma unroll
             for (int J = 0; J < JH; ++J) {
                 const int jc = JH * h + J;
-                const bf16x8 sh = rows_operand(sm.S[0], kLSV, jc, 0, lr, lg), slo = rows_operand(sm.S[1], kLSV, jc, 0, lr, lg);
-                const bf16x8 th = rows_operand(sm.dS[0], kLSV, jc, 0, lr, lg), tl = rows_operand(sm.dS[1], kLSV, jc, 0, lr, lg);
+                const bf16x8 sh = rows_operand(sm.u.a.S[0], kLSV, jc, 0, lr, lg), slo = rows_operand(sm.u.a.S[1], kLSV, jc, 0, lr, lg);
+                const bf16x8 th = rows_operand(sm.u.a.dS[0], kLSV, jc, 0, lr, lg), tl = rows_operand(sm.u.a.dS[1], kLSV, jc, 0, lr, lg);
                 aQ[J] = mma3(oh, ol, sh, slo, aQ[J]);
                 if (delta) aKt[J] = mma3(xh, xl, sh, slo, aKt[J]);
                 aKh[J] = mma3(eh, el, th, tl, aKh[J]);
@@ -2179,15 +2192,15 @@ __global__ __launch_bounds__(kThreads16, 1) void bwd_grads_a16_kernel(
 #pragma unroll
                 for (int J = 0; J < 4; ++J)
                     if (J <= w)
-                        aM[J] = mma3(oh, ol, vals_operand(sm.E[0], kLST, J, lr, lg),
-                                     vals_operand(sm.E[1], kLST, J, lr, lg), aM[J]);
+                        aM[J] = mma3(oh, ol, vals_operand(sm.u.a.E[0], kLST, J, lr, lg),
+                                     vals_operand(sm.u.a.E[1], kLST, J, lr, lg), aM[J]);
             } else if (delta) {
-                const bf16x8 dh = vals_operand(sm.dE[0], kLST, w, lr, lg), dl = vals_operand(sm.dE[1], kLST, w, lr, lg);
+                const bf16x8 dh = vals_operand(sm.u.a.dE[0], kLST, w, lr, lg), dl = vals_operand(sm.u.a.dE[1], kLST, w, lr, lg);
 #pragma unroll
                 for (int J = 0; J < 4; ++J)
                     if (J <= w)
-                        aM[J] = mma3(dh, dl, vals_operand(sm.X[0], kLST, J, lr, lg),
-                                     vals_operand(sm.X[1], kLST, J, lr, lg), aM[J]);
+                        aM[J] = mma3(dh, dl, vals_operand(sm.u.a.X[0], kLST, J, lr, lg),
+                                     vals_operand(sm.u.a.X[1], kLST, J, lr, lg), aM[J]);
             }
         }
     }
@@ -2201,69 +2214,251 @@ __global__ __launch_bounds__(kThreads16, 1) void bwd_grads_a16_kernel(
         if (sq == 0) sm.gsum[sr + 64 * u] = s;
     }
 
-    // dA (h = 0) or dT'' (h = 1), lower triangle incl. the diagonal, to the workspace
-    float *dM = (h == 0 ? wdA : wdTT) + (size_t)ci * C * C;
+    // ===================== the chunk's triangular algebra and pair terms, on this workgroup
+    // (in LDS from here on: T, dT'' -> dT -> dR -> W2, Y, dA with dM' above the diagonal, M, A -> W1 in T's
+    // place once T is read, the bf16 rows of k and q; G, beta, dbeta, |k|^2, dG)
+    constexpr int NCC = C * C / kThreads16;  // C x C values per thread
+    float rT[NCC], rM[NCC], rA[NCC];
+    uint4 rk[2], rq[2];
+    {
+        const float *Tg = wT + (size_t)ci * C * C, *Mg = wM + (size_t)ci * C * C, *Ag = wA + (size_t)ci * C * C;
 #pragma unroll
-    for (int J = 0; J < 4; ++J)
+        for (int u = 0; u < NCC; ++u) {
+            rT[u] = Tg[tid + u * kThreads16];
+            rM[u] = Mg[tid + u * kThreads16];
+            rA[u] = Ag[tid + u * kThreads16];
+        }
+        const auto rkb = rows_rsrc(kin + row0u * DK, nu, H * DK * 2, DK * 2);
+        const auto rqb = rows_rsrc(qin + row0u * DK, nu, H * DK * 2, DK * 2);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int idx = tid + u * kThreads16, r = idx >> 4, c0 = (idx & 15) * 8;
+            rk[u] = mx::buf_ld16(rkb, (r * H * DK + c0) * 2);
+            rq[u] = mx::buf_ld16(rqb, (r * H * DK + c0) * 2);
+        }
+    }
+    barrier_lds();  // every wavefront is done with the slice operands
+    float *sT = sm.u.b.T, *sX = sm.u.b.X, *sY = sm.u.b.Y, *sD = sm.u.b.D, *sMm = sm.u.b.M, *sAa = sm.u.b.A;
+    __bf16 *sKb = sm.u.b.K, *sQb = sm.u.b.Q;
+#pragma unroll
+    for (int J = 0; J < 4; ++J)  // dA (h = 0) into sD, dT'' (h = 1) into sX: lower triangle incl. the diagonal
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = 16 * w + 4 * lg + r, m = 16 * J + lr;
-            dM[i * C + m] = m <= i ? aM[J][r] : 0.f;
+            (h == 0 ? sD : sX)[i * kLCB + m] = m <= i ? aM[J][r] : 0.f;
         }
-    // parts of dq, dk through Q~, K~, K^, channel tiles 4 h .. (rows past the end are not written); of dG:
-    // dK~ K~ + dQ~ Q~ - dK^ K^ over the channels; for G_63 also sum_i dK^ K^ + dgam gam
-    const float *Gc = wG + (size_t)ci * C;
-    const float ge = Gc[C - 1];
-    const auto rkq = rows_rsrc(kin + row0u * DK, nu, H * DK * 2, DK * 2);
-    const auto rqq = rows_rsrc(qin + row0u * DK, nu, H * DK * 2, DK * 2);
-    float rowpart[4] = {0.f, 0.f, 0.f, 0.f};
-    float colh[JH];
 #pragma unroll
-    for (int J = 0; J < JH; ++J) {
-        colh[J] = 0.f;
-        const int ch = 16 * (JH * h + J) + lr;
+    for (int u = 0; u < NCC; ++u) {
+        const int idx = tid + u * kThreads16, r = idx / C, cc = idx % C;
+        sT[r * kLCB + cc] = rT[u];
+        sMm[r * kLCB + cc] = rM[u];
+        sAa[r * kLCB + cc] = rA[u];
+    }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * w + 4 * lg + r;
-            const float ei = gam[r], eh = gnd[r];
-            const float kv = buf_in<true>(rkq, i * H * DK + ch), qv = buf_in<true>(rqq, i * H * DK + ch);
-            if (i < n) {
-                const size_t off = (sl.row0 + (size_t)i * H) * DK + ch;
-                dq[off] = scale * ei * aQ[J][r];
-                dk[off] = ei * aKt[J][r] + eh * aKh[J][r];
+    for (int u = 0; u < 2; ++u) {
+        const int idx = tid + u * kThreads16, r = idx >> 4, c0 = (idx & 15) * 8;
+        *reinterpret_cast<uint4 *>(&sKb[r * kLQB + c0]) = rk[u];
+        *reinterpret_cast<uint4 *>(&sQb[r * kLQB + c0]) = rq[u];
+    }
+    if (tid < C) {
+        sm.G[tid] = wG[(size_t)ci * C + tid];
+        sm.beta[tid] = wB[(size_t)ci * C + tid];
+    }
+    barrier_lds();
+    // parts of dG through Q~, K~, K^ (rows 16 w .., channel tiles 4 h ..): dK~ K~ + dQ~ Q~ - dK^ K^ summed
+    // over the channels, and for G_63 the column sums of dK^ K^; dbeta_j = sum_i dT''_ij T_ij
+    auto kval = [&](int r, int c) { return static_cast<float>(sKb[r * kLQB + c]); };
+    {
+        float rowpart[4] = {0.f, 0.f, 0.f, 0.f};
+        float colh[JH];
+#pragma unroll
+        for (int J = 0; J < JH; ++J) {
+            colh[J] = 0.f;
+            const int ch = 16 * (JH * h + J) + lr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * w + 4 * lg + r;
+                const float ei = gam[r], eh = gnd[r];
+                const float kv = kval(i, ch), qv = static_cast<float>(sQb[i * kLQB + ch]);
+                const float khv = eh * kv;
+                rowpart[r] += aKt[J][r] * (ei * kv) + aQ[J][r] * (scale * ei * qv) - aKh[J][r] * khv;
+                colh[J] += aKh[J][r] * khv;
             }
-            const float khv = eh * kv;
-            rowpart[r] += aKt[J][r] * (ei * kv) + aQ[J][r] * (scale * ei * qv) - aKh[J][r] * khv;
-            colh[J] += aKh[J][r] * khv;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {  // sum over the 16 lanes of a row group; the halves meet in LDS
+            float sum = rowpart[r];
+            sum += __shfl_xor(sum, 1, 64);
+            sum += __shfl_xor(sum, 2, 64);
+            sum += __shfl_xor(sum, 4, 64);
+            sum += __shfl_xor(sum, 8, 64);
+            if (lr == 0) sm.rowp[h][16 * w + 4 * lg + r] = sum;
+        }
+#pragma unroll
+        for (int J = 0; J < JH; ++J) {
+            float sum = colh[J];
+            sum += __shfl_xor(sum, 16, 64);
+            sum += __shfl_xor(sum, 32, 64);
+            if (lg == 0) sm.H[w][16 * (JH * h + J) + lr] = sum;
+        }
+        if (tid < kThreads) {  // four lanes per column (every fourth row each), then a sum over the quad
+            const int j = tid >> 2, q4 = tid & 3;
+            float s = 0.f;
+            for (int r = j + q4; r < C; r += 4) s += sX[r * kLCB + j] * sT[r * kLCB + j];
+            s += __shfl_xor(s, 1, 64);
+            s += __shfl_xor(s, 2, 64);
+            if (q4 == 0) sm.dbeta[j] = s;
         }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {  // sum over the 16 lanes of a row group; the halves meet in LDS
-        float sum = rowpart[r];
-        sum += __shfl_xor(sum, 1, 64);
-        sum += __shfl_xor(sum, 2, 64);
-        sum += __shfl_xor(sum, 4, 64);
-        sum += __shfl_xor(sum, 8, 64);
-        if (lr == 0) sm.rowp[h][16 * w + 4 * lg + r] = sum;
-    }
-#pragma unroll
-    for (int J = 0; J < JH; ++J) {
-        float sum = colh[J];
-        sum += __shfl_xor(sum, 16, 64);
-        sum += __shfl_xor(sum, 32, 64);
-        if (lg == 0) sm.H[w][16 * (JH * h + J) + lr] = sum;
-    }
-    __syncthreads();
-    if (tid < C) wdG[(size_t)ci * C + tid] = sm.rowp[0][tid] + sm.rowp[1][tid];
-    if (tid < DK)
+    barrier_lds();
+    // dG of the tokens; the chunk-end decay's extra (per channel, then over channels below); dT = dT'' Diag(beta)
+    if (tid < C) sm.dG[tid] = sm.rowp[0][tid] + sm.rowp[1][tid];
+    if (tid < DK) {
+        const float ge = sm.G[C - 1];
         sm.H[0][tid] = ((sm.H[0][tid] + sm.H[1][tid]) + (sm.H[2][tid] + sm.H[3][tid])) + sm.gsum[tid] * __expf(ge);
-    __syncthreads();
-    if (wv == 0) {  // the sum over channels
+    }
+    for (int idx = tid; idx < C * C; idx += kThreads16) {
+        const int r = idx / C, cc = idx % C;
+        sX[r * kLCB + cc] *= sm.beta[cc];
+    }
+    barrier_lds();
+    if (wv == 0) {  // the sum over channels, to the last token's dG
         float s = 0.f;
         for (int cc = lane; cc < DK; cc += 64) s += sm.H[0][cc];
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-        if (lane == 0) wdG63[ci] = s;
+        if (lane == 0) sm.dG[C - 1] += s;
+    }
+    {  // Y = T' dT: rows 16 w .., column tiles 2 h, 2 h + 1
+        f32x4 y[2] = {z4, z4};
+        for (int kk = 0; kk < C; kk += 4) {
+            const float a = sT[(kk + lg) * kLCB + 16 * w + lr];
+#pragma unroll
+            for (int J = 0; J < 2; ++J) y[J] = mfma4(a, sX[(kk + lg) * kLCB + 16 * (2 * h + J) + lr], y[J]);
+        }
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sY[(16 * w + 4 * lg + r) * kLCB + 16 * (2 * h + J) + lr] = y[J][r];
+    }
+    barrier_lds();
+    {  // -dR = Y T': rows 16 w .., column tiles 2 h, 2 h + 1; dR (strictly lower) over dT
+        f32x4 d[2] = {z4, z4};
+        for (int kk = 0; kk < C; kk += 4) {
+            const float a = sY[(16 * w + lr) * kLCB + kk + lg];
+#pragma unroll
+            for (int J = 0; J < 2; ++J) d[J] = mfma4(a, sT[(16 * (2 * h + J) + lr) * kLCB + kk + lg], d[J]);
+        }
+        barrier_lds();  // dT and Y no longer read
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * w + 4 * lg + r, j = 16 * (2 * h + J) + lr;
+                sX[i * kLCB + j] = j < i ? -d[J][r] : 0.f;
+            }
+    }
+    barrier_lds();
+    // dbeta_i += sum_{j<i} dR_ij M_ij;  dM_ij = beta_i dR_ij -> sD[j][i] (j < i)
+    if (tid < kThreads) {
+        const int r = tid >> 2, q4 = tid & 3;
+        float s = 0.f;
+        for (int cc = q4; cc < r; cc += 4) s += sX[r * kLCB + cc] * sMm[r * kLCB + cc];
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        if (q4 == 0) sm.dbeta[r] += s;
+    }
+    for (int idx = tid; idx < C * C; idx += kThreads16) {
+        const int r = idx / C, cc = idx % C;
+        if (cc < r) sD[cc * kLCB + r] = sm.beta[r] * sX[r * kLCB + cc];
+    }
+    barrier_lds();
+    // dG_i += rowsum_i(Z) - colsum_i(Z), Z = dM o M + dA o A;  W1 = dM o P over T, W2 = scale dA o P over
+    // dR (P_ij = exp(G_i - G_j), j <= i);  |k_i|^2 for the Kaczmarz step size
+    if (tid < kThreads) {
+        const int r = tid >> 2, q4 = tid & 3;
+        float s = 0.f;
+        for (int j = q4; j < r; j += 4) s += sD[j * kLCB + r] * sMm[r * kLCB + j];
+        for (int j = q4; j <= r; j += 4) s += sD[r * kLCB + j] * sAa[r * kLCB + j];
+        for (int i = r + 1 + q4; i < C; i += 4) s -= sD[r * kLCB + i] * sMm[i * kLCB + r];
+        for (int i = r + q4; i < C; i += 4) s -= sD[i * kLCB + r] * sAa[i * kLCB + r];
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        if (q4 == 0) sm.dG[r] += s;
+    } else if (kaczmarz) {
+        const int r = (tid - kThreads) >> 2, q4 = tid & 3;
+        float s = 0.f;
+        for (int cc = q4; cc < DK; cc += 4) s += kval(r, cc) * kval(r, cc);
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        if (q4 == 0) sm.kk[r] = s;
+    }
+    for (int idx = tid; idx < C * C; idx += kThreads16) {
+        const int i = idx / C, j = idx % C;
+        const float p = j <= i ? __expf(sm.G[i] - sm.G[j]) : 0.f;
+        sT[i * kLCB + j] = j < i ? sD[j * kLCB + i] * p : 0.f;
+        sX[i * kLCB + j] = scale * sD[i * kLCB + j] * p;  // zero above the diagonal
+    }
+    barrier_lds();
+    // pair terms, rows 16 w .., channel tiles 4 h ..: dk += W1 K + W1' K + W2' Q, dq += W2 K (token j =
+    // 16 t + 4 lg + e in step (t, e): four tokens of a lane group are one transposing read of k or q)
+    {
+        f32x4 pk[JH], pq[JH];
+#pragma unroll
+        for (int J = 0; J < JH; ++J) pk[J] = pq[J] = z4;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float ak[4], aq[4], ad[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 16 * t + 4 * lg + e;
+                ak[e] = sT[(16 * w + lr) * kLCB + j] + sT[j * kLCB + 16 * w + lr];  // W1 + W1'
+                aq[e] = sX[j * kLCB + 16 * w + lr];                                   // W2'
+                ad[e] = sX[(16 * w + lr) * kLCB + j];                                 // W2
+            }
+#pragma unroll
+            for (int J = 0; J < JH; ++J) {
+                const int at = (16 * t + 4 * lg + (lr >> 2)) * kLQB + 16 * (JH * h + J) + 4 * (lr & 3);
+                const mx::bf16x4 k4 = mx::lds_read_tr(&sKb[at]);
+                const mx::bf16x4 q4 = mx::lds_read_tr(&sQb[at]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float kb = static_cast<float>(k4[e]), qb = static_cast<float>(q4[e]);
+                    pk[J] = mfma4(ak[e], kb, pk[J]);
+                    pk[J] = mfma4(aq[e], qb, pk[J]);
+                    pq[J] = mfma4(ad[e], kb, pq[J]);
+                }
+            }
+        }
+        // dq, dk: the parts through Q~, K~, K^ and the pair terms (rows past the end are not written)
+#pragma unroll
+        for (int J = 0; J < JH; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * w + 4 * lg + r, ch = 16 * (JH * h + J) + lr;
+                if (i < n) {
+                    const size_t off = (sl.row0 + (size_t)i * H) * DK + ch;
+                    float dkv = gam[r] * aKt[J][r] + gnd[r] * aKh[J][r] + pk[J][r];
+                    if (kaczmarz) dkv += -2.f * sm.beta[i] * sm.dbeta[i] / (sm.kk[i] + eps) * kval(i, ch);
+                    dk[off] = dkv;
+                    dq[off] = scale * gam[r] * aQ[J][r] + pq[J][r];
+                }
+            }
+    }
+    // dg = the reverse cumulative sum of dG over the chunk's tokens (a suffix sum across one wavefront);
+    // dbeta (deta for the Kaczmarz step size)
+    if (wv == 0) {
+        float run = sm.dG[lane];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float up = __shfl_down(run, off, 64);
+            if (lane + off < 64) run += up;
+        }
+        if (lane < n) dg[sl.row0 + (size_t)lane * H] = run;
+    } else if (wv == 1 && dbeta && lane < n) {  // no beta without the delta rule
+        float db = sm.dbeta[lane];
+        if (kaczmarz) db /= (sm.kk[lane] + eps);
+        dbeta[sl.row0 + (size_t)lane * H] = db;
     }
 }
 
@@ -2940,13 +3135,14 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
         hipLaunchKernelGGL((bwd_dstates_kernel<DK, DV, PC>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.dO, a.T,
                            a.H, a.NC, w.T, w.A, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.ds_final, w.dS, a.ds0, a.delta, a.tab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if constexpr (bwd_walk16(ops, DK, DV))
-        hipLaunchKernelGGL(bwd_grads_a16_kernel, dim3(nslot), dim3(kThreads16), 0, a.stream,
+    if constexpr (bwd_walk16(ops, DK, DV)) {  // every per-chunk gradient in one kernel
+        hipLaunchKernelGGL(bwd_grads16_kernel, dim3(nslot), dim3(kThreads16), 0, a.stream,
                            static_cast<const __bf16 *>(a.v), a.dO, static_cast<const __bf16 *>(a.k),
-                           static_cast<const __bf16 *>(a.q), a.T, a.H, a.NC, a.scale, w.G,
-                           static_cast<const char *>(w.rec), static_cast<const char *>(w.rrev), w.S, w.dS, w.dA, w.dTT,
-                           w.dG, w.dG63, a.dq, a.dk, a.dv, a.delta, a.tab);
-    else
+                           static_cast<const __bf16 *>(a.q), a.T, a.H, a.NC, a.eps, a.scale, w.T, w.M, w.A, w.G,
+                           w.beta, static_cast<const char *>(w.rec), static_cast<const char *>(w.rrev), w.S, w.dS,
+                           a.dq, a.dk, a.dv, a.dg, a.dbeta, a.delta, a.kaczmarz, a.tab);
+        return hipGetLastError();
+    } else
         hipLaunchKernelGGL((bwd_grads_a_kernel<DK, DV, PC, IB, !ops>), dim3(nslot), dim3(kThreads), 0, a.stream,
                            a.v, a.dO, a.T, a.H, a.NC, a.scale, w.T, w.A, w.G, w.beta, w.S, w.dS, w.Kt, w.Kh, w.Qt,
                            static_cast<const __bf16 *>(a.k), static_cast<const __bf16 *>(a.q), w.dA, w.dTT, w.dG,
