@@ -122,16 +122,22 @@ BwdWs carve_bwd(void *ws, size_t slots, bool ops) {
     }
     float *p = static_cast<float *>(ws);
     w.T = p; p += slots * C * C;
-    w.A = p; p += slots * C * C;
-    w.M = p; p += slots * C * C;
+    w.A = w.M = nullptr;
+    if (!bwd_walk16(ops, DK, DV)) {  // the bf16 path forms M and A where it uses them
+        w.A = p; p += slots * C * C;
+        w.M = p; p += slots * C * C;
+    }
     w.G = p; p += slots * C * GK;
     w.beta = p; p += slots * C;
     w.S = p; p += slots * DK * DV;
     w.dS = p; p += slots * DK * DV;
-    w.dA = p; p += slots * C * C;
-    w.dTT = p; p += slots * C * C;
-    w.dG = p; p += slots * C * GK;
-    w.dG63 = p; p += slots * GK;
+    w.dA = w.dTT = w.dG = w.dG63 = nullptr;
+    if (!bwd_walk16(ops, DK, DV)) {  // the bf16 path keeps these on the workgroup that forms them
+        w.dA = p; p += slots * C * C;
+        w.dTT = p; p += slots * C * C;
+        w.dG = p; p += slots * C * GK;
+        w.dG63 = p; p += slots * GK;
+    }
     w.Kt = w.Kh = w.Qt = nullptr;
     if (ops) {
         w.Kt = p; p += slots * C * DK;
@@ -144,9 +150,11 @@ BwdWs carve_bwd(void *ws, size_t slots, bool ops) {
 template <int DK, int DV, bool PC>
 size_t bwd_bytes(size_t slots, bool ops) {
     constexpr int GK = PC ? DK : 1;
+    const bool walk16 = bwd_walk16(ops, DK, DV);
+    const size_t grads = walk16 ? 0 : (size_t)4 * C * C + (size_t)C * GK + GK;  // A, M, dA, dT'', dG, dG63
     return slots * sizeof(float) *
-               ((size_t)5 * C * C + 2 * (size_t)C * GK + GK + C + 2 * (size_t)DK * DV + (ops ? 3 * (size_t)C * DK : 0)) +
-           (bwd_walk16(ops, DK, DV) ? slots * (mx::kRecBytes + kRevBytes) : 0);
+               ((size_t)C * C + (size_t)C * GK + C + 2 * (size_t)DK * DV + grads + (ops ? 3 * (size_t)C * DK : 0)) +
+           (walk16 ? slots * (mx::kRecBytes + kRevBytes) : 0);
 }
 
 // chunk slot ci -> token row of its token 0 and token count.  Fixed-length
@@ -459,7 +467,7 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
     }
 
     // ---- M and A; this wavefront's R = Diag(beta) M values stay in registers
-    float *Mg = wM + (size_t)ci * C * C, *Ag = wA + (size_t)ci * C * C;
+    float *Mg = wM ? wM + (size_t)ci * C * C : nullptr, *Ag = wA ? wA + (size_t)ci * C * C : nullptr;
     f32x4 rv[3], av[3];  // this wavefront's lower tiles of R and (for the record) A
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
@@ -514,8 +522,10 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
             const int i = 16 * I + 4 * lg + r, j = 16 * J + lr;
             const float pp = PC ? (j <= i ? 1.f : 0.f) : (j <= i ? __expf(sG[i][0] - sG[j][0]) : 0.f);
             const float m = delta && j < i ? mm[r] * pp : 0.f;
-            Mg[i * C + j] = m;
-            Ag[i * C + j] = scale * aa[r] * pp;
+            if (Mg) {  // not kept by the bf16 path, which forms them again from k and q
+                Mg[i * C + j] = m;
+                Ag[i * C + j] = scale * aa[r] * pp;
+            }
             if (s4 < 3 && t < 10) {
                 rv[s4 < 3 ? s4 : 0][r] = sBeta[i] * m;
                 av[s4 < 3 ? s4 : 0][r] = scale * aa[r] * pp;
@@ -2028,8 +2038,8 @@ constexpr int kThreads16 = 512;  // eight wavefronts
 __global__ __launch_bounds__(kThreads16, 1) void bwd_grads16_kernel(
     const __bf16 *__restrict__ v, const float *__restrict__ dO, const __bf16 *__restrict__ kin,
     const __bf16 *__restrict__ qin, int T, int H, int NC, float eps, float scale, const float *__restrict__ wT,
-    const float *__restrict__ wM, const float *__restrict__ wA, const float *__restrict__ wG,
-    const float *__restrict__ wB, const char *__restrict__ rec, const char *__restrict__ rrev,
+    const float *__restrict__ wG, const float *__restrict__ wB, const char *__restrict__ rec,
+    const char *__restrict__ rrev,
     const float *__restrict__ wS, const float *__restrict__ wdS, float *__restrict__ dq, float *__restrict__ dk,
     float *__restrict__ dv, float *__restrict__ dg, float *__restrict__ dbeta, bool delta, bool kaczmarz,
     SeqTable tb) {
@@ -2218,16 +2228,12 @@ __global__ __launch_bounds__(kThreads16, 1) void bwd_grads16_kernel(
     // (in LDS from here on: T, dT'' -> dT -> dR -> W2, Y, dA with dM' above the diagonal, M, A -> W1 in T's
     // place once T is read, the bf16 rows of k and q; G, beta, dbeta, |k|^2, dG)
     constexpr int NCC = C * C / kThreads16;  // C x C values per thread
-    float rT[NCC], rM[NCC], rA[NCC];
+    float rT[NCC];
     uint4 rk[2], rq[2];
     {
-        const float *Tg = wT + (size_t)ci * C * C, *Mg = wM + (size_t)ci * C * C, *Ag = wA + (size_t)ci * C * C;
+        const float *Tg = wT + (size_t)ci * C * C;
 #pragma unroll
-        for (int u = 0; u < NCC; ++u) {
-            rT[u] = Tg[tid + u * kThreads16];
-            rM[u] = Mg[tid + u * kThreads16];
-            rA[u] = Ag[tid + u * kThreads16];
-        }
+        for (int u = 0; u < NCC; ++u) rT[u] = Tg[tid + u * kThreads16];
         const auto rkb = rows_rsrc(kin + row0u * DK, nu, H * DK * 2, DK * 2);
         const auto rqb = rows_rsrc(qin + row0u * DK, nu, H * DK * 2, DK * 2);
 #pragma unroll
@@ -2251,8 +2257,6 @@ __global__ __launch_bounds__(kThreads16, 1) void bwd_grads16_kernel(
     for (int u = 0; u < NCC; ++u) {
         const int idx = tid + u * kThreads16, r = idx / C, cc = idx % C;
         sT[r * kLCB + cc] = rT[u];
-        sMm[r * kLCB + cc] = rM[u];
-        sAa[r * kLCB + cc] = rA[u];
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -2265,6 +2269,25 @@ __global__ __launch_bounds__(kThreads16, 1) void bwd_grads16_kernel(
         sm.beta[tid] = wB[(size_t)ci * C + tid];
     }
     barrier_lds();
+    {  // M_ij = (k k')_ij exp(G_i - G_j), j < i (h = 0), and A_ij = scale (q k')_ij exp(G_i - G_j), j <= i
+       // (h = 1): rows 16 w .., column tiles J <= w; exact bf16 products (only the lower parts are read)
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            if (J > w) continue;
+            f32x4 acc = z4;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                acc = mx::mma(h == 0 ? kA[kb] : rows_operand(sQb, kLQB, w, kb, lr, lg),
+                              rows_operand(sKb, kLQB, J, kb, lr, lg), acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * w + 4 * lg + r, j = 16 * J + lr;
+                const float p = j <= i ? __expf(sm.G[i] - sm.G[j]) : 0.f;
+                if (h == 0) sMm[i * kLCB + j] = delta && j < i ? acc[r] * p : 0.f;
+                else sAa[i * kLCB + j] = scale * acc[r] * p;
+            }
+        }
+    }
     // parts of dG through Q~, K~, K^ (rows 16 w .., channel tiles 4 h ..): dK~ K~ + dQ~ Q~ - dK^ K^ summed
     // over the channels, and for G_63 the column sums of dK^ K^; dbeta_j = sum_i dT''_ij T_ij
     auto kval = [&](int r, int c) { return static_cast<float>(sKb[r * kLQB + c]); };
@@ -2400,34 +2423,38 @@ __global__ __launch_bounds__(kThreads16, 1) void bwd_grads16_kernel(
         sX[i * kLCB + j] = scale * sD[i * kLCB + j] * p;  // zero above the diagonal
     }
     barrier_lds();
-    // pair terms, rows 16 w .., channel tiles 4 h ..: dk += W1 K + W1' K + W2' Q, dq += W2 K (token j =
-    // 16 t + 4 lg + e in step (t, e): four tokens of a lane group are one transposing read of k or q)
+    // pair terms, rows 16 w .., channel tiles 4 h ..: dk += W1 K + W1' K + W2' Q, dq += W2 K, on bf16 tiles
+    // (W1 + W1', W2', W2 split into hi + lo over token block kb; k, q exact, by transposing reads)
     {
         f32x4 pk[JH], pq[JH];
 #pragma unroll
         for (int J = 0; J < JH; ++J) pk[J] = pq[J] = z4;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            float ak[4], aq[4], ad[4];
+        for (int kb = 0; kb < 2; ++kb) {
+            float ak[8], aq[8], ad[8];
+            const int i = 16 * w + lr;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = 16 * t + 4 * lg + e;
-                ak[e] = sT[(16 * w + lr) * kLCB + j] + sT[j * kLCB + 16 * w + lr];  // W1 + W1'
-                aq[e] = sX[j * kLCB + 16 * w + lr];                                   // W2'
-                ad[e] = sX[(16 * w + lr) * kLCB + j];                                 // W2
+            for (int e = 0; e < 8; ++e) {
+                const int j = 32 * kb + mx::kperm(lg, e);
+                ak[e] = sT[i * kLCB + j] + sT[j * kLCB + i];  // W1 + W1'
+                aq[e] = sX[j * kLCB + i];                     // W2'
+                ad[e] = sX[i * kLCB + j];                     // W2
             }
+            bf16x8 akh, akl, aqh, aql, adh, adl;
+            mx::split8(ak, akh, akl);
+            mx::split8(aq, aqh, aql);
+            mx::split8(ad, adh, adl);
 #pragma unroll
             for (int J = 0; J < JH; ++J) {
-                const int at = (16 * t + 4 * lg + (lr >> 2)) * kLQB + 16 * (JH * h + J) + 4 * (lr & 3);
-                const mx::bf16x4 k4 = mx::lds_read_tr(&sKb[at]);
-                const mx::bf16x4 q4 = mx::lds_read_tr(&sQb[at]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float kb = static_cast<float>(k4[e]), qb = static_cast<float>(q4[e]);
-                    pk[J] = mfma4(ak[e], kb, pk[J]);
-                    pk[J] = mfma4(aq[e], qb, pk[J]);
-                    pq[J] = mfma4(ad[e], kb, pq[J]);
-                }
+                const int jc = JH * h + J;
+                const bf16x8 k8 = vals_operand(sKb + 32 * kb * kLQB, kLQB, jc, lr, lg);
+                const bf16x8 q8 = vals_operand(sQb + 32 * kb * kLQB, kLQB, jc, lr, lg);
+                pk[J] = mx::mma(akh, k8, pk[J]);
+                pk[J] = mx::mma(akl, k8, pk[J]);
+                pk[J] = mx::mma(aqh, q8, pk[J]);
+                pk[J] = mx::mma(aql, q8, pk[J]);
+                pq[J] = mx::mma(adh, k8, pq[J]);
+                pq[J] = mx::mma(adl, k8, pq[J]);
             }
         }
         // dq, dk: the parts through Q~, K~, K^ and the pair terms (rows past the end are not written)
@@ -3138,8 +3165,8 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
     if constexpr (bwd_walk16(ops, DK, DV)) {  // every per-chunk gradient in one kernel
         hipLaunchKernelGGL(bwd_grads16_kernel, dim3(nslot), dim3(kThreads16), 0, a.stream,
                            static_cast<const __bf16 *>(a.v), a.dO, static_cast<const __bf16 *>(a.k),
-                           static_cast<const __bf16 *>(a.q), a.T, a.H, a.NC, a.eps, a.scale, w.T, w.M, w.A, w.G,
-                           w.beta, static_cast<const char *>(w.rec), static_cast<const char *>(w.rrev), w.S, w.dS,
+                           static_cast<const __bf16 *>(a.q), a.T, a.H, a.NC, a.eps, a.scale, w.T, w.G, w.beta,
+                           static_cast<const char *>(w.rec), static_cast<const char *>(w.rrev), w.S, w.dS,
                            a.dq, a.dk, a.dv, a.dg, a.dbeta, a.delta, a.kaczmarz, a.tab);
         return hipGetLastError();
     } else

@@ -283,11 +283,12 @@ def test_backward_workspace_and_validation():
     """Per chunk slot: T, A, M, dA, dT'' (64 x 64 fp32 each), G and dG (64 x
     GK), GK, beta (64), the entering state and its gradient (Dk x Dv each),
     and the decayed K~, K^, Q~ (64 x Dk each) unless the decay is scalar and
-    q, k are bf16 (then the kernels form them from k, q and the token factors);
-    with bf16 q, k at d = 128 and scalar decay also the chunk records of the
-    bf16 walks: the forward walk's (25,088 bytes: T'' and A as bf16 hi/lo
-    fragments, two decay rows) and the reverse walk's (24,576 bytes: the
-    transposes of T'' and A as bf16 hi/lo fragments)."""
+    q, k are bf16 (then the kernels form them from k, q and the token factors).
+    With bf16 q, k at d = 128 and scalar decay: no A, M, dA, dT'', dG, dG63
+    (one kernel forms and uses them), and the chunk records of the bf16 walks: the
+    forward walk's (25,088 bytes: T'' and A as bf16 hi/lo fragments, two
+    decay rows) and the reverse walk's (24,576 bytes: the transposes of T''
+    and A as bf16 hi/lo fragments)."""
     lib = gdr.load_library()
     n = ctypes.c_size_t(0)
 
@@ -296,7 +297,7 @@ def test_backward_workspace_and_validation():
         return rc, n.value
 
     slots = 2 * 3 * 2
-    assert ws(_desc()) == (0, slots * (4 * (5 * 4096 + 2 * 64 + 1 + 64 + 2 * 128 * 128) + 25088 + 24576))
+    assert ws(_desc()) == (0, slots * (4 * (4096 + 64 + 64 + 2 * 128 * 128) + 25088 + 24576))
     assert ws(_desc(Dv=64)) == (0, slots * 4 * (5 * 4096 + 2 * 64 + 1 + 64 + 2 * 128 * 64))
     assert ws(_desc(qkv_dtype=__import__("torch").float32)) == (
         0, slots * 4 * (5 * 4096 + 2 * 64 + 1 + 64 + 2 * 128 * 128 + 3 * 64 * 128))
@@ -344,7 +345,7 @@ def test_backward_varlen_workspace_and_validation():
     N, T, H = 5, 1000, 3
     nc = (T + 63 * N) // 64
     table = -(-4 * (2 * (N + 1) + 2 * nc + N) // 256) * 256
-    slot = 4 * (5 * 4096 + 2 * 64 + 1 + 64 + 2 * 128 * 128) + 25088 + 24576  # bf16, scalar: records, no K~, K^, Q~
+    slot = 4 * (4096 + 64 + 64 + 2 * 128 * 128) + 25088 + 24576  # bf16, scalar: T, G, beta, states, records
     assert ws(_desc(B=N, T=T, H=H)) == (0, table + nc * H * slot)
     d = _desc(B=N, T=T, H=H)
     wsb = ws(d)[1]
