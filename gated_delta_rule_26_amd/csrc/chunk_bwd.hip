@@ -49,45 +49,16 @@ namespace gdr {
 namespace {
 
 using mx::state_slot;
+using mx::kRevTH;
+using mx::kRevTL;
+using mx::kRevAH;
+using mx::kRevAL;
+using mx::kRevBytes;
+using mx::upper_frag;
 constexpr int C = kChunk;
 constexpr int kThreads = 256;
 constexpr int kBV = 32;  // value columns per walk workgroup
 constexpr int kBS = 16;  // value columns per slice of grads A
-
-// ---- the reverse record of the bf16 reverse walk (bwd_dstates_bf16_kernel), per chunk slot
-constexpr int kRevTH = 0;                    // T''' hi, lo; A' hi, lo: six fragments each
-constexpr int kRevTL = 6 * mx::kFragBytes;
-constexpr int kRevAH = 12 * mx::kFragBytes;
-constexpr int kRevAL = 18 * mx::kFragBytes;
-constexpr int kRevBytes = 24 * mx::kFragBytes;
-// Upper-triangular fragment f (M, kb): rows 16 M .. of a 64 x 64 matrix, columns 32 kb + kperm(p, e).
-__host__ __device__ constexpr int upper_frag(int M, int kb) { return M < 2 ? 2 * M + kb : M + 2; }
-__host__ __device__ constexpr int ufrag_M(int f) { return f < 4 ? f >> 1 : f - 2; }
-__host__ __device__ constexpr int ufrag_kb(int f) { return f < 4 ? f & 1 : 1; }
-
-// The reverse record of one chunk from prep's tiles: T''' = Diag(beta) T' and A' as bf16 hi/lo A-operand
-// fragments of their upper triangles.
-__device__ __forceinline__ void pack_reverse(const mx::TriTiles &t, const float *beta, char *dst, int tid) {
-    for (int u = tid; u < 2 * 6 * 64; u += kThreads) {
-        const int mat = u / 384, f = (u >> 6) % 6, l = u & 63;
-        const int i = 16 * ufrag_M(f) + (l & 15), p = l >> 4, kb = ufrag_kb(f);
-        mx::bf16x8 hv, lv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int j = 32 * kb + mx::kperm(p, e);
-            float x = 0.f;
-            if (j >= i) {
-                const int I = i >> 4, J = j >> 4, at = (j & 15) * mx::LT + (i & 15);
-                x = mat == 0 ? t.Tb(J, I)[at] * beta[i] : t.A[mx::tile_id(J, I) * mx::kTile + at];
-            }
-            hv[e] = static_cast<__bf16>(x);
-            lv[e] = static_cast<__bf16>(x - static_cast<float>(hv[e]));
-        }
-        char *d = dst + (mat == 0 ? kRevTH : kRevAH) + f * mx::kFragBytes + l * 16;
-        *reinterpret_cast<mx::bf16x8 *>(d) = hv;
-        *reinterpret_cast<mx::bf16x8 *>(d + 6 * mx::kFragBytes) = lv;
-    }
-}
 
 // ---- workspace, per chunk slot ci (fixed-length: (b H + h) NC + c; packed: u H + h)
 struct BwdWs {
@@ -337,9 +308,7 @@ constexpr int kLB = 48;   // B operands of 32 columns, read column-wise
 // K~, K^, Q~ are written next; then the LDS that held k and q holds R as
 // 16x16 tiles and T = (I + R)^-1 is formed by the block inverse of the
 // forward pass's intra kernel (forward substitution on the diagonal blocks,
-// matrix-core products for the others).  With `rec` (scalar decay) the chunk
-// record of the forward pass's bf16 walk is written too, from the same T and
-// A: T'' and A as bf16 hi/lo operand fragments, exp(G) and exp(G_63 - G).
+// matrix-core products for the others).
 constexpr float kSpanMax = 64.f;
 
 template <int DK, bool PC, bool KZ, bool IN_BF16>
@@ -347,10 +316,9 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, int T, int H, int NC, float eps, float scale, float *__restrict__ wT,
     float *__restrict__ wA, float *__restrict__ wM, float *__restrict__ wG, float *__restrict__ wB,
-    float *__restrict__ wKt, float *__restrict__ wKh, float *__restrict__ wQt, char *__restrict__ rec,
-    char *__restrict__ rrev, bool delta, SeqTable tb) {
+    float *__restrict__ wKt, float *__restrict__ wKh, float *__restrict__ wQt, bool delta, SeqTable tb) {
     constexpr int GK = PC ? DK : 1;
-    static_assert(2 * C * (DK + 1) >= 26 * mx::kTile, "the R, T and A tiles must fit where k and q were");
+    static_assert(2 * C * (DK + 1) >= 16 * mx::kTile, "the R and T tiles must fit where k and q were");
     const int ci = blockIdx.x;
     if (!slot_used(ci, H, tb)) return;
     const Slot sl = slot_of(ci, T, H, NC, tb);
@@ -467,8 +435,8 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
     }
 
     // ---- M and A; this wavefront's R = Diag(beta) M values stay in registers
-    float *Mg = wM ? wM + (size_t)ci * C * C : nullptr, *Ag = wA ? wA + (size_t)ci * C * C : nullptr;
-    f32x4 rv[3], av[3];  // this wavefront's lower tiles of R and (for the record) A
+    float *Mg = wM + (size_t)ci * C * C, *Ag = wA + (size_t)ci * C * C;
+    f32x4 rv[3];
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
         const int t = w + 4 * s4;
@@ -522,14 +490,9 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
             const int i = 16 * I + 4 * lg + r, j = 16 * J + lr;
             const float pp = PC ? (j <= i ? 1.f : 0.f) : (j <= i ? __expf(sG[i][0] - sG[j][0]) : 0.f);
             const float m = delta && j < i ? mm[r] * pp : 0.f;
-            if (Mg) {  // not kept by the bf16 path, which forms them again from k and q
-                Mg[i * C + j] = m;
-                Ag[i * C + j] = scale * aa[r] * pp;
-            }
-            if (s4 < 3 && t < 10) {
-                rv[s4 < 3 ? s4 : 0][r] = sBeta[i] * m;
-                av[s4 < 3 ? s4 : 0][r] = scale * aa[r] * pp;
-            }
+            Mg[i * C + j] = m;
+            Ag[i * C + j] = scale * aa[r] * pp;
+            if (s4 < 3 && t < 10) rv[s4 < 3 ? s4 : 0][r] = sBeta[i] * m;
         }
     }
     for (int idx = tid; idx < C * GK; idx += kThreads) wG[(size_t)ci * C * GK + idx] = sG[idx / GK][idx % GK];
@@ -562,7 +525,7 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
 
     // ---- T = (I + R)^-1 on 16x16 tiles in the LDS of k and q
     float *tiles = &sKQ[0][0][0];
-    const mx::TriTiles tri{tiles, tiles + 10 * mx::kTile, tiles + 16 * mx::kTile};
+    const mx::TriTiles tri{tiles, tiles + 10 * mx::kTile, nullptr};
 #pragma unroll
     for (int s4 = 0; s4 < 3; ++s4) {
         const int t = w + 4 * s4;
@@ -572,26 +535,10 @@ __global__ __launch_bounds__(kThreads, PC ? 1 : 2) void bwd_prep_kernel(
             float *dst = &tri.R[mx::tile_id(I, J) * mx::kTile];
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(4 * lg + r) * mx::LT + lr] = rv[s4][r];
-            if (!PC && rec) {
-                float *da = &tri.A[mx::tile_id(I, J) * mx::kTile];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) da[(4 * lg + r) * mx::LT + lr] = av[s4][r];
-            }
         }
     }
     __syncthreads();
     mx::invert_unit_lower(tri, lane, w, lr, lg);  // ends with a barrier
-    if constexpr (!PC) {
-        if (rec) {  // the forward walk's record of this chunk
-            char *recb = rec + (size_t)ci * mx::kRecBytes;
-            mx::pack_T_A<true>(tri, sBeta, recb, tid);
-            if (tid < C) {
-                reinterpret_cast<float *>(recb + mx::kRecGam)[tid] = sE[0][tid];
-                reinterpret_cast<float *>(recb + mx::kRecGend)[tid] = sE[1][tid];
-            }
-            if (rrev) pack_reverse(tri, sBeta, rrev + (size_t)ci * kRevBytes, tid);
-        }
-    }
     float *Tg = wT + (size_t)ci * C * C;
     for (int idx4 = tid; idx4 < C * C / 4; idx4 += kThreads) {  // 16-byte stores
         const int i = idx4 / (C / 4), j = (idx4 % (C / 4)) * 4, I = i >> 4, J = j >> 4;
@@ -2137,6 +2084,7 @@ __global__ __launch_bounds__(kThreads16, 1) void bwd_grads16_kernel(
         fetch(min(j0 + kSW, DV - kSW));
         barrier_lds();
         // ---- X = V - exp(G) (k S),  dE = exp(G_63 - G) (k dS') + A' dO  (value tile h)
+        f32x4 x, de;
         {
             const int vt = h;
             f32x4 ps = z4, pd = z4;
@@ -2150,23 +2098,24 @@ __global__ __launch_bounds__(kThreads16, 1) void bwd_grads16_kernel(
                 pd = mx::mma(kA[kb], vals_operand(sm.u.a.dS[0] + rb, kLSV, vt, lr, lg), pd);
                 pd = mx::mma(kA[kb], vals_operand(sm.u.a.dS[1] + rb, kLSV, vt, lr, lg), pd);
             }
-            f32x4 de = gnd * pd;
+            de = gnd * pd;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
                 if (kb >= (w >> 1))
                     de = mma3(auh[kb], aul[kb], vals_operand(sm.u.a.O[0] + 32 * kb * kLSV, kLSV, vt, lr, lg),
                               vals_operand(sm.u.a.O[1] + 32 * kb * kLSV, kLSV, vt, lr, lg), de);
-            const f32x4 x = vv - gam * ps;
+            x = vv - gam * ps;
             store_tile(sm.u.a.X[0], sm.u.a.X[1], w, vt, x, lr, lg);
             store_tile(sm.u.a.dE[0], sm.u.a.dE[1], w, vt, de, lr, lg);
         }
         barrier_lds();
-        // ---- E = T'' X (token blocks kb <= w / 2),  dX = T''' dE (kb >= w / 2) = dV  (value tile h)
+        // ---- E = T'' X (token blocks kb <= w / 2),  dX = T''' dE (kb >= w / 2) = dV  (value tile h);
+        // without the delta rule T'' = I (E = X = V, dX = dE)
         {
             const int vt = h;
-            f32x4 ee = z4, dx = z4;
+            f32x4 ee = delta ? z4 : x, dx = delta ? z4 : de;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < 2 && delta; ++kb) {
                 if (kb <= (w >> 1))
                     ee = mma3(tlh[kb], tll[kb], rows_operand(sm.u.a.X[0], kLST, vt, kb, lr, lg),
                               rows_operand(sm.u.a.X[1], kLST, vt, kb, lr, lg), ee);
@@ -3101,6 +3050,48 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_walk_kernel(
 }
 
 // ============================================================ launch
+// bf16 q, k at d = 128 with scalar decay: the forward intra kernel's per-chunk work with its backward outputs,
+// the forward pass's bf16 walk storing the entering states, the bf16 reverse walk, then every per-chunk
+// gradient in one kernel.
+hipError_t launch_bwd16(const BwdArgs &a, const BwdWs &w, unsigned nslot, unsigned nwalk) {
+    ChunkArgs f{};
+    f.B = a.B;
+    f.T = a.T;
+    f.H = a.H;
+    f.Dk = mx::DK;
+    f.Dv = mx::DV;
+    f.NC = a.NC;
+    f.tab = a.tab;
+    f.qkv_bf16 = true;
+    f.kaczmarz = a.kaczmarz;
+    f.delta = a.delta;
+    f.eps = a.eps;
+    f.scale = a.scale;
+    f.q = a.q;
+    f.k = a.k;
+    f.v = a.v;
+    f.g = a.g;
+    f.beta = a.beta;
+    f.s0 = a.s0;
+    f.ws = w.rec;
+    f.stream = a.stream;
+    hipError_t e = launch_chunk_prep_bwd(f, w.T, w.G, w.beta, static_cast<char *>(w.rrev));
+    if (e != hipSuccess || (e = launch_chunk_states(f, w.S)) != hipSuccess) return e;
+    const __bf16 *qb = static_cast<const __bf16 *>(a.q), *kb = static_cast<const __bf16 *>(a.k);
+    const char *rec = static_cast<const char *>(w.rec), *rrev = static_cast<const char *>(w.rrev);
+    if (a.delta)
+        hipLaunchKernelGGL((bwd_dstates_bf16_kernel<true>), dim3(nwalk), dim3(kThreads), 0, a.stream, qb, kb, a.dO,
+                           a.T, a.H, a.NC, a.scale, rec, rrev, a.ds_final, w.dS, a.ds0, a.tab);
+    else
+        hipLaunchKernelGGL((bwd_dstates_bf16_kernel<false>), dim3(nwalk), dim3(kThreads), 0, a.stream, qb, kb, a.dO,
+                           a.T, a.H, a.NC, a.scale, rec, rrev, a.ds_final, w.dS, a.ds0, a.tab);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_grads16_kernel, dim3(nslot), dim3(kThreads16), 0, a.stream, static_cast<const __bf16 *>(a.v),
+                       a.dO, kb, qb, a.T, a.H, a.NC, a.eps, a.scale, w.T, w.G, w.beta, rec, rrev, w.S, w.dS, a.dq, a.dk,
+                       a.dv, a.dg, a.dbeta, a.delta, a.kaczmarz, a.tab);
+    return hipGetLastError();
+}
+
 template <int DK, int DV, bool PC, bool KZ, bool IB>
 hipError_t launch_bwd_t(const BwdArgs &a) {
     // packed batch: a.NC is the chunk bound of all sequences together
@@ -3109,35 +3100,13 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
     BwdWs w = carve_bwd<DK, DV, PC>(a.ws, slots, ops);
     const unsigned nslot = (unsigned)slots;
     const unsigned nwalk = (unsigned)(a.B * a.H * (DV / kBV));
+    if constexpr (bwd_walk16(ops, DK, DV)) return launch_bwd16(a, w, nslot, nwalk);
     hipLaunchKernelGGL((bwd_prep_kernel<DK, PC, KZ, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.q, a.k, a.g,
-                       a.beta, a.T, a.H, a.NC, a.eps, a.scale, w.T, w.A, w.M, w.G, w.beta, w.Kt, w.Kh, w.Qt,
-                       static_cast<char *>(w.rec), static_cast<char *>(w.rrev), a.delta, a.tab);
+                       a.beta, a.T, a.H, a.NC, a.eps, a.scale, w.T, w.A, w.M, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.delta,
+                       a.tab);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if constexpr (bwd_walk16(ops, DK, DV)) {  // the forward pass's bf16 walk over the records prep wrote
-        ChunkArgs f{};
-        f.B = a.B;
-        f.T = a.T;
-        f.H = a.H;
-        f.Dk = DK;
-        f.Dv = DV;
-        f.NC = a.NC;
-        f.tab = a.tab;
-        f.qkv_bf16 = true;
-        f.kaczmarz = a.kaczmarz;
-        f.delta = a.delta;
-        f.eps = a.eps;
-        f.scale = a.scale;
-        f.q = a.q;
-        f.k = a.k;
-        f.v = a.v;
-        f.g = a.g;
-        f.beta = a.beta;
-        f.s0 = a.s0;
-        f.ws = w.rec;
-        f.stream = a.stream;
-        if ((e = launch_chunk_states(f, w.S)) != hipSuccess) return e;
-    } else if constexpr (ops)
+    if constexpr (ops)
         hipLaunchKernelGGL((bwd_states_kernel<DK, DV, PC, IB>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.v, a.T,
                            a.H, a.NC, w.T, w.G, w.beta, w.Kt, w.Kh, a.s0, w.S, a.delta, a.tab);
     else
@@ -3145,16 +3114,7 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
                            static_cast<const __bf16 *>(a.v), static_cast<const __bf16 *>(a.k), a.T, a.H, a.NC, w.T,
                            w.G, w.beta, a.s0, w.S, a.delta, a.tab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if constexpr (bwd_walk16(ops, DK, DV)) {  // bf16 tiles, the records prep wrote
-        const __bf16 *qb = static_cast<const __bf16 *>(a.q), *kb = static_cast<const __bf16 *>(a.k);
-        const char *rec = static_cast<const char *>(w.rec), *rrev = static_cast<const char *>(w.rrev);
-        if (a.delta)
-            hipLaunchKernelGGL((bwd_dstates_bf16_kernel<true>), dim3(nwalk), dim3(kThreads), 0, a.stream, qb, kb, a.dO,
-                               a.T, a.H, a.NC, a.scale, rec, rrev, a.ds_final, w.dS, a.ds0, a.tab);
-        else
-            hipLaunchKernelGGL((bwd_dstates_bf16_kernel<false>), dim3(nwalk), dim3(kThreads), 0, a.stream, qb, kb,
-                               a.dO, a.T, a.H, a.NC, a.scale, rec, rrev, a.ds_final, w.dS, a.ds0, a.tab);
-    } else if constexpr (!ops)  // scalar decay with bf16 inputs: the walk on k and q themselves
+    if constexpr (!ops)  // scalar decay with bf16 inputs: the walk on k and q themselves
         hipLaunchKernelGGL((bwd_dstates_kq16_kernel<DK, DV>), dim3(nwalk), dim3(kThreads), 0, a.stream,
                            static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), a.dO, a.T, a.H, a.NC,
                            a.scale, w.T, w.A, w.G, w.beta, a.ds_final, w.dS, a.ds0, a.delta, a.tab);
@@ -3162,18 +3122,10 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
         hipLaunchKernelGGL((bwd_dstates_kernel<DK, DV, PC>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.dO, a.T,
                            a.H, a.NC, w.T, w.A, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.ds_final, w.dS, a.ds0, a.delta, a.tab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if constexpr (bwd_walk16(ops, DK, DV)) {  // every per-chunk gradient in one kernel
-        hipLaunchKernelGGL(bwd_grads16_kernel, dim3(nslot), dim3(kThreads16), 0, a.stream,
-                           static_cast<const __bf16 *>(a.v), a.dO, static_cast<const __bf16 *>(a.k),
-                           static_cast<const __bf16 *>(a.q), a.T, a.H, a.NC, a.eps, a.scale, w.T, w.G, w.beta,
-                           static_cast<const char *>(w.rec), static_cast<const char *>(w.rrev), w.S, w.dS,
-                           a.dq, a.dk, a.dv, a.dg, a.dbeta, a.delta, a.kaczmarz, a.tab);
-        return hipGetLastError();
-    } else
-        hipLaunchKernelGGL((bwd_grads_a_kernel<DK, DV, PC, IB, !ops>), dim3(nslot), dim3(kThreads), 0, a.stream,
-                           a.v, a.dO, a.T, a.H, a.NC, a.scale, w.T, w.A, w.G, w.beta, w.S, w.dS, w.Kt, w.Kh, w.Qt,
-                           static_cast<const __bf16 *>(a.k), static_cast<const __bf16 *>(a.q), w.dA, w.dTT, w.dG,
-                           w.dG63, a.dq, a.dk, a.dv, a.delta, a.tab);
+    hipLaunchKernelGGL((bwd_grads_a_kernel<DK, DV, PC, IB, !ops>), dim3(nslot), dim3(kThreads), 0, a.stream, a.v,
+                       a.dO, a.T, a.H, a.NC, a.scale, w.T, w.A, w.G, w.beta, w.S, w.dS, w.Kt, w.Kh, w.Qt,
+                       static_cast<const __bf16 *>(a.k), static_cast<const __bf16 *>(a.q), w.dA, w.dTT, w.dG, w.dG63,
+                       a.dq, a.dk, a.dv, a.delta, a.tab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grads_b_kernel<DK, PC, KZ, IB>), dim3(nslot), dim3(kThreads), 0, a.stream, a.q, a.k,
                        a.T, a.H, a.NC, a.eps, a.scale, w.T, w.M, w.A, w.G, w.beta, w.dA, w.dTT, w.dG, w.dG63, a.dq,
@@ -3214,7 +3166,7 @@ hipError_t launch_tile_fwd_t(const ChunkArgs &a, int stage) {
     if (stage != 1) {
         GDR_LAUNCH((bwd_prep_kernel<DK, PC, KZ, IB>), dim3((unsigned)slots), dim3(kThreads), a.stream, a.ev0,
                    stage == 0 ? a.ev1 : nullptr, a.q, a.k, a.g, a.beta, a.T, a.H, a.NC, a.eps, a.scale, wT, wA, wM, wG,
-                   wB, wKt, wKh, wQt, nullptr, nullptr, a.delta, a.tab);
+                   wB, wKt, wKh, wQt, a.delta, a.tab);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess || stage == 0) return e;
     }

@@ -80,11 +80,15 @@ struct alignas(16) IntraSmem {
     float kk[C];                // |k_i|^2 (Kaczmarz only)
 };
 
-template <bool KZ, bool DELTA>
+// With BWD (the backward pass's per-chunk inputs) the kernel also writes, per chunk, T itself (fp32, zero
+// above the diagonal; the identity without the delta rule), G and the write strengths to bT, bG, bB, and
+// the reverse record (the transposes of T'' and A as bf16 hi/lo fragments) to brev.
+template <bool KZ, bool DELTA, bool BWD = false>
 __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, int T, int H, int NC, int total, float eps, float scale,
-    char *__restrict__ ws, SeqTable tb) {
+    char *__restrict__ ws, SeqTable tb, float *__restrict__ bT, float *__restrict__ bG, float *__restrict__ bB,
+    char *__restrict__ brev) {
     __shared__ IntraSmem sm;
     if (tb.start) total = tb.cbase[tb.N] * H;  // packed batch: the chunks the table holds
     if (total <= 0) return;
@@ -235,6 +239,21 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_matrix_kernel(
     // ---- T = (I + R)^{-1}, then the T'' and A operand fragments
     if constexpr (DELTA) invert_unit_lower(tri, lane, w, lr, lg);
     pack_T_A<DELTA>(tri, sm.eta, recb, tid);
+    if constexpr (BWD) {
+        float *Tg = bT + (size_t)ci * C * C;
+        for (int idx4 = tid; idx4 < C * C / 4; idx4 += kIntraThreads) {  // 16-byte stores
+            const int i = idx4 / (C / 4), j = (idx4 % (C / 4)) * 4, I = i >> 4, J = j >> 4;
+            f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
+            if (DELTA && J <= I) t4 = *reinterpret_cast<const f32x4 *>(&tri.Tb(I, J)[(i & 15) * LT + (j & 15)]);
+            else if (!DELTA && (i >> 2) == (j >> 2)) t4[i & 3] = 1.f;  // the identity
+            reinterpret_cast<f32x4 *>(Tg)[idx4] = t4;
+        }
+        if (tid < C) {
+            bG[(size_t)ci * C + tid] = sm.G[tid];
+            bB[(size_t)ci * C + tid] = sm.eta[tid];
+        }
+        pack_reverse<DELTA>(tri, sm.eta, brev + (size_t)ci * kRevBytes, tid);
+    }
     }  // chunk loop
 }
 
@@ -680,7 +699,7 @@ hipError_t launch_intra(const ChunkArgs &a) {
     if (total == 0) return hipSuccess;
     GDR_LAUNCH((intra_matrix_kernel<KZ, DELTA>), dim3(intra_grid(total, 4)), dim3(kIntraThreads), a.stream, a.ev0,
                a.ev1, static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), a.g, a.beta, a.T, a.H, a.NC,
-               (int)total, a.eps, a.scale, static_cast<char *>(a.ws), a.tab);
+               (int)total, a.eps, a.scale, static_cast<char *>(a.ws), a.tab, nullptr, nullptr, nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -758,10 +777,28 @@ hipError_t launch_states_walk(const ChunkArgs &a, float *states) {
     return hipGetLastError();
 }
 
+// The backward pass's per-chunk inputs for bf16 q, k at d = 128 and scalar decay: the intra kernel with its
+// backward outputs.
+template <bool KZ, bool DELTA>
+hipError_t launch_intra_bwd(const ChunkArgs &a, float *bT, float *bG, float *bB, char *brev) {
+    const long total = chunk_slots(a);
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL((intra_matrix_kernel<KZ, DELTA, true>), dim3(intra_grid(total, 4)), dim3(kIntraThreads), 0,
+                       a.stream, static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), a.g, a.beta, a.T,
+                       a.H, a.NC, (int)total, a.eps, a.scale, static_cast<char *>(a.ws), a.tab, bT, bG, bB, brev);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_chunk_states(const ChunkArgs &a, float *states) {
     return a.delta ? launch_states_walk<true>(a, states) : launch_states_walk<false>(a, states);
+}
+
+hipError_t launch_chunk_prep_bwd(const ChunkArgs &a, float *T, float *G, float *beta, char *rrev) {
+    return !a.delta ? launch_intra_bwd<false, false>(a, T, G, beta, rrev)
+           : a.kaczmarz ? launch_intra_bwd<true, true>(a, T, G, beta, rrev)
+                        : launch_intra_bwd<false, true>(a, T, G, beta, rrev);
 }
 
 int mx::intra_grid(long total, int per_cu) {

@@ -103,6 +103,10 @@ hipError_t launch_chunk_tile(const ChunkArgs &a, int stage);
 // by the caller), the states to `states` at the records' indices ([Dk][Dv]
 // fp32 each).
 hipError_t launch_chunk_states(const ChunkArgs &a, float *states);
+// Its per-chunk inputs (the same case): the intra kernel's records into a.ws and, per chunk, T (fp32, 64 x
+// 64), G and the write strengths (64 each) and the reverse record (the transposes of T'' and A as bf16
+// hi/lo fragments, mx::kRevBytes) at the records' indices.
+hipError_t launch_chunk_prep_bwd(const ChunkArgs &a, float *T, float *G, float *beta, char *rrev);
 // Its per-channel-decay kernels (called by the two functions above).
 size_t chunk_matrix_pc_workspace_bytes(int B, int H, int NC);
 hipError_t launch_chunk_matrix_pc(const ChunkArgs &a, int stage);

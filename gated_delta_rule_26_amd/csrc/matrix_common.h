@@ -289,6 +289,43 @@ __device__ __forceinline__ void pack_T_A(const TriTiles &t, const float *beta, c
     }
 }
 
+// ---- the backward pass's reverse record of a chunk (scalar decay): the transposes of T'' and A as
+// bf16 hi + lo A-operand fragments of their upper triangles, for the reverse walk and the gradients.
+constexpr int kRevTH = 0;                    // T''' hi, lo; A' hi, lo: six fragments each
+constexpr int kRevTL = 6 * kFragBytes;
+constexpr int kRevAH = 12 * kFragBytes;
+constexpr int kRevAL = 18 * kFragBytes;
+constexpr int kRevBytes = 24 * kFragBytes;
+// Upper-triangular fragment f (M, kb): rows 16 M .. of a 64 x 64 matrix, columns 32 kb + kperm(p, e).
+__host__ __device__ constexpr int upper_frag(int M, int kb) { return M < 2 ? 2 * M + kb : M + 2; }
+__host__ __device__ constexpr int ufrag_M(int f) { return f < 4 ? f >> 1 : f - 2; }
+__host__ __device__ constexpr int ufrag_kb(int f) { return f < 4 ? f & 1 : 1; }
+
+// The reverse record from a chunk's tiles (T, A in LDS as the intra kernels keep them): T''' = Diag(beta) T'
+// and A' (A' only when WITH_T is false), by kIntraThreads threads.
+template <bool WITH_T>
+__device__ __forceinline__ void pack_reverse(const TriTiles &t, const float *beta, char *dst, int tid) {
+    for (int u = tid + (WITH_T ? 0 : 6 * 64); u < 2 * 6 * 64; u += kIntraThreads) {
+        const int mat = u / 384, f = (u >> 6) % 6, l = u & 63;
+        const int i = 16 * ufrag_M(f) + (l & 15), p = l >> 4, kb = ufrag_kb(f);
+        bf16x8 hv, lv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int j = 32 * kb + kperm(p, e);
+            float x = 0.f;
+            if (j >= i) {
+                const int I = i >> 4, J = j >> 4, at = (j & 15) * LT + (i & 15);
+                x = mat == 0 ? t.Tb(J, I)[at] * beta[i] : t.A[tile_id(J, I) * kTile + at];
+            }
+            hv[e] = static_cast<__bf16>(x);
+            lv[e] = static_cast<__bf16>(x - static_cast<float>(hv[e]));
+        }
+        char *d = dst + (mat == 0 ? kRevTH : kRevAH) + f * kFragBytes + l * 16;
+        *reinterpret_cast<bf16x8 *>(d) = hv;
+        *reinterpret_cast<bf16x8 *>(d + 6 * kFragBytes) = lv;
+    }
+}
+
 // ---- state walk
 constexpr int kStateThreads = 256;  // chain wavefronts 0, 1; helper wavefronts 2, 3
 constexpr int BV = 32;              // value columns per workgroup
