@@ -757,7 +757,7 @@ def main():
         bwd = bench_backward(w, x, args.backward_steps, 1)
         out["backward"] = {
             "workload": f"{w.name}: gdr_chunk_bwd on the same inputs, standard-normal dL/do, fp32 gradients "
-                        f"(fp32 arithmetic, matrix-core tiles)",
+                        f"({'fp32 tiles' if w.per_channel or w.dtype != 'bf16' or w.Dk != 128 or w.Dv != 128 else 'bf16 tiles with hi/lo split fp32 operands'})",
             **bwd,
             "train_step_tokens_per_s": w.B * w.T / ((head["warm"]["event_step_ms"] + bwd["ms_per_step"]) * 1e-3),
         }

@@ -1,6 +1,10 @@
-// Backward pass of the chunked forward pass (training), fp32 arithmetic: the
-// products on fp32 matrix-core tiles (v_mfma_f32_16x16x4_f32), the rest on the
-// vector ALUs.
+// Backward pass of the chunked forward pass (training).  For bf16 q/k/v at
+// d_k = d_v = 128 with scalar decay the products run on bf16 matrix-core
+// tiles with every fp32 operand split into hi + lo, as in the forward pass
+// (launch_bwd16: the forward intra kernel and walk of chunk_matrix.hip with
+// backward outputs, the reverse walk and one gradient kernel below); for
+// every other input on fp32 tiles (v_mfma_f32_16x16x4_f32), in the five
+// kernels listed further down.
 //
 // The pages derive no backward pass (the blog summary on the DeltaNet family
 // calls the chunked mode the training mode, "Pipeline Triton por chunks"), so
@@ -24,7 +28,7 @@
 // beta = eta / (|k|^2 + eps): deta = dbeta / (|k|^2 + eps),
 // dk += -2 beta dbeta / (|k|^2 + eps) k.
 //
-// Five kernels:
+// Five kernels on fp32 tiles:
 //  * prep (one workgroup per chunk): G, beta, M, A and T (as the forward
 //    vector intra kernel, with T itself instead of W and U);
 //  * forward walk (one workgroup per (sequence, head, 32 value columns)): the

@@ -190,7 +190,9 @@ int gdr_chunk_fwd_varlen(const gdr_desc *desc, const int32_t *cu_seqlens,
  * backward pass (the blog summary, "Pipeline Triton por chunks", calls the
  * chunked mode the training mode); it is reverse-mode differentiation of the
  * chunk algebra of gdr_chunk_fwd, with the chunk-entering states recomputed.
- * fp32 arithmetic (products on fp32 matrix-core tiles); fixed-length
+ * Products on matrix-core tiles: bf16 with fp32 operands split into hi + lo
+ * (the forward's arithmetic) for bf16 q/k/v at Dk = Dv = 128 with scalar
+ * decay, fp32 otherwise; fp32 accumulation and gradients; fixed-length
  * batches (packed ones: gdr_chunk_bwd_varlen below); desc->algo and
  * desc->o_dtype are ignored.  With GDR_DELTA_OFF
  * (the additive write) beta_or_eta and dbeta are ignored and may be NULL.
