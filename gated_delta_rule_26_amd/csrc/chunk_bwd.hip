@@ -85,14 +85,16 @@ constexpr bool bwd_stores_ops(bool per_channel, bool qkv_bf16) { return per_chan
 // the workspace.
 constexpr bool bwd_walk16(bool ops, int Dk, int Dv) { return !ops && Dk == 128 && Dv == 128; }
 
+// The bf16 path's records lead the workspace: the forward walk's, the segment space of its states walk
+// (time segments of long sequences), the reverse walk's.
 template <int DK, int DV, bool PC>
-BwdWs carve_bwd(void *ws, size_t slots, bool ops) {
+BwdWs carve_bwd(void *ws, size_t slots, bool ops, int BH, int NC) {
     constexpr int GK = PC ? DK : 1;
     BwdWs w;
     w.rec = w.rrev = nullptr;
     if (bwd_walk16(ops, DK, DV)) {
         w.rec = ws;
-        w.rrev = static_cast<char *>(ws) + slots * mx::kRecBytes;
+        w.rrev = static_cast<char *>(ws) + slots * mx::kRecBytes + chunk_states_segment_bytes(BH, NC);
         ws = static_cast<char *>(w.rrev) + slots * kRevBytes;
     }
     float *p = static_cast<float *>(ws);
@@ -123,13 +125,13 @@ BwdWs carve_bwd(void *ws, size_t slots, bool ops) {
 }
 
 template <int DK, int DV, bool PC>
-size_t bwd_bytes(size_t slots, bool ops) {
+size_t bwd_bytes(size_t slots, bool ops, int BH, int NC) {
     constexpr int GK = PC ? DK : 1;
     const bool walk16 = bwd_walk16(ops, DK, DV);
     const size_t grads = walk16 ? 0 : (size_t)4 * C * C + (size_t)C * GK + GK;  // A, M, dA, dT'', dG, dG63
     return slots * sizeof(float) *
                ((size_t)C * C + (size_t)C * GK + C + 2 * (size_t)DK * DV + grads + (ops ? 3 * (size_t)C * DK : 0)) +
-           (walk16 ? slots * (mx::kRecBytes + kRevBytes) : 0);
+           (walk16 ? slots * (mx::kRecBytes + kRevBytes) + chunk_states_segment_bytes(BH, NC) : 0);
 }
 
 // chunk slot ci -> token row of its token 0 and token count.  Fixed-length
@@ -3101,7 +3103,7 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
     // packed batch: a.NC is the chunk bound of all sequences together
     const size_t slots = (size_t)(a.tab.start ? 1 : a.B) * a.H * a.NC;
     constexpr bool ops = bwd_stores_ops(PC, IB);  // K~, K^, Q~ in the workspace
-    BwdWs w = carve_bwd<DK, DV, PC>(a.ws, slots, ops);
+    BwdWs w = carve_bwd<DK, DV, PC>(a.ws, slots, ops, (a.tab.start ? 1 : a.B) * a.H, a.NC);
     const unsigned nslot = (unsigned)slots;
     const unsigned nwalk = (unsigned)(a.B * a.H * (DV / kBV));
     if constexpr (bwd_walk16(ops, DK, DV)) return launch_bwd16(a, w, nslot, nwalk);
@@ -3222,13 +3224,14 @@ hipError_t launch_chunk_tile(const ChunkArgs &a, int stage) {
 size_t chunk_bwd_workspace_bytes(int B, int H, int NC, int Dk, int Dv, bool per_channel, bool qkv_bf16) {
     const size_t slots = (size_t)B * H * NC;
     const bool ops = bwd_stores_ops(per_channel, qkv_bf16);
+    const int BH = B * H;
     if (Dk == 128 && Dv == 128)
-        return per_channel ? bwd_bytes<128, 128, true>(slots, ops) : bwd_bytes<128, 128, false>(slots, ops);
+        return per_channel ? bwd_bytes<128, 128, true>(slots, ops, BH, NC) : bwd_bytes<128, 128, false>(slots, ops, BH, NC);
     if (Dk == 128 && Dv == 64)
-        return per_channel ? bwd_bytes<128, 64, true>(slots, ops) : bwd_bytes<128, 64, false>(slots, ops);
+        return per_channel ? bwd_bytes<128, 64, true>(slots, ops, BH, NC) : bwd_bytes<128, 64, false>(slots, ops, BH, NC);
     if (Dk == 64 && Dv == 128)
-        return per_channel ? bwd_bytes<64, 128, true>(slots, ops) : bwd_bytes<64, 128, false>(slots, ops);
-    return per_channel ? bwd_bytes<64, 64, true>(slots, ops) : bwd_bytes<64, 64, false>(slots, ops);
+        return per_channel ? bwd_bytes<64, 128, true>(slots, ops, BH, NC) : bwd_bytes<64, 128, false>(slots, ops, BH, NC);
+    return per_channel ? bwd_bytes<64, 64, true>(slots, ops, BH, NC) : bwd_bytes<64, 64, false>(slots, ops, BH, NC);
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs &a) {

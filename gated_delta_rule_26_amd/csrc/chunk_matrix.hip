@@ -764,16 +764,36 @@ hipError_t launch_state(const ChunkArgs &a) {
     return hipGetLastError();
 }
 
-// The backward pass's walk: one workgroup per (sequence, head, 32 value
-// columns), every chunk of the sequence, the entering states to `states`.
+// The backward pass's walk: one workgroup per (sequence, head, time segment,
+// 32 value columns), the entering states to `states`.  Time segments as in
+// launch_state (fixed-length batches): the chunk maps, the entering state of
+// every segment, then the segments' walks.
 template <bool DELTA>
 hipError_t launch_states_walk(const ChunkArgs &a, float *states) {
     if (chunk_slots(a) == 0) return hipSuccess;
     const int BH = a.B * a.H;
-    GDR_LAUNCH((state_matrix_kernel<false, true, DELTA, true>), dim3((unsigned)(BH * NS)), dim3(kStateThreads),
-               a.stream, nullptr, nullptr, static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k),
-               static_cast<const __bf16 *>(a.v), static_cast<const char *>(a.ws), a.s0, nullptr, states, a.T, a.H,
-               a.NC, BH, 1, a.NC, a.scale, a.tab);
+    const int P = a.tab.start ? 1 : walk_segments(BH, a.NC);
+    const __bf16 *q = static_cast<const __bf16 *>(a.q), *k = static_cast<const __bf16 *>(a.k),
+                 *v = static_cast<const __bf16 *>(a.v);
+    const char *ws = static_cast<const char *>(a.ws);
+    const int seg = (a.NC + P - 1) / P;
+    const float *s_in = a.s0;
+    if (P > 1) {
+        float *tr = reinterpret_cast<float *>(static_cast<char *>(a.ws) + (size_t)BH * a.NC * kRecBytes);
+        float *seg_state = tr + (size_t)BH * P * 2 * DK * DV;
+        hipLaunchKernelGGL((state_matrix_kernel<false, true, DELTA>), dim3((unsigned)(BH * P * 2 * NS)),
+                           dim3(kStateThreads), 0, a.stream, q, k, v, ws, nullptr, nullptr, tr, a.T, a.H, a.NC, BH * P,
+                           P, seg, a.scale, SeqTable{});
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(segment_combine_kernel, dim3((unsigned)(BH * (DV / kCombineCols))), dim3(256), 0, a.stream,
+                           tr, a.s0, seg_state, P);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        s_in = seg_state;
+    }
+    hipLaunchKernelGGL((state_matrix_kernel<false, true, DELTA, true>), dim3((unsigned)(BH * P * NS)),
+                       dim3(kStateThreads), 0, a.stream, q, k, v, ws, s_in, nullptr, states, a.T, a.H, a.NC, BH * P, P,
+                       seg, a.scale, a.tab);
     return hipGetLastError();
 }
 
@@ -790,6 +810,8 @@ hipError_t launch_intra_bwd(const ChunkArgs &a, float *bT, float *bG, float *bB,
 }
 
 }  // namespace
+
+size_t chunk_states_segment_bytes(int BH, int NC) { return segment_bytes(BH, NC); }
 
 hipError_t launch_chunk_states(const ChunkArgs &a, float *states) {
     return a.delta ? launch_states_walk<true>(a, states) : launch_states_walk<false>(a, states);

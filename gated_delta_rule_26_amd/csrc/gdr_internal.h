@@ -101,7 +101,10 @@ hipError_t launch_chunk_tile(const ChunkArgs &a, int stage);
 // Dk = Dv = 128, scalar decay): the bf16 walk without outputs over the chunk
 // records at a.ws (mx::kRecBytes each, in the intra kernel's format, written
 // by the caller), the states to `states` at the records' indices ([Dk][Dv]
-// fp32 each).
+// fp32 each).  Long sequences of a fixed-length batch walk in time segments,
+// whose chunk maps and entering states take chunk_states_segment_bytes(B H,
+// NC) right after the records.
+size_t chunk_states_segment_bytes(int BH, int NC);
 hipError_t launch_chunk_states(const ChunkArgs &a, float *states);
 // Its per-chunk inputs (the same case): the intra kernel's records into a.ws and, per chunk, T (fp32, 64 x
 // 64), G and the write strengths (64 each) and the reverse record (the transposes of T'' and A as bf16

@@ -153,6 +153,19 @@ def test_backward_full_workload_sampled(name, nheads):
         assert all(v < _tol("kda" if w.per_channel else "gdn", w.dtype) for v in errs.values()), errs
 
 
+def test_backward_long_sequence_in_time_segments():
+    """One 8,192-token sequence on two heads (128 chunks for two walks): the
+    entering states are walked in four time segments, as the forward pass
+    does for long sequences (chunk maps, entering states, then the segments);
+    with an initial state and a final-state gradient, every gradient against
+    the oracle."""
+    x = _case(6600, 1, 8192, 2, (128, 128), "kla", "bf16")
+    print("backward long sequence: GPU", flush=True)
+    errs = _run(x, "kla", "bf16")
+    print("backward long sequence: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert all(v < _tol("kla", "bf16") for v in errs.values()), errs
+
+
 def _packed_case(seed, lens, H, D, mode):
     m = MODES.get(mode, dict(per_channel=mode == "gla", kaczmarz=False))
     T = int(sum(lens))
