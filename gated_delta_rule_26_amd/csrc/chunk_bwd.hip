@@ -85,8 +85,13 @@ constexpr bool bwd_stores_ops(bool per_channel, bool qkv_bf16) { return per_chan
 // the workspace.
 constexpr bool bwd_walk16(bool ops, int Dk, int Dv) { return !ops && Dk == 128 && Dv == 128; }
 
-// The bf16 path's records lead the workspace: the forward walk's, the segment space of its states walk
-// (time segments of long sequences), the reverse walk's.
+// The bf16 path's records lead the workspace: the forward walk's, the segment spaces of the two walks
+// (time segments of long sequences: the forward chunk maps and entering states, then the reverse walk's N'
+// and entering gradients), the reverse walk's records.
+size_t rev_segment_bytes(int BH, int NC) {
+    const int P = chunk_walk_segments(BH, NC);
+    return P > 1 ? (size_t)BH * P * 2 * mx::DK * mx::DV * sizeof(float) : 0;
+}
 template <int DK, int DV, bool PC>
 BwdWs carve_bwd(void *ws, size_t slots, bool ops, int BH, int NC) {
     constexpr int GK = PC ? DK : 1;
@@ -94,7 +99,8 @@ BwdWs carve_bwd(void *ws, size_t slots, bool ops, int BH, int NC) {
     w.rec = w.rrev = nullptr;
     if (bwd_walk16(ops, DK, DV)) {
         w.rec = ws;
-        w.rrev = static_cast<char *>(ws) + slots * mx::kRecBytes + chunk_states_segment_bytes(BH, NC);
+        w.rrev = static_cast<char *>(ws) + slots * mx::kRecBytes + chunk_states_segment_bytes(BH, NC) +
+                 rev_segment_bytes(BH, NC);
         ws = static_cast<char *>(w.rrev) + slots * kRevBytes;
     }
     float *p = static_cast<float *>(ws);
@@ -131,7 +137,8 @@ size_t bwd_bytes(size_t slots, bool ops, int BH, int NC) {
     const size_t grads = walk16 ? 0 : (size_t)4 * C * C + (size_t)C * GK + GK;  // A, M, dA, dT'', dG, dG63
     return slots * sizeof(float) *
                ((size_t)C * C + (size_t)C * GK + C + 2 * (size_t)DK * DV + grads + (ops ? 3 * (size_t)C * DK : 0)) +
-           (walk16 ? slots * (mx::kRecBytes + kRevBytes) + chunk_states_segment_bytes(BH, NC) : 0);
+           (walk16 ? slots * (mx::kRecBytes + kRevBytes) + chunk_states_segment_bytes(BH, NC) + rev_segment_bytes(BH, NC)
+                   : 0);
 }
 
 // chunk slot ci -> token row of its token 0 and token count.  Fixed-length
@@ -1286,19 +1293,26 @@ struct alignas(16) RevSmem {
     float Gam[2][C], Gend[2][C];     // exp(G_i), exp(G_63 - G_i)
 };
 
-template <bool DELTA>
+// Time segments (fixed-length batches, P > 1): workgroup g = bh P + p walks chunks [p seg, (p+1) seg) of
+// its sequence.  With NPASS it starts from zero and writes only the gradient it reaches at the segment's
+// first chunk, to d_end[g] (the segment's N' of dS_start = M' dS_end + N'); otherwise it starts from
+// ds_final (last segment) or d_start[g], stores dS' of every chunk, and the first segment writes ds0.
+template <bool DELTA, bool NPASS>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dstates_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const float *__restrict__ dO, int T, int H, int NC,
     float scale, const char *__restrict__ rec, const char *__restrict__ rrev, const float *__restrict__ ds_final,
-    float *__restrict__ wdS, float *__restrict__ ds0, SeqTable tb) {
+    float *__restrict__ wdS, float *__restrict__ ds0, int P, int seg, const float *__restrict__ d_start,
+    float *__restrict__ d_end, SeqTable tb) {
     using mx::bf16x8;
     constexpr int DK = mx::DK, DV = mx::DV, LDK = DK + 16, NT = DV / kBV;
     __shared__ RevSmem sm;
-    int bh, tile;
-    state_slot(blockIdx.x, gridDim.x / NT, NT, bh, tile);
-    bh = walk_seq(bh, H, tb);
+    int g, tile;
+    state_slot(blockIdx.x, gridDim.x / NT, NT, g, tile);
+    g = walk_seq(g, H, tb);  // packed batches (P = 1): longest sequences first
+    const int bh = g / P, p = g % P;
     const BwdWalk wk = bwd_walk(bh, T, H, NC, tb);
-    const int nc = wk.nc, L = nc - 1;
+    const int c_lo = min(p * seg, wk.nc), c_hi = min(c_lo + seg, wk.nc);
+    const int nc = c_hi - c_lo, L = c_hi - 1;
     const int j0 = tile * kBV;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -1308,7 +1322,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dstates_bf16_kernel(
         // ================= chain wavefront: value columns jt .. jt+15
         const int jt = j0 + 16 * w;
         f32x4 S[8];  // dS'[16 i + 4 lg + r][jt + lr]
-        const float *sfin = ds_final ? ds_final + (size_t)bh * DK * DV : nullptr;
+        const float *sfin = NPASS ? nullptr
+                            : p < P - 1 ? d_start + (size_t)g * DK * DV
+                                        : (ds_final ? ds_final + (size_t)bh * DK * DV : nullptr);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -1318,7 +1334,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dstates_bf16_kernel(
             bf16x8 tAh[6], tAl[6], tBh[6], tBl[6];
             auto load_t = [&](int c, bf16x8 *th, bf16x8 *tl) __attribute__((always_inline)) {
                 if constexpr (DELTA) {
-                    const char *r = rrev + wk.slot(max(c, 0)) * kRevBytes;
+                    const char *r = rrev + wk.slot(max(c, c_lo)) * kRevBytes;
 #pragma unroll
                     for (int f = 0; f < 6; ++f) {
                         th[f] = *reinterpret_cast<const bf16x8 *>(r + kRevTH + f * mx::kFragBytes + lane * 16);
@@ -1331,7 +1347,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dstates_bf16_kernel(
             auto step = [&](int c, const bf16x8 *th, const bf16x8 *tl, bf16x8 *thn, bf16x8 *tln)
                             __attribute__((always_inline)) {
                 const int buf = c & 1;
-                {  // the gradient of chunk c's end state
+                if constexpr (!NPASS) {  // the gradient of chunk c's end state
                     float *d = wdS + wk.slot(c) * DK * DV;
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
@@ -1428,17 +1444,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dstates_bf16_kernel(
                 barrier_lds();
                 --c;
             }
-            for (; c >= 2; c -= 2) {
+            for (; c - 1 >= c_lo; c -= 2) {
                 step(c, tAh, tAl, tBh, tBl);
                 barrier_lds();
                 step(c - 1, tBh, tBl, tAh, tAl);
                 barrier_lds();
             }
-            step(0, tAh, tAl, tBh, tBl);
-            barrier_lds();
+            if (c >= c_lo) {  // the first chunk, even
+                step(c, tAh, tAl, tBh, tBl);
+                barrier_lds();
+            }
         }
-        if (ds0) {  // the gradient of the initial state
-            float *d = ds0 + (size_t)bh * DK * DV;
+        float *d = NPASS ? d_end + (size_t)g * DK * DV : (ds0 && p == 0 ? ds0 + (size_t)bh * DK * DV : nullptr);
+        if (d) {  // the gradient at the segment's start: N' of the segment, or of the initial state
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -1456,7 +1474,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dstates_bf16_kernel(
             return rows_rsrc(base + uniform(wk.row0(c)) * DK, uniform(wk.count(c)), qk_stride, DK * 2);
         };
         auto load_k = [&](int c) __attribute__((always_inline)) {
-            c = max(c, 0);
+            c = max(c, c_lo);
             const auto rk = qk_rsrc(k, c);
 #pragma unroll
             for (int u = 0; u < 8; ++u) kreg[u] = mx::buf_ld16(rk, (8 * (ht >> 4) + u) * qk_stride + 16 * (ht & 15));
@@ -1465,12 +1483,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dstates_bf16_kernel(
             gnd_reg = reinterpret_cast<const float *>(r + mx::kRecGend)[ht & 63];
         };
         auto load_q = [&](int c) __attribute__((always_inline)) {
-            const auto rq = qk_rsrc(q, max(c, 0));
+            const auto rq = qk_rsrc(q, max(c, c_lo));
 #pragma unroll
             for (int u = 0; u < 8; ++u) qreg[u] = mx::buf_ld16(rq, (8 * (ht >> 4) + u) * qk_stride + 16 * (ht & 15));
         };
         auto load_d = [&](int c) __attribute__((always_inline)) {
-            c = max(c, 0);
+            c = max(c, c_lo);
             const auto ro = rows_rsrc(dO + uniform(wk.row0(c)) * DV, uniform(wk.count(c)), H * DV * 4, DV * 4);
 #pragma unroll
             for (int t = 0; t < 4; ++t)
@@ -1559,7 +1577,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dstates_bf16_kernel(
         load_d(L - 1);
         barrier_lds();
         // during the chain's step on chunk c: k of c - 1 and q of c - 2 staged, chunk c - 1's products
-        for (int c = L; c >= 0; --c) {
+        for (int c = L; c >= c_lo; --c) {
             store_k((c - 1) & 1);
             store_q((c - 2) & 1);
             compute((c - 1) & 1);
@@ -1909,6 +1927,54 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_a_kernel(
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
             if (lane == 0) wdG63[ci] = s;
+        }
+    }
+}
+
+// Entering gradients of the reverse walk's time segments: D_P = ds_final (or zero), D_p = M_p' D_{p+1} +
+// N'_p for p = P-1 .. 1, with M_p the forward chunk map of segment p (S_end = M_p S_start + N_p, from the
+// states walk's transfer walk: the reverse map of a segment is its transpose) and N'_p the reverse walk
+// from zero over it; segment p walks from D_{p+1}, stored at d_start[bh P + p].  One workgroup per
+// (sequence, head, 16 value columns); thread t forms row t / 2, columns 8 (t % 2) .. +7 of its slice.
+__global__ __launch_bounds__(256) void rev_segment_combine_kernel(const float *__restrict__ tr,
+                                                                  const float *__restrict__ nrev,
+                                                                  const float *__restrict__ ds_final,
+                                                                  float *__restrict__ d_start, int P) {
+    constexpr int DK = mx::DK, DV = mx::DV, CC = 16, LM = DK + 1, NCS = DV / CC;
+    __shared__ float Ds[DK][CC];
+    __shared__ float Ms[DK * LM];  // M_p transposed: Ms[i][k] = M_p[k][i]
+    const int bh = blockIdx.x / NCS, cs = blockIdx.x % NCS;
+    const int t = threadIdx.x, i = t >> 1, jl = 8 * (t & 1), jb = cs * CC + jl;
+    const size_t mat = (size_t)DK * DV;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) Ds[i][jl + jj] = ds_final ? ds_final[bh * mat + i * DV + jb + jj] : 0.f;
+    for (int pp = P - 1; pp >= 1; --pp) {
+        const float *N = nrev + (size_t)(bh * P + pp) * mat;
+        const float *M = tr + ((size_t)(bh * P + pp) * 2 + 1) * mat;
+        constexpr int PER = DK * DK / 256;
+        float mr[PER], acc[8];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) mr[u] = M[t + u * 256];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) acc[jj] = N[i * DV + jb + jj];
+        __syncthreads();  // the previous step's reads of Ms and Ds are done
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int idx = t + u * 256;
+            Ms[(idx % DK) * LM + idx / DK] = mr[u];
+        }
+        __syncthreads();
+        for (int kk = 0; kk < DK; ++kk) {
+            const float m = Ms[i * LM + kk];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) acc[jj] = fmaf(m, Ds[kk][jl + jj], acc[jj]);
+        }
+        __syncthreads();
+        float *out = d_start + (size_t)(bh * P + pp - 1) * mat;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            Ds[i][jl + jj] = acc[jj];
+            out[i * DV + jb + jj] = acc[jj];
         }
     }
 }
@@ -3085,12 +3151,28 @@ hipError_t launch_bwd16(const BwdArgs &a, const BwdWs &w, unsigned nslot, unsign
     if (e != hipSuccess || (e = launch_chunk_states(f, w.S)) != hipSuccess) return e;
     const __bf16 *qb = static_cast<const __bf16 *>(a.q), *kb = static_cast<const __bf16 *>(a.k);
     const char *rec = static_cast<const char *>(w.rec), *rrev = static_cast<const char *>(w.rrev);
-    if (a.delta)
-        hipLaunchKernelGGL((bwd_dstates_bf16_kernel<true>), dim3(nwalk), dim3(kThreads), 0, a.stream, qb, kb, a.dO,
-                           a.T, a.H, a.NC, a.scale, rec, rrev, a.ds_final, w.dS, a.ds0, a.tab);
-    else
-        hipLaunchKernelGGL((bwd_dstates_bf16_kernel<false>), dim3(nwalk), dim3(kThreads), 0, a.stream, qb, kb, a.dO,
-                           a.T, a.H, a.NC, a.scale, rec, rrev, a.ds_final, w.dS, a.ds0, a.tab);
+    // the reverse walk, in the states walk's time segments (fixed-length batches)
+    const int BH = a.B * a.H;
+    const int P = a.tab.start ? 1 : chunk_walk_segments(BH, a.NC);
+    const int seg = (a.NC + P - 1) / P;
+    const float *d_start = nullptr;
+    if (P > 1) {
+        constexpr size_t mat = (size_t)mx::DK * mx::DV;
+        const float *tr = reinterpret_cast<const float *>(rec + (size_t)BH * a.NC * mx::kRecBytes);
+        float *nrev = const_cast<float *>(tr) + (size_t)BH * P * 3 * mat;  // after the forward's maps and states
+        float *dst = nrev + (size_t)BH * P * mat;
+        auto npass = a.delta ? bwd_dstates_bf16_kernel<true, true> : bwd_dstates_bf16_kernel<false, true>;
+        hipLaunchKernelGGL(npass, dim3(nwalk * P), dim3(kThreads), 0, a.stream, qb, kb, a.dO, a.T, a.H, a.NC, a.scale,
+                           rec, rrev, a.ds_final, w.dS, a.ds0, P, seg, nullptr, nrev, a.tab);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(rev_segment_combine_kernel, dim3((unsigned)(BH * (mx::DV / 16))), dim3(256), 0, a.stream,
+                           tr, nrev, a.ds_final, dst, P);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        d_start = dst;
+    }
+    auto walk = a.delta ? bwd_dstates_bf16_kernel<true, false> : bwd_dstates_bf16_kernel<false, false>;
+    hipLaunchKernelGGL(walk, dim3(nwalk * P), dim3(kThreads), 0, a.stream, qb, kb, a.dO, a.T, a.H, a.NC, a.scale, rec,
+                       rrev, a.ds_final, w.dS, a.ds0, P, seg, d_start, nullptr, a.tab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_grads16_kernel, dim3(nslot), dim3(kThreads16), 0, a.stream, static_cast<const __bf16 *>(a.v),
                        a.dO, kb, qb, a.T, a.H, a.NC, a.eps, a.scale, w.T, w.G, w.beta, rec, rrev, w.S, w.dS, a.dq, a.dk,

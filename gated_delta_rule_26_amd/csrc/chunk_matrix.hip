@@ -812,6 +812,7 @@ hipError_t launch_intra_bwd(const ChunkArgs &a, float *bT, float *bG, float *bB,
 }  // namespace
 
 size_t chunk_states_segment_bytes(int BH, int NC) { return segment_bytes(BH, NC); }
+int chunk_walk_segments(int BH, int NC) { return walk_segments(BH, NC); }
 
 hipError_t launch_chunk_states(const ChunkArgs &a, float *states) {
     return a.delta ? launch_states_walk<true>(a, states) : launch_states_walk<false>(a, states);

@@ -105,6 +105,7 @@ hipError_t launch_chunk_tile(const ChunkArgs &a, int stage);
 // whose chunk maps and entering states take chunk_states_segment_bytes(B H,
 // NC) right after the records.
 size_t chunk_states_segment_bytes(int BH, int NC);
+int chunk_walk_segments(int BH, int NC);  // the time segments of those walks (1: none)
 hipError_t launch_chunk_states(const ChunkArgs &a, float *states);
 // Its per-chunk inputs (the same case): the intra kernel's records into a.ws and, per chunk, T (fp32, 64 x
 // 64), G and the write strengths (64 each) and the reverse record (the transposes of T'' and A as bf16
