@@ -299,6 +299,11 @@ def test_backward_workspace_and_validation():
     slots = 2 * 3 * 2
     assert ws(_desc()) == (0, slots * (4 * (4096 + 64 + 64 + 2 * 128 * 128) + 25088 + 24576))
     assert ws(_desc(Dv=64)) == (0, slots * 4 * (5 * 4096 + 2 * 64 + 1 + 64 + 2 * 128 * 64))
+    # one 8,192-token sequence on two heads walks in four time segments: the forward chunk maps (two per
+    # segment) and entering states, then the reverse walk's N' and entering gradients, 128 x 128 fp32 each
+    long_slots = 1 * 2 * 128
+    assert ws(_desc(B=1, T=8192, H=2)) == (0, long_slots * (4 * (4096 + 64 + 64 + 2 * 128 * 128) + 25088 + 24576)
+                                           + 2 * 4 * 5 * 128 * 128 * 4)
     assert ws(_desc(qkv_dtype=__import__("torch").float32)) == (
         0, slots * 4 * (5 * 4096 + 2 * 64 + 1 + 64 + 2 * 128 * 128 + 3 * 64 * 128))
     assert ws(_desc(per_channel=True)) == (0, slots * 4 * (5 * 4096 + 2 * 64 * 128 + 128 + 64 + 2 * 128 * 128
