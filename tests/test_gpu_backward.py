@@ -63,13 +63,16 @@ def test_backward_parity(T, mode):
     assert all(v < _tol(mode, "bf16") for v in errs.values()), errs
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("D", [(64, 64), (64, 128), (128, 64)])
 @pytest.mark.parametrize("mode", ["gdn", "kda"])
-def test_backward_widths_fp32_inputs_and_scale(D, mode):
-    x = _case(6100, 1, 90, 3, D, mode, "f32")
-    errs = _run(x, mode, "f32", scale=D[0] ** -0.5)
-    print(f"backward {mode} D={D} f32: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
-    assert all(v < _tol(mode, "f32", D) for v in errs.values()), errs
+def test_backward_widths_input_dtypes_and_scale(D, mode, dtype):
+    """Widths of 64 (fp32 tiles); with bf16 inputs and scalar decay the
+    kernels that form the decayed operands from k and q themselves."""
+    x = _case(6100, 1, 90, 3, D, mode, dtype)
+    errs = _run(x, mode, dtype, scale=D[0] ** -0.5)
+    print(f"backward {mode} D={D} {dtype}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert all(v < _tol(mode, dtype, D) for v in errs.values()), errs
 
 
 @pytest.mark.parametrize("mode", ["gdn", "kda"])
