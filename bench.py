@@ -47,22 +47,22 @@ _SCALAR = ("gated_delta_rule_26_amd/csrc/chunk_matrix.hip", "gated_delta_rule_26
 _PER_CHANNEL = ("gated_delta_rule_26_amd/csrc/chunk_matrix_pc.hip", "gated_delta_rule_26_amd/csrc/matrix_common.h",
                 _BUILD)
 _DECODE = ("gated_delta_rule_26_amd/csrc/recurrent_step.hip", _BUILD)
-_SHA_SCALAR = "9ebaf047622d3d29e2589a54e85979969d6365cdfdfc7789f5d068f451bd0543"
+_SHA_SCALAR = "56ddce87d2e9f9048edeb14b17576298c1243a1b1d50385eeb534ea256465355"
 _SHA_PC = "33b1131f292acb6a99b56ad42a44c5b921576f955b5af34734db1d36c37f9f00"
 _SHA_DECODE = "32418c0ee1020b20d96212e92a32fa306ea808bb4ec78f7b7f401d35e5af79d4"
 MEASURED_TRAFFIC = {
-    ("matrix", "state", "gdn_prefill", "bf16"): (_SCALAR, _SHA_SCALAR, (148653.2 * 2.0 + 69648.7) * 1024),
+    ("matrix", "state", "gdn_prefill", "bf16"): (_SCALAR, _SHA_SCALAR, (148662.5 * 2.0 + 69642.4) * 1024),
     ("matrix", "intra", "gdn_prefill", "bf16"): (_SCALAR, _SHA_SCALAR, (66989.6 * 2.0 + 100352.0) * 1024),
-    ("matrix", "state", "gdn_prefill", "f32"): (_SCALAR, _SHA_SCALAR, (148655.2 * 2.0 + 135241.4) * 1024),
-    ("matrix", "intra", "gdn_prefill", "f32"): (_SCALAR, _SHA_SCALAR, (66989.6 * 2.0 + 100352.0) * 1024),
+    ("matrix", "state", "gdn_prefill", "f32"): (_SCALAR, _SHA_SCALAR, (148655.4 * 2.0 + 135233.3) * 1024),
+    ("matrix", "intra", "gdn_prefill", "f32"): (_SCALAR, _SHA_SCALAR, (66988.1 * 2.0 + 100352.0) * 1024),
     ("matrix", "state", "kda_prefill", "bf16"): (_PER_CHANNEL, _SHA_PC, (279781.7 * 2.0 + 93798.4) * 1024),
     ("matrix", "intra", "kda_prefill", "bf16"): (_PER_CHANNEL, _SHA_PC, (134521.8 * 2.0 + 493568.2) * 1024),
     # the state phase of the long sequence is three launches: the segment transfer walk, the
     # combine of the entering states and the per-segment walk
     ("matrix", "state", "kla_prefill", "bf16"): (_SCALAR, _SHA_SCALAR,
-                                                 (729584.4 * 2.0 + 8192.0 + 15394.5 * 2.0 + 4096.0
-                                                  + 1190059.3 * 2.0 + 525314.5) * 1024),
-    ("matrix", "intra", "kla_prefill", "bf16"): (_SCALAR, _SHA_SCALAR, (656372.0 * 2.0 + 802816.0) * 1024),
+                                                 (729447.8 * 2.0 + 8192.0 + 15394.5 * 2.0 + 4096.0
+                                                  + 1190059.2 * 2.0 + 525320.5) * 1024),
+    ("matrix", "intra", "kla_prefill", "bf16"): (_SCALAR, _SHA_SCALAR, (656379.1 * 2.0 + 802816.0) * 1024),
     ("decode", "step", "decode", "f32"): (_DECODE, _SHA_DECODE, (132913.0 * 2.0 + 264729.0) * 1024),
     ("decode", "step", "decode_512", "f32"): (_DECODE, _SHA_DECODE, (265782.2 * 2.0 + 529423.2) * 1024),
 }
@@ -73,10 +73,10 @@ MEASURED_TRAFFIC = {
 # (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) per second.  The issued flops count every bf16 hi/lo product, so they
 # exceed the algorithmic flops.  (files, sha, busy fraction, issued TFLOP/s), as for the traffic.
 MEASURED_MFMA = {
-    ("matrix", "state", "gdn_prefill", "bf16"): (_SCALAR, _SHA_SCALAR, 0.207, 500.1),
+    ("matrix", "state", "gdn_prefill", "bf16"): (_SCALAR, _SHA_SCALAR, 0.206, 497.0),
     ("matrix", "state", "kda_prefill", "bf16"): (_PER_CHANNEL, _SHA_PC, 0.080, 200.4),
     # the long sequence: transfer + combine + walk, weighted by duration
-    ("matrix", "state", "kla_prefill", "bf16"): (_SCALAR, _SHA_SCALAR, 0.255, 571.7),
+    ("matrix", "state", "kla_prefill", "bf16"): (_SCALAR, _SHA_SCALAR, 0.255, 573.4),
 }
 
 
