@@ -169,6 +169,14 @@ def mean(xs):
     return sum(xs) / len(xs) if xs else float("nan")
 
 
+def quantile(xs, f):
+    """Nearest-rank quantile: the smallest value with at least a fraction f of the values at or below it."""
+    ys = sorted(xs)
+    if not ys:
+        return float("nan")
+    return ys[min(len(ys) - 1, max(0, int(-(-f * len(ys) // 1)) - 1))]
+
+
 def _to_device(x, w, dev):
     import torch
     d = {}
@@ -299,6 +307,7 @@ def prefill_block(w, pre, algo, o_dtype):
         "algo": algo, "o_dtype": o_dtype,
         "tokens_per_s": w.B * w.T / (step_ms * 1e-3), "ms_per_step": step_ms,
         "ms_per_step_median": median(cold["step"]),
+        "ms_per_step_p10": quantile(cold["step"], 0.1), "ms_per_step_p90": quantile(cold["step"], 0.9),
         "intra_ms": intra_ms, "state_ms": state_ms,
         "timing": "cold caches: 512 MiB written before each step (outside the events); events recorded by the "
                   "first and last kernels of each stage",
@@ -716,7 +725,8 @@ def main():
                    "chunk": C, "algo": algo, "o_dtype": args.o_dtype, "timing": head["timing"]},
         "mfma_peak_frac": head["frac_bf16_mfma_peak"],
         "roofline": head["roofline"],
-        "prefill": {key: head[key] for key in ("tokens_per_s", "ms_per_step", "ms_per_step_median", "intra_ms",
+        "prefill": {key: head[key] for key in ("tokens_per_s", "ms_per_step", "ms_per_step_median",
+                                               "ms_per_step_p10", "ms_per_step_p90", "intra_ms",
                                                "state_ms", "warm", "alg_tflops", "frac_bf16_mfma_peak",
                                                "alg_bytes", "alg_gbps", "frac_hbm_peak",
                                                "alg_flops_per_token_head", "workspace_bytes")},

@@ -1,5 +1,5 @@
 """Host-side pieces of bench.py (no GPU): the refusal of several GPUs, the
-serving length mix, the algorithmic byte and flop counts, and the guard that
+serving length mix, the algorithmic byte and flop counts, the step-time quantiles and the guard that
 drops counter figures measured on other kernel sources."""
 import os
 import subprocess
@@ -46,3 +46,11 @@ def test_counter_figures_follow_their_sources():
 def test_cpu_model_is_named():
     name = bench.cpu_model()
     assert isinstance(name, str) and name and name != "x86_64"
+
+
+def test_step_time_quantiles_are_nearest_rank():
+    xs = [float(x) for x in range(20, 0, -1)]      # unsorted on purpose
+    assert (bench.quantile(xs, 0.1), bench.median(xs), bench.quantile(xs, 0.9)) == (2.0, 11.0, 18.0)
+    assert bench.quantile([3.5], 0.1) == bench.quantile([3.5], 0.9) == 3.5
+    assert bench.quantile(list(range(1, 11)), 0.9) == 9     # ceil(0.9 * 10) = the 9th value
+    assert bench.quantile([], 0.5) != bench.quantile([], 0.5)  # nan for no samples
