@@ -761,7 +761,16 @@ def main():
         torch.cuda.empty_cache()
 
     if not args.no_peaks:
-        out["peaks_measured"] = measured_peaks()
+        pk = measured_peaks()
+        # the headline figures against what this GPU measurably reaches, beside their fractions of the spec
+        pk["vs_measured"] = {
+            "state_kernel_gbps_frac_of_copy": head["roofline"]["achieved"] / pk["copy_gbps"]
+            if head["roofline"]["unit"] == "GB/s" else None,
+            "pass_alg_tflops_frac_of_gemm": head["alg_tflops"] / pk["bf16_gemm_tflops"],
+        }
+        if "decode" in out:
+            pk["vs_measured"]["decode_gbps_frac_of_copy"] = out["decode"]["roofline"]["achieved"] / pk["copy_gbps"]
+        out["peaks_measured"] = pk
 
     if args.backward_steps > 0:
         bwd = bench_backward(w, x, args.backward_steps, 1)
