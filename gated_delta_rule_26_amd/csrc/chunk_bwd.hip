@@ -34,7 +34,9 @@
 //  * forward walk (one workgroup per (sequence, head, 32 value columns)): the
 //    state entering every chunk, stored;
 //  * reverse walk (same grid, chunks in reverse): dS' of every chunk, stored,
-//    and the gradient of the initial state;
+//    and the gradient of the initial state (it reads no entering state, so
+//    the two walks run in one launch, side by side when they fit the compute
+//    units together);
 //  * grads A (one workgroup per chunk): the products over the value axis, in
 //    slices of 16 columns: dV, and the parts of dq, dk, dG that come through
 //    K~, Q~, K^ and gam; dA and dT'' to the workspace;
@@ -588,15 +590,24 @@ __device__ __forceinline__ float gval(const float (*sG)[GK], int i, int cc) {
 // Per chunk three barriers: the pair exchange; before the update, after this
 // chunk's K^ has landed; at the end, after the next chunk's operands have.
 // Only v goes through registers, one chunk ahead.
+// The walk's LDS (a struct, so that the launch below can overlay the reverse walk's on it).
+template <int DK>
+struct alignas(16) BwdStatesSmem {
+    float sKt[2][C * DK];
+    float sT[2][C * C];
+    float sKh[C * DK];
+    float sB[2][C];            // beta of the chunk's tokens
+    float sG[2][DK];           // G_63 per channel (scalar decay: the one value, repeated)
+    f32x4 sP[2][2][4][64];     // per pair and half: the partial K~ S tiles
+};
+// Workgroup `blk` of `nblk` (the walk's own numbering) in LDS `sm`.
 template <int DK, int DV, bool PC, bool IN_BF16>
-__global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__restrict__ v, int T, int H, int NC,
-                                                              const float *__restrict__ wT,
-                                                              const float *__restrict__ wG,
-                                                              const float *__restrict__ wB,
-                                                              const float *__restrict__ wKt,
-                                                              const float *__restrict__ wKh,
-                                                              const float *__restrict__ s0, float *__restrict__ wS,
-                                                              bool delta, SeqTable tb) {
+__device__ __forceinline__ void bwd_states_body(const void *__restrict__ v, int T, int H, int NC,
+                                                const float *__restrict__ wT, const float *__restrict__ wG,
+                                                const float *__restrict__ wB, const float *__restrict__ wKt,
+                                                const float *__restrict__ wKh, const float *__restrict__ s0,
+                                                float *__restrict__ wS, bool delta, SeqTable tb,
+                                                BwdStatesSmem<DK> &sm, int blk, int nblk) {
     constexpr int GK = PC ? DK : 1;
     constexpr int NT = DV / kBV;
     constexpr int HK = DK / 2, NTH = HK / 16;  // channels per wavefront of a pair, their 16-blocks
@@ -605,7 +616,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
     // XCD-aware placement: the value slices of one (sequence, head) share an XCD, so its L2 serves the
     // chunk operands they all read
     int bh, tile;
-    state_slot(blockIdx.x, gridDim.x / NT, NT, bh, tile);
+    state_slot(blk, nblk / NT, NT, bh, tile);
     bh = walk_seq(bh, H, tb);  // packed batches: longest sequences first
     const BwdWalk wk = bwd_walk(bh, T, H, NC, tb);
     const int j0 = tile * kBV;
@@ -614,12 +625,12 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(const void *__rest
     const int p = w >> 1, h = w & 1;
     const int jc = j0 + 16 * p + lr;  // this lane's value column
     const int kh0 = h * HK;           // first key channel of this wavefront's half
-    __shared__ __align__(16) float sKt[2][C * DK];
-    __shared__ __align__(16) float sT[2][C * C];
-    __shared__ __align__(16) float sKh[C * DK];
-    __shared__ __align__(16) float sB[2][C];    // beta of the chunk's tokens
-    __shared__ __align__(16) float sG[2][DK];   // G_63 per channel (scalar decay: the one value, repeated)
-    __shared__ f32x4 sP[2][2][4][64];           // per pair and half: the partial K~ S tiles
+    auto &sKt = sm.sKt;
+    auto &sT = sm.sT;
+    auto &sKh = sm.sKh;
+    auto &sB = sm.sB;
+    auto &sG = sm.sG;
+    auto &sP = sm.sP;
 
     // the next chunk's K~, T, beta and G_63 into buffer `b` (one small copy per wavefront: beta on
     // wavefronts 0 and 3, G_63 in 64-channel pieces on 1 and 2, beta again when there is one piece)
@@ -910,28 +921,36 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kq16_kernel(const __bf16 
 // as in the forward walk: K^ and A after the exchange barrier, T, Q~, K~, beta
 // and G_63 after the chunk's last barrier; dO goes through registers one chunk
 // ahead.
+template <int DK>
+struct alignas(16) BwdDstatesSmem {
+    static constexpr int LKR = DK + 8;  // K^: rows read as float4
+    static constexpr int LKC = DK + 4;  // Q~, K~: columns read one value per lane (4 lane groups in 4 bank quarters)
+    static constexpr int LTC = C + 4;   // A, T: columns
+    float sKh[C * LKR];
+    float sQt[C * LKC];
+    float sKt[C * LKC];
+    float sA[C * LTC];
+    float sT[C * LTC];
+    float sB[C];               // beta of the chunk's tokens
+    float sG[DK];              // G_63 per channel (scalar decay: the one value, repeated)
+    f32x4 sP[2][2][4][64];     // per pair and half: the partial dE tiles
+};
 template <int DK, int DV, bool PC>
-__global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__restrict__ dO, int T, int H, int NC,
-                                                               const float *__restrict__ wT,
-                                                               const float *__restrict__ wA,
-                                                               const float *__restrict__ wG,
-                                                               const float *__restrict__ wB,
-                                                               const float *__restrict__ wKt,
-                                                               const float *__restrict__ wKh,
-                                                               const float *__restrict__ wQt,
-                                                               const float *__restrict__ ds_final,
-                                                               float *__restrict__ wdS, float *__restrict__ ds0,
-                                                               bool delta, SeqTable tb) {
+__device__ __forceinline__ void bwd_dstates_body(const float *__restrict__ dO, int T, int H, int NC,
+                                                 const float *__restrict__ wT, const float *__restrict__ wA,
+                                                 const float *__restrict__ wG, const float *__restrict__ wB,
+                                                 const float *__restrict__ wKt, const float *__restrict__ wKh,
+                                                 const float *__restrict__ wQt, const float *__restrict__ ds_final,
+                                                 float *__restrict__ wdS, float *__restrict__ ds0, bool delta,
+                                                 SeqTable tb, BwdDstatesSmem<DK> &sm, int blk, int nblk) {
     constexpr int GK = PC ? DK : 1;
     constexpr int NT = DV / kBV;
     constexpr int HK = DK / 2, NTH = HK / 16;
-    constexpr int LKR = DK + 8;  // K^: rows read as float4
-    constexpr int LKC = DK + 4;  // Q~, K~: columns read one value per lane (4 lane groups in 4 bank quarters)
-    constexpr int LTC = C + 4;   // A, T: columns
+    constexpr int LKR = BwdDstatesSmem<DK>::LKR, LKC = BwdDstatesSmem<DK>::LKC, LTC = BwdDstatesSmem<DK>::LTC;
     // XCD-aware placement: the value slices of one (sequence, head) share an XCD, so its L2 serves the
     // chunk operands they all read
     int bh, tile;
-    state_slot(blockIdx.x, gridDim.x / NT, NT, bh, tile);
+    state_slot(blk, nblk / NT, NT, bh, tile);
     bh = walk_seq(bh, H, tb);  // packed batches: longest sequences first
     const BwdWalk wk = bwd_walk(bh, T, H, NC, tb);
     const int j0 = tile * kBV;
@@ -940,14 +959,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
     const int p = w >> 1, h = w & 1;
     const int jc = j0 + 16 * p + lr;
     const int kh0 = h * HK;
-    __shared__ float sKh[C * LKR];
-    __shared__ float sQt[C * LKC];
-    __shared__ float sKt[C * LKC];
-    __shared__ float sA[C * LTC];
-    __shared__ float sT[C * LTC];
-    __shared__ float sB[C];            // beta of the chunk's tokens
-    __shared__ float sG[DK];           // G_63 per channel (scalar decay: the one value, repeated)
-    __shared__ f32x4 sP[2][2][4][64];  // per pair and half: the partial dE tiles
+    auto &sKh = sm.sKh;
+    auto &sQt = sm.sQt;
+    auto &sKt = sm.sKt;
+    auto &sA = sm.sA;
+    auto &sT = sm.sT;
+    auto &sB = sm.sB;
+    auto &sG = sm.sG;
+    auto &sP = sm.sP;
 
     auto copy_ka = [&](size_t ci) __attribute__((always_inline)) {
         dma_rows<DK, LKR>(wKh + ci * C * DK, sKh, w, lane);
@@ -1067,6 +1086,36 @@ __global__ __launch_bounds__(kThreads) void bwd_dstates_kernel(const float *__re
 #pragma unroll
             for (int e = 0; e < 4; ++e) ds0[sbase + (size_t)(kh0 + 16 * t + 4 * lg + e) * DV + jc] = dsv[t][e];
     }
+}
+
+// ---- both walks in one launch.  The reverse walk reads no entering state,
+// so the two are independent: workgroups 0 .. nwalk-1 walk forward and
+// nwalk .. 2 nwalk-1 in reverse, each with the other's LDS overlaid on its
+// own.  With at most half as many walks as compute units (a few heads per
+// batch) the two run side by side instead of one after the other; otherwise
+// the workgroups are dispatched in order and the forward ones start first.
+// A walk's value slices keep workgroup ids equal mod 8 (one XCD), as their
+// offset by nwalk is the same for all of them.
+template <int DK>
+union BwdWalksSmem {
+    BwdStatesSmem<DK> fwd;
+    BwdDstatesSmem<DK> rev;
+};
+template <int DK, int DV, bool PC, bool IN_BF16>
+__global__ __launch_bounds__(kThreads) void bwd_walks_kernel(
+    const void *__restrict__ v, const float *__restrict__ dO, int T, int H, int NC, const float *__restrict__ wT,
+    const float *__restrict__ wA, const float *__restrict__ wG, const float *__restrict__ wB,
+    const float *__restrict__ wKt, const float *__restrict__ wKh, const float *__restrict__ wQt,
+    const float *__restrict__ s0, float *__restrict__ wS, const float *__restrict__ ds_final,
+    float *__restrict__ wdS, float *__restrict__ ds0, bool delta, SeqTable tb, int nwalk) {
+    __shared__ BwdWalksSmem<DK> sm;
+    const int blk = blockIdx.x;
+    if (blk < nwalk)
+        bwd_states_body<DK, DV, PC, IN_BF16>(v, T, H, NC, wT, wG, wB, wKt, wKh, s0, wS, delta, tb, sm.fwd, blk,
+                                             nwalk);
+    else
+        bwd_dstates_body<DK, DV, PC>(dO, T, H, NC, wT, wA, wG, wB, wKt, wKh, wQt, ds_final, wdS, ds0, delta, tb,
+                                     sm.rev, blk - nwalk, nwalk);
 }
 
 // ---- reverse walk, scalar decay with bf16 q and k
@@ -3194,21 +3243,19 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
                        a.tab);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if constexpr (ops)
-        hipLaunchKernelGGL((bwd_states_kernel<DK, DV, PC, IB>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.v, a.T,
-                           a.H, a.NC, w.T, w.G, w.beta, w.Kt, w.Kh, a.s0, w.S, a.delta, a.tab);
-    else
+    if constexpr (ops) {  // both walks in one launch (independent: side by side when they fit)
+        hipLaunchKernelGGL((bwd_walks_kernel<DK, DV, PC, IB>), dim3(2 * nwalk), dim3(kThreads), 0, a.stream, a.v,
+                           a.dO, a.T, a.H, a.NC, w.T, w.A, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.s0, w.S, a.ds_final, w.dS,
+                           a.ds0, a.delta, a.tab, (int)nwalk);
+    } else {  // scalar decay with bf16 inputs: the walks on k and q themselves
         hipLaunchKernelGGL((bwd_states_kq16_kernel<DK, DV>), dim3(nwalk), dim3(kThreads), 0, a.stream,
                            static_cast<const __bf16 *>(a.v), static_cast<const __bf16 *>(a.k), a.T, a.H, a.NC, w.T,
                            w.G, w.beta, a.s0, w.S, a.delta, a.tab);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if constexpr (!ops)  // scalar decay with bf16 inputs: the walk on k and q themselves
+        if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL((bwd_dstates_kq16_kernel<DK, DV>), dim3(nwalk), dim3(kThreads), 0, a.stream,
                            static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), a.dO, a.T, a.H, a.NC,
                            a.scale, w.T, w.A, w.G, w.beta, a.ds_final, w.dS, a.ds0, a.delta, a.tab);
-    else
-        hipLaunchKernelGGL((bwd_dstates_kernel<DK, DV, PC>), dim3(nwalk), dim3(kThreads), 0, a.stream, a.dO, a.T,
-                           a.H, a.NC, w.T, w.A, w.G, w.beta, w.Kt, w.Kh, w.Qt, a.ds_final, w.dS, a.ds0, a.delta, a.tab);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grads_a_kernel<DK, DV, PC, IB, !ops>), dim3(nslot), dim3(kThreads), 0, a.stream, a.v,
                        a.dO, a.T, a.H, a.NC, a.scale, w.T, w.A, w.G, w.beta, w.S, w.dS, w.Kt, w.Kh, w.Qt,
