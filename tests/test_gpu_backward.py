@@ -129,6 +129,18 @@ def test_backward_without_delta_rule(variant, T):
     assert all(v < _tol(variant, "bf16") for v in errs.values()), errs
 
 
+@pytest.mark.parametrize("mode", ["gdn", "kda"])
+def test_backward_more_walks_than_compute_units(mode):
+    """fp32 inputs on 80 heads: the fp32-tile path launches its forward and
+    reverse walks together, 320 of each (640 workgroups for 256 compute
+    units), so most of them wait for a free unit; every gradient of every
+    head against the oracle."""
+    x = _case(6200, 4, 70, 20, (128, 128), mode, "f32")
+    errs = _run(x, mode, "f32")
+    print(f"backward {mode} 80 heads: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert all(v < _tol(mode, "f32") for v in errs.values()), errs
+
+
 @pytest.mark.parametrize("name,nheads", [("gdn_prefill", 2), ("kda_prefill", 1)])
 def test_backward_full_workload_sampled(name, nheads):
     """The backward pass at the full size of a prefill workload (as the
