@@ -1090,8 +1090,8 @@ __device__ __forceinline__ void bwd_dstates_body(const float *__restrict__ dO, i
 
 // ---- both walks in one launch.  The reverse walk reads no entering state,
 // so the two are independent: workgroups 0 .. nwalk-1 walk forward and
-// nwalk .. 2 nwalk-1 in reverse, each with the other's LDS overlaid on its
-// own.  With at most half as many walks as compute units (a few heads per
+// nwalk .. 2 nwalk-1 in reverse, each in its own layout of one LDS block
+// (a union of the two).  With at most half as many walks as compute units (a few heads per
 // batch) the two run side by side instead of one after the other; otherwise
 // the workgroups are dispatched in order and the forward ones start first.
 // A walk's value slices keep workgroup ids equal mod 8 (one XCD), as their
