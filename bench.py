@@ -322,6 +322,12 @@ def prefill_block(w, pre, algo, o_dtype):
     }
 
 
+def backward_label(w) -> str:
+    tiles = ("fp32 tiles" if w.per_channel or w.dtype != "bf16" or w.Dk != 128 or w.Dv != 128
+             else "bf16 tiles with hi/lo split fp32 operands")
+    return f"{w.name}: gdr_chunk_bwd on the same inputs, standard-normal dL/do, fp32 gradients ({tiles})"
+
+
 def bench_backward(w, x, steps, warmup):
     """The backward pass (gdr_chunk_bwd) on the prefill workload's inputs
     with a seeded standard-normal dL/do; events around each call."""
@@ -666,7 +672,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the copy and GEMM peak measurements")
     ap.add_argument("--backward-steps", type=int, default=5,
-                    help="timed calls of the backward pass on the prefill workload (0: skip)")
+                    help="timed calls of the backward pass on each prefill workload (0: skip)")
     ap.add_argument("--next-rows-steps", type=int, default=5,
                     help="timed calls of the packed-batch, no-delta and multi-token recurrent entry points (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -744,6 +750,10 @@ def main():
         gpu_runs[name] = (wc, xc, {od: (host(pc["o"]), host(pc["s"]))})
         del pc
         torch.cuda.empty_cache()
+        if args.backward_steps > 0:
+            out["configs"][name]["backward"] = {"workload": backward_label(wc),
+                                                **bench_backward(wc, xc, args.backward_steps, 1)}
+            torch.cuda.empty_cache()
 
     decode_runs = None
     if not args.no_decode:
@@ -775,8 +785,7 @@ def main():
     if args.backward_steps > 0:
         bwd = bench_backward(w, x, args.backward_steps, 1)
         out["backward"] = {
-            "workload": f"{w.name}: gdr_chunk_bwd on the same inputs, standard-normal dL/do, fp32 gradients "
-                        f"({'fp32 tiles' if w.per_channel or w.dtype != 'bf16' or w.Dk != 128 or w.Dv != 128 else 'bf16 tiles with hi/lo split fp32 operands'})",
+            "workload": backward_label(w),
             **bwd,
             "train_step_tokens_per_s": w.B * w.T / ((head["warm"]["event_step_ms"] + bwd["ms_per_step"]) * 1e-3),
         }
